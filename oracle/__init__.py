@@ -1,0 +1,35 @@
+"""Plain, slow CPU oracle of the MoE layer forward.
+
+TEST INFRASTRUCTURE ONLY.  Only tests/, the smoke check in
+__graft_entry__.py and the cpu_baseline leg of bench.py may import it.  The
+product (combine_router_gating_amd) never imports, calls or loads it, and it
+imports nothing from the product.
+
+Everything is NumPy: floating point in float64 with one rounding at each
+point where the layer stores a tensor, except where the pages fix fp32 (the
+sigmoid scores used for expert selection, see fp32spec).
+"""
+from .fp32spec import exp_spec, sigmoid_spec
+from .moe import (
+    round_bf16,
+    round_to,
+    router_logits,
+    topk_indices,
+    score_and_select,
+    get_capacity,
+    drop_by_position,
+    route,
+    permute,
+    swiglu_rows,
+    grouped_experts,
+    combine,
+    moe_forward,
+    token_outputs,
+)
+
+__all__ = [
+    "exp_spec", "sigmoid_spec", "round_bf16", "round_to", "router_logits",
+    "topk_indices", "score_and_select", "get_capacity", "drop_by_position",
+    "route", "permute", "swiglu_rows", "grouped_experts", "combine",
+    "moe_forward", "token_outputs",
+]
