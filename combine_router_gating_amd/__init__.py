@@ -1,0 +1,22 @@
+"""MI355X-native single-GPU MoE layer forward: route -> permute -> grouped
+SwiGLU experts -> weighted combine, as HIP kernels behind a C interface
+(include/moe.h, built into libmoe.so)."""
+from .moe import (
+    moe_combine,
+    moe_forward,
+    moe_grouped_fc1_swiglu,
+    moe_grouped_fc2,
+    moe_grouped_mlp,
+    moe_max_rows,
+    moe_permute,
+    moe_route,
+    moe_route_capacity,
+    route_desc,
+)
+from ._lib import LIB_PATH, MoEError, load
+
+__all__ = [
+    "moe_combine", "moe_forward", "moe_grouped_fc1_swiglu", "moe_grouped_fc2", "moe_grouped_mlp",
+    "moe_max_rows", "moe_permute", "moe_route", "moe_route_capacity", "route_desc", "LIB_PATH",
+    "MoEError", "load",
+]

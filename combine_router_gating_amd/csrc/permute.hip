@@ -1,0 +1,134 @@
+// Dispatch preprocess: token rows to expert-major order.
+//
+// Megatron Core MoE 源码路径解析 §2 and §9: before the experts, the
+// dispatcher reorders token rows from sequence-major to expert-major layout;
+// MoE Internals: DeepSpeed-Megatron Expert Parallel Implementation §8 lists
+// the same step (permute tokens into expert order).  Rows are sorted by
+// (expert ascending, token ascending), which makes the order unique.
+//
+// Row of an entry (t, e): expert_offsets[e] + (entries of e in earlier token
+// blocks) + (entries of e earlier in t's block).  The first two terms come
+// from per-block counts and their scan (common.hip); the scatter kernel
+// counts the third from the block's map tile in LDS.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+// One workgroup per block of kCountBlock tokens, one wave per token.
+// Phase 1 (per token): ballot over the map row, 64 experts at a time, gives
+// the token's experts in ascending order and their rows.  Phase 2: write
+// row_id_map / permuted_probs / sorted_token and copy the token row, read
+// once, to each of its rows with 16-byte stores.
+__global__ void __launch_bounds__(256) permute_scatter_kernel(
+    const uint8_t* __restrict__ map, const float* __restrict__ probs, const uint4* __restrict__ x,
+    int64_t T, int E, int K, int chunks, const int32_t* __restrict__ blkoff,
+    const int32_t* __restrict__ expert_offsets, int64_t max_rows, uint4* __restrict__ px,
+    float* __restrict__ pprobs, int32_t* __restrict__ sorted_token, int32_t* __restrict__ row_id_map) {
+  __shared__ uint8_t tile[kCountBlock][kMaxExperts];
+  __shared__ int rows[kCountBlock][kMaxTopK];
+  __shared__ int exps[kCountBlock][kMaxTopK];
+  __shared__ int cnt[kCountBlock];
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
+  const int64_t t0 = static_cast<int64_t>(b) * kCountBlock;
+  const int nt = static_cast<int>(min(static_cast<int64_t>(kCountBlock), T - t0));
+  for (int i = threadIdx.x; i < nt * E; i += blockDim.x) tile[i / E][i % E] = map[t0 * E + i] != 0;
+  __syncthreads();
+
+  for (int tl = wave; tl < nt; tl += 4) {
+    int base_k = 0;
+    for (int c0 = 0; c0 < E; c0 += 64) {
+      const int e = c0 + lane;
+      const bool set = e < E && tile[tl][e];
+      const uint64_t mask = __ballot(set);
+      if (set) {
+        int prior = 0;
+        for (int u = 0; u < tl; ++u) prior += tile[u][e];
+        const int k = base_k + __popcll(mask & ((uint64_t(1) << lane) - 1));
+        if (k < K) {
+          rows[tl][k] = expert_offsets[e] + blkoff[static_cast<int64_t>(b) * E + e] + prior;
+          exps[tl][k] = e;
+        }
+      }
+      base_k += __popcll(mask);
+    }
+    if (lane == 0) cnt[tl] = min(base_k, K);
+  }
+  __syncthreads();
+
+  for (int tl = wave; tl < nt; tl += 4) {
+    const int64_t t = t0 + tl;
+    const int n = cnt[tl];
+    if (lane < K) row_id_map[t * K + lane] = lane < n ? rows[tl][lane] : -1;
+    if (lane < n) {
+      const int r = rows[tl][lane];
+      if (r < max_rows) {
+        pprobs[r] = probs[t * E + exps[tl][lane]];
+        sorted_token[r] = static_cast<int32_t>(t);
+      }
+    }
+    const uint4* src = x + t * chunks;
+    for (int i = lane; i < chunks; i += 64) {
+      const uint4 v = src[i];
+      for (int k = 0; k < n; ++k) {
+        const int r = rows[tl][k];
+        if (r < max_rows) px[static_cast<int64_t>(r) * chunks + i] = v;
+      }
+    }
+  }
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" size_t moe_permute_workspace_size(int64_t T, int64_t E) {
+  if (T <= 0 || E <= 0 || E > kMaxExperts) return 0;
+  return count_ws_bytes(T, E);
+}
+
+extern "C" moe_status moe_permute(int64_t T, int64_t h, int64_t E, int64_t K, int32_t dtype,
+                                  const void* x, const uint8_t* routing_map, const float* probs,
+                                  int64_t max_rows, void* permuted_x, float* permuted_probs,
+                                  int32_t* sorted_token, int32_t* row_id_map,
+                                  int32_t* expert_offsets, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  MOE_REQUIRE(T >= 0 && T < (int64_t(1) << 31), MOE_ERR_ARG, "moe_permute: T out of range");
+  MOE_REQUIRE(E >= 1 && E <= kMaxExperts, MOE_ERR_ARG, "moe_permute: E=%lld not in [1,%lld]",
+              (long long)E, (long long)kMaxExperts);
+  MOE_REQUIRE(K >= 1 && K <= E && K <= kMaxTopK, MOE_ERR_ARG, "moe_permute: bad K=%lld",
+              (long long)K);
+  MOE_REQUIRE(h >= 1 && h % 8 == 0, MOE_ERR_UNSUPPORTED, "moe_permute: h=%lld must be a multiple of 8",
+              (long long)h);
+  MOE_REQUIRE(dtype == MOE_F32 || dtype == MOE_BF16, MOE_ERR_ARG, "moe_permute: bad dtype %d", dtype);
+  MOE_REQUIRE(max_rows >= 0 && max_rows < (int64_t(1) << 31), MOE_ERR_ARG,
+              "moe_permute: max_rows out of range");
+  MOE_REQUIRE(T * E < (int64_t(1) << 31), MOE_ERR_UNSUPPORTED, "moe_permute: T*E too large");
+  MOE_REQUIRE(expert_offsets, MOE_ERR_ARG, "moe_permute: expert_offsets is required");
+  const hipStream_t s = as_stream(stream);
+  if (T == 0) {  // every other tensor is empty and may be NULL
+    launch_fill_i32(expert_offsets, E + 1, 0, s);
+    return check_launch("moe_permute(T=0)");
+  }
+  MOE_REQUIRE(x && routing_map && probs && row_id_map, MOE_ERR_ARG,
+              "moe_permute: NULL tensor argument");
+  MOE_REQUIRE(max_rows == 0 || (permuted_x && permuted_probs && sorted_token), MOE_ERR_ARG,
+              "moe_permute: NULL output with max_rows > 0");
+  const size_t need = moe_permute_workspace_size(T, E);
+  MOE_REQUIRE(workspace && workspace_bytes >= need, MOE_ERR_WORKSPACE,
+              "moe_permute: workspace of %zu bytes given, %zu needed", workspace_bytes, need);
+  const int64_t nblk = ceil_div(T, kCountBlock);
+  int32_t* hist = static_cast<int32_t*>(workspace);
+  int32_t* blkoff = hist + align_up(static_cast<size_t>(nblk * E) * sizeof(int32_t), 256) / 4;
+  launch_block_hist(routing_map, T, E, hist, s);
+  launch_count_scan(hist, nblk, E, -1, blkoff, nullptr, expert_offsets, s);
+  const int esize = dtype == MOE_BF16 ? 2 : 4;
+  const int chunks = static_cast<int>(h * esize / 16);
+  hipLaunchKernelGGL(permute_scatter_kernel, dim3(static_cast<unsigned>(nblk)), dim3(256), 0, s,
+                     routing_map, probs, static_cast<const uint4*>(x), T, static_cast<int>(E),
+                     static_cast<int>(K), chunks, blkoff, expert_offsets, max_rows,
+                     static_cast<uint4*>(permuted_x), permuted_probs, sorted_token, row_id_map);
+  return check_launch("moe_permute");
+}

@@ -1,0 +1,401 @@
+// Router forward: fp32 gating linear, score function, top-k, capacity drop.
+//
+// Megatron Core MoE 源码路径解析 §3: the router casts its input to fp32 and
+// applies a linear gate (optional bias) to get [T,E] logits.  §4/§5: top-k
+// routing with a score function produces fp32 probs and a [T,E] routing
+// map; with sigmoid scoring an fp32 expert bias shifts the choice only.
+// §8: with a capacity factor each expert keeps at most `capacity` tokens,
+// chosen by position (here: the earliest tokens), and the dropped entries
+// leave both the map and the probs.
+//
+// Kernels, in launch order:
+//   router_logits_kernel   logits = x w^T (+ b), fp32 FMA, LDS-tiled
+//   router_topk_kernel     one wave per token: scores, K rounds of a wave-wide
+//                          argmax, probs, map, per-block expert counts
+//   count_scan_kernel      (capacity only) per-expert prefix over blocks
+//   router_drop_kernel     (capacity only) clear entries ranked >= capacity
+#include <cmath>
+
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+// ------------------------------------------------------------- gating linear
+// Tile: 64 tokens x 64 experts per 256-thread workgroup, 4x4 outputs per
+// thread, k-slabs of 32 staged through LDS (x transposed so that a thread
+// reads its 4 tokens with one 16-byte LDS load).
+constexpr int LT = 64, LE = 64, LK = 32;
+
+template <typename XT>
+__device__ __forceinline__ float load_x(const XT* p);
+template <>
+__device__ __forceinline__ float load_x<float>(const float* p) { return *p; }
+template <>
+__device__ __forceinline__ float load_x<uint16_t>(const uint16_t* p) { return bf16_bits_to_f32(*p); }
+
+template <typename XT>
+__global__ void __launch_bounds__(256) router_logits_kernel(const XT* __restrict__ x,
+                                                            const float* __restrict__ w,
+                                                            const float* __restrict__ bias,
+                                                            float* __restrict__ logits, int64_t T,
+                                                            int h, int E) {
+  __shared__ float xs[LK][LT + 4];
+  __shared__ float ws[LK][LE + 4];
+  const int tid = threadIdx.x;
+  const int tx = tid % 16;  // experts tx*4 .. +3
+  const int ty = tid / 16;  // tokens  ty*4 .. +3
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * LT;
+  const int e0 = blockIdx.y * LE;
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < h; k0 += LK) {
+    // stage: 64 rows x 32 k for x and for w; each thread moves 8 elements of each
+    for (int i = tid; i < LT * LK; i += 256) {
+      const int r = i / LK, c = i % LK;
+      const int64_t t = t0 + r;
+      const int k = k0 + c;
+      xs[c][r] = (t < T && k < h) ? load_x<XT>(x + t * h + k) : 0.f;
+      const int e = e0 + r;
+      ws[c][r] = (e < E && k < h) ? w[static_cast<int64_t>(e) * h + k] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int c = 0; c < LK; ++c) {
+      const float4 xv = *reinterpret_cast<const float4*>(&xs[c][ty * 4]);
+      const float4 wv = *reinterpret_cast<const float4*>(&ws[c][tx * 4]);
+      const float xa[4] = {xv.x, xv.y, xv.z, xv.w};
+      const float wa[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(xa[i], wa[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t t = t0 + ty * 4 + i;
+    if (t >= T) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = e0 + tx * 4 + j;
+      if (e < E) logits[t * E + e] = acc[i][j] + (bias ? bias[e] : 0.f);
+    }
+  }
+}
+
+// ------------------------------------------------------- fixed fp32 sigmoid
+// exp(y) for y <= 0 by a fixed sequence of IEEE fp32 operations, each rounded
+// to nearest even with no fused multiply-add: n = rint(y*log2e); Cody-Waite
+// reduction r = (y - n*C1) - n*C2 with C1 = ln2 cut to 12 significant bits
+// and C2 = fp32(ln2 - C1); p = degree-7 Taylor polynomial of e^r in Horner
+// form with fp32(1/k!) coefficients; result ldexp(p, n); 0 below y = -86
+// (keeps every result in the fp32 normal range).
+__device__ __noinline__ float exp_fixed(float y) {
+#pragma clang fp contract(off)
+  const float log2e = 0x1.715476p+0f;  // fp32(1/ln 2)
+  const float c1 = 0x1.62ep-1f;        // ln 2 truncated to 12 bits
+  const float c2 = 0x1.0bfbe8p-15f;    // fp32(ln 2 - c1)
+  const float n = rintf(y * log2e);
+  const float r = (y - n * c1) - n * c2;
+  float p = 0x1.a01a02p-13f;           // 1/7!
+  p = p * r + 0x1.6c16c2p-10f;         // 1/6!
+  p = p * r + 0x1.111112p-7f;          // 1/5!
+  p = p * r + 0x1.555556p-5f;          // 1/4!
+  p = p * r + 0x1.555556p-3f;          // 1/3!
+  p = p * r + 0.5f;                    // 1/2!
+  p = p * r + 1.0f;                    // 1/1!
+  p = p * r + 1.0f;                    // 1/0!
+  const float out = ldexpf(p, static_cast<int>(n));
+  return (y < -86.0f) ? 0.0f : out;
+}
+
+// sigmoid(x) = 1/(1+e) for x >= 0, e/(1+e) for x < 0, with e = exp_fixed(-|x|).
+__device__ __noinline__ float sigmoid_fixed(float x) {
+#pragma clang fp contract(off)
+  const float e = exp_fixed(-fabsf(x));
+  const float den = 1.0f + e;
+  return (x >= 0.0f) ? (1.0f / den) : (e / den);
+}
+
+// --------------------------------------------------------------- top-k
+// (value descending, index ascending) is a strict total order on non-NaN
+// keys, so a butterfly reduction gives every lane the same winner.
+__device__ __forceinline__ bool better(float av, int ai, float bv, int bi) {
+  if (ai < 0) return false;
+  if (bi < 0) return true;
+  return av > bv || (av == bv && ai < bi);
+}
+
+template <int EPL>
+__global__ void __launch_bounds__(256) router_topk_kernel(
+    const float* __restrict__ logits, const float* __restrict__ expert_bias, int64_t T, int E,
+    int K, int score, int pre_softmax, float* __restrict__ scores_out, float* __restrict__ probs,
+    uint8_t* __restrict__ rmap, int32_t* __restrict__ hist) {
+  __shared__ int cnt[kMaxExperts];
+  const int lane = threadIdx.x % 64;
+  const int wave = threadIdx.x / 64;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;
+  __syncthreads();
+  constexpr int kTokPerWave = kCountBlock / 4;
+  for (int it = 0; it < kTokPerWave; ++it) {
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * kCountBlock + wave * kTokPerWave + it;
+    if (t >= T) break;  // wave-uniform
+    float l[EPL], s[EPL], key[EPL];
+    bool valid[EPL], taken[EPL];
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+      const int e = lane + 64 * j;
+      valid[j] = e < E;
+      taken[j] = false;
+      l[j] = valid[j] ? logits[t * E + e] : -INFINITY;
+    }
+    if (score == MOE_SCORE_SOFTMAX) {
+      float m = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) m = fmaxf(m, l[j]);
+      m = wave_max(m);
+      float sum = 0.f;
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) {
+        s[j] = valid[j] ? expf(l[j] - m) : 0.f;
+        sum += s[j];
+      }
+      sum = wave_sum(sum);
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) {
+        s[j] = s[j] / sum;
+        key[j] = l[j];
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) {
+        s[j] = valid[j] ? sigmoid_fixed(l[j]) : 0.f;
+        key[j] = (valid[j] && expert_bias) ? s[j] + expert_bias[lane + 64 * j] : s[j];
+      }
+    }
+    float top_logit = 0.f;
+    for (int k = 0; k < K; ++k) {
+      float bv = 0.f;
+      int bi = -1;
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) {
+        const int e = lane + 64 * j;
+        if (valid[j] && !taken[j] && better(key[j], e, bv, bi)) {
+          bv = key[j];
+          bi = e;
+        }
+      }
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) {
+        const float ov = __shfl_xor(bv, off, 64);
+        const int oi = __shfl_xor(bi, off, 64);
+        if (better(ov, oi, bv, bi)) {
+          bv = ov;
+          bi = oi;
+        }
+      }
+      bi = __shfl(bi, 0, 64);
+      if (k == 0) top_logit = __shfl(bv, 0, 64);
+#pragma unroll
+      for (int j = 0; j < EPL; ++j)
+        if (lane + 64 * j == bi) taken[j] = true;
+    }
+    float p[EPL];
+    if (score == MOE_SCORE_SOFTMAX && pre_softmax) {
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) p[j] = taken[j] ? s[j] : 0.f;
+    } else if (score == MOE_SCORE_SOFTMAX) {
+      // softmax over the K chosen logits; the first winner holds their maximum
+      float sum = 0.f;
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) {
+        p[j] = taken[j] ? expf(l[j] - top_logit) : 0.f;
+        sum += p[j];
+      }
+      sum = wave_sum(sum);
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) p[j] = p[j] / sum;
+    } else {
+      float sum = 0.f;
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) sum += taken[j] ? s[j] : 0.f;
+      sum = wave_sum(sum) + 1e-20f;
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) p[j] = taken[j] ? s[j] / sum : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+      const int e = lane + 64 * j;
+      if (!valid[j]) continue;
+      probs[t * E + e] = p[j];
+      rmap[t * E + e] = taken[j] ? 1 : 0;
+      if (scores_out) scores_out[t * E + e] = s[j];
+      if (taken[j]) atomicAdd(&cnt[e], 1);
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x)
+    hist[static_cast<int64_t>(blockIdx.x) * E + e] = cnt[e];
+}
+
+// ------------------------------------------------------------ capacity drop
+// Thread e walks the block's tokens in order; rank = tokens routed to e in
+// earlier blocks + earlier in this block.  Entries ranked >= cap are dropped.
+__global__ void __launch_bounds__(256) router_drop_kernel(const int32_t* __restrict__ blkoff,
+                                                          int64_t T, int E, int64_t cap,
+                                                          float* __restrict__ probs,
+                                                          uint8_t* __restrict__ rmap) {
+  const int b = blockIdx.x;
+  const int64_t t0 = static_cast<int64_t>(b) * kCountBlock;
+  const int nt = static_cast<int>(min(static_cast<int64_t>(kCountBlock), T - t0));
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    int64_t r = blkoff[static_cast<int64_t>(b) * E + e];
+    for (int i = 0; i < nt; ++i) {
+      const int64_t idx = (t0 + i) * E + e;
+      if (rmap[idx]) {
+        if (r >= cap) {
+          rmap[idx] = 0;
+          probs[idx] = 0.f;
+        }
+        ++r;
+      }
+    }
+  }
+}
+
+template <int EPL>
+void launch_topk(int64_t nblk, hipStream_t s, const float* logits, const float* eb, int64_t T,
+                 int E, int K, int score, int pre, float* scores, float* probs, uint8_t* map,
+                 int32_t* hist) {
+  hipLaunchKernelGGL(router_topk_kernel<EPL>, dim3(static_cast<unsigned>(nblk)), dim3(256), 0, s,
+                     logits, eb, T, E, K, score, pre, scores, probs, map, hist);
+}
+
+int64_t capacity_of(const moe_route_desc* d) {
+  if (!(d->capacity_factor > 0.f)) return -1;
+  const double ratio = static_cast<double>(d->T) * static_cast<double>(d->K) *
+                       static_cast<double>(d->capacity_factor) / static_cast<double>(d->E);
+  int64_t cap = static_cast<int64_t>(std::ceil(ratio));
+  if (cap < d->min_capacity) cap = d->min_capacity;
+  return cap >= d->T ? -1 : cap;
+}
+
+moe_status validate(const moe_route_desc* d) {
+  MOE_REQUIRE(d != nullptr, MOE_ERR_ARG, "moe_route: desc is NULL");
+  MOE_REQUIRE(d->T >= 0 && d->T < (int64_t(1) << 31), MOE_ERR_ARG, "moe_route: T=%lld out of range",
+              (long long)d->T);
+  MOE_REQUIRE(d->E >= 1 && d->E <= kMaxExperts, MOE_ERR_ARG, "moe_route: E=%lld not in [1,%lld]",
+              (long long)d->E, (long long)kMaxExperts);
+  MOE_REQUIRE(d->K >= 1 && d->K <= d->E && d->K <= kMaxTopK, MOE_ERR_ARG,
+              "moe_route: K=%lld must be in [1, min(E, %lld)]", (long long)d->K,
+              (long long)kMaxTopK);
+  MOE_REQUIRE(d->h >= 1 && d->h % 8 == 0, MOE_ERR_UNSUPPORTED,
+              "moe_route: h=%lld must be a positive multiple of 8", (long long)d->h);
+  MOE_REQUIRE(d->x_dtype == MOE_F32 || d->x_dtype == MOE_BF16, MOE_ERR_ARG,
+              "moe_route: bad x_dtype %d", d->x_dtype);
+  MOE_REQUIRE(d->score == MOE_SCORE_SOFTMAX || d->score == MOE_SCORE_SIGMOID, MOE_ERR_ARG,
+              "moe_route: bad score %d", d->score);
+  MOE_REQUIRE(d->min_capacity >= 0, MOE_ERR_ARG, "moe_route: min_capacity < 0");
+  MOE_REQUIRE(static_cast<int64_t>(d->T) * d->E < (int64_t(1) << 31), MOE_ERR_UNSUPPORTED,
+              "moe_route: T*E too large");
+  return MOE_OK;
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" size_t moe_route_workspace_size(const moe_route_desc* d) {
+  if (validate(d) != MOE_OK || d->T == 0) return 0;
+  const size_t logits = align_up(static_cast<size_t>(d->T * d->E) * sizeof(float), 256);
+  return logits + count_ws_bytes(d->T, d->E);
+}
+
+extern "C" int64_t moe_route_capacity(const moe_route_desc* d) {
+  if (validate(d) != MOE_OK) return -1;
+  return capacity_of(d);
+}
+
+extern "C" int64_t moe_max_rows(const moe_route_desc* d) {
+  if (validate(d) != MOE_OK) return -1;
+  const int64_t tk = d->T * d->K;
+  const int64_t cap = capacity_of(d);
+  return cap < 0 ? tk : std::min(tk, cap * d->E);
+}
+
+extern "C" moe_status moe_route(const moe_route_desc* d, const void* x, const float* w_router,
+                                const float* b_router, const float* expert_bias,
+                                const float* logits_in, float* logits_out, float* scores_out,
+                                float* probs, uint8_t* routing_map, int32_t* tokens_per_expert,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  moe_status st = validate(d);
+  if (st != MOE_OK) return st;
+  MOE_REQUIRE(tokens_per_expert, MOE_ERR_ARG, "moe_route: tokens_per_expert is required");
+  MOE_REQUIRE(expert_bias == nullptr || d->score == MOE_SCORE_SIGMOID, MOE_ERR_UNSUPPORTED,
+              "moe_route: expert_bias is defined for sigmoid scoring only");
+  const hipStream_t s = as_stream(stream);
+  const int64_t T = d->T, E = d->E;
+  if (T == 0) {  // [0,E] tensors may be NULL
+    launch_fill_i32(tokens_per_expert, E, 0, s);
+    return check_launch("moe_route(T=0)");
+  }
+  MOE_REQUIRE(probs && routing_map, MOE_ERR_ARG, "moe_route: probs and routing_map are required");
+  MOE_REQUIRE(logits_in || (x && w_router), MOE_ERR_ARG,
+              "moe_route: x and w_router are required unless logits_in is given");
+  const size_t need = moe_route_workspace_size(d);
+  MOE_REQUIRE(workspace && workspace_bytes >= need, MOE_ERR_WORKSPACE,
+              "moe_route: workspace of %zu bytes given, %zu needed", workspace_bytes, need);
+
+  char* ws = static_cast<char*>(workspace);
+  float* logits_ws = reinterpret_cast<float*>(ws);
+  int32_t* hist = reinterpret_cast<int32_t*>(ws + align_up(T * E * sizeof(float), 256));
+  const int64_t nblk = ceil_div(T, kCountBlock);
+  int32_t* blkoff = hist + align_up(static_cast<size_t>(nblk * E) * sizeof(int32_t), 256) / 4;
+
+  const float* logits = logits_in;
+  if (!logits) {
+    float* dst = logits_out ? logits_out : logits_ws;
+    dim3 grid(static_cast<unsigned>(ceil_div(T, LT)), static_cast<unsigned>(ceil_div(E, LE)));
+    if (d->x_dtype == MOE_BF16)
+      hipLaunchKernelGGL(router_logits_kernel<uint16_t>, grid, dim3(256), 0, s,
+                         static_cast<const uint16_t*>(x), w_router, b_router, dst, T,
+                         static_cast<int>(d->h), static_cast<int>(E));
+    else
+      hipLaunchKernelGGL(router_logits_kernel<float>, grid, dim3(256), 0, s,
+                         static_cast<const float*>(x), w_router, b_router, dst, T,
+                         static_cast<int>(d->h), static_cast<int>(E));
+    logits = dst;
+  } else if (logits_out && logits_out != logits_in) {
+    const hipError_t ce =
+        hipMemcpyAsync(logits_out, logits_in, T * E * sizeof(float), hipMemcpyDeviceToDevice, s);
+    MOE_REQUIRE(ce == hipSuccess, MOE_ERR_HIP, "moe_route: copy of logits_in failed: %s",
+                hipGetErrorString(ce));
+  }
+
+  const int Ei = static_cast<int>(E), Ki = static_cast<int>(d->K);
+  const int epl = static_cast<int>(ceil_div(E, 64));
+  if (epl <= 1)
+    launch_topk<1>(nblk, s, logits, expert_bias, T, Ei, Ki, d->score, d->pre_softmax, scores_out,
+                   probs, routing_map, hist);
+  else if (epl <= 2)
+    launch_topk<2>(nblk, s, logits, expert_bias, T, Ei, Ki, d->score, d->pre_softmax, scores_out,
+                   probs, routing_map, hist);
+  else if (epl <= 4)
+    launch_topk<4>(nblk, s, logits, expert_bias, T, Ei, Ki, d->score, d->pre_softmax, scores_out,
+                   probs, routing_map, hist);
+  else if (epl <= 8)
+    launch_topk<8>(nblk, s, logits, expert_bias, T, Ei, Ki, d->score, d->pre_softmax, scores_out,
+                   probs, routing_map, hist);
+  else
+    launch_topk<16>(nblk, s, logits, expert_bias, T, Ei, Ki, d->score, d->pre_softmax, scores_out,
+                    probs, routing_map, hist);
+
+  const int64_t cap = capacity_of(d);
+  launch_count_scan(hist, nblk, E, cap, blkoff, tokens_per_expert, nullptr, s);
+  if (cap >= 0)
+    hipLaunchKernelGGL(router_drop_kernel, dim3(static_cast<unsigned>(nblk)), dim3(256), 0, s, blkoff,
+                       T, Ei, cap, probs, routing_map);
+  return check_launch("moe_route");
+}

@@ -1,0 +1,252 @@
+"""Python binding of libmoe: same entry points as include/moe.h.
+
+Argument marshalling only.  Tensors are torch CUDA (HIP) tensors; outputs
+and workspaces are allocated with torch, every step of the layer runs in
+the library's HIP kernels, enqueued on torch's current stream.  There is
+no fallback: a missing library or a CPU tensor raises.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Dict, Optional
+
+import torch
+
+from . import _lib
+from ._lib import MOE_BF16, MOE_F32, MOE_SCORE_SIGMOID, MOE_SCORE_SOFTMAX, RouteDesc, check
+
+_DT = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16}
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream() -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+    return t
+
+
+def _dtype_code(t: torch.Tensor, name: str) -> int:
+    if t.dtype not in _DT:
+        raise ValueError(f"{name}: unsupported dtype {t.dtype}")
+    return _DT[t.dtype]
+
+
+def route_desc(T: int, h: int, E: int, K: int, x_dtype: torch.dtype, score: str = "softmax",
+               pre_softmax: bool = True, capacity_factor: float = 0.0,
+               min_capacity: int = 0) -> RouteDesc:
+    return RouteDesc(T, h, E, K, _DT[x_dtype],
+                     MOE_SCORE_SIGMOID if score == "sigmoid" else MOE_SCORE_SOFTMAX,
+                     1 if pre_softmax else 0, float(capacity_factor), int(min_capacity))
+
+
+def moe_max_rows(desc: RouteDesc) -> int:
+    return int(_lib.load().moe_max_rows(ctypes.byref(desc)))
+
+
+def moe_route_capacity(desc: RouteDesc) -> int:
+    return int(_lib.load().moe_route_capacity(ctypes.byref(desc)))
+
+
+def moe_route(x: Optional[torch.Tensor], w_router: Optional[torch.Tensor], *, K: int,
+              b_router: Optional[torch.Tensor] = None, expert_bias: Optional[torch.Tensor] = None,
+              score: str = "softmax", pre_softmax: bool = True, capacity_factor: float = 0.0,
+              min_capacity: int = 0, logits_in: Optional[torch.Tensor] = None,
+              want_logits: bool = False, want_scores: bool = False,
+              T: Optional[int] = None, h: Optional[int] = None) -> Dict[str, torch.Tensor]:
+    """Router forward (gating, score, top-k, capacity drop)."""
+    lib = _lib.load()
+    if logits_in is not None:
+        _need(logits_in, "logits_in", torch.float32)
+        T_, E = logits_in.shape
+        dev = logits_in.device
+        h_ = h if h is not None else (x.shape[1] if x is not None else 8)
+        xdt = x.dtype if x is not None else torch.float32
+    else:
+        _need(x, "x")
+        _need(w_router, "w_router", torch.float32)
+        T_, h_ = x.shape
+        E = w_router.shape[0]
+        _need(w_router, "w_router", torch.float32, (E, h_))
+        dev = x.device
+        xdt = x.dtype
+    if b_router is not None:
+        _need(b_router, "b_router", torch.float32, (E,))
+    if expert_bias is not None:
+        _need(expert_bias, "expert_bias", torch.float32, (E,))
+    desc = route_desc(T_, h_, E, K, xdt, score, pre_softmax, capacity_factor, min_capacity)
+    probs = torch.empty((T_, E), dtype=torch.float32, device=dev)
+    rmap = torch.empty((T_, E), dtype=torch.uint8, device=dev)
+    tpe = torch.empty((E,), dtype=torch.int32, device=dev)
+    logits = torch.empty((T_, E), dtype=torch.float32, device=dev) if want_logits else None
+    scores = torch.empty((T_, E), dtype=torch.float32, device=dev) if want_scores else None
+    ws_bytes = int(lib.moe_route_workspace_size(ctypes.byref(desc)))
+    ws = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=dev)
+    st = lib.moe_route(ctypes.byref(desc), _ptr(x) if logits_in is None else None,
+                       _ptr(w_router) if logits_in is None else None, _ptr(b_router),
+                       _ptr(expert_bias), _ptr(logits_in), _ptr(logits), _ptr(scores),
+                       _ptr(probs), _ptr(rmap), _ptr(tpe), _ptr(ws), ws_bytes, _stream())
+    check("moe_route", st)
+    out = {"probs": probs, "routing_map": rmap, "tokens_per_expert": tpe,
+           "max_rows": moe_max_rows(desc), "capacity": moe_route_capacity(desc)}
+    if logits is not None:
+        out["logits"] = logits
+    if scores is not None:
+        out["scores"] = scores
+    return out
+
+
+def moe_permute(x: torch.Tensor, routing_map: torch.Tensor, probs: torch.Tensor, K: int,
+                max_rows: int) -> Dict[str, torch.Tensor]:
+    """Expert-major permute of token rows."""
+    lib = _lib.load()
+    _need(x, "x")
+    T, h = x.shape
+    E = routing_map.shape[1]
+    _need(routing_map, "routing_map", torch.uint8, (T, E))
+    _need(probs, "probs", torch.float32, (T, E))
+    dev = x.device
+    rows = max(int(max_rows), 0)
+    px = torch.empty((rows, h), dtype=x.dtype, device=dev)
+    pp = torch.empty((rows,), dtype=torch.float32, device=dev)
+    st_tok = torch.empty((rows,), dtype=torch.int32, device=dev)
+    rid = torch.empty((T, K), dtype=torch.int32, device=dev)
+    offs = torch.empty((E + 1,), dtype=torch.int32, device=dev)
+    ws_bytes = int(lib.moe_permute_workspace_size(T, E))
+    ws = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=dev)
+    st = lib.moe_permute(T, h, E, K, _dtype_code(x, "x"), _ptr(x), _ptr(routing_map), _ptr(probs),
+                         rows, _ptr(px), _ptr(pp), _ptr(st_tok), _ptr(rid), _ptr(offs), _ptr(ws),
+                         ws_bytes, _stream())
+    check("moe_permute", st)
+    return {"permuted_x": px, "permuted_probs": pp, "sorted_token": st_tok, "row_id_map": rid,
+            "expert_offsets": offs}
+
+
+def _mlp_args(permuted_x, tokens_per_expert, w_a, w_b=None):
+    _need(permuted_x, "rows")
+    _need(tokens_per_expert, "tokens_per_expert", torch.int32)
+    E = tokens_per_expert.shape[0]
+    _need(w_a, "weight", permuted_x.dtype)
+    if w_b is not None:
+        _need(w_b, "weight", permuted_x.dtype, w_a.shape)
+    if w_a.shape[0] != E:
+        raise ValueError("weights and tokens_per_expert disagree on E")
+    return E
+
+
+def moe_grouped_fc1_swiglu(permuted_x: torch.Tensor, tokens_per_expert: torch.Tensor,
+                           w_gate: torch.Tensor, w_up: torch.Tensor,
+                           act: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """act = silu(x W_gate^T) * (x W_up^T), per expert row range."""
+    E = _mlp_args(permuted_x, tokens_per_expert, w_gate, w_up)
+    rows, h = permuted_x.shape
+    f = w_gate.shape[1]
+    _need(w_gate, "w_gate", permuted_x.dtype, (E, f, h))
+    if act is None:
+        act = torch.empty((rows, f), dtype=permuted_x.dtype, device=permuted_x.device)
+    _need(act, "act", permuted_x.dtype, (rows, f))
+    st = _lib.load().moe_grouped_fc1_swiglu(E, h, f, rows, _dtype_code(permuted_x, "x"),
+                                            _ptr(permuted_x), _ptr(tokens_per_expert),
+                                            _ptr(w_gate), _ptr(w_up), _ptr(act), _stream())
+    check("moe_grouped_fc1_swiglu", st)
+    return act
+
+
+def moe_grouped_fc2(act: torch.Tensor, tokens_per_expert: torch.Tensor, w_down: torch.Tensor,
+                    expert_out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """expert_out = act W_down^T, per expert row range."""
+    E = _mlp_args(act, tokens_per_expert, w_down)
+    rows, f = act.shape
+    h = w_down.shape[1]
+    _need(w_down, "w_down", act.dtype, (E, h, f))
+    if expert_out is None:
+        expert_out = torch.empty((rows, h), dtype=act.dtype, device=act.device)
+    _need(expert_out, "expert_out", act.dtype, (rows, h))
+    st = _lib.load().moe_grouped_fc2(E, h, f, rows, _dtype_code(act, "act"), _ptr(act),
+                                     _ptr(tokens_per_expert), _ptr(w_down), _ptr(expert_out),
+                                     _stream())
+    check("moe_grouped_fc2", st)
+    return expert_out
+
+
+def moe_grouped_mlp(permuted_x: torch.Tensor, tokens_per_expert: torch.Tensor,
+                    w_gate: torch.Tensor, w_up: torch.Tensor, w_down: torch.Tensor):
+    """SwiGLU MLP of every expert over its row range; returns (act, expert_out)."""
+    E = _mlp_args(permuted_x, tokens_per_expert, w_gate, w_up)
+    rows, h = permuted_x.shape
+    f = w_gate.shape[1]
+    _need(w_gate, "w_gate", permuted_x.dtype, (E, f, h))
+    _need(w_down, "w_down", permuted_x.dtype, (E, h, f))
+    act = torch.empty((rows, f), dtype=permuted_x.dtype, device=permuted_x.device)
+    out = torch.empty((rows, h), dtype=permuted_x.dtype, device=permuted_x.device)
+    st = _lib.load().moe_grouped_mlp(E, h, f, rows, _dtype_code(permuted_x, "x"), _ptr(permuted_x),
+                                     _ptr(tokens_per_expert), _ptr(w_gate), _ptr(w_up),
+                                     _ptr(w_down), _ptr(act), _ptr(out), _stream())
+    check("moe_grouped_mlp", st)
+    return act, out
+
+
+def moe_combine(expert_out: torch.Tensor, permuted_probs: torch.Tensor, row_id_map: torch.Tensor,
+                shared_out: Optional[torch.Tensor] = None,
+                out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """out[t] = sum_k p * expert_out[row_id_map[t,k]] (+ shared_out[t])."""
+    _need(expert_out, "expert_out")
+    rows, h = expert_out.shape
+    _need(permuted_probs, "permuted_probs", torch.float32, (rows,))
+    _need(row_id_map, "row_id_map", torch.int32)
+    T, K = row_id_map.shape
+    if shared_out is not None:
+        _need(shared_out, "shared_out", expert_out.dtype, (T, h))
+    if out is None:
+        out = torch.empty((T, h), dtype=expert_out.dtype, device=expert_out.device)
+    _need(out, "out", expert_out.dtype, (T, h))
+    st = _lib.load().moe_combine(T, h, K, _dtype_code(expert_out, "expert_out"), _ptr(expert_out),
+                                 _ptr(permuted_probs), _ptr(row_id_map), rows, _ptr(shared_out),
+                                 _ptr(out), _stream())
+    check("moe_combine", st)
+    return out
+
+
+def moe_forward(inp: Dict[str, torch.Tensor], *, K: int, score: str = "softmax",
+                pre_softmax: bool = True, capacity_factor: float = 0.0, min_capacity: int = 0,
+                want_logits: bool = False) -> Dict[str, torch.Tensor]:
+    """route -> permute -> grouped SwiGLU experts -> combine (+ shared expert).
+
+    `inp` holds the tensors datagen.make_inputs returns (x, w_router,
+    optional b_router / expert_bias, w_gate, w_up, w_down, optional
+    shared_gate / shared_up / shared_down).
+    """
+    x = inp["x"]
+    r = moe_route(x, inp["w_router"], K=K, b_router=inp.get("b_router"),
+                  expert_bias=inp.get("expert_bias"), score=score, pre_softmax=pre_softmax,
+                  capacity_factor=capacity_factor, min_capacity=min_capacity,
+                  want_logits=want_logits)
+    pm = moe_permute(x, r["routing_map"], r["probs"], K, r["max_rows"])
+    act = moe_grouped_fc1_swiglu(pm["permuted_x"], r["tokens_per_expert"], inp["w_gate"],
+                                 inp["w_up"])
+    y = moe_grouped_fc2(act, r["tokens_per_expert"], inp["w_down"])
+    shared_out = None
+    if "shared_gate" in inp:
+        T = x.shape[0]
+        ones = torch.full((1,), T, dtype=torch.int32, device=x.device)
+        s_act = moe_grouped_fc1_swiglu(x, ones, inp["shared_gate"][None], inp["shared_up"][None])
+        shared_out = moe_grouped_fc2(s_act, ones, inp["shared_down"][None])
+    out = moe_combine(y, pm["permuted_probs"], pm["row_id_map"], shared_out)
+    res = dict(r)
+    res.update(pm)
+    res.update({"act": act, "expert_out": y, "shared_out": shared_out, "out": out})
+    return res

@@ -1,0 +1,220 @@
+/*
+ * moe.h — C interface of a single-GPU Mixture-of-Experts layer forward for
+ * AMD Instinct MI355X (gfx950): route -> permute -> grouped SwiGLU experts
+ * -> weighted combine, for one GPU's local experts.
+ *
+ * Sources (web pages, cited by title and section):
+ *   [MC] "MoE我们喜欢你（三）：Megatron Core MoE 源码路径解析" — §2 layer main
+ *        path, §3 gating, §4 top-k routing, §5 score functions, §7 expert
+ *        bias, §8 token dropping, §9 dispatcher, §10 grouped experts,
+ *        §11 shared expert.
+ *   [DS] "MoE Internals: DeepSpeed-Megatron Expert Parallel Implementation"
+ *        — §3 capacity knobs, §8 the forward steps.
+ *   [MG] "Scalable Training of Mixture-of-Experts Models with Megatron Core"
+ *        (daily-arxiv summary) — grouped GEMM and sync-free dropless
+ *        execution under "计算效率优化".
+ *
+ * Conventions shared by every entry point:
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller.  The
+ *     library never allocates or frees device memory and keeps no state
+ *     between calls beyond the thread-local error message.
+ *   - Tensors are dense, row-major (last index fastest), with no padding.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls only
+ *     enqueue work on it and return; they never synchronise and never read
+ *     device data on the host (tokens_per_expert stays on the device).
+ *   - Host-side argument checks run before any launch.  On failure the call
+ *     returns a non-zero moe_status, launches nothing, and moe_last_error()
+ *     describes the problem.  A failed launch returns MOE_ERR_HIP.
+ *   - Device-resident index inputs (routing_map, tokens_per_expert,
+ *     row_id_map) are never trusted for addressing: kernels clamp to the
+ *     caller-stated sizes, so malformed values give wrong numbers, not
+ *     out-of-bounds accesses.  NaN/Inf inputs are outside the contract.
+ *   - Element dtypes: moe_dtype selects fp32 or bf16 for activations,
+ *     expert weights and outputs.  The router always computes in fp32.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_ARG = 1,          /* invalid argument (null pointer, bad size, K > E, ...) */
+  MOE_ERR_UNSUPPORTED = 2,  /* valid but not implemented (e.g. a size constraint below) */
+  MOE_ERR_WORKSPACE = 3,    /* workspace missing or smaller than *_workspace_size() */
+  MOE_ERR_HIP = 4           /* a HIP launch failed */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+typedef enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_score;
+
+/* Version of this interface. */
+int moe_abi_version(void);
+
+/* Message for the last non-OK status returned on the calling thread. */
+const char* moe_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * Router: gating linear + score function + top-k + capacity drop.
+ * [MC] §3 (logits = x W^T (+ b) in fp32), §4 (routing returns probs and a
+ * [T,E] routing map), §5 (score functions, selection-only expert bias), §8
+ * (capacity and the "position" drop policy); [DS] §3 (capacity factor,
+ * minimum capacity).
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  int64_t T;                /* tokens (sequence x batch, flattened) */
+  int64_t h;                /* hidden size; must be a multiple of 8 */
+  int64_t E;                /* experts, 1..1024 */
+  int64_t K;                /* experts per token, 1..E and <= 64 */
+  int32_t x_dtype;          /* moe_dtype of x */
+  int32_t score;            /* moe_score */
+  int32_t pre_softmax;      /* softmax only: 1 = softmax over all E, then top-K
+                               (probs are those softmax values); 0 = top-K of
+                               the logits, then softmax over the K chosen */
+  float capacity_factor;    /* <= 0: dropless.  > 0: capacity per expert =
+                               max(ceil(T*K*capacity_factor/E), min_capacity)
+                               (ratio computed in double); each expert keeps
+                               the earliest tokens routed to it */
+  int64_t min_capacity;     /* lower bound of the capacity; 0 = none */
+} moe_route_desc;
+
+/* Bytes of device workspace moe_route needs (0 is a valid answer only for
+ * T == 0). */
+size_t moe_route_workspace_size(const moe_route_desc* desc);
+
+/* Per-expert capacity for desc, or -1 when routing is dropless or when the
+ * capacity is at least T (then nothing can be dropped). */
+int64_t moe_route_capacity(const moe_route_desc* desc);
+
+/* Upper bound on the number of routed rows N = sum(tokens_per_expert):
+ * T*K when dropless, else min(T*K, E*capacity).  Size permute/expert
+ * buffers with it. */
+int64_t moe_max_rows(const moe_route_desc* desc);
+
+/*
+ * moe_route — router forward.
+ *   x            [T,h]  x_dtype         hidden states (ignored if logits_in)
+ *   w_router     [E,h]  fp32            gating weight (ignored if logits_in)
+ *   b_router     [E]    fp32 or NULL    gating bias; part of the logits, so it
+ *                                       affects both the choice and the probs
+ *   expert_bias  [E]    fp32 or NULL    sigmoid only: added to the scores for
+ *                                       the top-K choice, never to the probs
+ *                                       ([MC] §5, §7)
+ *   logits_in    [T,E]  fp32 or NULL    route from these logits instead of
+ *                                       computing x w^T (+b)
+ *   logits_out   [T,E]  fp32 or NULL    receives the logits
+ *   scores_out   [T,E]  fp32 or NULL    receives the score function over all E
+ *                                       (softmax over E, or sigmoid)
+ *   probs        [T,E]  fp32            out: combine weights, 0 off the map
+ *   routing_map  [T,E]  uint8           out: 1 where token t is routed to e
+ *   tokens_per_expert [E] int32         out: routing_map summed over tokens
+ *   workspace    moe_route_workspace_size(desc) bytes of device memory
+ * Top-K order: larger key first, lower expert index on ties.  Keys: the fp32
+ * logits for softmax (softmax is increasing), sigmoid(logit) (+ expert_bias)
+ * for sigmoid, where sigmoid is evaluated by a fixed sequence of IEEE fp32
+ * operations so that its bits are reproducible.  Sigmoid probs are the
+ * chosen scores over (their sum + 1e-20).
+ */
+moe_status moe_route(const moe_route_desc* desc, const void* x, const float* w_router,
+                     const float* b_router, const float* expert_bias, const float* logits_in,
+                     float* logits_out, float* scores_out, float* probs, uint8_t* routing_map,
+                     int32_t* tokens_per_expert, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+/* ------------------------------------------------------------------------
+ * Dispatch preprocess: permute token rows into expert-major order.
+ * [MC] §2 and §9 (rows go from token-major to expert-major order before the
+ * experts); [DS] §8 step 4.
+ * ------------------------------------------------------------------------ */
+
+/* Bytes of device workspace moe_permute needs. */
+size_t moe_permute_workspace_size(int64_t T, int64_t E);
+
+/*
+ * moe_permute — rows sorted by (expert ascending, token ascending).
+ *   x              [T,h]        dtype   h must be a multiple of 8
+ *   routing_map    [T,E]        uint8   nonzero = routed (at most K per row)
+ *   probs          [T,E]        fp32
+ *   permuted_x     [max_rows,h] dtype   out: permuted_x[i] = x[sorted_token[i]]
+ *   permuted_probs [max_rows]   fp32    out: probs[sorted_token[i], expert of row i]
+ *   sorted_token   [max_rows]   int32   out: source token of row i
+ *   row_id_map     [T,K]        int32   out: row of token t's k-th routed expert
+ *                                       (ascending expert order), -1 if unused
+ *   expert_offsets [E+1]        int32   out: first row of each expert; [E] = N
+ * Rows at index >= N are left untouched.  Rows beyond max_rows and routed
+ * entries beyond K in a map row are not written (outside the contract).
+ */
+moe_status moe_permute(int64_t T, int64_t h, int64_t E, int64_t K, int32_t dtype, const void* x,
+                       const uint8_t* routing_map, const float* probs, int64_t max_rows,
+                       void* permuted_x, float* permuted_probs, int32_t* sorted_token,
+                       int32_t* row_id_map, int32_t* expert_offsets, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Experts: SwiGLU MLP of every local expert as one grouped GEMM per layer.
+ * [MC] §10 (all local experts' MLPs run as a grouped GEMM instead of a loop
+ * of small GEMMs); [MG] 计算效率优化 (grouped GEMM; dropless routing without a
+ * host-device synchronisation).  The expert MLP is SwiGLU without biases:
+ *   act = silu(x W_gate[e]^T) * (x W_up[e]^T),   y = act W_down[e]^T,
+ * silu(g) = g * sigmoid(g).  Rows [off_e, off_e + n_e) belong to expert e,
+ * where n_e = tokens_per_expert[e] (read on the device only) and off_e is
+ * its prefix sum.  Accumulation is fp32; act and y are stored in `dtype`
+ * (bf16 rounded to nearest-even).  Sizes for MOE_BF16: h and f multiples
+ * of 64.  Rows at index >= sum(n_e) of act/expert_out are left untouched;
+ * counts are clamped so that no row index reaches max_rows.
+ * ------------------------------------------------------------------------ */
+
+/*
+ *   permuted_x        [max_rows,h]  dtype
+ *   tokens_per_expert [E]           int32 (device)
+ *   w_gate, w_up      [E,f,h]       dtype
+ *   w_down            [E,h,f]       dtype
+ *   act               [max_rows,f]  dtype   out (intermediate activation)
+ *   expert_out        [max_rows,h]  dtype   out (unweighted expert outputs)
+ */
+moe_status moe_grouped_mlp(int64_t E, int64_t h, int64_t f, int64_t max_rows, int32_t dtype,
+                           const void* permuted_x, const int32_t* tokens_per_expert,
+                           const void* w_gate, const void* w_up, const void* w_down, void* act,
+                           void* expert_out, void* stream);
+
+/* The first half of moe_grouped_mlp: act = silu(x W_gate^T) * (x W_up^T). */
+moe_status moe_grouped_fc1_swiglu(int64_t E, int64_t h, int64_t f, int64_t max_rows,
+                                  int32_t dtype, const void* permuted_x,
+                                  const int32_t* tokens_per_expert, const void* w_gate,
+                                  const void* w_up, void* act, void* stream);
+
+/* The second half of moe_grouped_mlp: expert_out = act W_down^T. */
+moe_status moe_grouped_fc2(int64_t E, int64_t h, int64_t f, int64_t max_rows, int32_t dtype,
+                           const void* act, const int32_t* tokens_per_expert,
+                           const void* w_down, void* expert_out, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Combine: unpermute and weight.  [MC] §2 (combine takes the expert outputs
+ * and the router probs; the shared expert's output is added afterwards),
+ * §11; [DS] §8 step 8.
+ *   out[t] = sum_{k: row_id_map[t,k] >= 0} permuted_probs[r] * expert_out[r]
+ *            (+ shared_out[t]),   r = row_id_map[t,k],
+ * summed in fp32 in ascending k (= ascending expert) order and rounded once
+ * to `dtype`: the result is bitwise reproducible.
+ *   expert_out     [max_rows,h] dtype
+ *   permuted_probs [max_rows]   fp32
+ *   row_id_map     [T,K]        int32   entries outside [0, max_rows) are skipped
+ *   shared_out     [T,h]        dtype or NULL
+ *   out            [T,h]        dtype   out
+ * h must be a multiple of 8.
+ * ------------------------------------------------------------------------ */
+moe_status moe_combine(int64_t T, int64_t h, int64_t K, int32_t dtype, const void* expert_out,
+                       const float* permuted_probs, const int32_t* row_id_map, int64_t max_rows,
+                       const void* shared_out, void* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

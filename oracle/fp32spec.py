@@ -12,7 +12,7 @@ IEEE fp32 operations (every multiply, add and divide rounded to nearest
 even, no fused multiply-add), and the selection is then bit-identical.
 
 exp_spec(y), y <= 0:
-  * y < -87: result 0 (below the fp32 normal range of the sigmoid tail);
+  * y < -86: result 0 (keeps every nonzero result in the fp32 normal range);
   * n = rint(y * log2(e)), halves to even, log2(e) rounded to fp32;
   * Cody-Waite reduction r = (y - n*C1) - n*C2, where C1 is ln 2 cut to
     12 significant bits (so n*C1 is exact for |n| < 2^12) and C2 is the fp32
@@ -36,7 +36,7 @@ _LOG2E = F32(1.0 / math.log(2.0))
 _C1 = F32(math.floor(math.log(2.0) * 4096.0) / 4096.0)
 _C2 = F32(math.log(2.0) - float(_C1))
 _TAYLOR = [F32(1.0 / math.factorial(k)) for k in range(8)]
-_EXP_FLOOR = F32(-87.0)
+_EXP_FLOOR = F32(-86.0)
 
 
 def exp_spec(y: np.ndarray) -> np.ndarray:

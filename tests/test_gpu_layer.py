@@ -1,0 +1,156 @@
+"""GPU parity of the whole layer (route -> permute -> experts -> combine).
+
+Small layers are compared in full against oracle.moe_forward (routing from
+the GPU's fp32 logits, which are themselves checked); the five full-size
+layers are compared on sampled tokens (oracle.token_outputs) and sampled
+expert rows, in the launch configuration the benchmark times.
+"""
+import numpy as np
+import pytest
+import torch
+
+import combine_router_gating_amd as moe
+import datagen
+import oracle
+from gpu_helpers import (assert_close, expert_weights_from, f64, log, routing_ref,
+                         shared_weights_from)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _forward(cfg, inp):
+    return moe.moe_forward(inp, K=cfg.K, score=cfg.score, pre_softmax=cfg.pre_softmax,
+                           capacity_factor=cfg.capacity_factor, min_capacity=cfg.min_capacity,
+                           want_logits=True)
+
+
+SMALL = [
+    datagen.CONFIGS["tiny"],
+    datagen.MoEConfig("small-bf16", T=300, h=256, E=8, K=2, f=512, dtype="bf16"),
+    datagen.MoEConfig("small-cap", T=515, h=128, E=16, K=1, f=256, dtype="bf16",
+                      capacity_factor=1.25, gate_bias="zipf"),
+    datagen.MoEConfig("small-renorm", T=200, h=192, E=32, K=4, f=128, dtype="bf16",
+                      pre_softmax=False),
+    datagen.MoEConfig("small-sigmoid", T=257, h=256, E=64, K=8, f=128, dtype="bf16",
+                      score="sigmoid", expert_bias=True, shared_f=192),
+    datagen.MoEConfig("small-f32-shared", T=99, h=64, E=4, K=4, f=96, dtype="f32",
+                      score="sigmoid", expert_bias=True, shared_f=64, capacity_factor=0.5),
+    datagen.MoEConfig("one-expert", T=70, h=64, E=1, K=1, f=64, dtype="bf16"),
+]
+
+
+@pytest.mark.parametrize("cfg", SMALL, ids=lambda c: c.name)
+def test_layer_small_full_compare(cfg):
+    log(f"layer small: {cfg}")
+    inp = datagen.make_inputs(cfg, seed=1, device=DEV)
+    res = _forward(cfg, inp)
+    torch.cuda.synchronize()
+    logits = res["logits"].cpu().numpy()
+    ref_logits = oracle.router_logits(f64(inp["x"]), f64(inp["w_router"]),
+                                      f64(inp["b_router"]) if "b_router" in inp else None)
+    assert_close(logits, ref_logits, "f32", "logits")
+    eb = inp["expert_bias"].cpu().numpy() if "expert_bias" in inp else None
+    ref = oracle.moe_forward(f64(inp["x"]), None, None,
+                             (f64(inp["w_gate"]), f64(inp["w_up"]), f64(inp["w_down"])),
+                             K=cfg.K, dtype=cfg.dtype, score=cfg.score, pre_softmax=cfg.pre_softmax,
+                             expert_bias=eb, capacity_factor=cfg.capacity_factor,
+                             min_capacity=cfg.min_capacity, shared=shared_weights_from(inp),
+                             logits=logits)
+    np.testing.assert_array_equal(res["routing_map"].cpu().numpy(), ref["routing_map"])
+    np.testing.assert_array_equal(res["tokens_per_expert"].cpu().numpy(), ref["tokens_per_expert"])
+    np.testing.assert_array_equal(res["row_id_map"].cpu().numpy(), ref["row_id_map"])
+    N = int(ref["expert_offsets"][-1])
+    np.testing.assert_array_equal(res["sorted_token"][:N].cpu().numpy(), ref["sorted_token"])
+    assert_close(f64(res["act"][:N]), ref["act"], cfg.dtype, "act")
+    assert_close(f64(res["expert_out"][:N]), ref["expert_out"], cfg.dtype, "expert_out")
+    if cfg.shared_f:
+        assert_close(f64(res["shared_out"]), ref["shared_out"], cfg.dtype, "shared_out")
+    assert_close(f64(res["out"]), ref["out"], cfg.dtype, "out")
+    # tokens whose every slot was dropped carry only the shared output (or zero)
+    empty = ref["routing_map"].sum(1) == 0
+    if empty.any():
+        exp = f64(res["shared_out"])[empty] if cfg.shared_f else 0.0
+        np.testing.assert_array_equal(f64(res["out"])[empty], exp)
+
+
+def test_layer_shared_weights_reduce_to_dense_times_prob_sum():
+    """Spec invariant: all experts sharing weights, out = SwiGLU(x) * sum(p)."""
+    cfg = datagen.MoEConfig("shared-w", T=400, h=128, E=8, K=2, f=256, dtype="f32")
+    inp = datagen.make_inputs(cfg, seed=4, device=DEV)
+    for k in ("w_gate", "w_up", "w_down"):
+        inp[k] = inp[k][:1].expand(cfg.E, -1, -1).contiguous()
+    res = _forward(cfg, inp)
+    torch.cuda.synchronize()
+    wg, wu, wd = (f64(inp[k][0]) for k in ("w_gate", "w_up", "w_down"))
+    _, dense = oracle.swiglu_rows(f64(inp["x"]), wg, wu, wd, "f32")
+    psum = res["probs"].to(torch.float64).sum(1, keepdim=True).cpu().numpy()
+    assert_close(f64(res["out"]), dense * psum, "f32", "out vs dense*sum(p)")
+
+
+@pytest.mark.parametrize("name,n_tok", [("tiny", 256), ("switch", 24), ("mixtral", 12),
+                                        ("qwen3", 8), ("dsv3", 4)])
+def test_layer_full_size_sampled(name, n_tok):
+    cfg = datagen.CONFIGS[name]
+    log(f"layer full size: {cfg}")
+    inp = datagen.make_inputs(cfg, seed=0, device=DEV)
+    res = _forward(cfg, inp)
+    torch.cuda.synchronize()
+    logits = res["logits"].cpu().numpy()
+    eb = inp["expert_bias"].cpu().numpy() if "expert_bias" in inp else None
+    ref = routing_ref(cfg, logits, eb)
+    rmap = ref["routing_map"]
+    np.testing.assert_array_equal(res["routing_map"].cpu().numpy(), rmap)
+    np.testing.assert_array_equal(res["tokens_per_expert"].cpu().numpy(), ref["tokens_per_expert"])
+    rng = np.random.default_rng(0)
+    toks = list(rng.choice(cfg.T, size=min(n_tok, cfg.T), replace=False))
+    empty = np.nonzero(rmap.sum(1) == 0)[0]
+    if len(empty):
+        toks.append(int(empty[0]))  # a fully dropped token, if any
+    xs = f64(inp["x"])
+    exp = oracle.token_outputs(toks, xs, rmap, ref["probs"], expert_weights_from(inp), cfg.dtype,
+                               shared_weights_from(inp))
+    got = f64(res["out"])[toks]
+    assert_close(got, exp, cfg.dtype, f"out[{name}]")
+    # sampled rows of the grouped GEMM output: first, busiest and last expert
+    n = ref["tokens_per_expert"]
+    offs = np.concatenate([[0], np.cumsum(n)])
+    st = res["sorted_token"].cpu().numpy()
+    for e in sorted({int(np.argmax(n)), int(np.nonzero(n)[0][0]), int(np.nonzero(n)[0][-1])}):
+        rows = rng.choice(np.arange(offs[e], offs[e + 1]), size=min(6, int(n[e])), replace=False)
+        wg, wu, wd = expert_weights_from(inp)(e)
+        _, y = oracle.swiglu_rows(xs[st[rows]], wg, wu, wd, cfg.dtype)
+        assert_close(f64(res["expert_out"][torch.from_numpy(rows).to(DEV)]), y, cfg.dtype,
+                     f"expert_out[{name}, e={e}]")
+
+
+def test_layer_is_bitwise_deterministic():
+    cfg = datagen.CONFIGS["qwen3"].replace(T=2048)
+    inp = datagen.make_inputs(cfg, seed=2, device=DEV)
+    a = _forward(cfg, inp)["out"].clone()
+    b = _forward(cfg, inp)["out"]
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_layer_graph_capture_replays_match_eager():
+    """The whole forward needs no host sync and no allocation by the
+    library: it captures into a graph; replays on new inputs match eager."""
+    cfg = datagen.MoEConfig("graph", T=512, h=256, E=16, K=2, f=256, dtype="bf16",
+                            capacity_factor=1.0)
+    inp = datagen.make_inputs(cfg, seed=5, device=DEV)
+    _forward(cfg, inp)  # warm up
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        res = _forward(cfg, inp)
+    for seed in (6, 7, 8):
+        new = datagen.make_inputs(cfg, seed=seed, device=DEV, with_experts=False)
+        inp["x"].copy_(new["x"])
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        eager = _forward(cfg, inp)
+        torch.cuda.synchronize()
+        assert torch.equal(res["out"], eager["out"]), f"replay with seed {seed}"
+        assert torch.equal(res["routing_map"], eager["routing_map"])
