@@ -1,0 +1,257 @@
+"""Benchmark of the MoE layer forward on one MI355X.
+
+One step = one full layer forward (route -> permute -> FC1+SwiGLU -> FC2
+(-> shared expert) -> combine) over one synthetic batch already resident in
+HBM.  Prints ONE JSON line.  The default workload is the Switch-style layer
+(T=8192, h=2048, E=64, top-1, capacity factor 1.25, bf16 with an fp32
+router); --config picks another layer shape.
+
+Per-stage durations come from HIP events recorded on the stream the kernels
+run on, over every timed step; the roofline object uses the dominant
+single-kernel stage.  `traffic` (HBM bytes per launch from rocprofv3
+FETCH_SIZE/WRITE_SIZE counters) is read from profiles/ and reported only
+while the kernel source is unchanged since the counters were taken.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer fwd tokens/sec + grouped-GEMM TFLOPS (% of MI355X bf16 MFMA peak)"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+FP32_PEAK_TFLOPS = 157.3        # MI355X fp32 (used for fp32 layers)
+KERNEL_SOURCES = {  # stage -> source file that holds its kernel
+    "route": "route.hip", "permute": "permute.hip", "fc1": "gmm.hip", "fc2": "gmm.hip",
+    "shared": "gmm.hip", "combine": "combine.hip",
+}
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--config", default="switch")
+    p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--cpu-sample-tokens", type=int, default=None,
+                   help="tokens the oracle runs for the cpu_baseline leg (default: per layer)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--calib-copy-mib", type=int, default=0,
+                   help="run one plain device copy of this size first (counter calibration)")
+    return p.parse_args()
+
+
+def source_hash(stage: str) -> str:
+    path = os.path.join(ROOT, "combine_router_gating_amd", "csrc", KERNEL_SOURCES[stage])
+    h = hashlib.sha256()
+    for f in (path, os.path.join(ROOT, "combine_router_gating_amd", "csrc", "moe_internal.h"),
+              os.path.join(ROOT, "combine_router_gating_amd", "build.py")):
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(stage: str, workload: str):
+    """HBM bytes per launch from a committed counter summary, if current."""
+    path = os.path.join(ROOT, "profiles", f"pmc_{stage}_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if line.startswith("- ") and ":" in line:
+            k, v = line[2:].split(":", 1)
+            kv[k.strip()] = v.strip().strip("`")
+    if kv.get("source_sha256") != source_hash(stage):
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def stage_work(cfg, n, T, fs):
+    """Algorithmic bytes and flops of each stage (kept rows only, no padding,
+    each tensor moved once)."""
+    b = 4 if cfg.dtype == "f32" else 2
+    h, f, E, K = cfg.h, cfg.f, cfg.E, cfg.K
+    N = int(sum(n))
+    active = int(sum(1 for v in n if v > 0))
+    w = {
+        "route": (T * h * b + E * h * 4 + T * E * (4 + 4 + 1) + E * 4, 2.0 * T * h * E),
+        "permute": (T * h * b + N * h * b + T * E * (1 + 4) + N * 8 + T * K * 4 + E * 4, 0.0),
+        "fc1": (active * 2 * h * f * b + N * h * b + N * f * b, 4.0 * N * h * f),
+        "fc2": (active * h * f * b + N * f * b + N * h * b, 2.0 * N * h * f),
+        "combine": (N * h * b + T * K * 4 + N * 4 + T * h * b + (T * h * b if fs else 0), 0.0),
+    }
+    if fs:
+        w["shared"] = (3 * h * fs * b + 2 * T * h * b + 2 * T * fs * b, 6.0 * T * h * fs)
+    return w
+
+
+def cpu_baseline(cfg, inp, sample_tokens):
+    """The oracle, as it stands, on the first `sample_tokens` tokens of the
+    batch run as a batch of their own (same weights and routing options)."""
+    import numpy as np
+
+    import datagen
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    S = min(sample_tokens, cfg.T)
+    f64 = datagen.to_f64
+    x = f64(inp["x"][:S])
+    wr = f64(inp["w_router"])
+    br = f64(inp["b_router"]) if "b_router" in inp else None
+    eb = inp["expert_bias"].cpu().numpy() if "expert_bias" in inp else None
+    # host copies of the weights in their stored values (fp32 holds bf16 exactly)
+    host = {k: inp[k].to("cpu", torch_float32()).numpy() for k in ("w_gate", "w_up", "w_down")}
+    shared = None
+    if "shared_gate" in inp:
+        shared = tuple(f64(inp[k]) for k in ("shared_gate", "shared_up", "shared_down"))
+
+    def weights(e):
+        return (host["w_gate"][e].astype(np.float64), host["w_up"][e].astype(np.float64),
+                host["w_down"][e].astype(np.float64))
+
+    t0 = time.perf_counter()
+    oracle.moe_forward(x, wr, br, weights, K=cfg.K, dtype=cfg.dtype, score=cfg.score,
+                       pre_softmax=cfg.pre_softmax, expert_bias=eb,
+                       capacity_factor=cfg.capacity_factor, min_capacity=cfg.min_capacity,
+                       shared=shared)
+    dt = time.perf_counter() - t0
+    return {"value": S / dt, "unit": "tokens/s", "cores": int(blas_threads), "kind": "oracle",
+            "sample": f"first {S} of {cfg.T} tokens run as one batch (same weights and routing "
+                      f"options; capacity recomputed for that batch), float64 NumPy, "
+                      f"{dt:.1f} s"}
+
+
+def torch_float32():
+    import torch
+    return torch.float32
+
+
+DEFAULT_CPU_SAMPLE = {"tiny": 256, "switch": 8192, "mixtral": 256, "qwen3": 512, "dsv3": 128}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(this layer runs on one GPU's share of experts)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import datagen
+    from combine_router_gating_amd.layer import MoELayerForward
+
+    cfg = datagen.CONFIGS[args.config]
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib * (1 << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device=dev)
+        bb = torch.empty_like(a)
+        bb.copy_(a)
+        torch.cuda.synchronize()
+        del a, bb
+    inp = datagen.make_inputs(cfg, seed=args.seed, device=dev)
+    layer = MoELayerForward(inp, K=cfg.K, score=cfg.score, pre_softmax=cfg.pre_softmax,
+                            capacity_factor=cfg.capacity_factor, min_capacity=cfg.min_capacity)
+    for _ in range(args.warmup):
+        layer.forward()
+    torch.cuda.synchronize()
+
+    # timed region: K steps, events at every stage boundary
+    stages = [s for s in layer.STAGES if s != "shared" or layer.shared]
+    events = []
+
+    def mark(name):
+        ev = torch.cuda.Event(enable_timing=True)
+        ev.record()
+        events[-1].append((name, ev))
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        events.append([])
+        layer.forward(mark)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    stage_ms = {s: 0.0 for s in stages}
+    for evs in events:
+        for (name, a), (_, b) in zip(evs[:-1], evs[1:]):
+            stage_ms[name] += a.elapsed_time(b)
+    stage_ms = {s: v / args.steps for s, v in stage_ms.items()}
+
+    n = layer.tokens_per_expert.cpu().tolist()
+    N = int(sum(n))
+    work = stage_work(cfg, n, cfg.T, layer.fs if layer.shared else 0)
+    gemm_stages = [s for s in ("fc1", "fc2", "shared") if s in stage_ms]
+    gemm_flops = sum(work[s][1] for s in gemm_stages)
+    gemm_ms = sum(stage_ms[s] for s in gemm_stages)
+    gemm_tflops = gemm_flops / (gemm_ms * 1e-3) / 1e12
+    peak_tf = MFMA_BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else FP32_PEAK_TFLOPS
+
+    single_kernel = ("fc1", "fc2", "shared", "combine")
+    dom = max((s for s in stage_ms if s in single_kernel), key=lambda s: stage_ms[s])
+    nbytes, flops = work[dom]
+    ridge = peak_tf * 1e12 / (HBM_PEAK_GBS * 1e9)
+    sec = stage_ms[dom] * 1e-3
+    if flops and flops / nbytes >= ridge:
+        roof = {"bound": "mfma", "achieved": flops / sec / 1e12, "peak": peak_tf,
+                "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": nbytes / sec / 1e9, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = read_traffic(dom, cfg.name)
+    roof["kernel"] = dom
+    roof["algorithmic_bytes"] = nbytes
+    roof["algorithmic_flops"] = flops
+    roof["avg_launch_ms"] = stage_ms[dom]
+
+    stage_report = {}
+    for s in stages:
+        nb, fl = work[s]
+        sec_s = stage_ms[s] * 1e-3
+        stage_report[s] = {"ms": round(stage_ms[s], 4), "GB/s": round(nb / sec_s / 1e9, 1),
+                           "TFLOP/s": round(fl / sec_s / 1e12, 1) if fl else 0.0}
+
+    value = cfg.T / (ms_per_step * 1e-3)
+    rec = {
+        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype,
+        "data": "synthetic (seeded; random-init weights)",
+        "config": {"workload": f"{cfg.name}: T={cfg.T} h={cfg.h} E={cfg.E} K={cfg.K} f={cfg.f}"
+                               f" {cfg.score}{'' if cfg.pre_softmax else '-renorm'}"
+                               f" cap={cfg.capacity_factor} shared_f={cfg.shared_f}",
+                   "tokens": cfg.T, "routed_rows": N, "dropped": cfg.T * cfg.K - N,
+                   "parallelism": "single GPU, EP=1"},
+        "gemm_tflops": gemm_tflops,
+        "gemm_frac_of_mfma_peak": gemm_tflops / peak_tf,
+        "stages": stage_report,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        S = args.cpu_sample_tokens or DEFAULT_CPU_SAMPLE.get(cfg.name, 256)
+        rec["cpu_baseline"] = cpu_baseline(cfg, inp, S)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,126 @@
+"""A preallocated MoE layer forward: buffers are allocated once (torch), the
+C arguments are built once, and each forward is a fixed sequence of libmoe
+calls on the current stream — no allocation and no host sync per call, so
+it can also be captured into a graph."""
+from __future__ import annotations
+
+import ctypes
+from typing import Callable, Dict, Optional
+
+import torch
+
+from . import _lib
+from ._lib import check
+from .moe import _dtype_code, _need, route_desc
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+class MoELayerForward:
+    """route -> permute -> FC1+SwiGLU -> FC2 (-> shared expert) -> combine."""
+
+    STAGES = ("route", "permute", "fc1", "fc2", "shared", "combine")
+
+    def __init__(self, inp: Dict[str, torch.Tensor], *, K: int, score: str = "softmax",
+                 pre_softmax: bool = True, capacity_factor: float = 0.0, min_capacity: int = 0):
+        self.lib = _lib.load()
+        self.inp = inp
+        x = _need(inp["x"], "x")
+        self.T, self.h = x.shape
+        self.E = inp["w_router"].shape[0]
+        self.f = inp["w_gate"].shape[1]
+        self.K = K
+        self.dt = _dtype_code(x, "x")
+        dev = x.device
+        self.desc = route_desc(self.T, self.h, self.E, K, x.dtype, score, pre_softmax,
+                               capacity_factor, min_capacity)
+        self.max_rows = int(self.lib.moe_max_rows(ctypes.byref(self.desc)))
+        T, h, E, f, R = self.T, self.h, self.E, self.f, self.max_rows
+        e = torch.empty
+        self.probs = e((T, E), dtype=torch.float32, device=dev)
+        self.routing_map = e((T, E), dtype=torch.uint8, device=dev)
+        self.tokens_per_expert = e((E,), dtype=torch.int32, device=dev)
+        self.logits = e((T, E), dtype=torch.float32, device=dev)
+        self.route_ws_bytes = int(self.lib.moe_route_workspace_size(ctypes.byref(self.desc)))
+        self.route_ws = e((max(self.route_ws_bytes, 1),), dtype=torch.uint8, device=dev)
+        self.permuted_x = e((R, h), dtype=x.dtype, device=dev)
+        self.permuted_probs = e((R,), dtype=torch.float32, device=dev)
+        self.sorted_token = e((R,), dtype=torch.int32, device=dev)
+        self.row_id_map = e((T, K), dtype=torch.int32, device=dev)
+        self.expert_offsets = e((E + 1,), dtype=torch.int32, device=dev)
+        self.perm_ws_bytes = int(self.lib.moe_permute_workspace_size(T, E))
+        self.perm_ws = e((max(self.perm_ws_bytes, 1),), dtype=torch.uint8, device=dev)
+        self.act = e((R, f), dtype=x.dtype, device=dev)
+        self.expert_out = e((R, h), dtype=x.dtype, device=dev)
+        self.out = e((T, h), dtype=x.dtype, device=dev)
+        self.shared = "shared_gate" in inp
+        if self.shared:
+            self.fs = inp["shared_gate"].shape[0]
+            self.shared_count = torch.full((1,), T, dtype=torch.int32, device=dev)
+            self.shared_act = e((T, self.fs), dtype=x.dtype, device=dev)
+            self.shared_out = e((T, h), dtype=x.dtype, device=dev)
+        else:
+            self.shared_out = None
+
+    def _stream(self):
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def route(self):
+        i = self.inp
+        check("moe_route", self.lib.moe_route(
+            ctypes.byref(self.desc), _p(i["x"]), _p(i["w_router"]), _p(i.get("b_router")),
+            _p(i.get("expert_bias")), None, _p(self.logits), None, _p(self.probs),
+            _p(self.routing_map), _p(self.tokens_per_expert), _p(self.route_ws),
+            self.route_ws_bytes, self._stream()))
+
+    def permute(self):
+        check("moe_permute", self.lib.moe_permute(
+            self.T, self.h, self.E, self.K, self.dt, _p(self.inp["x"]), _p(self.routing_map),
+            _p(self.probs), self.max_rows, _p(self.permuted_x), _p(self.permuted_probs),
+            _p(self.sorted_token), _p(self.row_id_map), _p(self.expert_offsets), _p(self.perm_ws),
+            self.perm_ws_bytes, self._stream()))
+
+    def fc1(self):
+        i = self.inp
+        check("moe_grouped_fc1_swiglu", self.lib.moe_grouped_fc1_swiglu(
+            self.E, self.h, self.f, self.max_rows, self.dt, _p(self.permuted_x),
+            _p(self.tokens_per_expert), _p(i["w_gate"]), _p(i["w_up"]), _p(self.act),
+            self._stream()))
+
+    def fc2(self):
+        check("moe_grouped_fc2", self.lib.moe_grouped_fc2(
+            self.E, self.h, self.f, self.max_rows, self.dt, _p(self.act),
+            _p(self.tokens_per_expert), _p(self.inp["w_down"]), _p(self.expert_out),
+            self._stream()))
+
+    def shared_expert(self):
+        if not self.shared:
+            return
+        i = self.inp
+        check("moe_grouped_fc1_swiglu", self.lib.moe_grouped_fc1_swiglu(
+            1, self.h, self.fs, self.T, self.dt, _p(i["x"]), _p(self.shared_count),
+            _p(i["shared_gate"]), _p(i["shared_up"]), _p(self.shared_act), self._stream()))
+        check("moe_grouped_fc2", self.lib.moe_grouped_fc2(
+            1, self.h, self.fs, self.T, self.dt, _p(self.shared_act), _p(self.shared_count),
+            _p(i["shared_down"]), _p(self.shared_out), self._stream()))
+
+    def combine(self):
+        check("moe_combine", self.lib.moe_combine(
+            self.T, self.h, self.K, self.dt, _p(self.expert_out), _p(self.permuted_probs),
+            _p(self.row_id_map), self.max_rows, _p(self.shared_out), _p(self.out),
+            self._stream()))
+
+    def forward(self, mark: Optional[Callable[[str], None]] = None) -> torch.Tensor:
+        """One layer forward.  `mark(name)` is called before each stage and
+        once more with "end" (used to record timing events)."""
+        for name in self.STAGES:
+            if name == "shared" and not self.shared:
+                continue
+            if mark:
+                mark(name)
+            getattr(self, "shared_expert" if name == "shared" else name)()
+        if mark:
+            mark("end")
+        return self.out
