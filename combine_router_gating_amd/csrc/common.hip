@@ -28,7 +28,8 @@ moe_status check_launch(const char* what) {
 
 size_t count_ws_bytes(int64_t T, int64_t E) {
   const int64_t nblk = ceil_div(T, kCountBlock);
-  return 2 * align_up(static_cast<size_t>(nblk * E) * sizeof(int32_t), 256);
+  return 2 * align_up(static_cast<size_t>(nblk * E) * sizeof(int32_t), 256) +
+         align_up(static_cast<size_t>(E) * sizeof(int32_t), 256);
 }
 
 // One workgroup per block of kCountBlock tokens: count the routed entries of
@@ -51,41 +52,29 @@ __global__ void __launch_bounds__(256) block_hist_kernel(const uint8_t* __restri
   for (int e = threadIdx.x; e < E; e += blockDim.x) hist[static_cast<int64_t>(b) * E + e] = cnt[e];
 }
 
-// One workgroup; thread e walks the blocks of expert e (loads are coalesced
-// across threads), then the kept totals are scanned over experts in LDS.
-__global__ void __launch_bounds__(1024) count_scan_kernel(const int32_t* __restrict__ hist,
-                                                          int nblk, int E, int64_t cap,
-                                                          int32_t* __restrict__ blkoff,
-                                                          int32_t* __restrict__ tokens_per_expert,
-                                                          int32_t* __restrict__ expert_offsets) {
-  __shared__ int part[1024];
-  const int e = threadIdx.x;
-  int kept = 0;
-  if (e < E) {
-    int run = 0;
-#pragma unroll 8
-    for (int b = 0; b < nblk; ++b) {
-      const int64_t i = static_cast<int64_t>(b) * E + e;
-      const int c = hist[i];
-      blkoff[i] = run;
-      run += c;
-    }
-    kept = (cap >= 0 && run > cap) ? static_cast<int>(cap) : run;
-    if (tokens_per_expert) tokens_per_expert[e] = kept;
+// One workgroup per expert: each thread sums a contiguous run of blocks,
+// the runs are scanned across the workgroup, then each thread writes the
+// exclusive prefixes of its run.
+__global__ void __launch_bounds__(256) count_scan_kernel(const int32_t* __restrict__ hist,
+                                                         int nblk, int E, int64_t cap,
+                                                         int32_t* __restrict__ blkoff,
+                                                         int32_t* __restrict__ kept) {
+  __shared__ int64_t scratch[4];
+  const int e = blockIdx.x;
+  const int per = (nblk + 255) / 256;
+  const int b0 = threadIdx.x * per;
+  const int b1 = min(nblk, b0 + per);
+  int64_t sum = 0;
+  for (int b = b0; b < b1; ++b) sum += hist[static_cast<int64_t>(b) * E + e];
+  int64_t total;
+  int64_t run = block_exclusive_scan256(sum, scratch, &total);
+  for (int b = b0; b < b1; ++b) {
+    const int64_t i = static_cast<int64_t>(b) * E + e;
+    const int c = hist[i];
+    blkoff[i] = static_cast<int32_t>(run);
+    run += c;
   }
-  part[e] = kept;
-  __syncthreads();
-  // Hillis-Steele inclusive scan over blockDim entries
-  for (int off = 1; off < static_cast<int>(blockDim.x); off <<= 1) {
-    int v = (e >= off) ? part[e - off] : 0;
-    __syncthreads();
-    part[e] += v;
-    __syncthreads();
-  }
-  if (expert_offsets && e < E) {
-    expert_offsets[e] = part[e] - kept;
-    if (e == E - 1) expert_offsets[E] = part[e];
-  }
+  if (threadIdx.x == 0) kept[e] = static_cast<int32_t>((cap >= 0 && total > cap) ? cap : total);
 }
 
 __global__ void fill_i32_kernel(int32_t* __restrict__ p, int64_t n, int32_t v) {
@@ -106,11 +95,9 @@ void launch_block_hist(const uint8_t* map, int64_t T, int64_t E, int32_t* hist, 
 }
 
 void launch_count_scan(const int32_t* hist, int64_t nblk, int64_t E, int64_t cap, int32_t* blkoff,
-                       int32_t* tokens_per_expert, int32_t* expert_offsets, hipStream_t s) {
-  const int threads = static_cast<int>(ceil_div(E, 64) * 64);
-  hipLaunchKernelGGL(count_scan_kernel, dim3(1), dim3(threads), 0, s, hist,
-                     static_cast<int>(nblk), static_cast<int>(E), cap, blkoff, tokens_per_expert,
-                     expert_offsets);
+                       int32_t* kept, hipStream_t s) {
+  hipLaunchKernelGGL(count_scan_kernel, dim3(static_cast<unsigned>(E)), dim3(256), 0, s, hist,
+                     static_cast<int>(nblk), static_cast<int>(E), cap, blkoff, kept);
 }
 
 }  // namespace moe

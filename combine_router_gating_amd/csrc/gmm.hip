@@ -50,30 +50,6 @@ struct Tile {
   int n0;      // first output column
 };
 
-// Exclusive scan over the 256 threads' values; returns the exclusive prefix,
-// *total gets the sum.  Uses `scratch` (>= 5 entries) in LDS.
-__device__ int64_t block_exclusive_scan(int64_t v, int64_t* scratch, int64_t* total) {
-  const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
-  int64_t incl = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int64_t o = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += o;
-  }
-  if (lane == 63) scratch[wave] = incl;
-  __syncthreads();
-  int64_t before = 0, all = 0;
-#pragma unroll
-  for (int w = 0; w < kThreads / 64; ++w) {
-    const int64_t s = scratch[w];
-    if (w < wave) before += s;
-    all += s;
-  }
-  __syncthreads();
-  *total = all;
-  return before + incl - v;
-}
-
 // Decode this workgroup's tile.  s_toff/s_roff/s_n: LDS arrays of E+1 / E+1 / E.
 template <int BM>
 __device__ bool decode_tile(const int32_t* __restrict__ counts, int E, int64_t max_rows, int NT,
@@ -91,7 +67,7 @@ __device__ bool decode_tile(const int32_t* __restrict__ counts, int E, int64_t m
     sum += v;
   }
   int64_t total_rows;
-  int64_t pre = block_exclusive_scan(sum, scratch, &total_rows);
+  int64_t pre = block_exclusive_scan256(sum, scratch, &total_rows);
   int tl[PER];
   int tsum = 0;
 #pragma unroll
@@ -109,7 +85,7 @@ __device__ bool decode_tile(const int32_t* __restrict__ counts, int E, int64_t m
     pre += c[j];
   }
   int64_t total_tiles;
-  int tpre = static_cast<int>(block_exclusive_scan(tsum, scratch, &total_tiles));
+  int tpre = static_cast<int>(block_exclusive_scan256(tsum, scratch, &total_tiles));
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
     const int e = tid * PER + j;

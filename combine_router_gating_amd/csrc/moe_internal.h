@@ -29,14 +29,14 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // ------------------------------------------- per-block expert counts and their scan
 // hist[b*E + e]   = number of tokens of block b (kCountBlock tokens) routed to e
 // blkoff[b*E + e] = number of tokens routed to e in blocks before b
-size_t count_ws_bytes(int64_t T, int64_t E);  // hist + blkoff
+size_t count_ws_bytes(int64_t T, int64_t E);  // hist + blkoff + kept[E]
 // Fill n int32 with v by a kernel (graph-capture friendly, no memset node).
 void launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);
 void launch_block_hist(const uint8_t* map, int64_t T, int64_t E, int32_t* hist, hipStream_t s);
-// per expert: blkoff (exclusive over blocks), kept = min(total, cap) (cap < 0: total),
-// tokens_per_expert = kept (if non-null), expert_offsets = exclusive scan of kept (if non-null)
+// One workgroup per expert: blkoff = exclusive prefix over blocks,
+// kept[e] = min(total, cap) (cap < 0: total).
 void launch_count_scan(const int32_t* hist, int64_t nblk, int64_t E, int64_t cap, int32_t* blkoff,
-                       int32_t* tokens_per_expert, int32_t* expert_offsets, hipStream_t s);
+                       int32_t* kept, hipStream_t s);
 
 // ---------------------------------------------------------------- device helpers
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
@@ -49,6 +49,32 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
   if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
   u += 0x7fffu + ((u >> 16) & 1u);
   return static_cast<uint16_t>(u >> 16);
+}
+
+// Exclusive scan over a 256-thread workgroup (4 waves).  Returns this
+// thread's exclusive prefix; *total receives the sum.  `scratch` is >= 4
+// LDS entries.  Every thread of the workgroup must call it.
+__device__ __forceinline__ int64_t block_exclusive_scan256(int64_t v, int64_t* scratch,
+                                                           int64_t* total) {
+  const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
+  int64_t incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int64_t o = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += o;
+  }
+  if (lane == 63) scratch[wave] = incl;
+  __syncthreads();
+  int64_t before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const int64_t s = scratch[w];
+    if (w < wave) before += s;
+    all += s;
+  }
+  __syncthreads();
+  *total = all;
+  return before + incl - v;
 }
 
 __device__ __forceinline__ float wave_sum(float v) {

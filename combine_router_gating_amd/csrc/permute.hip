@@ -7,9 +7,11 @@
 // (expert ascending, token ascending), which makes the order unique.
 //
 // Row of an entry (t, e): expert_offsets[e] + (entries of e in earlier token
-// blocks) + (entries of e earlier in t's block).  The first two terms come
-// from per-block counts and their scan (common.hip); the scatter kernel
-// counts the third from the block's map tile in LDS.
+// blocks) + (entries of e earlier in t's block).  The per-block counts and
+// their per-expert scan (common.hip) give the second term and each expert's
+// total; every scatter workgroup scans the totals in LDS for the first term
+// (workgroup 0 also stores expert_offsets) and counts the third term from
+// the block's map tile in LDS.
 #include "moe_internal.h"
 
 namespace moe {
@@ -23,17 +25,45 @@ namespace {
 __global__ void __launch_bounds__(256) permute_scatter_kernel(
     const uint8_t* __restrict__ map, const float* __restrict__ probs, const uint4* __restrict__ x,
     int64_t T, int E, int K, int chunks, const int32_t* __restrict__ blkoff,
-    const int32_t* __restrict__ expert_offsets, int64_t max_rows, uint4* __restrict__ px,
-    float* __restrict__ pprobs, int32_t* __restrict__ sorted_token, int32_t* __restrict__ row_id_map) {
+    const int32_t* __restrict__ totals, int32_t* __restrict__ expert_offsets, int64_t max_rows,
+    uint4* __restrict__ px, float* __restrict__ pprobs, int32_t* __restrict__ sorted_token,
+    int32_t* __restrict__ row_id_map) {
   __shared__ uint8_t tile[kCountBlock][kMaxExperts];
   __shared__ int rows[kCountBlock][kMaxTopK];
   __shared__ int exps[kCountBlock][kMaxTopK];
   __shared__ int cnt[kCountBlock];
+  __shared__ int s_off[kMaxExperts + 1];
+  __shared__ int64_t scratch[4];
   const int b = blockIdx.x;
   const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
   const int64_t t0 = static_cast<int64_t>(b) * kCountBlock;
   const int nt = static_cast<int>(min(static_cast<int64_t>(kCountBlock), T - t0));
   for (int i = threadIdx.x; i < nt * E; i += blockDim.x) tile[i / E][i % E] = map[t0 * E + i] != 0;
+  {  // expert offsets: exclusive scan of the totals, 4 experts per thread
+    constexpr int PER = kMaxExperts / 256;
+    int64_t v[PER], sum = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int e = threadIdx.x * PER + j;
+      v[j] = e < E ? totals[e] : 0;
+      sum += v[j];
+    }
+    int64_t all;
+    int64_t pre = block_exclusive_scan256(sum, scratch, &all);
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int e = threadIdx.x * PER + j;
+      if (e < E) {
+        s_off[e] = static_cast<int>(pre);
+        if (b == 0) expert_offsets[e] = static_cast<int>(pre);
+      }
+      pre += v[j];
+    }
+    if (threadIdx.x == 0) {
+      s_off[E] = static_cast<int>(all);
+      if (b == 0) expert_offsets[E] = static_cast<int>(all);
+    }
+  }
   __syncthreads();
 
   for (int tl = wave; tl < nt; tl += 4) {
@@ -47,7 +77,7 @@ __global__ void __launch_bounds__(256) permute_scatter_kernel(
         for (int u = 0; u < tl; ++u) prior += tile[u][e];
         const int k = base_k + __popcll(mask & ((uint64_t(1) << lane) - 1));
         if (k < K) {
-          rows[tl][k] = expert_offsets[e] + blkoff[static_cast<int64_t>(b) * E + e] + prior;
+          rows[tl][k] = s_off[e] + blkoff[static_cast<int64_t>(b) * E + e] + prior;
           exps[tl][k] = e;
         }
       }
@@ -122,13 +152,14 @@ extern "C" moe_status moe_permute(int64_t T, int64_t h, int64_t E, int64_t K, in
   const int64_t nblk = ceil_div(T, kCountBlock);
   int32_t* hist = static_cast<int32_t*>(workspace);
   int32_t* blkoff = hist + align_up(static_cast<size_t>(nblk * E) * sizeof(int32_t), 256) / 4;
+  int32_t* totals = blkoff + align_up(static_cast<size_t>(nblk * E) * sizeof(int32_t), 256) / 4;
   launch_block_hist(routing_map, T, E, hist, s);
-  launch_count_scan(hist, nblk, E, -1, blkoff, nullptr, expert_offsets, s);
+  launch_count_scan(hist, nblk, E, -1, blkoff, totals, s);
   const int esize = dtype == MOE_BF16 ? 2 : 4;
   const int chunks = static_cast<int>(h * esize / 16);
   hipLaunchKernelGGL(permute_scatter_kernel, dim3(static_cast<unsigned>(nblk)), dim3(256), 0, s,
                      routing_map, probs, static_cast<const uint4*>(x), T, static_cast<int>(E),
-                     static_cast<int>(K), chunks, blkoff, expert_offsets, max_rows,
+                     static_cast<int>(K), chunks, blkoff, totals, expert_offsets, max_rows,
                      static_cast<uint4*>(permuted_x), permuted_probs, sorted_token, row_id_map);
   return check_launch("moe_permute");
 }

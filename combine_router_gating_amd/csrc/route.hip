@@ -9,11 +9,16 @@
 // leave both the map and the probs.
 //
 // Kernels, in launch order:
-//   router_logits_kernel   logits = x w^T (+ b), fp32 FMA, LDS-tiled
-//   router_topk_kernel     one wave per token: scores, K rounds of a wave-wide
+//   router_logits_mfma     bf16 x: x w^T on bf16 MFMA with the fp32 weight split
+//                          exactly into three bf16 parts (fp32-accurate), split
+//                          over h into partial sums (more workgroups)
+//   router_logits_simt     fp32 x (or h not a multiple of 16): fp32 FMA, LDS-tiled
+//   router_topk_kernel     one wave per token: logits = partials summed in a
+//                          fixed order (+ b), scores, K rounds of a wave-wide
 //                          argmax, probs, map, per-block expert counts
 //   count_scan_kernel      (capacity only) per-expert prefix over blocks
 //   router_drop_kernel     (capacity only) clear entries ranked >= capacity
+#include <algorithm>
 #include <cmath>
 
 #include "moe_internal.h"
@@ -35,11 +40,10 @@ template <>
 __device__ __forceinline__ float load_x<uint16_t>(const uint16_t* p) { return bf16_bits_to_f32(*p); }
 
 template <typename XT>
-__global__ void __launch_bounds__(256) router_logits_kernel(const XT* __restrict__ x,
-                                                            const float* __restrict__ w,
-                                                            const float* __restrict__ bias,
-                                                            float* __restrict__ logits, int64_t T,
-                                                            int h, int E) {
+__global__ void __launch_bounds__(256) router_logits_simt(const XT* __restrict__ x,
+                                                          const float* __restrict__ w,
+                                                          float* __restrict__ logits, int64_t T,
+                                                          int h, int E) {
   __shared__ float xs[LK][LT + 4];
   __shared__ float ws[LK][LE + 4];
   const int tid = threadIdx.x;
@@ -79,10 +83,138 @@ __global__ void __launch_bounds__(256) router_logits_kernel(const XT* __restrict
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int e = e0 + tx * 4 + j;
-      if (e < E) logits[t * E + e] = acc[i][j] + (bias ? bias[e] : 0.f);
+      if (e < E) logits[t * E + e] = acc[i][j];
     }
   }
 }
+
+// ------------------------------------------------ gating linear on MFMA
+// bf16 x is exact in bf16; the fp32 weight w is split exactly into
+// w = hi + mid + lo, three bf16 values: hi keeps w's top 16 bits, the
+// subtraction w - hi is exact (same sign and exponent), mid keeps the top 16
+// bits of that remainder, and the last remainder has at most 8 significant
+// bits, so lo holds it exactly.  Each product x*part is exact in fp32 and the
+// MFMA accumulates in fp32: the logits have fp32 accuracy at bf16 MFMA rate.
+//
+// A wave owns 64 tokens x 64 experts (2x2 blocks of v_mfma_f32_32x32x16_bf16,
+// three MFMAs per block per 16-wide k step); the 4 waves of a workgroup tile
+// WT x WE such blocks.  Operands come straight from global memory (each
+// lane's 8 consecutive k values are contiguous); blockIdx.y selects a slice
+// of h whose partial sums go to their own [T, E] plane.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void split3(const float4 a, const float4 b, u32x4_t& hi, u32x4_t& mi,
+                                       u32x4_t& lo) {
+  const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  uint32_t h16[8], m16[8], l16[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const uint32_t u = __float_as_uint(v[q]);
+    const uint32_t hb = u & 0xffff0000u;
+    const float r1 = v[q] - __uint_as_float(hb);
+    const uint32_t u1 = __float_as_uint(r1);
+    const uint32_t mb = u1 & 0xffff0000u;
+    const float r2 = r1 - __uint_as_float(mb);
+    h16[q] = hb >> 16;
+    m16[q] = mb >> 16;
+    l16[q] = __float_as_uint(r2) >> 16;
+  }
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    hi[p] = h16[2 * p] | (h16[2 * p + 1] << 16);
+    mi[p] = m16[2 * p] | (m16[2 * p + 1] << 16);
+    lo[p] = l16[2 * p] | (l16[2 * p + 1] << 16);
+  }
+}
+
+template <int WT, int WE>
+__global__ void __launch_bounds__(256) router_logits_mfma(const uint16_t* __restrict__ x,
+                                                          const float* __restrict__ w,
+                                                          float* __restrict__ part, int64_t T,
+                                                          int h, int E, int kchunk) {
+  static_assert(WT * WE == 4, "4 waves");
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wt = wave / WE, we = wave % WE;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * (64 * WT) + wt * 64;
+  const int e0 = blockIdx.z * (64 * WE) + we * 64;
+  const int kb = blockIdx.y * kchunk;
+  const int ke = min(h, kb + kchunk);
+  const int l32 = lane & 31, koff = (lane >> 5) * 8;
+  const uint16_t* xr0 = x + min(t0 + l32, T - 1) * h + koff;
+  const uint16_t* xr1 = x + min(t0 + 32 + l32, T - 1) * h + koff;
+  const float* wr0 = w + static_cast<int64_t>(min(e0 + l32, E - 1)) * h + koff;
+  const float* wr1 = w + static_cast<int64_t>(min(e0 + 32 + l32, E - 1)) * h + koff;
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+  for (int k = kb; k < ke; k += 16) {
+    const bf16x8_t xb0 = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(xr0 + k));
+    const bf16x8_t xb1 = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(xr1 + k));
+    u32x4_t hi[2], mi[2], lo[2];
+    split3(*reinterpret_cast<const float4*>(wr0 + k), *reinterpret_cast<const float4*>(wr0 + k + 4),
+           hi[0], mi[0], lo[0]);
+    split3(*reinterpret_cast<const float4*>(wr1 + k), *reinterpret_cast<const float4*>(wr1 + k + 4),
+           hi[1], mi[1], lo[1]);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const bf16x8_t a0 = __builtin_bit_cast(bf16x8_t, hi[i]);
+      const bf16x8_t a1 = __builtin_bit_cast(bf16x8_t, mi[i]);
+      const bf16x8_t a2 = __builtin_bit_cast(bf16x8_t, lo[i]);
+      acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, xb0, acc[i][0], 0, 0, 0);
+      acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, xb1, acc[i][1], 0, 0, 0);
+      acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, xb0, acc[i][0], 0, 0, 0);
+      acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, xb1, acc[i][1], 0, 0, 0);
+      acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2, xb0, acc[i][0], 0, 0, 0);
+      acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2, xb1, acc[i][1], 0, 0, 0);
+    }
+  }
+  // lane holds [token l32 of block j][experts 8g + 4*(lane/32) + q of block i]
+  float* out = part + static_cast<int64_t>(blockIdx.y) * T * E;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int64_t t = t0 + j * 32 + l32;
+    if (t >= T) continue;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int e = e0 + i * 32 + g * 8 + (lane >> 5) * 4;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (e + q < E) out[t * E + e + q] = acc[i][j][g * 4 + q];
+      }
+  }
+}
+
+struct MfmaPlan {
+  int wt, we;
+  int64_t gx, gz;
+  int ksplit, kchunk;
+};
+
+// Wave layout and h-split for the MFMA gating linear: aim for >= 512
+// workgroups (two per CU) with at most 8 partial planes.
+MfmaPlan mfma_plan(int64_t T, int64_t h, int64_t E) {
+  MfmaPlan p;
+  p.we = E <= 64 ? 1 : (E <= 128 ? 2 : 4);
+  p.wt = 4 / p.we;
+  p.gx = ceil_div(T, 64 * p.wt);
+  p.gz = ceil_div(E, 64 * p.we);
+  const int64_t base = p.gx * p.gz;
+  int64_t ks = std::min<int64_t>(8, std::max<int64_t>(1, ceil_div(512, base)));
+  ks = std::min<int64_t>(ks, std::max<int64_t>(1, h / 128));
+  p.kchunk = static_cast<int>(ceil_div(ceil_div(h, ks), 16) * 16);
+  p.ksplit = static_cast<int>(ceil_div(h, p.kchunk));
+  return p;
+}
+
+bool use_mfma(const moe_route_desc* d) { return d->x_dtype == MOE_BF16 && d->h % 16 == 0; }
 
 // ------------------------------------------------------- fixed fp32 sigmoid
 // exp(y) for y <= 0 by a fixed sequence of IEEE fp32 operations, each rounded
@@ -129,8 +261,9 @@ __device__ __forceinline__ bool better(float av, int ai, float bv, int bi) {
 
 template <int EPL>
 __global__ void __launch_bounds__(256) router_topk_kernel(
-    const float* __restrict__ logits, const float* __restrict__ expert_bias, int64_t T, int E,
-    int K, int score, int pre_softmax, float* __restrict__ scores_out, float* __restrict__ probs,
+    const float* __restrict__ part, int nsplit, const float* __restrict__ bias,
+    const float* __restrict__ expert_bias, int64_t T, int E, int K, int score, int pre_softmax,
+    float* __restrict__ logits_out, float* __restrict__ scores_out, float* __restrict__ probs,
     uint8_t* __restrict__ rmap, int32_t* __restrict__ hist) {
   __shared__ int cnt[kMaxExperts];
   const int lane = threadIdx.x % 64;
@@ -148,7 +281,16 @@ __global__ void __launch_bounds__(256) router_topk_kernel(
       const int e = lane + 64 * j;
       valid[j] = e < E;
       taken[j] = false;
-      l[j] = valid[j] ? logits[t * E + e] : -INFINITY;
+      if (valid[j]) {
+        const int64_t idx = t * E + e;
+        float v = part[idx];
+        for (int sp = 1; sp < nsplit; ++sp) v += part[sp * T * E + idx];  // fixed order
+        if (bias) v += bias[e];
+        l[j] = v;
+        if (logits_out) logits_out[idx] = v;
+      } else {
+        l[j] = -INFINITY;
+      }
     }
     if (score == MOE_SCORE_SOFTMAX) {
       float m = -INFINITY;
@@ -264,12 +406,28 @@ __global__ void __launch_bounds__(256) router_drop_kernel(const int32_t* __restr
   }
 }
 
+struct TopkArgs {
+  const float* part;
+  int nsplit;
+  const float* bias;
+  const float* expert_bias;
+  int64_t T;
+  int E, K, score, pre;
+  float *logits_out, *scores, *probs;
+  uint8_t* map;
+  int32_t* hist;
+};
+
 template <int EPL>
-void launch_topk(int64_t nblk, hipStream_t s, const float* logits, const float* eb, int64_t T,
-                 int E, int K, int score, int pre, float* scores, float* probs, uint8_t* map,
-                 int32_t* hist) {
+void launch_topk(int64_t nblk, hipStream_t s, const TopkArgs& a) {
   hipLaunchKernelGGL(router_topk_kernel<EPL>, dim3(static_cast<unsigned>(nblk)), dim3(256), 0, s,
-                     logits, eb, T, E, K, score, pre, scores, probs, map, hist);
+                     a.part, a.nsplit, a.bias, a.expert_bias, a.T, a.E, a.K, a.score, a.pre,
+                     a.logits_out, a.scores, a.probs, a.map, a.hist);
+}
+
+size_t logits_ws_bytes(const moe_route_desc* d) {
+  const int64_t planes = use_mfma(d) ? mfma_plan(d->T, d->h, d->E).ksplit : 1;
+  return align_up(static_cast<size_t>(planes * d->T * d->E) * sizeof(float), 256);
 }
 
 int64_t capacity_of(const moe_route_desc* d) {
@@ -309,8 +467,7 @@ using namespace moe;
 
 extern "C" size_t moe_route_workspace_size(const moe_route_desc* d) {
   if (validate(d) != MOE_OK || d->T == 0) return 0;
-  const size_t logits = align_up(static_cast<size_t>(d->T * d->E) * sizeof(float), 256);
-  return logits + count_ws_bytes(d->T, d->E);
+  return logits_ws_bytes(d) + count_ws_bytes(d->T, d->E);
 }
 
 extern "C" int64_t moe_route_capacity(const moe_route_desc* d) {
@@ -349,53 +506,73 @@ extern "C" moe_status moe_route(const moe_route_desc* d, const void* x, const fl
               "moe_route: workspace of %zu bytes given, %zu needed", workspace_bytes, need);
 
   char* ws = static_cast<char*>(workspace);
-  float* logits_ws = reinterpret_cast<float*>(ws);
-  int32_t* hist = reinterpret_cast<int32_t*>(ws + align_up(T * E * sizeof(float), 256));
+  float* part_ws = reinterpret_cast<float*>(ws);
   const int64_t nblk = ceil_div(T, kCountBlock);
-  int32_t* blkoff = hist + align_up(static_cast<size_t>(nblk * E) * sizeof(int32_t), 256) / 4;
+  const size_t plane_bytes = align_up(static_cast<size_t>(nblk * E) * sizeof(int32_t), 256);
+  int32_t* hist = reinterpret_cast<int32_t*>(ws + logits_ws_bytes(d));
+  int32_t* blkoff = hist + plane_bytes / 4;
 
-  const float* logits = logits_in;
-  if (!logits) {
-    float* dst = logits_out ? logits_out : logits_ws;
+  TopkArgs ta{};
+  ta.expert_bias = expert_bias;
+  ta.T = T;
+  ta.E = static_cast<int>(E);
+  ta.K = static_cast<int>(d->K);
+  ta.score = d->score;
+  ta.pre = d->pre_softmax;
+  ta.logits_out = logits_out;
+  ta.scores = scores_out;
+  ta.probs = probs;
+  ta.map = routing_map;
+  ta.hist = hist;
+  if (logits_in) {
+    ta.part = logits_in;
+    ta.nsplit = 1;
+    ta.bias = nullptr;  // logits_in are complete logits
+  } else if (use_mfma(d)) {
+    const MfmaPlan p = mfma_plan(T, d->h, E);
+    const dim3 grid(static_cast<unsigned>(p.gx), static_cast<unsigned>(p.ksplit),
+                    static_cast<unsigned>(p.gz));
+    const uint16_t* xb = static_cast<const uint16_t*>(x);
+    const int hh = static_cast<int>(d->h), Ei = static_cast<int>(E);
+    if (p.we == 1)
+      hipLaunchKernelGGL((router_logits_mfma<4, 1>), grid, dim3(256), 0, s, xb, w_router, part_ws,
+                         T, hh, Ei, p.kchunk);
+    else if (p.we == 2)
+      hipLaunchKernelGGL((router_logits_mfma<2, 2>), grid, dim3(256), 0, s, xb, w_router, part_ws,
+                         T, hh, Ei, p.kchunk);
+    else
+      hipLaunchKernelGGL((router_logits_mfma<1, 4>), grid, dim3(256), 0, s, xb, w_router, part_ws,
+                         T, hh, Ei, p.kchunk);
+    ta.part = part_ws;
+    ta.nsplit = p.ksplit;
+    ta.bias = b_router;
+  } else {
     dim3 grid(static_cast<unsigned>(ceil_div(T, LT)), static_cast<unsigned>(ceil_div(E, LE)));
     if (d->x_dtype == MOE_BF16)
-      hipLaunchKernelGGL(router_logits_kernel<uint16_t>, grid, dim3(256), 0, s,
-                         static_cast<const uint16_t*>(x), w_router, b_router, dst, T,
+      hipLaunchKernelGGL(router_logits_simt<uint16_t>, grid, dim3(256), 0, s,
+                         static_cast<const uint16_t*>(x), w_router, part_ws, T,
                          static_cast<int>(d->h), static_cast<int>(E));
     else
-      hipLaunchKernelGGL(router_logits_kernel<float>, grid, dim3(256), 0, s,
-                         static_cast<const float*>(x), w_router, b_router, dst, T,
+      hipLaunchKernelGGL(router_logits_simt<float>, grid, dim3(256), 0, s,
+                         static_cast<const float*>(x), w_router, part_ws, T,
                          static_cast<int>(d->h), static_cast<int>(E));
-    logits = dst;
-  } else if (logits_out && logits_out != logits_in) {
-    const hipError_t ce =
-        hipMemcpyAsync(logits_out, logits_in, T * E * sizeof(float), hipMemcpyDeviceToDevice, s);
-    MOE_REQUIRE(ce == hipSuccess, MOE_ERR_HIP, "moe_route: copy of logits_in failed: %s",
-                hipGetErrorString(ce));
+    ta.part = part_ws;
+    ta.nsplit = 1;
+    ta.bias = b_router;
   }
 
-  const int Ei = static_cast<int>(E), Ki = static_cast<int>(d->K);
   const int epl = static_cast<int>(ceil_div(E, 64));
-  if (epl <= 1)
-    launch_topk<1>(nblk, s, logits, expert_bias, T, Ei, Ki, d->score, d->pre_softmax, scores_out,
-                   probs, routing_map, hist);
-  else if (epl <= 2)
-    launch_topk<2>(nblk, s, logits, expert_bias, T, Ei, Ki, d->score, d->pre_softmax, scores_out,
-                   probs, routing_map, hist);
-  else if (epl <= 4)
-    launch_topk<4>(nblk, s, logits, expert_bias, T, Ei, Ki, d->score, d->pre_softmax, scores_out,
-                   probs, routing_map, hist);
-  else if (epl <= 8)
-    launch_topk<8>(nblk, s, logits, expert_bias, T, Ei, Ki, d->score, d->pre_softmax, scores_out,
-                   probs, routing_map, hist);
-  else
-    launch_topk<16>(nblk, s, logits, expert_bias, T, Ei, Ki, d->score, d->pre_softmax, scores_out,
-                    probs, routing_map, hist);
+  if (epl <= 1) launch_topk<1>(nblk, s, ta);
+  else if (epl <= 2) launch_topk<2>(nblk, s, ta);
+  else if (epl <= 4) launch_topk<4>(nblk, s, ta);
+  else if (epl <= 8) launch_topk<8>(nblk, s, ta);
+  else launch_topk<16>(nblk, s, ta);
 
+  // per-expert counts: tokens_per_expert = min(count, capacity)
   const int64_t cap = capacity_of(d);
-  launch_count_scan(hist, nblk, E, cap, blkoff, tokens_per_expert, nullptr, s);
+  launch_count_scan(hist, nblk, E, cap, blkoff, tokens_per_expert, s);
   if (cap >= 0)
     hipLaunchKernelGGL(router_drop_kernel, dim3(static_cast<unsigned>(nblk)), dim3(256), 0, s, blkoff,
-                       T, Ei, cap, probs, routing_map);
+                       T, static_cast<int>(E), cap, probs, routing_map);
   return check_launch("moe_route");
 }
