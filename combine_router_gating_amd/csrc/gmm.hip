@@ -51,10 +51,10 @@ struct Tile {
 };
 
 // Decode this workgroup's tile.  s_toff/s_roff/s_n: LDS arrays of E+1 / E+1 / E.
-template <int BM>
+template <int BM, int NTHREADS = kThreads>
 __device__ bool decode_tile(const int32_t* __restrict__ counts, int E, int64_t max_rows, int NT,
                             int* s_toff, int* s_roff, int* s_n, int64_t* scratch, Tile& tile) {
-  constexpr int PER = kMaxExperts / kThreads;  // experts per thread
+  constexpr int PER = kMaxExperts / NTHREADS;  // experts per thread
   const int tid = threadIdx.x;
   int64_t c[PER];
   int64_t sum = 0;
@@ -67,7 +67,7 @@ __device__ bool decode_tile(const int32_t* __restrict__ counts, int E, int64_t m
     sum += v;
   }
   int64_t total_rows;
-  int64_t pre = block_exclusive_scan256(sum, scratch, &total_rows);
+  int64_t pre = block_exclusive_scan<NTHREADS / 64>(sum, scratch, &total_rows);
   int tl[PER];
   int tsum = 0;
 #pragma unroll
@@ -85,7 +85,7 @@ __device__ bool decode_tile(const int32_t* __restrict__ counts, int E, int64_t m
     pre += c[j];
   }
   int64_t total_tiles;
-  int tpre = static_cast<int>(block_exclusive_scan256(tsum, scratch, &total_tiles));
+  int tpre = static_cast<int>(block_exclusive_scan<NTHREADS / 64>(tsum, scratch, &total_tiles));
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
     const int e = tid * PER + j;
@@ -122,89 +122,181 @@ __device__ bool decode_tile(const int32_t* __restrict__ counts, int E, int64_t m
 
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
 
-// Global -> registers for one k-step: A rows, then the weight rows (the
-// first BN from B0, the next BN from B1 when the tile holds two matrices).
-template <int A_LD, int B_LD, int BN>
-__device__ __forceinline__ void gmm_gload(u32x4 (&ra)[A_LD], u32x4 (&rb)[B_LD],
-                                          const uint16_t* a_base, const uint16_t* b0_base,
-                                          const uint16_t* b1_base, const uint32_t (&a_off)[A_LD],
-                                          const uint32_t (&b_off)[B_LD], int kt) {
-  const uint32_t ko = static_cast<uint32_t>(kt) * BK;
-#pragma unroll
-  for (int i = 0; i < A_LD; ++i) ra[i] = *reinterpret_cast<const u32x4*>(a_base + a_off[i] + ko);
-#pragma unroll
-  for (int i = 0; i < B_LD; ++i) {
-    const uint16_t* bb = ((32 * i) / BN == 0) ? b0_base : b1_base;
-    rb[i] = *reinterpret_cast<const u32x4*>(bb + b_off[i] + ko);
-  }
-}
-
-// Registers -> one LDS stage, chunk c of row r at c ^ (r & 7).
-template <int A_LD, int B_LD, int BM>
-__device__ __forceinline__ void gmm_sstore(u32x4* sdst, const u32x4 (&ra)[A_LD],
-                                           const u32x4 (&rb)[B_LD], int r, int c) {
-#pragma unroll
-  for (int i = 0; i < A_LD; ++i) {
-    const int lr = r + 32 * i;
-    sdst[lr * 8 + (c ^ (lr & 7))] = ra[i];
-  }
-#pragma unroll
-  for (int i = 0; i < B_LD; ++i) {
-    const int br = BM + r + 32 * i;
-    sdst[br * 8 + (c ^ (br & 7))] = rb[i];
-  }
-}
-
 // ----------------------------------------------------------------- bf16 MFMA
-template <int BM, int BN, int WM, int WN, bool FC1>
-__global__ void __launch_bounds__(kThreads) gmm_bf16_kernel(
-    const uint16_t* __restrict__ A, const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1,
-    uint16_t* __restrict__ C, const int32_t* __restrict__ counts, int E, int N, int K,
-    int64_t max_rows) {
+// LDS stage layout: a stage holds ROWS = BM + NB*BN rows (activation rows
+// first, then the weight rows) of one SBK-wide k slab, SBK*2 bytes per row,
+// in 16-byte chunks.  gfx950's LDS serves a 16-byte-per-lane read 16 lanes
+// at a time across 64 four-byte banks (256 bytes), so chunks are
+// XOR-swizzled such that sixteen lanes reading the same logical chunk of
+// sixteen consecutive rows touch sixteen different 16-byte bank groups,
+// while a direct-to-LDS load still fills a contiguous 1 KB piece (lane i ->
+// bytes 16i):
+//   SBK = 32 (64-byte rows): rows 2L and 2L+1 share 128-byte line L;
+//     logical chunk lc = (row & 1) * 4 + c sits at lc ^ ((L >> 1) & 3);
+//   SBK = 64 (128-byte rows): chunk c of row r sits at c ^ ((r >> 1) & 7);
+//   SBK >= 128: chunk c of row r sits at (c & ~15) | ((c & 15) ^ (r & 15)).
+template <int SBK>
+__device__ __forceinline__ uint32_t lds_chunk_byte(int row, int c) {
+  if constexpr (SBK == 32) {
+    const int line = row >> 1;
+    const int lc = ((row & 1) << 2) | c;
+    return static_cast<uint32_t>(line * 128 + ((lc ^ ((line >> 1) & 3)) << 4));
+  } else if constexpr (SBK == 64) {
+    return static_cast<uint32_t>(row * 128 + ((c ^ ((row >> 1) & 7)) << 4));
+  } else {
+    const int pc = (c & ~15) | ((c & 15) ^ (row & 15));
+    return static_cast<uint32_t>(row * (SBK * 2) + (pc << 4));
+  }
+}
+
+// Inverse of lds_chunk_byte for a 16-byte piece at stage byte offset o.
+template <int SBK>
+__device__ __forceinline__ void lds_piece(int o, int& row, int& c) {
+  if constexpr (SBK == 32) {
+    const int line = o >> 7;
+    const int lc = ((o >> 4) & 7) ^ ((line >> 1) & 3);
+    row = 2 * line + (lc >> 2);
+    c = lc & 3;
+  } else if constexpr (SBK == 64) {
+    row = o >> 7;
+    c = ((o >> 4) & 7) ^ ((row >> 1) & 7);
+  } else {
+    row = o / (SBK * 2);
+    const int pc = (o % (SBK * 2)) >> 4;
+    c = (pc & ~15) | ((pc & 15) ^ (row & 15));
+  }
+}
+
+// Direct global -> LDS 16-byte load: lane i writes LDS bytes
+// [lds_base + 16 i, lds_base + 16 i + 16).  Issued as inline assembly so the
+// compiler does not serialise the pipeline with conservative waits; the
+// kernel waits for these loads itself (vmcnt) before a barrier.
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gptr), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "memory");
+}
+
+// Wait until at most n of this wave's vector-memory loads are outstanding.
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  // gfx9 encoding: vmcnt[3:0] bits 3:0, vmcnt[5:4] bits 15:14; expcnt and
+  // lgkmcnt left at their maxima (no wait)
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+__device__ __forceinline__ void block_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int LPW, int STAGES>
+__device__ __forceinline__ void wait_stage(int n_after) {
+  // n_after later stages may stay in flight (n_after <= STAGES - 2)
+  if constexpr (STAGES >= 6) { if (n_after >= 4) { wait_vmcnt<LPW * 4>(); return; } }
+  if constexpr (STAGES >= 5) { if (n_after >= 3) { wait_vmcnt<LPW * 3>(); return; } }
+  if constexpr (STAGES >= 4) { if (n_after >= 2) { wait_vmcnt<LPW * 2>(); return; } }
+  if constexpr (STAGES >= 3) { if (n_after >= 1) { wait_vmcnt<LPW * 1>(); return; } }
+  wait_vmcnt<0>();
+}
+
+// MFMA operand fragments of one 16-wide k step for one wave: MI activation
+// blocks and NB x NI weight blocks of 32 rows, 8 consecutive k per lane.
+template <int MI, int NB, int NI, int BM, int BN, int SBK, int WTM, int WTN>
+__device__ __forceinline__ void load_frags(bf16x8 (&a)[MI], bf16x8 (&b)[NB][NI], const char* st,
+                                           int kk, int wm, int wn, int l32, int hi) {
+  const int c = kk * 2 + hi;
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi) {
+    const int row = wm * WTM + mi * 32 + l32;
+    a[mi] = *reinterpret_cast<const bf16x8*>(st + lds_chunk_byte<SBK>(row, c));
+  }
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) {
+      const int row = BM + nb * BN + wn * WTN + ni * 32 + l32;
+      b[nb][ni] = *reinterpret_cast<const bf16x8*>(st + lds_chunk_byte<SBK>(row, c));
+    }
+}
+
+template <int MI, int NB, int NI>
+__device__ __forceinline__ void mfma_step(f32x16 (&acc)[NB][MI][NI], const bf16x8 (&a)[MI],
+                                          const bf16x8 (&b)[NB][NI]) {
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+        acc[nb][mi][ni] =
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[nb][ni], a[mi], acc[nb][mi][ni], 0, 0, 0);
+}
+
+// LDS bytes one tile body uses.
+template <int BM, int BN, bool FC1, int STAGES, int SBK>
+constexpr int body_lds_bytes() {
+  return STAGES * (BM + (FC1 ? 2 : 1) * BN) * SBK * 2;
+}
+
+// One output tile (BM rows of one expert x BN columns) of the grouped GEMM.
+// `smem` holds the pipeline stages; all 64*WM*WN threads take part.
+template <int BM, int BN, int WM, int WN, bool FC1, int STAGES, int SBK>
+__device__ __forceinline__ void gmm_tile(const Tile& tile, char* smem,
+                                         const uint16_t* __restrict__ A,
+                                         const uint16_t* __restrict__ B0,
+                                         const uint16_t* __restrict__ B1, uint16_t* __restrict__ C,
+                                         int N, int K) {
   constexpr int NB = FC1 ? 2 : 1;
-  constexpr int BROWS = NB * BN;
+  constexpr int ROWS = BM + NB * BN;
+  constexpr int NW = WM * WN;              // waves per workgroup
+  constexpr int STAGE_BYTES = ROWS * SBK * 2;
+  constexpr int LPW = STAGE_BYTES / (NW * 1024);  // direct loads (1 KB each) per wave per stage
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int MI = WTM / 32, NI = WTN / 32;
-  constexpr int A_LD = BM / 32, B_LD = BROWS / 32;
-  constexpr int STAGE = (BM + BROWS) * 8;  // 16-byte chunks per stage
-  static_assert(WM * WN == 4, "4 waves");
+  static_assert(NW == 4 || NW == 8, "4 or 8 waves");
   static_assert(MI >= 1 && NI >= 1, "wave tile must be at least 32x32");
+  static_assert(STAGE_BYTES % (NW * 1024) == 0, "whole direct loads per wave");
+  static_assert(SBK == 32 || SBK == 64 || SBK == 128 || SBK == 256, "k slab per stage");
+  static_assert(STAGES >= 3 && STAGES <= 6, "pipeline depth");
 
-  __shared__ u32x4 smem[2 * STAGE];
-  __shared__ int s_toff[kMaxExperts + 1];
-  __shared__ int s_roff[kMaxExperts];
-  __shared__ int s_n[kMaxExperts];
-  __shared__ int64_t s_scan[8];
-
-  const int NT = (N + BN - 1) / BN;
-  Tile tile;
-  if (!decode_tile<BM>(counts, E, max_rows, NT, s_toff, s_roff, s_n, s_scan, tile)) return;
   const int n0 = tile.n0 * BN;
-
   const int tid = threadIdx.x;
-  const int c = tid & 7, r = tid >> 3;  // chunk within a 128-byte row; row 0..31
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
+  const uint32_t smem_base = static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)smem));
 
-  // Global sources: wave-uniform bases plus 32-bit per-thread offsets.  Rows
-  // past the tile's valid rows (or past N) are clamped in range: they are
-  // computed but never stored.
-  const uint16_t* a_base = A + tile.row0 * static_cast<int64_t>(K);
+  // Sources of this lane's direct loads (fixed rows; k advances per stage).
+  // Rows past the tile's valid rows (or past N) are clamped in range: they
+  // are computed but never stored.
+  const uint16_t* src[LPW];
   const int64_t b_expert = static_cast<int64_t>(tile.e) * N * K;
-  const uint16_t* b0_base = B0 + b_expert;
-  const uint16_t* b1_base = (NB == 2 ? B1 : B0) + b_expert;
-  uint32_t a_off[A_LD], b_off[B_LD];
 #pragma unroll
-  for (int i = 0; i < A_LD; ++i) {
-    const int lr = min(r + 32 * i, tile.nrows - 1);
-    a_off[i] = static_cast<uint32_t>(lr) * K + c * 8;
+  for (int j = 0; j < LPW; ++j) {
+    int row, c;
+    lds_piece<SBK>((wave * LPW + j) * 1024 + lane * 16, row, c);
+    if (row < BM) {
+      const int lr = min(row, tile.nrows - 1);
+      src[j] = A + (tile.row0 + lr) * static_cast<int64_t>(K) + c * 8;
+    } else {
+      const int br = row - BM;
+      const uint16_t* base = (NB == 2 && br >= BN) ? B1 : B0;
+      const int n = min(n0 + (br % BN), N - 1);
+      src[j] = base + b_expert + static_cast<int64_t>(n) * K + c * 8;
+    }
   }
+  auto issue = [&](int kt) {
+    const uint32_t dst = smem_base + static_cast<uint32_t>((kt % STAGES) * STAGE_BYTES) +
+                         static_cast<uint32_t>(wave * LPW * 1024);
+    const int64_t ko = static_cast<int64_t>(kt) * SBK;
 #pragma unroll
-  for (int i = 0; i < B_LD; ++i) {
-    const int br = (r + 32 * i) % BN;  // row within one weight matrix
-    const int n = min(n0 + br, N - 1);
-    b_off[i] = static_cast<uint32_t>(n) * K + c * 8;
-  }
+    for (int j = 0; j < LPW; ++j) dma16(src[j] + ko, dst + j * 1024);
+  };
 
   f32x16 acc[NB][MI][NI];
 #pragma unroll
@@ -216,51 +308,51 @@ __global__ void __launch_bounds__(kThreads) gmm_bf16_kernel(
 #pragma unroll
         for (int q = 0; q < 16; ++q) acc[b][mi][ni][q] = 0.f;
 
-  u32x4 ra[A_LD], rb[B_LD];
+  // Pipeline: stages kt+1 .. kt+STAGES-2 are in flight while stage kt is
+  // multiplied; within a stage the fragments of step kk+1 are read from LDS
+  // while the MFMAs of step kk run; before the last step of stage kt the
+  // workgroup waits for stage kt+1, passes a barrier (after which every wave
+  // is done with stage kt-1, whose slot then receives stage kt+STAGES-1),
+  // and prefetches the first fragments of stage kt+1.
+  constexpr int KK = SBK / 16;
+  const int nk = K / SBK;
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (s < nk) issue(s);
+  wait_stage<LPW, STAGES>(min(STAGES - 2, nk - 1));
+  block_barrier();
 
-  const int nk = K / BK;
-  gmm_gload<A_LD, B_LD, BN>(ra, rb, a_base, b0_base, b1_base, a_off, b_off, 0);
-  gmm_sstore<A_LD, B_LD, BM>(smem, ra, rb, r, c);
-  __syncthreads();
-  const int lr32 = lane & 31, hi = lane >> 5;
+  const int l32 = lane & 31, hi = lane >> 5;
+  bf16x8 ca[MI], cb[NB][NI], na[MI], nb[NB][NI];
+  load_frags<MI, NB, NI, BM, BN, SBK, WTM, WTN>(ca, cb, smem, 0, wm, wn, l32, hi);
   for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) gmm_gload<A_LD, B_LD, BN>(ra, rb, a_base, b0_base, b1_base, a_off, b_off, kt + 1);
-    const u32x4* s = smem + (kt & 1) * STAGE;
+    const char* st = smem + (kt % STAGES) * STAGE_BYTES;
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      const int ch = kk * 2 + hi;
-      bf16x8 af[MI], bfr[NB][NI];
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi) {
-        const int row = wm * WTM + mi * 32 + lr32;
-        const u32x4 v = s[row * 8 + (ch ^ (row & 7))];
-        af[mi] = *reinterpret_cast<const bf16x8*>(&v);
+    for (int kk = 0; kk < KK; ++kk) {
+      if (kk + 1 < KK) {
+        load_frags<MI, NB, NI, BM, BN, SBK, WTM, WTN>(na, nb, st, kk + 1, wm, wn, l32, hi);
+      } else if (kt + 1 < nk) {
+        const int last = min(kt + STAGES - 2, nk - 1);  // newest stage issued so far
+        wait_stage<LPW, STAGES>(last - (kt + 1));
+        block_barrier();
+        if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1);
+        load_frags<MI, NB, NI, BM, BN, SBK, WTM, WTN>(
+            na, nb, smem + ((kt + 1) % STAGES) * STAGE_BYTES, 0, wm, wn, l32, hi);
       }
+      mfma_step<MI, NB, NI>(acc, ca, cb);
 #pragma unroll
-      for (int b = 0; b < NB; ++b)
+      for (int mi = 0; mi < MI; ++mi) ca[mi] = na[mi];
 #pragma unroll
-        for (int ni = 0; ni < NI; ++ni) {
-          const int row = BM + b * BN + wn * WTN + ni * 32 + lr32;
-          const u32x4 v = s[row * 8 + (ch ^ (row & 7))];
-          bfr[b][ni] = *reinterpret_cast<const bf16x8*>(&v);
-        }
+      for (int q = 0; q < NB; ++q)
 #pragma unroll
-      for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-          for (int ni = 0; ni < NI; ++ni)
-            acc[b][mi][ni] =
-                __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[b][ni], af[mi], acc[b][mi][ni], 0, 0, 0);
+        for (int ni = 0; ni < NI; ++ni) cb[q][ni] = nb[q][ni];
     }
-    if (kt + 1 < nk) gmm_sstore<A_LD, B_LD, BM>(smem + ((kt + 1) & 1) * STAGE, ra, rb, r, c);
-    __syncthreads();
   }
 
-  // epilogue: lane holds C[m = lr32][n = 8*g + 4*hi + q] of each 32x32 block
+  // epilogue: lane holds C[m = l32][n = 8*g + 4*hi + q] of each 32x32 block
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi) {
-    const int ml = wm * WTM + mi * 32 + lr32;
+    const int ml = wm * WTM + mi * 32 + l32;
     if (ml >= tile.nrows) continue;
     uint16_t* crow = C + (tile.row0 + ml) * static_cast<int64_t>(N);
 #pragma unroll
@@ -283,6 +375,58 @@ __global__ void __launch_bounds__(kThreads) gmm_bf16_kernel(
       }
   }
 }
+
+
+// The grouped-GEMM kernel: decode this workgroup's tile with BMAX-row
+// m-tiles, then run a tile body.  With 256-row m-tiles an expert's last,
+// ragged tile runs the 128- or 64-row body when it fits (less MFMA work
+// spent on padding); with shorter m-tiles the layer is weight-streaming
+// bound and one body serves every tile.  The choice is uniform per
+// workgroup.
+template <bool FC1, int BMAX, int BN, int NW, class Body256, class Body128, class Body64>
+__global__ void __launch_bounds__(NW * 64) gmm_bf16_kernel(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1,
+    uint16_t* __restrict__ C, const int32_t* __restrict__ counts, int E, int N, int K,
+    int64_t max_rows) {
+  constexpr int L256 = Body256::lds > Body128::lds ? Body256::lds : Body128::lds;
+  constexpr int LDS = BMAX == 256 ? (L256 > Body64::lds ? L256 : Body64::lds)
+                                 : (BMAX == 128 ? Body128::lds : Body64::lds);
+  constexpr int DECODE_BYTES = (3 * kMaxExperts + 1) * 4 + 64;
+  static_assert(LDS >= DECODE_BYTES, "decode scratch aliases the stages");
+  __shared__ __attribute__((aligned(1024))) char smem[LDS];
+  const int NT = (N + BN - 1) / BN;
+  Tile tile;
+  {
+    int* s_toff = reinterpret_cast<int*>(smem);
+    int* s_roff = s_toff + kMaxExperts + 1;
+    int* s_n = s_roff + kMaxExperts;
+    int64_t* s_scan = reinterpret_cast<int64_t*>(s_n + kMaxExperts + 1);
+    const bool mine =
+        decode_tile<BMAX, NW * 64>(counts, E, max_rows, NT, s_toff, s_roff, s_n, s_scan, tile);
+    __syncthreads();  // decode scratch is reused by the stages below
+    if (!mine) return;
+  }
+  tile.nrows = __builtin_amdgcn_readfirstlane(tile.nrows);
+  if constexpr (BMAX == 256) {
+    if (tile.nrows > 128) Body256::run(tile, smem, A, B0, B1, C, N, K);
+    else if (tile.nrows > 64) Body128::run(tile, smem, A, B0, B1, C, N, K);
+    else Body64::run(tile, smem, A, B0, B1, C, N, K);
+  } else if constexpr (BMAX == 128) {
+    Body128::run(tile, smem, A, B0, B1, C, N, K);
+  } else {
+    Body64::run(tile, smem, A, B0, B1, C, N, K);
+  }
+}
+
+template <int BM, int BN, int WM, int WN, bool FC1, int STAGES, int SBK>
+struct Body {
+  static constexpr int lds = body_lds_bytes<BM, BN, FC1, STAGES, SBK>();
+  __device__ __forceinline__ static void run(const Tile& t, char* smem, const uint16_t* A,
+                                             const uint16_t* B0, const uint16_t* B1, uint16_t* C,
+                                             int N, int K) {
+    gmm_tile<BM, BN, WM, WN, FC1, STAGES, SBK>(t, smem, A, B0, B1, C, N, K);
+  }
+};
 
 // ----------------------------------------------------------------- fp32 SIMT
 // For fp32 layers: 64x64 tiles, 16x16 threads with 4x4 outputs each (per
@@ -362,15 +506,15 @@ int64_t grid_for(int64_t max_rows, int64_t E, int BM, int64_t N, int BN) {
   return ceil_div(total, 8) * 8;
 }
 
-template <int BM, int BN, int WM, int WN, bool FC1>
+template <bool FC1, int BMAX, int BN, int NW, class B256, class B128, class B64>
 void launch_bf16(const void* A, const void* B0, const void* B1, void* C, const int32_t* counts,
                  int64_t E, int64_t N, int64_t K, int64_t max_rows, hipStream_t s) {
-  const int64_t g = grid_for(max_rows, E, BM, N, BN);
-  hipLaunchKernelGGL((gmm_bf16_kernel<BM, BN, WM, WN, FC1>), dim3(static_cast<unsigned>(g)),
-                     dim3(kThreads), 0, s, static_cast<const uint16_t*>(A),
-                     static_cast<const uint16_t*>(B0), static_cast<const uint16_t*>(B1),
-                     static_cast<uint16_t*>(C), counts, static_cast<int>(E), static_cast<int>(N),
-                     static_cast<int>(K), max_rows);
+  const int64_t g = grid_for(max_rows, E, BMAX, N, BN);
+  hipLaunchKernelGGL((gmm_bf16_kernel<FC1, BMAX, BN, NW, B256, B128, B64>),
+                     dim3(static_cast<unsigned>(g)), dim3(NW * 64), 0, s,
+                     static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B0),
+                     static_cast<const uint16_t*>(B1), static_cast<uint16_t*>(C), counts,
+                     static_cast<int>(E), static_cast<int>(N), static_cast<int>(K), max_rows);
 }
 
 template <bool FC1>
@@ -383,15 +527,28 @@ void launch_f32(const void* A, const void* B0, const void* B1, void* C, const in
                      static_cast<int>(E), static_cast<int>(N), static_cast<int>(K), max_rows);
 }
 
-// Tile height from the average rows per expert (known on the host without
+// Tile shape from the average rows per expert (known on the host without
 // reading the device counts): tall tiles amortise weight reads when experts
-// are large; short tiles waste fewer MFMA cycles on padding when they are not.
+// are large; shorter tiles waste fewer MFMA cycles on padding when they are
+// not.  All variants run 8 waves (two per SIMD, so one wave's MFMAs cover
+// the other's waits); the shapes were chosen by timing the variants on the
+// five layer shapes.
 int pick_bm(int64_t max_rows, int64_t E) {
   const int64_t avg = max_rows / E;
-  if (avg >= 512) return 256;
-  if (avg >= 192) return 128;
+  if (avg >= 192) return 256;
+  if (avg >= 80) return 128;
   return 64;
 }
+
+// Tile bodies (8 waves each; shapes chosen by timing the variants on the
+// five layer shapes with random operands).  FC1 tiles hold BN=128 columns
+// of W_gate and of W_up; FC2 tiles BN=256 columns of W_down.
+using Fc1Body256 = Body<256, 128, 4, 2, true, 4, 32>;
+using Fc1Body128 = Body<128, 128, 4, 2, true, 5, 32>;
+using Fc1Body64 = Body<64, 128, 2, 4, true, 4, 64>;
+using Fc2Body256 = Body<256, 256, 2, 4, false, 4, 32>;
+using Fc2Body128 = Body<128, 256, 4, 2, false, 5, 32>;
+using Fc2Body64 = Body<64, 256, 2, 4, false, 4, 64>;
 
 template <bool FC1>
 void launch_gemm(int32_t dtype, const void* A, const void* B0, const void* B1, void* C,
@@ -403,13 +560,19 @@ void launch_gemm(int32_t dtype, const void* A, const void* B0, const void* B1, v
   }
   const int bm = pick_bm(max_rows, E);
   if constexpr (FC1) {
-    if (bm == 256) launch_bf16<256, 128, 2, 2, FC1>(A, B0, B1, C, counts, E, N, K, max_rows, s);
-    else if (bm == 128) launch_bf16<128, 128, 2, 2, FC1>(A, B0, B1, C, counts, E, N, K, max_rows, s);
-    else launch_bf16<64, 128, 1, 4, FC1>(A, B0, B1, C, counts, E, N, K, max_rows, s);
+    if (bm == 256)
+      launch_bf16<true, 256, 128, 8, Fc1Body256, Fc1Body128, Fc1Body64>(A, B0, B1, C, counts, E, N, K, max_rows, s);
+    else if (bm == 128)
+      launch_bf16<true, 128, 128, 8, Fc1Body256, Fc1Body128, Fc1Body64>(A, B0, B1, C, counts, E, N, K, max_rows, s);
+    else
+      launch_bf16<true, 64, 128, 8, Fc1Body256, Fc1Body128, Fc1Body64>(A, B0, B1, C, counts, E, N, K, max_rows, s);
   } else {
-    if (bm == 256) launch_bf16<256, 256, 2, 2, FC1>(A, B0, B1, C, counts, E, N, K, max_rows, s);
-    else if (bm == 128) launch_bf16<128, 256, 2, 2, FC1>(A, B0, B1, C, counts, E, N, K, max_rows, s);
-    else launch_bf16<64, 256, 1, 4, FC1>(A, B0, B1, C, counts, E, N, K, max_rows, s);
+    if (bm == 256)
+      launch_bf16<false, 256, 256, 8, Fc2Body256, Fc2Body128, Fc2Body64>(A, B0, B1, C, counts, E, N, K, max_rows, s);
+    else if (bm == 128)
+      launch_bf16<false, 128, 256, 8, Fc2Body256, Fc2Body128, Fc2Body64>(A, B0, B1, C, counts, E, N, K, max_rows, s);
+    else
+      launch_bf16<false, 64, 256, 8, Fc2Body256, Fc2Body128, Fc2Body64>(A, B0, B1, C, counts, E, N, K, max_rows, s);
   }
 }
 

@@ -51,11 +51,11 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
   return static_cast<uint16_t>(u >> 16);
 }
 
-// Exclusive scan over a 256-thread workgroup (4 waves).  Returns this
-// thread's exclusive prefix; *total receives the sum.  `scratch` is >= 4
-// LDS entries.  Every thread of the workgroup must call it.
-__device__ __forceinline__ int64_t block_exclusive_scan256(int64_t v, int64_t* scratch,
-                                                           int64_t* total) {
+// Exclusive scan over a workgroup of NW waves.  Returns this thread's
+// exclusive prefix; *total receives the sum.  `scratch` is >= NW LDS
+// entries.  Every thread of the workgroup must call it.
+template <int NW>
+__device__ __forceinline__ int64_t block_exclusive_scan(int64_t v, int64_t* scratch, int64_t* total) {
   const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
   int64_t incl = v;
 #pragma unroll
@@ -67,7 +67,7 @@ __device__ __forceinline__ int64_t block_exclusive_scan256(int64_t v, int64_t* s
   __syncthreads();
   int64_t before = 0, all = 0;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
+  for (int w = 0; w < NW; ++w) {
     const int64_t s = scratch[w];
     if (w < wave) before += s;
     all += s;
@@ -75,6 +75,11 @@ __device__ __forceinline__ int64_t block_exclusive_scan256(int64_t v, int64_t* s
   __syncthreads();
   *total = all;
   return before + incl - v;
+}
+
+__device__ __forceinline__ int64_t block_exclusive_scan256(int64_t v, int64_t* scratch,
+                                                           int64_t* total) {
+  return block_exclusive_scan<4>(v, scratch, total);
 }
 
 __device__ __forceinline__ float wave_sum(float v) {

@@ -34,7 +34,8 @@ CASES = [
     # counts, h, f, dtype
     ([60, 0, 13, 100], 64, 128, torch.bfloat16),
     ([130, 1, 0, 64, 200], 128, 192, torch.bfloat16),
-    ([300, 250], 128, 256, torch.bfloat16),          # tall tiles (avg >= 192)
+    ([100, 90, 150, 0, 97], 128, 192, torch.bfloat16),  # 128-row tiles (80 <= avg < 192)
+    ([300, 250], 128, 256, torch.bfloat16),          # 256-row tiles (avg >= 192)
     ([700, 513, 1], 192, 384, torch.bfloat16),       # tallest tiles (avg >= 512)
     ([0, 0, 5], 64, 64, torch.bfloat16),
     ([33, 7, 90], 40, 72, torch.float32),            # fp32 path, odd sizes
