@@ -540,15 +540,20 @@ int pick_bm(int64_t max_rows, int64_t E) {
   return 64;
 }
 
-// Tile bodies (8 waves each; shapes chosen by timing the variants on the
-// five layer shapes with random operands).  FC1 tiles hold BN=128 columns
-// of W_gate and of W_up; FC2 tiles BN=256 columns of W_down.
-using Fc1Body256 = Body<256, 128, 4, 2, true, 4, 32>;
-using Fc1Body128 = Body<128, 128, 4, 2, true, 5, 32>;
-using Fc1Body64 = Body<64, 128, 2, 4, true, 4, 64>;
-using Fc2Body256 = Body<256, 256, 2, 4, false, 4, 32>;
-using Fc2Body128 = Body<128, 256, 4, 2, false, 5, 32>;
-using Fc2Body64 = Body<64, 256, 2, 4, false, 4, 64>;
+// Tile bodies (8 waves each; shapes chosen by timing variants on the five
+// layer shapes with random operands).  All bodies of one launch share the
+// column tiling.  256-row launches (large experts, MFMA-bound): FC1 tiles
+// hold BN=128 columns of W_gate and of W_up, FC2 tiles 256 columns of
+// W_down, and ragged tails run 128- or 64-row bodies.  128- and 64-row
+// launches (small experts, weight-streaming bound) use one body each.
+using Fc1B256 = Body<256, 128, 4, 2, true, 4, 32>;
+using Fc1B128 = Body<128, 128, 4, 2, true, 5, 32>;
+using Fc1B64 = Body<64, 128, 2, 4, true, 4, 64>;
+using Fc1Stream128 = Body<128, 128, 2, 4, true, 3, 64>;
+using Fc2B256 = Body<256, 256, 2, 4, false, 4, 32>;
+using Fc2B128 = Body<128, 256, 4, 2, false, 5, 32>;
+using Fc2B64 = Body<64, 256, 2, 4, false, 4, 64>;
+using Fc2Stream128 = Body<128, 128, 2, 4, false, 4, 64>;
 
 template <bool FC1>
 void launch_gemm(int32_t dtype, const void* A, const void* B0, const void* B1, void* C,
@@ -561,18 +566,18 @@ void launch_gemm(int32_t dtype, const void* A, const void* B0, const void* B1, v
   const int bm = pick_bm(max_rows, E);
   if constexpr (FC1) {
     if (bm == 256)
-      launch_bf16<true, 256, 128, 8, Fc1Body256, Fc1Body128, Fc1Body64>(A, B0, B1, C, counts, E, N, K, max_rows, s);
+      launch_bf16<true, 256, 128, 8, Fc1B256, Fc1B128, Fc1B64>(A, B0, B1, C, counts, E, N, K, max_rows, s);
     else if (bm == 128)
-      launch_bf16<true, 128, 128, 8, Fc1Body256, Fc1Body128, Fc1Body64>(A, B0, B1, C, counts, E, N, K, max_rows, s);
+      launch_bf16<true, 128, 128, 8, Fc1Stream128, Fc1Stream128, Fc1Stream128>(A, B0, B1, C, counts, E, N, K, max_rows, s);
     else
-      launch_bf16<true, 64, 128, 8, Fc1Body256, Fc1Body128, Fc1Body64>(A, B0, B1, C, counts, E, N, K, max_rows, s);
+      launch_bf16<true, 64, 128, 8, Fc1B64, Fc1B64, Fc1B64>(A, B0, B1, C, counts, E, N, K, max_rows, s);
   } else {
     if (bm == 256)
-      launch_bf16<false, 256, 256, 8, Fc2Body256, Fc2Body128, Fc2Body64>(A, B0, B1, C, counts, E, N, K, max_rows, s);
+      launch_bf16<false, 256, 256, 8, Fc2B256, Fc2B128, Fc2B64>(A, B0, B1, C, counts, E, N, K, max_rows, s);
     else if (bm == 128)
-      launch_bf16<false, 128, 256, 8, Fc2Body256, Fc2Body128, Fc2Body64>(A, B0, B1, C, counts, E, N, K, max_rows, s);
+      launch_bf16<false, 128, 128, 8, Fc2Stream128, Fc2Stream128, Fc2Stream128>(A, B0, B1, C, counts, E, N, K, max_rows, s);
     else
-      launch_bf16<false, 64, 256, 8, Fc2Body256, Fc2Body128, Fc2Body64>(A, B0, B1, C, counts, E, N, K, max_rows, s);
+      launch_bf16<false, 64, 256, 8, Fc2B64, Fc2B64, Fc2B64>(A, B0, B1, C, counts, E, N, K, max_rows, s);
   }
 }
 
