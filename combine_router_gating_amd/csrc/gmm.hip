@@ -195,11 +195,13 @@ __device__ __forceinline__ void block_barrier() {
 
 template <int LPW, int STAGES>
 __device__ __forceinline__ void wait_stage(int n_after) {
-  // n_after later stages may stay in flight (n_after <= STAGES - 2)
-  if constexpr (STAGES >= 6) { if (n_after >= 4) { wait_vmcnt<LPW * 4>(); return; } }
-  if constexpr (STAGES >= 5) { if (n_after >= 3) { wait_vmcnt<LPW * 3>(); return; } }
-  if constexpr (STAGES >= 4) { if (n_after >= 2) { wait_vmcnt<LPW * 2>(); return; } }
-  if constexpr (STAGES >= 3) { if (n_after >= 1) { wait_vmcnt<LPW * 1>(); return; } }
+  // wait until at most n_after later stages (of this wave's loads) are in
+  // flight; n_after <= STAGES - 1
+  if constexpr (STAGES >= 6) { if (n_after >= 5) { wait_vmcnt<LPW * 5>(); return; } }
+  if constexpr (STAGES >= 5) { if (n_after >= 4) { wait_vmcnt<LPW * 4>(); return; } }
+  if constexpr (STAGES >= 4) { if (n_after >= 3) { wait_vmcnt<LPW * 3>(); return; } }
+  if constexpr (STAGES >= 3) { if (n_after >= 2) { wait_vmcnt<LPW * 2>(); return; } }
+  if (n_after >= 1) { wait_vmcnt<LPW * 1>(); return; }
   wait_vmcnt<0>();
 }
 
@@ -244,7 +246,7 @@ constexpr int body_lds_bytes() {
 
 // One output tile (BM rows of one expert x BN columns) of the grouped GEMM.
 // `smem` holds the pipeline stages; all 64*WM*WN threads take part.
-template <int BM, int BN, int WM, int WN, bool FC1, int STAGES, int SBK>
+template <int BM, int BN, int WM, int WN, bool FC1, int STAGES, int SBK, bool DEEP>
 __device__ __forceinline__ void gmm_tile(const Tile& tile, char* smem,
                                          const uint16_t* __restrict__ A,
                                          const uint16_t* __restrict__ B0,
@@ -308,44 +310,72 @@ __device__ __forceinline__ void gmm_tile(const Tile& tile, char* smem,
 #pragma unroll
         for (int q = 0; q < 16; ++q) acc[b][mi][ni][q] = 0.f;
 
-  // Pipeline: stages kt+1 .. kt+STAGES-2 are in flight while stage kt is
-  // multiplied; within a stage the fragments of step kk+1 are read from LDS
-  // while the MFMAs of step kk run; before the last step of stage kt the
-  // workgroup waits for stage kt+1, passes a barrier (after which every wave
-  // is done with stage kt-1, whose slot then receives stage kt+STAGES-1),
-  // and prefetches the first fragments of stage kt+1.
   constexpr int KK = SBK / 16;
   const int nk = K / SBK;
+  const int l32 = lane & 31, hi = lane >> 5;
+  bf16x8 ca[MI], cb[NB][NI], na[MI], nb[NB][NI];
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s)
     if (s < nk) issue(s);
-  wait_stage<LPW, STAGES>(min(STAGES - 2, nk - 1));
-  block_barrier();
-
-  const int l32 = lane & 31, hi = lane >> 5;
-  bf16x8 ca[MI], cb[NB][NI], na[MI], nb[NB][NI];
-  load_frags<MI, NB, NI, BM, BN, SBK, WTM, WTN>(ca, cb, smem, 0, wm, wn, l32, hi);
-  for (int kt = 0; kt < nk; ++kt) {
-    const char* st = smem + (kt % STAGES) * STAGE_BYTES;
+  if constexpr (DEEP) {
+    // Memory-depth schedule (weight-streaming bodies): at the top of
+    // iteration kt a barrier frees stage kt-1's slot, stage kt+STAGES-1 is
+    // issued into it, and only stage kt is waited for, so STAGES-1 stages
+    // stay in flight while stage kt is multiplied.  Fragments of step kk+1
+    // are read while the MFMAs of step kk run.
+    for (int kt = 0; kt < nk; ++kt) {
+      block_barrier();
+      if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1);
+      wait_stage<LPW, STAGES>(min(kt + STAGES - 1, nk - 1) - kt);
+      block_barrier();
+      const char* st = smem + (kt % STAGES) * STAGE_BYTES;
+      load_frags<MI, NB, NI, BM, BN, SBK, WTM, WTN>(ca, cb, st, 0, wm, wn, l32, hi);
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      if (kk + 1 < KK) {
-        load_frags<MI, NB, NI, BM, BN, SBK, WTM, WTN>(na, nb, st, kk + 1, wm, wn, l32, hi);
-      } else if (kt + 1 < nk) {
-        const int last = min(kt + STAGES - 2, nk - 1);  // newest stage issued so far
-        wait_stage<LPW, STAGES>(last - (kt + 1));
-        block_barrier();
-        if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1);
-        load_frags<MI, NB, NI, BM, BN, SBK, WTM, WTN>(
-            na, nb, smem + ((kt + 1) % STAGES) * STAGE_BYTES, 0, wm, wn, l32, hi);
+      for (int kk = 0; kk < KK; ++kk) {
+        if (kk + 1 < KK)
+          load_frags<MI, NB, NI, BM, BN, SBK, WTM, WTN>(na, nb, st, kk + 1, wm, wn, l32, hi);
+        mfma_step<MI, NB, NI>(acc, ca, cb);
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi) ca[mi] = na[mi];
+#pragma unroll
+        for (int q = 0; q < NB; ++q)
+#pragma unroll
+          for (int ni = 0; ni < NI; ++ni) cb[q][ni] = nb[q][ni];
       }
-      mfma_step<MI, NB, NI>(acc, ca, cb);
+    }
+  } else {
+    // Compute schedule (MFMA-bound bodies): stages kt+1 .. kt+STAGES-2 are
+    // in flight while stage kt is multiplied; within a stage the fragments
+    // of step kk+1 are read while the MFMAs of step kk run; before the last
+    // step of stage kt the workgroup waits for stage kt+1, passes a barrier
+    // (after which every wave is done with stage kt-1, whose slot then
+    // receives stage kt+STAGES-1), and prefetches the first fragments of
+    // stage kt+1.
+    wait_stage<LPW, STAGES>(min(STAGES - 2, nk - 1));
+    block_barrier();
+    load_frags<MI, NB, NI, BM, BN, SBK, WTM, WTN>(ca, cb, smem, 0, wm, wn, l32, hi);
+    for (int kt = 0; kt < nk; ++kt) {
+      const char* st = smem + (kt % STAGES) * STAGE_BYTES;
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi) ca[mi] = na[mi];
+      for (int kk = 0; kk < KK; ++kk) {
+        if (kk + 1 < KK) {
+          load_frags<MI, NB, NI, BM, BN, SBK, WTM, WTN>(na, nb, st, kk + 1, wm, wn, l32, hi);
+        } else if (kt + 1 < nk) {
+          const int last = min(kt + STAGES - 2, nk - 1);  // newest stage issued so far
+          wait_stage<LPW, STAGES>(last - (kt + 1));
+          block_barrier();
+          if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1);
+          load_frags<MI, NB, NI, BM, BN, SBK, WTM, WTN>(
+              na, nb, smem + ((kt + 1) % STAGES) * STAGE_BYTES, 0, wm, wn, l32, hi);
+        }
+        mfma_step<MI, NB, NI>(acc, ca, cb);
 #pragma unroll
-      for (int q = 0; q < NB; ++q)
+        for (int mi = 0; mi < MI; ++mi) ca[mi] = na[mi];
 #pragma unroll
-        for (int ni = 0; ni < NI; ++ni) cb[q][ni] = nb[q][ni];
+        for (int q = 0; q < NB; ++q)
+#pragma unroll
+          for (int ni = 0; ni < NI; ++ni) cb[q][ni] = nb[q][ni];
+      }
     }
   }
 
@@ -418,13 +448,13 @@ __global__ void __launch_bounds__(NW * 64) gmm_bf16_kernel(
   }
 }
 
-template <int BM, int BN, int WM, int WN, bool FC1, int STAGES, int SBK>
+template <int BM, int BN, int WM, int WN, bool FC1, int STAGES, int SBK, bool DEEP = false>
 struct Body {
   static constexpr int lds = body_lds_bytes<BM, BN, FC1, STAGES, SBK>();
   __device__ __forceinline__ static void run(const Tile& t, char* smem, const uint16_t* A,
                                              const uint16_t* B0, const uint16_t* B1, uint16_t* C,
                                              int N, int K) {
-    gmm_tile<BM, BN, WM, WN, FC1, STAGES, SBK>(t, smem, A, B0, B1, C, N, K);
+    gmm_tile<BM, BN, WM, WN, FC1, STAGES, SBK, DEEP>(t, smem, A, B0, B1, C, N, K);
   }
 };
 
@@ -549,7 +579,7 @@ int pick_bm(int64_t max_rows, int64_t E) {
 using Fc1B256 = Body<256, 128, 4, 2, true, 4, 32>;
 using Fc1B128 = Body<128, 128, 4, 2, true, 5, 32>;
 using Fc1B64 = Body<64, 128, 2, 4, true, 4, 64>;
-using Fc1Stream128 = Body<128, 128, 2, 4, true, 3, 64>;
+using Fc1Stream128 = Body<128, 128, 2, 4, true, 3, 64, true>;
 using Fc2B256 = Body<256, 256, 2, 4, false, 4, 32>;
 using Fc2B128 = Body<128, 256, 4, 2, false, 5, 32>;
 using Fc2B64 = Body<64, 256, 2, 4, false, 4, 64>;

@@ -104,10 +104,11 @@ __global__ void __launch_bounds__(256) router_logits_simt(const XT* __restrict__
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ void split3(const float4 a, const float4 b, u32x4_t& hi, u32x4_t& mi,
+__device__ __forceinline__ void split3(const f32x4_t a, const f32x4_t b, u32x4_t& hi, u32x4_t& mi,
                                        u32x4_t& lo) {
-  const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  const float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
   uint32_t h16[8], m16[8], l16[8];
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
@@ -153,25 +154,42 @@ __global__ void __launch_bounds__(256) router_logits_mfma(const uint16_t* __rest
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
-  for (int k = kb; k < ke; k += 16) {
-    const bf16x8_t xb0 = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(xr0 + k));
-    const bf16x8_t xb1 = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(xr1 + k));
-    u32x4_t hi[2], mi[2], lo[2];
-    split3(*reinterpret_cast<const float4*>(wr0 + k), *reinterpret_cast<const float4*>(wr0 + k + 4),
-           hi[0], mi[0], lo[0]);
-    split3(*reinterpret_cast<const float4*>(wr1 + k), *reinterpret_cast<const float4*>(wr1 + k + 4),
-           hi[1], mi[1], lo[1]);
+  // Loads of RB consecutive 16-wide k steps are issued before their MFMAs,
+  // so RB memory latencies overlap.  Steps past the chunk end load a valid
+  // clamped address and are skipped (uniform branch).
+  constexpr int RB = 4;
+  for (int k = kb; k < ke; k += 16 * RB) {
+    u32x4_t xv[RB][2];
+    f32x4_t wv[RB][2][2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const bf16x8_t a0 = __builtin_bit_cast(bf16x8_t, hi[i]);
-      const bf16x8_t a1 = __builtin_bit_cast(bf16x8_t, mi[i]);
-      const bf16x8_t a2 = __builtin_bit_cast(bf16x8_t, lo[i]);
-      acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, xb0, acc[i][0], 0, 0, 0);
-      acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, xb1, acc[i][1], 0, 0, 0);
-      acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, xb0, acc[i][0], 0, 0, 0);
-      acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, xb1, acc[i][1], 0, 0, 0);
-      acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2, xb0, acc[i][0], 0, 0, 0);
-      acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2, xb1, acc[i][1], 0, 0, 0);
+    for (int s = 0; s < RB; ++s) {
+      const int kk = min(k + 16 * s, ke - 16);
+      xv[s][0] = *reinterpret_cast<const u32x4_t*>(xr0 + kk);
+      xv[s][1] = *reinterpret_cast<const u32x4_t*>(xr1 + kk);
+      wv[s][0][0] = *reinterpret_cast<const f32x4_t*>(wr0 + kk);
+      wv[s][0][1] = *reinterpret_cast<const f32x4_t*>(wr0 + kk + 4);
+      wv[s][1][0] = *reinterpret_cast<const f32x4_t*>(wr1 + kk);
+      wv[s][1][1] = *reinterpret_cast<const f32x4_t*>(wr1 + kk + 4);
+    }
+#pragma unroll
+    for (int s = 0; s < RB; ++s) {
+      if (k + 16 * s >= ke) break;
+      const bf16x8_t xb0 = __builtin_bit_cast(bf16x8_t, xv[s][0]);
+      const bf16x8_t xb1 = __builtin_bit_cast(bf16x8_t, xv[s][1]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        u32x4_t hi, mi, lo;
+        split3(wv[s][i][0], wv[s][i][1], hi, mi, lo);
+        const bf16x8_t a0 = __builtin_bit_cast(bf16x8_t, hi);
+        const bf16x8_t a1 = __builtin_bit_cast(bf16x8_t, mi);
+        const bf16x8_t a2 = __builtin_bit_cast(bf16x8_t, lo);
+        acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, xb0, acc[i][0], 0, 0, 0);
+        acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, xb1, acc[i][1], 0, 0, 0);
+        acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, xb0, acc[i][0], 0, 0, 0);
+        acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, xb1, acc[i][1], 0, 0, 0);
+        acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2, xb0, acc[i][0], 0, 0, 0);
+        acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2, xb1, acc[i][1], 0, 0, 0);
+      }
     }
   }
   // lane holds [token l32 of block j][experts 8g + 4*(lane/32) + q of block i]
@@ -192,6 +210,8 @@ __global__ void __launch_bounds__(256) router_logits_mfma(const uint16_t* __rest
   }
 }
 
+constexpr int kMaxSplit = 8;  // partial-logit planes at most
+
 struct MfmaPlan {
   int wt, we;
   int64_t gx, gz;
@@ -207,7 +227,7 @@ MfmaPlan mfma_plan(int64_t T, int64_t h, int64_t E) {
   p.gx = ceil_div(T, 64 * p.wt);
   p.gz = ceil_div(E, 64 * p.we);
   const int64_t base = p.gx * p.gz;
-  int64_t ks = std::min<int64_t>(8, std::max<int64_t>(1, ceil_div(512, base)));
+  int64_t ks = std::min<int64_t>(kMaxSplit, std::max<int64_t>(1, ceil_div(512, base)));
   ks = std::min<int64_t>(ks, std::max<int64_t>(1, h / 128));
   p.kchunk = static_cast<int>(ceil_div(ceil_div(h, ks), 16) * 16);
   p.ksplit = static_cast<int>(ceil_div(h, p.kchunk));
@@ -271,8 +291,31 @@ __global__ void __launch_bounds__(256) router_topk_kernel(
   for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;
   __syncthreads();
   constexpr int kTokPerWave = kCountBlock / 4;
+  // Phase 1: logits of all of this wave's tokens (every partial plane is
+  // loaded before any is summed; planes are summed in order, then the bias).
+  float lt[kTokPerWave][EPL];
+  const int64_t tw = static_cast<int64_t>(blockIdx.x) * kCountBlock + wave * kTokPerWave;
+#pragma unroll
   for (int it = 0; it < kTokPerWave; ++it) {
-    const int64_t t = static_cast<int64_t>(blockIdx.x) * kCountBlock + wave * kTokPerWave + it;
+    const int64_t t = min(tw + it, T - 1);  // clamped; tokens past T are skipped below
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+      const int e = min(lane + 64 * j, E - 1);
+      const int64_t idx = t * E + e;
+      float pv[kMaxSplit];
+#pragma unroll
+      for (int sp = 0; sp < kMaxSplit; ++sp) pv[sp] = sp < nsplit ? part[sp * T * E + idx] : 0.f;
+      float v = pv[0];
+#pragma unroll
+      for (int sp = 1; sp < kMaxSplit; ++sp)
+        if (sp < nsplit) v += pv[sp];
+      if (bias) v += bias[e];
+      lt[it][j] = v;
+    }
+  }
+#pragma unroll
+  for (int it = 0; it < kTokPerWave; ++it) {
+    const int64_t t = tw + it;
     if (t >= T) break;  // wave-uniform
     float l[EPL], s[EPL], key[EPL];
     bool valid[EPL], taken[EPL];
@@ -281,16 +324,8 @@ __global__ void __launch_bounds__(256) router_topk_kernel(
       const int e = lane + 64 * j;
       valid[j] = e < E;
       taken[j] = false;
-      if (valid[j]) {
-        const int64_t idx = t * E + e;
-        float v = part[idx];
-        for (int sp = 1; sp < nsplit; ++sp) v += part[sp * T * E + idx];  // fixed order
-        if (bias) v += bias[e];
-        l[j] = v;
-        if (logits_out) logits_out[idx] = v;
-      } else {
-        l[j] = -INFINITY;
-      }
+      l[j] = valid[j] ? lt[it][j] : -INFINITY;
+      if (valid[j] && logits_out) logits_out[t * E + e] = l[j];
     }
     if (score == MOE_SCORE_SOFTMAX) {
       float m = -INFINITY;
