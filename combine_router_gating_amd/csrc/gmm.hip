@@ -138,9 +138,7 @@ __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f +
 template <int SBK>
 __device__ __forceinline__ uint32_t lds_chunk_byte(int row, int c) {
   if constexpr (SBK == 32) {
-    const int line = row >> 1;
-    const int lc = ((row & 1) << 2) | c;
-    return static_cast<uint32_t>(line * 128 + ((lc ^ ((line >> 1) & 3)) << 4));
+    return lds_swz64b(row, c);
   } else if constexpr (SBK == 64) {
     return static_cast<uint32_t>(row * 128 + ((c ^ ((row >> 1) & 7)) << 4));
   } else {
@@ -186,6 +184,16 @@ __device__ __forceinline__ void wait_vmcnt() {
   // lgkmcnt left at their maxima (no wait)
   __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
 }
+
+__device__ __forceinline__ void wait_lgkm0() {
+  // lgkmcnt(0); vmcnt and expcnt left at their maxima
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
+}
+
+// Pipeline schedules of a tile body (see gmm_tile).
+constexpr int kSchedCompute = 0;
+constexpr int kSchedDeep = 1;
+constexpr int kSchedReg = 2;
 
 __device__ __forceinline__ void block_barrier() {
   asm volatile("" ::: "memory");
@@ -246,7 +254,7 @@ constexpr int body_lds_bytes() {
 
 // One output tile (BM rows of one expert x BN columns) of the grouped GEMM.
 // `smem` holds the pipeline stages; all 64*WM*WN threads take part.
-template <int BM, int BN, int WM, int WN, bool FC1, int STAGES, int SBK, bool DEEP>
+template <int BM, int BN, int WM, int WN, bool FC1, int STAGES, int SBK, int SCHED>
 __device__ __forceinline__ void gmm_tile(const Tile& tile, char* smem,
                                          const uint16_t* __restrict__ A,
                                          const uint16_t* __restrict__ B0,
@@ -263,7 +271,8 @@ __device__ __forceinline__ void gmm_tile(const Tile& tile, char* smem,
   static_assert(MI >= 1 && NI >= 1, "wave tile must be at least 32x32");
   static_assert(STAGE_BYTES % (NW * 1024) == 0, "whole direct loads per wave");
   static_assert(SBK == 32 || SBK == 64 || SBK == 128 || SBK == 256, "k slab per stage");
-  static_assert(STAGES >= 3 && STAGES <= 6, "pipeline depth");
+  static_assert((SCHED == kSchedReg && STAGES == 2) || (SCHED != kSchedReg && STAGES >= 3 && STAGES <= 6),
+                "pipeline depth");
 
   const int n0 = tile.n0 * BN;
   const int tid = threadIdx.x;
@@ -314,10 +323,54 @@ __device__ __forceinline__ void gmm_tile(const Tile& tile, char* smem,
   const int nk = K / SBK;
   const int l32 = lane & 31, hi = lane >> 5;
   bf16x8 ca[MI], cb[NB][NI], na[MI], nb[NB][NI];
+  if constexpr (SCHED != kSchedReg) {
 #pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s)
-    if (s < nk) issue(s);
-  if constexpr (DEEP) {
+    for (int s = 0; s < STAGES - 1; ++s)
+      if (s < nk) issue(s);
+  }
+  if constexpr (SCHED == kSchedReg) {
+    // Register-staged schedule: two LDS slots; stage kt+1 waits in registers
+    // (ordinary 16-byte global loads) while stage kt is multiplied, is
+    // written to LDS after it, and stage kt+2's loads are issued behind the
+    // barrier.
+    u32x4 rg[LPW];
+    const int piece = wave * LPW * 1024 + lane * 16;
+    auto gload = [&](int kt) {
+      const int64_t ko = static_cast<int64_t>(kt) * SBK;
+#pragma unroll
+      for (int j = 0; j < LPW; ++j) rg[j] = *reinterpret_cast<const u32x4*>(src[j] + ko);
+    };
+    auto sstore = [&](int slot) {
+      char* d = smem + slot * STAGE_BYTES + piece;
+#pragma unroll
+      for (int j = 0; j < LPW; ++j) *reinterpret_cast<u32x4*>(d + j * 1024) = rg[j];
+    };
+    gload(0);
+    sstore(0);
+    if (nk > 1) gload(1);
+    wait_lgkm0();
+    block_barrier();
+    for (int kt = 0; kt < nk; ++kt) {
+      const char* st = smem + (kt & 1) * STAGE_BYTES;
+      load_frags<MI, NB, NI, BM, BN, SBK, WTM, WTN>(ca, cb, st, 0, wm, wn, l32, hi);
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        if (kk + 1 < KK)
+          load_frags<MI, NB, NI, BM, BN, SBK, WTM, WTN>(na, nb, st, kk + 1, wm, wn, l32, hi);
+        mfma_step<MI, NB, NI>(acc, ca, cb);
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi) ca[mi] = na[mi];
+#pragma unroll
+        for (int q = 0; q < NB; ++q)
+#pragma unroll
+          for (int ni = 0; ni < NI; ++ni) cb[q][ni] = nb[q][ni];
+      }
+      if (kt + 1 < nk) sstore((kt + 1) & 1);
+      wait_lgkm0();
+      block_barrier();
+      if (kt + 2 < nk) gload(kt + 2);
+    }
+  } else if constexpr (SCHED == kSchedDeep) {
     // Memory-depth schedule (weight-streaming bodies): at the top of
     // iteration kt a barrier frees stage kt-1's slot, stage kt+STAGES-1 is
     // issued into it, and only stage kt is waited for, so STAGES-1 stages
@@ -448,13 +501,13 @@ __global__ void __launch_bounds__(NW * 64) gmm_bf16_kernel(
   }
 }
 
-template <int BM, int BN, int WM, int WN, bool FC1, int STAGES, int SBK, bool DEEP = false>
+template <int BM, int BN, int WM, int WN, bool FC1, int STAGES, int SBK, int SCHED = kSchedCompute>
 struct Body {
   static constexpr int lds = body_lds_bytes<BM, BN, FC1, STAGES, SBK>();
   __device__ __forceinline__ static void run(const Tile& t, char* smem, const uint16_t* A,
                                              const uint16_t* B0, const uint16_t* B1, uint16_t* C,
                                              int N, int K) {
-    gmm_tile<BM, BN, WM, WN, FC1, STAGES, SBK, DEEP>(t, smem, A, B0, B1, C, N, K);
+    gmm_tile<BM, BN, WM, WN, FC1, STAGES, SBK, SCHED>(t, smem, A, B0, B1, C, N, K);
   }
 };
 
@@ -579,7 +632,7 @@ int pick_bm(int64_t max_rows, int64_t E) {
 using Fc1B256 = Body<256, 128, 4, 2, true, 4, 32>;
 using Fc1B128 = Body<128, 128, 4, 2, true, 5, 32>;
 using Fc1B64 = Body<64, 128, 2, 4, true, 4, 64>;
-using Fc1Stream128 = Body<128, 128, 2, 4, true, 3, 64, true>;
+using Fc1Stream128 = Body<128, 128, 2, 4, true, 3, 64, kSchedDeep>;
 using Fc2B256 = Body<256, 256, 2, 4, false, 4, 32>;
 using Fc2B128 = Body<128, 256, 4, 2, false, 5, 32>;
 using Fc2B64 = Body<64, 256, 2, 4, false, 4, 64>;

@@ -82,6 +82,17 @@ __device__ __forceinline__ int64_t block_exclusive_scan256(int64_t v, int64_t* s
   return block_exclusive_scan<4>(v, scratch, total);
 }
 
+// LDS layout for tiles of 64-byte rows (32 bf16 of k) read as 16-byte MFMA
+// fragments: rows 2L and 2L+1 share 128-byte line L, and logical chunk
+// lc = (row & 1) * 4 + c (c = 0..3) sits at physical chunk lc ^ ((L >> 1) & 3),
+// so 16 lanes reading one chunk of 16 consecutive rows hit 16 different
+// 16-byte bank groups (gfx950: 64 banks of 4 bytes, 16 lanes per cycle).
+__device__ __forceinline__ uint32_t lds_swz64b(int row, int c) {
+  const int line = row >> 1;
+  const int lc = ((row & 1) << 2) | c;
+  return static_cast<uint32_t>(line * 128 + ((lc ^ ((line >> 1) & 3)) << 4));
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);

@@ -9,9 +9,10 @@
 // leave both the map and the probs.
 //
 // Kernels, in launch order:
-//   router_logits_mfma     bf16 x: x w^T on bf16 MFMA with the fp32 weight split
-//                          exactly into three bf16 parts (fp32-accurate), split
-//                          over h into partial sums (more workgroups)
+//   router_logits_lds      bf16 x: x w^T on bf16 MFMA with the fp32 weight split
+//                          exactly into three bf16 parts (fp32-accurate), both
+//                          operands staged through LDS, split over h into
+//                          partial sums (more workgroups)
 //   router_logits_simt     fp32 x (or h not a multiple of 16): fp32 FMA, LDS-tiled
 //   router_topk_kernel     one wave per token: logits = partials summed in a
 //                          fixed order (+ b), scores, K rounds of a wave-wide
@@ -98,55 +99,95 @@ __global__ void __launch_bounds__(256) router_logits_simt(const XT* __restrict__
 //
 // A wave owns 64 tokens x 64 experts (2x2 blocks of v_mfma_f32_32x32x16_bf16,
 // three MFMAs per block per 16-wide k step); the 4 waves of a workgroup tile
-// WT x WE such blocks.  Operands come straight from global memory (each
-// lane's 8 consecutive k values are contiguous); blockIdx.y selects a slice
-// of h whose partial sums go to their own [T, E] plane.
+// WT x WE such blocks.  blockIdx.y selects a slice of h whose partial sums go
+// to their own [T, E] plane.
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ void split3(const f32x4_t a, const f32x4_t b, u32x4_t& hi, u32x4_t& mi,
-                                       u32x4_t& lo) {
-  const float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-  uint32_t h16[8], m16[8], l16[8];
+// Split four fp32 weights into their hi/mid/lo bf16 parts, packed as 4 bf16
+// (8 bytes) per part.
+__device__ __forceinline__ void split4(const f32x4_t v, uint2& hi, uint2& mi, uint2& lo) {
+  uint32_t h16[4], m16[4], l16[4];
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
+  for (int q = 0; q < 4; ++q) {
     const uint32_t u = __float_as_uint(v[q]);
     const uint32_t hb = u & 0xffff0000u;
     const float r1 = v[q] - __uint_as_float(hb);
-    const uint32_t u1 = __float_as_uint(r1);
-    const uint32_t mb = u1 & 0xffff0000u;
+    const uint32_t mb = __float_as_uint(r1) & 0xffff0000u;
     const float r2 = r1 - __uint_as_float(mb);
     h16[q] = hb >> 16;
     m16[q] = mb >> 16;
     l16[q] = __float_as_uint(r2) >> 16;
   }
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    hi[p] = h16[2 * p] | (h16[2 * p + 1] << 16);
-    mi[p] = m16[2 * p] | (m16[2 * p + 1] << 16);
-    lo[p] = l16[2 * p] | (l16[2 * p + 1] << 16);
-  }
+  hi = make_uint2(h16[0] | (h16[1] << 16), h16[2] | (h16[3] << 16));
+  mi = make_uint2(m16[0] | (m16[1] << 16), m16[2] | (m16[3] << 16));
+  lo = make_uint2(l16[0] | (l16[1] << 16), l16[2] | (l16[3] << 16));
 }
 
+// Gating linear on MFMA with LDS staging.  A workgroup owns BT = 64*WT
+// tokens x BE = 64*WE experts over one slice of h; each 32-wide k slab of x
+// (BT rows) and of the weight (BE rows, split into three bf16 planes while
+// it is staged) is loaded once with coalesced row loads into LDS (two
+// slots: slab s+1 waits in registers while slab s is multiplied), and each
+// wave reads its 64x64 fragments from LDS.
 template <int WT, int WE>
-__global__ void __launch_bounds__(256) router_logits_mfma(const uint16_t* __restrict__ x,
-                                                          const float* __restrict__ w,
-                                                          float* __restrict__ part, int64_t T,
-                                                          int h, int E, int kchunk) {
+__global__ void __launch_bounds__(256) router_logits_lds(const uint16_t* __restrict__ x,
+                                                         const float* __restrict__ w,
+                                                         float* __restrict__ part, int64_t T,
+                                                         int h, int E, int kchunk) {
   static_assert(WT * WE == 4, "4 waves");
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int BT = 64 * WT, BE = 64 * WE;
+  constexpr int ROWS = BT + 3 * BE;          // x rows, then planes hi, mid, lo
+  constexpr int STAGE = ROWS * 64;           // 32 bf16 (64 bytes) per row
+  constexpr int XP = BT * 4 / 256;           // 16-byte x pieces per thread per slab
+  constexpr int WP = BE * 8 / 256;           // 4-float weight pieces per thread per slab
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wt = wave / WE, we = wave % WE;
-  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * (64 * WT) + wt * 64;
-  const int e0 = blockIdx.z * (64 * WE) + we * 64;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * BT;
+  const int e0 = blockIdx.z * BE;
   const int kb = blockIdx.y * kchunk;
-  const int ke = min(h, kb + kchunk);
-  const int l32 = lane & 31, koff = (lane >> 5) * 8;
-  const uint16_t* xr0 = x + min(t0 + l32, T - 1) * h + koff;
-  const uint16_t* xr1 = x + min(t0 + 32 + l32, T - 1) * h + koff;
-  const float* wr0 = w + static_cast<int64_t>(min(e0 + l32, E - 1)) * h + koff;
-  const float* wr1 = w + static_cast<int64_t>(min(e0 + 32 + l32, E - 1)) * h + koff;
+  const int nsl = (min(h, kb + kchunk) - kb) / 32;
+  const uint16_t* xsrc[XP];
+  const float* wsrc[WP];
+#pragma unroll
+  for (int i = 0; i < XP; ++i) {
+    const int p = tid + 256 * i, r = p >> 2, c = p & 3;
+    xsrc[i] = x + min(t0 + r, T - 1) * h + kb + c * 8;
+  }
+#pragma unroll
+  for (int i = 0; i < WP; ++i) {
+    const int p = tid + 256 * i, r = p >> 3, c8 = p & 7;
+    wsrc[i] = w + static_cast<int64_t>(min(e0 + r, E - 1)) * h + kb + c8 * 4;
+  }
+  u32x4_t rx[XP];
+  f32x4_t rw[WP];
+  auto gload = [&](int sl) {
+#pragma unroll
+    for (int i = 0; i < XP; ++i) rx[i] = *reinterpret_cast<const u32x4_t*>(xsrc[i] + sl * 32);
+#pragma unroll
+    for (int i = 0; i < WP; ++i) rw[i] = *reinterpret_cast<const f32x4_t*>(wsrc[i] + sl * 32);
+  };
+  auto sstore = [&](int slot) {
+    char* st = smem + slot * STAGE;
+#pragma unroll
+    for (int i = 0; i < XP; ++i) {
+      const int p = tid + 256 * i;
+      *reinterpret_cast<u32x4_t*>(st + lds_swz64b(p >> 2, p & 3)) = rx[i];
+    }
+#pragma unroll
+    for (int i = 0; i < WP; ++i) {
+      const int p = tid + 256 * i, r = p >> 3, c8 = p & 7;
+      uint2 ph, pm, pl;
+      split4(rw[i], ph, pm, pl);
+      *reinterpret_cast<uint2*>(st + lds_swz64b(BT + r, c8 >> 1) + (c8 & 1) * 8) = ph;
+      *reinterpret_cast<uint2*>(st + lds_swz64b(BT + BE + r, c8 >> 1) + (c8 & 1) * 8) = pm;
+      *reinterpret_cast<uint2*>(st + lds_swz64b(BT + 2 * BE + r, c8 >> 1) + (c8 & 1) * 8) = pl;
+    }
+  };
   f32x16_t acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -154,55 +195,51 @@ __global__ void __launch_bounds__(256) router_logits_mfma(const uint16_t* __rest
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
-  // Loads of RB consecutive 16-wide k steps are issued before their MFMAs,
-  // so RB memory latencies overlap.  Steps past the chunk end load a valid
-  // clamped address and are skipped (uniform branch).
-  constexpr int RB = 4;
-  for (int k = kb; k < ke; k += 16 * RB) {
-    u32x4_t xv[RB][2];
-    f32x4_t wv[RB][2][2];
+  const int l32 = lane & 31, hi = lane >> 5;
+  gload(0);
+  sstore(0);
+  if (nsl > 1) gload(1);
+  __syncthreads();
+  for (int sl = 0; sl < nsl; ++sl) {
+    const char* st = smem + (sl & 1) * STAGE;
 #pragma unroll
-    for (int s = 0; s < RB; ++s) {
-      const int kk = min(k + 16 * s, ke - 16);
-      xv[s][0] = *reinterpret_cast<const u32x4_t*>(xr0 + kk);
-      xv[s][1] = *reinterpret_cast<const u32x4_t*>(xr1 + kk);
-      wv[s][0][0] = *reinterpret_cast<const f32x4_t*>(wr0 + kk);
-      wv[s][0][1] = *reinterpret_cast<const f32x4_t*>(wr0 + kk + 4);
-      wv[s][1][0] = *reinterpret_cast<const f32x4_t*>(wr1 + kk);
-      wv[s][1][1] = *reinterpret_cast<const f32x4_t*>(wr1 + kk + 4);
+    for (int kk = 0; kk < 2; ++kk) {
+      const int c = kk * 2 + hi;
+      bf16x8_t xb[2], wb[3][2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        xb[j] = *reinterpret_cast<const bf16x8_t*>(st + lds_swz64b(wt * 64 + j * 32 + l32, c));
+#pragma unroll
+      for (int pl = 0; pl < 3; ++pl)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          wb[pl][i] = *reinterpret_cast<const bf16x8_t*>(
+              st + lds_swz64b(BT + pl * BE + we * 64 + i * 32 + l32, c));
+#pragma unroll
+      for (int pl = 0; pl < 3; ++pl)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wb[pl][i], xb[j], acc[i][j], 0, 0, 0);
     }
-#pragma unroll
-    for (int s = 0; s < RB; ++s) {
-      if (k + 16 * s >= ke) break;
-      const bf16x8_t xb0 = __builtin_bit_cast(bf16x8_t, xv[s][0]);
-      const bf16x8_t xb1 = __builtin_bit_cast(bf16x8_t, xv[s][1]);
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        u32x4_t hi, mi, lo;
-        split3(wv[s][i][0], wv[s][i][1], hi, mi, lo);
-        const bf16x8_t a0 = __builtin_bit_cast(bf16x8_t, hi);
-        const bf16x8_t a1 = __builtin_bit_cast(bf16x8_t, mi);
-        const bf16x8_t a2 = __builtin_bit_cast(bf16x8_t, lo);
-        acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, xb0, acc[i][0], 0, 0, 0);
-        acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, xb1, acc[i][1], 0, 0, 0);
-        acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, xb0, acc[i][0], 0, 0, 0);
-        acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, xb1, acc[i][1], 0, 0, 0);
-        acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2, xb0, acc[i][0], 0, 0, 0);
-        acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2, xb1, acc[i][1], 0, 0, 0);
-      }
-    }
+    if (sl + 1 < nsl) sstore((sl + 1) & 1);
+    __syncthreads();
+    if (sl + 2 < nsl) gload(sl + 2);
   }
   // lane holds [token l32 of block j][experts 8g + 4*(lane/32) + q of block i]
   float* out = part + static_cast<int64_t>(blockIdx.y) * T * E;
+  const int64_t tw = t0 + wt * 64;
+  const int ew = e0 + we * 64;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const int64_t t = t0 + j * 32 + l32;
+    const int64_t t = tw + j * 32 + l32;
     if (t >= T) continue;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int e = e0 + i * 32 + g * 8 + (lane >> 5) * 4;
+        const int e = ew + i * 32 + g * 8 + hi * 4;
 #pragma unroll
         for (int q = 0; q < 4; ++q)
           if (e + q < E) out[t * E + e + q] = acc[i][j][g * 4 + q];
@@ -229,12 +266,12 @@ MfmaPlan mfma_plan(int64_t T, int64_t h, int64_t E) {
   const int64_t base = p.gx * p.gz;
   int64_t ks = std::min<int64_t>(kMaxSplit, std::max<int64_t>(1, ceil_div(512, base)));
   ks = std::min<int64_t>(ks, std::max<int64_t>(1, h / 128));
-  p.kchunk = static_cast<int>(ceil_div(ceil_div(h, ks), 16) * 16);
+  p.kchunk = static_cast<int>(ceil_div(ceil_div(h, ks), 32) * 32);
   p.ksplit = static_cast<int>(ceil_div(h, p.kchunk));
   return p;
 }
 
-bool use_mfma(const moe_route_desc* d) { return d->x_dtype == MOE_BF16 && d->h % 16 == 0; }
+bool use_mfma(const moe_route_desc* d) { return d->x_dtype == MOE_BF16 && d->h % 32 == 0; }
 
 // ------------------------------------------------------- fixed fp32 sigmoid
 // exp(y) for y <= 0 by a fixed sequence of IEEE fp32 operations, each rounded
@@ -570,13 +607,13 @@ extern "C" moe_status moe_route(const moe_route_desc* d, const void* x, const fl
     const uint16_t* xb = static_cast<const uint16_t*>(x);
     const int hh = static_cast<int>(d->h), Ei = static_cast<int>(E);
     if (p.we == 1)
-      hipLaunchKernelGGL((router_logits_mfma<4, 1>), grid, dim3(256), 0, s, xb, w_router, part_ws,
+      hipLaunchKernelGGL((router_logits_lds<4, 1>), grid, dim3(256), 0, s, xb, w_router, part_ws,
                          T, hh, Ei, p.kchunk);
     else if (p.we == 2)
-      hipLaunchKernelGGL((router_logits_mfma<2, 2>), grid, dim3(256), 0, s, xb, w_router, part_ws,
+      hipLaunchKernelGGL((router_logits_lds<2, 2>), grid, dim3(256), 0, s, xb, w_router, part_ws,
                          T, hh, Ei, p.kchunk);
     else
-      hipLaunchKernelGGL((router_logits_mfma<1, 4>), grid, dim3(256), 0, s, xb, w_router, part_ws,
+      hipLaunchKernelGGL((router_logits_lds<1, 4>), grid, dim3(256), 0, s, xb, w_router, part_ws,
                          T, hh, Ei, p.kchunk);
     ta.part = part_ws;
     ta.nsplit = p.ksplit;
