@@ -194,6 +194,7 @@ __device__ __forceinline__ void wait_lgkm0() {
 constexpr int kSchedCompute = 0;
 constexpr int kSchedDeep = 1;
 constexpr int kSchedReg = 2;
+constexpr int kSchedRing = 3;
 
 __device__ __forceinline__ void block_barrier() {
   asm volatile("" ::: "memory");
@@ -246,6 +247,31 @@ __device__ __forceinline__ void mfma_step(f32x16 (&acc)[NB][MI][NI], const bf16x
             __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[nb][ni], a[mi], acc[nb][mi][ni], 0, 0, 0);
 }
 
+// mfma_step that also issues direct loads between the MFMAs: after the
+// MFMA at position p0 + i (counted from the last barrier) piece j of the
+// pending stage is issued when p0 + i == j * SPREAD.  Callers pass p0 from
+// fully unrolled loops, so the position tests fold to constants; the
+// scheduling barrier keeps each load between its two MFMAs.
+template <int MI, int NB, int NI, int SPREAD, int LPW, class Issue>
+__device__ __forceinline__ void mfma_step_dma(f32x16 (&acc)[NB][MI][NI], const bf16x8 (&a)[MI],
+                                              const bf16x8 (&b)[NB][NI], int p0, bool pending,
+                                              const Issue& issue_piece) {
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) {
+        acc[nb][mi][ni] =
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[nb][ni], a[mi], acc[nb][mi][ni], 0, 0, 0);
+        const int pos = p0 + (nb * MI + mi) * NI + ni;
+        if (pos % SPREAD == 0 && pos / SPREAD < LPW) {
+          if (pending) issue_piece(pos / SPREAD);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+}
+
 // LDS bytes one tile body uses.
 template <int BM, int BN, bool FC1, int STAGES, int SBK>
 constexpr int body_lds_bytes() {
@@ -254,7 +280,7 @@ constexpr int body_lds_bytes() {
 
 // One output tile (BM rows of one expert x BN columns) of the grouped GEMM.
 // `smem` holds the pipeline stages; all 64*WM*WN threads take part.
-template <int BM, int BN, int WM, int WN, bool FC1, int STAGES, int SBK, int SCHED>
+template <int BM, int BN, int WM, int WN, bool FC1, int STAGES, int SBK, int SCHED, int SPREAD>
 __device__ __forceinline__ void gmm_tile(const Tile& tile, char* smem,
                                          const uint16_t* __restrict__ A,
                                          const uint16_t* __restrict__ B0,
@@ -271,7 +297,8 @@ __device__ __forceinline__ void gmm_tile(const Tile& tile, char* smem,
   static_assert(MI >= 1 && NI >= 1, "wave tile must be at least 32x32");
   static_assert(STAGE_BYTES % (NW * 1024) == 0, "whole direct loads per wave");
   static_assert(SBK == 32 || SBK == 64 || SBK == 128 || SBK == 256, "k slab per stage");
-  static_assert((SCHED == kSchedReg && STAGES == 2) || (SCHED != kSchedReg && STAGES >= 3 && STAGES <= 6),
+  static_assert((SCHED == kSchedReg && STAGES == 2) || (SCHED == kSchedRing && STAGES >= 2 && STAGES <= 6) ||
+                    (SCHED != kSchedReg && SCHED != kSchedRing && STAGES >= 3 && STAGES <= 6),
                 "pipeline depth");
 
   const int n0 = tile.n0 * BN;
@@ -323,7 +350,11 @@ __device__ __forceinline__ void gmm_tile(const Tile& tile, char* smem,
   const int nk = K / SBK;
   const int l32 = lane & 31, hi = lane >> 5;
   bf16x8 ca[MI], cb[NB][NI], na[MI], nb[NB][NI];
-  if constexpr (SCHED != kSchedReg) {
+  if constexpr (SCHED == kSchedRing) {
+#pragma unroll
+    for (int s = 0; s < STAGES; ++s)
+      if (s < nk) issue(s);
+  } else if constexpr (SCHED != kSchedReg) {
 #pragma unroll
     for (int s = 0; s < STAGES - 1; ++s)
       if (s < nk) issue(s);
@@ -369,6 +400,62 @@ __device__ __forceinline__ void gmm_tile(const Tile& tile, char* smem,
       wait_lgkm0();
       block_barrier();
       if (kt + 2 < nk) gload(kt + 2);
+    }
+  } else if constexpr (SCHED == kSchedRing) {
+    // Ring schedule: every slot holds a stage in flight or being multiplied.
+    // Before the last 16-wide step of stage kt each wave has read all of
+    // stage kt's fragments into registers (lgkmcnt 0); the workgroup waits
+    // for stage kt+1 and passes a barrier, after which stage kt's slot
+    // receives stage kt+STAGES and the first fragments of stage kt+1 are
+    // read while the last MFMAs of stage kt run.  With SPREAD > 0 the
+    // stage's direct loads are not issued at once after the barrier but one
+    // every SPREAD MFMAs, so that a wave stalled on a full memory queue
+    // still has MFMAs in flight.
+    constexpr int MPK = NB * MI * NI;  // MFMAs per 16-wide step
+    static_assert(SPREAD == 0 || LPW * SPREAD <= MPK * KK, "loads spread past the next barrier");
+    int pend = -1;  // stage whose loads are being spread (issued at the last barrier)
+    auto issue_piece = [&](int j) {
+      const uint32_t dst = smem_base + static_cast<uint32_t>((pend % STAGES) * STAGE_BYTES) +
+                           static_cast<uint32_t>(wave * LPW * 1024 + j * 1024);
+      dma16(src[j] + static_cast<int64_t>(pend) * SBK, dst);
+    };
+    wait_stage<LPW, STAGES>(min(STAGES - 1, nk - 1));
+    block_barrier();
+    load_frags<MI, NB, NI, BM, BN, SBK, WTM, WTN>(ca, cb, smem, 0, wm, wn, l32, hi);
+    for (int kt = 0; kt < nk; ++kt) {
+      const char* st = smem + (kt % STAGES) * STAGE_BYTES;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        if (kk + 1 < KK) {
+          load_frags<MI, NB, NI, BM, BN, SBK, WTM, WTN>(na, nb, st, kk + 1, wm, wn, l32, hi);
+        } else if (kt + 1 < nk) {
+          const int last = min(kt + STAGES - 1, nk - 1);  // newest stage issued so far
+          wait_stage<LPW, STAGES>(last - (kt + 1));
+          wait_lgkm0();
+          block_barrier();
+          pend = kt + STAGES < nk ? kt + STAGES : -1;
+          if constexpr (SPREAD == 0) {
+            if (pend >= 0) issue(pend);
+          }
+          load_frags<MI, NB, NI, BM, BN, SBK, WTM, WTN>(
+              na, nb, smem + ((kt + 1) % STAGES) * STAGE_BYTES, 0, wm, wn, l32, hi);
+        }
+        if constexpr (SPREAD == 0) {
+          mfma_step<MI, NB, NI>(acc, ca, cb);
+        } else {
+          // MFMA positions since the last barrier: the last step of a stage
+          // follows it directly; steps 0..KK-2 continue from the previous
+          // iteration's barrier.
+          mfma_step_dma<MI, NB, NI, SPREAD, LPW>(acc, ca, cb, kk + 1 == KK ? 0 : (kk + 1) * MPK,
+                                                 pend >= 0, issue_piece);
+        }
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi) ca[mi] = na[mi];
+#pragma unroll
+        for (int q = 0; q < NB; ++q)
+#pragma unroll
+          for (int ni = 0; ni < NI; ++ni) cb[q][ni] = nb[q][ni];
+      }
     }
   } else if constexpr (SCHED == kSchedDeep) {
     // Memory-depth schedule (weight-streaming bodies): at the top of
@@ -501,13 +588,14 @@ __global__ void __launch_bounds__(NW * 64) gmm_bf16_kernel(
   }
 }
 
-template <int BM, int BN, int WM, int WN, bool FC1, int STAGES, int SBK, int SCHED = kSchedCompute>
+template <int BM, int BN, int WM, int WN, bool FC1, int STAGES, int SBK, int SCHED = kSchedCompute,
+          int SPREAD = 0>
 struct Body {
   static constexpr int lds = body_lds_bytes<BM, BN, FC1, STAGES, SBK>();
   __device__ __forceinline__ static void run(const Tile& t, char* smem, const uint16_t* A,
                                              const uint16_t* B0, const uint16_t* B1, uint16_t* C,
                                              int N, int K) {
-    gmm_tile<BM, BN, WM, WN, FC1, STAGES, SBK, SCHED>(t, smem, A, B0, B1, C, N, K);
+    gmm_tile<BM, BN, WM, WN, FC1, STAGES, SBK, SCHED, SPREAD>(t, smem, A, B0, B1, C, N, K);
   }
 };
 
@@ -629,12 +717,12 @@ int pick_bm(int64_t max_rows, int64_t E) {
 // hold BN=128 columns of W_gate and of W_up, FC2 tiles 256 columns of
 // W_down, and ragged tails run 128- or 64-row bodies.  128- and 64-row
 // launches (small experts, weight-streaming bound) use one body each.
-using Fc1B256 = Body<256, 128, 4, 2, true, 4, 32>;
-using Fc1B128 = Body<128, 128, 4, 2, true, 5, 32>;
+using Fc1B256 = Body<256, 128, 2, 4, true, 2, 64, kSchedRing, 2>;
+using Fc1B128 = Body<128, 128, 2, 4, true, 3, 64, kSchedRing, 2>;
 using Fc1B64 = Body<64, 128, 2, 4, true, 4, 64>;
-using Fc1Stream128 = Body<128, 128, 2, 4, true, 3, 64, kSchedDeep>;
-using Fc2B256 = Body<256, 256, 2, 4, false, 4, 32>;
-using Fc2B128 = Body<128, 256, 4, 2, false, 5, 32>;
+using Fc1Stream128 = Body<128, 128, 2, 4, true, 3, 64, kSchedRing, 2>;
+using Fc2B256 = Body<256, 256, 4, 2, false, 2, 64, kSchedRing, 2>;
+using Fc2B128 = Body<128, 256, 2, 4, false, 3, 64, kSchedRing, 2>;
 using Fc2B64 = Body<64, 256, 2, 4, false, 4, 64>;
 using Fc2Stream128 = Body<128, 128, 2, 4, false, 4, 64>;
 
