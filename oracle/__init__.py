@@ -9,7 +9,7 @@ Everything is NumPy: floating point in float64 with one rounding at each
 point where the layer stores a tensor, except where the pages fix fp32 (the
 sigmoid scores used for expert selection, see fp32spec).
 """
-from .fp32spec import exp_spec, sigmoid_spec
+from .fp32spec import exp_spec, log1p_spec, sigmoid_spec, softplus_spec, sqrtsoftplus_spec
 from .moe import (
     round_bf16,
     round_to,
@@ -17,8 +17,13 @@ from .moe import (
     topk_indices,
     score_and_select,
     get_capacity,
+    capacity_mask,
+    apply_token_dropping,
     drop_by_position,
     route,
+    aux_loss,
+    accumulate_tokens,
+    update_expert_bias,
     permute,
     swiglu_rows,
     grouped_experts,
@@ -28,8 +33,10 @@ from .moe import (
 )
 
 __all__ = [
-    "exp_spec", "sigmoid_spec", "round_bf16", "round_to", "router_logits",
-    "topk_indices", "score_and_select", "get_capacity", "drop_by_position",
+    "exp_spec", "log1p_spec", "sigmoid_spec", "softplus_spec", "sqrtsoftplus_spec", "round_bf16", "round_to", "router_logits",
+    "topk_indices", "score_and_select", "get_capacity", "capacity_mask",
+    "apply_token_dropping", "drop_by_position", "aux_loss", "accumulate_tokens",
+    "update_expert_bias",
     "route", "permute", "swiglu_rows", "grouped_experts", "combine",
     "moe_forward", "token_outputs",
 ]

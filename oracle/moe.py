@@ -25,7 +25,7 @@ from typing import Callable, Dict, Optional, Sequence, Tuple, Union
 
 import numpy as np
 
-from .fp32spec import sigmoid_spec
+from .fp32spec import sigmoid_spec, sqrtsoftplus_spec
 
 F32 = np.float32
 F64 = np.float64
@@ -115,10 +115,12 @@ def score_and_select(logits, K: int, score: str = "softmax", pre_softmax: bool =
         With an expert bias the choice is made on s + bias (one fp32 add) and
         the probs come from the unbiased s of the chosen experts; the probs
         are s / (sum of chosen s + 1e-20).
+    sqrtsoftplus: as sigmoid with s = sqrt(softplus(logit)) in fp32
+        (fp32spec.sqrtsoftplus_spec); the page handles both the same way.
 
     Returns (probs [T,E] fp32, zero off the map; routing_map [T,E] uint8;
     scores [T,E] fp32 = the score function over all E: the full softmax for
-    both softmax modes, s for sigmoid).
+    both softmax modes, s for sigmoid and sqrtsoftplus).
     """
     l = np.asarray(logits, F32)
     T, E = l.shape
@@ -133,8 +135,8 @@ def score_and_select(logits, K: int, score: str = "softmax", pre_softmax: bool =
         else:
             p_sel = _softmax64(l[rows, sel])
         scores = full.astype(F32)
-    elif score == "sigmoid":
-        s = sigmoid_spec(l)
+    elif score in ("sigmoid", "sqrtsoftplus"):
+        s = sigmoid_spec(l) if score == "sigmoid" else sqrtsoftplus_spec(l)
         key = s if expert_bias is None else (s + np.asarray(expert_bias, F32)[None, :]).astype(F32)
         sel = topk_indices(key, K)
         s_sel = s[rows, sel].astype(F64)
@@ -168,32 +170,62 @@ def get_capacity(num_tokens: int, num_experts: int, capacity_factor: float,
     return max(cap, int(min_capacity))
 
 
-def drop_by_position(probs, routing_map, capacity: int) -> Tuple[np.ndarray, np.ndarray]:
-    """Capacity dropping with the "position" policy ([MC] §8).
+def capacity_mask(probs, routing_map, capacity: int, drop_policy: str = "position") -> np.ndarray:
+    """The per-expert capacity mask of [MC] §8 (uint8 [T, E]).
 
-    When the capacity is at least the token count nothing is dropped (no
-    expert can receive more than T tokens).  Otherwise each expert keeps the
-    first `capacity` tokens routed to it, in ascending token order (reading:
-    the page keeps entries by their position in the routing map; the
-    earliest tokens win).  Dropped entries get map 0 and prob 0; nothing is
-    re-routed or renormalised (final probs = probs * final map).
+    When the capacity is at least the token count the mask is all ones (no
+    expert can receive more than T tokens).  Otherwise, for each expert, the
+    mask marks `capacity` of the T tokens, the first ones in this order:
+      "position": routed tokens before unrouted ones, each in ascending token
+                  order (the page ranks the routing-map entries themselves;
+                  reading: among equal entries the earliest token first);
+      "probs":    larger routing prob first, among equal probs the earlier
+                  token (the page ranks the routing probs; same tie reading).
+    Unrouted tokens have prob 0, so they only enter the mask when fewer than
+    `capacity` tokens were routed to the expert.
     """
-    p = np.array(probs, dtype=F32, copy=True)
-    m = np.array(routing_map, dtype=np.uint8, copy=True)
+    p = np.asarray(probs, F32)
+    m = np.asarray(routing_map, np.uint8)
     T, E = m.shape
     if capacity >= T:
-        return p, m
+        return np.ones((T, E), np.uint8)
+    mask = np.zeros((T, E), np.uint8)
+    t = np.arange(T)
     for e in range(E):
-        routed = np.nonzero(m[:, e])[0]
-        dropped = routed[capacity:]
-        m[dropped, e] = 0
-        p[dropped, e] = 0.0
-    return p, m
+        if drop_policy == "position":
+            order = np.lexsort((t, -m[:, e].astype(np.int64)))  # map desc, then t asc
+        elif drop_policy == "probs":
+            order = np.lexsort((t, -p[:, e].astype(F64)))       # prob desc, then t asc
+        else:
+            raise ValueError(drop_policy)
+        mask[order[:capacity], e] = 1
+    return mask
+
+
+def apply_token_dropping(probs, routing_map, capacity: int, drop_policy: str = "position",
+                         pad_to_capacity: bool = False) -> Tuple[np.ndarray, np.ndarray]:
+    """Capacity dropping ([MC] §8): final map = the capacity mask when
+    padding to capacity, else routing map AND mask; final probs = probs *
+    final map (nothing is re-routed or renormalised).  Returns (probs
+    fp32, map uint8)."""
+    mask = capacity_mask(probs, routing_map, capacity, drop_policy)
+    m = np.asarray(routing_map, np.uint8)
+    final_map = mask if pad_to_capacity else (m & mask)
+    final_probs = (np.asarray(probs, F32) * final_map).astype(F32)
+    return final_probs, final_map.astype(np.uint8)
+
+
+def drop_by_position(probs, routing_map, capacity: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Capacity dropping with the "position" policy and no padding: each
+    expert keeps the first `capacity` tokens routed to it, in ascending
+    token order; dropped entries get map 0 and prob 0."""
+    return apply_token_dropping(probs, routing_map, capacity, "position", False)
 
 
 def route(x=None, w_router=None, b_router=None, *, K: int, score: str = "softmax",
           pre_softmax: bool = True, expert_bias=None, capacity_factor: float = 0.0,
-          min_capacity: int = 0, logits=None) -> Dict[str, np.ndarray]:
+          min_capacity: int = 0, drop_policy: str = "position", pad_to_capacity: bool = False,
+          logits=None) -> Dict[str, np.ndarray]:
     """The router: gating -> score/top-k -> optional capacity drop ([MC] §4).
 
     Pass `logits` to route given fp32 logits (skipping the gating linear).
@@ -207,7 +239,7 @@ def route(x=None, w_router=None, b_router=None, *, K: int, score: str = "softmax
     T, E = logits.shape
     if capacity_factor > 0:
         cap = get_capacity(T * K, E, capacity_factor, min_capacity)
-        probs, rmap = drop_by_position(probs0, map0, cap)
+        probs, rmap = apply_token_dropping(probs0, map0, cap, drop_policy, pad_to_capacity)
     else:
         cap = -1
         probs, rmap = probs0, map0
@@ -216,6 +248,58 @@ def route(x=None, w_router=None, b_router=None, *, K: int, score: str = "softmax
         "probs": probs, "routing_map": rmap, "capacity": cap,
         "tokens_per_expert": rmap.sum(axis=0).astype(np.int32),
     }
+
+
+# --------------------------------------------------------------------------
+# router side outputs: load-balancing loss value, expert-bias controller
+#   ([MC] §6, §7)
+# --------------------------------------------------------------------------
+
+
+def aux_loss(scores, tokens_per_expert, K: int, score: str = "softmax") -> float:
+    """Forward value of the switch load-balancing loss, E * sum_i f_i * P_i
+    ([MC] §6).
+
+    f_i = tokens_per_expert[i] / (T * K): the share of the T*K routing
+          assignments that expert i actually received (the final map, after
+          any dropping: the page applies the loss after token dropping, §4);
+    P_i = mean over tokens of the router's probability mass on expert i: the
+          full softmax for softmax scoring; for sigmoid and sqrtsoftplus the
+          scores normalised per token to sum 1 (+1e-20, as for the probs).
+    Uniform routing gives exactly 1.  No coefficient is applied.
+    """
+    s = np.asarray(scores, F64)
+    T, E = s.shape
+    if T == 0:
+        return 0.0
+    if score != "softmax":
+        s = s / (s.sum(axis=1, keepdims=True) + 1e-20)
+    P = s.mean(axis=0)
+    f = np.asarray(tokens_per_expert, F64) / float(T * K)
+    return float(E * np.sum(f * P))
+
+
+def accumulate_tokens(local_tokens_per_expert, tokens_per_expert) -> np.ndarray:
+    """The controller's running count ([MC] §7): local += this batch's
+    tokens_per_expert (int64)."""
+    return (np.asarray(local_tokens_per_expert, np.int64) +
+            np.asarray(tokens_per_expert, np.int64)).astype(np.int64)
+
+
+def update_expert_bias(local_tokens_per_expert, expert_bias, update_rate: float) -> np.ndarray:
+    """One step of the loss-free balance controller ([MC] §7): an expert
+    loaded above the mean count moves its bias down by the rate, one below
+    the mean moves it up, one at the mean keeps it.
+
+    bias_new = bias + sign(mean - count) * rate, one fp32 add.  Reading: the
+    sign is decided exactly (sign(sum - E*count) in integers), so no
+    rounding of the mean can flip it.  On one GPU there is no all-reduce.
+    """
+    c = np.asarray(local_tokens_per_expert, np.int64)
+    E = c.shape[0]
+    d = int(c.sum()) - E * c
+    sign = np.sign(d).astype(F32)
+    return (np.asarray(expert_bias, F32) + sign * F32(update_rate)).astype(F32)
 
 
 # --------------------------------------------------------------------------
@@ -233,8 +317,12 @@ def permute(x, routing_map, probs, K: int) -> Dict[str, np.ndarray]:
       permuted_probs[i] = probs[t_i, e_i]
       sorted_token[i]   = t_i
       expert_offsets    = [0, n_0, n_0+n_1, ...]  (E+1 entries)
-      row_id_map[t, k]  = row of token t's k-th routed expert in ascending
-                          expert order, -1 for unused slots (K columns).
+      row_id_map[t, k]  = row of token t's k-th weighted entry (map 1 and
+                          prob != 0) in ascending expert order, -1 for
+                          unused slots (K columns).  Entries with prob 0
+                          (capacity padding) have rows but add nothing to
+                          the combine, so they take no slot; a token has at
+                          most K nonzero probs.
     """
     rmap = np.asarray(routing_map).astype(bool)
     T, E = rmap.shape
@@ -246,11 +334,14 @@ def permute(x, routing_map, probs, K: int) -> Dict[str, np.ndarray]:
     slot = np.zeros(T, np.int64)
     # visit rows token by token in ascending expert order to fill the slots
     order = np.lexsort((e_idx, t_idx))
+    pr = np.asarray(probs, F32)
     for i in order:
         t = t_idx[i]
+        if pr[t, e_idx[i]] == 0:
+            continue
         k = slot[t]
         if k >= K:
-            raise ValueError(f"token {t} is routed to more than K={K} experts")
+            raise ValueError(f"token {t} has more than K={K} nonzero probs")
         row_id_map[t, k] = i
         slot[t] = k + 1
     return {
@@ -365,6 +456,7 @@ def combine(expert_out, permuted_probs, row_id_map, dtype: str, shared_out=None)
 def moe_forward(x, w_router, b_router, weights: WeightSource, *, K: int, dtype: str,
                 score: str = "softmax", pre_softmax: bool = True, expert_bias=None,
                 capacity_factor: float = 0.0, min_capacity: int = 0,
+                drop_policy: str = "position", pad_to_capacity: bool = False,
                 shared: Optional[Sequence[np.ndarray]] = None,
                 logits=None) -> Dict[str, np.ndarray]:
     """route -> permute -> experts -> combine (+ shared expert) ([MC] §2).
@@ -374,7 +466,8 @@ def moe_forward(x, w_router, b_router, weights: WeightSource, *, K: int, dtype: 
     """
     r = route(x, w_router, b_router, K=K, score=score, pre_softmax=pre_softmax,
               expert_bias=expert_bias, capacity_factor=capacity_factor,
-              min_capacity=min_capacity, logits=logits)
+              min_capacity=min_capacity, drop_policy=drop_policy,
+              pad_to_capacity=pad_to_capacity, logits=logits)
     pm = permute(x, r["routing_map"], r["probs"], K)
     act, y = grouped_experts(pm["permuted_x"], pm["tokens_per_expert"], weights, dtype)
     shared_out = None
