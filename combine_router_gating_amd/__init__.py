@@ -2,6 +2,7 @@
 SwiGLU experts -> weighted combine, as HIP kernels behind a C interface
 (include/moe.h, built into libmoe.so)."""
 from .moe import (
+    moe_accumulate_tokens_per_expert,
     moe_combine,
     moe_forward,
     moe_grouped_fc1_swiglu,
@@ -11,11 +12,14 @@ from .moe import (
     moe_permute,
     moe_route,
     moe_route_capacity,
+    moe_router_aux_loss,
+    moe_update_expert_bias,
     route_desc,
 )
 from ._lib import LIB_PATH, MoEError, load
 
 __all__ = [
+    "moe_accumulate_tokens_per_expert", "moe_router_aux_loss", "moe_update_expert_bias",
     "moe_combine", "moe_forward", "moe_grouped_fc1_swiglu", "moe_grouped_fc2", "moe_grouped_mlp",
     "moe_max_rows", "moe_permute", "moe_route", "moe_route_capacity", "route_desc", "LIB_PATH",
     "MoEError", "load",

@@ -12,7 +12,8 @@ c_i64, c_i32, c_sz, c_vp, c_f32 = (ctypes.c_int64, ctypes.c_int32, ctypes.c_size
 
 MOE_OK, MOE_ERR_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 MOE_F32, MOE_BF16 = 0, 1
-MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
+MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID, MOE_SCORE_SQRTSOFTPLUS = 0, 1, 2
+MOE_DROP_POSITION, MOE_DROP_PROBS = 0, 1
 
 
 class RouteDesc(ctypes.Structure):
@@ -22,6 +23,7 @@ class RouteDesc(ctypes.Structure):
         ("T", c_i64), ("h", c_i64), ("E", c_i64), ("K", c_i64),
         ("x_dtype", c_i32), ("score", c_i32), ("pre_softmax", c_i32),
         ("capacity_factor", c_f32), ("min_capacity", c_i64),
+        ("drop_policy", c_i32), ("pad_to_capacity", c_i32),
     ]
 
 
@@ -34,6 +36,11 @@ SIGNATURES = {
     "moe_max_rows": (c_i64, [ctypes.POINTER(RouteDesc)]),
     "moe_route": (c_i32, [ctypes.POINTER(RouteDesc), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                           c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
+    "moe_aux_loss_workspace_size": (c_sz, [c_i64, c_i64]),
+    "moe_router_aux_loss": (c_i32, [c_i64, c_i64, c_i64, c_i32, c_vp, c_vp, c_vp, c_vp, c_sz,
+                                    c_vp]),
+    "moe_accumulate_tokens_per_expert": (c_i32, [c_i64, c_vp, c_vp, c_vp]),
+    "moe_update_expert_bias": (c_i32, [c_i64, c_vp, c_vp, c_f32, c_i32, c_vp]),
     "moe_permute_workspace_size": (c_sz, [c_i64, c_i64]),
     "moe_permute": (c_i32, [c_i64, c_i64, c_i64, c_i64, c_i32, c_vp, c_vp, c_vp, c_i64, c_vp,
                             c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),

@@ -18,10 +18,14 @@ namespace moe {
 namespace {
 
 // One workgroup per block of kCountBlock tokens, one wave per token.
-// Phase 1 (per token): ballot over the map row, 64 experts at a time, gives
-// the token's experts in ascending order and their rows.  Phase 2: write
+// Phase 1 (per token): ballots over the map row, 64 experts at a time, give
+// the token's entries in ascending expert order and their rows; the entries
+// with a nonzero prob take the token's combine slots (at most K: only the
+// chosen experts have nonzero probs; padding to capacity adds entries with
+// prob 0, which need rows but add nothing to the combine).  Phase 2: write
 // row_id_map / permuted_probs / sorted_token and copy the token row, read
-// once, to each of its rows with 16-byte stores.
+// once, to each of its first kMaxTopK rows with 16-byte stores; further
+// rows (padding only) are copied entry by entry.
 __global__ void __launch_bounds__(256) permute_scatter_kernel(
     const uint8_t* __restrict__ map, const float* __restrict__ probs, const uint4* __restrict__ x,
     int64_t T, int E, int K, int chunks, const int32_t* __restrict__ blkoff,
@@ -31,7 +35,9 @@ __global__ void __launch_bounds__(256) permute_scatter_kernel(
   __shared__ uint8_t tile[kCountBlock][kMaxExperts];
   __shared__ int rows[kCountBlock][kMaxTopK];
   __shared__ int exps[kCountBlock][kMaxTopK];
+  __shared__ int slot_rows[kCountBlock][kMaxTopK];
   __shared__ int cnt[kCountBlock];
+  __shared__ int nslot[kCountBlock];
   __shared__ int s_off[kMaxExperts + 1];
   __shared__ int64_t scratch[4];
   const int b = blockIdx.x;
@@ -66,31 +72,51 @@ __global__ void __launch_bounds__(256) permute_scatter_kernel(
   }
   __syncthreads();
 
+  // row of entry (token tl of this block, expert e)
+  auto row_of = [&](int tl, int e) {
+    int prior = 0;
+    for (int u = 0; u < tl; ++u) prior += tile[u][e];
+    return s_off[e] + blkoff[static_cast<int64_t>(b) * E + e] + prior;
+  };
+  const uint64_t below = (uint64_t(1) << lane) - 1;
+
   for (int tl = wave; tl < nt; tl += 4) {
-    int base_k = 0;
+    const int64_t t = t0 + tl;
+    int base = 0, ks = 0;
     for (int c0 = 0; c0 < E; c0 += 64) {
       const int e = c0 + lane;
       const bool set = e < E && tile[tl][e];
+      const bool nz = set && probs[t * E + e] != 0.f;
       const uint64_t mask = __ballot(set);
+      const uint64_t nzmask = __ballot(nz);
       if (set) {
-        int prior = 0;
-        for (int u = 0; u < tl; ++u) prior += tile[u][e];
-        const int k = base_k + __popcll(mask & ((uint64_t(1) << lane) - 1));
-        if (k < K) {
-          rows[tl][k] = s_off[e] + blkoff[static_cast<int64_t>(b) * E + e] + prior;
-          exps[tl][k] = e;
+        const int r = row_of(tl, e);
+        const int j = base + __popcll(mask & below);
+        if (j < kMaxTopK) {
+          rows[tl][j] = r;
+          exps[tl][j] = e;
+        }
+        if (nz) {
+          const int k = ks + __popcll(nzmask & below);
+          if (k < K) slot_rows[tl][k] = r;
         }
       }
-      base_k += __popcll(mask);
+      base += __popcll(mask);
+      ks += __popcll(nzmask);
     }
-    if (lane == 0) cnt[tl] = min(base_k, K);
+    if (lane == 0) {
+      cnt[tl] = base;
+      nslot[tl] = min(ks, K);
+    }
   }
   __syncthreads();
 
   for (int tl = wave; tl < nt; tl += 4) {
     const int64_t t = t0 + tl;
-    const int n = cnt[tl];
-    if (lane < K) row_id_map[t * K + lane] = lane < n ? rows[tl][lane] : -1;
+    const int n_all = cnt[tl];
+    const int n = min(n_all, kMaxTopK);
+    const int ns = nslot[tl];
+    if (lane < K) row_id_map[t * K + lane] = lane < ns ? slot_rows[tl][lane] : -1;
     if (lane < n) {
       const int r = rows[tl][lane];
       if (r < max_rows) {
@@ -104,6 +130,28 @@ __global__ void __launch_bounds__(256) permute_scatter_kernel(
       for (int k = 0; k < n; ++k) {
         const int r = rows[tl][k];
         if (r < max_rows) px[static_cast<int64_t>(r) * chunks + i] = v;
+      }
+    }
+    if (n_all > kMaxTopK) {  // padding entries past the first kMaxTopK
+      int base = 0;
+      for (int c0 = 0; c0 < E; c0 += 64) {
+        const int e = c0 + lane;
+        const bool set = e < E && tile[tl][e];
+        const uint64_t mask = __ballot(set);
+        const int j = base + __popcll(mask & below);
+        const int r = (set && j >= kMaxTopK) ? row_of(tl, e) : -1;
+        if (r >= 0 && r < max_rows) {
+          pprobs[r] = probs[t * E + e];
+          sorted_token[r] = static_cast<int32_t>(t);
+        }
+        uint64_t todo = __ballot(r >= 0 && r < max_rows);
+        while (todo) {
+          const int src_lane = __builtin_ctzll(todo);
+          todo &= todo - 1;
+          const int rr = __shfl(r, src_lane, 64);
+          for (int i = lane; i < chunks; i += 64) px[static_cast<int64_t>(rr) * chunks + i] = src[i];
+        }
+        base += __popcll(mask);
       }
     }
   }

@@ -307,6 +307,29 @@ __device__ __noinline__ float sigmoid_fixed(float x) {
   return (x >= 0.0f) ? (1.0f / den) : (e / den);
 }
 
+// sqrt(softplus(x)) by a fixed fp32 sequence: softplus(x) = x for x > 20,
+// else max(x, 0) + log1p(e) with e = exp_fixed(-|x|); log1p(u), 0 <= u <= 1,
+// is 2*atanh(s) with s = u/(2+u) <= 1/3: (2*s) * q, q the degree-7 Horner
+// polynomial in s*s with fp32(1/(2j+1)) coefficients; then the correctly
+// rounded square root.
+__device__ __noinline__ float sqrtsoftplus_fixed(float x) {
+#pragma clang fp contract(off)
+  const float e = exp_fixed(-fabsf(x));
+  const float s = e / (2.0f + e);
+  const float s2 = s * s;
+  float q = 0x1.111112p-4f;          // 1/15
+  q = q * s2 + 0x1.3b13b2p-4f;       // 1/13
+  q = q * s2 + 0x1.745d18p-4f;       // 1/11
+  q = q * s2 + 0x1.c71c72p-4f;       // 1/9
+  q = q * s2 + 0x1.24924ap-3f;       // 1/7
+  q = q * s2 + 0x1.99999ap-3f;       // 1/5
+  q = q * s2 + 0x1.555556p-2f;       // 1/3
+  q = q * s2 + 1.0f;                 // 1/1
+  const float l1p = (2.0f * s) * q;
+  const float sp = (x > 20.0f) ? x : (fmaxf(x, 0.0f) + l1p);
+  return sqrtf(sp);  // correctly rounded (no fast-math flags)
+}
+
 // --------------------------------------------------------------- top-k
 // (value descending, index ascending) is a strict total order on non-NaN
 // keys, so a butterfly reduction gives every lane the same winner.
@@ -384,7 +407,8 @@ __global__ void __launch_bounds__(256) router_topk_kernel(
     } else {
 #pragma unroll
       for (int j = 0; j < EPL; ++j) {
-        s[j] = valid[j] ? sigmoid_fixed(l[j]) : 0.f;
+        s[j] = valid[j] ? (score == MOE_SCORE_SIGMOID ? sigmoid_fixed(l[j]) : sqrtsoftplus_fixed(l[j]))
+                        : 0.f;
         key[j] = (valid[j] && expert_bias) ? s[j] + expert_bias[lane + 64 * j] : s[j];
       }
     }
@@ -478,6 +502,182 @@ __global__ void __launch_bounds__(256) router_drop_kernel(const int32_t* __restr
   }
 }
 
+// ------------------------------------------------- capacity mask per expert
+// One workgroup per expert e: the capacity mask of column e is the first
+// `cap` of the T tokens by (key descending, token ascending), with key =
+// the routing prob (probs policy) or the map entry (position policy).  The
+// cap-th largest key v is found by a radix select over the 31 magnitude
+// bits (4 passes of 8 bits, LDS histograms); then every token with key > v
+// is in the mask, and of the tokens with key == v the earliest `need`
+// ones (an ordered block scan over the tokens).  The final map is the mask
+// (padding to capacity) or map AND mask; final probs = probs * final map;
+// tokens_per_expert[e] = column sum of the final map.
+__device__ __forceinline__ uint32_t cap_key(const float* probs, const uint8_t* rmap, int64_t idx,
+                                            int policy) {
+  return policy == MOE_DROP_PROBS ? (__float_as_uint(probs[idx]) & 0x7fffffffu)
+                                  : (rmap[idx] ? 1u : 0u);
+}
+
+__global__ void __launch_bounds__(256) router_capacity_kernel(int64_t T, int E, int64_t cap,
+                                                              int policy, int pad,
+                                                              float* __restrict__ probs,
+                                                              uint8_t* __restrict__ rmap,
+                                                              int32_t* __restrict__ counts) {
+  __shared__ int hist[256];
+  __shared__ int64_t scratch[4];
+  __shared__ uint32_t s_digit;
+  __shared__ int64_t s_rank;
+  const int e = blockIdx.x;
+  const int tid = threadIdx.x;
+  // rank (1-based) of the wanted key among keys sharing the prefix so far
+  int64_t rank = cap;
+  uint32_t prefix = 0, pmask = 0;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    hist[tid] = 0;
+    __syncthreads();
+    for (int64_t t = tid; t < T; t += 256) {
+      const uint32_t k = cap_key(probs, rmap, t * E + e, policy);
+      if ((k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & 255], 1);
+    }
+    __syncthreads();
+    if (tid == 0) {
+      // walk digits from the top until the count reaches the rank
+      int64_t acc = 0;
+      int d = 255;
+      for (; d > 0; --d) {
+        if (acc + hist[d] >= rank) break;
+        acc += hist[d];
+      }
+      s_digit = static_cast<uint32_t>(d);
+      s_rank = rank - acc;
+    }
+    __syncthreads();
+    prefix |= s_digit << shift;
+    pmask |= 255u << shift;
+    rank = s_rank;
+    __syncthreads();
+  }
+  const uint32_t v = prefix;  // the cap-th largest key
+  // `rank` = how many tokens with key == v belong to the mask (earliest first)
+  const int64_t need = rank;
+  int64_t seen = 0;  // tokens with key == v in earlier chunks
+  int64_t kept = 0;
+  for (int64_t t0 = 0; t0 < T; t0 += 256) {
+    const int64_t t = t0 + tid;
+    uint32_t k = 0;
+    bool eq = false;
+    if (t < T) {
+      k = cap_key(probs, rmap, t * E + e, policy);
+      eq = k == v;
+    }
+    int64_t tot;
+    const int64_t before = seen + block_exclusive_scan256(eq ? 1 : 0, scratch, &tot);
+    seen += tot;
+    if (t < T) {
+      const bool in_mask = k > v || (eq && before < need);
+      const int64_t idx = t * E + e;
+      const bool routed = rmap[idx] != 0;
+      const bool fin = pad ? in_mask : (routed && in_mask);
+      if (routed && !fin) {  // dropped
+        rmap[idx] = 0;
+        probs[idx] = 0.f;
+      } else if (!routed && fin) {  // padding (its prob is already 0)
+        rmap[idx] = 1;
+      }
+      kept += fin ? 1 : 0;
+    }
+  }
+  int64_t total;
+  block_exclusive_scan256(kept, scratch, &total);
+  if (tid == 0) counts[e] = static_cast<int32_t>(total);
+}
+
+// ------------------------------------------- load-balancing loss value
+// Pass 1: workgroup b handles tokens [64b, 64b+64): per token the score row
+// sum (sigmoid-type scores are normalised per token; softmax rows are used
+// as they are), then each thread accumulates its experts' normalised scores
+// over the 64 tokens in token order into partial[b][e].  Pass 2 (one
+// workgroup): P[e] = sum of the partials in block order / T, term[e] =
+// n_e * P[e], loss = E / (T*K) * sum_e term[e] by a fixed-order tree.
+constexpr int kAuxTok = 64;
+
+__global__ void __launch_bounds__(256) aux_partial_kernel(const float* __restrict__ scores,
+                                                          int64_t T, int E, int normalise,
+                                                          float* __restrict__ partial) {
+  __shared__ float inv[kAuxTok];
+  const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kAuxTok;
+  const int nt = static_cast<int>(min(static_cast<int64_t>(kAuxTok), T - t0));
+  for (int tl = wave; tl < kAuxTok; tl += 4) {
+    float sum = 0.f;
+    if (normalise && tl < nt)
+      for (int e = lane; e < E; e += 64) sum += scores[(t0 + tl) * E + e];
+    sum = wave_sum(sum);
+    if (lane == 0) inv[tl] = normalise ? 1.0f / (sum + 1e-20f) : 1.0f;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 256) {
+    float acc = 0.f;
+    for (int tl = 0; tl < nt; ++tl) acc += scores[(t0 + tl) * E + e] * inv[tl];
+    partial[static_cast<int64_t>(blockIdx.x) * E + e] = acc;
+  }
+}
+
+__global__ void __launch_bounds__(256) aux_final_kernel(const float* __restrict__ partial,
+                                                        int64_t nblk, int64_t T, int E, int K,
+                                                        const int32_t* __restrict__ counts,
+                                                        float* __restrict__ loss) {
+  __shared__ float red[256];
+  float term = 0.f;
+  for (int e = threadIdx.x; e < E; e += 256) {
+    float P = 0.f;
+    for (int64_t b = 0; b < nblk; ++b) P += partial[b * E + e];
+    term += static_cast<float>(counts[e]) * (P / static_cast<float>(T));
+  }
+  red[threadIdx.x] = term;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0)
+    loss[0] = red[0] * (static_cast<float>(E) / (static_cast<float>(T) * static_cast<float>(K)));
+}
+
+// ------------------------------------------------- expert-bias controller
+__global__ void __launch_bounds__(256) accumulate_tokens_kernel(int E,
+                                                                const int32_t* __restrict__ tpe,
+                                                                int64_t* __restrict__ local) {
+  for (int e = blockIdx.x * 256 + threadIdx.x; e < E; e += gridDim.x * 256) local[e] += tpe[e];
+}
+
+// bias[e] += sign(S - E*c[e]) * rate with S = sum of the counts (exact
+// integer comparison of the count with the mean); optionally zero the counts.
+__global__ void __launch_bounds__(256) update_bias_kernel(int E, int64_t* __restrict__ local,
+                                                          float* __restrict__ bias, float rate,
+                                                          int reset) {
+  __shared__ int64_t scratch[4];
+  constexpr int PER = kMaxExperts / 256;
+  int64_t c[PER], sum = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int e = threadIdx.x * PER + j;
+    c[j] = e < E ? local[e] : 0;
+    sum += c[j];
+  }
+  int64_t S;
+  block_exclusive_scan256(sum, scratch, &S);
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int e = threadIdx.x * PER + j;
+    if (e >= E) continue;
+    const int64_t d = S - static_cast<int64_t>(E) * c[j];
+    const float sgn = d > 0 ? 1.0f : (d < 0 ? -1.0f : 0.0f);
+    bias[e] = bias[e] + sgn * rate;
+    if (reset) local[e] = 0;
+  }
+}
+
 struct TopkArgs {
   const float* part;
   int nsplit;
@@ -502,12 +702,19 @@ size_t logits_ws_bytes(const moe_route_desc* d) {
   return align_up(static_cast<size_t>(planes * d->T * d->E) * sizeof(float), 256);
 }
 
-int64_t capacity_of(const moe_route_desc* d) {
+// max(ceil(T*K*cf/E), min_capacity), or -1 when dropless (cf <= 0)
+int64_t raw_capacity(const moe_route_desc* d) {
   if (!(d->capacity_factor > 0.f)) return -1;
   const double ratio = static_cast<double>(d->T) * static_cast<double>(d->K) *
                        static_cast<double>(d->capacity_factor) / static_cast<double>(d->E);
   int64_t cap = static_cast<int64_t>(std::ceil(ratio));
   if (cap < d->min_capacity) cap = d->min_capacity;
+  return cap;
+}
+
+// capacity that can drop anything, or -1 (dropless, or capacity >= T)
+int64_t capacity_of(const moe_route_desc* d) {
+  const int64_t cap = raw_capacity(d);
   return cap >= d->T ? -1 : cap;
 }
 
@@ -524,8 +731,11 @@ moe_status validate(const moe_route_desc* d) {
               "moe_route: h=%lld must be a positive multiple of 8", (long long)d->h);
   MOE_REQUIRE(d->x_dtype == MOE_F32 || d->x_dtype == MOE_BF16, MOE_ERR_ARG,
               "moe_route: bad x_dtype %d", d->x_dtype);
-  MOE_REQUIRE(d->score == MOE_SCORE_SOFTMAX || d->score == MOE_SCORE_SIGMOID, MOE_ERR_ARG,
-              "moe_route: bad score %d", d->score);
+  MOE_REQUIRE(d->score == MOE_SCORE_SOFTMAX || d->score == MOE_SCORE_SIGMOID ||
+                  d->score == MOE_SCORE_SQRTSOFTPLUS,
+              MOE_ERR_ARG, "moe_route: bad score %d", d->score);
+  MOE_REQUIRE(d->drop_policy == MOE_DROP_POSITION || d->drop_policy == MOE_DROP_PROBS, MOE_ERR_ARG,
+              "moe_route: bad drop_policy %d", d->drop_policy);
   MOE_REQUIRE(d->min_capacity >= 0, MOE_ERR_ARG, "moe_route: min_capacity < 0");
   MOE_REQUIRE(static_cast<int64_t>(d->T) * d->E < (int64_t(1) << 31), MOE_ERR_UNSUPPORTED,
               "moe_route: T*E too large");
@@ -550,6 +760,8 @@ extern "C" int64_t moe_route_capacity(const moe_route_desc* d) {
 extern "C" int64_t moe_max_rows(const moe_route_desc* d) {
   if (validate(d) != MOE_OK) return -1;
   const int64_t tk = d->T * d->K;
+  const int64_t raw = raw_capacity(d);
+  if (raw >= 0 && d->pad_to_capacity) return std::min(raw, d->T) * d->E;  // every expert padded
   const int64_t cap = capacity_of(d);
   return cap < 0 ? tk : std::min(tk, cap * d->E);
 }
@@ -562,8 +774,8 @@ extern "C" moe_status moe_route(const moe_route_desc* d, const void* x, const fl
   moe_status st = validate(d);
   if (st != MOE_OK) return st;
   MOE_REQUIRE(tokens_per_expert, MOE_ERR_ARG, "moe_route: tokens_per_expert is required");
-  MOE_REQUIRE(expert_bias == nullptr || d->score == MOE_SCORE_SIGMOID, MOE_ERR_UNSUPPORTED,
-              "moe_route: expert_bias is defined for sigmoid scoring only");
+  MOE_REQUIRE(expert_bias == nullptr || d->score != MOE_SCORE_SOFTMAX, MOE_ERR_UNSUPPORTED,
+              "moe_route: expert_bias is defined for sigmoid and sqrtsoftplus scoring only");
   const hipStream_t s = as_stream(stream);
   const int64_t T = d->T, E = d->E;
   if (T == 0) {  // [0,E] tensors may be NULL
@@ -640,11 +852,86 @@ extern "C" moe_status moe_route(const moe_route_desc* d, const void* x, const fl
   else if (epl <= 8) launch_topk<8>(nblk, s, ta);
   else launch_topk<16>(nblk, s, ta);
 
-  // per-expert counts: tokens_per_expert = min(count, capacity)
+  const int64_t raw = raw_capacity(d);
+  if (raw >= 0 && (d->drop_policy == MOE_DROP_PROBS || d->pad_to_capacity)) {
+    // per-expert capacity mask (probs policy, or padding to capacity)
+    if (raw >= T && !d->pad_to_capacity) {
+      launch_count_scan(hist, nblk, E, -1, blkoff, tokens_per_expert, s);  // nothing dropped
+    } else {
+      hipLaunchKernelGGL(router_capacity_kernel, dim3(static_cast<unsigned>(E)), dim3(256), 0, s, T,
+                         static_cast<int>(E), std::min(raw, T), d->drop_policy,
+                         d->pad_to_capacity, probs, routing_map, tokens_per_expert);
+    }
+    return check_launch("moe_route");
+  }
+  // position policy: tokens_per_expert = min(count, capacity), then drop
+  // entries ranked >= capacity
   const int64_t cap = capacity_of(d);
   launch_count_scan(hist, nblk, E, cap, blkoff, tokens_per_expert, s);
   if (cap >= 0)
     hipLaunchKernelGGL(router_drop_kernel, dim3(static_cast<unsigned>(nblk)), dim3(256), 0, s, blkoff,
                        T, static_cast<int>(E), cap, probs, routing_map);
   return check_launch("moe_route");
+}
+
+extern "C" size_t moe_aux_loss_workspace_size(int64_t T, int64_t E) {
+  if (T <= 0 || E <= 0 || E > kMaxExperts) return 0;
+  return align_up(static_cast<size_t>(ceil_div(T, kAuxTok) * E) * sizeof(float), 256);
+}
+
+extern "C" moe_status moe_router_aux_loss(int64_t T, int64_t E, int64_t K, int32_t score,
+                                          const float* scores, const int32_t* tokens_per_expert,
+                                          float* loss, void* workspace, size_t workspace_bytes,
+                                          void* stream) {
+  MOE_REQUIRE(T >= 0 && T < (int64_t(1) << 31), MOE_ERR_ARG, "moe_router_aux_loss: T out of range");
+  MOE_REQUIRE(E >= 1 && E <= kMaxExperts, MOE_ERR_ARG, "moe_router_aux_loss: E=%lld not in [1,%lld]",
+              (long long)E, (long long)kMaxExperts);
+  MOE_REQUIRE(K >= 1 && K <= E, MOE_ERR_ARG, "moe_router_aux_loss: bad K=%lld", (long long)K);
+  MOE_REQUIRE(score == MOE_SCORE_SOFTMAX || score == MOE_SCORE_SIGMOID ||
+                  score == MOE_SCORE_SQRTSOFTPLUS,
+              MOE_ERR_ARG, "moe_router_aux_loss: bad score %d", score);
+  MOE_REQUIRE(T * E < (int64_t(1) << 31), MOE_ERR_UNSUPPORTED, "moe_router_aux_loss: T*E too large");
+  MOE_REQUIRE(loss && tokens_per_expert, MOE_ERR_ARG, "moe_router_aux_loss: NULL output or counts");
+  const hipStream_t s = as_stream(stream);
+  if (T == 0) {
+    launch_fill_i32(reinterpret_cast<int32_t*>(loss), 1, 0, s);  // 0.0f
+    return check_launch("moe_router_aux_loss(T=0)");
+  }
+  MOE_REQUIRE(scores, MOE_ERR_ARG, "moe_router_aux_loss: scores is NULL");
+  const size_t need = moe_aux_loss_workspace_size(T, E);
+  MOE_REQUIRE(workspace && workspace_bytes >= need, MOE_ERR_WORKSPACE,
+              "moe_router_aux_loss: workspace of %zu bytes given, %zu needed", workspace_bytes, need);
+  const int64_t nblk = ceil_div(T, kAuxTok);
+  float* partial = static_cast<float*>(workspace);
+  hipLaunchKernelGGL(aux_partial_kernel, dim3(static_cast<unsigned>(nblk)), dim3(256), 0, s, scores,
+                     T, static_cast<int>(E), score == MOE_SCORE_SOFTMAX ? 0 : 1, partial);
+  hipLaunchKernelGGL(aux_final_kernel, dim3(1), dim3(256), 0, s, partial, nblk, T,
+                     static_cast<int>(E), static_cast<int>(K), tokens_per_expert, loss);
+  return check_launch("moe_router_aux_loss");
+}
+
+extern "C" moe_status moe_accumulate_tokens_per_expert(int64_t E, const int32_t* tokens_per_expert,
+                                                       int64_t* local_tokens_per_expert,
+                                                       void* stream) {
+  MOE_REQUIRE(E >= 1 && E <= kMaxExperts, MOE_ERR_ARG,
+              "moe_accumulate_tokens_per_expert: E=%lld not in [1,%lld]", (long long)E,
+              (long long)kMaxExperts);
+  MOE_REQUIRE(tokens_per_expert && local_tokens_per_expert, MOE_ERR_ARG,
+              "moe_accumulate_tokens_per_expert: NULL tensor argument");
+  hipLaunchKernelGGL(accumulate_tokens_kernel, dim3(static_cast<unsigned>(ceil_div(E, 256))),
+                     dim3(256), 0, as_stream(stream), static_cast<int>(E), tokens_per_expert,
+                     local_tokens_per_expert);
+  return check_launch("moe_accumulate_tokens_per_expert");
+}
+
+extern "C" moe_status moe_update_expert_bias(int64_t E, int64_t* local_tokens_per_expert,
+                                             float* expert_bias, float update_rate, int32_t reset,
+                                             void* stream) {
+  MOE_REQUIRE(E >= 1 && E <= kMaxExperts, MOE_ERR_ARG,
+              "moe_update_expert_bias: E=%lld not in [1,%lld]", (long long)E, (long long)kMaxExperts);
+  MOE_REQUIRE(local_tokens_per_expert && expert_bias, MOE_ERR_ARG,
+              "moe_update_expert_bias: NULL tensor argument");
+  hipLaunchKernelGGL(update_bias_kernel, dim3(1), dim3(256), 0, as_stream(stream),
+                     static_cast<int>(E), local_tokens_per_expert, expert_bias, update_rate, reset);
+  return check_launch("moe_update_expert_bias");
 }

@@ -13,9 +13,13 @@ from typing import Dict, Optional
 import torch
 
 from . import _lib
-from ._lib import MOE_BF16, MOE_F32, MOE_SCORE_SIGMOID, MOE_SCORE_SOFTMAX, RouteDesc, check
+from ._lib import (MOE_BF16, MOE_DROP_POSITION, MOE_DROP_PROBS, MOE_F32, MOE_SCORE_SIGMOID,
+                   MOE_SCORE_SOFTMAX, MOE_SCORE_SQRTSOFTPLUS, RouteDesc, check)
 
 _DT = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16}
+_SCORE = {"softmax": MOE_SCORE_SOFTMAX, "sigmoid": MOE_SCORE_SIGMOID,
+          "sqrtsoftplus": MOE_SCORE_SQRTSOFTPLUS}
+_DROP = {"position": MOE_DROP_POSITION, "probs": MOE_DROP_PROBS}
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -48,10 +52,15 @@ def _dtype_code(t: torch.Tensor, name: str) -> int:
 
 def route_desc(T: int, h: int, E: int, K: int, x_dtype: torch.dtype, score: str = "softmax",
                pre_softmax: bool = True, capacity_factor: float = 0.0,
-               min_capacity: int = 0) -> RouteDesc:
-    return RouteDesc(T, h, E, K, _DT[x_dtype],
-                     MOE_SCORE_SIGMOID if score == "sigmoid" else MOE_SCORE_SOFTMAX,
-                     1 if pre_softmax else 0, float(capacity_factor), int(min_capacity))
+               min_capacity: int = 0, drop_policy: str = "position",
+               pad_to_capacity: bool = False) -> RouteDesc:
+    if score not in _SCORE:
+        raise ValueError(f"unknown score function {score!r}")
+    if drop_policy not in _DROP:
+        raise ValueError(f"unknown drop policy {drop_policy!r}")
+    return RouteDesc(T, h, E, K, _DT[x_dtype], _SCORE[score], 1 if pre_softmax else 0,
+                     float(capacity_factor), int(min_capacity), _DROP[drop_policy],
+                     1 if pad_to_capacity else 0)
 
 
 def moe_max_rows(desc: RouteDesc) -> int:
@@ -65,7 +74,8 @@ def moe_route_capacity(desc: RouteDesc) -> int:
 def moe_route(x: Optional[torch.Tensor], w_router: Optional[torch.Tensor], *, K: int,
               b_router: Optional[torch.Tensor] = None, expert_bias: Optional[torch.Tensor] = None,
               score: str = "softmax", pre_softmax: bool = True, capacity_factor: float = 0.0,
-              min_capacity: int = 0, logits_in: Optional[torch.Tensor] = None,
+              min_capacity: int = 0, drop_policy: str = "position", pad_to_capacity: bool = False,
+              logits_in: Optional[torch.Tensor] = None,
               want_logits: bool = False, want_scores: bool = False,
               T: Optional[int] = None, h: Optional[int] = None) -> Dict[str, torch.Tensor]:
     """Router forward (gating, score, top-k, capacity drop)."""
@@ -88,7 +98,8 @@ def moe_route(x: Optional[torch.Tensor], w_router: Optional[torch.Tensor], *, K:
         _need(b_router, "b_router", torch.float32, (E,))
     if expert_bias is not None:
         _need(expert_bias, "expert_bias", torch.float32, (E,))
-    desc = route_desc(T_, h_, E, K, xdt, score, pre_softmax, capacity_factor, min_capacity)
+    desc = route_desc(T_, h_, E, K, xdt, score, pre_softmax, capacity_factor, min_capacity,
+                      drop_policy, pad_to_capacity)
     probs = torch.empty((T_, E), dtype=torch.float32, device=dev)
     rmap = torch.empty((T_, E), dtype=torch.uint8, device=dev)
     tpe = torch.empty((E,), dtype=torch.int32, device=dev)
@@ -108,6 +119,47 @@ def moe_route(x: Optional[torch.Tensor], w_router: Optional[torch.Tensor], *, K:
     if scores is not None:
         out["scores"] = scores
     return out
+
+
+def moe_router_aux_loss(scores: torch.Tensor, tokens_per_expert: torch.Tensor, *, K: int,
+                        score: str = "softmax") -> torch.Tensor:
+    """Forward value of the load-balancing loss, E * sum_e f_e * P_e (fp32 [1])."""
+    lib = _lib.load()
+    _need(scores, "scores", torch.float32)
+    T, E = scores.shape
+    _need(tokens_per_expert, "tokens_per_expert", torch.int32, (E,))
+    loss = torch.empty((1,), dtype=torch.float32, device=scores.device)
+    ws_bytes = int(lib.moe_aux_loss_workspace_size(T, E))
+    ws = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=scores.device)
+    st = lib.moe_router_aux_loss(T, E, K, _SCORE[score], _ptr(scores), _ptr(tokens_per_expert),
+                                 _ptr(loss), _ptr(ws), ws_bytes, _stream())
+    check("moe_router_aux_loss", st)
+    return loss
+
+
+def moe_accumulate_tokens_per_expert(tokens_per_expert: torch.Tensor,
+                                     local_tokens_per_expert: torch.Tensor) -> torch.Tensor:
+    """local_tokens_per_expert += tokens_per_expert (int64, in place)."""
+    E = tokens_per_expert.shape[0]
+    _need(tokens_per_expert, "tokens_per_expert", torch.int32, (E,))
+    _need(local_tokens_per_expert, "local_tokens_per_expert", torch.int64, (E,))
+    st = _lib.load().moe_accumulate_tokens_per_expert(E, _ptr(tokens_per_expert),
+                                                      _ptr(local_tokens_per_expert), _stream())
+    check("moe_accumulate_tokens_per_expert", st)
+    return local_tokens_per_expert
+
+
+def moe_update_expert_bias(local_tokens_per_expert: torch.Tensor, expert_bias: torch.Tensor,
+                           update_rate: float, reset: bool = True) -> torch.Tensor:
+    """expert_bias += sign(mean - count) * update_rate (in place); optionally
+    zero the running counts."""
+    E = expert_bias.shape[0]
+    _need(local_tokens_per_expert, "local_tokens_per_expert", torch.int64, (E,))
+    _need(expert_bias, "expert_bias", torch.float32, (E,))
+    st = _lib.load().moe_update_expert_bias(E, _ptr(local_tokens_per_expert), _ptr(expert_bias),
+                                            float(update_rate), 1 if reset else 0, _stream())
+    check("moe_update_expert_bias", st)
+    return expert_bias
 
 
 def moe_permute(x: torch.Tensor, routing_map: torch.Tensor, probs: torch.Tensor, K: int,
@@ -223,6 +275,7 @@ def moe_combine(expert_out: torch.Tensor, permuted_probs: torch.Tensor, row_id_m
 
 def moe_forward(inp: Dict[str, torch.Tensor], *, K: int, score: str = "softmax",
                 pre_softmax: bool = True, capacity_factor: float = 0.0, min_capacity: int = 0,
+                drop_policy: str = "position", pad_to_capacity: bool = False,
                 want_logits: bool = False) -> Dict[str, torch.Tensor]:
     """route -> permute -> grouped SwiGLU experts -> combine (+ shared expert).
 
@@ -234,6 +287,7 @@ def moe_forward(inp: Dict[str, torch.Tensor], *, K: int, score: str = "softmax",
     r = moe_route(x, inp["w_router"], K=K, b_router=inp.get("b_router"),
                   expert_bias=inp.get("expert_bias"), score=score, pre_softmax=pre_softmax,
                   capacity_factor=capacity_factor, min_capacity=min_capacity,
+                  drop_policy=drop_policy, pad_to_capacity=pad_to_capacity,
                   want_logits=want_logits)
     pm = moe_permute(x, r["routing_map"], r["probs"], K, r["max_rows"])
     act = moe_grouped_fc1_swiglu(pm["permuted_x"], r["tokens_per_expert"], inp["w_gate"],

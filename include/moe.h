@@ -52,9 +52,15 @@ typedef enum {
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
-typedef enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_score;
+typedef enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1, MOE_SCORE_SQRTSOFTPLUS = 2 } moe_score;
 
-/* Version of this interface. */
+/* Which tokens an expert keeps when more than its capacity are routed to it
+ * ([MC] §8): the earliest tokens ("position"), or the tokens with the
+ * largest routing probs ("probs"; equal probs: the earlier token). */
+typedef enum { MOE_DROP_POSITION = 0, MOE_DROP_PROBS = 1 } moe_drop_policy;
+
+/* Version of this interface (2: drop policy, padding to capacity,
+ * sqrtsoftplus scores, router side outputs). */
 int moe_abi_version(void);
 
 /* Message for the last non-OK status returned on the calling thread. */
@@ -64,8 +70,8 @@ const char* moe_last_error(void);
  * Router: gating linear + score function + top-k + capacity drop.
  * [MC] §3 (logits = x W^T (+ b) in fp32), §4 (routing returns probs and a
  * [T,E] routing map), §5 (score functions, selection-only expert bias), §8
- * (capacity and the "position" drop policy); [DS] §3 (capacity factor,
- * minimum capacity).
+ * (capacity, the "position" and "probs" drop policies, padding to
+ * capacity); [DS] §3 (capacity factor, minimum capacity).
  * ------------------------------------------------------------------------ */
 typedef struct {
   int64_t T;                /* tokens (sequence x batch, flattened) */
@@ -79,9 +85,16 @@ typedef struct {
                                the logits, then softmax over the K chosen */
   float capacity_factor;    /* <= 0: dropless.  > 0: capacity per expert =
                                max(ceil(T*K*capacity_factor/E), min_capacity)
-                               (ratio computed in double); each expert keeps
-                               the earliest tokens routed to it */
+                               (ratio computed in double) */
   int64_t min_capacity;     /* lower bound of the capacity; 0 = none */
+  int32_t drop_policy;      /* moe_drop_policy (with a capacity) */
+  int32_t pad_to_capacity;  /* with a capacity: 1 = every expert receives
+                               exactly min(capacity, T) tokens: the capacity
+                               mask itself becomes the routing map, so an
+                               expert with fewer routed tokens is padded with
+                               the earliest tokens not routed to it (prob 0);
+                               a capacity >= T routes every token to every
+                               expert.  0 = map AND mask */
 } moe_route_desc;
 
 /* Bytes of device workspace moe_route needs (0 is a valid answer only for
@@ -93,8 +106,8 @@ size_t moe_route_workspace_size(const moe_route_desc* desc);
 int64_t moe_route_capacity(const moe_route_desc* desc);
 
 /* Upper bound on the number of routed rows N = sum(tokens_per_expert):
- * T*K when dropless, else min(T*K, E*capacity).  Size permute/expert
- * buffers with it. */
+ * T*K when dropless, else min(T*K, E*capacity); E*min(capacity, T) when
+ * padding to capacity.  Size permute/expert buffers with it. */
 int64_t moe_max_rows(const moe_route_desc* desc);
 
 /*
@@ -103,29 +116,72 @@ int64_t moe_max_rows(const moe_route_desc* desc);
  *   w_router     [E,h]  fp32            gating weight (ignored if logits_in)
  *   b_router     [E]    fp32 or NULL    gating bias; part of the logits, so it
  *                                       affects both the choice and the probs
- *   expert_bias  [E]    fp32 or NULL    sigmoid only: added to the scores for
- *                                       the top-K choice, never to the probs
- *                                       ([MC] §5, §7)
+ *   expert_bias  [E]    fp32 or NULL    sigmoid / sqrtsoftplus only: added to the
+ *                                       scores for the top-K choice, never to
+ *                                       the probs ([MC] §5, §7)
  *   logits_in    [T,E]  fp32 or NULL    route from these logits instead of
  *                                       computing x w^T (+b)
  *   logits_out   [T,E]  fp32 or NULL    receives the logits
  *   scores_out   [T,E]  fp32 or NULL    receives the score function over all E
- *                                       (softmax over E, or sigmoid)
+ *                                       (softmax over E, sigmoid or sqrtsoftplus)
  *   probs        [T,E]  fp32            out: combine weights, 0 off the map
  *   routing_map  [T,E]  uint8           out: 1 where token t is routed to e
  *   tokens_per_expert [E] int32         out: routing_map summed over tokens
  *   workspace    moe_route_workspace_size(desc) bytes of device memory
  * Top-K order: larger key first, lower expert index on ties.  Keys: the fp32
- * logits for softmax (softmax is increasing), sigmoid(logit) (+ expert_bias)
- * for sigmoid, where sigmoid is evaluated by a fixed sequence of IEEE fp32
- * operations so that its bits are reproducible.  Sigmoid probs are the
- * chosen scores over (their sum + 1e-20).
+ * logits for softmax (softmax is increasing); score(logit) (+ expert_bias)
+ * for sigmoid and sqrtsoftplus = sqrt(log(1 + e^x)), both evaluated by
+ * fixed sequences of IEEE fp32 operations so that their bits are
+ * reproducible.  Sigmoid / sqrtsoftplus probs are the chosen scores over
+ * (their sum + 1e-20).  With a capacity, the drop policy and padding act on
+ * these probs and map after the choice; dropped entries get map 0, prob 0.
  */
 moe_status moe_route(const moe_route_desc* desc, const void* x, const float* w_router,
                      const float* b_router, const float* expert_bias, const float* logits_in,
                      float* logits_out, float* scores_out, float* probs, uint8_t* routing_map,
                      int32_t* tokens_per_expert, void* workspace, size_t workspace_bytes,
                      void* stream);
+
+/* ------------------------------------------------------------------------
+ * Router side outputs.  [MC] §6: the switch load-balancing loss has the form
+ * E * sum_i f_i * P_i; §7: loss-free balance keeps an fp32 expert bias and
+ * a running per-expert token count, and moves the bias one step of the
+ * update rate by the sign of (mean count - count).
+ * ------------------------------------------------------------------------ */
+
+/* Bytes of device workspace moe_router_aux_loss needs. */
+size_t moe_aux_loss_workspace_size(int64_t T, int64_t E);
+
+/*
+ * moe_router_aux_loss — forward value of the load-balancing loss (no
+ * coefficient): loss = E * sum_e f_e * P_e with f_e = tokens_per_expert[e]
+ * / (T*K) and P_e = mean over tokens of the router's probability mass on e:
+ * the softmax scores as given, or for sigmoid / sqrtsoftplus the scores
+ * normalised per token to sum 1 (over their sum + 1e-20).  fp32, summed in a
+ * fixed order (reproducible).
+ *   scores            [T,E] fp32   the scores_out of moe_route
+ *   tokens_per_expert [E]   int32  the moe_route output (after dropping)
+ *   loss              [1]   fp32   out
+ */
+moe_status moe_router_aux_loss(int64_t T, int64_t E, int64_t K, int32_t score,
+                               const float* scores, const int32_t* tokens_per_expert,
+                               float* loss, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/* local_tokens_per_expert[e] += tokens_per_expert[e]   (int64 running count) */
+moe_status moe_accumulate_tokens_per_expert(int64_t E, const int32_t* tokens_per_expert,
+                                            int64_t* local_tokens_per_expert, void* stream);
+
+/*
+ * moe_update_expert_bias — one controller step on one GPU (no all-reduce):
+ *   expert_bias[e] += sign(mean - local[e]) * update_rate   (one fp32 add)
+ * where the sign is decided exactly as sign(sum(local) - E * local[e]).  With
+ * reset != 0 the running counts are then set to 0.
+ *   local_tokens_per_expert [E] int64 (in, and out when reset)
+ *   expert_bias             [E] fp32  (in/out)
+ */
+moe_status moe_update_expert_bias(int64_t E, int64_t* local_tokens_per_expert, float* expert_bias,
+                                  float update_rate, int32_t reset, void* stream);
 
 /* ------------------------------------------------------------------------
  * Dispatch preprocess: permute token rows into expert-major order.
@@ -139,16 +195,20 @@ size_t moe_permute_workspace_size(int64_t T, int64_t E);
 /*
  * moe_permute — rows sorted by (expert ascending, token ascending).
  *   x              [T,h]        dtype   h must be a multiple of 8
- *   routing_map    [T,E]        uint8   nonzero = routed (at most K per row)
- *   probs          [T,E]        fp32
+ *   routing_map    [T,E]        uint8   nonzero = routed (any number per row:
+ *                                       padding to capacity adds entries)
+ *   probs          [T,E]        fp32    at most K nonzero per row
  *   permuted_x     [max_rows,h] dtype   out: permuted_x[i] = x[sorted_token[i]]
  *   permuted_probs [max_rows]   fp32    out: probs[sorted_token[i], expert of row i]
  *   sorted_token   [max_rows]   int32   out: source token of row i
- *   row_id_map     [T,K]        int32   out: row of token t's k-th routed expert
- *                                       (ascending expert order), -1 if unused
+ *   row_id_map     [T,K]        int32   out: row of token t's k-th map entry with
+ *                                       a nonzero prob (ascending expert order),
+ *                                       -1 if unused.  Entries with prob 0 get
+ *                                       rows but no slot: they add nothing to
+ *                                       the combine.
  *   expert_offsets [E+1]        int32   out: first row of each expert; [E] = N
- * Rows at index >= N are left untouched.  Rows beyond max_rows and routed
- * entries beyond K in a map row are not written (outside the contract).
+ * Rows at index >= N are left untouched.  Rows beyond max_rows and nonzero
+ * probs beyond K in a row are not written (outside the contract).
  */
 moe_status moe_permute(int64_t T, int64_t h, int64_t E, int64_t K, int32_t dtype, const void* x,
                        const uint8_t* routing_map, const float* probs, int64_t max_rows,

@@ -28,13 +28,15 @@ def test_library_exports_every_declared_function():
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(_lib.SIGNATURES) == names
-    assert lib.moe_abi_version() == 1
+    assert lib.moe_abi_version() == 2
 
 
 def test_route_desc_layout_matches_c():
-    # int64 x4, int32 x3, float, int64: 56 bytes with natural alignment
-    assert ctypes.sizeof(_lib.RouteDesc) == 56
+    # int64 x4, int32 x3, float, int64, int32 x2: 64 bytes with natural alignment
+    assert ctypes.sizeof(_lib.RouteDesc) == 64
     assert _lib.RouteDesc.min_capacity.offset == 48
+    assert _lib.RouteDesc.drop_policy.offset == 56
+    assert _lib.RouteDesc.pad_to_capacity.offset == 60
 
 
 def _desc(**kw):
