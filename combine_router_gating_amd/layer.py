@@ -24,7 +24,8 @@ class MoELayerForward:
     STAGES = ("route", "permute", "fc1", "fc2", "shared", "combine")
 
     def __init__(self, inp: Dict[str, torch.Tensor], *, K: int, score: str = "softmax",
-                 pre_softmax: bool = True, capacity_factor: float = 0.0, min_capacity: int = 0):
+                 pre_softmax: bool = True, capacity_factor: float = 0.0, min_capacity: int = 0,
+                 drop_policy: str = "position", pad_to_capacity: bool = False):
         self.lib = _lib.load()
         self.inp = inp
         x = _need(inp["x"], "x")
@@ -35,7 +36,7 @@ class MoELayerForward:
         self.dt = _dtype_code(x, "x")
         dev = x.device
         self.desc = route_desc(self.T, self.h, self.E, K, x.dtype, score, pre_softmax,
-                               capacity_factor, min_capacity)
+                               capacity_factor, min_capacity, drop_policy, pad_to_capacity)
         self.max_rows = int(self.lib.moe_max_rows(ctypes.byref(self.desc)))
         T, h, E, f, R = self.T, self.h, self.E, self.f, self.max_rows
         e = torch.empty

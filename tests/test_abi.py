@@ -135,3 +135,50 @@ def test_product_does_not_import_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"^\s*(import|from)\s+oracle\b", text, re.M), f
                 assert "oracle/" not in text, f
+
+
+def test_max_rows_with_padding_to_capacity():
+    d = _desc(capacity_factor=0.5, pad_to_capacity=True)          # cap 64 < T
+    assert moe.moe_max_rows(d) == 64 * 64
+    d = _desc(capacity_factor=100.0, pad_to_capacity=True)        # cap >= T: every pair
+    assert moe.moe_max_rows(d) == 8192 * 64
+    d = _desc(capacity_factor=0.0, pad_to_capacity=True)          # dropless: no padding
+    assert moe.moe_max_rows(d) == 8192
+
+
+def test_route_rejects_bad_policy_and_score():
+    d = _desc()
+    d.drop_policy = 5
+    st, msg = _status("moe_route", ctypes.byref(d), *([None] * 10), None, 0, None)
+    assert st == _lib.MOE_ERR_ARG and "drop_policy" in msg
+    d = _desc()
+    d.score = 3
+    st, msg = _status("moe_route", ctypes.byref(d), *([None] * 10), None, 0, None)
+    assert st == _lib.MOE_ERR_ARG and "score" in msg
+    with pytest.raises(ValueError):
+        moe.route_desc(8, 8, 4, 1, torch.float32, score="tanh")
+    with pytest.raises(ValueError):
+        moe.route_desc(8, 8, 4, 1, torch.float32, drop_policy="random")
+
+
+def test_side_output_entry_points_reject_bad_arguments():
+    p = ctypes.c_void_p(16)
+    st, _ = _status("moe_router_aux_loss", 10, 0, 1, 0, p, p, p, p, 1 << 20, None)
+    assert st == _lib.MOE_ERR_ARG                                   # E = 0
+    st, _ = _status("moe_router_aux_loss", 10, 4, 5, 0, p, p, p, p, 1 << 20, None)
+    assert st == _lib.MOE_ERR_ARG                                   # K > E
+    st, _ = _status("moe_router_aux_loss", 10, 4, 2, 9, p, p, p, p, 1 << 20, None)
+    assert st == _lib.MOE_ERR_ARG                                   # score
+    st, _ = _status("moe_router_aux_loss", 10, 4, 2, 0, p, p, None, p, 1 << 20, None)
+    assert st == _lib.MOE_ERR_ARG                                   # no output
+    st, _ = _status("moe_router_aux_loss", 100, 4, 2, 0, p, p, p, p, 4, None)
+    assert st == _lib.MOE_ERR_WORKSPACE
+    assert moe.load().moe_aux_loss_workspace_size(100, 4) >= 2 * 4 * 4
+    st, _ = _status("moe_accumulate_tokens_per_expert", 0, p, p, None)
+    assert st == _lib.MOE_ERR_ARG
+    st, _ = _status("moe_accumulate_tokens_per_expert", 4, None, p, None)
+    assert st == _lib.MOE_ERR_ARG
+    st, _ = _status("moe_update_expert_bias", 2000, p, p, ctypes.c_float(0.1), 1, None)
+    assert st == _lib.MOE_ERR_ARG
+    st, _ = _status("moe_update_expert_bias", 4, p, None, ctypes.c_float(0.1), 1, None)
+    assert st == _lib.MOE_ERR_ARG
