@@ -7,10 +7,19 @@ HBM.  Prints ONE JSON line.  The default workload is the Switch-style layer
 router); --config picks another layer shape.
 
 Per-stage durations come from HIP events recorded on the stream the kernels
-run on, over every timed step; the roofline object uses the dominant
-single-kernel stage.  `traffic` (HBM bytes per launch from rocprofv3
-FETCH_SIZE/WRITE_SIZE counters) is read from profiles/ and reported only
-while the kernel source is unchanged since the counters were taken.
+run on, over every timed step (median, p10, p90 are reported); the roofline
+object uses the dominant single-kernel stage.  `traffic` (HBM bytes per
+launch from rocprofv3 FETCH_SIZE/WRITE_SIZE counters) is read from profiles/
+and reported only while the kernel source is unchanged since the counters
+were taken.  After the timed region, a second pass times each step with the
+last-level caches flushed first (a 512 MiB write before every step; the
+flush is outside the events) and reports it as "cold".
+
+Layer options (on by default, --no-gather / --no-overlap to turn off): the
+permute writes no row copies and FC1 gathers token rows through
+sorted_token; the shared expert (when the layer has one) runs on a second
+stream, joined before the combine.  With the overlap on, main-stream stage
+times include contention with the shared expert.
 """
 from __future__ import annotations
 
@@ -47,6 +56,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="run one plain device copy of this size first (counter calibration)")
+    p.add_argument("--no-gather", action="store_true", help="materialise permuted_x")
+    p.add_argument("--no-overlap", action="store_true", help="shared expert on the main stream")
+    p.add_argument("--no-cold", action="store_true", help="skip the cache-flushed pass")
     return p.parse_args()
 
 
@@ -77,16 +89,17 @@ def read_traffic(stage: str, workload: str):
         return None
 
 
-def stage_work(cfg, n, T, fs):
+def stage_work(cfg, n, T, fs, gather=False):
     """Algorithmic bytes and flops of each stage (kept rows only, no padding,
-    each tensor moved once)."""
+    each tensor moved once).  With `gather` the permute moves no rows."""
     b = 4 if cfg.dtype == "f32" else 2
     h, f, E, K = cfg.h, cfg.f, cfg.E, cfg.K
     N = int(sum(n))
     active = int(sum(1 for v in n if v > 0))
     w = {
         "route": (T * h * b + E * h * 4 + T * E * (4 + 4 + 1) + E * 4, 2.0 * T * h * E),
-        "permute": (T * h * b + N * h * b + T * E * (1 + 4) + N * 8 + T * K * 4 + E * 4, 0.0),
+        "permute": ((0 if gather else T * h * b + N * h * b) + T * E * (1 + 4) + N * 8 + T * K * 4
+                    + E * 4, 0.0),
         "fc1": (active * 2 * h * f * b + N * h * b + N * f * b, 4.0 * N * h * f),
         "fc2": (active * h * f * b + N * f * b + N * h * b, 2.0 * N * h * f),
         "combine": (N * h * b + T * K * 4 + N * 4 + T * h * b + (T * h * b if fs else 0), 0.0),
@@ -96,7 +109,7 @@ def stage_work(cfg, n, T, fs):
     return w
 
 
-def cpu_baseline(cfg, inp, sample_tokens):
+def cpu_baseline(cfg, inp, sample_tokens, min_seconds=10.0):
     """The oracle, as it stands, on the first `sample_tokens` tokens of the
     batch run as a batch of their own (same weights and routing options)."""
     import numpy as np
@@ -125,16 +138,21 @@ def cpu_baseline(cfg, inp, sample_tokens):
         return (host["w_gate"][e].astype(np.float64), host["w_up"][e].astype(np.float64),
                 host["w_down"][e].astype(np.float64))
 
-    t0 = time.perf_counter()
-    oracle.moe_forward(x, wr, br, weights, K=cfg.K, dtype=cfg.dtype, score=cfg.score,
-                       pre_softmax=cfg.pre_softmax, expert_bias=eb,
-                       capacity_factor=cfg.capacity_factor, min_capacity=cfg.min_capacity,
-                       shared=shared)
-    dt = time.perf_counter() - t0
+    # repeat the sample until about 10 s of CPU work have been timed
+    runs, total = 0, 0.0
+    while runs == 0 or (total < min_seconds and runs < 20):
+        t0 = time.perf_counter()
+        oracle.moe_forward(x, wr, br, weights, K=cfg.K, dtype=cfg.dtype, score=cfg.score,
+                           pre_softmax=cfg.pre_softmax, expert_bias=eb,
+                           capacity_factor=cfg.capacity_factor, min_capacity=cfg.min_capacity,
+                           shared=shared)
+        total += time.perf_counter() - t0
+        runs += 1
+    dt = total / runs
     return {"value": S / dt, "unit": "tokens/s", "cores": int(blas_threads), "kind": "oracle",
             "sample": f"first {S} of {cfg.T} tokens run as one batch (same weights and routing "
                       f"options; capacity recomputed for that batch), float64 NumPy, "
-                      f"{dt:.1f} s"}
+                      f"{runs} run(s), {total:.1f} s in total"}
 
 
 def torch_float32():
@@ -143,6 +161,11 @@ def torch_float32():
 
 
 DEFAULT_CPU_SAMPLE = {"tiny": 256, "switch": 8192, "mixtral": 256, "qwen3": 512, "dsv3": 128}
+
+
+def pct(v, q):
+    import numpy as np
+    return float(np.percentile(np.asarray(v), q))
 
 
 def main():
@@ -167,14 +190,16 @@ def main():
         torch.cuda.synchronize()
         del a, bb
     inp = datagen.make_inputs(cfg, seed=args.seed, device=dev)
+    gather = not args.no_gather
     layer = MoELayerForward(inp, K=cfg.K, score=cfg.score, pre_softmax=cfg.pre_softmax,
-                            capacity_factor=cfg.capacity_factor, min_capacity=cfg.min_capacity)
+                            capacity_factor=cfg.capacity_factor, min_capacity=cfg.min_capacity,
+                            gather=gather, overlap_shared=not args.no_overlap)
     for _ in range(args.warmup):
         layer.forward()
     torch.cuda.synchronize()
 
-    # timed region: K steps, events at every stage boundary
-    stages = [s for s in layer.STAGES if s != "shared" or layer.shared]
+    # timed region: K steps, events at every stage boundary on the main stream
+    stages = layer.stages()
     events = []
 
     def mark(name):
@@ -191,20 +216,24 @@ def main():
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
 
-    stage_ms = {s: 0.0 for s in stages}
+    per_step = {s: [] for s in stages}
+    fwd = []
     for evs in events:
         for (name, a), (_, b) in zip(evs[:-1], evs[1:]):
-            stage_ms[name] += a.elapsed_time(b)
-    stage_ms = {s: v / args.steps for s, v in stage_ms.items()}
+            per_step[name].append(a.elapsed_time(b))
+        fwd.append(evs[0][1].elapsed_time(evs[-1][1]))
+    stage_ms = {s: sum(v) / len(v) for s, v in per_step.items()}
 
     n = layer.tokens_per_expert.cpu().tolist()
     N = int(sum(n))
-    work = stage_work(cfg, n, cfg.T, layer.fs if layer.shared else 0)
+    work = stage_work(cfg, n, cfg.T, layer.fs if layer.shared else 0, gather)
     gemm_stages = [s for s in ("fc1", "fc2", "shared") if s in stage_ms]
     gemm_flops = sum(work[s][1] for s in gemm_stages)
+    gemm_bytes = sum(work[s][0] for s in gemm_stages)
     gemm_ms = sum(stage_ms[s] for s in gemm_stages)
     gemm_tflops = gemm_flops / (gemm_ms * 1e-3) / 1e12
     peak_tf = MFMA_BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else FP32_PEAK_TFLOPS
+    attainable_tf = min(peak_tf, gemm_flops / gemm_bytes * HBM_PEAK_GBS * 1e9 / 1e12)
 
     single_kernel = ("fc1", "fc2", "shared", "combine")
     dom = max((s for s in stage_ms if s in single_kernel), key=lambda s: stage_ms[s])
@@ -228,8 +257,30 @@ def main():
     for s in stages:
         nb, fl = work[s]
         sec_s = stage_ms[s] * 1e-3
-        stage_report[s] = {"ms": round(stage_ms[s], 4), "GB/s": round(nb / sec_s / 1e9, 1),
+        stage_report[s] = {"ms": round(stage_ms[s], 4), "p10": round(pct(per_step[s], 10), 4),
+                           "p50": round(pct(per_step[s], 50), 4),
+                           "p90": round(pct(per_step[s], 90), 4),
+                           "GB/s": round(nb / sec_s / 1e9, 1),
                            "TFLOP/s": round(fl / sec_s / 1e12, 1) if fl else 0.0}
+
+    cold = None
+    if not args.no_cold:
+        flush = torch.empty((512 << 20) // 4, dtype=torch.float32, device=dev)
+        cold_ms = []
+        for i in range(max(5, min(args.steps, 20))):
+            flush.fill_(float(i))
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            layer.forward()
+            b.record()
+            torch.cuda.synchronize()
+            cold_ms.append(a.elapsed_time(b))
+        del flush
+        cold = {"tokens_per_s_median": cfg.T / (pct(cold_ms, 50) * 1e-3),
+                "ms_p10": round(pct(cold_ms, 10), 4), "ms_p50": round(pct(cold_ms, 50), 4),
+                "ms_p90": round(pct(cold_ms, 90), 4), "steps": len(cold_ms),
+                "flush": "512 MiB device write before each step, outside the events"}
 
     value = cfg.T / (ms_per_step * 1e-3)
     rec = {
@@ -241,12 +292,19 @@ def main():
                                f" {cfg.score}{'' if cfg.pre_softmax else '-renorm'}"
                                f" cap={cfg.capacity_factor} shared_f={cfg.shared_f}",
                    "tokens": cfg.T, "routed_rows": N, "dropped": cfg.T * cfg.K - N,
-                   "parallelism": "single GPU, EP=1"},
+                   "parallelism": "single GPU, EP=1",
+                   "gather_fc1": gather, "shared_overlap": layer.overlap_shared},
+        "forward_ms": {"mean": sum(fwd) / len(fwd), "p10": pct(fwd, 10), "p50": pct(fwd, 50),
+                       "p90": pct(fwd, 90)},
         "gemm_tflops": gemm_tflops,
         "gemm_frac_of_mfma_peak": gemm_tflops / peak_tf,
+        "gemm_attainable_tflops": attainable_tf,
+        "gemm_frac_of_attainable": gemm_tflops / attainable_tf,
         "stages": stage_report,
         "roofline": roof,
     }
+    if cold:
+        rec["cold"] = cold
     if not args.no_cpu_baseline:
         S = args.cpu_sample_tokens or DEFAULT_CPU_SAMPLE.get(cfg.name, 256)
         rec["cpu_baseline"] = cpu_baseline(cfg, inp, S)

@@ -48,6 +48,8 @@ SIGNATURES = {
                                 c_vp, c_vp, c_vp]),
     "moe_grouped_fc1_swiglu": (c_i32, [c_i64, c_i64, c_i64, c_i64, c_i32, c_vp, c_vp, c_vp,
                                        c_vp, c_vp, c_vp]),
+    "moe_grouped_fc1_swiglu_gather": (c_i32, [c_i64, c_i64, c_i64, c_i64, c_i32, c_i64, c_vp,
+                                              c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "moe_grouped_fc2": (c_i32, [c_i64, c_i64, c_i64, c_i64, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "moe_combine": (c_i32, [c_i64, c_i64, c_i64, c_i32, c_vp, c_vp, c_vp, c_i64, c_vp, c_vp,
                             c_vp]),

@@ -283,6 +283,7 @@ constexpr int body_lds_bytes() {
 template <int BM, int BN, int WM, int WN, bool FC1, int STAGES, int SBK, int SCHED, int SPREAD>
 __device__ __forceinline__ void gmm_tile(const Tile& tile, char* smem,
                                          const uint16_t* __restrict__ A,
+                                         const int32_t* __restrict__ gather, int64_t a_rows,
                                          const uint16_t* __restrict__ B0,
                                          const uint16_t* __restrict__ B1, uint16_t* __restrict__ C,
                                          int N, int K) {
@@ -320,7 +321,9 @@ __device__ __forceinline__ void gmm_tile(const Tile& tile, char* smem,
     lds_piece<SBK>((wave * LPW + j) * 1024 + lane * 16, row, c);
     if (row < BM) {
       const int lr = min(row, tile.nrows - 1);
-      src[j] = A + (tile.row0 + lr) * static_cast<int64_t>(K) + c * 8;
+      int64_t ar = tile.row0 + lr;
+      if (gather) ar = min(max(static_cast<int64_t>(gather[ar]), int64_t(0)), a_rows - 1);
+      src[j] = A + ar * static_cast<int64_t>(K) + c * 8;
     } else {
       const int br = row - BM;
       const uint16_t* base = (NB == 2 && br >= BN) ? B1 : B0;
@@ -555,7 +558,8 @@ __device__ __forceinline__ void gmm_tile(const Tile& tile, char* smem,
 // workgroup.
 template <bool FC1, int BMAX, int BN, int NW, class Body256, class Body128, class Body64>
 __global__ void __launch_bounds__(NW * 64) gmm_bf16_kernel(
-    const uint16_t* __restrict__ A, const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1,
+    const uint16_t* __restrict__ A, const int32_t* __restrict__ gather, int64_t a_rows,
+    const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1,
     uint16_t* __restrict__ C, const int32_t* __restrict__ counts, int E, int N, int K,
     int64_t max_rows) {
   constexpr int L256 = Body256::lds > Body128::lds ? Body256::lds : Body128::lds;
@@ -578,13 +582,13 @@ __global__ void __launch_bounds__(NW * 64) gmm_bf16_kernel(
   }
   tile.nrows = __builtin_amdgcn_readfirstlane(tile.nrows);
   if constexpr (BMAX == 256) {
-    if (tile.nrows > 128) Body256::run(tile, smem, A, B0, B1, C, N, K);
-    else if (tile.nrows > 64) Body128::run(tile, smem, A, B0, B1, C, N, K);
-    else Body64::run(tile, smem, A, B0, B1, C, N, K);
+    if (tile.nrows > 128) Body256::run(tile, smem, A, gather, a_rows, B0, B1, C, N, K);
+    else if (tile.nrows > 64) Body128::run(tile, smem, A, gather, a_rows, B0, B1, C, N, K);
+    else Body64::run(tile, smem, A, gather, a_rows, B0, B1, C, N, K);
   } else if constexpr (BMAX == 128) {
-    Body128::run(tile, smem, A, B0, B1, C, N, K);
+    Body128::run(tile, smem, A, gather, a_rows, B0, B1, C, N, K);
   } else {
-    Body64::run(tile, smem, A, B0, B1, C, N, K);
+    Body64::run(tile, smem, A, gather, a_rows, B0, B1, C, N, K);
   }
 }
 
@@ -593,9 +597,11 @@ template <int BM, int BN, int WM, int WN, bool FC1, int STAGES, int SBK, int SCH
 struct Body {
   static constexpr int lds = body_lds_bytes<BM, BN, FC1, STAGES, SBK>();
   __device__ __forceinline__ static void run(const Tile& t, char* smem, const uint16_t* A,
+                                             const int32_t* gather, int64_t a_rows,
                                              const uint16_t* B0, const uint16_t* B1, uint16_t* C,
                                              int N, int K) {
-    gmm_tile<BM, BN, WM, WN, FC1, STAGES, SBK, SCHED, SPREAD>(t, smem, A, B0, B1, C, N, K);
+    gmm_tile<BM, BN, WM, WN, FC1, STAGES, SBK, SCHED, SPREAD>(t, smem, A, gather, a_rows, B0, B1, C,
+                                                              N, K);
   }
 };
 
@@ -606,6 +612,8 @@ constexpr int FM = 64, FN = 64, FK = 16;
 
 template <bool FC1>
 __global__ void __launch_bounds__(kThreads) gmm_f32_kernel(const float* __restrict__ A,
+                                                           const int32_t* __restrict__ gather,
+                                                           int64_t a_rows,
                                                            const float* __restrict__ B0,
                                                            const float* __restrict__ B1,
                                                            float* __restrict__ C,
@@ -629,7 +637,9 @@ __global__ void __launch_bounds__(kThreads) gmm_f32_kernel(const float* __restri
       const int rr = i / FK, kk = i % FK;
       const int k = k0 + kk;
       const int lr = min(rr, tile.nrows - 1);
-      as[kk][rr] = k < K ? A[(tile.row0 + lr) * static_cast<int64_t>(K) + k] : 0.f;
+      int64_t ar = tile.row0 + lr;
+      if (gather) ar = min(max(static_cast<int64_t>(gather[ar]), int64_t(0)), a_rows - 1);
+      as[kk][rr] = k < K ? A[ar * static_cast<int64_t>(K) + k] : 0.f;
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
         const float* B = b == 0 ? B0 : B1;
@@ -677,25 +687,35 @@ int64_t grid_for(int64_t max_rows, int64_t E, int BM, int64_t N, int BN) {
   return ceil_div(total, 8) * 8;
 }
 
+// The activation operand: row i of the grouped GEMM is row gather[i] of
+// `base` (rows in [0, rows)) when `gather` is given, else row i.
+struct AOperand {
+  const void* base;
+  const int32_t* gather;
+  int64_t rows;
+};
+
 template <bool FC1, int BMAX, int BN, int NW, class B256, class B128, class B64>
-void launch_bf16(const void* A, const void* B0, const void* B1, void* C, const int32_t* counts,
+void launch_bf16(const AOperand& a, const void* B0, const void* B1, void* C, const int32_t* counts,
                  int64_t E, int64_t N, int64_t K, int64_t max_rows, hipStream_t s) {
   const int64_t g = grid_for(max_rows, E, BMAX, N, BN);
   hipLaunchKernelGGL((gmm_bf16_kernel<FC1, BMAX, BN, NW, B256, B128, B64>),
                      dim3(static_cast<unsigned>(g)), dim3(NW * 64), 0, s,
-                     static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B0),
-                     static_cast<const uint16_t*>(B1), static_cast<uint16_t*>(C), counts,
-                     static_cast<int>(E), static_cast<int>(N), static_cast<int>(K), max_rows);
+                     static_cast<const uint16_t*>(a.base), a.gather, a.rows,
+                     static_cast<const uint16_t*>(B0), static_cast<const uint16_t*>(B1),
+                     static_cast<uint16_t*>(C), counts, static_cast<int>(E), static_cast<int>(N),
+                     static_cast<int>(K), max_rows);
 }
 
 template <bool FC1>
-void launch_f32(const void* A, const void* B0, const void* B1, void* C, const int32_t* counts,
+void launch_f32(const AOperand& a, const void* B0, const void* B1, void* C, const int32_t* counts,
                 int64_t E, int64_t N, int64_t K, int64_t max_rows, hipStream_t s) {
   const int64_t g = grid_for(max_rows, E, FM, N, FN);
   hipLaunchKernelGGL((gmm_f32_kernel<FC1>), dim3(static_cast<unsigned>(g)), dim3(kThreads), 0, s,
-                     static_cast<const float*>(A), static_cast<const float*>(B0),
-                     static_cast<const float*>(B1), static_cast<float*>(C), counts,
-                     static_cast<int>(E), static_cast<int>(N), static_cast<int>(K), max_rows);
+                     static_cast<const float*>(a.base), a.gather, a.rows,
+                     static_cast<const float*>(B0), static_cast<const float*>(B1),
+                     static_cast<float*>(C), counts, static_cast<int>(E), static_cast<int>(N),
+                     static_cast<int>(K), max_rows);
 }
 
 // Tile shape from the average rows per expert (known on the host without
@@ -727,7 +747,7 @@ using Fc2B64 = Body<64, 256, 2, 4, false, 4, 64>;
 using Fc2Stream128 = Body<128, 128, 2, 4, false, 4, 64>;
 
 template <bool FC1>
-void launch_gemm(int32_t dtype, const void* A, const void* B0, const void* B1, void* C,
+void launch_gemm(int32_t dtype, const AOperand& A, const void* B0, const void* B1, void* C,
                  const int32_t* counts, int64_t E, int64_t N, int64_t K, int64_t max_rows,
                  hipStream_t s) {
   if (dtype == MOE_F32) {
@@ -784,9 +804,27 @@ extern "C" moe_status moe_grouped_fc1_swiglu(int64_t E, int64_t h, int64_t f, in
   if (max_rows == 0) return MOE_OK;
   MOE_REQUIRE(permuted_x && tokens_per_expert && w_gate && w_up && act, MOE_ERR_ARG,
               "moe_grouped_fc1_swiglu: NULL tensor argument");
-  launch_gemm<true>(dtype, permuted_x, w_gate, w_up, act, tokens_per_expert, E, f, h, max_rows,
-                    as_stream(stream));
+  launch_gemm<true>(dtype, AOperand{permuted_x, nullptr, max_rows}, w_gate, w_up, act,
+                    tokens_per_expert, E, f, h, max_rows, as_stream(stream));
   return check_launch("moe_grouped_fc1_swiglu");
+}
+
+extern "C" moe_status moe_grouped_fc1_swiglu_gather(int64_t E, int64_t h, int64_t f,
+                                                    int64_t max_rows, int32_t dtype, int64_t T,
+                                                    const void* x, const int32_t* sorted_token,
+                                                    const int32_t* tokens_per_expert,
+                                                    const void* w_gate, const void* w_up, void* act,
+                                                    void* stream) {
+  moe_status st = validate("moe_grouped_fc1_swiglu_gather", E, h, f, max_rows, dtype);
+  if (st != MOE_OK) return st;
+  MOE_REQUIRE(T >= 0 && T < (int64_t(1) << 31), MOE_ERR_ARG,
+              "moe_grouped_fc1_swiglu_gather: T out of range");
+  if (max_rows == 0 || T == 0) return MOE_OK;
+  MOE_REQUIRE(x && sorted_token && tokens_per_expert && w_gate && w_up && act, MOE_ERR_ARG,
+              "moe_grouped_fc1_swiglu_gather: NULL tensor argument");
+  launch_gemm<true>(dtype, AOperand{x, sorted_token, T}, w_gate, w_up, act, tokens_per_expert, E,
+                    f, h, max_rows, as_stream(stream));
+  return check_launch("moe_grouped_fc1_swiglu_gather");
 }
 
 extern "C" moe_status moe_grouped_fc2(int64_t E, int64_t h, int64_t f, int64_t max_rows,
@@ -798,8 +836,8 @@ extern "C" moe_status moe_grouped_fc2(int64_t E, int64_t h, int64_t f, int64_t m
   if (max_rows == 0) return MOE_OK;
   MOE_REQUIRE(act && tokens_per_expert && w_down && expert_out, MOE_ERR_ARG,
               "moe_grouped_fc2: NULL tensor argument");
-  launch_gemm<false>(dtype, act, w_down, nullptr, expert_out, tokens_per_expert, E, h, f, max_rows,
-                     as_stream(stream));
+  launch_gemm<false>(dtype, AOperand{act, nullptr, max_rows}, w_down, nullptr, expert_out,
+                     tokens_per_expert, E, h, f, max_rows, as_stream(stream));
   return check_launch("moe_grouped_fc2");
 }
 

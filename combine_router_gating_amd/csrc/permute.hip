@@ -125,11 +125,13 @@ __global__ void __launch_bounds__(256) permute_scatter_kernel(
       }
     }
     const uint4* src = x + t * chunks;
-    for (int i = lane; i < chunks; i += 64) {
-      const uint4 v = src[i];
-      for (int k = 0; k < n; ++k) {
-        const int r = rows[tl][k];
-        if (r < max_rows) px[static_cast<int64_t>(r) * chunks + i] = v;
+    if (px) {
+      for (int i = lane; i < chunks; i += 64) {
+        const uint4 v = src[i];
+        for (int k = 0; k < n; ++k) {
+          const int r = rows[tl][k];
+          if (r < max_rows) px[static_cast<int64_t>(r) * chunks + i] = v;
+        }
       }
     }
     if (n_all > kMaxTopK) {  // padding entries past the first kMaxTopK
@@ -149,7 +151,8 @@ __global__ void __launch_bounds__(256) permute_scatter_kernel(
           const int src_lane = __builtin_ctzll(todo);
           todo &= todo - 1;
           const int rr = __shfl(r, src_lane, 64);
-          for (int i = lane; i < chunks; i += 64) px[static_cast<int64_t>(rr) * chunks + i] = src[i];
+          if (px)
+            for (int i = lane; i < chunks; i += 64) px[static_cast<int64_t>(rr) * chunks + i] = src[i];
         }
         base += __popcll(mask);
       }
@@ -190,9 +193,10 @@ extern "C" moe_status moe_permute(int64_t T, int64_t h, int64_t E, int64_t K, in
     launch_fill_i32(expert_offsets, E + 1, 0, s);
     return check_launch("moe_permute(T=0)");
   }
-  MOE_REQUIRE(x && routing_map && probs && row_id_map, MOE_ERR_ARG,
+  MOE_REQUIRE(routing_map && probs && row_id_map, MOE_ERR_ARG,
               "moe_permute: NULL tensor argument");
-  MOE_REQUIRE(max_rows == 0 || (permuted_x && permuted_probs && sorted_token), MOE_ERR_ARG,
+  MOE_REQUIRE(x || !permuted_x, MOE_ERR_ARG, "moe_permute: x is NULL but permuted_x is not");
+  MOE_REQUIRE(max_rows == 0 || (permuted_probs && sorted_token), MOE_ERR_ARG,
               "moe_permute: NULL output with max_rows > 0");
   const size_t need = moe_permute_workspace_size(T, E);
   MOE_REQUIRE(workspace && workspace_bytes >= need, MOE_ERR_WORKSPACE,

@@ -1,7 +1,12 @@
 """A preallocated MoE layer forward: buffers are allocated once (torch), the
 C arguments are built once, and each forward is a fixed sequence of libmoe
 calls on the current stream — no allocation and no host sync per call, so
-it can also be captured into a graph."""
+it can also be captured into a graph.
+
+Options: `gather` skips the permuted copy of x (the permute writes indices
+and probs only, and FC1 reads token rows through sorted_token);
+`overlap_shared` runs the shared expert on a second stream (default
+priority) from the start of the forward, joined before the combine."""
 from __future__ import annotations
 
 import ctypes
@@ -25,7 +30,8 @@ class MoELayerForward:
 
     def __init__(self, inp: Dict[str, torch.Tensor], *, K: int, score: str = "softmax",
                  pre_softmax: bool = True, capacity_factor: float = 0.0, min_capacity: int = 0,
-                 drop_policy: str = "position", pad_to_capacity: bool = False):
+                 drop_policy: str = "position", pad_to_capacity: bool = False,
+                 gather: bool = False, overlap_shared: bool = False):
         self.lib = _lib.load()
         self.inp = inp
         x = _need(inp["x"], "x")
@@ -46,7 +52,8 @@ class MoELayerForward:
         self.logits = e((T, E), dtype=torch.float32, device=dev)
         self.route_ws_bytes = int(self.lib.moe_route_workspace_size(ctypes.byref(self.desc)))
         self.route_ws = e((max(self.route_ws_bytes, 1),), dtype=torch.uint8, device=dev)
-        self.permuted_x = e((R, h), dtype=x.dtype, device=dev)
+        self.gather = gather
+        self.permuted_x = None if gather else e((R, h), dtype=x.dtype, device=dev)
         self.permuted_probs = e((R,), dtype=torch.float32, device=dev)
         self.sorted_token = e((R,), dtype=torch.int32, device=dev)
         self.row_id_map = e((T, K), dtype=torch.int32, device=dev)
@@ -64,6 +71,11 @@ class MoELayerForward:
             self.shared_out = e((T, h), dtype=x.dtype, device=dev)
         else:
             self.shared_out = None
+        self.overlap_shared = bool(overlap_shared and self.shared)
+        if self.overlap_shared:
+            self.side = torch.cuda.Stream(device=dev)  # default priority
+            self.ev_fork = torch.cuda.Event()
+            self.ev_join = torch.cuda.Event()
 
     def _stream(self):
         return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
@@ -78,13 +90,20 @@ class MoELayerForward:
 
     def permute(self):
         check("moe_permute", self.lib.moe_permute(
-            self.T, self.h, self.E, self.K, self.dt, _p(self.inp["x"]), _p(self.routing_map),
+            self.T, self.h, self.E, self.K, self.dt, None if self.gather else _p(self.inp["x"]),
+            _p(self.routing_map),
             _p(self.probs), self.max_rows, _p(self.permuted_x), _p(self.permuted_probs),
             _p(self.sorted_token), _p(self.row_id_map), _p(self.expert_offsets), _p(self.perm_ws),
             self.perm_ws_bytes, self._stream()))
 
     def fc1(self):
         i = self.inp
+        if self.gather:
+            check("moe_grouped_fc1_swiglu_gather", self.lib.moe_grouped_fc1_swiglu_gather(
+                self.E, self.h, self.f, self.max_rows, self.dt, self.T, _p(i["x"]),
+                _p(self.sorted_token), _p(self.tokens_per_expert), _p(i["w_gate"]), _p(i["w_up"]),
+                _p(self.act), self._stream()))
+            return
         check("moe_grouped_fc1_swiglu", self.lib.moe_grouped_fc1_swiglu(
             self.E, self.h, self.f, self.max_rows, self.dt, _p(self.permuted_x),
             _p(self.tokens_per_expert), _p(i["w_gate"]), _p(i["w_up"]), _p(self.act),
@@ -113,12 +132,23 @@ class MoELayerForward:
             _p(self.row_id_map), self.max_rows, _p(self.shared_out), _p(self.out),
             self._stream()))
 
+    def stages(self):
+        """Stage names in launch order on the main stream."""
+        return [n for n in self.STAGES if n != "shared" or (self.shared and not self.overlap_shared)]
+
     def forward(self, mark: Optional[Callable[[str], None]] = None) -> torch.Tensor:
-        """One layer forward.  `mark(name)` is called before each stage and
-        once more with "end" (used to record timing events)."""
-        for name in self.STAGES:
-            if name == "shared" and not self.shared:
-                continue
+        """One layer forward.  `mark(name)` is called before each main-stream
+        stage and once more with "end" (used to record timing events)."""
+        if self.overlap_shared:
+            main = torch.cuda.current_stream()
+            self.ev_fork.record(main)
+            self.side.wait_event(self.ev_fork)
+            with torch.cuda.stream(self.side):
+                self.shared_expert()
+                self.ev_join.record(self.side)
+        for name in self.stages():
+            if name == "combine" and self.overlap_shared:
+                torch.cuda.current_stream().wait_event(self.ev_join)
             if mark:
                 mark(name)
             getattr(self, "shared_expert" if name == "shared" else name)()

@@ -163,8 +163,9 @@ def moe_update_expert_bias(local_tokens_per_expert: torch.Tensor, expert_bias: t
 
 
 def moe_permute(x: torch.Tensor, routing_map: torch.Tensor, probs: torch.Tensor, K: int,
-                max_rows: int) -> Dict[str, torch.Tensor]:
-    """Expert-major permute of token rows."""
+                max_rows: int, copy_rows: bool = True) -> Dict[str, torch.Tensor]:
+    """Expert-major permute of token rows (copy_rows=False: indices and probs
+    only, for the gathering FC1)."""
     lib = _lib.load()
     _need(x, "x")
     T, h = x.shape
@@ -173,14 +174,15 @@ def moe_permute(x: torch.Tensor, routing_map: torch.Tensor, probs: torch.Tensor,
     _need(probs, "probs", torch.float32, (T, E))
     dev = x.device
     rows = max(int(max_rows), 0)
-    px = torch.empty((rows, h), dtype=x.dtype, device=dev)
+    px = torch.empty((rows, h), dtype=x.dtype, device=dev) if copy_rows else None
     pp = torch.empty((rows,), dtype=torch.float32, device=dev)
     st_tok = torch.empty((rows,), dtype=torch.int32, device=dev)
     rid = torch.empty((T, K), dtype=torch.int32, device=dev)
     offs = torch.empty((E + 1,), dtype=torch.int32, device=dev)
     ws_bytes = int(lib.moe_permute_workspace_size(T, E))
     ws = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=dev)
-    st = lib.moe_permute(T, h, E, K, _dtype_code(x, "x"), _ptr(x), _ptr(routing_map), _ptr(probs),
+    st = lib.moe_permute(T, h, E, K, _dtype_code(x, "x"), _ptr(x) if copy_rows else None,
+                         _ptr(routing_map), _ptr(probs),
                          rows, _ptr(px), _ptr(pp), _ptr(st_tok), _ptr(rid), _ptr(offs), _ptr(ws),
                          ws_bytes, _stream())
     check("moe_permute", st)
@@ -215,6 +217,26 @@ def moe_grouped_fc1_swiglu(permuted_x: torch.Tensor, tokens_per_expert: torch.Te
                                             _ptr(permuted_x), _ptr(tokens_per_expert),
                                             _ptr(w_gate), _ptr(w_up), _ptr(act), _stream())
     check("moe_grouped_fc1_swiglu", st)
+    return act
+
+
+def moe_grouped_fc1_swiglu_gather(x: torch.Tensor, sorted_token: torch.Tensor,
+                                  tokens_per_expert: torch.Tensor, w_gate: torch.Tensor,
+                                  w_up: torch.Tensor, act: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """act = silu(x[sorted_token] W_gate^T) * (x[sorted_token] W_up^T), per expert row range."""
+    E = _mlp_args(x, tokens_per_expert, w_gate, w_up)
+    T, h = x.shape
+    rows = sorted_token.shape[0]
+    _need(sorted_token, "sorted_token", torch.int32, (rows,))
+    f = w_gate.shape[1]
+    _need(w_gate, "w_gate", x.dtype, (E, f, h))
+    if act is None:
+        act = torch.empty((rows, f), dtype=x.dtype, device=x.device)
+    _need(act, "act", x.dtype, (rows, f))
+    st = _lib.load().moe_grouped_fc1_swiglu_gather(E, h, f, rows, _dtype_code(x, "x"), T, _ptr(x),
+                                                   _ptr(sorted_token), _ptr(tokens_per_expert),
+                                                   _ptr(w_gate), _ptr(w_up), _ptr(act), _stream())
+    check("moe_grouped_fc1_swiglu_gather", st)
     return act
 
 
@@ -276,8 +298,10 @@ def moe_combine(expert_out: torch.Tensor, permuted_probs: torch.Tensor, row_id_m
 def moe_forward(inp: Dict[str, torch.Tensor], *, K: int, score: str = "softmax",
                 pre_softmax: bool = True, capacity_factor: float = 0.0, min_capacity: int = 0,
                 drop_policy: str = "position", pad_to_capacity: bool = False,
-                want_logits: bool = False) -> Dict[str, torch.Tensor]:
+                gather: bool = False, want_logits: bool = False) -> Dict[str, torch.Tensor]:
     """route -> permute -> grouped SwiGLU experts -> combine (+ shared expert).
+    With gather=True the permute writes no row copies and FC1 reads the
+    token rows through sorted_token.
 
     `inp` holds the tensors datagen.make_inputs returns (x, w_router,
     optional b_router / expert_bias, w_gate, w_up, w_down, optional
@@ -289,9 +313,13 @@ def moe_forward(inp: Dict[str, torch.Tensor], *, K: int, score: str = "softmax",
                   capacity_factor=capacity_factor, min_capacity=min_capacity,
                   drop_policy=drop_policy, pad_to_capacity=pad_to_capacity,
                   want_logits=want_logits)
-    pm = moe_permute(x, r["routing_map"], r["probs"], K, r["max_rows"])
-    act = moe_grouped_fc1_swiglu(pm["permuted_x"], r["tokens_per_expert"], inp["w_gate"],
-                                 inp["w_up"])
+    pm = moe_permute(x, r["routing_map"], r["probs"], K, r["max_rows"], copy_rows=not gather)
+    if gather:
+        act = moe_grouped_fc1_swiglu_gather(x, pm["sorted_token"], r["tokens_per_expert"],
+                                            inp["w_gate"], inp["w_up"])
+    else:
+        act = moe_grouped_fc1_swiglu(pm["permuted_x"], r["tokens_per_expert"], inp["w_gate"],
+                                     inp["w_up"])
     y = moe_grouped_fc2(act, r["tokens_per_expert"], inp["w_down"])
     shared_out = None
     if "shared_gate" in inp:

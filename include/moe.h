@@ -198,7 +198,9 @@ size_t moe_permute_workspace_size(int64_t T, int64_t E);
  *   routing_map    [T,E]        uint8   nonzero = routed (any number per row:
  *                                       padding to capacity adds entries)
  *   probs          [T,E]        fp32    at most K nonzero per row
- *   permuted_x     [max_rows,h] dtype   out: permuted_x[i] = x[sorted_token[i]]
+ *   permuted_x     [max_rows,h] dtype   out: permuted_x[i] = x[sorted_token[i]];
+ *                                       may be NULL (then x may be NULL too): no
+ *                                       rows are copied, for the gathering FC1
  *   permuted_probs [max_rows]   fp32    out: probs[sorted_token[i], expert of row i]
  *   sorted_token   [max_rows]   int32   out: source token of row i
  *   row_id_map     [T,K]        int32   out: row of token t's k-th map entry with
@@ -248,6 +250,23 @@ moe_status moe_grouped_fc1_swiglu(int64_t E, int64_t h, int64_t f, int64_t max_r
                                   int32_t dtype, const void* permuted_x,
                                   const int32_t* tokens_per_expert, const void* w_gate,
                                   const void* w_up, void* act, void* stream);
+
+/*
+ * moe_grouped_fc1_swiglu_gather — the first half of moe_grouped_mlp reading
+ * its rows straight from the token-major input: row i of the grouped GEMM is
+ * x[sorted_token[i]] (moe_permute's sorted_token; values are clamped to
+ * [0, T)), so permuted_x need not be materialised.  [MG] 计算效率优化 lists
+ * memory-efficient permutation among the MoE optimisations; the result is
+ * identical to moe_grouped_fc1_swiglu on moe_permute's permuted_x.
+ *   x            [T,h]         dtype
+ *   sorted_token [max_rows]    int32
+ *   (other arguments as moe_grouped_fc1_swiglu)
+ */
+moe_status moe_grouped_fc1_swiglu_gather(int64_t E, int64_t h, int64_t f, int64_t max_rows,
+                                         int32_t dtype, int64_t T, const void* x,
+                                         const int32_t* sorted_token,
+                                         const int32_t* tokens_per_expert, const void* w_gate,
+                                         const void* w_up, void* act, void* stream);
 
 /* The second half of moe_grouped_mlp: expert_out = act W_down^T. */
 moe_status moe_grouped_fc2(int64_t E, int64_t h, int64_t f, int64_t max_rows, int32_t dtype,

@@ -1,0 +1,125 @@
+"""GPU checks of the fused/overlapped layer variants.
+
+The gathering FC1 (rows read through sorted_token instead of a permuted
+copy) and the shared expert on a second stream change where data is read
+and when kernels run, not the arithmetic: outputs must equal the plain
+path bit for bit, and the plain path is itself checked against the oracle
+elsewhere.  A small layer is also compared with the oracle directly.
+"""
+import numpy as np
+import pytest
+import torch
+
+import combine_router_gating_amd as moe
+import datagen
+import oracle
+from combine_router_gating_amd.layer import MoELayerForward
+from gpu_helpers import assert_close, f64, log, shared_weights_from
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+CFGS = [
+    datagen.MoEConfig("g-bf16", T=300, h=256, E=8, K=2, f=512, dtype="bf16"),
+    datagen.MoEConfig("g-cap", T=515, h=128, E=16, K=1, f=256, dtype="bf16", capacity_factor=1.25,
+                      gate_bias="zipf"),
+    datagen.MoEConfig("g-sig", T=257, h=256, E=64, K=8, f=128, dtype="bf16", score="sigmoid",
+                      expert_bias=True, shared_f=192),
+    datagen.MoEConfig("g-f32", T=99, h=64, E=4, K=4, f=96, dtype="f32", shared_f=64,
+                      capacity_factor=0.5),
+]
+
+
+@pytest.mark.parametrize("cfg", CFGS, ids=lambda c: c.name)
+def test_gather_fc1_equals_permuted_fc1(cfg):
+    log(f"gather fc1: {cfg}")
+    inp = datagen.make_inputs(cfg, seed=3, device=DEV)
+    kw = dict(K=cfg.K, score=cfg.score, pre_softmax=cfg.pre_softmax,
+              capacity_factor=cfg.capacity_factor)
+    a = moe.moe_forward(inp, gather=False, **kw)
+    b = moe.moe_forward(inp, gather=True, **kw)
+    torch.cuda.synchronize()
+    N = int(a["expert_offsets"][-1].item())
+    assert b["permuted_x"] is None
+    assert torch.equal(a["act"][:N], b["act"][:N])
+    assert torch.equal(a["out"], b["out"])
+    # and the gathered activation against the oracle
+    st = a["sorted_token"][:N].cpu().numpy()
+    w = (f64(inp["w_gate"]), f64(inp["w_up"]), f64(inp["w_down"]))
+    act, _ = oracle.grouped_experts(f64(inp["x"])[st], a["tokens_per_expert"].cpu().numpy(), w,
+                                    cfg.dtype)
+    assert_close(f64(b["act"][:N]), act, cfg.dtype, "act")
+
+
+def test_gather_clamps_out_of_range_indices():
+    """sorted_token entries outside [0, T) are clamped, never dereferenced."""
+    T, h, f, E = 64, 128, 128, 2
+    x = torch.randn(T, h, device=DEV).to(torch.bfloat16)
+    wg = (torch.randn(E, f, h, device=DEV) * 0.05).to(torch.bfloat16)
+    wu = (torch.randn(E, f, h, device=DEV) * 0.05).to(torch.bfloat16)
+    counts = torch.tensor([40, 24], dtype=torch.int32, device=DEV)
+    st = torch.arange(64, dtype=torch.int32, device=DEV)
+    st[5] = -7
+    st[9] = 10 ** 6
+    got = moe.moe_grouped_fc1_swiglu_gather(x, st, counts, wg, wu)
+    idx = st.clamp(0, T - 1).long()
+    ref = moe.moe_grouped_fc1_swiglu(x[idx].contiguous(), counts, wg, wu)
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref)
+
+
+@pytest.mark.parametrize("name", ["tiny", "switch", "dsv3"])
+def test_layer_options_give_identical_outputs(name):
+    cfg = datagen.CONFIGS[name]
+    if name == "dsv3":
+        cfg = cfg.replace(T=1024)
+    log(f"layer options: {cfg}")
+    inp = datagen.make_inputs(cfg, seed=0, device=DEV)
+    kw = dict(K=cfg.K, score=cfg.score, pre_softmax=cfg.pre_softmax,
+              capacity_factor=cfg.capacity_factor, min_capacity=cfg.min_capacity)
+    outs = []
+    for gather, overlap in ((False, False), (True, False), (True, True), (False, True)):
+        layer = MoELayerForward(inp, gather=gather, overlap_shared=overlap, **kw)
+        for _ in range(2):
+            out = layer.forward()
+        torch.cuda.synchronize()
+        outs.append(out.clone())
+    for o in outs[1:]:
+        assert torch.equal(outs[0], o)
+
+
+def test_layer_overlap_graph_capture_replays():
+    cfg = datagen.MoEConfig("g-graph", T=512, h=256, E=16, K=2, f=256, dtype="bf16", shared_f=128)
+    inp = datagen.make_inputs(cfg, seed=5, device=DEV)
+    layer = MoELayerForward(inp, K=cfg.K, gather=True, overlap_shared=True)
+    layer.forward()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        out = layer.forward()
+    plain = MoELayerForward(inp, K=cfg.K)
+    for seed in (6, 7, 8):
+        new = datagen.make_inputs(cfg, seed=seed, device=DEV, with_experts=False)
+        inp["x"].copy_(new["x"])
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ref = plain.forward()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), f"replay with seed {seed}"
+
+
+def test_small_layer_with_options_against_the_oracle():
+    cfg = CFGS[2]
+    inp = datagen.make_inputs(cfg, seed=9, device=DEV)
+    layer = MoELayerForward(inp, K=cfg.K, score=cfg.score, gather=True, overlap_shared=True)
+    out = layer.forward()
+    torch.cuda.synchronize()
+    logits = layer.logits.cpu().numpy()
+    ref = oracle.moe_forward(f64(inp["x"]), None, None,
+                             (f64(inp["w_gate"]), f64(inp["w_up"]), f64(inp["w_down"])),
+                             K=cfg.K, dtype=cfg.dtype, score=cfg.score,
+                             expert_bias=inp["expert_bias"].cpu().numpy(),
+                             shared=shared_weights_from(inp), logits=logits)
+    np.testing.assert_array_equal(layer.routing_map.cpu().numpy(), ref["routing_map"])
+    assert_close(f64(out), ref["out"], cfg.dtype, "out")
