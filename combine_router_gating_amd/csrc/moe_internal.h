@@ -82,15 +82,91 @@ __device__ __forceinline__ int64_t block_exclusive_scan256(int64_t v, int64_t* s
   return block_exclusive_scan<4>(v, scratch, total);
 }
 
-// LDS layout for tiles of 64-byte rows (32 bf16 of k) read as 16-byte MFMA
-// fragments: rows 2L and 2L+1 share 128-byte line L, and logical chunk
-// lc = (row & 1) * 4 + c (c = 0..3) sits at physical chunk lc ^ ((L >> 1) & 3),
-// so 16 lanes reading one chunk of 16 consecutive rows hit 16 different
-// 16-byte bank groups (gfx950: 64 banks of 4 bytes, 16 lanes per cycle).
-__device__ __forceinline__ uint32_t lds_swz64b(int row, int c) {
-  const int line = row >> 1;
-  const int lc = ((row & 1) << 2) | c;
-  return static_cast<uint32_t>(line * 128 + ((lc ^ ((line >> 1) & 3)) << 4));
+// ------------------------------------------ LDS staging of MFMA operand tiles
+// A stage holds rows of one SBK-wide k slab of bf16 values (SBK*2 bytes per
+// row) in 16-byte chunks.  gfx950's LDS serves a 16-byte-per-lane read 16 lanes
+// at a time across 64 four-byte banks (256 bytes), so chunks are
+// XOR-swizzled such that sixteen lanes reading the same logical chunk of
+// sixteen consecutive rows touch sixteen different 16-byte bank groups,
+// while a direct-to-LDS load still fills a contiguous 1 KB piece (lane i ->
+// bytes 16i):
+//   SBK = 32 (64-byte rows): rows 2L and 2L+1 share 128-byte line L;
+//     logical chunk lc = (row & 1) * 4 + c sits at lc ^ ((L >> 1) & 3);
+//   SBK = 64 (128-byte rows): chunk c of row r sits at c ^ ((r >> 1) & 7);
+//   SBK >= 128: chunk c of row r sits at (c & ~15) | ((c & 15) ^ (r & 15)).
+template <int SBK>
+__device__ __forceinline__ uint32_t lds_chunk_byte(int row, int c) {
+  if constexpr (SBK == 32) {
+    const int line = row >> 1;
+    const int lc = ((row & 1) << 2) | c;
+    return static_cast<uint32_t>(line * 128 + ((lc ^ ((line >> 1) & 3)) << 4));
+  } else if constexpr (SBK == 64) {
+    return static_cast<uint32_t>(row * 128 + ((c ^ ((row >> 1) & 7)) << 4));
+  } else {
+    const int pc = (c & ~15) | ((c & 15) ^ (row & 15));
+    return static_cast<uint32_t>(row * (SBK * 2) + (pc << 4));
+  }
+}
+
+// Inverse of lds_chunk_byte for a 16-byte piece at stage byte offset o.
+template <int SBK>
+__device__ __forceinline__ void lds_piece(int o, int& row, int& c) {
+  if constexpr (SBK == 32) {
+    const int line = o >> 7;
+    const int lc = ((o >> 4) & 7) ^ ((line >> 1) & 3);
+    row = 2 * line + (lc >> 2);
+    c = lc & 3;
+  } else if constexpr (SBK == 64) {
+    row = o >> 7;
+    c = ((o >> 4) & 7) ^ ((row >> 1) & 7);
+  } else {
+    row = o / (SBK * 2);
+    const int pc = (o % (SBK * 2)) >> 4;
+    c = (pc & ~15) | ((pc & 15) ^ (row & 15));
+  }
+}
+
+// Direct global -> LDS 16-byte load: lane i writes LDS bytes
+// [lds_base + 16 i, lds_base + 16 i + 16).  Issued as inline assembly so the
+// compiler does not serialise the pipeline with conservative waits; the
+// kernel waits for these loads itself (vmcnt) before a barrier.
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gptr), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "memory");
+}
+
+// Wait until at most n of this wave's vector-memory loads are outstanding.
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  // gfx9 encoding: vmcnt[3:0] bits 3:0, vmcnt[5:4] bits 15:14; expcnt and
+  // lgkmcnt left at their maxima (no wait)
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+__device__ __forceinline__ void wait_lgkm0() {
+  // lgkmcnt(0); vmcnt and expcnt left at their maxima
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
+}
+
+__device__ __forceinline__ void block_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int LPW, int STAGES>
+__device__ __forceinline__ void wait_stage(int n_after) {
+  // wait until at most n_after later stages (of this wave's loads) are in
+  // flight; n_after <= STAGES - 1
+  if constexpr (STAGES >= 6) { if (n_after >= 5) { wait_vmcnt<LPW * 5>(); return; } }
+  if constexpr (STAGES >= 5) { if (n_after >= 4) { wait_vmcnt<LPW * 4>(); return; } }
+  if constexpr (STAGES >= 4) { if (n_after >= 3) { wait_vmcnt<LPW * 3>(); return; } }
+  if constexpr (STAGES >= 3) { if (n_after >= 2) { wait_vmcnt<LPW * 2>(); return; } }
+  if (n_after >= 1) { wait_vmcnt<LPW * 1>(); return; }
+  wait_vmcnt<0>();
 }
 
 __device__ __forceinline__ float wave_sum(float v) {

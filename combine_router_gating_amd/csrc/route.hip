@@ -9,10 +9,10 @@
 // leave both the map and the probs.
 //
 // Kernels, in launch order:
-//   router_logits_lds      bf16 x: x w^T on bf16 MFMA with the fp32 weight split
+//   router_logits_ring     bf16 x: x w^T on bf16 MFMA with the fp32 weight split
 //                          exactly into three bf16 parts (fp32-accurate), both
-//                          operands staged through LDS, split over h into
-//                          partial sums (more workgroups)
+//                          operands streamed through a ring of LDS stages,
+//                          split over h into partial sums (more workgroups)
 //   router_logits_simt     fp32 x (or h not a multiple of 16): fp32 FMA, LDS-tiled
 //   router_topk_kernel     one wave per token: logits = partials summed in a
 //                          fixed order (+ b), scores, K rounds of a wave-wide
@@ -106,87 +106,86 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-// Split four fp32 weights into their hi/mid/lo bf16 parts, packed as 4 bf16
-// (8 bytes) per part.
-__device__ __forceinline__ void split4(const f32x4_t v, uint2& hi, uint2& mi, uint2& lo) {
-  uint32_t h16[4], m16[4], l16[4];
+// Split eight fp32 weights into their hi/mid/lo bf16 parts (see above),
+// each part as one 8-wide bf16 MFMA operand.
+__device__ __forceinline__ void split8(const f32x4_t a, const f32x4_t b, bf16x8_t& hi,
+                                       bf16x8_t& mi, bf16x8_t& lo) {
+  u32x4_t h, m, l;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const uint32_t u = __float_as_uint(v[q]);
-    const uint32_t hb = u & 0xffff0000u;
-    const float r1 = v[q] - __uint_as_float(hb);
-    const uint32_t mb = __float_as_uint(r1) & 0xffff0000u;
-    const float r2 = r1 - __uint_as_float(mb);
-    h16[q] = hb >> 16;
-    m16[q] = mb >> 16;
-    l16[q] = __float_as_uint(r2) >> 16;
+    uint32_t hs[2], ms[2], ls[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const float v = (q < 2) ? a[2 * q + r] : b[2 * (q - 2) + r];
+      const uint32_t hb = __float_as_uint(v) & 0xffff0000u;
+      const float r1 = v - __uint_as_float(hb);
+      const uint32_t mb = __float_as_uint(r1) & 0xffff0000u;
+      const float r2 = r1 - __uint_as_float(mb);
+      hs[r] = hb >> 16;
+      ms[r] = mb >> 16;
+      ls[r] = __float_as_uint(r2) >> 16;
+    }
+    h[q] = hs[0] | (hs[1] << 16);
+    m[q] = ms[0] | (ms[1] << 16);
+    l[q] = ls[0] | (ls[1] << 16);
   }
-  hi = make_uint2(h16[0] | (h16[1] << 16), h16[2] | (h16[3] << 16));
-  mi = make_uint2(m16[0] | (m16[1] << 16), m16[2] | (m16[3] << 16));
-  lo = make_uint2(l16[0] | (l16[1] << 16), l16[2] | (l16[3] << 16));
+  hi = __builtin_bit_cast(bf16x8_t, h);
+  mi = __builtin_bit_cast(bf16x8_t, m);
+  lo = __builtin_bit_cast(bf16x8_t, l);
 }
 
-// Gating linear on MFMA with LDS staging.  A workgroup owns BT = 64*WT
-// tokens x BE = 64*WE experts over one slice of h; each 32-wide k slab of x
-// (BT rows) and of the weight (BE rows, split into three bf16 planes while
-// it is staged) is loaded once with coalesced row loads into LDS (two
-// slots: slab s+1 waits in registers while slab s is multiplied), and each
-// wave reads its 64x64 fragments from LDS.
-template <int WT, int WE>
-__global__ void __launch_bounds__(256) router_logits_lds(const uint16_t* __restrict__ x,
-                                                         const float* __restrict__ w,
-                                                         float* __restrict__ part, int64_t T,
-                                                         int h, int E, int kchunk) {
+// Gating linear on MFMA through a ring of LDS stages.  A workgroup owns
+// BT = 64*WT tokens x BE = 64*WE experts over one slice of h, in SK-wide k
+// slabs; a stage holds one slab's x rows (BT x 2*SK bytes of bf16) and
+// weight rows (BE x 4*SK bytes of fp32), filled by direct global->LDS loads, and
+// STAGES-1 slabs stay in flight while one is multiplied.  Each wave reads
+// its 64x64 fragments from LDS and splits the fp32 weight fragment into its
+// three bf16 parts in registers (three MFMAs per block and k step).
+template <int WT, int WE, int STAGES, int SK>
+__global__ void __launch_bounds__(256) router_logits_ring(const uint16_t* __restrict__ x,
+                                                          const float* __restrict__ w,
+                                                          float* __restrict__ part, int64_t T,
+                                                          int h, int E, int kchunk) {
   static_assert(WT * WE == 4, "4 waves");
   constexpr int BT = 64 * WT, BE = 64 * WE;
-  constexpr int ROWS = BT + 3 * BE;          // x rows, then planes hi, mid, lo
-  constexpr int STAGE = ROWS * 64;           // 32 bf16 (64 bytes) per row
-  constexpr int XP = BT * 4 / 256;           // 16-byte x pieces per thread per slab
-  constexpr int WP = BE * 8 / 256;           // 4-float weight pieces per thread per slab
-  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+  static_assert(SK == 32 || SK == 64, "k per slab");
+  constexpr int XB = BT * SK * 2;  // x bytes per stage
+  constexpr int WB = BE * SK * 4;  // weight bytes per stage
+  constexpr int STAGE = XB + WB;
+  constexpr int LPW = STAGE / 4096;  // 1 KB direct loads per wave per stage
+  static_assert(STAGE % 4096 == 0, "whole loads per wave");
+  __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wt = wave / WE, we = wave % WE;
   const int64_t t0 = static_cast<int64_t>(blockIdx.x) * BT;
   const int e0 = blockIdx.z * BE;
   const int kb = blockIdx.y * kchunk;
-  const int nsl = (min(h, kb + kchunk) - kb) / 32;
-  const uint16_t* xsrc[XP];
-  const float* wsrc[WP];
+  const int nsl = (min(h, kb + kchunk) - kb) / SK;
+  const uint32_t smem_base = static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)smem));
+  // this lane's sources (rows clamped in range; their results are never stored)
+  const char* src[LPW];
+  int step[LPW];
 #pragma unroll
-  for (int i = 0; i < XP; ++i) {
-    const int p = tid + 256 * i, r = p >> 2, c = p & 3;
-    xsrc[i] = x + min(t0 + r, T - 1) * h + kb + c * 8;
-  }
-#pragma unroll
-  for (int i = 0; i < WP; ++i) {
-    const int p = tid + 256 * i, r = p >> 3, c8 = p & 7;
-    wsrc[i] = w + static_cast<int64_t>(min(e0 + r, E - 1)) * h + kb + c8 * 4;
-  }
-  u32x4_t rx[XP];
-  f32x4_t rw[WP];
-  auto gload = [&](int sl) {
-#pragma unroll
-    for (int i = 0; i < XP; ++i) rx[i] = *reinterpret_cast<const u32x4_t*>(xsrc[i] + sl * 32);
-#pragma unroll
-    for (int i = 0; i < WP; ++i) rw[i] = *reinterpret_cast<const f32x4_t*>(wsrc[i] + sl * 32);
-  };
-  auto sstore = [&](int slot) {
-    char* st = smem + slot * STAGE;
-#pragma unroll
-    for (int i = 0; i < XP; ++i) {
-      const int p = tid + 256 * i;
-      *reinterpret_cast<u32x4_t*>(st + lds_swz64b(p >> 2, p & 3)) = rx[i];
+  for (int j = 0; j < LPW; ++j) {
+    const int o = (wave * LPW + j) * 1024 + lane * 16;
+    int row, c;
+    if (o < XB) {
+      lds_piece<SK>(o, row, c);
+      src[j] = reinterpret_cast<const char*>(x + min(t0 + row, T - 1) * h + kb + c * 8);
+      step[j] = SK * 2;
+    } else {
+      lds_piece<2 * SK>(o - XB, row, c);
+      src[j] = reinterpret_cast<const char*>(w + static_cast<int64_t>(min(e0 + row, E - 1)) * h +
+                                             kb + c * 4);
+      step[j] = SK * 4;
     }
+  }
+  auto issue = [&](int sl) {
+    const uint32_t dst = smem_base + static_cast<uint32_t>((sl % STAGES) * STAGE + wave * LPW * 1024);
 #pragma unroll
-    for (int i = 0; i < WP; ++i) {
-      const int p = tid + 256 * i, r = p >> 3, c8 = p & 7;
-      uint2 ph, pm, pl;
-      split4(rw[i], ph, pm, pl);
-      *reinterpret_cast<uint2*>(st + lds_swz64b(BT + r, c8 >> 1) + (c8 & 1) * 8) = ph;
-      *reinterpret_cast<uint2*>(st + lds_swz64b(BT + BE + r, c8 >> 1) + (c8 & 1) * 8) = pm;
-      *reinterpret_cast<uint2*>(st + lds_swz64b(BT + 2 * BE + r, c8 >> 1) + (c8 & 1) * 8) = pl;
-    }
+    for (int j = 0; j < LPW; ++j) dma16(src[j] + static_cast<int64_t>(sl) * step[j], dst + j * 1024);
   };
   f32x16_t acc[2][2];
 #pragma unroll
@@ -196,36 +195,43 @@ __global__ void __launch_bounds__(256) router_logits_lds(const uint16_t* __restr
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
   const int l32 = lane & 31, hi = lane >> 5;
-  gload(0);
-  sstore(0);
-  if (nsl > 1) gload(1);
-  __syncthreads();
-  for (int sl = 0; sl < nsl; ++sl) {
-    const char* st = smem + (sl & 1) * STAGE;
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int c = kk * 2 + hi;
-      bf16x8_t xb[2], wb[3][2];
+  for (int sl = 0; sl < STAGES; ++sl)
+    if (sl < nsl) issue(sl);
+  for (int sl = 0; sl < nsl; ++sl) {
+    wait_stage<LPW, STAGES>(min(sl + STAGES - 1, nsl - 1) - sl);
+    block_barrier();
+    const char* st = smem + (sl % STAGES) * STAGE;
+#pragma unroll
+    for (int kk = 0; kk < SK / 16; ++kk) {
+      bf16x8_t xb[2], wp[3][2];
 #pragma unroll
       for (int j = 0; j < 2; ++j)
-        xb[j] = *reinterpret_cast<const bf16x8_t*>(st + lds_swz64b(wt * 64 + j * 32 + l32, c));
+        xb[j] = *reinterpret_cast<const bf16x8_t*>(
+            st + lds_chunk_byte<SK>(wt * 64 + j * 32 + l32, kk * 2 + hi));
 #pragma unroll
-      for (int pl = 0; pl < 3; ++pl)
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-          wb[pl][i] = *reinterpret_cast<const bf16x8_t*>(
-              st + lds_swz64b(BT + pl * BE + we * 64 + i * 32 + l32, c));
+      for (int i = 0; i < 2; ++i) {
+        const int row = we * 64 + i * 32 + l32;
+        const int cw = kk * 4 + hi * 2;
+        const f32x4_t a =
+            *reinterpret_cast<const f32x4_t*>(st + XB + lds_chunk_byte<2 * SK>(row, cw));
+        const f32x4_t b =
+            *reinterpret_cast<const f32x4_t*>(st + XB + lds_chunk_byte<2 * SK>(row, cw + 1));
+        split8(a, b, wp[0][i], wp[1][i], wp[2][i]);
+      }
 #pragma unroll
       for (int pl = 0; pl < 3; ++pl)
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
           for (int j = 0; j < 2; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wb[pl][i], xb[j], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wp[pl][i], xb[j], acc[i][j], 0, 0, 0);
     }
-    if (sl + 1 < nsl) sstore((sl + 1) & 1);
-    __syncthreads();
-    if (sl + 2 < nsl) gload(sl + 2);
+    if (sl + STAGES < nsl) {
+      wait_lgkm0();
+      block_barrier();  // every wave is done with this slot
+      issue(sl + STAGES);
+    }
   }
   // lane holds [token l32 of block j][experts 8g + 4*(lane/32) + q of block i]
   float* out = part + static_cast<int64_t>(blockIdx.y) * T * E;
@@ -259,7 +265,7 @@ struct MfmaPlan {
 // workgroups (two per CU) with at most 8 partial planes.
 MfmaPlan mfma_plan(int64_t T, int64_t h, int64_t E) {
   MfmaPlan p;
-  p.we = E <= 64 ? 1 : (E <= 128 ? 2 : 4);
+  p.we = E <= 64 ? 1 : 2;  // 4 waves of 64x64: 256 x 64 or 128 x 128 per workgroup
   p.wt = 4 / p.we;
   p.gx = ceil_div(T, 64 * p.wt);
   p.gz = ceil_div(E, 64 * p.we);
@@ -819,13 +825,13 @@ extern "C" moe_status moe_route(const moe_route_desc* d, const void* x, const fl
     const uint16_t* xb = static_cast<const uint16_t*>(x);
     const int hh = static_cast<int>(d->h), Ei = static_cast<int>(E);
     if (p.we == 1)
-      hipLaunchKernelGGL((router_logits_lds<4, 1>), grid, dim3(256), 0, s, xb, w_router, part_ws,
+      hipLaunchKernelGGL((router_logits_ring<4, 1, 4, 32>), grid, dim3(256), 0, s, xb, w_router, part_ws,
                          T, hh, Ei, p.kchunk);
     else if (p.we == 2)
-      hipLaunchKernelGGL((router_logits_lds<2, 2>), grid, dim3(256), 0, s, xb, w_router, part_ws,
+      hipLaunchKernelGGL((router_logits_ring<2, 2, 4, 32>), grid, dim3(256), 0, s, xb, w_router, part_ws,
                          T, hh, Ei, p.kchunk);
     else
-      hipLaunchKernelGGL((router_logits_lds<1, 4>), grid, dim3(256), 0, s, xb, w_router, part_ws,
+      hipLaunchKernelGGL((router_logits_ring<1, 4, 4, 32>), grid, dim3(256), 0, s, xb, w_router, part_ws,
                          T, hh, Ei, p.kchunk);
     ta.part = part_ws;
     ta.nsplit = p.ksplit;
