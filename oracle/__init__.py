@@ -9,6 +9,7 @@ Everything is NumPy: floating point in float64 with one rounding at each
 point where the layer stores a tensor, except where the pages fix fp32 (the
 sigmoid scores used for expert selection, see fp32spec).
 """
+from . import mx
 from .fp32spec import exp_spec, log1p_spec, sigmoid_spec, softplus_spec, sqrtsoftplus_spec
 from .moe import (
     round_bf16,
@@ -33,6 +34,7 @@ from .moe import (
 )
 
 __all__ = [
+    "mx",
     "exp_spec", "log1p_spec", "sigmoid_spec", "softplus_spec", "sqrtsoftplus_spec", "round_bf16", "round_to", "router_logits",
     "topk_indices", "score_and_select", "get_capacity", "capacity_mask",
     "apply_token_dropping", "drop_by_position", "aux_loss", "accumulate_tokens",
