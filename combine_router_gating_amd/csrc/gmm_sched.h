@@ -1,0 +1,99 @@
+// Device-side tile scheduler shared by the grouped GEMM kernels (bf16 and
+// MXFP8): every workgroup scans tokens_per_expert in LDS and decodes its own
+// tile (expert, n-tile, m-tile) from its workgroup id, with no host sync.
+#pragma once
+
+#include "moe_internal.h"
+
+namespace moe {
+
+constexpr int kGemmThreads = 256;
+
+struct Tile {
+  int e;       // expert
+  int64_t row0;  // first global row of this m-tile
+  int nrows;   // valid rows in this m-tile (>= 1)
+  int n0;      // first output column
+};
+
+// Decode this workgroup's tile.  s_toff/s_roff/s_n: LDS arrays of E+1 / E+1 / E.
+template <int BM, int NTHREADS = kGemmThreads>
+__device__ bool decode_tile(const int32_t* __restrict__ counts, int E, int64_t max_rows, int NT,
+                            int* s_toff, int* s_roff, int* s_n, int64_t* scratch, Tile& tile) {
+  constexpr int PER = kMaxExperts / NTHREADS;  // experts per thread
+  const int tid = threadIdx.x;
+  int64_t c[PER];
+  int64_t sum = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int e = tid * PER + j;
+    int64_t v = e < E ? static_cast<int64_t>(counts[e]) : 0;
+    v = v < 0 ? 0 : (v > max_rows ? max_rows : v);
+    c[j] = v;
+    sum += v;
+  }
+  int64_t total_rows;
+  int64_t pre = block_exclusive_scan<NTHREADS / 64>(sum, scratch, &total_rows);
+  int tl[PER];
+  int tsum = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int e = tid * PER + j;
+    const int64_t start = pre < max_rows ? pre : max_rows;
+    const int64_t end = pre + c[j] < max_rows ? pre + c[j] : max_rows;
+    const int n = static_cast<int>(end - start);
+    tl[j] = (n + BM - 1) / BM;
+    tsum += tl[j];
+    if (e < E) {
+      s_roff[e] = static_cast<int>(start);
+      s_n[e] = n;
+    }
+    pre += c[j];
+  }
+  int64_t total_tiles;
+  int tpre = static_cast<int>(block_exclusive_scan<NTHREADS / 64>(tsum, scratch, &total_tiles));
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int e = tid * PER + j;
+    if (e < E) s_toff[e] = tpre;
+    tpre += tl[j];
+  }
+  if (tid == 0) s_toff[E] = static_cast<int>(total_tiles);
+  __syncthreads();
+
+  const int64_t total = total_tiles * NT;
+  const int64_t per = (total + 7) / 8;
+  const int64_t bid = blockIdx.x;
+  const int64_t slot = bid / 8;
+  if (slot >= per) return false;
+  const int64_t L = (bid % 8) * per + slot;
+  if (L >= total) return false;
+  // largest e with s_toff[e] * NT <= L (experts without tiles are skipped)
+  int lo = 0, hi = E;  // invariant: s_toff[lo]*NT <= L < s_toff[hi]*NT
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) / 2;
+    if (static_cast<int64_t>(s_toff[mid]) * NT <= L) lo = mid; else hi = mid;
+  }
+  const int e = lo;
+  const int mt = s_toff[e + 1] - s_toff[e];
+  const int64_t r = L - static_cast<int64_t>(s_toff[e]) * NT;
+  const int nt = static_cast<int>(r / mt);
+  const int mtile = static_cast<int>(r % mt);
+  tile.e = e;
+  tile.row0 = s_roff[e] + static_cast<int64_t>(mtile) * BM;
+  tile.nrows = min(BM, s_n[e] - mtile * BM);
+  tile.n0 = nt;
+  return true;
+}
+
+__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
+
+// Workgroups for the worst case: every expert's row count rounded up to BM
+// (surplus workgroups exit after decoding), a multiple of 8 (one per XCD).
+inline int64_t grid_for(int64_t max_rows, int64_t E, int BM, int64_t N, int BN) {
+  const int64_t mtiles = (max_rows + E * (BM - 1)) / BM;
+  const int64_t total = mtiles * ceil_div(N, BN);
+  return ceil_div(total, 8) * 8;
+}
+
+}  // namespace moe

@@ -60,7 +60,7 @@ typedef enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1, MOE_SCORE_SQRTSOFTP
 typedef enum { MOE_DROP_POSITION = 0, MOE_DROP_PROBS = 1 } moe_drop_policy;
 
 /* Version of this interface (2: drop policy, padding to capacity,
- * sqrtsoftplus scores, router side outputs). */
+ * sqrtsoftplus scores, router side outputs, gathering FC1, MXFP8 GEMMs). */
 int moe_abi_version(void);
 
 /* Message for the last non-OK status returned on the calling thread. */
@@ -272,6 +272,50 @@ moe_status moe_grouped_fc1_swiglu_gather(int64_t E, int64_t h, int64_t f, int64_
 moe_status moe_grouped_fc2(int64_t E, int64_t h, int64_t f, int64_t max_rows, int32_t dtype,
                            const void* act, const int32_t* tokens_per_expert,
                            const void* w_down, void* expert_out, void* stream);
+
+/* ------------------------------------------------------------------------
+ * MXFP8 expert GEMMs.  [MG] FP8/FP4 低精度训练 and 计算效率优化 name FP8 GEMMs for
+ * the MoE experts without a scaling recipe; the format here is the OCP
+ * Microscaling MXFP8-E4M3 block format, which gfx950's scaled MFMA executes:
+ * 32 consecutive values along the reduction dimension share an E8M0 scale
+ * byte X = 2^(floor(log2 amax) - 8) (code = exponent + 127; an all-zero
+ * block has code 0); each value is stored as the E4M3 code of V / X
+ * (nearest, ties to even, saturated to +-448).  Codes are [rows, cols]
+ * uint8, scales [rows, cols/32] uint8, both row-major.
+ * ------------------------------------------------------------------------ */
+
+/* moe_mxfp8_quantize — quantise src [rows, cols] (dtype bf16 or fp32) along
+ * cols (a multiple of 32) into codes [rows, cols] and scales [rows, cols/32].
+ * Use it on x per forward, and once on the weights ([E*f, h] for W_gate and
+ * W_up, [E*h, f] for W_down). */
+moe_status moe_mxfp8_quantize(int64_t rows, int64_t cols, int32_t dtype, const void* src,
+                              uint8_t* codes, uint8_t* scales, void* stream);
+
+/*
+ * moe_grouped_fc1_swiglu_mxfp8 — act = silu(x Wg^T) * (x Wu^T) on MXFP8
+ * operands, fp32 accumulation, act quantised to MXFP8 along f.
+ *   x_codes, x_scales   [T,h], [T,h/32]   token-major MXFP8 x
+ *   sorted_token        [max_rows] int32 or NULL: GEMM row i reads x row
+ *                       sorted_token[i] (clamped to [0, T)); NULL: rows are
+ *                       already expert-major ([max_rows, h])
+ *   wg_*, wu_*          [E,f,h], [E,f,h/32]
+ *   act_codes, act_scales  [max_rows,f], [max_rows,f/32]   out
+ * h and f multiples of 128.  Rows >= sum(tokens_per_expert) untouched.
+ */
+moe_status moe_grouped_fc1_swiglu_mxfp8(int64_t E, int64_t h, int64_t f, int64_t max_rows,
+                                        int64_t T, const uint8_t* x_codes, const uint8_t* x_scales,
+                                        const int32_t* sorted_token,
+                                        const int32_t* tokens_per_expert, const uint8_t* wg_codes,
+                                        const uint8_t* wg_scales, const uint8_t* wu_codes,
+                                        const uint8_t* wu_scales, uint8_t* act_codes,
+                                        uint8_t* act_scales, void* stream);
+
+/* moe_grouped_fc2_mxfp8 — expert_out [max_rows,h] (bf16) = act Wd^T on MXFP8
+ * act ([max_rows,f], [max_rows,f/32]) and Wd ([E,h,f], [E,h,f/32]). */
+moe_status moe_grouped_fc2_mxfp8(int64_t E, int64_t h, int64_t f, int64_t max_rows,
+                                 const uint8_t* act_codes, const uint8_t* act_scales,
+                                 const int32_t* tokens_per_expert, const uint8_t* wd_codes,
+                                 const uint8_t* wd_scales, void* expert_out, void* stream);
 
 /* ------------------------------------------------------------------------
  * Combine: unpermute and weight.  [MC] §2 (combine takes the expert outputs

@@ -1,0 +1,140 @@
+"""GPU parity of the MXFP8 path (quantisation, FC1 + SwiGLU with fused act
+quantisation, FC2) against the oracle's MXFP8 definitions (oracle/mx.py).
+
+Quantisation from bf16/fp32 inputs is bit-exact.  The GEMMs take exact
+inputs (the GPU's own codes, whose values the oracle decodes).  The scaled
+fp8 MFMA does not accumulate exactly in fp32: its result is within a few
+1e-5 of the sum of |products| (measured on the hardware with random
+operands), so the bound used here is EPS = 2^-12 times that sum.  FC2's
+bf16 output is compared within the bf16 tolerance.  FC1's act codes are a
+quantisation of the GPU's act: every dequantised value must be within half
+an E4M3 step of the exact act (or its saturation error), plus EPS times the
+act's sensitivity to the two dot products; and almost all codes agree.
+"""
+import numpy as np
+import pytest
+import torch
+
+import combine_router_gating_amd as moe
+from gpu_helpers import assert_close, log
+from oracle import mx
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _np(t):
+    return t.cpu().numpy()
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_quantize_bit_exact(dtype):
+    rng = np.random.default_rng(0)
+    rows, cols = 300, 256
+    v = rng.standard_normal((rows, cols)) * np.exp(rng.standard_normal((rows, 1)) * 4)
+    v[0] = 0.0                                            # all-zero blocks
+    v[1, :32] = 448.0 * 2.0 ** -20 * np.arange(32) / 31   # saturation / ties region
+    v[2, :32] = 1e-40                                      # subnormal-magnitude block
+    v[3, 5] = 1e30
+    v[4, :32] = (np.arange(32) - 16) * 2.0 ** -12          # exact values
+    # midpoints between E4M3 neighbours at scale 2^-8 (ties to even)
+    v[5, :32] = (np.arange(32) + 0.5) * 2.0 ** -9 * 8 * 2 ** -8
+    v[5, 31] = 1.0
+    t = torch.from_numpy(v).to(dtype).to(DEV)
+    codes, scales = moe.moe_mxfp8_quantize(t)
+    torch.cuda.synchronize()
+    ref_c, ref_s = mx.mx_quantize(t.float().cpu().double().numpy())
+    np.testing.assert_array_equal(_np(scales), ref_s)
+    np.testing.assert_array_equal(_np(codes), ref_c)
+
+
+def _weights(rng, E, n, k, std):
+    w = torch.from_numpy(rng.standard_normal((E, n, k)) * std).to(torch.bfloat16).to(DEV)
+    c, s = moe.moe_mxfp8_quantize(w.reshape(E * n, k))
+    return c.reshape(E, n, k), s.reshape(E, n, k // 32)
+
+
+def _dq(codes, scales):
+    return mx.mx_dequantize(_np(codes), _np(scales))
+
+
+CASES = [  # E, h, f, counts
+    (4, 128, 256, [100, 0, 37, 200]),
+    (8, 256, 384, [64, 65, 1, 128, 129, 0, 255, 300]),
+    (3, 512, 128, [300, 20, 513]),
+    (64, 256, 256, [80 + (i * 7) % 60 for i in range(64)]),
+]
+
+
+@pytest.mark.parametrize("E,h,f,counts", CASES)
+@pytest.mark.parametrize("gather", [False, True])
+def test_fc1_fc2_mxfp8(E, h, f, counts, gather):
+    log(f"mxfp8 E={E} h={h} f={f} rows={sum(counts)} gather={gather}")
+    rng = np.random.default_rng(E * 31 + h)
+    N = sum(counts)
+    T = N + 17 if gather else N
+    x = torch.from_numpy(rng.standard_normal((T, h))).to(torch.bfloat16).to(DEV)
+    xc, xs = moe.moe_mxfp8_quantize(x)
+    if gather:
+        st = torch.from_numpy(rng.permutation(T)[:N].astype(np.int32)).to(DEV)
+    else:
+        st = None
+    wg = _weights(rng, E, f, h, 0.05)
+    wu = _weights(rng, E, f, h, 0.05)
+    wd = _weights(rng, E, h, f, 0.05)
+    cnt = torch.tensor(counts, dtype=torch.int32, device=DEV)
+    ac, asc = moe.moe_grouped_fc1_swiglu_mxfp8(xc, xs, st, cnt, wg, wu, N)
+    y = moe.moe_grouped_fc2_mxfp8(ac, asc, cnt, wd)
+    torch.cuda.synchronize()
+    xq = _dq(xc, xs)
+    rows = _np(st) if gather else np.arange(N)
+    xq = xq[rows]
+    wgq, wuq, wdq = (_dq(c, s) for c, s in (wg, wu, wd))
+    off = np.concatenate([[0], np.cumsum(counts)])
+    act_exact = np.zeros((N, f))
+    sens = np.zeros((N, f))  # |d act| per unit of |dg| = EPS * sum|x wg| (and likewise for u)
+    for e in range(E):
+        r = slice(off[e], off[e + 1])
+        g = xq[r] @ wgq[e].T
+        u = xq[r] @ wuq[e].T
+        sg = 1 / (1 + np.exp(-g))
+        act_exact[r] = g * sg * u
+        ga = np.abs(xq[r]) @ np.abs(wgq[e]).T
+        ua = np.abs(xq[r]) @ np.abs(wuq[e]).T
+        sens[r] = 1.1 * np.abs(u) * ga + np.abs(g * sg) * ua
+    # FC1: the GPU's block scales are the oracle's except where the block's
+    # largest |act| is within fp32 accumulation error of a power of two ...
+    ref_c, ref_s = mx.mx_quantize(act_exact)
+    got_c, got_s = _np(ac)[:N], _np(asc)[:N]
+    amax = np.abs(act_exact).reshape(N, f // 32, 32).max(-1)
+    near_pow2 = np.abs(amax / np.ldexp(1.0, np.round(np.log2(np.maximum(amax, 1e-300))).astype(int)) - 1) < 1e-4
+    bad_s = (got_s != ref_s) & ~near_pow2
+    assert not bad_s.any(), (np.argwhere(bad_s)[:5], got_s[bad_s][:5], ref_s[bad_s][:5])
+    # ... and every dequantised value is the exact act rounded to E4M3 under
+    # its block scale, up to the MFMA's accumulation error
+    EPS = 2.0 ** -12
+    X = np.repeat(np.ldexp(1.0, got_s.astype(int) - 127), 32, axis=1)
+    dq = mx.e4m3_value(got_c) * X
+    a = np.abs(act_exact) / X
+    step = np.ldexp(1.0, np.floor(np.log2(np.maximum(a, 2.0 ** -6))).astype(int) - 3) * X
+    rounding = np.where(a > 448, np.abs(act_exact) - 448 * X, 0.5 * step)
+    bound = rounding + EPS * sens + step * 1e-9
+    bad = np.abs(dq - act_exact) > bound
+    assert not bad.any(), (int(bad.sum()), np.argwhere(bad)[:5], dq[bad][:5], act_exact[bad][:5],
+                           bound[bad][:5])
+    assert (got_c == mx.mx_quantize(act_exact)[0]).mean() > 0.99
+    # FC2 on the GPU's act codes: exact inputs, bf16 output
+    y_ref = np.zeros((N, h))
+    for e in range(E):
+        r = slice(off[e], off[e + 1])
+        y_ref[r] = dq[r] @ wdq[e].T
+    assert_close(_np(y[:N].float()), y_ref, "bf16", "y")
+
+
+def test_mxfp8_rejects_bad_sizes():
+    p = None
+    lib = moe.load()
+    import ctypes
+    q = ctypes.c_void_p(16)
+    assert lib.moe_mxfp8_quantize(4, 48, 1, q, q, q, p) == 2          # cols % 32
+    assert lib.moe_grouped_fc2_mxfp8(4, 192, 256, 8, q, q, q, q, q, q, p) == 2  # h % 128
