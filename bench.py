@@ -37,11 +37,13 @@ if ROOT not in sys.path:
 METRIC = "MoE-layer fwd tokens/sec + grouped-GEMM TFLOPS (% of MI355X bf16 MFMA peak)"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+MFMA_FP8_PEAK_TFLOPS = 5000.0   # MI355X dense fp8 MFMA, published
 FP32_PEAK_TFLOPS = 157.3        # MI355X fp32 (used for fp32 layers)
 KERNEL_SOURCES = {  # stage -> source file that holds its kernel
     "route": "route.hip", "permute": "permute.hip", "fc1": "gmm.hip", "fc2": "gmm.hip",
-    "shared": "gmm.hip", "combine": "combine.hip",
+    "shared": "gmm.hip", "combine": "combine.hip", "quantize": "mx.hip",
 }
+MX_SOURCES = {"fc1": "gmm_mx.hip", "fc2": "gmm_mx.hip", "shared": "gmm_mx.hip"}
 
 
 def parse():
@@ -59,11 +61,14 @@ def parse():
     p.add_argument("--no-gather", action="store_true", help="materialise permuted_x")
     p.add_argument("--no-overlap", action="store_true", help="shared expert on the main stream")
     p.add_argument("--no-cold", action="store_true", help="skip the cache-flushed pass")
+    p.add_argument("--precision", default="bf16", choices=("bf16", "mxfp8"),
+                   help="expert GEMM operands (mxfp8: OCP MX blocks of 32, E4M3)")
     return p.parse_args()
 
 
-def source_hash(stage: str) -> str:
-    path = os.path.join(ROOT, "combine_router_gating_amd", "csrc", KERNEL_SOURCES[stage])
+def source_hash(stage: str, mx: bool = False) -> str:
+    src = MX_SOURCES[stage] if mx and stage in MX_SOURCES else KERNEL_SOURCES[stage]
+    path = os.path.join(ROOT, "combine_router_gating_amd", "csrc", src)
     h = hashlib.sha256()
     for f in (path, os.path.join(ROOT, "combine_router_gating_amd", "csrc", "moe_internal.h"),
               os.path.join(ROOT, "combine_router_gating_amd", "build.py")):
@@ -71,9 +76,9 @@ def source_hash(stage: str) -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(stage: str, workload: str):
+def read_traffic(stage: str, workload: str, mx: bool = False):
     """HBM bytes per launch from a committed counter summary, if current."""
-    path = os.path.join(ROOT, "profiles", f"pmc_{stage}_{workload}.md")
+    path = os.path.join(ROOT, "profiles", f"pmc_{stage}_{workload}{'_mxfp8' if mx else ''}.md")
     if not os.path.exists(path):
         return None
     kv = {}
@@ -81,7 +86,7 @@ def read_traffic(stage: str, workload: str):
         if line.startswith("- ") and ":" in line:
             k, v = line[2:].split(":", 1)
             kv[k.strip()] = v.strip().strip("`")
-    if kv.get("source_sha256") != source_hash(stage):
+    if kv.get("source_sha256") != source_hash(stage, mx):
         return None
     try:
         return float(kv["traffic_bytes_per_launch"])
@@ -89,9 +94,11 @@ def read_traffic(stage: str, workload: str):
         return None
 
 
-def stage_work(cfg, n, T, fs, gather=False):
+def stage_work(cfg, n, T, fs, gather=False, mx=False):
     """Algorithmic bytes and flops of each stage (kept rows only, no padding,
-    each tensor moved once).  With `gather` the permute moves no rows."""
+    each tensor moved once).  With `gather` the permute moves no rows; with
+    `mx` the GEMM operands are MXFP8 (1 byte per value + 1 scale byte per 32)
+    and the expert outputs bf16."""
     b = 4 if cfg.dtype == "f32" else 2
     h, f, E, K = cfg.h, cfg.f, cfg.E, cfg.K
     N = int(sum(n))
@@ -106,6 +113,13 @@ def stage_work(cfg, n, T, fs, gather=False):
     }
     if fs:
         w["shared"] = (3 * h * fs * b + 2 * T * h * b + 2 * T * fs * b, 6.0 * T * h * fs)
+    if mx:
+        q = 1.0 + 1.0 / 32
+        w["quantize"] = (T * h * b + T * h * q, 0.0)
+        w["fc1"] = (active * 2 * h * f * q + N * h * q + N * f * q, 4.0 * N * h * f)
+        w["fc2"] = (active * h * f * q + N * f * q + N * h * b, 2.0 * N * h * f)
+        if fs:
+            w["shared"] = (3 * h * fs * q + T * h * q + 2 * T * fs * q + T * h * b, 6.0 * T * h * fs)
     return w
 
 
@@ -191,9 +205,11 @@ def main():
         del a, bb
     inp = datagen.make_inputs(cfg, seed=args.seed, device=dev)
     gather = not args.no_gather
+    mx = args.precision == "mxfp8"
     layer = MoELayerForward(inp, K=cfg.K, score=cfg.score, pre_softmax=cfg.pre_softmax,
                             capacity_factor=cfg.capacity_factor, min_capacity=cfg.min_capacity,
-                            gather=gather, overlap_shared=not args.no_overlap)
+                            gather=gather, overlap_shared=not args.no_overlap,
+                            precision=args.precision)
     for _ in range(args.warmup):
         layer.forward()
     torch.cuda.synchronize()
@@ -226,13 +242,14 @@ def main():
 
     n = layer.tokens_per_expert.cpu().tolist()
     N = int(sum(n))
-    work = stage_work(cfg, n, cfg.T, layer.fs if layer.shared else 0, gather)
+    work = stage_work(cfg, n, cfg.T, layer.fs if layer.shared else 0, gather, mx)
     gemm_stages = [s for s in ("fc1", "fc2", "shared") if s in stage_ms]
     gemm_flops = sum(work[s][1] for s in gemm_stages)
     gemm_bytes = sum(work[s][0] for s in gemm_stages)
     gemm_ms = sum(stage_ms[s] for s in gemm_stages)
     gemm_tflops = gemm_flops / (gemm_ms * 1e-3) / 1e12
-    peak_tf = MFMA_BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else FP32_PEAK_TFLOPS
+    peak_tf = (MFMA_FP8_PEAK_TFLOPS if mx else
+               MFMA_BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else FP32_PEAK_TFLOPS)
     attainable_tf = min(peak_tf, gemm_flops / gemm_bytes * HBM_PEAK_GBS * 1e9 / 1e12)
 
     single_kernel = ("fc1", "fc2", "shared", "combine")
@@ -247,7 +264,7 @@ def main():
         roof = {"bound": "hbm", "achieved": nbytes / sec / 1e9, "peak": HBM_PEAK_GBS,
                 "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = read_traffic(dom, cfg.name)
+    roof["traffic"] = read_traffic(dom, cfg.name, mx)
     roof["kernel"] = dom
     roof["algorithmic_bytes"] = nbytes
     roof["algorithmic_flops"] = flops
@@ -286,14 +303,16 @@ def main():
     rec = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "mxfp8-e4m3 expert GEMMs (OCP MX blocks of 32), bf16 elsewhere" if mx else cfg.dtype,
         "data": "synthetic (seeded; random-init weights)",
         "config": {"workload": f"{cfg.name}: T={cfg.T} h={cfg.h} E={cfg.E} K={cfg.K} f={cfg.f}"
                                f" {cfg.score}{'' if cfg.pre_softmax else '-renorm'}"
                                f" cap={cfg.capacity_factor} shared_f={cfg.shared_f}",
                    "tokens": cfg.T, "routed_rows": N, "dropped": cfg.T * cfg.K - N,
                    "parallelism": "single GPU, EP=1",
-                   "gather_fc1": gather, "shared_overlap": layer.overlap_shared},
+                   "gather_fc1": layer.gather, "shared_overlap": layer.overlap_shared,
+                   "expert_precision": args.precision},
         "forward_ms": {"mean": sum(fwd) / len(fwd), "p10": pct(fwd, 10), "p50": pct(fwd, 50),
                        "p90": pct(fwd, 90)},
         "gemm_tflops": gemm_tflops,

@@ -39,20 +39,22 @@ __device__ __forceinline__ void dma4(const void* gptr, uint32_t lds_base) {
 
 struct MxA {
   const uint8_t* codes;    // [a_rows, K]
-  const uint8_t* scales;   // [a_rows, K/32]
+  const uint8_t* scales;   // row-major [a_rows, K/32], or k-tiled [K/128, a_rows, 4]
   const int32_t* gather;   // GEMM row i reads source row gather[i], or row i if NULL
   int64_t rows;            // a_rows
+  bool tiled;              // scale layout
 };
 struct MxB {
   const uint8_t* codes0;   // [E, N, K]
-  const uint8_t* scales0;  // [E, N, K/32]
+  const uint8_t* scales0;  // k-tiled [E, K/128, N, 4]
   const uint8_t* codes1;   // FC1: W_up
   const uint8_t* scales1;
 };
 struct MxOut {
   uint8_t* codes;      // FC1: act codes [max_rows, N]
-  uint8_t* scales;     // FC1: act scales [max_rows, N/32]
+  uint8_t* scales;     // FC1: act scales, k-tiled [N/128, max_rows, 4]
   uint16_t* bf16;      // FC2: expert_out [max_rows, N]
+  int64_t rows;        // max_rows
 };
 
 template <int BM, int BN, bool FC1, int NW, int STAGES>
@@ -85,7 +87,7 @@ __device__ __forceinline__ void mx_tile(const Tile& tile, char* smem, const MxA&
   const int l32 = lane & 31, hi = lane >> 5;
   const uint32_t smem_base = static_cast<uint32_t>(
       reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)smem));
-  const int64_t KB = K / 32;  // scale bytes per row
+  const int64_t KB = K / 32;  // scale bytes per row (row-major layout)
   const int64_t b_expert = static_cast<int64_t>(tile.e) * N;
 
   // source row (clamped in range; padding rows are computed, never stored)
@@ -108,16 +110,22 @@ __device__ __forceinline__ void mx_tile(const Tile& tile, char* smem, const MxA&
       src[j] = base + (b_expert + n) * K + c * 16;
     }
   }
+  // this lane's scale dword of stage kt: ssrc + kt * sstep (k-tiled layouts
+  // put consecutive rows next to each other, so a wave's loads coalesce)
   const uint8_t* ssrc;
+  int64_t sstep;
   {
     const int r = min(wave * 64 + lane, ROWS - 1);
     if (r < BM) {
-      ssrc = A.scales + a_row(r) * KB;
+      const int64_t ar = a_row(r);
+      ssrc = A.tiled ? A.scales + ar * 4 : A.scales + ar * KB;
+      sstep = A.tiled ? A.rows * 4 : 4;
     } else {
       const int br = r - BM;
       const uint8_t* base = (NB == 2 && br >= BN) ? B.scales1 : B.scales0;
       const int n = min(n0 + (br % BN), N - 1);
-      ssrc = base + (b_expert + n) * KB;
+      ssrc = base + (static_cast<int64_t>(tile.e) * (K / kMxK) * N + n) * 4;
+      sstep = static_cast<int64_t>(N) * 4;
     }
   }
   auto issue = [&](int kt) {
@@ -125,7 +133,7 @@ __device__ __forceinline__ void mx_tile(const Tile& tile, char* smem, const MxA&
     const int64_t ko = static_cast<int64_t>(kt) * kMxK;
 #pragma unroll
     for (int j = 0; j < LPW; ++j) dma16(src[j] + ko, dst + (wave * LPW + j) * 1024);
-    dma4(ssrc + kt * 4, dst + DATA + wave * 256);
+    dma4(ssrc + kt * sstep, dst + DATA + wave * 256);
   };
 
   f32x16 acc[NB][MI][NI];
@@ -216,7 +224,8 @@ __device__ __forceinline__ void mx_tile(const Tile& tile, char* smem, const MxA&
             for (int q = 0; q < 4; ++q) word |= e4m3_code(v[4 * g + q] * inv) << (8 * q);
             *reinterpret_cast<uint32_t*>(O.codes + grow * N + nc + 8 * g + 4 * hi) = word;
           }
-          if (hi == 0) O.scales[grow * (N / 32) + nc / 32] = static_cast<uint8_t>(e + 127);
+          if (hi == 0)
+            O.scales[((nc / kMxK) * O.rows + grow) * 4 + ((nc / 32) & 3)] = static_cast<uint8_t>(e + 127);
         }
       } else {
         if (!row_ok || nc >= N) continue;
@@ -334,9 +343,9 @@ extern "C" moe_status moe_grouped_fc1_swiglu_mxfp8(
   MOE_REQUIRE(x_codes && x_scales && tokens_per_expert && wg_codes && wg_scales && wu_codes &&
                   wu_scales && act_codes && act_scales,
               MOE_ERR_ARG, "moe_grouped_fc1_swiglu_mxfp8: NULL tensor argument");
-  const MxA a{x_codes, x_scales, sorted_token, sorted_token ? T : max_rows};
+  const MxA a{x_codes, x_scales, sorted_token, sorted_token ? T : max_rows, false};
   const MxB b{wg_codes, wg_scales, wu_codes, wu_scales};
-  const MxOut o{act_codes, act_scales, nullptr};
+  const MxOut o{act_codes, act_scales, nullptr, max_rows};
   const hipStream_t s = as_stream(stream);
   const int bm = pick_bm_mx(max_rows, E);
   if (bm == 256)
@@ -358,9 +367,9 @@ extern "C" moe_status moe_grouped_fc2_mxfp8(int64_t E, int64_t h, int64_t f, int
   if (max_rows == 0) return MOE_OK;
   MOE_REQUIRE(act_codes && act_scales && tokens_per_expert && wd_codes && wd_scales && expert_out,
               MOE_ERR_ARG, "moe_grouped_fc2_mxfp8: NULL tensor argument");
-  const MxA a{act_codes, act_scales, nullptr, max_rows};
+  const MxA a{act_codes, act_scales, nullptr, max_rows, true};
   const MxB b{wd_codes, wd_scales, nullptr, nullptr};
-  const MxOut o{nullptr, nullptr, static_cast<uint16_t*>(expert_out)};
+  const MxOut o{nullptr, nullptr, static_cast<uint16_t*>(expert_out), max_rows};
   const hipStream_t s = as_stream(stream);
   const int bm = pick_bm_mx(max_rows, E);
   if (bm == 256)

@@ -10,6 +10,11 @@
 // rounded to the nearest E4M3 value, ties to even, saturated to +-448.
 // E4M3: sign, 4 exponent bits (bias 7), 3 mantissa bits, subnormals
 // m * 2^-9, no infinities.
+//
+// Scale layouts: row-major [rows, cols/32], or k-tiled for GEMM operands
+// whose rows a tile reads contiguously: [rows/R, cols/128, R, 4], so that
+// the 4 scales of one 128-wide k stage of R consecutive rows are one
+// contiguous run of 4R bytes (R = rows per expert for a weight).
 #include "mx_codec.h"
 
 namespace moe {
@@ -19,7 +24,8 @@ namespace {
 // One lane per 32-value block; a wave covers 64 consecutive blocks of a row.
 template <typename T>
 __global__ void __launch_bounds__(256) mx_quantize_kernel(const T* __restrict__ src, int64_t rows,
-                                                          int64_t cols, uint8_t* __restrict__ codes,
+                                                          int64_t cols, int64_t tile_rows,
+                                                          uint8_t* __restrict__ codes,
                                                           uint8_t* __restrict__ scales) {
   const int64_t nb = cols / 32;
   const int64_t blk = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
@@ -48,7 +54,14 @@ __global__ void __launch_bounds__(256) mx_quantize_kernel(const T* __restrict__ 
   uint4* out = reinterpret_cast<uint4*>(codes + row * cols + b * 32);
   out[0] = make_uint4(w[0], w[1], w[2], w[3]);
   out[1] = make_uint4(w[4], w[5], w[6], w[7]);
-  scales[row * nb + b] = static_cast<uint8_t>(e + 127);
+  int64_t si;
+  if (tile_rows > 0) {  // [rows/tile_rows, cols/128, tile_rows, 4]
+    const int64_t g = row / tile_rows, r = row % tile_rows;
+    si = ((g * (cols / 128) + b / 4) * tile_rows + r) * 4 + (b & 3);
+  } else {
+    si = row * nb + b;
+  }
+  scales[si] = static_cast<uint8_t>(e + 127);
 }
 
 }  // namespace
@@ -56,12 +69,17 @@ __global__ void __launch_bounds__(256) mx_quantize_kernel(const T* __restrict__ 
 
 using namespace moe;
 
-extern "C" moe_status moe_mxfp8_quantize(int64_t rows, int64_t cols, int32_t dtype, const void* src,
-                                         uint8_t* codes, uint8_t* scales, void* stream) {
+extern "C" moe_status moe_mxfp8_quantize(int64_t rows, int64_t cols, int64_t tile_rows,
+                                         int32_t dtype, const void* src, uint8_t* codes,
+                                         uint8_t* scales, void* stream) {
   MOE_REQUIRE(rows >= 0 && cols >= 0, MOE_ERR_ARG, "moe_mxfp8_quantize: negative size");
   MOE_REQUIRE(cols % 32 == 0, MOE_ERR_UNSUPPORTED, "moe_mxfp8_quantize: cols=%lld is not a multiple of 32",
               (long long)cols);
   MOE_REQUIRE(dtype == MOE_F32 || dtype == MOE_BF16, MOE_ERR_ARG, "moe_mxfp8_quantize: bad dtype %d", dtype);
+  MOE_REQUIRE(tile_rows >= 0, MOE_ERR_ARG, "moe_mxfp8_quantize: tile_rows < 0");
+  MOE_REQUIRE(tile_rows == 0 || (cols % 128 == 0 && rows % tile_rows == 0), MOE_ERR_UNSUPPORTED,
+              "moe_mxfp8_quantize: the k-tiled scale layout needs cols %% 128 == 0 and rows %% "
+              "tile_rows == 0");
   MOE_REQUIRE(rows * (cols / 32) < (int64_t(1) << 40), MOE_ERR_UNSUPPORTED, "moe_mxfp8_quantize: too large");
   if (rows == 0 || cols == 0) return MOE_OK;
   MOE_REQUIRE(src && codes && scales, MOE_ERR_ARG, "moe_mxfp8_quantize: NULL tensor argument");
@@ -69,9 +87,9 @@ extern "C" moe_status moe_mxfp8_quantize(int64_t rows, int64_t cols, int32_t dty
   const dim3 grid(static_cast<unsigned>(ceil_div(blocks, 256)));
   if (dtype == MOE_BF16)
     hipLaunchKernelGGL(mx_quantize_kernel<uint16_t>, grid, dim3(256), 0, as_stream(stream),
-                       static_cast<const uint16_t*>(src), rows, cols, codes, scales);
+                       static_cast<const uint16_t*>(src), rows, cols, tile_rows, codes, scales);
   else
     hipLaunchKernelGGL(mx_quantize_kernel<float>, grid, dim3(256), 0, as_stream(stream),
-                       static_cast<const float*>(src), rows, cols, codes, scales);
+                       static_cast<const float*>(src), rows, cols, tile_rows, codes, scales);
   return check_launch("moe_mxfp8_quantize");
 }

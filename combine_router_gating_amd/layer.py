@@ -6,7 +6,10 @@ it can also be captured into a graph.
 Options: `gather` skips the permuted copy of x (the permute writes indices
 and probs only, and FC1 reads token rows through sorted_token);
 `overlap_shared` runs the shared expert on a second stream (default
-priority) from the start of the forward, joined before the combine."""
+priority) from the start of the forward, joined before the combine;
+`precision="mxfp8"` runs the expert GEMMs (routed and shared) on MXFP8
+operands: the weights are quantised once here, x once per forward (the
+router still reads the bf16 x), FC1 writes MXFP8 act, FC2 bf16 outputs."""
 from __future__ import annotations
 
 import ctypes
@@ -26,12 +29,12 @@ def _p(t: Optional[torch.Tensor]):
 class MoELayerForward:
     """route -> permute -> FC1+SwiGLU -> FC2 (-> shared expert) -> combine."""
 
-    STAGES = ("route", "permute", "fc1", "fc2", "shared", "combine")
+    STAGES = ("quantize", "route", "permute", "fc1", "fc2", "shared", "combine")
 
     def __init__(self, inp: Dict[str, torch.Tensor], *, K: int, score: str = "softmax",
                  pre_softmax: bool = True, capacity_factor: float = 0.0, min_capacity: int = 0,
                  drop_policy: str = "position", pad_to_capacity: bool = False,
-                 gather: bool = False, overlap_shared: bool = False):
+                 gather: bool = False, overlap_shared: bool = False, precision: str = "bf16"):
         self.lib = _lib.load()
         self.inp = inp
         x = _need(inp["x"], "x")
@@ -52,25 +55,42 @@ class MoELayerForward:
         self.logits = e((T, E), dtype=torch.float32, device=dev)
         self.route_ws_bytes = int(self.lib.moe_route_workspace_size(ctypes.byref(self.desc)))
         self.route_ws = e((max(self.route_ws_bytes, 1),), dtype=torch.uint8, device=dev)
-        self.gather = gather
-        self.permuted_x = None if gather else e((R, h), dtype=x.dtype, device=dev)
+        if precision not in ("bf16", "mxfp8"):
+            raise ValueError(f"unknown precision {precision!r}")
+        self.mx = precision == "mxfp8"
+        if self.mx and x.dtype != torch.bfloat16:
+            raise ValueError("the MXFP8 experts take a bf16 layer")
+        self.gather = gather or self.mx
+        self.permuted_x = None if self.gather else e((R, h), dtype=x.dtype, device=dev)
         self.permuted_probs = e((R,), dtype=torch.float32, device=dev)
         self.sorted_token = e((R,), dtype=torch.int32, device=dev)
         self.row_id_map = e((T, K), dtype=torch.int32, device=dev)
         self.expert_offsets = e((E + 1,), dtype=torch.int32, device=dev)
         self.perm_ws_bytes = int(self.lib.moe_permute_workspace_size(T, E))
         self.perm_ws = e((max(self.perm_ws_bytes, 1),), dtype=torch.uint8, device=dev)
-        self.act = e((R, f), dtype=x.dtype, device=dev)
+        self.act = None if self.mx else e((R, f), dtype=x.dtype, device=dev)
         self.expert_out = e((R, h), dtype=x.dtype, device=dev)
         self.out = e((T, h), dtype=x.dtype, device=dev)
         self.shared = "shared_gate" in inp
         if self.shared:
             self.fs = inp["shared_gate"].shape[0]
             self.shared_count = torch.full((1,), T, dtype=torch.int32, device=dev)
-            self.shared_act = e((T, self.fs), dtype=x.dtype, device=dev)
+            self.shared_act = None if self.mx else e((T, self.fs), dtype=x.dtype, device=dev)
             self.shared_out = e((T, h), dtype=x.dtype, device=dev)
         else:
             self.shared_out = None
+        if self.mx:
+            u8 = torch.uint8
+            q = self._quantize_weight
+            self.wq = {k: q(inp[k]) for k in ("w_gate", "w_up", "w_down")}
+            self.xq = (e((T, h), dtype=u8, device=dev), e((T, h // 32), dtype=u8, device=dev))
+            self.actq = (e((R, f), dtype=u8, device=dev), e((f // 128, R, 4), dtype=u8, device=dev))
+            if self.shared:
+                self.wq.update({k: q(inp[k][None]) for k in ("shared_gate", "shared_up",
+                                                              "shared_down")})
+                fs = self.fs
+                self.shared_actq = (e((T, fs), dtype=u8, device=dev),
+                                    e((fs // 128, T, 4), dtype=u8, device=dev))
         self.overlap_shared = bool(overlap_shared and self.shared)
         if self.overlap_shared:
             self.side = torch.cuda.Stream(device=dev)  # default priority
@@ -79,6 +99,20 @@ class MoELayerForward:
 
     def _stream(self):
         return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def _quantize_weight(self, w: torch.Tensor):
+        """MXFP8 codes and k-tiled scales of a [E, n, k] weight along k (done once)."""
+        E, n, k = w.shape
+        codes = torch.empty((E, n, k), dtype=torch.uint8, device=w.device)
+        scales = torch.empty((E, k // 128, n, 4), dtype=torch.uint8, device=w.device)
+        check("moe_mxfp8_quantize", self.lib.moe_mxfp8_quantize(
+            E * n, k, n, self.dt, _p(w), _p(codes), _p(scales), self._stream()))
+        return codes, scales
+
+    def quantize(self):
+        check("moe_mxfp8_quantize", self.lib.moe_mxfp8_quantize(
+            self.T, self.h, 0, self.dt, _p(self.inp["x"]), _p(self.xq[0]), _p(self.xq[1]),
+            self._stream()))
 
     def route(self):
         i = self.inp
@@ -98,6 +132,13 @@ class MoELayerForward:
 
     def fc1(self):
         i = self.inp
+        if self.mx:
+            wg, wu = self.wq["w_gate"], self.wq["w_up"]
+            check("moe_grouped_fc1_swiglu_mxfp8", self.lib.moe_grouped_fc1_swiglu_mxfp8(
+                self.E, self.h, self.f, self.max_rows, self.T, _p(self.xq[0]), _p(self.xq[1]),
+                _p(self.sorted_token), _p(self.tokens_per_expert), _p(wg[0]), _p(wg[1]),
+                _p(wu[0]), _p(wu[1]), _p(self.actq[0]), _p(self.actq[1]), self._stream()))
+            return
         if self.gather:
             check("moe_grouped_fc1_swiglu_gather", self.lib.moe_grouped_fc1_swiglu_gather(
                 self.E, self.h, self.f, self.max_rows, self.dt, self.T, _p(i["x"]),
@@ -110,6 +151,13 @@ class MoELayerForward:
             self._stream()))
 
     def fc2(self):
+        if self.mx:
+            wd = self.wq["w_down"]
+            check("moe_grouped_fc2_mxfp8", self.lib.moe_grouped_fc2_mxfp8(
+                self.E, self.h, self.f, self.max_rows, _p(self.actq[0]), _p(self.actq[1]),
+                _p(self.tokens_per_expert), _p(wd[0]), _p(wd[1]), _p(self.expert_out),
+                self._stream()))
+            return
         check("moe_grouped_fc2", self.lib.moe_grouped_fc2(
             self.E, self.h, self.f, self.max_rows, self.dt, _p(self.act),
             _p(self.tokens_per_expert), _p(self.inp["w_down"]), _p(self.expert_out),
@@ -119,6 +167,17 @@ class MoELayerForward:
         if not self.shared:
             return
         i = self.inp
+        if self.mx:
+            wg, wu, wd = (self.wq[k] for k in ("shared_gate", "shared_up", "shared_down"))
+            check("moe_grouped_fc1_swiglu_mxfp8", self.lib.moe_grouped_fc1_swiglu_mxfp8(
+                1, self.h, self.fs, self.T, self.T, _p(self.xq[0]), _p(self.xq[1]), None,
+                _p(self.shared_count), _p(wg[0]), _p(wg[1]), _p(wu[0]), _p(wu[1]),
+                _p(self.shared_actq[0]), _p(self.shared_actq[1]), self._stream()))
+            check("moe_grouped_fc2_mxfp8", self.lib.moe_grouped_fc2_mxfp8(
+                1, self.h, self.fs, self.T, _p(self.shared_actq[0]), _p(self.shared_actq[1]),
+                _p(self.shared_count), _p(wd[0]), _p(wd[1]), _p(self.shared_out),
+                self._stream()))
+            return
         check("moe_grouped_fc1_swiglu", self.lib.moe_grouped_fc1_swiglu(
             1, self.h, self.fs, self.T, self.dt, _p(i["x"]), _p(self.shared_count),
             _p(i["shared_gate"]), _p(i["shared_up"]), _p(self.shared_act), self._stream()))
@@ -134,19 +193,31 @@ class MoELayerForward:
 
     def stages(self):
         """Stage names in launch order on the main stream."""
-        return [n for n in self.STAGES if n != "shared" or (self.shared and not self.overlap_shared)]
+        keep = []
+        for n in self.STAGES:
+            if n == "quantize" and not self.mx:
+                continue
+            if n == "shared" and (not self.shared or self.overlap_shared):
+                continue
+            keep.append(n)
+        return keep
+
+    def _fork_shared(self):
+        main = torch.cuda.current_stream()
+        self.ev_fork.record(main)
+        self.side.wait_event(self.ev_fork)
+        with torch.cuda.stream(self.side):
+            self.shared_expert()
+            self.ev_join.record(self.side)
 
     def forward(self, mark: Optional[Callable[[str], None]] = None) -> torch.Tensor:
         """One layer forward.  `mark(name)` is called before each main-stream
         stage and once more with "end" (used to record timing events)."""
-        if self.overlap_shared:
-            main = torch.cuda.current_stream()
-            self.ev_fork.record(main)
-            self.side.wait_event(self.ev_fork)
-            with torch.cuda.stream(self.side):
-                self.shared_expert()
-                self.ev_join.record(self.side)
+        forked = not self.overlap_shared
         for name in self.stages():
+            if not forked and name != "quantize":  # the shared expert reads the quantised x
+                self._fork_shared()
+                forked = True
             if name == "combine" and self.overlap_shared:
                 torch.cuda.current_stream().wait_event(self.ev_join)
             if mark:

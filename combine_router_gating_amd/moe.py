@@ -274,24 +274,36 @@ def moe_grouped_mlp(permuted_x: torch.Tensor, tokens_per_expert: torch.Tensor,
     return act, out
 
 
-def moe_mxfp8_quantize(src: torch.Tensor):
-    """MXFP8-E4M3 of a 2-D tensor along its last dim: (codes uint8, scales uint8)."""
+def moe_mxfp8_quantize(src: torch.Tensor, tile_rows: int = 0):
+    """MXFP8-E4M3 of a 2-D tensor along its last dim: (codes uint8 [rows, cols],
+    scales uint8): row-major [rows, cols/32] when tile_rows = 0, else k-tiled
+    [rows/R, cols/128, R, 4] with R = tile_rows."""
     _need(src, "src")
-    if src.dim() != 2:
-        src = src.reshape(-1, src.shape[-1])
     rows, cols = src.shape
     codes = torch.empty((rows, cols), dtype=torch.uint8, device=src.device)
-    scales = torch.empty((rows, cols // 32), dtype=torch.uint8, device=src.device)
-    st = _lib.load().moe_mxfp8_quantize(rows, cols, _dtype_code(src, "src"), _ptr(src), _ptr(codes),
-                                        _ptr(scales), _stream())
+    if tile_rows:
+        scales = torch.empty((rows // tile_rows, cols // 128, tile_rows, 4), dtype=torch.uint8,
+                             device=src.device)
+    else:
+        scales = torch.empty((rows, cols // 32), dtype=torch.uint8, device=src.device)
+    st = _lib.load().moe_mxfp8_quantize(rows, cols, int(tile_rows), _dtype_code(src, "src"),
+                                        _ptr(src), _ptr(codes), _ptr(scales), _stream())
     check("moe_mxfp8_quantize", st)
     return codes, scales
 
 
+def moe_mxfp8_quantize_weight(w: torch.Tensor):
+    """A [E, n, k] weight in the layout the MXFP8 GEMMs read: (codes [E, n, k],
+    scales k-tiled [E, k/128, n, 4])."""
+    E, n, k = w.shape
+    codes, scales = moe_mxfp8_quantize(w.reshape(E * n, k), tile_rows=n)
+    return codes.reshape(E, n, k), scales
+
+
 def moe_grouped_fc1_swiglu_mxfp8(x_codes, x_scales, sorted_token, tokens_per_expert, wg, wu,
                                  max_rows: int, act=None):
-    """MXFP8 FC1 + SwiGLU: wg/wu = (codes [E,f,h], scales [E,f,h/32]);
-    returns (act_codes [max_rows,f], act_scales [max_rows,f/32])."""
+    """MXFP8 FC1 + SwiGLU: wg/wu from moe_mxfp8_quantize_weight; returns
+    (act_codes [max_rows,f], act_scales k-tiled [f/128, max_rows, 4])."""
     T, h = x_codes.shape
     E, f, _ = wg[0].shape
     _need(x_codes, "x_codes", torch.uint8)
@@ -299,12 +311,12 @@ def moe_grouped_fc1_swiglu_mxfp8(x_codes, x_scales, sorted_token, tokens_per_exp
     _need(tokens_per_expert, "tokens_per_expert", torch.int32, (E,))
     for name, (c, sc) in (("wg", wg), ("wu", wu)):
         _need(c, name, torch.uint8, (E, f, h))
-        _need(sc, name + " scales", torch.uint8, (E, f, h // 32))
+        _need(sc, name + " scales", torch.uint8, (E, h // 128, f, 4))
     if sorted_token is not None:
         _need(sorted_token, "sorted_token", torch.int32)
     if act is None:
         act = (torch.empty((max_rows, f), dtype=torch.uint8, device=x_codes.device),
-               torch.empty((max_rows, f // 32), dtype=torch.uint8, device=x_codes.device))
+               torch.empty((f // 128, max_rows, 4), dtype=torch.uint8, device=x_codes.device))
     st = _lib.load().moe_grouped_fc1_swiglu_mxfp8(
         E, h, f, max_rows, T, _ptr(x_codes), _ptr(x_scales), _ptr(sorted_token),
         _ptr(tokens_per_expert), _ptr(wg[0]), _ptr(wg[1]), _ptr(wu[0]), _ptr(wu[1]), _ptr(act[0]),
@@ -314,13 +326,13 @@ def moe_grouped_fc1_swiglu_mxfp8(x_codes, x_scales, sorted_token, tokens_per_exp
 
 
 def moe_grouped_fc2_mxfp8(act_codes, act_scales, tokens_per_expert, wd, expert_out=None):
-    """MXFP8 FC2: wd = (codes [E,h,f], scales [E,h,f/32]); returns bf16 [max_rows,h]."""
+    """MXFP8 FC2 on FC1's act: wd from moe_mxfp8_quantize_weight; returns bf16 [max_rows,h]."""
     rows, f = act_codes.shape
     E, h, _ = wd[0].shape
     _need(act_codes, "act_codes", torch.uint8)
-    _need(act_scales, "act_scales", torch.uint8, (rows, f // 32))
+    _need(act_scales, "act_scales", torch.uint8, (f // 128, rows, 4))
     _need(wd[0], "wd", torch.uint8, (E, h, f))
-    _need(wd[1], "wd scales", torch.uint8, (E, h, f // 32))
+    _need(wd[1], "wd scales", torch.uint8, (E, f // 128, h, 4))
     if expert_out is None:
         expert_out = torch.empty((rows, h), dtype=torch.bfloat16, device=act_codes.device)
     st = _lib.load().moe_grouped_fc2_mxfp8(E, h, f, rows, _ptr(act_codes), _ptr(act_scales),

@@ -281,25 +281,31 @@ moe_status moe_grouped_fc2(int64_t E, int64_t h, int64_t f, int64_t max_rows, in
  * byte X = 2^(floor(log2 amax) - 8) (code = exponent + 127; an all-zero
  * block has code 0); each value is stored as the E4M3 code of V / X
  * (nearest, ties to even, saturated to +-448).  Codes are [rows, cols]
- * uint8, scales [rows, cols/32] uint8, both row-major.
+ * uint8.  Scales are uint8 in one of two layouts: row-major [rows, cols/32],
+ * or k-tiled with R rows per group, [rows/R, cols/128, R, 4] (the 4 scales
+ * of one 128-wide k stage of R consecutive rows are contiguous), which the
+ * GEMMs read for the weights (R = rows per expert) and for act.
  * ------------------------------------------------------------------------ */
 
 /* moe_mxfp8_quantize — quantise src [rows, cols] (dtype bf16 or fp32) along
- * cols (a multiple of 32) into codes [rows, cols] and scales [rows, cols/32].
- * Use it on x per forward, and once on the weights ([E*f, h] for W_gate and
- * W_up, [E*h, f] for W_down). */
-moe_status moe_mxfp8_quantize(int64_t rows, int64_t cols, int32_t dtype, const void* src,
-                              uint8_t* codes, uint8_t* scales, void* stream);
+ * cols (a multiple of 32) into codes [rows, cols] and scales: row-major when
+ * tile_rows = 0, else k-tiled with R = tile_rows (cols % 128 == 0, rows %
+ * tile_rows == 0).  Use it on x per forward (row-major), and once on the
+ * weights (k-tiled: [E*f, h] with tile_rows = f for W_gate and W_up,
+ * [E*h, f] with tile_rows = h for W_down). */
+moe_status moe_mxfp8_quantize(int64_t rows, int64_t cols, int64_t tile_rows, int32_t dtype,
+                              const void* src, uint8_t* codes, uint8_t* scales, void* stream);
 
 /*
  * moe_grouped_fc1_swiglu_mxfp8 — act = silu(x Wg^T) * (x Wu^T) on MXFP8
- * operands, fp32 accumulation, act quantised to MXFP8 along f.
- *   x_codes, x_scales   [T,h], [T,h/32]   token-major MXFP8 x
+ * operands, fp32 accumulation in the MFMA, act quantised to MXFP8 along f.
+ *   x_codes, x_scales   [T,h], row-major [T,h/32]   token-major MXFP8 x
  *   sorted_token        [max_rows] int32 or NULL: GEMM row i reads x row
  *                       sorted_token[i] (clamped to [0, T)); NULL: rows are
  *                       already expert-major ([max_rows, h])
- *   wg_*, wu_*          [E,f,h], [E,f,h/32]
- *   act_codes, act_scales  [max_rows,f], [max_rows,f/32]   out
+ *   wg_*, wu_*          codes [E,f,h], scales k-tiled with R = f
+ *   act_codes           [max_rows,f]                          out
+ *   act_scales          k-tiled [f/128, max_rows, 4] (R = max_rows)   out
  * h and f multiples of 128.  Rows >= sum(tokens_per_expert) untouched.
  */
 moe_status moe_grouped_fc1_swiglu_mxfp8(int64_t E, int64_t h, int64_t f, int64_t max_rows,
@@ -311,7 +317,8 @@ moe_status moe_grouped_fc1_swiglu_mxfp8(int64_t E, int64_t h, int64_t f, int64_t
                                         uint8_t* act_scales, void* stream);
 
 /* moe_grouped_fc2_mxfp8 — expert_out [max_rows,h] (bf16) = act Wd^T on MXFP8
- * act ([max_rows,f], [max_rows,f/32]) and Wd ([E,h,f], [E,h,f/32]). */
+ * act (as moe_grouped_fc1_swiglu_mxfp8 writes it) and Wd (codes [E,h,f],
+ * scales k-tiled with R = h). */
 moe_status moe_grouped_fc2_mxfp8(int64_t E, int64_t h, int64_t f, int64_t max_rows,
                                  const uint8_t* act_codes, const uint8_t* act_scales,
                                  const int32_t* tokens_per_expert, const uint8_t* wd_codes,

@@ -48,14 +48,35 @@ def test_quantize_bit_exact(dtype):
     np.testing.assert_array_equal(_np(codes), ref_c)
 
 
+def untile(scales):
+    """k-tiled scales [G, cols/128, R, 4] (or [cols/128, R, 4]) -> row-major
+    [G, R, cols/32] (or [R, cols/32])."""
+    s = _np(scales)
+    s = np.swapaxes(s, -3, -2)
+    return s.reshape(s.shape[:-2] + (-1,))
+
+
+@pytest.mark.parametrize("tile_rows", [1, 8, 96])
+def test_quantize_tiled_layout(tile_rows):
+    rng = np.random.default_rng(tile_rows)
+    rows, cols = 192, 384
+    t = torch.from_numpy(rng.standard_normal((rows, cols)) * 3).to(torch.bfloat16).to(DEV)
+    c0, s0 = moe.moe_mxfp8_quantize(t)
+    c1, s1 = moe.moe_mxfp8_quantize(t, tile_rows=tile_rows)
+    torch.cuda.synchronize()
+    assert torch.equal(c0, c1)
+    assert s1.shape == (rows // tile_rows, cols // 128, tile_rows, 4)
+    np.testing.assert_array_equal(untile(s1).reshape(rows, cols // 32), _np(s0))
+
+
 def _weights(rng, E, n, k, std):
     w = torch.from_numpy(rng.standard_normal((E, n, k)) * std).to(torch.bfloat16).to(DEV)
-    c, s = moe.moe_mxfp8_quantize(w.reshape(E * n, k))
-    return c.reshape(E, n, k), s.reshape(E, n, k // 32)
+    return moe.moe_mxfp8_quantize_weight(w)
 
 
 def _dq(codes, scales):
-    return mx.mx_dequantize(_np(codes), _np(scales))
+    """Dequantise codes with k-tiled scales."""
+    return mx.mx_dequantize(_np(codes), untile(scales))
 
 
 CASES = [  # E, h, f, counts
@@ -86,7 +107,7 @@ def test_fc1_fc2_mxfp8(E, h, f, counts, gather):
     ac, asc = moe.moe_grouped_fc1_swiglu_mxfp8(xc, xs, st, cnt, wg, wu, N)
     y = moe.moe_grouped_fc2_mxfp8(ac, asc, cnt, wd)
     torch.cuda.synchronize()
-    xq = _dq(xc, xs)
+    xq = mx.mx_dequantize(_np(xc), _np(xs))
     rows = _np(st) if gather else np.arange(N)
     xq = xq[rows]
     wgq, wuq, wdq = (_dq(c, s) for c, s in (wg, wu, wd))
@@ -105,7 +126,7 @@ def test_fc1_fc2_mxfp8(E, h, f, counts, gather):
     # FC1: the GPU's block scales are the oracle's except where the block's
     # largest |act| is within fp32 accumulation error of a power of two ...
     ref_c, ref_s = mx.mx_quantize(act_exact)
-    got_c, got_s = _np(ac)[:N], _np(asc)[:N]
+    got_c, got_s = _np(ac)[:N], untile(asc)[:N]
     amax = np.abs(act_exact).reshape(N, f // 32, 32).max(-1)
     near_pow2 = np.abs(amax / np.ldexp(1.0, np.round(np.log2(np.maximum(amax, 1e-300))).astype(int)) - 1) < 1e-4
     bad_s = (got_s != ref_s) & ~near_pow2
@@ -136,5 +157,54 @@ def test_mxfp8_rejects_bad_sizes():
     lib = moe.load()
     import ctypes
     q = ctypes.c_void_p(16)
-    assert lib.moe_mxfp8_quantize(4, 48, 1, q, q, q, p) == 2          # cols % 32
+    assert lib.moe_mxfp8_quantize(4, 48, 0, 1, q, q, q, p) == 2       # cols % 32
+    assert lib.moe_mxfp8_quantize(4, 96, 2, 1, q, q, q, p) == 2       # tiled: cols % 128
+    assert lib.moe_mxfp8_quantize(6, 128, 4, 1, q, q, q, p) == 2      # tiled: rows % R
     assert lib.moe_grouped_fc2_mxfp8(4, 192, 256, 8, q, q, q, q, q, q, p) == 2  # h % 128
+
+
+@pytest.mark.parametrize("overlap", [False, True])
+def test_layer_mxfp8_against_the_oracle(overlap):
+    import datagen
+    import oracle
+    from combine_router_gating_amd.layer import MoELayerForward
+    from gpu_helpers import f64
+    cfg = datagen.MoEConfig("mx-layer", T=300, h=256, E=16, K=2, f=384, dtype="bf16", score="sigmoid",
+                            expert_bias=True, shared_f=256, capacity_factor=0.8)
+    log(f"mxfp8 layer overlap={overlap}: {cfg}")
+    inp = datagen.make_inputs(cfg, seed=3, device=DEV)
+    layer = MoELayerForward(inp, K=cfg.K, score=cfg.score, capacity_factor=cfg.capacity_factor,
+                            overlap_shared=overlap, precision="mxfp8")
+    out = layer.forward().clone()
+    torch.cuda.synchronize()
+    # routing is the bf16 layer's (same router kernels)
+    ref_r = oracle.route(logits=layer.logits.cpu().numpy(), K=cfg.K, score=cfg.score,
+                         expert_bias=inp["expert_bias"].cpu().numpy(),
+                         capacity_factor=cfg.capacity_factor)
+    np.testing.assert_array_equal(_np(layer.routing_map), ref_r["routing_map"])
+    # x quantisation: bit-exact
+    xc, xs = mx.mx_quantize(f64(inp["x"]))
+    np.testing.assert_array_equal(_np(layer.xq[0]), xc)
+    np.testing.assert_array_equal(_np(layer.xq[1]), xs)
+    # expert outputs from the GPU's act codes (exact inputs) and the combine
+    pm = oracle.permute(f64(inp["x"]), ref_r["routing_map"], ref_r["probs"], cfg.K)
+    N = int(pm["expert_offsets"][-1])
+    act = mx.mx_dequantize(_np(layer.actq[0])[:N], untile(layer.actq[1])[:N])
+    wd = _dq(*layer.wq["w_down"])
+    n = pm["tokens_per_expert"]
+    off = np.concatenate([[0], np.cumsum(n)])
+    y = np.zeros((N, cfg.h))
+    for e in range(cfg.E):
+        y[off[e]:off[e + 1]] = act[off[e]:off[e + 1]] @ wd[e].T
+    y = oracle.round_bf16(y)
+    sact = _dq(*layer.shared_actq)
+    swd = _dq(*layer.wq["shared_down"])[0]
+    shared = oracle.round_bf16(sact @ swd.T)
+    ref_out = oracle.combine(y, pm["permuted_probs"], pm["row_id_map"], "bf16", shared)
+    assert_close(f64(out), ref_out, "bf16", "out")
+    # the same forward without the overlap gives the same bits
+    plain = MoELayerForward(inp, K=cfg.K, score=cfg.score, capacity_factor=cfg.capacity_factor,
+                            precision="mxfp8")
+    o2 = plain.forward()
+    torch.cuda.synchronize()
+    assert torch.equal(out, o2)
