@@ -69,9 +69,10 @@ def parse():
 def source_hash(stage: str, mx: bool = False) -> str:
     src = MX_SOURCES[stage] if mx and stage in MX_SOURCES else KERNEL_SOURCES[stage]
     path = os.path.join(ROOT, "combine_router_gating_amd", "csrc", src)
+    csrc = os.path.join(ROOT, "combine_router_gating_amd", "csrc")
+    headers = sorted(os.path.join(csrc, f) for f in os.listdir(csrc) if f.endswith(".h"))
     h = hashlib.sha256()
-    for f in (path, os.path.join(ROOT, "combine_router_gating_amd", "csrc", "moe_internal.h"),
-              os.path.join(ROOT, "combine_router_gating_amd", "build.py")):
+    for f in [path] + headers + [os.path.join(ROOT, "combine_router_gating_amd", "build.py")]:
         h.update(open(f, "rb").read())
     return h.hexdigest()[:16]
 

@@ -17,6 +17,8 @@
 // The tile scheduler is the bf16 GEMM's (gmm_sched.h); a stage holds 128 k
 // (128 bytes per row, the same swizzled LDS layout) plus the rows' 4 scale
 // bytes, all filled by direct global->LDS loads.
+#include <type_traits>
+
 #include "gmm_sched.h"
 #include "mx_codec.h"
 
@@ -35,6 +37,19 @@ __device__ __forceinline__ void dma4(const void* gptr, uint32_t lds_base) {
                :
                : "v"(gptr), "s"(__builtin_amdgcn_readfirstlane(lds_base))
                : "memory");
+}
+
+// acc += (b with scale sb) x (a with scale sa), fenced.  The scaled fp8
+// MFMA reads its 8-register operands over several cycles after it issues;
+// the compiler's hazard model does not cover that, and a value it placed in
+// a dead operand register right after the MFMA was seen to corrupt the
+// product.  So no instruction of this wave issues for 16 wait states after
+// it (the scheduling barriers keep the window next to the MFMA).
+__device__ __forceinline__ void mx_mfma(f32x16& acc, const i32x8& b, const i32x8& a, int sb, int sa) {
+  acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, acc, 0, 0, 0, sb, 0, sa);
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 struct MxA {
@@ -63,7 +78,7 @@ constexpr int mx_lds_bytes() {
 }
 
 // One output tile (BM rows of one expert x BN columns).
-template <int BM, int BN, int WM, int WN, bool FC1, int STAGES>
+template <int BM, int BN, int WM, int WN, bool FC1, int STAGES, int SPREAD>
 __device__ __forceinline__ void mx_tile(const Tile& tile, char* smem, const MxA& A, const MxB& B,
                                         const MxOut& O, int N, int K) {
   constexpr int NB = FC1 ? 2 : 1;
@@ -88,6 +103,7 @@ __device__ __forceinline__ void mx_tile(const Tile& tile, char* smem, const MxA&
   const uint32_t smem_base = static_cast<uint32_t>(
       reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)smem));
   const int64_t KB = K / 32;  // scale bytes per row (row-major layout)
+  const int nk = K / kMxK;    // stages
   const int64_t b_expert = static_cast<int64_t>(tile.e) * N;
 
   // source row (clamped in range; padding rows are computed, never stored)
@@ -96,16 +112,20 @@ __device__ __forceinline__ void mx_tile(const Tile& tile, char* smem, const MxA&
     if (A.gather) ar = min(max(static_cast<int64_t>(A.gather[ar]), int64_t(0)), A.rows - 1);
     return ar;
   };
+  // A 1 KB piece covers 8 whole LDS rows, and BM and BN are multiples of 64,
+  // so whether a piece (or a wave's scale row) belongs to A, W0 or W1 is the
+  // same in every lane: the branches below are uniform.
   const uint8_t* src[LPW];
 #pragma unroll
   for (int j = 0; j < LPW; ++j) {
+    const int prow0 = (wave * LPW + j) * 8;  // first LDS row of the piece
     int row, c;
     lds_piece<64>((wave * LPW + j) * 1024 + lane * 16, row, c);
-    if (row < BM) {
+    if (prow0 < BM) {
       src[j] = A.codes + a_row(row) * K + c * 16;
     } else {
       const int br = row - BM;
-      const uint8_t* base = (NB == 2 && br >= BN) ? B.codes1 : B.codes0;
+      const uint8_t* base = (NB == 2 && prow0 - BM >= BN) ? B.codes1 : B.codes0;
       const int n = min(n0 + (br % BN), N - 1);
       src[j] = base + (b_expert + n) * K + c * 16;
     }
@@ -116,24 +136,29 @@ __device__ __forceinline__ void mx_tile(const Tile& tile, char* smem, const MxA&
   int64_t sstep;
   {
     const int r = min(wave * 64 + lane, ROWS - 1);
-    if (r < BM) {
+    if (wave * 64 < BM) {
       const int64_t ar = a_row(r);
       ssrc = A.tiled ? A.scales + ar * 4 : A.scales + ar * KB;
       sstep = A.tiled ? A.rows * 4 : 4;
     } else {
       const int br = r - BM;
-      const uint8_t* base = (NB == 2 && br >= BN) ? B.scales1 : B.scales0;
+      const uint8_t* base = (NB == 2 && wave * 64 - BM >= BN) ? B.scales1 : B.scales0;
       const int n = min(n0 + (br % BN), N - 1);
-      ssrc = base + (static_cast<int64_t>(tile.e) * (K / kMxK) * N + n) * 4;
+      ssrc = base + (static_cast<int64_t>(tile.e) * nk * N + n) * 4;
       sstep = static_cast<int64_t>(N) * 4;
     }
   }
-  auto issue = [&](int kt) {
+  // piece j < LPW of stage kt: 1 KB of codes; piece LPW: the 256-byte scale load
+  auto issue_piece = [&](int kt, int j) {
     const uint32_t dst = smem_base + static_cast<uint32_t>((kt % STAGES) * STAGE_BYTES);
-    const int64_t ko = static_cast<int64_t>(kt) * kMxK;
+    if (j < LPW)
+      dma16(src[j] + static_cast<int64_t>(kt) * kMxK, dst + (wave * LPW + j) * 1024);
+    else
+      dma4(ssrc + kt * sstep, dst + DATA + wave * 256);
+  };
+  auto issue = [&](int kt) {
 #pragma unroll
-    for (int j = 0; j < LPW; ++j) dma16(src[j] + ko, dst + (wave * LPW + j) * 1024);
-    dma4(ssrc + kt * sstep, dst + DATA + wave * 256);
+    for (int j = 0; j < LPWT; ++j) issue_piece(kt, j);
   };
 
   f32x16 acc[NB][MI][NI];
@@ -146,54 +171,109 @@ __device__ __forceinline__ void mx_tile(const Tile& tile, char* smem, const MxA&
 #pragma unroll
         for (int q = 0; q < 16; ++q) acc[b][mi][ni][q] = 0.f;
 
-  const int nk = K / kMxK;
+  // Fragments and block scales of one 64-wide k step (s = 0, 1) of a stage:
+  // the current ones and the next step's, read while the current MFMAs run.
+  i32x8 ca[MI], cb[NB][NI], na[MI], nb[NB][NI];
+  int cas[MI], cbs[NB][NI], nas[MI], nbs[NB][NI];
+  auto frag = [&](i32x8& f, int& sv, const char* st, int s, int row) {
+    const uint32_t* sc = reinterpret_cast<const uint32_t*>(st + DATA);
+    const i32x4 lo = *reinterpret_cast<const i32x4*>(st + lds_chunk_byte<64>(row, 4 * s + hi));
+    const i32x4 up = *reinterpret_cast<const i32x4*>(st + lds_chunk_byte<64>(row, 4 * s + 2 + hi));
+    f = __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7);
+    sv = static_cast<int>(sc[row] >> (8 * (2 * s + hi)));
+  };
+  auto load_step = [&](i32x8 (&af)[MI], int (&as)[MI], i32x8 (&bf)[NB][NI], int (&bs)[NB][NI],
+                       const char* st, int s) {
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) frag(af[mi], as[mi], st, s, wm * WTM + mi * 32 + l32);
+#pragma unroll
+    for (int q = 0; q < NB; ++q)
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+        frag(bf[q][ni], bs[q][ni], st, s, BM + q * BN + wn * WTN + ni * 32 + l32);
+  };
+
+  // Ring schedule (as in the bf16 GEMM): every slot holds a stage in flight
+  // or being multiplied.  During the first 64-wide step of stage kt each
+  // wave reads the rest of stage kt into registers; before the second step
+  // the workgroup waits for stage kt+1 and passes one barrier, after which
+  // stage kt's slot receives stage kt+STAGES while the second step's MFMAs
+  // run: with SPREAD its pieces are spread evenly between those MFMAs,
+  // else all are issued at the barrier.  The loop is split where the loads
+  // stop, so that each iteration is one straight block (the fences around
+  // the MFMAs only hold within a block, and the waits are constants).
+  constexpr int MPK = NB * MI * NI;  // MFMAs per 64-wide step
+  // MFMAs of the current fragments; with NEXT the next step's fragments are
+  // read from (nst, ns) first; with LOADS stage `pend` is issued.
+  auto step = [&](auto next_c, auto loads_c, const char* nst, int ns, int pend) {
+    constexpr bool NEXT = decltype(next_c)::value, LOADS = decltype(loads_c)::value;
+    if constexpr (LOADS && !SPREAD) issue(pend);
+    if constexpr (NEXT) load_step(na, nas, nb, nbs, nst, ns);
+#pragma unroll
+    for (int q = 0; q < NB; ++q)
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) {
+          mx_mfma(acc[q][mi][ni], cb[q][ni], ca[mi], cbs[q][ni], cas[mi]);
+          if constexpr (LOADS && SPREAD) {
+            const int pos = (q * MI + mi) * NI + ni;
+#pragma unroll
+            for (int j = 0; j < LPWT; ++j)
+              if (j * MPK / LPWT == pos) issue_piece(pend, j);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+    if constexpr (NEXT) {
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) {
+        ca[mi] = na[mi];
+        cas[mi] = nas[mi];
+      }
+#pragma unroll
+      for (int q = 0; q < NB; ++q)
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) {
+          cb[q][ni] = nb[q][ni];
+          cbs[q][ni] = nbs[q][ni];
+        }
+    }
+  };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  auto slot = [&](int kt) { return smem + (kt % STAGES) * STAGE_BYTES; };
+
 #pragma unroll
   for (int s = 0; s < STAGES; ++s)
     if (s < nk) issue(s);
-  for (int kt = 0; kt < nk; ++kt) {
-    wait_stage<LPWT, STAGES>(min(kt + STAGES - 1, nk - 1) - kt);
-    block_barrier();
-    const char* st = smem + (kt % STAGES) * STAGE_BYTES;
-    const uint32_t* sc = reinterpret_cast<const uint32_t*>(st + DATA);
-#pragma unroll
-    for (int s = 0; s < kMxK / 64; ++s) {
-      i32x8 af[MI], bf[NB][NI];
-      int as[MI], bs[NB][NI];
-      const int shift = 8 * (2 * s + hi);
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi) {
-        const int row = wm * WTM + mi * 32 + l32;
-        const i32x4 lo = *reinterpret_cast<const i32x4*>(st + lds_chunk_byte<64>(row, 4 * s + hi));
-        const i32x4 up = *reinterpret_cast<const i32x4*>(st + lds_chunk_byte<64>(row, 4 * s + 2 + hi));
-        af[mi] = __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7);
-        as[mi] = static_cast<int>(sc[row] >> shift);
-      }
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni) {
-          const int row = BM + nb * BN + wn * WTN + ni * 32 + l32;
-          const i32x4 lo = *reinterpret_cast<const i32x4*>(st + lds_chunk_byte<64>(row, 4 * s + hi));
-          const i32x4 up =
-              *reinterpret_cast<const i32x4*>(st + lds_chunk_byte<64>(row, 4 * s + 2 + hi));
-          bf[nb][ni] = __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7);
-          bs[nb][ni] = static_cast<int>(sc[row] >> shift);
-        }
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-          for (int ni = 0; ni < NI; ++ni)
-            acc[nb][mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                bf[nb][ni], af[mi], acc[nb][mi][ni], 0, 0, 0, bs[nb][ni], 0, as[mi]);
-    }
-    if (kt + STAGES < nk) {
-      wait_lgkm0();
-      block_barrier();  // every wave is done with this slot
-      issue(kt + STAGES);
-    }
+  wait_stage<LPWT, STAGES>(min(STAGES - 1, nk - 1));
+  block_barrier();
+  load_step(ca, cas, cb, cbs, smem, 0);
+  int kt = 0;
+  for (; kt + STAGES < nk; ++kt) {  // a stage to load after each barrier
+    step(T_{}, F_{}, slot(kt), 1, 0);
+    wait_vmcnt<(STAGES - 2) * LPWT>();  // stage kt+1 has landed
+    wait_lgkm0();
+    block_barrier();                    // and every wave is done with stage kt
+    step(T_{}, T_{}, slot(kt + 1), 0, kt + STAGES);
   }
+  for (; kt + 1 < nk; ++kt) {  // nothing left to load
+    step(T_{}, F_{}, slot(kt), 1, 0);
+    wait_vmcnt<0>();
+    wait_lgkm0();
+    block_barrier();
+    step(T_{}, F_{}, slot(kt + 1), 0, 0);
+  }
+  step(T_{}, F_{}, slot(nk - 1), 1, 0);  // last stage
+  step(F_{}, F_{}, smem, 0, 0);
+  // the accumulators are complete here: this keeps the last MFMAs (and
+  // their fences) from being sunk into the epilogue's conditional stores
+#pragma unroll
+  for (int q = 0; q < NB; ++q)
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) asm volatile("" : "+v"(acc[q][mi][ni]));
 
   // epilogue: lane holds C[m = l32][n = 8g + 4*hi + q] of each 32x32 block
 #pragma unroll
@@ -244,73 +324,62 @@ __device__ __forceinline__ void mx_tile(const Tile& tile, char* smem, const MxA&
   }
 }
 
-template <int BM, int BN, int WM, int WN, bool FC1, int STAGES>
+template <int BM_, int BN_, int WM, int WN, bool FC1, int STAGES, int SPREAD>
 struct MxBody {
+  static constexpr int BM = BM_, BN = BN_;
   static constexpr int lds = mx_lds_bytes<BM, BN, FC1, WM * WN, STAGES>();
   __device__ __forceinline__ static void run(const Tile& t, char* smem, const MxA& A, const MxB& B,
                                              const MxOut& O, int N, int K) {
-    mx_tile<BM, BN, WM, WN, FC1, STAGES>(t, smem, A, B, O, N, K);
+    mx_tile<BM, BN, WM, WN, FC1, STAGES, SPREAD>(t, smem, A, B, O, N, K);
   }
 };
 
-// Decode the tile with BMAX-row m-tiles, then run a body (ragged tails of
-// 256-row launches run the 128- or 64-row body).
-template <bool FC1, int BMAX, int BN, class Body256, class Body128, class Body64>
+// Decode this workgroup's tile (Body::BM-row m-tiles, Body::BN columns), run the body.
+template <bool FC1, class Body>
 __global__ void __launch_bounds__(512) gmm_mx_kernel(MxA A, MxB B, MxOut O,
                                                      const int32_t* __restrict__ counts, int E,
                                                      int N, int K, int64_t max_rows) {
-  constexpr int L256 = Body256::lds > Body128::lds ? Body256::lds : Body128::lds;
-  constexpr int LDS = BMAX == 256 ? (L256 > Body64::lds ? L256 : Body64::lds)
-                                 : (BMAX == 128 ? Body128::lds : Body64::lds);
   constexpr int DECODE_BYTES = (3 * kMaxExperts + 1) * 4 + 64;
-  static_assert(LDS >= DECODE_BYTES, "decode scratch aliases the stages");
-  __shared__ __attribute__((aligned(1024))) char smem[LDS];
-  const int NT = (N + BN - 1) / BN;
+  static_assert(Body::lds >= DECODE_BYTES, "decode scratch aliases the stages");
+  __shared__ __attribute__((aligned(1024))) char smem[Body::lds];
+  const int NT = (N + Body::BN - 1) / Body::BN;
   Tile tile;
   {
     int* s_toff = reinterpret_cast<int*>(smem);
     int* s_roff = s_toff + kMaxExperts + 1;
     int* s_n = s_roff + kMaxExperts;
     int64_t* s_scan = reinterpret_cast<int64_t*>(s_n + kMaxExperts + 1);
-    const bool mine = decode_tile<BMAX, 512>(counts, E, max_rows, NT, s_toff, s_roff, s_n, s_scan, tile);
+    const bool mine =
+        decode_tile<Body::BM, 512>(counts, E, max_rows, NT, s_toff, s_roff, s_n, s_scan, tile);
     __syncthreads();
-    if (!mine) return;
+    // the decode is the same in every lane: say so to the compiler, so that
+    // the tile loop runs as uniform (scalar) control flow
+    if (!__builtin_amdgcn_readfirstlane(static_cast<int>(mine))) return;
   }
+  tile.e = __builtin_amdgcn_readfirstlane(tile.e);
+  tile.n0 = __builtin_amdgcn_readfirstlane(tile.n0);
   tile.nrows = __builtin_amdgcn_readfirstlane(tile.nrows);
-  if constexpr (BMAX == 256) {
-    if (tile.nrows > 128) Body256::run(tile, smem, A, B, O, N, K);
-    else if (tile.nrows > 64) Body128::run(tile, smem, A, B, O, N, K);
-    else Body64::run(tile, smem, A, B, O, N, K);
-  } else if constexpr (BMAX == 128) {
-    Body128::run(tile, smem, A, B, O, N, K);
-  } else {
-    Body64::run(tile, smem, A, B, O, N, K);
-  }
+  tile.row0 = static_cast<int64_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(tile.row0)));
+  Body::run(tile, smem, A, B, O, N, K);
 }
 
-// Bodies (8 waves).  LDS per stage = rows * 128 + 2 KB of scales.
-using MxFc1B256 = MxBody<256, 128, 2, 4, true, 2>;
-using MxFc1B128 = MxBody<128, 128, 2, 4, true, 3>;
-using MxFc1B64 = MxBody<64, 128, 2, 4, true, 3>;
-using MxFc2B256 = MxBody<256, 256, 4, 2, false, 2>;
-using MxFc2B128w = MxBody<128, 256, 2, 4, false, 3>;
-using MxFc2B64w = MxBody<64, 256, 2, 4, false, 3>;
-using MxFc2B128 = MxBody<128, 128, 2, 4, false, 4>;
+// Bodies (8 waves, two per SIMD).  LDS per stage = rows * 128 + 2 KB of
+// scales.  Loads are spread one per MFMA where a stage's loads fit into its
+// two steps' MFMAs.  (256-row tiles need 128 accumulator registers per lane
+// and, with the fp8 fragments, spill.)
+using MxFc1B128 = MxBody<128, 128, 2, 4, true, 3, 1>;
+using MxFc1B64 = MxBody<64, 128, 2, 4, true, 3, 0>;
+using MxFc2B128w = MxBody<128, 256, 2, 4, false, 3, 1>;
+using MxFc2B128 = MxBody<128, 128, 2, 4, false, 4, 0>;
+using MxFc2B64w = MxBody<64, 256, 2, 4, false, 3, 0>;
 
-template <bool FC1, int BMAX, int BN, class B256, class B128, class B64>
+template <bool FC1, class Body>
 void launch_mx(const MxA& a, const MxB& b, const MxOut& o, const int32_t* counts, int64_t E,
                int64_t N, int64_t K, int64_t max_rows, hipStream_t s) {
-  const int64_t g = grid_for(max_rows, E, BMAX, N, BN);
-  hipLaunchKernelGGL((gmm_mx_kernel<FC1, BMAX, BN, B256, B128, B64>), dim3(static_cast<unsigned>(g)),
-                     dim3(512), 0, s, a, b, o, counts, static_cast<int>(E), static_cast<int>(N),
-                     static_cast<int>(K), max_rows);
-}
-
-int pick_bm_mx(int64_t max_rows, int64_t E) {
-  const int64_t avg = max_rows / E;
-  if (avg >= 192) return 256;
-  if (avg >= 80) return 128;
-  return 64;
+  const int64_t g = grid_for(max_rows, E, Body::BM, N, Body::BN);
+  hipLaunchKernelGGL((gmm_mx_kernel<FC1, Body>), dim3(static_cast<unsigned>(g)), dim3(512), 0, s, a,
+                     b, o, counts, static_cast<int>(E), static_cast<int>(N), static_cast<int>(K),
+                     max_rows);
 }
 
 moe_status validate_mx(const char* who, int64_t E, int64_t h, int64_t f, int64_t max_rows) {
@@ -347,13 +416,10 @@ extern "C" moe_status moe_grouped_fc1_swiglu_mxfp8(
   const MxB b{wg_codes, wg_scales, wu_codes, wu_scales};
   const MxOut o{act_codes, act_scales, nullptr, max_rows};
   const hipStream_t s = as_stream(stream);
-  const int bm = pick_bm_mx(max_rows, E);
-  if (bm == 256)
-    launch_mx<true, 256, 128, MxFc1B256, MxFc1B128, MxFc1B64>(a, b, o, tokens_per_expert, E, f, h, max_rows, s);
-  else if (bm == 128)
-    launch_mx<true, 128, 128, MxFc1B128, MxFc1B128, MxFc1B128>(a, b, o, tokens_per_expert, E, f, h, max_rows, s);
+  if (max_rows / E >= 80)
+    launch_mx<true, MxFc1B128>(a, b, o, tokens_per_expert, E, f, h, max_rows, s);
   else
-    launch_mx<true, 64, 128, MxFc1B64, MxFc1B64, MxFc1B64>(a, b, o, tokens_per_expert, E, f, h, max_rows, s);
+    launch_mx<true, MxFc1B64>(a, b, o, tokens_per_expert, E, f, h, max_rows, s);
   return check_launch("moe_grouped_fc1_swiglu_mxfp8");
 }
 
@@ -371,12 +437,12 @@ extern "C" moe_status moe_grouped_fc2_mxfp8(int64_t E, int64_t h, int64_t f, int
   const MxB b{wd_codes, wd_scales, nullptr, nullptr};
   const MxOut o{nullptr, nullptr, static_cast<uint16_t*>(expert_out), max_rows};
   const hipStream_t s = as_stream(stream);
-  const int bm = pick_bm_mx(max_rows, E);
-  if (bm == 256)
-    launch_mx<false, 256, 256, MxFc2B256, MxFc2B128w, MxFc2B64w>(a, b, o, tokens_per_expert, E, h, f, max_rows, s);
-  else if (bm == 128)
-    launch_mx<false, 128, 128, MxFc2B128, MxFc2B128, MxFc2B128>(a, b, o, tokens_per_expert, E, h, f, max_rows, s);
+  const int64_t avg = max_rows / E;
+  if (avg >= 192)
+    launch_mx<false, MxFc2B128w>(a, b, o, tokens_per_expert, E, h, f, max_rows, s);
+  else if (avg >= 80)
+    launch_mx<false, MxFc2B128>(a, b, o, tokens_per_expert, E, h, f, max_rows, s);
   else
-    launch_mx<false, 64, 256, MxFc2B64w, MxFc2B64w, MxFc2B64w>(a, b, o, tokens_per_expert, E, h, f, max_rows, s);
+    launch_mx<false, MxFc2B64w>(a, b, o, tokens_per_expert, E, h, f, max_rows, s);
   return check_launch("moe_grouped_fc2_mxfp8");
 }
