@@ -29,6 +29,8 @@
 // 16-byte fragment reads are bank-conflict free.  The weight tile feeds the
 // MFMA's first operand and the activation tile its second, so each lane
 // ends with 4 consecutive output columns of one row (8-byte bf16 stores).
+#include <type_traits>
+
 #include "gmm_sched.h"
 
 namespace moe {
@@ -82,31 +84,6 @@ __device__ __forceinline__ void mfma_step(f32x16 (&acc)[NB][MI][NI], const bf16x
       for (int ni = 0; ni < NI; ++ni)
         acc[nb][mi][ni] =
             __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[nb][ni], a[mi], acc[nb][mi][ni], 0, 0, 0);
-}
-
-// mfma_step that also issues direct loads between the MFMAs: after the
-// MFMA at position p0 + i (counted from the last barrier) piece j of the
-// pending stage is issued when p0 + i == j * SPREAD.  Callers pass p0 from
-// fully unrolled loops, so the position tests fold to constants; the
-// scheduling barrier keeps each load between its two MFMAs.
-template <int MI, int NB, int NI, int SPREAD, int LPW, class Issue>
-__device__ __forceinline__ void mfma_step_dma(f32x16 (&acc)[NB][MI][NI], const bf16x8 (&a)[MI],
-                                              const bf16x8 (&b)[NB][NI], int p0, bool pending,
-                                              const Issue& issue_piece) {
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-      for (int ni = 0; ni < NI; ++ni) {
-        acc[nb][mi][ni] =
-            __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[nb][ni], a[mi], acc[nb][mi][ni], 0, 0, 0);
-        const int pos = p0 + (nb * MI + mi) * NI + ni;
-        if (pos % SPREAD == 0 && pos / SPREAD < LPW) {
-          if (pending) issue_piece(pos / SPREAD);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
 }
 
 // LDS bytes one tile body uses.
@@ -247,56 +224,106 @@ __device__ __forceinline__ void gmm_tile(const Tile& tile, char* smem,
     // stage kt's fragments into registers (lgkmcnt 0); the workgroup waits
     // for stage kt+1 and passes a barrier, after which stage kt's slot
     // receives stage kt+STAGES and the first fragments of stage kt+1 are
-    // read while the last MFMAs of stage kt run.  With SPREAD > 0 the
-    // stage's direct loads are not issued at once after the barrier but one
-    // every SPREAD MFMAs, so that a wave stalled on a full memory queue
-    // still has MFMAs in flight.
+    // read while the last MFMAs of stage kt run.  With SPREAD > 0 the new
+    // stage's direct loads are not issued at once but one every SPREAD
+    // MFMAs (counted from the barrier, so they continue into the first
+    // steps of stage kt+1), so that a wave stalled on a full memory queue
+    // still has MFMAs in flight.  The loop is split where the loads stop,
+    // so that each iteration is straight-line code with constant waits (a
+    // branch per load would split the block and let the compiler move the
+    // MFMAs away from the loads placed between them).
     constexpr int MPK = NB * MI * NI;  // MFMAs per 16-wide step
     static_assert(SPREAD == 0 || LPW * SPREAD <= MPK * KK, "loads spread past the next barrier");
-    int pend = -1;  // stage whose loads are being spread (issued at the last barrier)
-    auto issue_piece = [&](int j) {
-      const uint32_t dst = smem_base + static_cast<uint32_t>((pend % STAGES) * STAGE_BYTES) +
+    auto piece = [&](int stage, int j) {
+      const uint32_t dst = smem_base + static_cast<uint32_t>((stage % STAGES) * STAGE_BYTES) +
                            static_cast<uint32_t>(wave * LPW * 1024 + j * 1024);
-      dma16(src[j] + static_cast<int64_t>(pend) * SBK, dst);
+      dma16(src[j] + static_cast<int64_t>(stage) * SBK, dst);
+    };
+    // one step's MFMAs; with ON, the pieces of `stage` due at MFMA
+    // positions p0 .. p0+MPK-1 (counted from the barrier) are issued between them
+    auto mfmas = [&](auto on_c, int p0, int stage) {
+      constexpr bool ON = decltype(on_c)::value;
+#pragma unroll
+      for (int q = 0; q < NB; ++q)
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+          for (int ni = 0; ni < NI; ++ni) {
+            acc[q][mi][ni] =
+                __builtin_amdgcn_mfma_f32_32x32x16_bf16(cb[q][ni], ca[mi], acc[q][mi][ni], 0, 0, 0);
+            if constexpr (ON) {
+              const int pos = p0 + (q * MI + mi) * NI + ni;
+              if (pos % SPREAD == 0 && pos / SPREAD < LPW) {
+                piece(stage, pos / SPREAD);
+                __builtin_amdgcn_sched_barrier(0);
+              }
+            }
+          }
+    };
+    auto advance = [&]() {
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) ca[mi] = na[mi];
+#pragma unroll
+      for (int q = 0; q < NB; ++q)
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) cb[q][ni] = nb[q][ni];
+    };
+    using T_ = std::true_type;
+    using F_ = std::false_type;
+    // Stage kt.  PREV: stage kt-1+STAGES is being spread (issued from the
+    // previous barrier on); CUR: stage kt+STAGES is issued at this one;
+    // LAST: the final stage (no barrier).
+    auto iter = [&](auto prev_c, auto cur_c, auto last_c, int kt) {
+      constexpr bool PREV = decltype(prev_c)::value && SPREAD > 0;
+      constexpr bool CUR = decltype(cur_c)::value, LAST = decltype(last_c)::value;
+      const char* st = smem + (kt % STAGES) * STAGE_BYTES;
+#pragma unroll
+      for (int kk = 0; kk + 1 < KK; ++kk) {
+        __builtin_amdgcn_sched_barrier(0);  // steps stay in order (bounded live fragments)
+        load_frags<MI, NB, NI, BM, BN, SBK, WTM, WTN>(na, nb, st, kk + 1, wm, wn, l32, hi);
+        mfmas(std::integral_constant<bool, PREV>{}, (kk + 1) * MPK, kt - 1 + STAGES);
+        advance();
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (!LAST) {
+        // stage kt+1 has landed: at most the stages after it are in flight
+        if constexpr (decltype(prev_c)::value || CUR) wait_vmcnt<(STAGES - 2) * LPW>();
+        else wait_vmcnt<0>();
+        wait_lgkm0();
+        block_barrier();
+        if constexpr (CUR && SPREAD == 0) issue(kt + STAGES);
+        load_frags<MI, NB, NI, BM, BN, SBK, WTM, WTN>(
+            na, nb, smem + ((kt + 1) % STAGES) * STAGE_BYTES, 0, wm, wn, l32, hi);
+        mfmas(std::integral_constant<bool, CUR && (SPREAD > 0)>{}, 0, kt + STAGES);
+        advance();
+      } else {
+        mfmas(F_{}, 0, 0);
+      }
     };
     wait_stage<LPW, STAGES>(min(STAGES - 1, nk - 1));
     block_barrier();
     load_frags<MI, NB, NI, BM, BN, SBK, WTM, WTN>(ca, cb, smem, 0, wm, wn, l32, hi);
-    for (int kt = 0; kt < nk; ++kt) {
-      const char* st = smem + (kt % STAGES) * STAGE_BYTES;
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        if (kk + 1 < KK) {
-          load_frags<MI, NB, NI, BM, BN, SBK, WTM, WTN>(na, nb, st, kk + 1, wm, wn, l32, hi);
-        } else if (kt + 1 < nk) {
-          const int last = min(kt + STAGES - 1, nk - 1);  // newest stage issued so far
-          wait_stage<LPW, STAGES>(last - (kt + 1));
-          wait_lgkm0();
-          block_barrier();
-          pend = kt + STAGES < nk ? kt + STAGES : -1;
-          if constexpr (SPREAD == 0) {
-            if (pend >= 0) issue(pend);
-          }
-          load_frags<MI, NB, NI, BM, BN, SBK, WTM, WTN>(
-              na, nb, smem + ((kt + 1) % STAGES) * STAGE_BYTES, 0, wm, wn, l32, hi);
-        }
-        if constexpr (SPREAD == 0) {
-          mfma_step<MI, NB, NI>(acc, ca, cb);
-        } else {
-          // MFMA positions since the last barrier: the last step of a stage
-          // follows it directly; steps 0..KK-2 continue from the previous
-          // iteration's barrier.
-          mfma_step_dma<MI, NB, NI, SPREAD, LPW>(acc, ca, cb, kk + 1 == KK ? 0 : (kk + 1) * MPK,
-                                                 pend >= 0, issue_piece);
-        }
-#pragma unroll
-        for (int mi = 0; mi < MI; ++mi) ca[mi] = na[mi];
-#pragma unroll
-        for (int q = 0; q < NB; ++q)
-#pragma unroll
-          for (int ni = 0; ni < NI; ++ni) cb[q][ni] = nb[q][ni];
-      }
+    int kt = 0;
+    if (nk > 1) {
+      if (STAGES < nk) iter(F_{}, T_{}, F_{}, 0);
+      else iter(F_{}, F_{}, F_{}, 0);
+      kt = 1;
     }
+    for (; kt + STAGES < nk; ++kt) iter(T_{}, T_{}, F_{}, kt);
+    if (kt >= 1 && kt + STAGES == nk && kt + 1 < nk) {  // its predecessor issued the last stage
+      iter(T_{}, F_{}, F_{}, kt);
+      ++kt;
+    }
+    for (; kt + 1 < nk; ++kt) iter(F_{}, F_{}, F_{}, kt);
+    iter(F_{}, F_{}, T_{}, nk - 1);
+    // the accumulators are complete here: keep the last MFMAs out of the
+    // epilogue's conditional blocks
+#pragma unroll
+    for (int q = 0; q < NB; ++q)
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) asm volatile("" : "+v"(acc[q][mi][ni]));
   } else if constexpr (SCHED == kSchedDeep) {
     // Memory-depth schedule (weight-streaming bodies): at the top of
     // iteration kt a barrier frees stage kt-1's slot, stage kt+STAGES-1 is
