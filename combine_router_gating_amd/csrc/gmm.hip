@@ -38,9 +38,6 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-// Native 16-byte vector (HIP's uint4 is a struct, which defeats scalar
-// replacement of register arrays).
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr int BK = 64;
@@ -49,9 +46,7 @@ constexpr int BK = 64;
 // ----------------------------------------------------------------- bf16 MFMA
 // Pipeline schedules of a tile body (see gmm_tile).
 constexpr int kSchedCompute = 0;
-constexpr int kSchedDeep = 1;
-constexpr int kSchedReg = 2;
-constexpr int kSchedRing = 3;
+constexpr int kSchedRing = 1;
 
 // MFMA operand fragments of one 16-wide k step for one wave: MI activation
 // blocks and NB x NI weight blocks of 32 rows, 8 consecutive k per lane.
@@ -112,8 +107,9 @@ __device__ __forceinline__ void gmm_tile(const Tile& tile, char* smem,
   static_assert(MI >= 1 && NI >= 1, "wave tile must be at least 32x32");
   static_assert(STAGE_BYTES % (NW * 1024) == 0, "whole direct loads per wave");
   static_assert(SBK == 32 || SBK == 64 || SBK == 128 || SBK == 256, "k slab per stage");
-  static_assert((SCHED == kSchedReg && STAGES == 2) || (SCHED == kSchedRing && STAGES >= 2 && STAGES <= 6) ||
-                    (SCHED != kSchedReg && SCHED != kSchedRing && STAGES >= 3 && STAGES <= 6),
+  static_assert(SCHED == kSchedCompute || SCHED == kSchedRing, "schedule");
+  static_assert((SCHED == kSchedRing && STAGES >= 2 && STAGES <= 6) ||
+                    (SCHED == kSchedCompute && STAGES >= 3 && STAGES <= 6),
                 "pipeline depth");
 
   const int n0 = tile.n0 * BN;
@@ -171,54 +167,12 @@ __device__ __forceinline__ void gmm_tile(const Tile& tile, char* smem,
 #pragma unroll
     for (int s = 0; s < STAGES; ++s)
       if (s < nk) issue(s);
-  } else if constexpr (SCHED != kSchedReg) {
+  } else {
 #pragma unroll
     for (int s = 0; s < STAGES - 1; ++s)
       if (s < nk) issue(s);
   }
-  if constexpr (SCHED == kSchedReg) {
-    // Register-staged schedule: two LDS slots; stage kt+1 waits in registers
-    // (ordinary 16-byte global loads) while stage kt is multiplied, is
-    // written to LDS after it, and stage kt+2's loads are issued behind the
-    // barrier.
-    u32x4 rg[LPW];
-    const int piece = wave * LPW * 1024 + lane * 16;
-    auto gload = [&](int kt) {
-      const int64_t ko = static_cast<int64_t>(kt) * SBK;
-#pragma unroll
-      for (int j = 0; j < LPW; ++j) rg[j] = *reinterpret_cast<const u32x4*>(src[j] + ko);
-    };
-    auto sstore = [&](int slot) {
-      char* d = smem + slot * STAGE_BYTES + piece;
-#pragma unroll
-      for (int j = 0; j < LPW; ++j) *reinterpret_cast<u32x4*>(d + j * 1024) = rg[j];
-    };
-    gload(0);
-    sstore(0);
-    if (nk > 1) gload(1);
-    wait_lgkm0();
-    block_barrier();
-    for (int kt = 0; kt < nk; ++kt) {
-      const char* st = smem + (kt & 1) * STAGE_BYTES;
-      load_frags<MI, NB, NI, BM, BN, SBK, WTM, WTN>(ca, cb, st, 0, wm, wn, l32, hi);
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        if (kk + 1 < KK)
-          load_frags<MI, NB, NI, BM, BN, SBK, WTM, WTN>(na, nb, st, kk + 1, wm, wn, l32, hi);
-        mfma_step<MI, NB, NI>(acc, ca, cb);
-#pragma unroll
-        for (int mi = 0; mi < MI; ++mi) ca[mi] = na[mi];
-#pragma unroll
-        for (int q = 0; q < NB; ++q)
-#pragma unroll
-          for (int ni = 0; ni < NI; ++ni) cb[q][ni] = nb[q][ni];
-      }
-      if (kt + 1 < nk) sstore((kt + 1) & 1);
-      wait_lgkm0();
-      block_barrier();
-      if (kt + 2 < nk) gload(kt + 2);
-    }
-  } else if constexpr (SCHED == kSchedRing) {
+  if constexpr (SCHED == kSchedRing) {
     // Ring schedule: every slot holds a stage in flight or being multiplied.
     // Before the last 16-wide step of stage kt each wave has read all of
     // stage kt's fragments into registers (lgkmcnt 0); the workgroup waits
@@ -324,32 +278,6 @@ __device__ __forceinline__ void gmm_tile(const Tile& tile, char* smem,
       for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni) asm volatile("" : "+v"(acc[q][mi][ni]));
-  } else if constexpr (SCHED == kSchedDeep) {
-    // Memory-depth schedule (weight-streaming bodies): at the top of
-    // iteration kt a barrier frees stage kt-1's slot, stage kt+STAGES-1 is
-    // issued into it, and only stage kt is waited for, so STAGES-1 stages
-    // stay in flight while stage kt is multiplied.  Fragments of step kk+1
-    // are read while the MFMAs of step kk run.
-    for (int kt = 0; kt < nk; ++kt) {
-      block_barrier();
-      if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1);
-      wait_stage<LPW, STAGES>(min(kt + STAGES - 1, nk - 1) - kt);
-      block_barrier();
-      const char* st = smem + (kt % STAGES) * STAGE_BYTES;
-      load_frags<MI, NB, NI, BM, BN, SBK, WTM, WTN>(ca, cb, st, 0, wm, wn, l32, hi);
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        if (kk + 1 < KK)
-          load_frags<MI, NB, NI, BM, BN, SBK, WTM, WTN>(na, nb, st, kk + 1, wm, wn, l32, hi);
-        mfma_step<MI, NB, NI>(acc, ca, cb);
-#pragma unroll
-        for (int mi = 0; mi < MI; ++mi) ca[mi] = na[mi];
-#pragma unroll
-        for (int q = 0; q < NB; ++q)
-#pragma unroll
-          for (int ni = 0; ni < NI; ++ni) cb[q][ni] = nb[q][ni];
-      }
-    }
   } else {
     // Compute schedule (MFMA-bound bodies): stages kt+1 .. kt+STAGES-2 are
     // in flight while stage kt is multiplied; within a stage the fragments
