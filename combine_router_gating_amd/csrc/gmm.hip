@@ -81,6 +81,38 @@ __device__ __forceinline__ void mfma_step(f32x16 (&acc)[NB][MI][NI], const bf16x
             __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[nb][ni], a[mi], acc[nb][mi][ni], 0, 0, 0);
 }
 
+// Epilogue: lane holds C[m = l32][n = 8*g + 4*hi + q] of each 32x32 block;
+// FC1 applies silu(gate) * up.  Rows >= nrows and columns >= N are not stored.
+template <int MI, int NB, int NI, int WTM, int WTN, bool FC1>
+__device__ __forceinline__ void store_tile(const f32x16 (&acc)[NB][MI][NI], uint16_t* __restrict__ C,
+                                           int64_t row0, int nrows, int n0, int N, int wm, int wn,
+                                           int l32, int hi) {
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi) {
+    const int ml = wm * WTM + mi * 32 + l32;
+    if (ml >= nrows) continue;
+    uint16_t* crow = C + (row0 + ml) * static_cast<int64_t>(N);
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int n = n0 + wn * WTN + ni * 32 + g * 8 + hi * 4;
+        if (n >= N) continue;
+        uint16_t o[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float v = FC1 ? silu_mul(acc[0][mi][ni][g * 4 + q], acc[NB - 1][mi][ni][g * 4 + q])
+                              : acc[0][mi][ni][g * 4 + q];
+          o[q] = f32_to_bf16_bits(v);
+        }
+        uint2 pk;
+        pk.x = static_cast<uint32_t>(o[0]) | (static_cast<uint32_t>(o[1]) << 16);
+        pk.y = static_cast<uint32_t>(o[2]) | (static_cast<uint32_t>(o[3]) << 16);
+        *reinterpret_cast<uint2*>(crow + n) = pk;
+      }
+  }
+}
+
 // LDS bytes one tile body uses.
 template <int BM, int BN, bool FC1, int STAGES, int SBK>
 constexpr int body_lds_bytes() {
@@ -314,31 +346,7 @@ __device__ __forceinline__ void gmm_tile(const Tile& tile, char* smem,
     }
   }
 
-  // epilogue: lane holds C[m = l32][n = 8*g + 4*hi + q] of each 32x32 block
-#pragma unroll
-  for (int mi = 0; mi < MI; ++mi) {
-    const int ml = wm * WTM + mi * 32 + l32;
-    if (ml >= tile.nrows) continue;
-    uint16_t* crow = C + (tile.row0 + ml) * static_cast<int64_t>(N);
-#pragma unroll
-    for (int ni = 0; ni < NI; ++ni)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int n = n0 + wn * WTN + ni * 32 + g * 8 + hi * 4;
-        if (n >= N) continue;
-        uint16_t o[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float v = FC1 ? silu_mul(acc[0][mi][ni][g * 4 + q], acc[NB - 1][mi][ni][g * 4 + q])
-                              : acc[0][mi][ni][g * 4 + q];
-          o[q] = f32_to_bf16_bits(v);
-        }
-        uint2 pk;
-        pk.x = static_cast<uint32_t>(o[0]) | (static_cast<uint32_t>(o[1]) << 16);
-        pk.y = static_cast<uint32_t>(o[2]) | (static_cast<uint32_t>(o[3]) << 16);
-        *reinterpret_cast<uint2*>(crow + n) = pk;
-      }
-  }
+  store_tile<MI, NB, NI, WTM, WTN, FC1>(acc, C, tile.row0, tile.nrows, n0, N, wm, wn, l32, hi);
 }
 
 

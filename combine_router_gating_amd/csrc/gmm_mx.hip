@@ -31,14 +31,6 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kMxK = 128;  // k per stage: 128 E4M3 bytes per row, 4 scale bytes
 
-// Direct 4-byte global -> LDS load: lane i writes LDS bytes [base + 4 i, +4).
-__device__ __forceinline__ void dma4(const void* gptr, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
-               :
-               : "v"(gptr), "s"(__builtin_amdgcn_readfirstlane(lds_base))
-               : "memory");
-}
-
 // acc += (b with scale sb) x (a with scale sa), fenced.  The scaled fp8
 // MFMA reads its 8-register operands over several cycles after it issues;
 // the compiler's hazard model does not cover that, and a value it placed in

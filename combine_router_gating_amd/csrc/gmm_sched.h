@@ -16,10 +16,13 @@ struct Tile {
   int n0;      // first output column
 };
 
-// Decode this workgroup's tile.  s_toff/s_roff/s_n: LDS arrays of E+1 / E+1 / E.
+// Scan the per-expert row counts into LDS: s_roff[e] = first row of expert
+// e, s_n[e] = its rows, s_toff[e] = its first m-tile (s_toff[E] = all m-tiles).
+// Counts are clamped so that the rows stay within max_rows.  Returns the
+// number of m-tiles; all threads of the workgroup take part.
 template <int BM, int NTHREADS = kGemmThreads>
-__device__ bool decode_tile(const int32_t* __restrict__ counts, int E, int64_t max_rows, int NT,
-                            int* s_toff, int* s_roff, int* s_n, int64_t* scratch, Tile& tile) {
+__device__ int64_t decode_counts(const int32_t* __restrict__ counts, int E, int64_t max_rows,
+                                 int* s_toff, int* s_roff, int* s_n, int64_t* scratch) {
   constexpr int PER = kMaxExperts / NTHREADS;  // experts per thread
   const int tid = threadIdx.x;
   int64_t c[PER];
@@ -60,14 +63,14 @@ __device__ bool decode_tile(const int32_t* __restrict__ counts, int E, int64_t m
   }
   if (tid == 0) s_toff[E] = static_cast<int>(total_tiles);
   __syncthreads();
+  return total_tiles;
+}
 
-  const int64_t total = total_tiles * NT;
-  const int64_t per = (total + 7) / 8;
-  const int64_t bid = blockIdx.x;
-  const int64_t slot = bid / 8;
-  if (slot >= per) return false;
-  const int64_t L = (bid % 8) * per + slot;
-  if (L >= total) return false;
+// Logical tile L (expert -> n-tile -> m-tile order, so the m-tiles sharing a
+// weight slab are adjacent) of the decoded counts; NT n-tiles per expert.
+template <int BM>
+__device__ Tile tile_at(int64_t L, int NT, int E, const int* s_toff, const int* s_roff,
+                        const int* s_n) {
   // largest e with s_toff[e] * NT <= L (experts without tiles are skipped)
   int lo = 0, hi = E;  // invariant: s_toff[lo]*NT <= L < s_toff[hi]*NT
   while (hi - lo > 1) {
@@ -79,10 +82,35 @@ __device__ bool decode_tile(const int32_t* __restrict__ counts, int E, int64_t m
   const int64_t r = L - static_cast<int64_t>(s_toff[e]) * NT;
   const int nt = static_cast<int>(r / mt);
   const int mtile = static_cast<int>(r % mt);
+  Tile tile;
   tile.e = e;
   tile.row0 = s_roff[e] + static_cast<int64_t>(mtile) * BM;
   tile.nrows = min(BM, s_n[e] - mtile * BM);
   tile.n0 = nt;
+  return tile;
+}
+
+// Logical tiles are spread so that each XCD (workgroup id mod 8) runs a
+// contiguous range of them (the weight slabs its CUs share stay in its L2):
+// workgroup b's k-th tile (k = 0 for one tile per workgroup) is
+// xcd_tile(b + k * grid, total).  Returns -1 when there is none.
+__device__ __forceinline__ int64_t xcd_tile(int64_t bid, int64_t total) {
+  const int64_t per = (total + 7) / 8;
+  const int64_t slot = bid / 8;
+  if (slot >= per) return -1;
+  const int64_t L = (bid % 8) * per + slot;
+  return L < total ? L : -1;
+}
+
+// Decode this workgroup's tile.  s_toff/s_roff/s_n: LDS arrays of E+1 / E+1 / E.
+template <int BM, int NTHREADS = kGemmThreads>
+__device__ bool decode_tile(const int32_t* __restrict__ counts, int E, int64_t max_rows, int NT,
+                            int* s_toff, int* s_roff, int* s_n, int64_t* scratch, Tile& tile) {
+  const int64_t total_tiles =
+      decode_counts<BM, NTHREADS>(counts, E, max_rows, s_toff, s_roff, s_n, scratch);
+  const int64_t L = xcd_tile(blockIdx.x, total_tiles * NT);
+  if (L < 0) return false;
+  tile = tile_at<BM>(L, NT, E, s_toff, s_roff, s_n);
   return true;
 }
 

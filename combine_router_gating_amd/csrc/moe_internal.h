@@ -137,6 +137,14 @@ __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
                : "memory");
 }
 
+// Direct 4-byte global -> LDS load: lane i writes LDS bytes [base + 4 i, +4).
+__device__ __forceinline__ void dma4(const void* gptr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :
+               : "v"(gptr), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "memory");
+}
+
 // Wait until at most n of this wave's vector-memory loads are outstanding.
 template <int n>
 __device__ __forceinline__ void wait_vmcnt() {
