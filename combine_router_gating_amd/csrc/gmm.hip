@@ -539,7 +539,7 @@ using Fc1Stream128 = Body<128, 128, 2, 4, true, 3, 64, kSchedRing, 2>;
 using Fc2B256 = Body<256, 256, 4, 2, false, 2, 64, kSchedRing, 2>;
 using Fc2B128 = Body<128, 256, 2, 4, false, 3, 64, kSchedRing, 2>;
 using Fc2B64 = Body<64, 256, 2, 4, false, 4, 64>;
-using Fc2Stream128 = Body<128, 128, 2, 4, false, 4, 64>;
+using Fc2Stream128 = Body<128, 128, 2, 4, false, 4, 64, kSchedRing, 1>;
 
 template <bool FC1>
 void launch_gemm(int32_t dtype, const AOperand& A, const void* B0, const void* B1, void* C,
