@@ -535,11 +535,10 @@ int pick_bm(int64_t max_rows, int64_t E) {
 using Fc1B256 = Body<256, 128, 2, 4, true, 2, 64, kSchedRing, 2>;
 using Fc1B128 = Body<128, 128, 2, 4, true, 3, 64, kSchedRing, 2>;
 using Fc1B64 = Body<64, 128, 2, 4, true, 4, 64>;
-using Fc1Stream128 = Body<128, 128, 2, 4, true, 3, 64, kSchedRing, 2>;
 using Fc2B256 = Body<256, 256, 4, 2, false, 2, 64, kSchedRing, 2>;
 using Fc2B128 = Body<128, 256, 2, 4, false, 3, 64, kSchedRing, 2>;
 using Fc2B64 = Body<64, 256, 2, 4, false, 4, 64>;
-using Fc2Stream128 = Body<128, 128, 2, 4, false, 4, 64, kSchedRing, 1>;
+using Fc2B128n = Body<128, 128, 2, 4, false, 4, 64, kSchedRing, 1>;  // 128-row launches
 
 template <bool FC1>
 void launch_gemm(int32_t dtype, const AOperand& A, const void* B0, const void* B1, void* C,
@@ -554,14 +553,14 @@ void launch_gemm(int32_t dtype, const AOperand& A, const void* B0, const void* B
     if (bm == 256)
       launch_bf16<true, 256, 128, 8, Fc1B256, Fc1B128, Fc1B64>(A, B0, B1, C, counts, E, N, K, max_rows, s);
     else if (bm == 128)
-      launch_bf16<true, 128, 128, 8, Fc1Stream128, Fc1Stream128, Fc1Stream128>(A, B0, B1, C, counts, E, N, K, max_rows, s);
+      launch_bf16<true, 128, 128, 8, Fc1B128, Fc1B128, Fc1B128>(A, B0, B1, C, counts, E, N, K, max_rows, s);
     else
       launch_bf16<true, 64, 128, 8, Fc1B64, Fc1B64, Fc1B64>(A, B0, B1, C, counts, E, N, K, max_rows, s);
   } else {
     if (bm == 256)
       launch_bf16<false, 256, 256, 8, Fc2B256, Fc2B128, Fc2B64>(A, B0, B1, C, counts, E, N, K, max_rows, s);
     else if (bm == 128)
-      launch_bf16<false, 128, 128, 8, Fc2Stream128, Fc2Stream128, Fc2Stream128>(A, B0, B1, C, counts, E, N, K, max_rows, s);
+      launch_bf16<false, 128, 128, 8, Fc2B128n, Fc2B128n, Fc2B128n>(A, B0, B1, C, counts, E, N, K, max_rows, s);
     else
       launch_bf16<false, 64, 256, 8, Fc2B64, Fc2B64, Fc2B64>(A, B0, B1, C, counts, E, N, K, max_rows, s);
   }
