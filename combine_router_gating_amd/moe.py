@@ -314,9 +314,16 @@ def moe_grouped_fc1_swiglu_mxfp8(x_codes, x_scales, sorted_token, tokens_per_exp
         _need(sc, name + " scales", torch.uint8, (E, h // 128, f, 4))
     if sorted_token is not None:
         _need(sorted_token, "sorted_token", torch.int32)
+        if sorted_token.numel() < max_rows:
+            raise ValueError("sorted_token needs max_rows entries")
+    elif T < max_rows:
+        raise ValueError("without sorted_token, x holds the GEMM rows: it needs max_rows rows")
     if act is None:
         act = (torch.empty((max_rows, f), dtype=torch.uint8, device=x_codes.device),
                torch.empty((f // 128, max_rows, 4), dtype=torch.uint8, device=x_codes.device))
+    else:
+        _need(act[0], "act codes", torch.uint8, (max_rows, f))
+        _need(act[1], "act scales", torch.uint8, (f // 128, max_rows, 4))
     st = _lib.load().moe_grouped_fc1_swiglu_mxfp8(
         E, h, f, max_rows, T, _ptr(x_codes), _ptr(x_scales), _ptr(sorted_token),
         _ptr(tokens_per_expert), _ptr(wg[0]), _ptr(wg[1]), _ptr(wu[0]), _ptr(wu[1]), _ptr(act[0]),

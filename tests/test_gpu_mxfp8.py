@@ -208,3 +208,80 @@ def test_layer_mxfp8_against_the_oracle(overlap):
     o2 = plain.forward()
     torch.cuda.synchronize()
     assert torch.equal(out, o2)
+
+
+def test_layer_mxfp8_graph_capture_replays():
+    """The MXFP8 forward (x quantisation, router, permute, MXFP8 GEMMs,
+    shared expert on a second stream, combine) captures into a graph; replays
+    on new inputs equal the eager forward bit for bit."""
+    import datagen
+    from combine_router_gating_amd.layer import MoELayerForward
+    cfg = datagen.MoEConfig("mx-graph", T=512, h=256, E=16, K=2, f=256, dtype="bf16", shared_f=128)
+    inp = datagen.make_inputs(cfg, seed=5, device=DEV)
+    layer = MoELayerForward(inp, K=cfg.K, overlap_shared=True, precision="mxfp8")
+    layer.forward()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        out = layer.forward()
+    plain = MoELayerForward(inp, K=cfg.K, precision="mxfp8")
+    for seed in (6, 7, 8):
+        new = datagen.make_inputs(cfg, seed=seed, device=DEV, with_experts=False)
+        inp["x"].copy_(new["x"])
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ref = plain.forward()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), f"replay with seed {seed}"
+
+
+def test_mxfp8_gemm_edge_cases():
+    """One row in one expert of three, the smallest sizes (h = f = 128), and
+    nothing to do (max_rows = 0) all behave."""
+    rng = np.random.default_rng(11)
+    E, h, f = 3, 128, 128
+    counts = [0, 1, 0]
+    x = torch.from_numpy(rng.standard_normal((1, h))).to(torch.bfloat16).to(DEV)
+    xc, xs = moe.moe_mxfp8_quantize(x)
+    wg, wu, wd = (_weights(rng, E, n, k, 0.1) for n, k in ((f, h), (f, h), (h, f)))
+    cnt = torch.tensor(counts, dtype=torch.int32, device=DEV)
+    ac, asc = moe.moe_grouped_fc1_swiglu_mxfp8(xc, xs, None, cnt, wg, wu, 1)
+    y = moe.moe_grouped_fc2_mxfp8(ac, asc, cnt, wd)
+    torch.cuda.synchronize()
+    xq = mx.mx_dequantize(_np(xc), _np(xs))
+    g, u = xq @ _dq(*wg)[1].T, xq @ _dq(*wu)[1].T
+    act = mx.mx_dequantize(_np(ac), untile(asc))
+    exact = g / (1 + np.exp(-g)) * u
+    assert np.abs(act - exact).max() <= 0.07 * np.abs(exact).max() + 1e-6
+    assert_close(_np(y.float()), act @ _dq(*wd)[1].T, "bf16", "y")
+    import ctypes
+    lib = moe.load()
+    q = ctypes.c_void_p(16)
+    assert lib.moe_grouped_fc1_swiglu_mxfp8(E, h, f, 0, 1, q, q, None, q, q, q, q, q, q, q, None) == 0
+    assert lib.moe_grouped_fc2_mxfp8(E, h, f, 0, q, q, q, q, q, q, None) == 0
+
+
+def test_mxfp8_gemm_counts_past_max_rows_stay_in_bounds():
+    """tokens_per_expert claiming more rows than max_rows: the GEMMs clamp to
+    max_rows and write nothing past it (checked with guard rows)."""
+    rng = np.random.default_rng(12)
+    E, h, f, R = 4, 128, 256, 200
+    x = torch.from_numpy(rng.standard_normal((R, h))).to(torch.bfloat16).to(DEV)
+    xc, xs = moe.moe_mxfp8_quantize(x)
+    wg, wu, wd = (_weights(rng, E, n, k, 0.05) for n, k in ((f, h), (f, h), (h, f)))
+    cnt = torch.tensor([100, 90, 80, 70], dtype=torch.int32, device=DEV)  # 340 > R
+    guard = 64
+    act_c = torch.full((R + guard, f), 0x5a, dtype=torch.uint8, device=DEV)
+    act_s = torch.full((f // 128, R, 4), 0x5a, dtype=torch.uint8, device=DEV)
+    moe.moe_grouped_fc1_swiglu_mxfp8(xc, xs, None, cnt, wg, wu, R, act=(act_c[:R], act_s))
+    y = torch.full((R + guard, h), 7.0, dtype=torch.bfloat16, device=DEV)
+    import ctypes
+    p = lambda t: ctypes.c_void_p(t.data_ptr())
+    st = moe.load().moe_grouped_fc2_mxfp8(E, h, f, R, p(act_c), p(act_s), p(cnt), p(wd[0]), p(wd[1]),
+                                         p(y), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert st == 0
+    torch.cuda.synchronize()
+    assert (act_c[R:] == 0x5a).all()
+    assert (y[R:] == 7.0).all()
+    assert torch.isfinite(y[:R].float()).all()
