@@ -121,6 +121,35 @@ def test_permute_combine_mlp_reject_bad_sizes():
     assert st == _lib.MOE_ERR_ARG  # NULL counts
 
 
+def test_mxfp8_entry_points_reject_bad_sizes():
+    p = ctypes.c_void_p(16)
+    st, _ = _status("moe_mxfp8_quantize", 4, 48, 0, _lib.MOE_BF16, p, p, p, None)
+    assert st == _lib.MOE_ERR_UNSUPPORTED  # cols % 32
+    st, _ = _status("moe_mxfp8_quantize", 4, 96, 2, _lib.MOE_BF16, p, p, p, None)
+    assert st == _lib.MOE_ERR_UNSUPPORTED  # k-tiled: cols % 128
+    st, _ = _status("moe_mxfp8_quantize", 6, 128, 4, _lib.MOE_BF16, p, p, p, None)
+    assert st == _lib.MOE_ERR_UNSUPPORTED  # k-tiled: rows % tile_rows
+    st, _ = _status("moe_mxfp8_quantize", 4, 128, -1, _lib.MOE_BF16, p, p, p, None)
+    assert st == _lib.MOE_ERR_ARG
+    st, _ = _status("moe_mxfp8_quantize", 4, 128, 0, 7, p, p, p, None)
+    assert st == _lib.MOE_ERR_ARG  # dtype
+    st, _ = _status("moe_mxfp8_quantize", 4, 128, 0, _lib.MOE_BF16, None, p, p, None)
+    assert st == _lib.MOE_ERR_ARG  # NULL source
+    st, msg = _status("moe_grouped_fc1_swiglu_mxfp8", 4, 192, 256, 8, 8, p, p, None, p, p, p, p, p,
+                      p, p, None)
+    assert st == _lib.MOE_ERR_UNSUPPORTED and "multiples of 128" in msg
+    st, _ = _status("moe_grouped_fc1_swiglu_mxfp8", 0, 128, 128, 8, 8, p, p, None, p, p, p, p, p,
+                    p, p, None)
+    assert st == _lib.MOE_ERR_ARG  # E
+    st, _ = _status("moe_grouped_fc1_swiglu_mxfp8", 4, 128, 128, 8, 8, p, p, None, None, p, p, p, p,
+                    p, p, None)
+    assert st == _lib.MOE_ERR_ARG  # NULL counts
+    st, _ = _status("moe_grouped_fc2_mxfp8", 4, 128, 320, 8, p, p, p, p, p, p, None)
+    assert st == _lib.MOE_ERR_UNSUPPORTED  # f % 128
+    st, _ = _status("moe_grouped_fc2_mxfp8", 4, 128, 128, 8, p, p, p, p, p, None, None)
+    assert st == _lib.MOE_ERR_ARG  # NULL output
+
+
 def test_wrapper_rejects_cpu_tensors():
     x = torch.zeros(4, 8)
     with pytest.raises(ValueError):
