@@ -285,3 +285,91 @@ def test_mxfp8_gemm_counts_past_max_rows_stay_in_bounds():
     assert (act_c[R:] == 0x5a).all()
     assert (y[R:] == 7.0).all()
     assert torch.isfinite(y[:R].float()).all()
+
+
+def _act_bound(act_exact, sens, scale_bytes):
+    """Allowed |dq(act) - act_exact|: half an E4M3 step under the block scale
+    (or the saturation error) plus the MFMA accumulation bound."""
+    EPS = 2.0 ** -12
+    X = np.repeat(np.ldexp(1.0, scale_bytes.astype(int) - 127), 32, axis=-1)
+    a = np.abs(act_exact) / X
+    step = np.ldexp(1.0, np.floor(np.log2(np.maximum(a, 2.0 ** -6))).astype(int) - 3) * X
+    rounding = np.where(a > 448, np.abs(act_exact) - 448 * X, 0.5 * step)
+    return rounding + EPS * sens + step * 1e-9
+
+
+@pytest.mark.parametrize("name,n_tok", [("switch", 6), ("dsv3", 2)])
+def test_layer_mxfp8_full_size_sampled(name, n_tok):
+    """The MXFP8 layer at full size, in the configuration the bench times
+    (gathering FC1, overlapped shared expert): routing bit-exact on the
+    GPU's logits; x quantisation bit-exact; sampled act rows within the
+    accumulation bound of the exact SwiGLU of the GPU's MXFP8 operands;
+    those rows' expert outputs and sampled tokens' outputs within the bf16
+    tolerance of the oracle run on the GPU's act codes."""
+    import datagen
+    import oracle
+    from combine_router_gating_amd.layer import MoELayerForward
+    from gpu_helpers import f64, routing_ref
+    cfg = datagen.CONFIGS[name]
+    log(f"mxfp8 layer full size: {cfg}")
+    inp = datagen.make_inputs(cfg, seed=0, device=DEV)
+    layer = MoELayerForward(inp, K=cfg.K, score=cfg.score, pre_softmax=cfg.pre_softmax,
+                            capacity_factor=cfg.capacity_factor, min_capacity=cfg.min_capacity,
+                            gather=True, overlap_shared=True, precision="mxfp8")
+    out = layer.forward()
+    torch.cuda.synchronize()
+    eb = inp["expert_bias"].cpu().numpy() if "expert_bias" in inp else None
+    ref = routing_ref(cfg, layer.logits.cpu().numpy(), eb)
+    np.testing.assert_array_equal(_np(layer.routing_map), ref["routing_map"])
+    xc, xs = mx.mx_quantize(f64(inp["x"]))
+    np.testing.assert_array_equal(_np(layer.xq[0]), xc)
+    np.testing.assert_array_equal(_np(layer.xq[1]), xs)
+    xq = mx.mx_dequantize(xc, xs)
+    pm = oracle.permute(np.zeros((cfg.T, 1)), ref["routing_map"], ref["probs"], cfg.K)
+    n = pm["tokens_per_expert"]
+    offs = np.concatenate([[0], np.cumsum(n)])
+    np.testing.assert_array_equal(_np(layer.sorted_token)[:offs[-1]], pm["sorted_token"])
+    act_c, act_s = _np(layer.actq[0]), untile(layer.actq[1])
+    wq = {k: layer.wq[k] for k in ("w_gate", "w_up", "w_down")}
+
+    def expert_w(e, keys=("w_gate", "w_up", "w_down")):
+        return [mx.mx_dequantize(_np(wq[k][0][e]), untile(wq[k][1][e][None])[0]) for k in keys]
+
+    def gpu_rows(t, rows):
+        return f64(t[torch.from_numpy(np.asarray(rows, dtype=np.int64)).to(DEV)])
+
+    def y_rows(rows, e, wd):
+        return oracle.round_bf16(mx.mx_dequantize(act_c[rows], act_s[rows]) @ wd.T)
+
+    rng = np.random.default_rng(1)
+    for e in sorted({int(np.argmax(n)), int(np.nonzero(n)[0][-1])}):
+        rows = rng.choice(np.arange(offs[e], offs[e + 1]), size=min(4, int(n[e])), replace=False)
+        wg, wu, wd = expert_w(e)
+        xr = xq[pm["sorted_token"][rows]]
+        g, u = xr @ wg.T, xr @ wu.T
+        sg = 1 / (1 + np.exp(-g))
+        exact = g * sg * u
+        sens = 1.1 * np.abs(u) * (np.abs(xr) @ np.abs(wg).T) + np.abs(g * sg) * (np.abs(xr) @ np.abs(wu).T)
+        dq = mx.mx_dequantize(act_c[rows], act_s[rows])
+        bad = np.abs(dq - exact) > _act_bound(exact, sens, act_s[rows])
+        assert not bad.any(), (name, e, int(bad.sum()))
+        assert_close(gpu_rows(layer.expert_out, rows), y_rows(rows, e, wd), "bf16",
+                     f"expert_out[{name}, e={e}]")
+    # sampled tokens: combine of the oracle's expert outputs (from the GPU's act codes)
+    toks = rng.choice(cfg.T, size=n_tok, replace=False)
+    shared = None
+    if "shared_gate" in inp:
+        swd = mx.mx_dequantize(_np(layer.wq["shared_down"][0][0]), untile(layer.wq["shared_down"][1])[0])
+        sact = mx.mx_dequantize(_np(layer.shared_actq[0])[toks], untile(layer.shared_actq[1])[toks])
+        shared = oracle.round_bf16(sact @ swd.T)
+    for i, t in enumerate(toks):
+        acc = np.zeros(cfg.h)
+        for k in range(cfg.K):
+            r = int(pm["row_id_map"][t, k])
+            if r < 0:
+                continue
+            e = int(np.searchsorted(offs, r, side="right") - 1)
+            acc += pm["permuted_probs"][r] * y_rows(np.array([r]), e, expert_w(e, ("w_down",))[0])[0]
+        if shared is not None:
+            acc += shared[i]
+        assert_close(gpu_rows(out, [t]), oracle.round_bf16(acc)[None], "bf16", f"out[{name}, t={t}]")
