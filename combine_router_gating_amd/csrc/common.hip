@@ -1,5 +1,6 @@
 // Error reporting, interface version, and the per-block expert counting
 // kernels shared by the router (capacity drop) and the permute.
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <string>
@@ -49,32 +50,93 @@ __global__ void __launch_bounds__(256) block_hist_kernel(const uint8_t* __restri
     if (base[i]) atomicAdd(&cnt[i % E], 1);
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += blockDim.x) hist[static_cast<int64_t>(b) * E + e] = cnt[e];
+  for (int e = threadIdx.x; e < E; e += blockDim.x)
+    hist[static_cast<int64_t>(e) * gridDim.x + b] = cnt[e];
 }
 
-// One workgroup per expert: each thread sums a contiguous run of blocks,
-// the runs are scanned across the workgroup, then each thread writes the
-// exclusive prefixes of its run.
+// Workgroup (e, s) scans chunk s of expert e's blocks: the counts before
+// and after the chunk are summed, the chunk's own blocks are split into
+// contiguous runs, one per thread, and scanned across the workgroup; each
+// thread writes the exclusive prefixes of its run.  With a capacity and the
+// map, the same pass drops expert e's entries ranked >= cap (rank = entries
+// of e in earlier tokens, so the earliest tokens are kept): the one block
+// whose ranks cross cap is walked in token order, and every entry of the
+// blocks after it (all ranked >= cap) is cleared by the whole workgroup.
 __global__ void __launch_bounds__(256) count_scan_kernel(const int32_t* __restrict__ hist,
                                                          int nblk, int E, int64_t cap,
                                                          int32_t* __restrict__ blkoff,
-                                                         int32_t* __restrict__ kept) {
+                                                         int32_t* __restrict__ kept, int64_t T,
+                                                         float* __restrict__ probs,
+                                                         uint8_t* __restrict__ rmap) {
   __shared__ int64_t scratch[4];
+  __shared__ int s_past;  // first block of the chunk whose entries all rank >= cap
   const int e = blockIdx.x;
-  const int per = (nblk + 255) / 256;
-  const int b0 = threadIdx.x * per;
-  const int b1 = min(nblk, b0 + per);
-  int64_t sum = 0;
-  for (int b = b0; b < b1; ++b) sum += hist[static_cast<int64_t>(b) * E + e];
-  int64_t total;
-  int64_t run = block_exclusive_scan256(sum, scratch, &total);
+  const int cb = (nblk + static_cast<int>(gridDim.y) - 1) / static_cast<int>(gridDim.y);
+  const int c0 = min(nblk, static_cast<int>(blockIdx.y) * cb);
+  const int c1 = min(nblk, c0 + cb);
+  const int32_t* h = hist + static_cast<int64_t>(e) * nblk;
+  const int per = (c1 - c0 + 255) / 256;
+  const int b0 = c0 + static_cast<int>(threadIdx.x) * per;
+  const int b1 = min(c1, b0 + per);
+  int64_t sum = 0, pre = 0, post = 0;
+  for (int b = b0; b < b1; ++b) sum += h[b];
+  for (int b = threadIdx.x; b < c0; b += 256) pre += h[b];
+  for (int b = c1 + static_cast<int>(threadIdx.x); b < nblk; b += 256) post += h[b];
+  int64_t chunk, outside;
+  int64_t run = block_exclusive_scan256(sum, scratch, &chunk);
+  // counts are below 2^31, so both sums fit one 64-bit word without a carry
+  block_exclusive_scan256((pre << 32) | post, scratch, &outside);
+  const int64_t before = outside >> 32;
+  const int64_t total = before + chunk + (outside & 0xffffffffll);
+  run += before;
+  const bool drop = rmap && cap >= 0 && total > cap;
+  if (threadIdx.x == 0) {
+    s_past = c1;
+    if (blockIdx.y == 0) kept[e] = static_cast<int32_t>((cap >= 0 && total > cap) ? cap : total);
+  }
+  __syncthreads();
   for (int b = b0; b < b1; ++b) {
-    const int64_t i = static_cast<int64_t>(b) * E + e;
-    const int c = hist[i];
-    blkoff[i] = static_cast<int32_t>(run);
+    const int c = h[b];
+    blkoff[static_cast<int64_t>(b) * E + e] = static_cast<int32_t>(run);
+    if (drop && run >= cap) atomicMin(&s_past, b);
+    if (drop && run < cap && run + c > cap) {
+      const int64_t t0 = static_cast<int64_t>(b) * kCountBlock;
+      const int nt = static_cast<int>(min(static_cast<int64_t>(kCountBlock), T - t0));
+      uint8_t m[kCountBlock];
+#pragma unroll
+      for (int i = 0; i < kCountBlock; ++i) m[i] = i < nt ? rmap[(t0 + i) * E + e] : 0;
+      int64_t r = run;
+#pragma unroll
+      for (int i = 0; i < kCountBlock; ++i) {
+        if (m[i]) {
+          if (r >= cap) {
+            rmap[(t0 + i) * E + e] = 0;
+            probs[(t0 + i) * E + e] = 0.f;
+          }
+          ++r;
+        }
+      }
+    }
     run += c;
   }
-  if (threadIdx.x == 0) kept[e] = static_cast<int32_t>((cap >= 0 && total > cap) ? cap : total);
+  if (drop) {
+    __syncthreads();
+    const int64_t end = min(T, static_cast<int64_t>(c1) * kCountBlock);
+    constexpr int kU = 4;
+    for (int64_t t = static_cast<int64_t>(s_past) * kCountBlock + threadIdx.x; t < end;
+         t += 256 * kU) {
+      uint8_t m[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) m[u] = t + 256 * u < end ? rmap[(t + 256 * u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        if (m[u]) {
+          rmap[(t + 256 * u) * E + e] = 0;
+          probs[(t + 256 * u) * E + e] = 0.f;
+        }
+      }
+    }
+  }
 }
 
 __global__ void fill_i32_kernel(int32_t* __restrict__ p, int64_t n, int32_t v) {
@@ -95,9 +157,12 @@ void launch_block_hist(const uint8_t* map, int64_t T, int64_t E, int32_t* hist, 
 }
 
 void launch_count_scan(const int32_t* hist, int64_t nblk, int64_t E, int64_t cap, int32_t* blkoff,
-                       int32_t* kept, hipStream_t s) {
-  hipLaunchKernelGGL(count_scan_kernel, dim3(static_cast<unsigned>(E)), dim3(256), 0, s, hist,
-                     static_cast<int>(nblk), static_cast<int>(E), cap, blkoff, kept);
+                       int32_t* kept, hipStream_t s, int64_t T, float* probs, uint8_t* rmap) {
+  // chunks of about 64 blocks, at most 16 per expert (each reads the whole row)
+  const int64_t chunks = std::min<int64_t>(16, std::max<int64_t>(1, ceil_div(nblk, 64)));
+  hipLaunchKernelGGL(count_scan_kernel, dim3(static_cast<unsigned>(E), static_cast<unsigned>(chunks)),
+                     dim3(256), 0, s, hist,
+                     static_cast<int>(nblk), static_cast<int>(E), cap, blkoff, kept, T, probs, rmap);
 }
 
 }  // namespace moe

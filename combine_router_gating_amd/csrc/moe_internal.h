@@ -27,16 +27,20 @@ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 // ------------------------------------------- per-block expert counts and their scan
-// hist[b*E + e]   = number of tokens of block b (kCountBlock tokens) routed to e
-// blkoff[b*E + e] = number of tokens routed to e in blocks before b
+// hist[e*nblk + b] = number of tokens of block b (kCountBlock tokens) routed
+//                    to e (expert-major, so that the per-expert scan reads a
+//                    contiguous run)
+// blkoff[b*E + e]  = number of tokens routed to e in blocks before b
 size_t count_ws_bytes(int64_t T, int64_t E);  // hist + blkoff + kept[E]
 // Fill n int32 with v by a kernel (graph-capture friendly, no memset node).
 void launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);
 void launch_block_hist(const uint8_t* map, int64_t T, int64_t E, int32_t* hist, hipStream_t s);
 // One workgroup per expert: blkoff = exclusive prefix over blocks,
-// kept[e] = min(total, cap) (cap < 0: total).
+// kept[e] = min(total, cap) (cap < 0: total).  With cap >= 0 and rmap/probs
+// ([T,E]), also drops the entries ranked >= cap (earliest tokens kept).
 void launch_count_scan(const int32_t* hist, int64_t nblk, int64_t E, int64_t cap, int32_t* blkoff,
-                       int32_t* kept, hipStream_t s);
+                       int32_t* kept, hipStream_t s, int64_t T = 0, float* probs = nullptr,
+                       uint8_t* rmap = nullptr);
 
 // ---------------------------------------------------------------- device helpers
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {

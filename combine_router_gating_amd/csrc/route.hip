@@ -17,8 +17,8 @@
 //   router_topk_kernel     one wave per token: logits = partials summed in a
 //                          fixed order (+ b), scores, K rounds of a wave-wide
 //                          argmax, probs, map, per-block expert counts
-//   count_scan_kernel      (capacity only) per-expert prefix over blocks
-//   router_drop_kernel     (capacity only) clear entries ranked >= capacity
+//   count_scan_kernel      per-expert prefix over blocks and tokens_per_expert;
+//                          with a capacity, also clears the entries ranked >= capacity
 #include <algorithm>
 #include <cmath>
 
@@ -480,32 +480,7 @@ __global__ void __launch_bounds__(256) router_topk_kernel(
   }
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += blockDim.x)
-    hist[static_cast<int64_t>(blockIdx.x) * E + e] = cnt[e];
-}
-
-// ------------------------------------------------------------ capacity drop
-// Thread e walks the block's tokens in order; rank = tokens routed to e in
-// earlier blocks + earlier in this block.  Entries ranked >= cap are dropped.
-__global__ void __launch_bounds__(256) router_drop_kernel(const int32_t* __restrict__ blkoff,
-                                                          int64_t T, int E, int64_t cap,
-                                                          float* __restrict__ probs,
-                                                          uint8_t* __restrict__ rmap) {
-  const int b = blockIdx.x;
-  const int64_t t0 = static_cast<int64_t>(b) * kCountBlock;
-  const int nt = static_cast<int>(min(static_cast<int64_t>(kCountBlock), T - t0));
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    int64_t r = blkoff[static_cast<int64_t>(b) * E + e];
-    for (int i = 0; i < nt; ++i) {
-      const int64_t idx = (t0 + i) * E + e;
-      if (rmap[idx]) {
-        if (r >= cap) {
-          rmap[idx] = 0;
-          probs[idx] = 0.f;
-        }
-        ++r;
-      }
-    }
-  }
+    hist[static_cast<int64_t>(e) * gridDim.x + blockIdx.x] = cnt[e];
 }
 
 // ------------------------------------------------- capacity mask per expert
@@ -873,10 +848,7 @@ extern "C" moe_status moe_route(const moe_route_desc* d, const void* x, const fl
   // position policy: tokens_per_expert = min(count, capacity), then drop
   // entries ranked >= capacity
   const int64_t cap = capacity_of(d);
-  launch_count_scan(hist, nblk, E, cap, blkoff, tokens_per_expert, s);
-  if (cap >= 0)
-    hipLaunchKernelGGL(router_drop_kernel, dim3(static_cast<unsigned>(nblk)), dim3(256), 0, s, blkoff,
-                       T, static_cast<int>(E), cap, probs, routing_map);
+  launch_count_scan(hist, nblk, E, cap, blkoff, tokens_per_expert, s, T, probs, routing_map);
   return check_launch("moe_route");
 }
 

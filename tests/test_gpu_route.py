@@ -101,7 +101,8 @@ def test_sigmoid_bits_match_the_oracle():
 
 @pytest.mark.parametrize("T,E,K,cf,minc", [(200, 8, 2, 0.5, 0), (1000, 16, 1, 1.0, 0),
                                            (97, 4, 2, 0.1, 3), (300, 64, 4, 0.25, 1),
-                                           (64, 8, 8, 0.01, 0), (50, 5, 1, 0.05, 0)])
+                                           (64, 8, 8, 0.01, 0), (50, 5, 1, 0.05, 0),
+                                           (20003, 4, 1, 0.9, 0), (70001, 8, 2, 0.8, 0)])
 def test_capacity_drop_keeps_earliest(T, E, K, cf, minc):
     log(f"capacity: T={T} E={E} K={K} cf={cf} min={minc}")
     rng = np.random.default_rng(T + E)
