@@ -14,9 +14,11 @@
 //                          operands streamed through a ring of LDS stages,
 //                          split over h into partial sums (more workgroups)
 //   router_logits_simt     fp32 x (or h not a multiple of 16): fp32 FMA, LDS-tiled
-//   router_topk_kernel     one wave per token: logits = partials summed in a
-//                          fixed order (+ b), scores, K rounds of a wave-wide
-//                          argmax, probs, map, per-block expert counts
+//   router_topk_row_kernel E <= 256: one 16-lane row per token (16 tokens per
+//                          workgroup at once): logits = partials summed in a
+//                          fixed order (+ b), scores, K rounds of an argmax over
+//                          the row (DPP exchanges), probs, map, per-block counts
+//   router_topk_kernel     E > 256: the same with one wave per token
 //   count_scan_kernel      per-expert prefix over blocks and tokens_per_expert;
 //                          with a capacity, also clears the entries ranked >= capacity
 #include <algorithm>
@@ -483,6 +485,183 @@ __global__ void __launch_bounds__(256) router_topk_kernel(
     hist[static_cast<int64_t>(e) * gridDim.x + blockIdx.x] = cnt[e];
 }
 
+// Top-k with one 16-lane row per token (E <= 256): a workgroup's 16 rows
+// are its 16 tokens, all handled at once; lane r of a row holds experts
+// r*VPL .. r*VPL+VPL-1 (contiguous, so a row reads a token's logits with
+// vector loads).  Reductions over the row are DPP exchanges within the
+// 16-lane row (swap neighbours, swap pairs, half-row mirror, row mirror),
+// after which every lane of the row holds the same result.
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(dpp_i<CTRL>(__float_as_int(v)));
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // lane i <- lane 7-i within each 8
+constexpr int kDppMirror = 0x140;      // lane i <- lane 15-i within the row
+
+__device__ __forceinline__ float row_max(float v) {
+  v = fmaxf(v, dpp_f<kDppXor1>(v));
+  v = fmaxf(v, dpp_f<kDppXor2>(v));
+  v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
+  return fmaxf(v, dpp_f<kDppMirror>(v));
+}
+__device__ __forceinline__ float row_sum(float v) {
+  v += dpp_f<kDppXor1>(v);
+  v += dpp_f<kDppXor2>(v);
+  v += dpp_f<kDppHalfMirror>(v);
+  return v + dpp_f<kDppMirror>(v);
+}
+template <int CTRL>
+__device__ __forceinline__ void arg_step(float& bv, int& bi) {
+  const float ov = dpp_f<CTRL>(bv);
+  const int oi = dpp_i<CTRL>(bi);
+  if (better(ov, oi, bv, bi)) {
+    bv = ov;
+    bi = oi;
+  }
+}
+
+template <int VPL>
+__global__ void __launch_bounds__(256) router_topk_row_kernel(
+    const float* __restrict__ part, int nsplit, const float* __restrict__ bias,
+    const float* __restrict__ expert_bias, int64_t T, int E, int K, int score, int pre_softmax,
+    float* __restrict__ logits_out, float* __restrict__ scores_out, float* __restrict__ probs,
+    uint8_t* __restrict__ rmap, int32_t* __restrict__ hist) {
+  static_assert(kCountBlock == 16, "one token per 16-lane row");
+  __shared__ int cnt[16 * VPL];
+  for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;
+  __syncthreads();
+  const int r = threadIdx.x & 15;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kCountBlock + threadIdx.x / 16;
+  const int e0 = r * VPL;
+  if (t < T) {  // uniform over the row
+    bool valid[VPL], taken[VPL];
+    float l[VPL], s[VPL], key[VPL];
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) {
+      valid[j] = e0 + j < E;
+      taken[j] = false;
+    }
+    // logits: every partial plane loaded first, summed in plane order, then the bias
+    float pv[kMaxSplit][VPL];
+    const int64_t row = t * E;
+    const bool vec = (VPL % 4 == 0) && (E % 4 == 0);
+#pragma unroll
+    for (int sp = 0; sp < kMaxSplit; ++sp) {
+      if (sp < nsplit) {
+        const float* src = part + static_cast<int64_t>(sp) * T * E + row;
+        if (vec) {  // E % 4 == 0: a group of 4 is wholly in or out of the row
+#pragma unroll
+          for (int j = 0; j < VPL; j += 4) {
+            const float4 q = valid[j] ? *reinterpret_cast<const float4*>(src + e0 + j)
+                                      : make_float4(0.f, 0.f, 0.f, 0.f);
+            pv[sp][j] = q.x;
+            pv[sp][j + 1] = q.y;
+            pv[sp][j + 2] = q.z;
+            pv[sp][j + 3] = q.w;
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < VPL; ++j) pv[sp][j] = valid[j] ? src[e0 + j] : 0.f;
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) {
+      float v = pv[0][j];
+#pragma unroll
+      for (int sp = 1; sp < kMaxSplit; ++sp)
+        if (sp < nsplit) v += pv[sp][j];
+      if (bias && valid[j]) v += bias[e0 + j];
+      l[j] = valid[j] ? v : -INFINITY;
+      if (valid[j] && logits_out) logits_out[row + e0 + j] = l[j];
+    }
+    if (score == MOE_SCORE_SOFTMAX) {
+      float m = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < VPL; ++j) m = fmaxf(m, l[j]);
+      m = row_max(m);
+      float sum = 0.f;
+#pragma unroll
+      for (int j = 0; j < VPL; ++j) {
+        s[j] = valid[j] ? expf(l[j] - m) : 0.f;
+        sum += s[j];
+      }
+      sum = row_sum(sum);
+#pragma unroll
+      for (int j = 0; j < VPL; ++j) {
+        s[j] = s[j] / sum;
+        key[j] = l[j];
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < VPL; ++j) {
+        s[j] = valid[j] ? (score == MOE_SCORE_SIGMOID ? sigmoid_fixed(l[j]) : sqrtsoftplus_fixed(l[j]))
+                        : 0.f;
+        key[j] = (valid[j] && expert_bias) ? s[j] + expert_bias[e0 + j] : s[j];
+      }
+    }
+    float top_logit = 0.f;
+    for (int k = 0; k < K; ++k) {
+      float bv = 0.f;
+      int bi = -1;
+#pragma unroll
+      for (int j = 0; j < VPL; ++j)
+        if (valid[j] && !taken[j] && better(key[j], e0 + j, bv, bi)) {
+          bv = key[j];
+          bi = e0 + j;
+        }
+      arg_step<kDppXor1>(bv, bi);
+      arg_step<kDppXor2>(bv, bi);
+      arg_step<kDppHalfMirror>(bv, bi);
+      arg_step<kDppMirror>(bv, bi);
+      if (k == 0) top_logit = bv;
+#pragma unroll
+      for (int j = 0; j < VPL; ++j)
+        if (e0 + j == bi) taken[j] = true;
+    }
+    float p[VPL];
+    if (score == MOE_SCORE_SOFTMAX && pre_softmax) {
+#pragma unroll
+      for (int j = 0; j < VPL; ++j) p[j] = taken[j] ? s[j] : 0.f;
+    } else if (score == MOE_SCORE_SOFTMAX) {
+      // softmax over the K chosen logits; the first winner holds their maximum
+      float sum = 0.f;
+#pragma unroll
+      for (int j = 0; j < VPL; ++j) {
+        p[j] = taken[j] ? expf(l[j] - top_logit) : 0.f;
+        sum += p[j];
+      }
+      sum = row_sum(sum);
+#pragma unroll
+      for (int j = 0; j < VPL; ++j) p[j] = p[j] / sum;
+    } else {
+      float sum = 0.f;
+#pragma unroll
+      for (int j = 0; j < VPL; ++j) sum += taken[j] ? s[j] : 0.f;
+      sum = row_sum(sum) + 1e-20f;
+#pragma unroll
+      for (int j = 0; j < VPL; ++j) p[j] = taken[j] ? s[j] / sum : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) {
+      if (!valid[j]) continue;
+      probs[row + e0 + j] = p[j];
+      rmap[row + e0 + j] = taken[j] ? 1 : 0;
+      if (scores_out) scores_out[row + e0 + j] = s[j];
+      if (taken[j]) atomicAdd(&cnt[e0 + j], 1);
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x)
+    hist[static_cast<int64_t>(e) * gridDim.x + blockIdx.x] = cnt[e];
+}
+
 // ------------------------------------------------- capacity mask per expert
 // One workgroup per expert e: the capacity mask of column e is the first
 // `cap` of the T tokens by (key descending, token ascending), with key =
@@ -678,6 +857,13 @@ void launch_topk(int64_t nblk, hipStream_t s, const TopkArgs& a) {
                      a.logits_out, a.scores, a.probs, a.map, a.hist);
 }
 
+template <int VPL>
+void launch_topk_row(int64_t nblk, hipStream_t s, const TopkArgs& a) {
+  hipLaunchKernelGGL(router_topk_row_kernel<VPL>, dim3(static_cast<unsigned>(nblk)), dim3(256), 0, s,
+                     a.part, a.nsplit, a.bias, a.expert_bias, a.T, a.E, a.K, a.score, a.pre,
+                     a.logits_out, a.scores, a.probs, a.map, a.hist);
+}
+
 size_t logits_ws_bytes(const moe_route_desc* d) {
   const int64_t planes = use_mfma(d) ? mfma_plan(d->T, d->h, d->E).ksplit : 1;
   return align_up(static_cast<size_t>(planes * d->T * d->E) * sizeof(float), 256);
@@ -826,10 +1012,13 @@ extern "C" moe_status moe_route(const moe_route_desc* d, const void* x, const fl
     ta.bias = b_router;
   }
 
+  const int vpl = static_cast<int>(ceil_div(E, 16));
   const int epl = static_cast<int>(ceil_div(E, 64));
-  if (epl <= 1) launch_topk<1>(nblk, s, ta);
-  else if (epl <= 2) launch_topk<2>(nblk, s, ta);
-  else if (epl <= 4) launch_topk<4>(nblk, s, ta);
+  if (vpl <= 1) launch_topk_row<1>(nblk, s, ta);
+  else if (vpl <= 2) launch_topk_row<2>(nblk, s, ta);
+  else if (vpl <= 4) launch_topk_row<4>(nblk, s, ta);
+  else if (vpl <= 8) launch_topk_row<8>(nblk, s, ta);
+  else if (vpl <= 16) launch_topk_row<16>(nblk, s, ta);
   else if (epl <= 8) launch_topk<8>(nblk, s, ta);
   else launch_topk<16>(nblk, s, ta);
 

@@ -55,7 +55,8 @@ def test_route_full_size(name):
 
 @pytest.mark.parametrize("score,pre", [("softmax", True), ("softmax", False), ("sigmoid", True)])
 @pytest.mark.parametrize("T,E,K", [(37, 8, 2), (100, 64, 1), (65, 128, 8), (33, 256, 8),
-                                   (20, 1000, 6), (16, 3, 3), (1, 1, 1)])
+                                   (20, 1000, 6), (16, 3, 3), (1, 1, 1), (50, 20, 3),
+                                   (40, 100, 4), (30, 250, 8), (21, 257, 3)])
 def test_route_ties_from_given_logits(score, pre, T, E, K):
     """Integer-valued logits (many exact ties) and all-equal rows: the lowest
     expert index must win every tie, bit-exactly."""
