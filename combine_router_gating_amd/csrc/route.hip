@@ -109,47 +109,59 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 // Split eight fp32 weights into their hi/mid/lo bf16 parts (see above),
-// each part as one 8-wide bf16 MFMA operand.
+// each part as one 8-wide bf16 MFMA operand.  A part's bf16 value is the top
+// half of an fp32 word (v, then r1 = v - hi, then r2 = r1 - mid), so two
+// parts are packed by one byte permute of the two words' top halves.
+__device__ __forceinline__ uint32_t top_halves(float lo_elem, float hi_elem) {
+  // bytes 2,3 of lo_elem then bytes 2,3 of hi_elem (selector indices 4-7 pick
+  // from the first operand, 0-3 from the second)
+  return __builtin_amdgcn_perm(__float_as_uint(hi_elem), __float_as_uint(lo_elem), 0x07060302u);
+}
 __device__ __forceinline__ void split8(const f32x4_t a, const f32x4_t b, bf16x8_t& hi,
                                        bf16x8_t& mi, bf16x8_t& lo) {
+  float v[8], r1[8], r2[8];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    v[q] = a[q];
+    v[q + 4] = b[q];
+  }
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    r1[q] = v[q] - __uint_as_float(__float_as_uint(v[q]) & 0xffff0000u);
+    r2[q] = r1[q] - __uint_as_float(__float_as_uint(r1[q]) & 0xffff0000u);
+  }
   u32x4_t h, m, l;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    uint32_t hs[2], ms[2], ls[2];
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const float v = (q < 2) ? a[2 * q + r] : b[2 * (q - 2) + r];
-      const uint32_t hb = __float_as_uint(v) & 0xffff0000u;
-      const float r1 = v - __uint_as_float(hb);
-      const uint32_t mb = __float_as_uint(r1) & 0xffff0000u;
-      const float r2 = r1 - __uint_as_float(mb);
-      hs[r] = hb >> 16;
-      ms[r] = mb >> 16;
-      ls[r] = __float_as_uint(r2) >> 16;
-    }
-    h[q] = hs[0] | (hs[1] << 16);
-    m[q] = ms[0] | (ms[1] << 16);
-    l[q] = ls[0] | (ls[1] << 16);
+    h[q] = top_halves(v[2 * q], v[2 * q + 1]);
+    m[q] = top_halves(r1[2 * q], r1[2 * q + 1]);
+    l[q] = top_halves(r2[2 * q], r2[2 * q + 1]);
   }
   hi = __builtin_bit_cast(bf16x8_t, h);
   mi = __builtin_bit_cast(bf16x8_t, m);
   lo = __builtin_bit_cast(bf16x8_t, l);
 }
 
-// Gating linear on MFMA through a ring of LDS stages.  A workgroup owns
-// BT = 64*WT tokens x BE = 64*WE experts over one slice of h, in SK-wide k
-// slabs; a stage holds one slab's x rows (BT x 2*SK bytes of bf16) and
-// weight rows (BE x 4*SK bytes of fp32), filled by direct global->LDS loads, and
-// STAGES-1 slabs stay in flight while one is multiplied.  Each wave reads
-// its 64x64 fragments from LDS and splits the fp32 weight fragment into its
-// three bf16 parts in registers (three MFMAs per block and k step).
-template <int WT, int WE, int STAGES, int SK>
+// Gating linear on MFMA through a ring of LDS stages.  A wave owns 32*NI
+// experts x 32*NJ tokens (NI x NJ blocks of v_mfma_f32_32x32x16_bf16, three
+// MFMAs per block and k step); the 4 waves of a workgroup are WT along tokens
+// x WE along experts, so a workgroup owns BT = 32*NJ*WT tokens x BE =
+// 32*NI*WE experts over one slice of h, in SK-wide k slabs.  A stage holds
+// one slab's x rows (BT x 2*SK bytes of bf16) and weight rows (BE x 4*SK
+// bytes of fp32), filled by direct global->LDS loads, and STAGES-1 slabs
+// stay in flight while one is multiplied.  Each wave reads its fragments
+// from LDS and splits its fp32 weight fragments into their three bf16 parts
+// in registers: with NI = 1 a wave splits one fragment per k step for four
+// token blocks, which keeps the split's VALU work under the MFMA time.
+// blockIdx.y selects a slice of h whose partial sums go to their own [T, E]
+// plane.
+template <int WT, int WE, int NI, int NJ, int STAGES, int SK>
 __global__ void __launch_bounds__(256) router_logits_ring(const uint16_t* __restrict__ x,
                                                           const float* __restrict__ w,
                                                           float* __restrict__ part, int64_t T,
                                                           int h, int E, int kchunk) {
   static_assert(WT * WE == 4, "4 waves");
-  constexpr int BT = 64 * WT, BE = 64 * WE;
+  constexpr int BT = 32 * NJ * WT, BE = 32 * NI * WE;
   static_assert(SK == 32 || SK == 64, "k per slab");
   constexpr int XB = BT * SK * 2;  // x bytes per stage
   constexpr int WB = BE * SK * 4;  // weight bytes per stage
@@ -189,11 +201,11 @@ __global__ void __launch_bounds__(256) router_logits_ring(const uint16_t* __rest
 #pragma unroll
     for (int j = 0; j < LPW; ++j) dma16(src[j] + static_cast<int64_t>(sl) * step[j], dst + j * 1024);
   };
-  f32x16_t acc[2][2];
+  f32x16_t acc[NI][NJ];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < NI; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
   const int l32 = lane & 31, hi = lane >> 5;
@@ -206,14 +218,14 @@ __global__ void __launch_bounds__(256) router_logits_ring(const uint16_t* __rest
     const char* st = smem + (sl % STAGES) * STAGE;
 #pragma unroll
     for (int kk = 0; kk < SK / 16; ++kk) {
-      bf16x8_t xb[2], wp[3][2];
+      bf16x8_t xb[NJ], wp[3][NI];
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < NJ; ++j)
         xb[j] = *reinterpret_cast<const bf16x8_t*>(
-            st + lds_chunk_byte<SK>(wt * 64 + j * 32 + l32, kk * 2 + hi));
+            st + lds_chunk_byte<SK>(wt * 32 * NJ + j * 32 + l32, kk * 2 + hi));
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int row = we * 64 + i * 32 + l32;
+      for (int i = 0; i < NI; ++i) {
+        const int row = we * 32 * NI + i * 32 + l32;
         const int cw = kk * 4 + hi * 2;
         const f32x4_t a =
             *reinterpret_cast<const f32x4_t*>(st + XB + lds_chunk_byte<2 * SK>(row, cw));
@@ -224,9 +236,9 @@ __global__ void __launch_bounds__(256) router_logits_ring(const uint16_t* __rest
 #pragma unroll
       for (int pl = 0; pl < 3; ++pl)
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < NI; ++i)
 #pragma unroll
-          for (int j = 0; j < 2; ++j)
+          for (int j = 0; j < NJ; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wp[pl][i], xb[j], acc[i][j], 0, 0, 0);
     }
     if (sl + STAGES < nsl) {
@@ -235,44 +247,71 @@ __global__ void __launch_bounds__(256) router_logits_ring(const uint16_t* __rest
       issue(sl + STAGES);
     }
   }
-  // lane holds [token l32 of block j][experts 8g + 4*(lane/32) + q of block i]
-  float* out = part + static_cast<int64_t>(blockIdx.y) * T * E;
-  const int64_t tw = t0 + wt * 64;
-  const int ew = e0 + we * 64;
+  // Epilogue through LDS (the ring is free once every wave is past its last
+  // slab): lane holds [token l32 of block j][experts 8g + 4*(lane/32) + q of
+  // block i]; the tile is written to LDS rows of BE floats (+4 of padding
+  // against bank conflicts), then each plane row is stored with contiguous
+  // 16-byte stores (16 lanes per 256 bytes) instead of scattered dwords.
+  constexpr int OS = BE + 4;
+  static_assert(BT * OS * 4 <= STAGES * STAGE, "output tile fits the ring");
+  __syncthreads();
+  float* ot = reinterpret_cast<float*>(smem);
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int64_t t = tw + j * 32 + l32;
-    if (t >= T) continue;
+  for (int j = 0; j < NJ; ++j)
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < NI; ++i)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int e = ew + i * 32 + g * 8 + hi * 4;
+        const int tl = wt * 32 * NJ + j * 32 + l32;
+        const int el = we * 32 * NI + i * 32 + g * 8 + hi * 4;
+        f32x4_t v;
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          if (e + q < E) out[t * E + e + q] = acc[i][j][g * 4 + q];
+        for (int q = 0; q < 4; ++q) v[q] = acc[i][j][g * 4 + q];
+        *reinterpret_cast<f32x4_t*>(ot + tl * OS + el) = v;
       }
+  __syncthreads();
+  float* out = part + static_cast<int64_t>(blockIdx.y) * T * E;
+  constexpr int CPR = BE / 4;  // 16-byte chunks per tile row
+  const bool vec = E % 4 == 0;
+  for (int c = tid; c < BT * CPR; c += 256) {
+    const int rl = c / CPR, e = e0 + (c % CPR) * 4;
+    const int64_t t = t0 + rl;
+    if (t >= T || e >= E) continue;
+    const f32x4_t v = *reinterpret_cast<const f32x4_t*>(ot + rl * OS + (c % CPR) * 4);
+    if (vec) {
+      *reinterpret_cast<f32x4_t*>(out + t * E + e) = v;
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (e + q < E) out[t * E + e + q] = v[q];
+    }
   }
 }
 
 constexpr int kMaxSplit = 8;  // partial-logit planes at most
 
 struct MfmaPlan {
-  int wt, we;
+  int shape;  // 0: 256 x 32 (E <= 32), 1: 256 x 64 (E <= 64), 2: 128 x 128 tokens x experts
+  int bt, be;
   int64_t gx, gz;
   int ksplit, kchunk;
 };
 
-// Wave layout and h-split for the MFMA gating linear: aim for >= 512
-// workgroups (two per CU) with at most 8 partial planes.
+// Workgroup tile and h-split for the MFMA gating linear: the narrowest
+// expert tile that covers E (up to 128), then h split into at most 8
+// partial planes of >= 128 so that about 256 workgroups (one per CU) run.
+// Timed on the Switch-, Mixtral-, Qwen3- and DeepSeek-V3-shaped routers,
+// more planes (two workgroups per CU) were slower or equal: the extra plane
+// traffic outweighs the occupancy.
 MfmaPlan mfma_plan(int64_t T, int64_t h, int64_t E) {
   MfmaPlan p;
-  p.we = E <= 64 ? 1 : 2;  // 4 waves of 64x64: 256 x 64 or 128 x 128 per workgroup
-  p.wt = 4 / p.we;
-  p.gx = ceil_div(T, 64 * p.wt);
-  p.gz = ceil_div(E, 64 * p.we);
+  p.shape = E <= 32 ? 0 : E <= 64 ? 1 : 2;
+  p.bt = p.shape == 2 ? 128 : 256;
+  p.be = p.shape == 0 ? 32 : p.shape == 1 ? 64 : 128;
+  p.gx = ceil_div(T, p.bt);
+  p.gz = ceil_div(E, p.be);
   const int64_t base = p.gx * p.gz;
-  int64_t ks = std::min<int64_t>(kMaxSplit, std::max<int64_t>(1, ceil_div(512, base)));
+  int64_t ks = std::min<int64_t>(kMaxSplit, std::max<int64_t>(1, ceil_div(256, base)));
   ks = std::min<int64_t>(ks, std::max<int64_t>(1, h / 128));
   p.kchunk = static_cast<int>(ceil_div(ceil_div(h, ks), 32) * 32);
   p.ksplit = static_cast<int>(ceil_div(h, p.kchunk));
@@ -288,7 +327,7 @@ bool use_mfma(const moe_route_desc* d) { return d->x_dtype == MOE_BF16 && d->h %
 // and C2 = fp32(ln2 - C1); p = degree-7 Taylor polynomial of e^r in Horner
 // form with fp32(1/k!) coefficients; result ldexp(p, n); 0 below y = -86
 // (keeps every result in the fp32 normal range).
-__device__ __noinline__ float exp_fixed(float y) {
+__device__ __forceinline__ float exp_fixed(float y) {
 #pragma clang fp contract(off)
   const float log2e = 0x1.715476p+0f;  // fp32(1/ln 2)
   const float c1 = 0x1.62ep-1f;        // ln 2 truncated to 12 bits
@@ -308,7 +347,7 @@ __device__ __noinline__ float exp_fixed(float y) {
 }
 
 // sigmoid(x) = 1/(1+e) for x >= 0, e/(1+e) for x < 0, with e = exp_fixed(-|x|).
-__device__ __noinline__ float sigmoid_fixed(float x) {
+__device__ __forceinline__ float sigmoid_fixed(float x) {
 #pragma clang fp contract(off)
   const float e = exp_fixed(-fabsf(x));
   const float den = 1.0f + e;
@@ -320,7 +359,7 @@ __device__ __noinline__ float sigmoid_fixed(float x) {
 // is 2*atanh(s) with s = u/(2+u) <= 1/3: (2*s) * q, q the degree-7 Horner
 // polynomial in s*s with fp32(1/(2j+1)) coefficients; then the correctly
 // rounded square root.
-__device__ __noinline__ float sqrtsoftplus_fixed(float x) {
+__device__ __forceinline__ float sqrtsoftplus_fixed(float x) {
 #pragma clang fp contract(off)
   const float e = exp_fixed(-fabsf(x));
   const float s = e / (2.0f + e);
@@ -520,10 +559,10 @@ template <int CTRL>
 __device__ __forceinline__ void arg_step(float& bv, int& bi) {
   const float ov = dpp_f<CTRL>(bv);
   const int oi = dpp_i<CTRL>(bi);
-  if (better(ov, oi, bv, bi)) {
-    bv = ov;
-    bi = oi;
-  }
+  // better(ov, oi, bv, bi) as selects
+  const bool c = oi >= 0 && (bi < 0 || ov > bv || (ov == bv && oi < bi));
+  bv = c ? ov : bv;
+  bi = c ? oi : bi;
 }
 
 template <int VPL>
@@ -531,7 +570,7 @@ __global__ void __launch_bounds__(256) router_topk_row_kernel(
     const float* __restrict__ part, int nsplit, const float* __restrict__ bias,
     const float* __restrict__ expert_bias, int64_t T, int E, int K, int score, int pre_softmax,
     float* __restrict__ logits_out, float* __restrict__ scores_out, float* __restrict__ probs,
-    uint8_t* __restrict__ rmap, int32_t* __restrict__ hist) {
+    uint8_t* __restrict__ rmap, int32_t* __restrict__ hist, int aligned) {
   static_assert(kCountBlock == 16, "one token per 16-lane row");
   __shared__ int cnt[16 * VPL];
   for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;
@@ -540,46 +579,53 @@ __global__ void __launch_bounds__(256) router_topk_row_kernel(
   const int64_t t = static_cast<int64_t>(blockIdx.x) * kCountBlock + threadIdx.x / 16;
   const int e0 = r * VPL;
   if (t < T) {  // uniform over the row
-    bool valid[VPL], taken[VPL];
+    bool valid[VPL];
     float l[VPL], s[VPL], key[VPL];
 #pragma unroll
     for (int j = 0; j < VPL; ++j) {
       valid[j] = e0 + j < E;
-      taken[j] = false;
     }
-    // logits: every partial plane loaded first, summed in plane order, then the bias
-    float pv[kMaxSplit][VPL];
+    // logits: the partial planes summed in plane order, then the bias
     const int64_t row = t * E;
-    const bool vec = (VPL % 4 == 0) && (E % 4 == 0);
+    // groups of 4 experts as vectors: E % 4 == 0 and every array 16-byte
+    // aligned (the map 4-byte aligned)
+    const bool vec = (VPL % 4 == 0) && (E % 4 == 0) && aligned;
+    auto load_plane = [&](int sp, float* v) {
+      const float* src = part + static_cast<int64_t>(sp) * T * E + row;
+      if (vec) {  // E % 4 == 0: a group of 4 is wholly in or out of the row
 #pragma unroll
-    for (int sp = 0; sp < kMaxSplit; ++sp) {
-      if (sp < nsplit) {
-        const float* src = part + static_cast<int64_t>(sp) * T * E + row;
-        if (vec) {  // E % 4 == 0: a group of 4 is wholly in or out of the row
-#pragma unroll
-          for (int j = 0; j < VPL; j += 4) {
-            const float4 q = valid[j] ? *reinterpret_cast<const float4*>(src + e0 + j)
-                                      : make_float4(0.f, 0.f, 0.f, 0.f);
-            pv[sp][j] = q.x;
-            pv[sp][j + 1] = q.y;
-            pv[sp][j + 2] = q.z;
-            pv[sp][j + 3] = q.w;
-          }
-        } else {
-#pragma unroll
-          for (int j = 0; j < VPL; ++j) pv[sp][j] = valid[j] ? src[e0 + j] : 0.f;
+        for (int j = 0; j < VPL; j += 4) {
+          const float4 q = valid[j] ? *reinterpret_cast<const float4*>(src + e0 + j)
+                                    : make_float4(0.f, 0.f, 0.f, 0.f);
+          v[j] = q.x;
+          v[j + 1] = q.y;
+          v[j + 2] = q.z;
+          v[j + 3] = q.w;
         }
+      } else {
+#pragma unroll
+        for (int j = 0; j < VPL; ++j) v[j] = valid[j] ? src[e0 + j] : 0.f;
       }
+    };
+    float acc[VPL];
+    load_plane(0, acc);
+    constexpr int kInFlight = VPL <= 4 ? 7 : VPL <= 8 ? 4 : 2;  // planes loaded together
+    for (int sp0 = 1; sp0 < nsplit; sp0 += kInFlight) {
+      float pv[kInFlight][VPL];
+#pragma unroll
+      for (int u = 0; u < kInFlight; ++u)
+        if (sp0 + u < nsplit) load_plane(sp0 + u, pv[u]);
+#pragma unroll
+      for (int u = 0; u < kInFlight; ++u)
+        if (sp0 + u < nsplit)
+#pragma unroll
+          for (int j = 0; j < VPL; ++j) acc[j] += pv[u][j];
     }
 #pragma unroll
     for (int j = 0; j < VPL; ++j) {
-      float v = pv[0][j];
-#pragma unroll
-      for (int sp = 1; sp < kMaxSplit; ++sp)
-        if (sp < nsplit) v += pv[sp][j];
+      float v = acc[j];
       if (bias && valid[j]) v += bias[e0 + j];
       l[j] = valid[j] ? v : -INFINITY;
-      if (valid[j] && logits_out) logits_out[row + e0 + j] = l[j];
     }
     if (score == MOE_SCORE_SOFTMAX) {
       float m = -INFINITY;
@@ -606,25 +652,31 @@ __global__ void __launch_bounds__(256) router_topk_row_kernel(
         key[j] = (valid[j] && expert_bias) ? s[j] + expert_bias[e0 + j] : s[j];
       }
     }
+    // K rounds of argmax, branch-free: bit j of `tk` marks expert e0 + j taken.
+    // Within a lane experts are scanned in ascending order, so a later equal
+    // key never displaces the earlier one.
     float top_logit = 0.f;
+    uint32_t tk = 0;
     for (int k = 0; k < K; ++k) {
       float bv = 0.f;
       int bi = -1;
 #pragma unroll
-      for (int j = 0; j < VPL; ++j)
-        if (valid[j] && !taken[j] && better(key[j], e0 + j, bv, bi)) {
-          bv = key[j];
-          bi = e0 + j;
-        }
+      for (int j = 0; j < VPL; ++j) {
+        const bool c = valid[j] && !((tk >> j) & 1u) && (bi < 0 || key[j] > bv);
+        bv = c ? key[j] : bv;
+        bi = c ? e0 + j : bi;
+      }
       arg_step<kDppXor1>(bv, bi);
       arg_step<kDppXor2>(bv, bi);
       arg_step<kDppHalfMirror>(bv, bi);
       arg_step<kDppMirror>(bv, bi);
       if (k == 0) top_logit = bv;
-#pragma unroll
-      for (int j = 0; j < VPL; ++j)
-        if (e0 + j == bi) taken[j] = true;
+      const uint32_t d = static_cast<uint32_t>(bi - e0);
+      tk |= d < static_cast<uint32_t>(VPL) ? 1u << d : 0u;
     }
+    bool taken[VPL];
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) taken[j] = (tk >> j) & 1u;
     float p[VPL];
     if (score == MOE_SCORE_SOFTMAX && pre_softmax) {
 #pragma unroll
@@ -648,14 +700,32 @@ __global__ void __launch_bounds__(256) router_topk_row_kernel(
 #pragma unroll
       for (int j = 0; j < VPL; ++j) p[j] = taken[j] ? s[j] / sum : 0.f;
     }
+    if (vec) {  // whole groups of 4: 16-byte stores (4 bytes for the map)
 #pragma unroll
-    for (int j = 0; j < VPL; ++j) {
-      if (!valid[j]) continue;
-      probs[row + e0 + j] = p[j];
-      rmap[row + e0 + j] = taken[j] ? 1 : 0;
-      if (scores_out) scores_out[row + e0 + j] = s[j];
-      if (taken[j]) atomicAdd(&cnt[e0 + j], 1);
+      for (int j = 0; j < VPL; j += 4) {
+        if (!valid[j]) continue;
+        *reinterpret_cast<float4*>(probs + row + e0 + j) = make_float4(p[j], p[j + 1], p[j + 2], p[j + 3]);
+        *reinterpret_cast<uint32_t*>(rmap + row + e0 + j) =
+            (taken[j] ? 1u : 0u) | (taken[j + 1] ? 1u << 8 : 0u) | (taken[j + 2] ? 1u << 16 : 0u) |
+            (taken[j + 3] ? 1u << 24 : 0u);
+        if (logits_out)
+          *reinterpret_cast<float4*>(logits_out + row + e0 + j) = make_float4(l[j], l[j + 1], l[j + 2], l[j + 3]);
+        if (scores_out)
+          *reinterpret_cast<float4*>(scores_out + row + e0 + j) = make_float4(s[j], s[j + 1], s[j + 2], s[j + 3]);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < VPL; ++j) {
+        if (!valid[j]) continue;
+        probs[row + e0 + j] = p[j];
+        rmap[row + e0 + j] = taken[j] ? 1 : 0;
+        if (logits_out) logits_out[row + e0 + j] = l[j];
+        if (scores_out) scores_out[row + e0 + j] = s[j];
+      }
     }
+#pragma unroll
+    for (int j = 0; j < VPL; ++j)
+      if (valid[j] && taken[j]) atomicAdd(&cnt[e0 + j], 1);
   }
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += blockDim.x)
@@ -859,9 +929,12 @@ void launch_topk(int64_t nblk, hipStream_t s, const TopkArgs& a) {
 
 template <int VPL>
 void launch_topk_row(int64_t nblk, hipStream_t s, const TopkArgs& a) {
+  const uintptr_t f = reinterpret_cast<uintptr_t>(a.part) | reinterpret_cast<uintptr_t>(a.logits_out) |
+                      reinterpret_cast<uintptr_t>(a.scores) | reinterpret_cast<uintptr_t>(a.probs);
+  const int aligned = (f % 16 == 0) && (reinterpret_cast<uintptr_t>(a.map) % 4 == 0);
   hipLaunchKernelGGL(router_topk_row_kernel<VPL>, dim3(static_cast<unsigned>(nblk)), dim3(256), 0, s,
                      a.part, a.nsplit, a.bias, a.expert_bias, a.T, a.E, a.K, a.score, a.pre,
-                     a.logits_out, a.scores, a.probs, a.map, a.hist);
+                     a.logits_out, a.scores, a.probs, a.map, a.hist, aligned);
 }
 
 size_t logits_ws_bytes(const moe_route_desc* d) {
@@ -985,15 +1058,15 @@ extern "C" moe_status moe_route(const moe_route_desc* d, const void* x, const fl
                     static_cast<unsigned>(p.gz));
     const uint16_t* xb = static_cast<const uint16_t*>(x);
     const int hh = static_cast<int>(d->h), Ei = static_cast<int>(E);
-    if (p.we == 1)
-      hipLaunchKernelGGL((router_logits_ring<4, 1, 4, 32>), grid, dim3(256), 0, s, xb, w_router, part_ws,
-                         T, hh, Ei, p.kchunk);
-    else if (p.we == 2)
-      hipLaunchKernelGGL((router_logits_ring<2, 2, 4, 32>), grid, dim3(256), 0, s, xb, w_router, part_ws,
-                         T, hh, Ei, p.kchunk);
+    if (p.shape == 0)
+      hipLaunchKernelGGL((router_logits_ring<4, 1, 1, 2, 3, 32>), grid, dim3(256), 0, s, xb, w_router,
+                         part_ws, T, hh, Ei, p.kchunk);
+    else if (p.shape == 1)
+      hipLaunchKernelGGL((router_logits_ring<2, 2, 1, 4, 3, 32>), grid, dim3(256), 0, s, xb, w_router,
+                         part_ws, T, hh, Ei, p.kchunk);
     else
-      hipLaunchKernelGGL((router_logits_ring<1, 4, 4, 32>), grid, dim3(256), 0, s, xb, w_router, part_ws,
-                         T, hh, Ei, p.kchunk);
+      hipLaunchKernelGGL((router_logits_ring<1, 4, 1, 4, 3, 32>), grid, dim3(256), 0, s, xb, w_router,
+                         part_ws, T, hh, Ei, p.kchunk);
     ta.part = part_ws;
     ta.nsplit = p.ksplit;
     ta.bias = b_router;

@@ -126,3 +126,42 @@ def test_route_empty_batch():
     torch.cuda.synchronize()
     assert r["tokens_per_expert"].cpu().tolist() == [0, 0, 0, 0]
     assert r["routing_map"].shape == (0, 4)
+
+
+@pytest.mark.parametrize("T,h,E,K", [(1000, 96, 8, 2), (777, 160, 40, 1), (300, 256, 100, 4),
+                                     (129, 2048, 64, 1), (2000, 512, 200, 8), (65, 4096, 300, 6),
+                                     (33, 32, 3, 2)])
+def test_gating_bf16_ragged_tiles(T, h, E, K):
+    """The MFMA gating linear on shapes that leave ragged token, expert and
+    k tiles (each expert-tile width, several h splits): logits within the
+    fp32 tolerance of the float64 oracle, routing bit-exact given them."""
+    log(f"gating ragged: T={T} h={h} E={E} K={K}")
+    g = torch.Generator().manual_seed(T * 7 + E)
+    x = torch.randn((T, h), generator=g).to(torch.bfloat16)
+    w = torch.randn((E, h), generator=g) / h ** 0.5
+    b = torch.randn((E,), generator=g) * 0.1
+    r = moe.moe_route(x.to(DEV), w.to(DEV), K=K, b_router=b.to(DEV), want_logits=True)
+    torch.cuda.synchronize()
+    logits = r["logits"].cpu().numpy()
+    ref_logits = oracle.router_logits(f64(x), f64(w), f64(b))
+    assert_close(logits, ref_logits, "f32", "logits")
+    ref = oracle.route(logits=logits, K=K)
+    np.testing.assert_array_equal(r["routing_map"].cpu().numpy(), ref["routing_map"])
+    np.testing.assert_array_equal(r["tokens_per_expert"].cpu().numpy(), ref["tokens_per_expert"])
+
+
+def test_route_logits_in_unaligned_matches_aligned():
+    """Logits handed over at an address that is not 16-byte aligned take the
+    scalar path of the top-k kernel and give the same bits."""
+    T, E, K = 70, 64, 4
+    rng = np.random.default_rng(5)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    flat = torch.zeros(T * E + 1, dtype=torch.float32, device=DEV)
+    flat[1:] = torch.from_numpy(logits.ravel()).to(DEV)
+    unaligned = flat[1:].view(T, E)
+    assert unaligned.data_ptr() % 16 != 0
+    a = moe.moe_route(None, None, K=K, logits_in=torch.from_numpy(logits).to(DEV))
+    b = moe.moe_route(None, None, K=K, logits_in=unaligned)
+    torch.cuda.synchronize()
+    for k in ("routing_map", "probs", "tokens_per_expert"):
+        assert torch.equal(a[k], b[k]), k
