@@ -20,8 +20,8 @@ struct Chunk;  // 16 bytes of one row, as fp32 values
 template <>
 struct Chunk<true> {
   static constexpr int N = 8;
-  __device__ static void load(const uint4* p, float* v) {
-    const uint4 u = *p;
+  __device__ static void load(const uint4* p, float* v) { from(*p, v); }
+  __device__ static void from(const uint4 u, float* v) {
     const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -42,21 +42,23 @@ struct Chunk<true> {
 template <>
 struct Chunk<false> {
   static constexpr int N = 4;
-  __device__ static void load(const uint4* p, float* v) {
-    const float4 f = *reinterpret_cast<const float4*>(p);
-    v[0] = f.x;
-    v[1] = f.y;
-    v[2] = f.z;
-    v[3] = f.w;
+  __device__ static void load(const uint4* p, float* v) { from(*p, v); }
+  __device__ static void from(const uint4 u, float* v) {
+    v[0] = __uint_as_float(u.x);
+    v[1] = __uint_as_float(u.y);
+    v[2] = __uint_as_float(u.z);
+    v[3] = __uint_as_float(u.w);
   }
   __device__ static void store(uint4* p, const float* v) {
     *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
   }
 };
 
-constexpr int kUnroll = 4;  // 16-byte chunks per lane in flight
-
-template <bool BF16>
+// A wave's loads for KG of its token's K rows (KU 16-byte chunks per lane of
+// each) are all issued before any is accumulated, so a token keeps KG*KU*1 KB
+// in flight instead of one row's chunks at a time; the accumulation order
+// (ascending k, one fma per element) is unchanged.
+template <bool BF16, int KG, int KU>
 __global__ void __launch_bounds__(256) combine_kernel(const uint4* __restrict__ y,
                                                       const float* __restrict__ pprobs,
                                                       const int32_t* __restrict__ row_id_map,
@@ -77,41 +79,82 @@ __global__ void __launch_bounds__(256) combine_kernel(const uint4* __restrict__ 
       my_p = pprobs[r];
     }
   }
-  for (int c0 = 0; c0 < chunks; c0 += 64 * kUnroll) {
-    float acc[kUnroll][C::N];
+  for (int c0 = 0; c0 < chunks; c0 += 64 * KU) {
+    uint4 sh[KU];
+    if (shared) {
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u)
+      for (int u = 0; u < KU; ++u) {
+        const int c = c0 + u * 64 + lane;
+        if (c < chunks) sh[u] = shared[t * chunks + c];
+      }
+    }
+    float acc[KU][C::N];
+#pragma unroll
+    for (int u = 0; u < KU; ++u)
 #pragma unroll
       for (int i = 0; i < C::N; ++i) acc[u][i] = 0.f;
-    for (int k = 0; k < K; ++k) {
-      const int r = __shfl(my_row, k, 64);
-      if (r < 0) continue;  // wave-uniform
-      const float p = __shfl(my_p, k, 64);
-      const uint4* src = y + static_cast<int64_t>(r) * chunks;
-      float v[kUnroll][C::N];
+    for (int k0 = 0; k0 < K; k0 += KG) {
+      int r[KG];
+      float p[KG];
+      uint4 raw[KG][KU];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int c = c0 + u * 64 + lane;
-        if (c < chunks) C::load(src + c, v[u]);
+      for (int g = 0; g < KG; ++g) {
+        r[g] = __shfl(my_row, min(k0 + g, 63), 64);
+        p[g] = __shfl(my_p, min(k0 + g, 63), 64);
+        if (k0 + g >= K) r[g] = -1;
       }
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u)
+      for (int g = 0; g < KG; ++g) {
+        if (r[g] < 0) continue;  // wave-uniform
+        const uint4* src = y + static_cast<int64_t>(r[g]) * chunks;
 #pragma unroll
-        for (int i = 0; i < C::N; ++i) acc[u][i] = fmaf(p, v[u][i], acc[u][i]);
+        for (int u = 0; u < KU; ++u) {
+          const int c = c0 + u * 64 + lane;
+          if (c < chunks) raw[g][u] = src[c];
+        }
+      }
+#pragma unroll
+      for (int g = 0; g < KG; ++g) {
+        if (r[g] < 0) continue;
+#pragma unroll
+        for (int u = 0; u < KU; ++u) {
+          float v[C::N];
+          C::from(raw[g][u], v);
+#pragma unroll
+          for (int i = 0; i < C::N; ++i) acc[u][i] = fmaf(p[g], v[i], acc[u][i]);
+        }
+      }
     }
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
+    for (int u = 0; u < KU; ++u) {
       const int c = c0 + u * 64 + lane;
       if (c >= chunks) continue;
       if (shared) {
         float sv[C::N];
-        C::load(shared + t * chunks + c, sv);
+        C::from(sh[u], sv);
 #pragma unroll
         for (int i = 0; i < C::N; ++i) acc[u][i] += sv[i];
       }
       C::store(out + t * chunks + c, acc[u]);
     }
   }
+}
+
+template <bool BF16, int KG, int KU>
+void launch_combine(dim3 grid, hipStream_t s, const void* y, const float* pp, const int32_t* rim,
+                    int64_t T, int chunks, int K, int64_t max_rows, const void* shared, void* out) {
+  hipLaunchKernelGGL((combine_kernel<BF16, KG, KU>), grid, dim3(256), 0, s,
+                     static_cast<const uint4*>(y), pp, rim, T, chunks, K, max_rows,
+                     static_cast<const uint4*>(shared), static_cast<uint4*>(out));
+}
+
+template <bool BF16>
+void dispatch_combine(dim3 grid, hipStream_t s, const void* y, const float* pp, const int32_t* rim,
+                      int64_t T, int chunks, int K, int64_t max_rows, const void* shared, void* out) {
+  if (K <= 1) launch_combine<BF16, 1, 8>(grid, s, y, pp, rim, T, chunks, K, max_rows, shared, out);
+  else if (K <= 2) launch_combine<BF16, 2, 4>(grid, s, y, pp, rim, T, chunks, K, max_rows, shared, out);
+  else if (K <= 4) launch_combine<BF16, 4, 4>(grid, s, y, pp, rim, T, chunks, K, max_rows, shared, out);
+  else launch_combine<BF16, 8, 2>(grid, s, y, pp, rim, T, chunks, K, max_rows, shared, out);
 }
 
 }  // namespace
@@ -136,15 +179,12 @@ extern "C" moe_status moe_combine(int64_t T, int64_t h, int64_t K, int32_t dtype
   const int esize = dtype == MOE_BF16 ? 2 : 4;
   const int chunks = static_cast<int>(h * esize / 16);
   const dim3 grid(static_cast<unsigned>(ceil_div(T, 4)));
+  const int Ki = static_cast<int>(K);
   if (dtype == MOE_BF16)
-    hipLaunchKernelGGL(combine_kernel<true>, grid, dim3(256), 0, s,
-                       static_cast<const uint4*>(expert_out), permuted_probs, row_id_map, T, chunks,
-                       static_cast<int>(K), max_rows, static_cast<const uint4*>(shared_out),
-                       static_cast<uint4*>(out));
+    dispatch_combine<true>(grid, s, expert_out, permuted_probs, row_id_map, T, chunks, Ki, max_rows,
+                           shared_out, out);
   else
-    hipLaunchKernelGGL(combine_kernel<false>, grid, dim3(256), 0, s,
-                       static_cast<const uint4*>(expert_out), permuted_probs, row_id_map, T, chunks,
-                       static_cast<int>(K), max_rows, static_cast<const uint4*>(shared_out),
-                       static_cast<uint4*>(out));
+    dispatch_combine<false>(grid, s, expert_out, permuted_probs, row_id_map, T, chunks, Ki, max_rows,
+                            shared_out, out);
   return check_launch("moe_combine");
 }

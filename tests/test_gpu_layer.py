@@ -154,3 +154,28 @@ def test_layer_graph_capture_replays_match_eager():
         torch.cuda.synchronize()
         assert torch.equal(res["out"], eager["out"]), f"replay with seed {seed}"
         assert torch.equal(res["routing_map"], eager["routing_map"])
+
+
+@pytest.mark.parametrize("name,n_tok", [("switch", 16), ("dsv3", 3)])
+def test_layer_bench_configuration_full_size_sampled(name, n_tok):
+    """The layer object exactly as the benchmark runs it (gathering FC1,
+    shared expert on a second stream) against the oracle on sampled tokens
+    of the full-size layer."""
+    from combine_router_gating_amd.layer import MoELayerForward
+    cfg = datagen.CONFIGS[name]
+    log(f"layer bench configuration: {cfg}")
+    inp = datagen.make_inputs(cfg, seed=1, device=DEV)
+    layer = MoELayerForward(inp, K=cfg.K, score=cfg.score, pre_softmax=cfg.pre_softmax,
+                            capacity_factor=cfg.capacity_factor, min_capacity=cfg.min_capacity,
+                            gather=True, overlap_shared=True)
+    out = layer.forward()
+    torch.cuda.synchronize()
+    logits = layer.logits.cpu().numpy()
+    eb = inp["expert_bias"].cpu().numpy() if "expert_bias" in inp else None
+    ref = routing_ref(cfg, logits, eb)
+    np.testing.assert_array_equal(layer.routing_map.cpu().numpy(), ref["routing_map"])
+    toks = list(np.random.default_rng(3).choice(cfg.T, size=n_tok, replace=False))
+    exp = oracle.token_outputs(toks, f64(inp["x"]), ref["routing_map"], ref["probs"],
+                               expert_weights_from(inp), cfg.dtype, shared_weights_from(inp))
+    assert_close(f64(out)[toks], exp, cfg.dtype, f"out[{name}]")
+
