@@ -17,10 +17,12 @@ is unchanged since the counters were taken.  After the timed region, a second pa
 last-level caches flushed first (a 512 MiB write before every step; the
 flush is outside the events) and reports it as "cold".
 
-Layer options (on by default, --no-gather / --no-overlap to turn off): the
-permute writes no row copies and FC1 gathers token rows through
-sorted_token; the shared expert (when the layer has one) runs on a second
-stream, joined before the combine.  With the overlap on, main-stream stage
+Layer options (on by default, --no-gather / --no-overlap /
+--no-fuse-route-permute to turn off): the permute writes no row copies and
+FC1 gathers token rows through sorted_token; the shared expert (when the
+layer has one) runs on a second stream, joined before the combine; route and
+permute run as one library call (moe_route_permute), which reuses the
+router's counting pass for the permute.  With the overlap on, main-stream stage
 times include contention with the shared expert.
 """
 from __future__ import annotations
@@ -42,7 +44,8 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 MFMA_FP8_PEAK_TFLOPS = 5000.0   # MI355X dense fp8 MFMA, published
 FP32_PEAK_TFLOPS = 157.3        # MI355X fp32 (used for fp32 layers)
 KERNEL_SOURCES = {  # stage -> source file that holds its kernel
-    "route": "route.hip", "permute": "permute.hip", "fc1": "gmm.hip", "fc2": "gmm.hip",
+    "route": "route.hip", "permute": "permute.hip", "route_permute": "route.hip",
+    "fc1": "gmm.hip", "fc2": "gmm.hip",
     "shared": "gmm.hip", "combine": "combine.hip", "quantize": "mx.hip",
 }
 MX_SOURCES = {"fc1": "gmm_mx.hip", "fc2": "gmm_mx.hip", "shared": "gmm_mx.hip"}
@@ -62,6 +65,8 @@ def parse():
                    help="run one plain device copy of this size first (counter calibration)")
     p.add_argument("--no-gather", action="store_true", help="materialise permuted_x")
     p.add_argument("--no-overlap", action="store_true", help="shared expert on the main stream")
+    p.add_argument("--no-fuse-route-permute", action="store_true",
+                   help="route and permute as two library calls")
     p.add_argument("--no-cold", action="store_true", help="skip the cache-flushed pass")
     p.add_argument("--precision", default="bf16", choices=("bf16", "mxfp8"),
                    help="expert GEMM operands (mxfp8: OCP MX blocks of 32, E4M3)")
@@ -116,6 +121,9 @@ def stage_work(cfg, n, T, fs, gather=False, mx=False):
     }
     if fs:
         w["shared"] = (3 * h * fs * b + 2 * T * h * b + 2 * T * fs * b, 6.0 * T * h * fs)
+    # route and permute as one call: the map and probs are written once and
+    # read back by the scatter
+    w["route_permute"] = (w["route"][0] + w["permute"][0], w["route"][1])
     if mx:
         q = 1.0 + 1.0 / 32
         w["quantize"] = (T * h * b + T * h * q, 0.0)
@@ -212,7 +220,8 @@ def main():
     layer = MoELayerForward(inp, K=cfg.K, score=cfg.score, pre_softmax=cfg.pre_softmax,
                             capacity_factor=cfg.capacity_factor, min_capacity=cfg.min_capacity,
                             gather=gather, overlap_shared=not args.no_overlap,
-                            precision=args.precision)
+                            precision=args.precision,
+                            fuse_route_permute=not args.no_fuse_route_permute)
     for _ in range(args.warmup):
         layer.forward()
     torch.cuda.synchronize()
@@ -338,6 +347,7 @@ def main():
                    "tokens": cfg.T, "routed_rows": N, "dropped": cfg.T * cfg.K - N,
                    "parallelism": "single GPU, EP=1",
                    "gather_fc1": layer.gather, "shared_overlap": layer.overlap_shared,
+                   "route_permute_fused": layer.fused,
                    "expert_precision": args.precision},
         "forward_ms": {"mean": sum(fwd) / len(fwd), "p10": pct(fwd, 10), "p50": pct(fwd, 50),
                        "p90": pct(fwd, 90)},

@@ -17,6 +17,7 @@ from .moe import (
     moe_permute,
     moe_route,
     moe_route_capacity,
+    moe_route_permute,
     moe_router_aux_loss,
     moe_update_expert_bias,
     route_desc,
@@ -28,6 +29,6 @@ __all__ = [
     "moe_combine", "moe_forward", "moe_grouped_fc1_swiglu", "moe_grouped_fc1_swiglu_gather",
     "moe_grouped_fc2", "moe_grouped_fc1_swiglu_mxfp8", "moe_grouped_fc2_mxfp8", "moe_mxfp8_quantize",
     "moe_mxfp8_quantize_weight", "moe_grouped_mlp",
-    "moe_max_rows", "moe_permute", "moe_route", "moe_route_capacity", "route_desc", "LIB_PATH",
+    "moe_max_rows", "moe_permute", "moe_route", "moe_route_capacity", "moe_route_permute", "route_desc", "LIB_PATH",
     "MoEError", "load",
 ]

@@ -42,6 +42,10 @@ SIGNATURES = {
     "moe_accumulate_tokens_per_expert": (c_i32, [c_i64, c_vp, c_vp, c_vp]),
     "moe_update_expert_bias": (c_i32, [c_i64, c_vp, c_vp, c_f32, c_i32, c_vp]),
     "moe_permute_workspace_size": (c_sz, [c_i64, c_i64]),
+    "moe_route_permute_workspace_size": (c_sz, [ctypes.POINTER(RouteDesc)]),
+    "moe_route_permute": (c_i32, [ctypes.POINTER(RouteDesc), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                  c_vp, c_vp, c_vp, c_vp, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                  c_vp, c_sz, c_vp]),
     "moe_permute": (c_i32, [c_i64, c_i64, c_i64, c_i64, c_i32, c_vp, c_vp, c_vp, c_i64, c_vp,
                             c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "moe_grouped_mlp": (c_i32, [c_i64, c_i64, c_i64, c_i64, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp,

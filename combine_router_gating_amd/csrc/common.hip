@@ -97,7 +97,7 @@ __global__ void __launch_bounds__(256) count_scan_kernel(const int32_t* __restri
   __syncthreads();
   for (int b = b0; b < b1; ++b) {
     const int c = h[b];
-    blkoff[static_cast<int64_t>(b) * E + e] = static_cast<int32_t>(run);
+    blkoff[static_cast<int64_t>(b) * E + e] = static_cast<int32_t>(cap >= 0 && run > cap ? cap : run);
     if (drop && run >= cap) atomicMin(&s_past, b);
     if (drop && run < cap && run + c > cap) {
       const int64_t t0 = static_cast<int64_t>(b) * kCountBlock;

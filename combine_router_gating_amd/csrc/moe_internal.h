@@ -30,17 +30,30 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // hist[e*nblk + b] = number of tokens of block b (kCountBlock tokens) routed
 //                    to e (expert-major, so that the per-expert scan reads a
 //                    contiguous run)
-// blkoff[b*E + e]  = number of tokens routed to e in blocks before b
+// blkoff[b*E + e]  = number of tokens routed to e in blocks before b (with a
+//                    capacity: of those kept, min(that number, cap))
 size_t count_ws_bytes(int64_t T, int64_t E);  // hist + blkoff + kept[E]
 // Fill n int32 with v by a kernel (graph-capture friendly, no memset node).
 void launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);
 void launch_block_hist(const uint8_t* map, int64_t T, int64_t E, int32_t* hist, hipStream_t s);
-// One workgroup per expert: blkoff = exclusive prefix over blocks,
-// kept[e] = min(total, cap) (cap < 0: total).  With cap >= 0 and rmap/probs
-// ([T,E]), also drops the entries ranked >= cap (earliest tokens kept).
+// Workgroups per expert and chunk of blocks: blkoff = exclusive prefix over
+// blocks (min(prefix, cap) when cap >= 0), kept[e] = min(total, cap) (cap <
+// 0: total).  With cap >= 0 and rmap/probs ([T,E]), also drops the entries
+// ranked >= cap (earliest tokens kept), so that blkoff and kept then count
+// the final map.
 void launch_count_scan(const int32_t* hist, int64_t nblk, int64_t E, int64_t cap, int32_t* blkoff,
                        int32_t* kept, hipStream_t s, int64_t T = 0, float* probs = nullptr,
                        uint8_t* rmap = nullptr);
+
+// moe_permute's body.  With given_blkoff (per-block exclusive offsets of each
+// expert's entries, block-major [nblk, E]) and given_totals (entries per
+// expert), the counting passes are skipped and the workspace is not used.
+moe_status permute_impl(int64_t T, int64_t h, int64_t E, int64_t K, int32_t dtype, const void* x,
+                        const uint8_t* routing_map, const float* probs, int64_t max_rows,
+                        void* permuted_x, float* permuted_probs, int32_t* sorted_token,
+                        int32_t* row_id_map, int32_t* expert_offsets, void* workspace,
+                        size_t workspace_bytes, hipStream_t s, const int32_t* given_blkoff,
+                        const int32_t* given_totals);
 
 // ---------------------------------------------------------------- device helpers
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {

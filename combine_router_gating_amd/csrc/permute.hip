@@ -170,12 +170,14 @@ extern "C" size_t moe_permute_workspace_size(int64_t T, int64_t E) {
   return count_ws_bytes(T, E);
 }
 
-extern "C" moe_status moe_permute(int64_t T, int64_t h, int64_t E, int64_t K, int32_t dtype,
-                                  const void* x, const uint8_t* routing_map, const float* probs,
-                                  int64_t max_rows, void* permuted_x, float* permuted_probs,
-                                  int32_t* sorted_token, int32_t* row_id_map,
-                                  int32_t* expert_offsets, void* workspace, size_t workspace_bytes,
-                                  void* stream) {
+namespace moe {
+
+moe_status permute_impl(int64_t T, int64_t h, int64_t E, int64_t K, int32_t dtype, const void* x,
+                        const uint8_t* routing_map, const float* probs, int64_t max_rows,
+                        void* permuted_x, float* permuted_probs, int32_t* sorted_token,
+                        int32_t* row_id_map, int32_t* expert_offsets, void* workspace,
+                        size_t workspace_bytes, hipStream_t s, const int32_t* given_blkoff,
+                        const int32_t* given_totals) {
   MOE_REQUIRE(T >= 0 && T < (int64_t(1) << 31), MOE_ERR_ARG, "moe_permute: T out of range");
   MOE_REQUIRE(E >= 1 && E <= kMaxExperts, MOE_ERR_ARG, "moe_permute: E=%lld not in [1,%lld]",
               (long long)E, (long long)kMaxExperts);
@@ -188,7 +190,6 @@ extern "C" moe_status moe_permute(int64_t T, int64_t h, int64_t E, int64_t K, in
               "moe_permute: max_rows out of range");
   MOE_REQUIRE(T * E < (int64_t(1) << 31), MOE_ERR_UNSUPPORTED, "moe_permute: T*E too large");
   MOE_REQUIRE(expert_offsets, MOE_ERR_ARG, "moe_permute: expert_offsets is required");
-  const hipStream_t s = as_stream(stream);
   if (T == 0) {  // every other tensor is empty and may be NULL
     launch_fill_i32(expert_offsets, E + 1, 0, s);
     return check_launch("moe_permute(T=0)");
@@ -198,15 +199,21 @@ extern "C" moe_status moe_permute(int64_t T, int64_t h, int64_t E, int64_t K, in
   MOE_REQUIRE(x || !permuted_x, MOE_ERR_ARG, "moe_permute: x is NULL but permuted_x is not");
   MOE_REQUIRE(max_rows == 0 || (permuted_probs && sorted_token), MOE_ERR_ARG,
               "moe_permute: NULL output with max_rows > 0");
-  const size_t need = moe_permute_workspace_size(T, E);
-  MOE_REQUIRE(workspace && workspace_bytes >= need, MOE_ERR_WORKSPACE,
-              "moe_permute: workspace of %zu bytes given, %zu needed", workspace_bytes, need);
   const int64_t nblk = ceil_div(T, kCountBlock);
-  int32_t* hist = static_cast<int32_t*>(workspace);
-  int32_t* blkoff = hist + align_up(static_cast<size_t>(nblk * E) * sizeof(int32_t), 256) / 4;
-  int32_t* totals = blkoff + align_up(static_cast<size_t>(nblk * E) * sizeof(int32_t), 256) / 4;
-  launch_block_hist(routing_map, T, E, hist, s);
-  launch_count_scan(hist, nblk, E, -1, blkoff, totals, s);
+  const int32_t* blkoff = given_blkoff;
+  const int32_t* totals = given_totals;
+  if (!blkoff) {
+    const size_t need = moe_permute_workspace_size(T, E);
+    MOE_REQUIRE(workspace && workspace_bytes >= need, MOE_ERR_WORKSPACE,
+                "moe_permute: workspace of %zu bytes given, %zu needed", workspace_bytes, need);
+    int32_t* hist = static_cast<int32_t*>(workspace);
+    int32_t* off = hist + align_up(static_cast<size_t>(nblk * E) * sizeof(int32_t), 256) / 4;
+    int32_t* tot = off + align_up(static_cast<size_t>(nblk * E) * sizeof(int32_t), 256) / 4;
+    launch_block_hist(routing_map, T, E, hist, s);
+    launch_count_scan(hist, nblk, E, -1, off, tot, s);
+    blkoff = off;
+    totals = tot;
+  }
   const int esize = dtype == MOE_BF16 ? 2 : 4;
   const int chunks = static_cast<int>(h * esize / 16);
   hipLaunchKernelGGL(permute_scatter_kernel, dim3(static_cast<unsigned>(nblk)), dim3(256), 0, s,
@@ -214,4 +221,17 @@ extern "C" moe_status moe_permute(int64_t T, int64_t h, int64_t E, int64_t K, in
                      static_cast<int>(K), chunks, blkoff, totals, expert_offsets, max_rows,
                      static_cast<uint4*>(permuted_x), permuted_probs, sorted_token, row_id_map);
   return check_launch("moe_permute");
+}
+
+}  // namespace moe
+
+extern "C" moe_status moe_permute(int64_t T, int64_t h, int64_t E, int64_t K, int32_t dtype,
+                                  const void* x, const uint8_t* routing_map, const float* probs,
+                                  int64_t max_rows, void* permuted_x, float* permuted_probs,
+                                  int32_t* sorted_token, int32_t* row_id_map,
+                                  int32_t* expert_offsets, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  return permute_impl(T, h, E, K, dtype, x, routing_map, probs, max_rows, permuted_x,
+                      permuted_probs, sorted_token, row_id_map, expert_offsets, workspace,
+                      workspace_bytes, as_stream(stream), nullptr, nullptr);
 }

@@ -1006,17 +1006,23 @@ extern "C" int64_t moe_max_rows(const moe_route_desc* d) {
   return cap < 0 ? tk : std::min(tk, cap * d->E);
 }
 
-extern "C" moe_status moe_route(const moe_route_desc* d, const void* x, const float* w_router,
-                                const float* b_router, const float* expert_bias,
-                                const float* logits_in, float* logits_out, float* scores_out,
-                                float* probs, uint8_t* routing_map, int32_t* tokens_per_expert,
-                                void* workspace, size_t workspace_bytes, void* stream) {
+namespace moe {
+namespace {
+
+// moe_route's body.  *counted (if given) is set to the per-block offsets of
+// the final map (block-major [nblk, E], the counting pass's blkoff) when the
+// path leaves them there (position policy or nothing dropped), else NULL.
+moe_status route_impl(const moe_route_desc* d, const void* x, const float* w_router,
+                      const float* b_router, const float* expert_bias, const float* logits_in,
+                      float* logits_out, float* scores_out, float* probs, uint8_t* routing_map,
+                      int32_t* tokens_per_expert, void* workspace, size_t workspace_bytes,
+                      hipStream_t s, const int32_t** counted) {
+  if (counted) *counted = nullptr;
   moe_status st = validate(d);
   if (st != MOE_OK) return st;
   MOE_REQUIRE(tokens_per_expert, MOE_ERR_ARG, "moe_route: tokens_per_expert is required");
   MOE_REQUIRE(expert_bias == nullptr || d->score != MOE_SCORE_SOFTMAX, MOE_ERR_UNSUPPORTED,
               "moe_route: expert_bias is defined for sigmoid and sqrtsoftplus scoring only");
-  const hipStream_t s = as_stream(stream);
   const int64_t T = d->T, E = d->E;
   if (T == 0) {  // [0,E] tensors may be NULL
     launch_fill_i32(tokens_per_expert, E, 0, s);
@@ -1100,6 +1106,7 @@ extern "C" moe_status moe_route(const moe_route_desc* d, const void* x, const fl
     // per-expert capacity mask (probs policy, or padding to capacity)
     if (raw >= T && !d->pad_to_capacity) {
       launch_count_scan(hist, nblk, E, -1, blkoff, tokens_per_expert, s);  // nothing dropped
+      if (counted) *counted = blkoff;
     } else {
       hipLaunchKernelGGL(router_capacity_kernel, dim3(static_cast<unsigned>(E)), dim3(256), 0, s, T,
                          static_cast<int>(E), std::min(raw, T), d->drop_policy,
@@ -1111,8 +1118,55 @@ extern "C" moe_status moe_route(const moe_route_desc* d, const void* x, const fl
   // entries ranked >= capacity
   const int64_t cap = capacity_of(d);
   launch_count_scan(hist, nblk, E, cap, blkoff, tokens_per_expert, s, T, probs, routing_map);
+  if (counted) *counted = blkoff;
   return check_launch("moe_route");
 }
+
+}  // namespace
+}  // namespace moe
+
+extern "C" moe_status moe_route(const moe_route_desc* d, const void* x, const float* w_router,
+                                const float* b_router, const float* expert_bias,
+                                const float* logits_in, float* logits_out, float* scores_out,
+                                float* probs, uint8_t* routing_map, int32_t* tokens_per_expert,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  return route_impl(d, x, w_router, b_router, expert_bias, logits_in, logits_out, scores_out, probs,
+                    routing_map, tokens_per_expert, workspace, workspace_bytes, as_stream(stream),
+                    nullptr);
+}
+
+extern "C" size_t moe_route_permute_workspace_size(const moe_route_desc* d) {
+  if (validate(d) != MOE_OK || d->T == 0) return 0;
+  return align_up(moe_route_workspace_size(d), 256) + moe_permute_workspace_size(d->T, d->E);
+}
+
+extern "C" moe_status moe_route_permute(const moe_route_desc* d, const void* x, const float* w_router,
+                                        const float* b_router, const float* expert_bias,
+                                        const float* logits_in, float* logits_out,
+                                        float* scores_out, float* probs, uint8_t* routing_map,
+                                        int32_t* tokens_per_expert, int64_t max_rows,
+                                        void* permuted_x, float* permuted_probs,
+                                        int32_t* sorted_token, int32_t* row_id_map,
+                                        int32_t* expert_offsets, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
+  moe_status st = validate(d);
+  if (st != MOE_OK) return st;
+  const size_t route_bytes = align_up(moe_route_workspace_size(d), 256);
+  const size_t need = moe_route_permute_workspace_size(d);
+  MOE_REQUIRE(d->T == 0 || (workspace && workspace_bytes >= need), MOE_ERR_WORKSPACE,
+              "moe_route_permute: workspace of %zu bytes given, %zu needed", workspace_bytes, need);
+  const hipStream_t s = as_stream(stream);
+  const int32_t* counted = nullptr;
+  st = route_impl(d, x, w_router, b_router, expert_bias, logits_in, logits_out, scores_out, probs,
+                  routing_map, tokens_per_expert, workspace, route_bytes, s, &counted);
+  if (st != MOE_OK) return st;
+  char* pws = d->T == 0 ? nullptr : static_cast<char*>(workspace) + route_bytes;
+  return permute_impl(d->T, d->h, d->E, d->K, d->x_dtype, x, routing_map, probs, max_rows,
+                      permuted_x, permuted_probs, sorted_token, row_id_map, expert_offsets, pws,
+                      d->T == 0 ? 0 : workspace_bytes - route_bytes, s, counted,
+                      counted ? tokens_per_expert : nullptr);
+}
+
 
 extern "C" size_t moe_aux_loss_workspace_size(int64_t T, int64_t E) {
   if (T <= 0 || E <= 0 || E > kMaxExperts) return 0;

@@ -7,7 +7,10 @@ Options: `gather` skips the permuted copy of x (the permute writes indices
 and probs only, and FC1 reads token rows through sorted_token);
 `overlap_shared` runs the shared expert on a second stream (default
 priority) from the start of the forward, joined before the combine;
-`precision="mxfp8"` runs the expert GEMMs (routed and shared) on MXFP8
+`fuse_route_permute` (on by default) runs route and permute as one library
+call (moe_route_permute, one "route_permute" stage), which reuses the
+router's per-block counts for the permute; the outputs are bitwise those of
+the two calls.  `precision="mxfp8"` runs the expert GEMMs (routed and shared) on MXFP8
 operands: the weights are quantised once here, x once per forward (the
 router still reads the bf16 x), FC1 writes MXFP8 act, FC2 bf16 outputs."""
 from __future__ import annotations
@@ -29,12 +32,13 @@ def _p(t: Optional[torch.Tensor]):
 class MoELayerForward:
     """route -> permute -> FC1+SwiGLU -> FC2 (-> shared expert) -> combine."""
 
-    STAGES = ("quantize", "route", "permute", "fc1", "fc2", "shared", "combine")
+    STAGES = ("quantize", "route", "permute", "route_permute", "fc1", "fc2", "shared", "combine")
 
     def __init__(self, inp: Dict[str, torch.Tensor], *, K: int, score: str = "softmax",
                  pre_softmax: bool = True, capacity_factor: float = 0.0, min_capacity: int = 0,
                  drop_policy: str = "position", pad_to_capacity: bool = False,
-                 gather: bool = False, overlap_shared: bool = False, precision: str = "bf16"):
+                 gather: bool = False, overlap_shared: bool = False, precision: str = "bf16",
+                 fuse_route_permute: bool = True):
         self.lib = _lib.load()
         self.inp = inp
         x = _need(inp["x"], "x")
@@ -53,7 +57,10 @@ class MoELayerForward:
         self.routing_map = e((T, E), dtype=torch.uint8, device=dev)
         self.tokens_per_expert = e((E,), dtype=torch.int32, device=dev)
         self.logits = e((T, E), dtype=torch.float32, device=dev)
-        self.route_ws_bytes = int(self.lib.moe_route_workspace_size(ctypes.byref(self.desc)))
+        self.fused = bool(fuse_route_permute)
+        ws_fn = (self.lib.moe_route_permute_workspace_size if self.fused
+                 else self.lib.moe_route_workspace_size)
+        self.route_ws_bytes = int(ws_fn(ctypes.byref(self.desc)))
         self.route_ws = e((max(self.route_ws_bytes, 1),), dtype=torch.uint8, device=dev)
         if precision not in ("bf16", "mxfp8"):
             raise ValueError(f"unknown precision {precision!r}")
@@ -120,6 +127,16 @@ class MoELayerForward:
             ctypes.byref(self.desc), _p(i["x"]), _p(i["w_router"]), _p(i.get("b_router")),
             _p(i.get("expert_bias")), None, _p(self.logits), None, _p(self.probs),
             _p(self.routing_map), _p(self.tokens_per_expert), _p(self.route_ws),
+            self.route_ws_bytes, self._stream()))
+
+    def route_permute(self):
+        i = self.inp
+        check("moe_route_permute", self.lib.moe_route_permute(
+            ctypes.byref(self.desc), _p(i["x"]), _p(i["w_router"]), _p(i.get("b_router")),
+            _p(i.get("expert_bias")), None, _p(self.logits), None, _p(self.probs),
+            _p(self.routing_map), _p(self.tokens_per_expert), self.max_rows,
+            _p(self.permuted_x), _p(self.permuted_probs), _p(self.sorted_token),
+            _p(self.row_id_map), _p(self.expert_offsets), _p(self.route_ws),
             self.route_ws_bytes, self._stream()))
 
     def permute(self):
@@ -198,6 +215,8 @@ class MoELayerForward:
             if n == "quantize" and not self.mx:
                 continue
             if n == "shared" and (not self.shared or self.overlap_shared):
+                continue
+            if (n in ("route", "permute") and self.fused) or (n == "route_permute" and not self.fused):
                 continue
             keep.append(n)
         return keep

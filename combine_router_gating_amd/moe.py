@@ -121,6 +121,69 @@ def moe_route(x: Optional[torch.Tensor], w_router: Optional[torch.Tensor], *, K:
     return out
 
 
+def moe_route_permute(x: Optional[torch.Tensor], w_router: Optional[torch.Tensor], *, K: int,
+                      b_router: Optional[torch.Tensor] = None,
+                      expert_bias: Optional[torch.Tensor] = None, score: str = "softmax",
+                      pre_softmax: bool = True, capacity_factor: float = 0.0, min_capacity: int = 0,
+                      drop_policy: str = "position", pad_to_capacity: bool = False,
+                      logits_in: Optional[torch.Tensor] = None, want_logits: bool = False,
+                      want_scores: bool = False, copy_rows: bool = True,
+                      h: Optional[int] = None) -> Dict[str, torch.Tensor]:
+    """moe_route then moe_permute of its outputs in one library call (the
+    permute reuses the router's counting); the union of both results."""
+    lib = _lib.load()
+    if logits_in is not None:
+        _need(logits_in, "logits_in", torch.float32)
+        T_, E = logits_in.shape
+        dev = logits_in.device
+        h_ = h if h is not None else (x.shape[1] if x is not None else 8)
+        xdt = x.dtype if x is not None else torch.float32
+    else:
+        _need(x, "x")
+        _need(w_router, "w_router", torch.float32)
+        T_, h_ = x.shape
+        E = w_router.shape[0]
+        _need(w_router, "w_router", torch.float32, (E, h_))
+        dev = x.device
+        xdt = x.dtype
+    if copy_rows:
+        _need(x, "x")
+    if b_router is not None:
+        _need(b_router, "b_router", torch.float32, (E,))
+    if expert_bias is not None:
+        _need(expert_bias, "expert_bias", torch.float32, (E,))
+    desc = route_desc(T_, h_, E, K, xdt, score, pre_softmax, capacity_factor, min_capacity,
+                      drop_policy, pad_to_capacity)
+    rows = max(moe_max_rows(desc), 0)
+    e = torch.empty
+    out = {"probs": e((T_, E), dtype=torch.float32, device=dev),
+           "routing_map": e((T_, E), dtype=torch.uint8, device=dev),
+           "tokens_per_expert": e((E,), dtype=torch.int32, device=dev),
+           "permuted_x": e((rows, h_), dtype=xdt, device=dev) if copy_rows else None,
+           "permuted_probs": e((rows,), dtype=torch.float32, device=dev),
+           "sorted_token": e((rows,), dtype=torch.int32, device=dev),
+           "row_id_map": e((T_, K), dtype=torch.int32, device=dev),
+           "expert_offsets": e((E + 1,), dtype=torch.int32, device=dev),
+           "max_rows": rows, "capacity": moe_route_capacity(desc)}
+    logits = e((T_, E), dtype=torch.float32, device=dev) if want_logits else None
+    scores = e((T_, E), dtype=torch.float32, device=dev) if want_scores else None
+    ws_bytes = int(lib.moe_route_permute_workspace_size(ctypes.byref(desc)))
+    ws = e((max(ws_bytes, 1),), dtype=torch.uint8, device=dev)
+    st = lib.moe_route_permute(
+        ctypes.byref(desc), _ptr(x) if (logits_in is None or copy_rows) else None,
+        _ptr(w_router) if logits_in is None else None, _ptr(b_router), _ptr(expert_bias),
+        _ptr(logits_in), _ptr(logits), _ptr(scores), _ptr(out["probs"]), _ptr(out["routing_map"]),
+        _ptr(out["tokens_per_expert"]), rows, _ptr(out["permuted_x"]), _ptr(out["permuted_probs"]),
+        _ptr(out["sorted_token"]), _ptr(out["row_id_map"]), _ptr(out["expert_offsets"]), _ptr(ws),
+        ws_bytes, _stream())
+    check("moe_route_permute", st)
+    if logits is not None:
+        out["logits"] = logits
+    if scores is not None:
+        out["scores"] = scores
+    return out
+
+
 def moe_router_aux_loss(scores: torch.Tensor, tokens_per_expert: torch.Tensor, *, K: int,
                         score: str = "softmax") -> torch.Tensor:
     """Forward value of the load-balancing loss, E * sum_e f_e * P_e (fp32 [1])."""

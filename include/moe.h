@@ -218,6 +218,36 @@ moe_status moe_permute(int64_t T, int64_t h, int64_t E, int64_t K, int32_t dtype
                        int32_t* row_id_map, int32_t* expert_offsets, void* workspace,
                        size_t workspace_bytes, void* stream);
 
+/* Bytes of device workspace moe_route_permute needs (0 when T == 0 or the
+ * descriptor is invalid). */
+size_t moe_route_permute_workspace_size(const moe_route_desc* d);
+
+/*
+ * moe_route_permute — moe_route, then moe_permute of its routing_map and
+ * probs (with h = d->h, E = d->E, K = d->K, dtype = d->x_dtype), in one
+ * call: the router and the dispatch preprocess of [MC] §2 back to back.
+ * Every output is bitwise what the two calls write.  The permute's row of
+ * an entry needs, per token block and expert, the count of that expert's
+ * kept entries in earlier blocks; the router's counting pass already has
+ * them (under the position policy, or when nothing is dropped, an expert
+ * keeps its earliest entries, so the kept count before a block is
+ * min(routed count before it, capacity)), so the permute's own counting
+ * passes are skipped there (two kernels fewer).  The probs policy and
+ * padding to capacity count the final map again.
+ *   route arguments    as moe_route
+ *   permute arguments  as moe_permute (x may be NULL when logits_in is given
+ *                      and permuted_x is NULL)
+ *   workspace          moe_route_permute_workspace_size(d) bytes
+ * Errors: those of moe_route and moe_permute.
+ */
+moe_status moe_route_permute(const moe_route_desc* d, const void* x, const float* w_router,
+                             const float* b_router, const float* expert_bias,
+                             const float* logits_in, float* logits_out, float* scores_out,
+                             float* probs, uint8_t* routing_map, int32_t* tokens_per_expert,
+                             int64_t max_rows, void* permuted_x, float* permuted_probs,
+                             int32_t* sorted_token, int32_t* row_id_map, int32_t* expert_offsets,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------------------
  * Experts: SwiGLU MLP of every local expert as one grouped GEMM per layer.
  * [MC] §10 (all local experts' MLPs run as a grouped GEMM instead of a loop

@@ -78,8 +78,10 @@ def test_layer_options_give_identical_outputs(name):
     kw = dict(K=cfg.K, score=cfg.score, pre_softmax=cfg.pre_softmax,
               capacity_factor=cfg.capacity_factor, min_capacity=cfg.min_capacity)
     outs = []
-    for gather, overlap in ((False, False), (True, False), (True, True), (False, True)):
-        layer = MoELayerForward(inp, gather=gather, overlap_shared=overlap, **kw)
+    for gather, overlap, fuse in ((False, False, False), (True, False, True), (True, True, True),
+                                  (False, True, False), (False, False, True)):
+        layer = MoELayerForward(inp, gather=gather, overlap_shared=overlap,
+                                fuse_route_permute=fuse, **kw)
         for _ in range(2):
             out = layer.forward()
         torch.cuda.synchronize()

@@ -119,3 +119,38 @@ def test_permute_empty_batch():
     torch.cuda.synchronize()
     assert pm["expert_offsets"].cpu().tolist() == [0] * 5
     assert out.shape == (0, 16)
+
+
+ROUTE_PERMUTE_CASES = [
+    # T, h, E, K, score, capacity_factor, drop_policy, pad, copy_rows
+    (1000, 64, 16, 2, "softmax", 0.0, "position", False, True),
+    (515, 128, 16, 1, "softmax", 1.25, "position", False, True),
+    (2003, 256, 64, 1, "softmax", 1.0, "position", False, False),
+    (300, 64, 8, 2, "softmax", 0.5, "probs", False, True),
+    (300, 64, 8, 2, "softmax", 0.5, "position", True, False),
+    (64, 32, 256, 8, "sigmoid", 0.0, "position", False, True),
+    (77, 64, 5, 5, "softmax", 4.0, "position", False, True),  # capacity above T: nothing dropped
+]
+
+
+@pytest.mark.parametrize("T,h,E,K,score,cf,policy,pad,copy_rows", ROUTE_PERMUTE_CASES)
+def test_route_permute_is_bitwise_route_then_permute(T, h, E, K, score, cf, policy, pad, copy_rows):
+    log(f"route+permute: T={T} h={h} E={E} K={K} {score} cf={cf} {policy} pad={pad} copy={copy_rows}")
+    g = torch.Generator().manual_seed(T + E * 7)
+    x = torch.randn((T, h), generator=g).to(torch.bfloat16).to(DEV)
+    w = (torch.randn((E, h), generator=g) / h ** 0.5).to(DEV)
+    w[0] += 0.3  # a popular expert, so that capacities drop entries
+    eb = (torch.randn((E,), generator=g) * 0.1).to(DEV) if score == "sigmoid" else None
+    kw = dict(K=K, score=score, expert_bias=eb, capacity_factor=cf, drop_policy=policy,
+              pad_to_capacity=pad)
+    a = moe.moe_route(x, w, **kw)
+    pa = moe.moe_permute(x, a["routing_map"], a["probs"], K, a["max_rows"], copy_rows=copy_rows)
+    b = moe.moe_route_permute(x, w, copy_rows=copy_rows, **kw)
+    torch.cuda.synchronize()
+    for k in ("probs", "routing_map", "tokens_per_expert"):
+        assert torch.equal(a[k], b[k]), k
+    N = int(a["tokens_per_expert"].sum())
+    for k in ("row_id_map", "expert_offsets"):
+        assert torch.equal(pa[k], b[k]), k
+    for k in ("permuted_probs", "sorted_token") + (("permuted_x",) if copy_rows else ()):
+        assert torch.equal(pa[k][:N], b[k][:N]), k
