@@ -84,3 +84,27 @@ def test_grouped_mlp_all_experts_share_weights():
     _, y1 = moe.moe_grouped_mlp(x, one, wg[:1].contiguous(), wu[:1].contiguous(), wd[:1].contiguous())
     torch.cuda.synchronize()
     assert torch.equal(y[:N], y1[:N])
+
+
+def test_weight_streaming_tiles_many_per_workgroup():
+    """128-row tiles (80 <= rows per expert < 192) with more tiles than
+    workgroups, so each workgroup runs several tiles back to back; the
+    gathering FC1 reads the same rows through sorted_token and must give
+    bitwise the same act."""
+    rng = np.random.default_rng(11)
+    counts = [int(c) for c in rng.integers(80, 140, size=80)]
+    counts[3] = 0
+    h, f = 256, 512
+    log(f"many tiles per workgroup: E={len(counts)} N={sum(counts)} h={h} f={f}")
+    x, wg, wu, wd, tpe, N = _case(counts, h, f, torch.bfloat16, seed=12)
+    act, y = moe.moe_grouped_mlp(x, tpe, wg, wu, wd)
+    T = N + 9
+    perm = torch.randperm(T, device=DEV)[:N].to(torch.int32)
+    xt = torch.zeros((T, h), dtype=x.dtype, device=DEV)
+    xt[perm.long()] = x[:N]
+    a2 = moe.moe_grouped_fc1_swiglu_gather(xt, perm, tpe, wg, wu)
+    torch.cuda.synchronize()
+    assert torch.equal(act[:N], a2[:N])
+    ref_act, ref_y = oracle.grouped_experts(f64(x), np.array(counts), (f64(wg), f64(wu), f64(wd)), "bf16")
+    assert_close(f64(act[:N]), ref_act, "bf16", "act")
+    assert_close(f64(y[:N]), ref_y, "bf16", "expert_out")
