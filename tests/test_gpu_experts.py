@@ -86,16 +86,15 @@ def test_grouped_mlp_all_experts_share_weights():
     assert torch.equal(y[:N], y1[:N])
 
 
-def test_weight_streaming_tiles_many_per_workgroup():
-    """128-row tiles (80 <= rows per expert < 192) with more tiles than
-    workgroups, so each workgroup runs several tiles back to back; the
-    gathering FC1 reads the same rows through sorted_token and must give
-    bitwise the same act."""
+def test_weight_streaming_tiles_over_several_rounds():
+    """128-row tiles (80 <= rows per expert < 192), more tiles than the chip
+    runs at once, an empty expert; the gathering FC1 reads the same rows
+    through sorted_token and must give bitwise the same act."""
     rng = np.random.default_rng(11)
     counts = [int(c) for c in rng.integers(80, 140, size=80)]
     counts[3] = 0
     h, f = 256, 512
-    log(f"many tiles per workgroup: E={len(counts)} N={sum(counts)} h={h} f={f}")
+    log(f"several rounds of 128-row tiles: E={len(counts)} N={sum(counts)} h={h} f={f}")
     x, wg, wu, wd, tpe, N = _case(counts, h, f, torch.bfloat16, seed=12)
     act, y = moe.moe_grouped_mlp(x, tpe, wg, wu, wd)
     T = N + 9
