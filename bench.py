@@ -22,7 +22,9 @@ Layer options (on by default, --no-gather / --no-overlap /
 FC1 gathers token rows through sorted_token; the shared expert (when the
 layer has one) runs on a second stream, joined before the combine; route and
 permute run as one library call (moe_route_permute), which reuses the
-router's counting pass for the permute.  With the overlap on, main-stream stage
+router's counting pass for the permute; top-1 layers without a shared expert
+run FC2 with the combine as its epilogue (moe_grouped_fc2_combine,
+--no-fuse-combine to turn off).  With the overlap on, main-stream stage
 times include contention with the shared expert.
 """
 from __future__ import annotations
@@ -45,7 +47,7 @@ MFMA_FP8_PEAK_TFLOPS = 5000.0   # MI355X dense fp8 MFMA, published
 FP32_PEAK_TFLOPS = 157.3        # MI355X fp32 (used for fp32 layers)
 KERNEL_SOURCES = {  # stage -> source file that holds its kernel
     "route": "route.hip", "permute": "permute.hip", "route_permute": "route.hip",
-    "fc1": "gmm.hip", "fc2": "gmm.hip",
+    "fc1": "gmm.hip", "fc2": "gmm.hip", "fc2_combine": "gmm.hip",
     "shared": "gmm.hip", "combine": "combine.hip", "quantize": "mx.hip",
 }
 MX_SOURCES = {"fc1": "gmm_mx.hip", "fc2": "gmm_mx.hip", "shared": "gmm_mx.hip"}
@@ -67,6 +69,8 @@ def parse():
     p.add_argument("--no-overlap", action="store_true", help="shared expert on the main stream")
     p.add_argument("--no-fuse-route-permute", action="store_true",
                    help="route and permute as two library calls")
+    p.add_argument("--no-fuse-combine", action="store_true",
+                   help="top-1 layers: FC2 and the combine as two library calls")
     p.add_argument("--no-cold", action="store_true", help="skip the cache-flushed pass")
     p.add_argument("--precision", default="bf16", choices=("bf16", "mxfp8"),
                    help="expert GEMM operands (mxfp8: OCP MX blocks of 32, E4M3)")
@@ -124,6 +128,10 @@ def stage_work(cfg, n, T, fs, gather=False, mx=False):
     # route and permute as one call: the map and probs are written once and
     # read back by the scatter
     w["route_permute"] = (w["route"][0] + w["permute"][0], w["route"][1])
+    # FC2 with the top-1 combine as its epilogue: act and W_down read, out
+    # written (kept rows scaled, dropped rows zero), no expert_out round trip
+    w["fc2_combine"] = (active * h * f * b + N * f * b + T * h * b + N * 8 + T * K * 4,
+                        2.0 * N * h * f)
     if mx:
         q = 1.0 + 1.0 / 32
         w["quantize"] = (T * h * b + T * h * q, 0.0)
@@ -221,7 +229,8 @@ def main():
                             capacity_factor=cfg.capacity_factor, min_capacity=cfg.min_capacity,
                             gather=gather, overlap_shared=not args.no_overlap,
                             precision=args.precision,
-                            fuse_route_permute=not args.no_fuse_route_permute)
+                            fuse_route_permute=not args.no_fuse_route_permute,
+                            fuse_combine=not args.no_fuse_combine)
     for _ in range(args.warmup):
         layer.forward()
     torch.cuda.synchronize()
@@ -250,7 +259,7 @@ def main():
             per_step[name].append(a.elapsed_time(b))
         fwd.append(evs[0][1].elapsed_time(evs[-1][1]))
     stage_ms = {s: sum(v) / len(v) for s, v in per_step.items()}
-    single_kernel = ("fc1", "fc2", "shared", "combine")
+    single_kernel = ("fc1", "fc2", "fc2_combine", "shared", "combine")
     dom = max((s for s in stage_ms if s in single_kernel), key=lambda s: stage_ms[s])
     after_dom = stages[stages.index(dom) + 1] if stages.index(dom) + 1 < len(stages) else "end"
 
@@ -279,7 +288,7 @@ def main():
     n = layer.tokens_per_expert.cpu().tolist()
     N = int(sum(n))
     work = stage_work(cfg, n, cfg.T, layer.fs if layer.shared else 0, gather, mx)
-    gemm_stages = [s for s in ("fc1", "fc2", "shared") if s in stage_ms]
+    gemm_stages = [s for s in ("fc1", "fc2", "fc2_combine", "shared") if s in stage_ms]
     gemm_flops = sum(work[s][1] for s in gemm_stages)
     gemm_bytes = sum(work[s][0] for s in gemm_stages)
     gemm_ms = sum(stage_ms[s] for s in gemm_stages)
@@ -347,7 +356,7 @@ def main():
                    "tokens": cfg.T, "routed_rows": N, "dropped": cfg.T * cfg.K - N,
                    "parallelism": "single GPU, EP=1",
                    "gather_fc1": layer.gather, "shared_overlap": layer.overlap_shared,
-                   "route_permute_fused": layer.fused,
+                   "route_permute_fused": layer.fused, "fc2_combine_fused": layer.fused_combine,
                    "expert_precision": args.precision},
         "forward_ms": {"mean": sum(fwd) / len(fwd), "p10": pct(fwd, 10), "p50": pct(fwd, 50),
                        "p90": pct(fwd, 90)},

@@ -113,6 +113,68 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[NB][MI][NI], uint
   }
 }
 
+// FC2 with the K = 1 combine as its epilogue: row r of the tile goes to
+// out[tok[r]] scaled by prob[r], rounded as moe_grouped_fc2 then moe_combine
+// round it (y to bf16 first, then p*y + 0 in fp32, then to bf16), so the
+// result is bitwise theirs.  out == nullptr: the plain epilogue.
+struct CombineEpi {
+  const int32_t* tok;
+  const float* prob;
+  uint16_t* out;
+  int64_t T;
+};
+
+template <int MI, int NI, int WTM, int WTN>
+__device__ __forceinline__ void store_tile_combine(const f32x16 (&acc)[1][MI][NI],
+                                                   const CombineEpi& epi, int64_t row0, int nrows,
+                                                   int n0, int N, int wm, int wn, int l32, int hi) {
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi) {
+    const int ml = wm * WTM + mi * 32 + l32;
+    if (ml >= nrows) continue;
+    const int64_t r = row0 + ml;
+    const int64_t t = min(max(static_cast<int64_t>(epi.tok[r]), int64_t(0)), epi.T - 1);
+    const float p = epi.prob[r];
+    uint16_t* crow = epi.out + t * static_cast<int64_t>(N);
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int n = n0 + wn * WTN + ni * 32 + g * 8 + hi * 4;
+        if (n >= N) continue;
+        uint16_t o[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float y = bf16_bits_to_f32(f32_to_bf16_bits(acc[0][mi][ni][g * 4 + q]));
+          o[q] = f32_to_bf16_bits(fmaf(p, y, 0.f));
+        }
+        uint2 pk;
+        pk.x = static_cast<uint32_t>(o[0]) | (static_cast<uint32_t>(o[1]) << 16);
+        pk.y = static_cast<uint32_t>(o[2]) | (static_cast<uint32_t>(o[3]) << 16);
+        *reinterpret_cast<uint2*>(crow + n) = pk;
+      }
+  }
+}
+
+// Zero rows of the tokens with no kept row (row_id_map[t] outside
+// [0, max_rows)); a wave covers 16 tokens (workgroup z: tokens from
+// z * 16 * waves), 16-byte stores.
+__device__ __forceinline__ void zero_dropped_rows(const int32_t* __restrict__ row_id_map,
+                                                  int64_t max_rows, uint16_t* __restrict__ out,
+                                                  int64_t T, int N, int z) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int chunks = N / 8;
+  const int64_t t0 = (static_cast<int64_t>(z) * (blockDim.x >> 6) + wave) * 16;
+  for (int i = 0; i < 16; ++i) {
+    const int64_t t = t0 + i;
+    if (t >= T) break;
+    const int r = row_id_map[t];
+    if (r >= 0 && r < max_rows) continue;
+    uint4* row = reinterpret_cast<uint4*>(out + t * static_cast<int64_t>(N));
+    for (int c = lane; c < chunks; c += 64) row[c] = make_uint4(0, 0, 0, 0);
+  }
+}
+
 // LDS bytes one tile body uses.
 template <int BM, int BN, bool FC1, int STAGES, int SBK>
 constexpr int body_lds_bytes() {
@@ -121,13 +183,14 @@ constexpr int body_lds_bytes() {
 
 // One output tile (BM rows of one expert x BN columns) of the grouped GEMM.
 // `smem` holds the pipeline stages; all 64*WM*WN threads take part.
-template <int BM, int BN, int WM, int WN, bool FC1, int STAGES, int SBK, int SCHED, int SPREAD>
+template <int BM, int BN, int WM, int WN, bool FC1, int STAGES, int SBK, int SCHED, int SPREAD,
+          bool CMB>
 __device__ __forceinline__ void gmm_tile(const Tile& tile, char* smem,
                                          const uint16_t* __restrict__ A,
                                          const int32_t* __restrict__ gather, int64_t a_rows,
                                          const uint16_t* __restrict__ B0,
                                          const uint16_t* __restrict__ B1, uint16_t* __restrict__ C,
-                                         int N, int K) {
+                                         int N, int K, const CombineEpi& epi) {
   constexpr int NB = FC1 ? 2 : 1;
   constexpr int ROWS = BM + NB * BN;
   constexpr int NW = WM * WN;              // waves per workgroup
@@ -346,7 +409,10 @@ __device__ __forceinline__ void gmm_tile(const Tile& tile, char* smem,
     }
   }
 
-  store_tile<MI, NB, NI, WTM, WTN, FC1>(acc, C, tile.row0, tile.nrows, n0, N, wm, wn, l32, hi);
+  if constexpr (CMB && !FC1)
+    store_tile_combine<MI, NI, WTM, WTN>(acc, epi, tile.row0, tile.nrows, n0, N, wm, wn, l32, hi);
+  else
+    store_tile<MI, NB, NI, WTM, WTN, FC1>(acc, C, tile.row0, tile.nrows, n0, N, wm, wn, l32, hi);
 }
 
 
@@ -356,12 +422,20 @@ __device__ __forceinline__ void gmm_tile(const Tile& tile, char* smem,
 // spent on padding); with shorter m-tiles the layer is weight-streaming
 // bound and one body serves every tile.  The choice is uniform per
 // workgroup.
-template <bool FC1, int BMAX, int BN, int NW, class Body256, class Body128, class Body64>
+template <bool FC1, int BMAX, int BN, int NW, class Body256, class Body128, class Body64,
+          bool CMB = false>
 __global__ void __launch_bounds__(NW * 64) gmm_bf16_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ gather, int64_t a_rows,
     const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1,
     uint16_t* __restrict__ C, const int32_t* __restrict__ counts, int E, int N, int K,
-    int64_t max_rows) {
+    int64_t max_rows, CombineEpi epi, const int32_t* __restrict__ row_id_map, int zero_wgs) {
+  if constexpr (CMB) {
+    const int z = static_cast<int>(blockIdx.x) - static_cast<int>(gridDim.x - zero_wgs);
+    if (z >= 0) {  // the last workgroups zero the dropped tokens (in the tail of the tiles)
+      zero_dropped_rows(row_id_map, max_rows, epi.out, epi.T, N, z);
+      return;
+    }
+  }
   constexpr int L256 = Body256::lds > Body128::lds ? Body256::lds : Body128::lds;
   constexpr int LDS = BMAX == 256 ? (L256 > Body64::lds ? L256 : Body64::lds)
                                  : (BMAX == 128 ? Body128::lds : Body64::lds);
@@ -382,13 +456,13 @@ __global__ void __launch_bounds__(NW * 64) gmm_bf16_kernel(
   }
   tile.nrows = __builtin_amdgcn_readfirstlane(tile.nrows);
   if constexpr (BMAX == 256) {
-    if (tile.nrows > 128) Body256::run(tile, smem, A, gather, a_rows, B0, B1, C, N, K);
-    else if (tile.nrows > 64) Body128::run(tile, smem, A, gather, a_rows, B0, B1, C, N, K);
-    else Body64::run(tile, smem, A, gather, a_rows, B0, B1, C, N, K);
+    if (tile.nrows > 128) Body256::template run<CMB>(tile, smem, A, gather, a_rows, B0, B1, C, N, K, epi);
+    else if (tile.nrows > 64) Body128::template run<CMB>(tile, smem, A, gather, a_rows, B0, B1, C, N, K, epi);
+    else Body64::template run<CMB>(tile, smem, A, gather, a_rows, B0, B1, C, N, K, epi);
   } else if constexpr (BMAX == 128) {
-    Body128::run(tile, smem, A, gather, a_rows, B0, B1, C, N, K);
+    Body128::template run<CMB>(tile, smem, A, gather, a_rows, B0, B1, C, N, K, epi);
   } else {
-    Body64::run(tile, smem, A, gather, a_rows, B0, B1, C, N, K);
+    Body64::template run<CMB>(tile, smem, A, gather, a_rows, B0, B1, C, N, K, epi);
   }
 }
 
@@ -396,12 +470,13 @@ template <int BM, int BN, int WM, int WN, bool FC1, int STAGES, int SBK, int SCH
           int SPREAD = 0>
 struct Body {
   static constexpr int lds = body_lds_bytes<BM, BN, FC1, STAGES, SBK>();
+  template <bool CMB>
   __device__ __forceinline__ static void run(const Tile& t, char* smem, const uint16_t* A,
                                              const int32_t* gather, int64_t a_rows,
                                              const uint16_t* B0, const uint16_t* B1, uint16_t* C,
-                                             int N, int K) {
-    gmm_tile<BM, BN, WM, WN, FC1, STAGES, SBK, SCHED, SPREAD>(t, smem, A, gather, a_rows, B0, B1, C,
-                                                              N, K);
+                                             int N, int K, const CombineEpi& epi) {
+    gmm_tile<BM, BN, WM, WN, FC1, STAGES, SBK, SCHED, SPREAD, CMB>(t, smem, A, gather, a_rows, B0,
+                                                                   B1, C, N, K, epi);
   }
 };
 
@@ -490,16 +565,34 @@ struct AOperand {
   int64_t rows;
 };
 
+// With a combine epilogue (cmb.epi.out set), ceil(T / (16 * waves))
+// workgroups after the tile workgroups zero the dropped tokens' rows (they
+// are dispatched last, onto CUs the last round of tiles leaves idle).
+struct CombineArgs {
+  CombineEpi epi{nullptr, nullptr, nullptr, 0};
+  const int32_t* row_id_map = nullptr;
+};
+
 template <bool FC1, int BMAX, int BN, int NW, class B256, class B128, class B64>
 void launch_bf16(const AOperand& a, const void* B0, const void* B1, void* C, const int32_t* counts,
-                 int64_t E, int64_t N, int64_t K, int64_t max_rows, hipStream_t s) {
+                 int64_t E, int64_t N, int64_t K, int64_t max_rows, hipStream_t s,
+                 const CombineArgs& cmb = CombineArgs{}) {
   const int64_t g = grid_for(max_rows, E, BMAX, N, BN);
-  hipLaunchKernelGGL((gmm_bf16_kernel<FC1, BMAX, BN, NW, B256, B128, B64>),
-                     dim3(static_cast<unsigned>(g)), dim3(NW * 64), 0, s,
-                     static_cast<const uint16_t*>(a.base), a.gather, a.rows,
-                     static_cast<const uint16_t*>(B0), static_cast<const uint16_t*>(B1),
-                     static_cast<uint16_t*>(C), counts, static_cast<int>(E), static_cast<int>(N),
-                     static_cast<int>(K), max_rows);
+  const int64_t z = cmb.epi.out ? ceil_div(cmb.epi.T, NW * 16) : 0;
+  const auto args = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(g + z)), dim3(NW * 64), 0, s,
+                       static_cast<const uint16_t*>(a.base), a.gather, a.rows,
+                       static_cast<const uint16_t*>(B0), static_cast<const uint16_t*>(B1),
+                       static_cast<uint16_t*>(C), counts, static_cast<int>(E), static_cast<int>(N),
+                       static_cast<int>(K), max_rows, cmb.epi, cmb.row_id_map, static_cast<int>(z));
+  };
+  if constexpr (!FC1 && BMAX != 256) {  // (launch_gemm runs the combine epilogue on <= 128 rows)
+    if (cmb.epi.out) {
+      args(gmm_bf16_kernel<FC1, BMAX, BN, NW, B256, B128, B64, true>);
+      return;
+    }
+  }
+  args(gmm_bf16_kernel<FC1, BMAX, BN, NW, B256, B128, B64, false>);
 }
 
 template <bool FC1>
@@ -543,12 +636,13 @@ using Fc2B128n = Body<128, 128, 2, 4, false, 4, 64, kSchedRing, 1>;  // 128-row 
 template <bool FC1>
 void launch_gemm(int32_t dtype, const AOperand& A, const void* B0, const void* B1, void* C,
                  const int32_t* counts, int64_t E, int64_t N, int64_t K, int64_t max_rows,
-                 hipStream_t s) {
+                 hipStream_t s, const CombineArgs& cmb = CombineArgs{}) {
   if (dtype == MOE_F32) {
     launch_f32<FC1>(A, B0, B1, C, counts, E, N, K, max_rows, s);
     return;
   }
-  const int bm = pick_bm(max_rows, E);
+  int bm = pick_bm(max_rows, E);
+  if (!FC1 && cmb.epi.out && bm == 256) bm = 128;  // the combine epilogue runs 128- and 64-row bodies
   if constexpr (FC1) {
     if (bm == 256)
       launch_bf16<true, 256, 128, 8, Fc1B256, Fc1B128, Fc1B64>(A, B0, B1, C, counts, E, N, K, max_rows, s);
@@ -560,9 +654,9 @@ void launch_gemm(int32_t dtype, const AOperand& A, const void* B0, const void* B
     if (bm == 256)
       launch_bf16<false, 256, 256, 8, Fc2B256, Fc2B128, Fc2B64>(A, B0, B1, C, counts, E, N, K, max_rows, s);
     else if (bm == 128)
-      launch_bf16<false, 128, 128, 8, Fc2B128n, Fc2B128n, Fc2B128n>(A, B0, B1, C, counts, E, N, K, max_rows, s);
+      launch_bf16<false, 128, 128, 8, Fc2B128n, Fc2B128n, Fc2B128n>(A, B0, B1, C, counts, E, N, K, max_rows, s, cmb);
     else
-      launch_bf16<false, 64, 256, 8, Fc2B64, Fc2B64, Fc2B64>(A, B0, B1, C, counts, E, N, K, max_rows, s);
+      launch_bf16<false, 64, 256, 8, Fc2B64, Fc2B64, Fc2B64>(A, B0, B1, C, counts, E, N, K, max_rows, s, cmb);
   }
 }
 
@@ -633,6 +727,30 @@ extern "C" moe_status moe_grouped_fc2(int64_t E, int64_t h, int64_t f, int64_t m
   launch_gemm<false>(dtype, AOperand{act, nullptr, max_rows}, w_down, nullptr, expert_out,
                      tokens_per_expert, E, h, f, max_rows, as_stream(stream));
   return check_launch("moe_grouped_fc2");
+}
+
+extern "C" moe_status moe_grouped_fc2_combine(int64_t E, int64_t h, int64_t f, int64_t max_rows,
+                                              int32_t dtype, int64_t T, const void* act,
+                                              const int32_t* tokens_per_expert, const void* w_down,
+                                              const float* permuted_probs,
+                                              const int32_t* sorted_token,
+                                              const int32_t* row_id_map, void* out, void* stream) {
+  moe_status st = validate("moe_grouped_fc2_combine", E, h, f, max_rows, dtype);
+  if (st != MOE_OK) return st;
+  MOE_REQUIRE(dtype == MOE_BF16, MOE_ERR_UNSUPPORTED, "moe_grouped_fc2_combine: bf16 only");
+  MOE_REQUIRE(T >= 0 && T < (int64_t(1) << 31), MOE_ERR_ARG,
+              "moe_grouped_fc2_combine: T out of range");
+  if (T == 0) return MOE_OK;
+  MOE_REQUIRE(row_id_map && out && tokens_per_expert && w_down, MOE_ERR_ARG,
+              "moe_grouped_fc2_combine: NULL tensor argument");
+  MOE_REQUIRE(max_rows == 0 || (act && permuted_probs && sorted_token), MOE_ERR_ARG,
+              "moe_grouped_fc2_combine: NULL tensor argument");
+  CombineArgs cmb;
+  cmb.epi = CombineEpi{sorted_token, permuted_probs, static_cast<uint16_t*>(out), T};
+  cmb.row_id_map = row_id_map;
+  launch_gemm<false>(dtype, AOperand{act, nullptr, max_rows}, w_down, nullptr, nullptr,
+                     tokens_per_expert, E, h, f, max_rows, as_stream(stream), cmb);
+  return check_launch("moe_grouped_fc2_combine");
 }
 
 extern "C" moe_status moe_grouped_mlp(int64_t E, int64_t h, int64_t f, int64_t max_rows,

@@ -7,6 +7,9 @@ Options: `gather` skips the permuted copy of x (the permute writes indices
 and probs only, and FC1 reads token rows through sorted_token);
 `overlap_shared` runs the shared expert on a second stream (default
 priority) from the start of the forward, joined before the combine;
+`fuse_combine` (on by default; top-1 bf16 layers without a shared expert)
+runs FC2 with the combine as its epilogue (moe_grouped_fc2_combine, one
+"fc2_combine" stage): no expert_out round trip, bitwise the same output.
 `fuse_route_permute` (on by default) runs route and permute as one library
 call (moe_route_permute, one "route_permute" stage), which reuses the
 router's per-block counts for the permute; the outputs are bitwise those of
@@ -32,13 +35,14 @@ def _p(t: Optional[torch.Tensor]):
 class MoELayerForward:
     """route -> permute -> FC1+SwiGLU -> FC2 (-> shared expert) -> combine."""
 
-    STAGES = ("quantize", "route", "permute", "route_permute", "fc1", "fc2", "shared", "combine")
+    STAGES = ("quantize", "route", "permute", "route_permute", "fc1", "fc2", "shared", "combine",
+              "fc2_combine")
 
     def __init__(self, inp: Dict[str, torch.Tensor], *, K: int, score: str = "softmax",
                  pre_softmax: bool = True, capacity_factor: float = 0.0, min_capacity: int = 0,
                  drop_policy: str = "position", pad_to_capacity: bool = False,
                  gather: bool = False, overlap_shared: bool = False, precision: str = "bf16",
-                 fuse_route_permute: bool = True):
+                 fuse_route_permute: bool = True, fuse_combine: bool = True):
         self.lib = _lib.load()
         self.inp = inp
         x = _need(inp["x"], "x")
@@ -99,6 +103,8 @@ class MoELayerForward:
                 self.shared_actq = (e((T, fs), dtype=u8, device=dev),
                                     e((fs // 128, T, 4), dtype=u8, device=dev))
         self.overlap_shared = bool(overlap_shared and self.shared)
+        self.fused_combine = bool(fuse_combine and K == 1 and not self.shared and not self.mx
+                                  and x.dtype == torch.bfloat16)
         if self.overlap_shared:
             self.side = torch.cuda.Stream(device=dev)  # default priority
             self.ev_fork = torch.cuda.Event()
@@ -202,6 +208,12 @@ class MoELayerForward:
             1, self.h, self.fs, self.T, self.dt, _p(self.shared_act), _p(self.shared_count),
             _p(i["shared_down"]), _p(self.shared_out), self._stream()))
 
+    def fc2_combine(self):
+        check("moe_grouped_fc2_combine", self.lib.moe_grouped_fc2_combine(
+            self.E, self.h, self.f, self.max_rows, self.dt, self.T, _p(self.act),
+            _p(self.tokens_per_expert), _p(self.inp["w_down"]), _p(self.permuted_probs),
+            _p(self.sorted_token), _p(self.row_id_map), _p(self.out), self._stream()))
+
     def combine(self):
         check("moe_combine", self.lib.moe_combine(
             self.T, self.h, self.K, self.dt, _p(self.expert_out), _p(self.permuted_probs),
@@ -216,7 +228,13 @@ class MoELayerForward:
                 continue
             if n == "shared" and (not self.shared or self.overlap_shared):
                 continue
-            if (n in ("route", "permute") and self.fused) or (n == "route_permute" and not self.fused):
+            if n in ("route", "permute") and self.fused:
+                continue
+            if n == "route_permute" and not self.fused:
+                continue
+            if n in ("fc2", "combine") and self.fused_combine:
+                continue
+            if n == "fc2_combine" and not self.fused_combine:
                 continue
             keep.append(n)
         return keep

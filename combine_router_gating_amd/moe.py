@@ -320,6 +320,34 @@ def moe_grouped_fc2(act: torch.Tensor, tokens_per_expert: torch.Tensor, w_down: 
     return expert_out
 
 
+def moe_grouped_fc2_combine(act: torch.Tensor, tokens_per_expert: torch.Tensor,
+                            w_down: torch.Tensor, permuted_probs: torch.Tensor,
+                            sorted_token: torch.Tensor, row_id_map: torch.Tensor,
+                            out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Top-1 combine fused into FC2: out[t] = p * (act W_down^T)[row of t],
+    zero for dropped tokens; bitwise moe_grouped_fc2 then moe_combine (K=1)."""
+    E = _mlp_args(act, tokens_per_expert, w_down)
+    rows, f = act.shape
+    h = w_down.shape[1]
+    _need(w_down, "w_down", act.dtype, (E, h, f))
+    T = row_id_map.shape[0]
+    if row_id_map.dim() == 2:
+        if row_id_map.shape[1] != 1:
+            raise ValueError("moe_grouped_fc2_combine is for top-1 routing (row_id_map [T, 1])")
+    _need(row_id_map, "row_id_map", torch.int32)
+    _need(permuted_probs, "permuted_probs", torch.float32, (rows,))
+    _need(sorted_token, "sorted_token", torch.int32, (rows,))
+    if out is None:
+        out = torch.empty((T, h), dtype=act.dtype, device=act.device)
+    _need(out, "out", act.dtype, (T, h))
+    st = _lib.load().moe_grouped_fc2_combine(E, h, f, rows, _dtype_code(act, "act"), T, _ptr(act),
+                                             _ptr(tokens_per_expert), _ptr(w_down),
+                                             _ptr(permuted_probs), _ptr(sorted_token),
+                                             _ptr(row_id_map), _ptr(out), _stream())
+    check("moe_grouped_fc2_combine", st)
+    return out
+
+
 def moe_grouped_mlp(permuted_x: torch.Tensor, tokens_per_expert: torch.Tensor,
                     w_gate: torch.Tensor, w_up: torch.Tensor, w_down: torch.Tensor):
     """SwiGLU MLP of every expert over its row range; returns (act, expert_out)."""

@@ -263,6 +263,29 @@ moe_status moe_route_permute(const moe_route_desc* d, const void* x, const float
  * ------------------------------------------------------------------------ */
 
 /*
+ * moe_grouped_fc2_combine — moe_grouped_fc2 with moe_combine as its
+ * epilogue, for top-1 routing (K = 1) without a shared expert: [MC] §2's
+ * combine weights each token's single expert output by its prob, so row r
+ * of the grouped GEMM goes straight to out[sorted_token[r]] as
+ * p[r] * y[r], and the tokens whose entry was dropped (row_id_map[t]
+ * outside [0, max_rows)) get zero rows.  The rounding is the two calls'
+ * (y to bf16, then p*y in fp32, then to bf16): out is bitwise what
+ * moe_grouped_fc2 followed by moe_combine (K = 1, no shared_out) writes,
+ * without the expert_out round trip through HBM.  bf16 only.
+ *   act, tokens_per_expert, w_down  as moe_grouped_fc2
+ *   permuted_probs [max_rows] fp32, sorted_token [max_rows] int32 (values
+ *                  clamped to [0, T)), row_id_map [T] int32  as moe_permute
+ *                  writes them with K = 1
+ *   out            [T,h]  bf16  out
+ * Errors: those of moe_grouped_fc2; MOE_ERR_UNSUPPORTED for fp32.
+ */
+moe_status moe_grouped_fc2_combine(int64_t E, int64_t h, int64_t f, int64_t max_rows,
+                                   int32_t dtype, int64_t T, const void* act,
+                                   const int32_t* tokens_per_expert, const void* w_down,
+                                   const float* permuted_probs, const int32_t* sorted_token,
+                                   const int32_t* row_id_map, void* out, void* stream);
+
+/*
  *   permuted_x        [max_rows,h]  dtype
  *   tokens_per_expert [E]           int32 (device)
  *   w_gate, w_up      [E,f,h]       dtype

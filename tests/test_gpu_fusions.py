@@ -78,10 +78,11 @@ def test_layer_options_give_identical_outputs(name):
     kw = dict(K=cfg.K, score=cfg.score, pre_softmax=cfg.pre_softmax,
               capacity_factor=cfg.capacity_factor, min_capacity=cfg.min_capacity)
     outs = []
-    for gather, overlap, fuse in ((False, False, False), (True, False, True), (True, True, True),
-                                  (False, True, False), (False, False, True)):
+    for gather, overlap, fuse, fcmb in ((False, False, False, False), (True, False, True, True),
+                                        (True, True, True, False), (False, True, False, True),
+                                        (False, False, True, True)):
         layer = MoELayerForward(inp, gather=gather, overlap_shared=overlap,
-                                fuse_route_permute=fuse, **kw)
+                                fuse_route_permute=fuse, fuse_combine=fcmb, **kw)
         for _ in range(2):
             out = layer.forward()
         torch.cuda.synchronize()

@@ -154,3 +154,35 @@ def test_route_permute_is_bitwise_route_then_permute(T, h, E, K, score, cf, poli
         assert torch.equal(pa[k], b[k]), k
     for k in ("permuted_probs", "sorted_token") + (("permuted_x",) if copy_rows else ()):
         assert torch.equal(pa[k][:N], b[k][:N]), k
+
+
+FC2_COMBINE_CASES = [
+    # T, h, f, E, capacity_factor, hot: 64-, 128- and (forced to 128-) 256-row regimes
+    (515, 128, 256, 16, 1.0, 2.0),     # drops, ~32 rows per expert
+    (2000, 256, 128, 16, 1.25, 1.0),   # ~125 rows per expert (128-row tiles)
+    (3000, 128, 192, 8, 0.0, 0.0),     # dropless, ~375 rows per expert
+    (1, 64, 64, 4, 0.0, 0.0),
+    (40, 64, 128, 4, 0.05, 3.0),       # most tokens dropped
+]
+
+
+@pytest.mark.parametrize("T,h,f,E,cf,hot", FC2_COMBINE_CASES)
+def test_fc2_combine_is_bitwise_fc2_then_combine(T, h, f, E, cf, hot):
+    log(f"fc2+combine: T={T} h={h} f={f} E={E} cf={cf}")
+    g = torch.Generator().manual_seed(T + h + E)
+    x = torch.randn((T, h), generator=g).to(torch.bfloat16).to(DEV)
+    w = (torch.randn((E, h), generator=g) / h ** 0.5).to(DEV)
+    w[0] += hot / h ** 0.5
+    wg = (torch.randn((E, f, h), generator=g) * 0.05).to(torch.bfloat16).to(DEV)
+    wu = (torch.randn((E, f, h), generator=g) * 0.05).to(torch.bfloat16).to(DEV)
+    wd = (torch.randn((E, h, f), generator=g) * 0.05).to(torch.bfloat16).to(DEV)
+    r = moe.moe_route_permute(x, w, K=1, capacity_factor=cf)
+    tpe = r["tokens_per_expert"]
+    act = moe.moe_grouped_fc1_swiglu(r["permuted_x"], tpe, wg, wu)
+    y = moe.moe_grouped_fc2(act, tpe, wd)
+    ref = moe.moe_combine(y, r["permuted_probs"], r["row_id_map"])
+    out = torch.full((T, h), float("nan"), dtype=torch.bfloat16, device=DEV)
+    moe.moe_grouped_fc2_combine(act, tpe, wd, r["permuted_probs"], r["sorted_token"],
+                                r["row_id_map"], out=out)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
