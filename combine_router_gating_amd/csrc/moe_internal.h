@@ -45,6 +45,13 @@ void launch_count_scan(const int32_t* hist, int64_t nblk, int64_t E, int64_t cap
                        int32_t* kept, hipStream_t s, int64_t T = 0, float* probs = nullptr,
                        uint8_t* rmap = nullptr);
 
+// moe_permute's argument checks (no GPU call).
+moe_status permute_check(int64_t T, int64_t h, int64_t E, int64_t K, int32_t dtype, const void* x,
+                         const uint8_t* routing_map, const float* probs, int64_t max_rows,
+                         const void* permuted_x, const float* permuted_probs,
+                         const int32_t* sorted_token, const int32_t* row_id_map,
+                         const int32_t* expert_offsets);
+
 // moe_permute's body.  With given_blkoff (per-block exclusive offsets of each
 // expert's entries, block-major [nblk, E]) and given_totals (entries per
 // expert), the counting passes are skipped and the workspace is not used.

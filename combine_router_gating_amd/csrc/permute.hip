@@ -172,12 +172,11 @@ extern "C" size_t moe_permute_workspace_size(int64_t T, int64_t E) {
 
 namespace moe {
 
-moe_status permute_impl(int64_t T, int64_t h, int64_t E, int64_t K, int32_t dtype, const void* x,
-                        const uint8_t* routing_map, const float* probs, int64_t max_rows,
-                        void* permuted_x, float* permuted_probs, int32_t* sorted_token,
-                        int32_t* row_id_map, int32_t* expert_offsets, void* workspace,
-                        size_t workspace_bytes, hipStream_t s, const int32_t* given_blkoff,
-                        const int32_t* given_totals) {
+moe_status permute_check(int64_t T, int64_t h, int64_t E, int64_t K, int32_t dtype, const void* x,
+                         const uint8_t* routing_map, const float* probs, int64_t max_rows,
+                         const void* permuted_x, const float* permuted_probs,
+                         const int32_t* sorted_token, const int32_t* row_id_map,
+                         const int32_t* expert_offsets) {
   MOE_REQUIRE(T >= 0 && T < (int64_t(1) << 31), MOE_ERR_ARG, "moe_permute: T out of range");
   MOE_REQUIRE(E >= 1 && E <= kMaxExperts, MOE_ERR_ARG, "moe_permute: E=%lld not in [1,%lld]",
               (long long)E, (long long)kMaxExperts);
@@ -190,15 +189,29 @@ moe_status permute_impl(int64_t T, int64_t h, int64_t E, int64_t K, int32_t dtyp
               "moe_permute: max_rows out of range");
   MOE_REQUIRE(T * E < (int64_t(1) << 31), MOE_ERR_UNSUPPORTED, "moe_permute: T*E too large");
   MOE_REQUIRE(expert_offsets, MOE_ERR_ARG, "moe_permute: expert_offsets is required");
-  if (T == 0) {  // every other tensor is empty and may be NULL
-    launch_fill_i32(expert_offsets, E + 1, 0, s);
-    return check_launch("moe_permute(T=0)");
-  }
+  if (T == 0) return MOE_OK;  // every other tensor is empty and may be NULL
   MOE_REQUIRE(routing_map && probs && row_id_map, MOE_ERR_ARG,
               "moe_permute: NULL tensor argument");
   MOE_REQUIRE(x || !permuted_x, MOE_ERR_ARG, "moe_permute: x is NULL but permuted_x is not");
   MOE_REQUIRE(max_rows == 0 || (permuted_probs && sorted_token), MOE_ERR_ARG,
               "moe_permute: NULL output with max_rows > 0");
+  return MOE_OK;
+}
+
+moe_status permute_impl(int64_t T, int64_t h, int64_t E, int64_t K, int32_t dtype, const void* x,
+                        const uint8_t* routing_map, const float* probs, int64_t max_rows,
+                        void* permuted_x, float* permuted_probs, int32_t* sorted_token,
+                        int32_t* row_id_map, int32_t* expert_offsets, void* workspace,
+                        size_t workspace_bytes, hipStream_t s, const int32_t* given_blkoff,
+                        const int32_t* given_totals) {
+  const moe_status st = permute_check(T, h, E, K, dtype, x, routing_map, probs, max_rows,
+                                      permuted_x, permuted_probs, sorted_token, row_id_map,
+                                      expert_offsets);
+  if (st != MOE_OK) return st;
+  if (T == 0) {
+    launch_fill_i32(expert_offsets, E + 1, 0, s);
+    return check_launch("moe_permute(T=0)");
+  }
   const int64_t nblk = ceil_div(T, kCountBlock);
   const int32_t* blkoff = given_blkoff;
   const int32_t* totals = given_totals;

@@ -1151,6 +1151,10 @@ extern "C" moe_status moe_route_permute(const moe_route_desc* d, const void* x, 
                                         size_t workspace_bytes, void* stream) {
   moe_status st = validate(d);
   if (st != MOE_OK) return st;
+  // the permute's arguments are checked before anything is launched
+  st = permute_check(d->T, d->h, d->E, d->K, d->x_dtype, x, routing_map, probs, max_rows,
+                     permuted_x, permuted_probs, sorted_token, row_id_map, expert_offsets);
+  if (st != MOE_OK) return st;
   const size_t route_bytes = align_up(moe_route_workspace_size(d), 256);
   const size_t need = moe_route_permute_workspace_size(d);
   MOE_REQUIRE(d->T == 0 || (workspace && workspace_bytes >= need), MOE_ERR_WORKSPACE,

@@ -211,3 +211,33 @@ def test_side_output_entry_points_reject_bad_arguments():
     assert st == _lib.MOE_ERR_ARG
     st, _ = _status("moe_update_expert_bias", 4, p, None, ctypes.c_float(0.1), 1, None)
     assert st == _lib.MOE_ERR_ARG
+
+
+def test_fused_entry_points_reject_bad_arguments_before_launching():
+    p = ctypes.c_void_p(16)
+    big = 1 << 40
+    d = _desc(K=65, E=128)
+    st, _ = _status("moe_route_permute", ctypes.byref(d), *([None] * 10), 0, *([None] * 5), None,
+                    0, None)
+    assert st == _lib.MOE_ERR_ARG  # bad descriptor
+    d = _desc()
+    # route arguments complete, permute outputs missing: refused before any launch
+    st, msg = _status("moe_route_permute", ctypes.byref(d), p, p, None, None, None, None, None,
+                      p, p, p, 100, None, p, p, p, None, p, big, None)
+    assert st == _lib.MOE_ERR_ARG and "expert_offsets" in msg
+    st, msg = _status("moe_route_permute", ctypes.byref(d), p, p, None, None, None, None, None,
+                      p, p, p, 100, p, p, p, p, p, p, 16, None)
+    assert st == _lib.MOE_ERR_WORKSPACE
+    st, _ = _status("moe_grouped_fc2_combine", 8, 128, 256, 64, _lib.MOE_F32, 10, p, p, p, p, p, p,
+                    p, None)
+    assert st == _lib.MOE_ERR_UNSUPPORTED  # bf16 only
+    st, _ = _status("moe_grouped_fc2_combine", 8, 128, 256, 64, _lib.MOE_BF16, -1, p, p, p, p, p,
+                    p, p, None)
+    assert st == _lib.MOE_ERR_ARG  # T
+    st, _ = _status("moe_grouped_fc2_combine", 8, 128, 256, 64, _lib.MOE_BF16, 10, p, p, p, p, p,
+                    None, p, None)
+    assert st == _lib.MOE_ERR_ARG  # NULL row_id_map
+    st, msg = _status("moe_grouped_fc2_combine", 8, 100, 256, 64, _lib.MOE_BF16, 10, p, p, p, p, p,
+                      p, p, None)
+    assert st == _lib.MOE_ERR_UNSUPPORTED and "multiples of 64" in msg
+
