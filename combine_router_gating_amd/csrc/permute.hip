@@ -35,35 +35,57 @@ __global__ void __launch_bounds__(256) permute_scatter_kernel(
   __shared__ uint8_t tile[kCountBlock][kMaxExperts];
   __shared__ int rows[kCountBlock][kMaxTopK];
   __shared__ int exps[kCountBlock][kMaxTopK];
+  __shared__ float sel_probs[kCountBlock][kMaxTopK];
   __shared__ int slot_rows[kCountBlock][kMaxTopK];
   __shared__ int cnt[kCountBlock];
   __shared__ int nslot[kCountBlock];
   __shared__ int s_off[kMaxExperts + 1];
+  __shared__ int s_blk[kMaxExperts];
   __shared__ int64_t scratch[4];
   const int b = blockIdx.x;
   const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
   const int64_t t0 = static_cast<int64_t>(b) * kCountBlock;
   const int nt = static_cast<int>(min(static_cast<int64_t>(kCountBlock), T - t0));
+  // Every global read the block needs first is issued up front (one round
+  // trip): the experts' totals and this block's offsets, the map tile, and
+  // (E <= 256) the probs of this wave's tokens.
+  constexpr int PER = kMaxExperts / 256;
+  constexpr int PC = 4;  // 64-expert chunks of probs held per token (E <= 256)
+  int64_t v[PER];
+  int bo[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int e = threadIdx.x * PER + j;
+    v[j] = e < E ? totals[e] : 0;
+    bo[j] = e < E ? blkoff[static_cast<int64_t>(b) * E + e] : 0;
+  }
+  const bool pre = E <= PC * 64;
+  float pv[kCountBlock / 4][PC];
+  if (pre) {
+#pragma unroll
+    for (int i = 0; i < kCountBlock / 4; ++i)
+#pragma unroll
+      for (int c = 0; c < PC; ++c) {
+        const int tl = wave + 4 * i, e = c * 64 + lane;
+        pv[i][c] = (tl < nt && e < E) ? probs[(t0 + tl) * E + e] : 0.f;
+      }
+  }
   for (int i = threadIdx.x; i < nt * E; i += blockDim.x) tile[i / E][i % E] = map[t0 * E + i] != 0;
   {  // expert offsets: exclusive scan of the totals, 4 experts per thread
-    constexpr int PER = kMaxExperts / 256;
-    int64_t v[PER], sum = 0;
+    int64_t sum = 0;
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int e = threadIdx.x * PER + j;
-      v[j] = e < E ? totals[e] : 0;
-      sum += v[j];
-    }
+    for (int j = 0; j < PER; ++j) sum += v[j];
     int64_t all;
-    int64_t pre = block_exclusive_scan256(sum, scratch, &all);
+    int64_t pre_sum = block_exclusive_scan256(sum, scratch, &all);
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const int e = threadIdx.x * PER + j;
       if (e < E) {
-        s_off[e] = static_cast<int>(pre);
-        if (b == 0) expert_offsets[e] = static_cast<int>(pre);
+        s_off[e] = static_cast<int>(pre_sum);
+        s_blk[e] = bo[j];
+        if (b == 0) expert_offsets[e] = static_cast<int>(pre_sum);
       }
-      pre += v[j];
+      pre_sum += v[j];
     }
     if (threadIdx.x == 0) {
       s_off[E] = static_cast<int>(all);
@@ -76,17 +98,28 @@ __global__ void __launch_bounds__(256) permute_scatter_kernel(
   auto row_of = [&](int tl, int e) {
     int prior = 0;
     for (int u = 0; u < tl; ++u) prior += tile[u][e];
-    return s_off[e] + blkoff[static_cast<int64_t>(b) * E + e] + prior;
+    return s_off[e] + s_blk[e] + prior;
   };
   const uint64_t below = (uint64_t(1) << lane) - 1;
 
-  for (int tl = wave; tl < nt; tl += 4) {
+#pragma unroll
+  for (int i = 0; i < kCountBlock / 4; ++i) {
+    const int tl = wave + 4 * i;
+    if (tl >= nt) break;  // wave-uniform
     const int64_t t = t0 + tl;
     int base = 0, ks = 0;
     for (int c0 = 0; c0 < E; c0 += 64) {
       const int e = c0 + lane;
       const bool set = e < E && tile[tl][e];
-      const bool nz = set && probs[t * E + e] != 0.f;
+      float pr = 0.f;
+      if (pre) {
+#pragma unroll
+        for (int c = 0; c < PC; ++c)
+          if (c * 64 == c0) pr = pv[i][c];
+      } else if (set) {
+        pr = probs[t * E + e];
+      }
+      const bool nz = set && pr != 0.f;
       const uint64_t mask = __ballot(set);
       const uint64_t nzmask = __ballot(nz);
       if (set) {
@@ -95,6 +128,7 @@ __global__ void __launch_bounds__(256) permute_scatter_kernel(
         if (j < kMaxTopK) {
           rows[tl][j] = r;
           exps[tl][j] = e;
+          sel_probs[tl][j] = pr;
         }
         if (nz) {
           const int k = ks + __popcll(nzmask & below);
@@ -120,7 +154,7 @@ __global__ void __launch_bounds__(256) permute_scatter_kernel(
     if (lane < n) {
       const int r = rows[tl][lane];
       if (r < max_rows) {
-        pprobs[r] = probs[t * E + exps[tl][lane]];
+        pprobs[r] = sel_probs[tl][lane];
         sorted_token[r] = static_cast<int32_t>(t);
       }
     }
