@@ -68,13 +68,28 @@ __global__ void __launch_bounds__(256) count_scan_kernel(const int32_t* __restri
                                                          int32_t* __restrict__ kept, int64_t T,
                                                          float* __restrict__ probs,
                                                          uint8_t* __restrict__ rmap) {
+  constexpr int kPre = 1024;  // map column bytes of a chunk held in LDS (64 blocks)
   __shared__ int64_t scratch[4];
   __shared__ int s_past;  // first block of the chunk whose entries all rank >= cap
+  __shared__ uint8_t s_m[kPre];
   const int e = blockIdx.x;
   const int cb = (nblk + static_cast<int>(gridDim.y) - 1) / static_cast<int>(gridDim.y);
   const int c0 = min(nblk, static_cast<int>(blockIdx.y) * cb);
   const int c1 = min(nblk, c0 + cb);
   const int32_t* h = hist + static_cast<int64_t>(e) * nblk;
+  // With a capacity, the chunk's map column is read together with the counts
+  // (one round trip), so the drop below reads it from LDS.
+  const int64_t ct0 = static_cast<int64_t>(c0) * kCountBlock;
+  const int64_t ct1 = min(T, static_cast<int64_t>(c1) * kCountBlock);
+  const bool pref = rmap && cap >= 0 && ct1 - ct0 <= kPre;
+  uint8_t pm[kPre / 256];
+  if (pref) {
+#pragma unroll
+    for (int u = 0; u < kPre / 256; ++u) {
+      const int64_t t = ct0 + threadIdx.x + 256 * u;
+      pm[u] = t < ct1 ? rmap[t * E + e] : 0;
+    }
+  }
   const int per = (c1 - c0 + 255) / 256;
   const int b0 = c0 + static_cast<int>(threadIdx.x) * per;
   const int b1 = min(c1, b0 + per);
@@ -94,7 +109,12 @@ __global__ void __launch_bounds__(256) count_scan_kernel(const int32_t* __restri
     s_past = c1;
     if (blockIdx.y == 0) kept[e] = static_cast<int32_t>((cap >= 0 && total > cap) ? cap : total);
   }
+  if (pref) {
+#pragma unroll
+    for (int u = 0; u < kPre / 256; ++u) s_m[threadIdx.x + 256 * u] = pm[u];
+  }
   __syncthreads();
+  auto map_at = [&](int64_t t) -> uint8_t { return pref ? s_m[t - ct0] : rmap[t * E + e]; };
   for (int b = b0; b < b1; ++b) {
     const int c = h[b];
     blkoff[static_cast<int64_t>(b) * E + e] = static_cast<int32_t>(cap >= 0 && run > cap ? cap : run);
@@ -104,7 +124,7 @@ __global__ void __launch_bounds__(256) count_scan_kernel(const int32_t* __restri
       const int nt = static_cast<int>(min(static_cast<int64_t>(kCountBlock), T - t0));
       uint8_t m[kCountBlock];
 #pragma unroll
-      for (int i = 0; i < kCountBlock; ++i) m[i] = i < nt ? rmap[(t0 + i) * E + e] : 0;
+      for (int i = 0; i < kCountBlock; ++i) m[i] = i < nt ? map_at(t0 + i) : 0;
       int64_t r = run;
 #pragma unroll
       for (int i = 0; i < kCountBlock; ++i) {
@@ -127,7 +147,7 @@ __global__ void __launch_bounds__(256) count_scan_kernel(const int32_t* __restri
          t += 256 * kU) {
       uint8_t m[kU];
 #pragma unroll
-      for (int u = 0; u < kU; ++u) m[u] = t + 256 * u < end ? rmap[(t + 256 * u) * E + e] : 0;
+      for (int u = 0; u < kU; ++u) m[u] = t + 256 * u < end ? map_at(t + 256 * u) : 0;
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
         if (m[u]) {
