@@ -156,7 +156,7 @@ def test_layer_graph_capture_replays_match_eager():
         assert torch.equal(res["routing_map"], eager["routing_map"])
 
 
-@pytest.mark.parametrize("name,n_tok", [("switch", 16), ("dsv3", 3)])
+@pytest.mark.parametrize("name,n_tok", [("switch", 16), ("mixtral", 6), ("qwen3", 4), ("dsv3", 3)])
 def test_layer_bench_configuration_full_size_sampled(name, n_tok):
     """The layer object exactly as the benchmark runs it (gathering FC1,
     shared expert on a second stream) against the oracle on sampled tokens
