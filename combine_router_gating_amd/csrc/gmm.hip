@@ -612,9 +612,13 @@ void launch_f32(const AOperand& a, const void* B0, const void* B1, void* C, cons
 // not.  All variants run 8 waves (two per SIMD, so one wave's MFMAs cover
 // the other's waits); the shapes were chosen by timing the variants on the
 // five layer shapes.
-int pick_bm(int64_t max_rows, int64_t E) {
+// FC1 takes 256-row m-tiles from 128 rows per expert on: an expert with
+// 129-256 rows is then one tile (the 256-row body) instead of a full tile
+// and a short one that streams the same weight slab again (timed on the
+// Switch layer with capacity 160: 440 vs 445 us).
+int pick_bm(int64_t max_rows, int64_t E, bool fc1) {
   const int64_t avg = max_rows / E;
-  if (avg >= 192) return 256;
+  if (avg >= (fc1 ? 128 : 192)) return 256;
   if (avg >= 80) return 128;
   return 64;
 }
@@ -641,7 +645,7 @@ void launch_gemm(int32_t dtype, const AOperand& A, const void* B0, const void* B
     launch_f32<FC1>(A, B0, B1, C, counts, E, N, K, max_rows, s);
     return;
   }
-  int bm = pick_bm(max_rows, E);
+  int bm = pick_bm(max_rows, E, FC1);
   if (!FC1 && cmb.epi.out && bm == 256) bm = 128;  // the combine epilogue runs 128- and 64-row bodies
   if constexpr (FC1) {
     if (bm == 256)
