@@ -19,51 +19,60 @@ struct Tile {
 // Scan the per-expert row counts into LDS: s_roff[e] = first row of expert
 // e, s_n[e] = its rows, s_toff[e] = its first m-tile (s_toff[E] = all m-tiles).
 // Counts are clamped so that the rows stay within max_rows.  Returns the
-// number of m-tiles; all threads of the workgroup take part.
+// number of m-tiles; all threads of the workgroup call it.  The first wave
+// does the work alone (64 experts per step, every count loaded up front,
+// wave-level scans), so the workgroup passes a single barrier: this runs
+// before every tile, on its critical path.
 template <int BM, int NTHREADS = kGemmThreads>
 __device__ int64_t decode_counts(const int32_t* __restrict__ counts, int E, int64_t max_rows,
                                  int* s_toff, int* s_roff, int* s_n, int64_t* scratch) {
-  constexpr int PER = kMaxExperts / NTHREADS;  // experts per thread
-  const int tid = threadIdx.x;
-  int64_t c[PER];
-  int64_t sum = 0;
+  (void)scratch;
+  constexpr int kSteps = kMaxExperts / 64;
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const int steps = (E + 63) / 64;
+    int cv[kSteps];
 #pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const int e = tid * PER + j;
-    int64_t v = e < E ? static_cast<int64_t>(counts[e]) : 0;
-    v = v < 0 ? 0 : (v > max_rows ? max_rows : v);
-    c[j] = v;
-    sum += v;
-  }
-  int64_t total_rows;
-  int64_t pre = block_exclusive_scan<NTHREADS / 64>(sum, scratch, &total_rows);
-  int tl[PER];
-  int tsum = 0;
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const int e = tid * PER + j;
-    const int64_t start = pre < max_rows ? pre : max_rows;
-    const int64_t end = pre + c[j] < max_rows ? pre + c[j] : max_rows;
-    const int n = static_cast<int>(end - start);
-    tl[j] = (n + BM - 1) / BM;
-    tsum += tl[j];
-    if (e < E) {
-      s_roff[e] = static_cast<int>(start);
-      s_n[e] = n;
+    for (int j = 0; j < kSteps; ++j) {
+      const int e = j * 64 + lane;
+      const int v = (j < steps && e < E) ? counts[e] : 0;
+      cv[j] = v < 0 ? 0 : (v > max_rows ? static_cast<int>(max_rows) : v);
     }
-    pre += c[j];
-  }
-  int64_t total_tiles;
-  int tpre = static_cast<int>(block_exclusive_scan<NTHREADS / 64>(tsum, scratch, &total_tiles));
+    int64_t run = 0;  // rows before this step's experts
+    int trun = 0;     // m-tiles before them
 #pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const int e = tid * PER + j;
-    if (e < E) s_toff[e] = tpre;
-    tpre += tl[j];
+    for (int j = 0; j < kSteps; ++j) {
+      if (j >= steps) break;  // wave-uniform
+      const int e = j * 64 + lane;
+      int64_t incl = cv[j];
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int64_t o = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += o;
+      }
+      const int64_t pre = run + incl - cv[j];
+      run += __shfl(incl, 63, 64);
+      const int64_t start = pre < max_rows ? pre : max_rows;
+      const int64_t end = pre + cv[j] < max_rows ? pre + cv[j] : max_rows;
+      const int n = static_cast<int>(end - start);
+      const int tl = (n + BM - 1) / BM;
+      int tincl = tl;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_up(tincl, off, 64);
+        if (lane >= off) tincl += o;
+      }
+      if (e < E) {
+        s_roff[e] = static_cast<int>(start);
+        s_n[e] = n;
+        s_toff[e] = trun + tincl - tl;
+      }
+      trun += __shfl(tincl, 63, 64);
+    }
+    if (lane == 0) s_toff[E] = trun;
   }
-  if (tid == 0) s_toff[E] = static_cast<int>(total_tiles);
   __syncthreads();
-  return total_tiles;
+  return s_toff[E];
 }
 
 // Logical tile L (expert -> n-tile -> m-tile order, so the m-tiles sharing a

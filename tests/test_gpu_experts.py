@@ -107,3 +107,18 @@ def test_weight_streaming_tiles_over_several_rounds():
     ref_act, ref_y = oracle.grouped_experts(f64(x), np.array(counts), (f64(wg), f64(wu), f64(wd)), "bf16")
     assert_close(f64(act[:N]), ref_act, "bf16", "act")
     assert_close(f64(y[:N]), ref_y, "bf16", "expert_out")
+
+
+def test_grouped_mlp_many_experts_mostly_empty():
+    """700 experts (the tile decode's counts span eleven 64-expert steps),
+    most of them empty, a few with rows."""
+    counts = [0] * 700
+    for e, c in ((0, 5), (63, 70), (64, 1), (250, 130), (511, 3), (699, 40)):
+        counts[e] = c
+    log(f"many experts: E={len(counts)} N={sum(counts)}")
+    x, wg, wu, wd, tpe, N = _case(counts, 64, 128, torch.bfloat16, seed=21)
+    act, y = moe.moe_grouped_mlp(x, tpe, wg, wu, wd)
+    torch.cuda.synchronize()
+    ref_act, ref_y = oracle.grouped_experts(f64(x), np.array(counts), (f64(wg), f64(wu), f64(wd)), "bf16")
+    assert_close(f64(act[:N]), ref_act, "bf16", "act")
+    assert_close(f64(y[:N]), ref_y, "bf16", "expert_out")
