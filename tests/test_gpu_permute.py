@@ -186,3 +186,18 @@ def test_fc2_combine_is_bitwise_fc2_then_combine(T, h, f, E, cf, hot):
                                 r["row_id_map"], out=out)
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+
+
+def test_fused_calls_on_an_empty_batch():
+    x = torch.zeros((0, 64), dtype=torch.bfloat16, device=DEV)
+    w = torch.zeros((8, 64), dtype=torch.float32, device=DEV)
+    r = moe.moe_route_permute(x, w, K=1, capacity_factor=1.0)
+    torch.cuda.synchronize()
+    assert r["tokens_per_expert"].cpu().tolist() == [0] * 8
+    assert r["expert_offsets"].cpu().tolist() == [0] * 9
+    act = torch.zeros((0, 128), dtype=torch.bfloat16, device=DEV)
+    wd = torch.zeros((8, 64, 128), dtype=torch.bfloat16, device=DEV)
+    out = moe.moe_grouped_fc2_combine(act, r["tokens_per_expert"], wd, r["permuted_probs"],
+                                      r["sorted_token"], r["row_id_map"])
+    torch.cuda.synchronize()
+    assert out.shape == (0, 64)
