@@ -60,7 +60,8 @@ typedef enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1, MOE_SCORE_SQRTSOFTP
 typedef enum { MOE_DROP_POSITION = 0, MOE_DROP_PROBS = 1 } moe_drop_policy;
 
 /* Version of this interface (2: drop policy, padding to capacity,
- * sqrtsoftplus scores, router side outputs, gathering FC1, MXFP8 GEMMs). */
+ * sqrtsoftplus scores, router side outputs, gathering FC1, MXFP8 GEMMs;
+ * 3: moe_route_permute, moe_grouped_fc2_combine). */
 int moe_abi_version(void);
 
 /* Message for the last non-OK status returned on the calling thread. */
