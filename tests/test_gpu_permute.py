@@ -34,6 +34,7 @@ def _routing(T, E, K, seed, cf=0.0, hot=0.0):
     (129, 2048, 16, 1, 0.5, torch.bfloat16),
     (64, 7168, 256, 8, 0.0, torch.bfloat16),
     (40, 64, 1000, 6, 0.0, torch.float32),
+    (20, 32, 1024, 64, 0.0, torch.float32),
 ])
 def test_permute_matches_oracle(T, h, E, K, cf, dt):
     log(f"permute: T={T} h={h} E={E} K={K} cf={cf} {dt}")
@@ -79,6 +80,8 @@ def test_permute_full_size(name):
     (300, 256, 8, 2, torch.bfloat16, False),
     (129, 2056, 16, 3, torch.bfloat16, True),
     (64, 7168, 256, 8, torch.bfloat16, True),
+    (50, 64, 128, 12, torch.bfloat16, False),  # K past one group of 8 loads
+    (20, 32, 1024, 64, torch.float32, True),   # the largest K and E
 ])
 def test_combine_matches_oracle(T, h, E, K, dt, shared):
     log(f"combine: T={T} h={h} E={E} K={K} {dt} shared={shared}")
