@@ -23,8 +23,8 @@ FC1 gathers token rows through sorted_token; the shared expert (when the
 layer has one) runs on a second stream, joined before the combine; route and
 permute run as one library call (moe_route_permute), which reuses the
 router's counting pass for the permute; top-1 layers without a shared expert
-run FC2 with the combine as its epilogue (moe_grouped_fc2_combine,
---no-fuse-combine to turn off).  With the overlap on, main-stream stage
+run FC2 with the combine as its epilogue (moe_grouped_fc2_combine, or its
+MXFP8 twin; --no-fuse-combine to turn off).  With the overlap on, main-stream stage
 times include contention with the shared expert.
 """
 from __future__ import annotations
@@ -50,7 +50,8 @@ KERNEL_SOURCES = {  # stage -> source file that holds its kernel
     "fc1": "gmm.hip", "fc2": "gmm.hip", "fc2_combine": "gmm.hip",
     "shared": "gmm.hip", "combine": "combine.hip", "quantize": "mx.hip",
 }
-MX_SOURCES = {"fc1": "gmm_mx.hip", "fc2": "gmm_mx.hip", "shared": "gmm_mx.hip"}
+MX_SOURCES = {"fc1": "gmm_mx.hip", "fc2": "gmm_mx.hip", "fc2_combine": "gmm_mx.hip",
+              "shared": "gmm_mx.hip"}
 
 
 def parse():
@@ -137,6 +138,8 @@ def stage_work(cfg, n, T, fs, gather=False, mx=False):
         w["quantize"] = (T * h * b + T * h * q, 0.0)
         w["fc1"] = (active * 2 * h * f * q + N * h * q + N * f * q, 4.0 * N * h * f)
         w["fc2"] = (active * h * f * q + N * f * q + N * h * b, 2.0 * N * h * f)
+        w["fc2_combine"] = (active * h * f * q + N * f * q + T * h * b + N * 8 + T * K * 4,
+                            2.0 * N * h * f)
         if fs:
             w["shared"] = (3 * h * fs * q + T * h * q + 2 * T * fs * q + T * h * b, 6.0 * T * h * fs)
     return w

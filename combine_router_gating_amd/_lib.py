@@ -59,6 +59,8 @@ SIGNATURES = {
                                              c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "moe_grouped_fc2_mxfp8": (c_i32, [c_i64, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp,
                                       c_vp, c_vp]),
+    "moe_grouped_fc2_combine_mxfp8": (c_i32, [c_i64, c_i64, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp,
+                                              c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "moe_grouped_fc2": (c_i32, [c_i64, c_i64, c_i64, c_i64, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "moe_grouped_fc2_combine": (c_i32, [c_i64, c_i64, c_i64, c_i64, c_i32, c_i64, c_vp, c_vp, c_vp,
                                         c_vp, c_vp, c_vp, c_vp, c_vp]),

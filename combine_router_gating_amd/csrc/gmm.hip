@@ -113,17 +113,6 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[NB][MI][NI], uint
   }
 }
 
-// FC2 with the K = 1 combine as its epilogue: row r of the tile goes to
-// out[tok[r]] scaled by prob[r], rounded as moe_grouped_fc2 then moe_combine
-// round it (y to bf16 first, then p*y + 0 in fp32, then to bf16), so the
-// result is bitwise theirs.  out == nullptr: the plain epilogue.
-struct CombineEpi {
-  const int32_t* tok;
-  const float* prob;
-  uint16_t* out;
-  int64_t T;
-};
-
 template <int MI, int NI, int WTM, int WTN>
 __device__ __forceinline__ void store_tile_combine(const f32x16 (&acc)[1][MI][NI],
                                                    const CombineEpi& epi, int64_t row0, int nrows,
@@ -133,9 +122,8 @@ __device__ __forceinline__ void store_tile_combine(const f32x16 (&acc)[1][MI][NI
     const int ml = wm * WTM + mi * 32 + l32;
     if (ml >= nrows) continue;
     const int64_t r = row0 + ml;
-    const int64_t t = min(max(static_cast<int64_t>(epi.tok[r]), int64_t(0)), epi.T - 1);
     const float p = epi.prob[r];
-    uint16_t* crow = epi.out + t * static_cast<int64_t>(N);
+    uint16_t* crow = epi.out + epi.token(r) * static_cast<int64_t>(N);
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
@@ -144,34 +132,12 @@ __device__ __forceinline__ void store_tile_combine(const f32x16 (&acc)[1][MI][NI
         if (n >= N) continue;
         uint16_t o[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float y = bf16_bits_to_f32(f32_to_bf16_bits(acc[0][mi][ni][g * 4 + q]));
-          o[q] = f32_to_bf16_bits(fmaf(p, y, 0.f));
-        }
+        for (int q = 0; q < 4; ++q) o[q] = combine_bf16(p, acc[0][mi][ni][g * 4 + q]);
         uint2 pk;
         pk.x = static_cast<uint32_t>(o[0]) | (static_cast<uint32_t>(o[1]) << 16);
         pk.y = static_cast<uint32_t>(o[2]) | (static_cast<uint32_t>(o[3]) << 16);
         *reinterpret_cast<uint2*>(crow + n) = pk;
       }
-  }
-}
-
-// Zero rows of the tokens with no kept row (row_id_map[t] outside
-// [0, max_rows)); a wave covers 16 tokens (workgroup z: tokens from
-// z * 16 * waves), 16-byte stores.
-__device__ __forceinline__ void zero_dropped_rows(const int32_t* __restrict__ row_id_map,
-                                                  int64_t max_rows, uint16_t* __restrict__ out,
-                                                  int64_t T, int N, int z) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int chunks = N / 8;
-  const int64_t t0 = (static_cast<int64_t>(z) * (blockDim.x >> 6) + wave) * 16;
-  for (int i = 0; i < 16; ++i) {
-    const int64_t t = t0 + i;
-    if (t >= T) break;
-    const int r = row_id_map[t];
-    if (r >= 0 && r < max_rows) continue;
-    uint4* row = reinterpret_cast<uint4*>(out + t * static_cast<int64_t>(N));
-    for (int c = lane; c < chunks; c += 64) row[c] = make_uint4(0, 0, 0, 0);
   }
 }
 

@@ -62,6 +62,8 @@ struct MxOut {
   uint8_t* scales;     // FC1: act scales, k-tiled [N/128, max_rows, 4]
   uint16_t* bf16;      // FC2: expert_out [max_rows, N]
   int64_t rows;        // max_rows
+  CombineEpi cmb{nullptr, nullptr, nullptr, 0};  // FC2 with the top-1 combine: out [T, N]
+  const int32_t* row_id_map = nullptr;           // [T] (dropped tokens' zero rows)
 };
 
 template <int BM, int BN, bool FC1, int NW, int STAGES>
@@ -70,7 +72,7 @@ constexpr int mx_lds_bytes() {
 }
 
 // One output tile (BM rows of one expert x BN columns).
-template <int BM, int BN, int WM, int WN, bool FC1, int STAGES, int SPREAD>
+template <int BM, int BN, int WM, int WN, bool FC1, int STAGES, int SPREAD, bool CMB>
 __device__ __forceinline__ void mx_tile(const Tile& tile, char* smem, const MxA& A, const MxB& B,
                                         const MxOut& O, int N, int K) {
   constexpr int NB = FC1 ? 2 : 1;
@@ -299,6 +301,19 @@ __device__ __forceinline__ void mx_tile(const Tile& tile, char* smem, const MxA&
           if (hi == 0)
             O.scales[((nc / kMxK) * O.rows + grow) * 4 + ((nc / 32) & 3)] = static_cast<uint8_t>(e + 127);
         }
+      } else if constexpr (CMB) {
+        if (!row_ok || nc >= N) continue;
+        const float p = O.cmb.prob[grow];
+        uint16_t* crow = O.cmb.out + O.cmb.token(grow) * N;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          uint2 pk;
+          pk.x = static_cast<uint32_t>(combine_bf16(p, acc[0][mi][ni][4 * g])) |
+                 (static_cast<uint32_t>(combine_bf16(p, acc[0][mi][ni][4 * g + 1])) << 16);
+          pk.y = static_cast<uint32_t>(combine_bf16(p, acc[0][mi][ni][4 * g + 2])) |
+                 (static_cast<uint32_t>(combine_bf16(p, acc[0][mi][ni][4 * g + 3])) << 16);
+          *reinterpret_cast<uint2*>(crow + nc + 8 * g + 4 * hi) = pk;
+        }
       } else {
         if (!row_ok || nc >= N) continue;
         uint16_t* crow = O.bf16 + grow * N;
@@ -320,17 +335,27 @@ template <int BM_, int BN_, int WM, int WN, bool FC1, int STAGES, int SPREAD>
 struct MxBody {
   static constexpr int BM = BM_, BN = BN_;
   static constexpr int lds = mx_lds_bytes<BM, BN, FC1, WM * WN, STAGES>();
+  template <bool CMB>
   __device__ __forceinline__ static void run(const Tile& t, char* smem, const MxA& A, const MxB& B,
                                              const MxOut& O, int N, int K) {
-    mx_tile<BM, BN, WM, WN, FC1, STAGES, SPREAD>(t, smem, A, B, O, N, K);
+    mx_tile<BM, BN, WM, WN, FC1, STAGES, SPREAD, CMB>(t, smem, A, B, O, N, K);
   }
 };
 
 // Decode this workgroup's tile (Body::BM-row m-tiles, Body::BN columns), run the body.
-template <bool FC1, class Body>
+// With the combine epilogue (CMB), the last zero_wgs workgroups write the
+// dropped tokens' zero rows.
+template <bool FC1, class Body, bool CMB = false>
 __global__ void __launch_bounds__(512) gmm_mx_kernel(MxA A, MxB B, MxOut O,
                                                      const int32_t* __restrict__ counts, int E,
-                                                     int N, int K, int64_t max_rows) {
+                                                     int N, int K, int64_t max_rows, int zero_wgs) {
+  if constexpr (CMB) {
+    const int z = static_cast<int>(blockIdx.x) - static_cast<int>(gridDim.x - zero_wgs);
+    if (z >= 0) {
+      zero_dropped_rows(O.row_id_map, max_rows, O.cmb.out, O.cmb.T, N, z);
+      return;
+    }
+  }
   constexpr int DECODE_BYTES = (3 * kMaxExperts + 1) * 4 + 64;
   static_assert(Body::lds >= DECODE_BYTES, "decode scratch aliases the stages");
   __shared__ __attribute__((aligned(1024))) char smem[Body::lds];
@@ -352,7 +377,7 @@ __global__ void __launch_bounds__(512) gmm_mx_kernel(MxA A, MxB B, MxOut O,
   tile.n0 = __builtin_amdgcn_readfirstlane(tile.n0);
   tile.nrows = __builtin_amdgcn_readfirstlane(tile.nrows);
   tile.row0 = static_cast<int64_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(tile.row0)));
-  Body::run(tile, smem, A, B, O, N, K);
+  Body::template run<CMB>(tile, smem, A, B, O, N, K);
 }
 
 // Bodies (8 waves, two per SIMD).  LDS per stage = rows * 128 + 2 KB of
@@ -369,9 +394,18 @@ template <bool FC1, class Body>
 void launch_mx(const MxA& a, const MxB& b, const MxOut& o, const int32_t* counts, int64_t E,
                int64_t N, int64_t K, int64_t max_rows, hipStream_t s) {
   const int64_t g = grid_for(max_rows, E, Body::BM, N, Body::BN);
+  if constexpr (!FC1) {
+    if (o.cmb.out) {
+      const int64_t z = ceil_div(o.cmb.T, 8 * 16);  // 8 waves of 16 tokens
+      hipLaunchKernelGGL((gmm_mx_kernel<FC1, Body, true>), dim3(static_cast<unsigned>(g + z)),
+                         dim3(512), 0, s, a, b, o, counts, static_cast<int>(E), static_cast<int>(N),
+                         static_cast<int>(K), max_rows, static_cast<int>(z));
+      return;
+    }
+  }
   hipLaunchKernelGGL((gmm_mx_kernel<FC1, Body>), dim3(static_cast<unsigned>(g)), dim3(512), 0, s, a,
                      b, o, counts, static_cast<int>(E), static_cast<int>(N), static_cast<int>(K),
-                     max_rows);
+                     max_rows, 0);
 }
 
 moe_status validate_mx(const char* who, int64_t E, int64_t h, int64_t f, int64_t max_rows) {
@@ -385,6 +419,17 @@ moe_status validate_mx(const char* who, int64_t E, int64_t h, int64_t f, int64_t
   MOE_REQUIRE(E * f < (int64_t(1) << 31) && E * h < (int64_t(1) << 31), MOE_ERR_UNSUPPORTED,
               "%s: E*f or E*h too large", who);
   return MOE_OK;
+}
+
+void launch_fc2_mx(const MxA& a, const MxB& b, const MxOut& o, const int32_t* counts, int64_t E,
+                   int64_t h, int64_t f, int64_t max_rows, hipStream_t s) {
+  const int64_t avg = max_rows / E;
+  if (avg >= 192)
+    launch_mx<false, MxFc2B128w>(a, b, o, counts, E, h, f, max_rows, s);
+  else if (avg >= 80)
+    launch_mx<false, MxFc2B128>(a, b, o, counts, E, h, f, max_rows, s);
+  else
+    launch_mx<false, MxFc2B64w>(a, b, o, counts, E, h, f, max_rows, s);
 }
 
 }  // namespace
@@ -427,14 +472,30 @@ extern "C" moe_status moe_grouped_fc2_mxfp8(int64_t E, int64_t h, int64_t f, int
               MOE_ERR_ARG, "moe_grouped_fc2_mxfp8: NULL tensor argument");
   const MxA a{act_codes, act_scales, nullptr, max_rows, true};
   const MxB b{wd_codes, wd_scales, nullptr, nullptr};
-  const MxOut o{nullptr, nullptr, static_cast<uint16_t*>(expert_out), max_rows};
-  const hipStream_t s = as_stream(stream);
-  const int64_t avg = max_rows / E;
-  if (avg >= 192)
-    launch_mx<false, MxFc2B128w>(a, b, o, tokens_per_expert, E, h, f, max_rows, s);
-  else if (avg >= 80)
-    launch_mx<false, MxFc2B128>(a, b, o, tokens_per_expert, E, h, f, max_rows, s);
-  else
-    launch_mx<false, MxFc2B64w>(a, b, o, tokens_per_expert, E, h, f, max_rows, s);
+  MxOut o{nullptr, nullptr, static_cast<uint16_t*>(expert_out), max_rows};
+  launch_fc2_mx(a, b, o, tokens_per_expert, E, h, f, max_rows, as_stream(stream));
   return check_launch("moe_grouped_fc2_mxfp8");
+}
+
+extern "C" moe_status moe_grouped_fc2_combine_mxfp8(
+    int64_t E, int64_t h, int64_t f, int64_t max_rows, int64_t T, const uint8_t* act_codes,
+    const uint8_t* act_scales, const int32_t* tokens_per_expert, const uint8_t* wd_codes,
+    const uint8_t* wd_scales, const float* permuted_probs, const int32_t* sorted_token,
+    const int32_t* row_id_map, void* out, void* stream) {
+  moe_status st = validate_mx("moe_grouped_fc2_combine_mxfp8", E, h, f, max_rows);
+  if (st != MOE_OK) return st;
+  MOE_REQUIRE(T >= 0 && T < (int64_t(1) << 31), MOE_ERR_ARG,
+              "moe_grouped_fc2_combine_mxfp8: T out of range");
+  if (T == 0) return MOE_OK;
+  MOE_REQUIRE(tokens_per_expert && wd_codes && wd_scales && row_id_map && out, MOE_ERR_ARG,
+              "moe_grouped_fc2_combine_mxfp8: NULL tensor argument");
+  MOE_REQUIRE(max_rows == 0 || (act_codes && act_scales && permuted_probs && sorted_token),
+              MOE_ERR_ARG, "moe_grouped_fc2_combine_mxfp8: NULL tensor argument");
+  const MxA a{act_codes, act_scales, nullptr, max_rows, true};
+  const MxB b{wd_codes, wd_scales, nullptr, nullptr};
+  MxOut o{nullptr, nullptr, nullptr, max_rows};
+  o.cmb = CombineEpi{sorted_token, permuted_probs, static_cast<uint16_t*>(out), T};
+  o.row_id_map = row_id_map;
+  launch_fc2_mx(a, b, o, tokens_per_expert, E, h, f, max_rows, as_stream(stream));
+  return check_launch("moe_grouped_fc2_combine_mxfp8");
 }

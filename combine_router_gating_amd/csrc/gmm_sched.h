@@ -125,6 +125,43 @@ __device__ bool decode_tile(const int32_t* __restrict__ counts, int E, int64_t m
 
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
 
+// FC2 with the K = 1 combine as its epilogue: row r of the tile goes to
+// out[tok[r]] scaled by prob[r], rounded as the separate FC2 and combine
+// round it (y to bf16 first, then p*y + 0 in fp32, then to bf16), so the
+// result is bitwise theirs.
+struct CombineEpi {
+  const int32_t* tok;
+  const float* prob;
+  uint16_t* out;
+  int64_t T;
+  __device__ __forceinline__ int64_t token(int64_t r) const {
+    return min(max(static_cast<int64_t>(tok[r]), int64_t(0)), T - 1);
+  }
+};
+
+__device__ __forceinline__ uint16_t combine_bf16(float p, float acc) {
+  return f32_to_bf16_bits(fmaf(p, bf16_bits_to_f32(f32_to_bf16_bits(acc)), 0.f));
+}
+
+// Zero rows of the tokens with no kept row (row_id_map[t] outside
+// [0, max_rows)); a wave covers 16 tokens (workgroup z: tokens from
+// z * 16 * waves), 16-byte stores.
+__device__ __forceinline__ void zero_dropped_rows(const int32_t* __restrict__ row_id_map,
+                                                  int64_t max_rows, uint16_t* __restrict__ out,
+                                                  int64_t T, int N, int z) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int chunks = N / 8;
+  const int64_t t0 = (static_cast<int64_t>(z) * (blockDim.x >> 6) + wave) * 16;
+  for (int i = 0; i < 16; ++i) {
+    const int64_t t = t0 + i;
+    if (t >= T) break;
+    const int r = row_id_map[t];
+    if (r >= 0 && r < max_rows) continue;
+    uint4* row = reinterpret_cast<uint4*>(out + t * static_cast<int64_t>(N));
+    for (int c = lane; c < chunks; c += 64) row[c] = make_uint4(0, 0, 0, 0);
+  }
+}
+
 // Workgroups for the worst case: every expert's row count rounded up to BM
 // (surplus workgroups exit after decoding), a multiple of 8 (one per XCD).
 inline int64_t grid_for(int64_t max_rows, int64_t E, int BM, int64_t N, int BN) {

@@ -8,8 +8,9 @@ and probs only, and FC1 reads token rows through sorted_token);
 `overlap_shared` runs the shared expert on a second stream (default
 priority) from the start of the forward, joined before the combine;
 `fuse_combine` (on by default; top-1 bf16 layers without a shared expert)
-runs FC2 with the combine as its epilogue (moe_grouped_fc2_combine, one
-"fc2_combine" stage): no expert_out round trip, bitwise the same output.
+runs FC2 with the combine as its epilogue (moe_grouped_fc2_combine, or
+moe_grouped_fc2_combine_mxfp8 for MXFP8 experts; one "fc2_combine" stage):
+no expert_out round trip, bitwise the same output.
 `fuse_route_permute` (on by default) runs route and permute as one library
 call (moe_route_permute, one "route_permute" stage), which reuses the
 router's per-block counts for the permute; the outputs are bitwise those of
@@ -103,7 +104,7 @@ class MoELayerForward:
                 self.shared_actq = (e((T, fs), dtype=u8, device=dev),
                                     e((fs // 128, T, 4), dtype=u8, device=dev))
         self.overlap_shared = bool(overlap_shared and self.shared)
-        self.fused_combine = bool(fuse_combine and K == 1 and not self.shared and not self.mx
+        self.fused_combine = bool(fuse_combine and K == 1 and not self.shared
                                   and x.dtype == torch.bfloat16)
         if self.overlap_shared:
             self.side = torch.cuda.Stream(device=dev)  # default priority
@@ -209,6 +210,14 @@ class MoELayerForward:
             _p(i["shared_down"]), _p(self.shared_out), self._stream()))
 
     def fc2_combine(self):
+        if self.mx:
+            wd = self.wq["w_down"]
+            check("moe_grouped_fc2_combine_mxfp8", self.lib.moe_grouped_fc2_combine_mxfp8(
+                self.E, self.h, self.f, self.max_rows, self.T, _p(self.actq[0]),
+                _p(self.actq[1]), _p(self.tokens_per_expert), _p(wd[0]), _p(wd[1]),
+                _p(self.permuted_probs), _p(self.sorted_token), _p(self.row_id_map),
+                _p(self.out), self._stream()))
+            return
         check("moe_grouped_fc2_combine", self.lib.moe_grouped_fc2_combine(
             self.E, self.h, self.f, self.max_rows, self.dt, self.T, _p(self.act),
             _p(self.tokens_per_expert), _p(self.inp["w_down"]), _p(self.permuted_probs),

@@ -440,6 +440,35 @@ def moe_grouped_fc2_mxfp8(act_codes, act_scales, tokens_per_expert, wd, expert_o
     return expert_out
 
 
+def moe_grouped_fc2_combine_mxfp8(act_codes, act_scales, tokens_per_expert, wd, permuted_probs,
+                                  sorted_token, row_id_map, out=None):
+    """Top-1 combine fused into the MXFP8 FC2: out[t] = p * y[row of t] (bf16
+    [T,h]), zero for dropped tokens; bitwise moe_grouped_fc2_mxfp8 then
+    moe_combine (K=1)."""
+    rows, f = act_codes.shape
+    E, h, _ = wd[0].shape
+    _need(act_codes, "act_codes", torch.uint8)
+    _need(act_scales, "act_scales", torch.uint8, (f // 128, rows, 4))
+    _need(wd[0], "wd", torch.uint8, (E, h, f))
+    _need(wd[1], "wd scales", torch.uint8, (E, f // 128, h, 4))
+    _need(tokens_per_expert, "tokens_per_expert", torch.int32, (E,))
+    T = row_id_map.shape[0]
+    if row_id_map.dim() == 2 and row_id_map.shape[1] != 1:
+        raise ValueError("moe_grouped_fc2_combine_mxfp8 is for top-1 routing (row_id_map [T, 1])")
+    _need(row_id_map, "row_id_map", torch.int32)
+    _need(permuted_probs, "permuted_probs", torch.float32, (rows,))
+    _need(sorted_token, "sorted_token", torch.int32, (rows,))
+    if out is None:
+        out = torch.empty((T, h), dtype=torch.bfloat16, device=act_codes.device)
+    _need(out, "out", torch.bfloat16, (T, h))
+    st = _lib.load().moe_grouped_fc2_combine_mxfp8(
+        E, h, f, rows, T, _ptr(act_codes), _ptr(act_scales), _ptr(tokens_per_expert), _ptr(wd[0]),
+        _ptr(wd[1]), _ptr(permuted_probs), _ptr(sorted_token), _ptr(row_id_map), _ptr(out),
+        _stream())
+    check("moe_grouped_fc2_combine_mxfp8", st)
+    return out
+
+
 def moe_combine(expert_out: torch.Tensor, permuted_probs: torch.Tensor, row_id_map: torch.Tensor,
                 shared_out: Optional[torch.Tensor] = None,
                 out: Optional[torch.Tensor] = None) -> torch.Tensor:

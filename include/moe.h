@@ -61,7 +61,8 @@ typedef enum { MOE_DROP_POSITION = 0, MOE_DROP_PROBS = 1 } moe_drop_policy;
 
 /* Version of this interface (2: drop policy, padding to capacity,
  * sqrtsoftplus scores, router side outputs, gathering FC1, MXFP8 GEMMs;
- * 3: moe_route_permute, moe_grouped_fc2_combine). */
+ * 3: moe_route_permute, moe_grouped_fc2_combine,
+ * moe_grouped_fc2_combine_mxfp8). */
 int moe_abi_version(void);
 
 /* Message for the last non-OK status returned on the calling thread. */
@@ -377,6 +378,24 @@ moe_status moe_grouped_fc2_mxfp8(int64_t E, int64_t h, int64_t f, int64_t max_ro
                                  const uint8_t* act_codes, const uint8_t* act_scales,
                                  const int32_t* tokens_per_expert, const uint8_t* wd_codes,
                                  const uint8_t* wd_scales, void* expert_out, void* stream);
+
+/* moe_grouped_fc2_combine_mxfp8 — moe_grouped_fc2_mxfp8 with the top-1
+ * combine as its epilogue, as moe_grouped_fc2_combine is to
+ * moe_grouped_fc2 ([MC] §2: each token's one expert output weighted by its
+ * prob; dropped tokens get zero rows).  out [T,h] bf16 is bitwise what
+ * moe_grouped_fc2_mxfp8 followed by moe_combine (K = 1, no shared_out)
+ * writes.  permuted_probs, sorted_token, row_id_map as moe_permute writes
+ * them with K = 1.  Errors: those of moe_grouped_fc2_mxfp8; MOE_ERR_ARG for
+ * T out of range or a NULL tensor (act, probs and sorted_token may be NULL
+ * only when max_rows = 0).  T = 0 is a no-op. */
+moe_status moe_grouped_fc2_combine_mxfp8(int64_t E, int64_t h, int64_t f, int64_t max_rows,
+                                         int64_t T, const uint8_t* act_codes,
+                                         const uint8_t* act_scales,
+                                         const int32_t* tokens_per_expert,
+                                         const uint8_t* wd_codes, const uint8_t* wd_scales,
+                                         const float* permuted_probs,
+                                         const int32_t* sorted_token, const int32_t* row_id_map,
+                                         void* out, void* stream);
 
 /* ------------------------------------------------------------------------
  * Combine: unpermute and weight.  [MC] §2 (combine takes the expert outputs

@@ -241,3 +241,15 @@ def test_fused_entry_points_reject_bad_arguments_before_launching():
                       p, p, None)
     assert st == _lib.MOE_ERR_UNSUPPORTED and "multiples of 64" in msg
 
+    st, _ = _status("moe_grouped_fc2_combine_mxfp8", 8, 128, 256, 64, -1, p, p, p, p, p, p, p, p,
+                    p, None)
+    assert st == _lib.MOE_ERR_ARG  # T
+    st, _ = _status("moe_grouped_fc2_combine_mxfp8", 8, 128, 256, 64, 10, p, p, p, p, p, p, p,
+                    None, p, None)
+    assert st == _lib.MOE_ERR_ARG  # NULL row_id_map
+    st, _ = _status("moe_grouped_fc2_combine_mxfp8", 8, 128, 256, 64, 10, p, p, p, p, p, None, p,
+                    p, p, None)
+    assert st == _lib.MOE_ERR_ARG  # NULL probs with rows to combine
+    st, msg = _status("moe_grouped_fc2_combine_mxfp8", 8, 192, 256, 64, 10, p, p, p, p, p, p, p,
+                      p, p, None)
+    assert st == _lib.MOE_ERR_UNSUPPORTED and "multiples of 128" in msg

@@ -287,6 +287,67 @@ def test_mxfp8_gemm_counts_past_max_rows_stay_in_bounds():
     assert torch.isfinite(y[:R].float()).all()
 
 
+FC2_COMBINE_CASES = [
+    # T, h, f, E, capacity_factor, hot: the three FC2 bodies (avg rows < 80, < 192, >= 192)
+    (515, 128, 256, 16, 1.0, 2.0),     # drops, ~33 rows per expert
+    (2000, 256, 128, 16, 1.25, 1.0),   # ~157 rows per expert
+    (3000, 128, 256, 8, 0.0, 0.0),     # dropless, 375 rows per expert
+    (1, 128, 128, 4, 0.0, 0.0),
+    (40, 128, 128, 4, 0.05, 3.0),      # most tokens dropped
+]
+
+
+@pytest.mark.parametrize("T,h,f,E,cf,hot", FC2_COMBINE_CASES)
+def test_fc2_combine_mxfp8_is_bitwise_fc2_then_combine(T, h, f, E, cf, hot):
+    """The top-1 combine fused into the MXFP8 FC2 writes the bits of
+    moe_grouped_fc2_mxfp8 followed by moe_combine (K = 1), dropped tokens'
+    rows included; twice in a row into the same buffer."""
+    log(f"mxfp8 fc2+combine: T={T} h={h} f={f} E={E} cf={cf}")
+    rng = np.random.default_rng(T + h + E)
+    x = torch.from_numpy(rng.standard_normal((T, h))).to(torch.bfloat16).to(DEV)
+    w = torch.from_numpy(rng.standard_normal((E, h)) / h ** 0.5).float().to(DEV)
+    w[0] += hot / h ** 0.5
+    wg, wu, wd = (_weights(rng, E, n, k, 0.05) for n, k in ((f, h), (f, h), (h, f)))
+    r = moe.moe_route_permute(x, w, K=1, capacity_factor=cf, copy_rows=False)
+    tpe, st = r["tokens_per_expert"], r["sorted_token"]
+    R = st.shape[0]
+    xc, xs = moe.moe_mxfp8_quantize(x)
+    ac, asc = moe.moe_grouped_fc1_swiglu_mxfp8(xc, xs, st, tpe, wg, wu, R)
+    y = moe.moe_grouped_fc2_mxfp8(ac, asc, tpe, wd)
+    ref = moe.moe_combine(y, r["permuted_probs"], r["row_id_map"])
+    out = torch.full((T, h), float("nan"), dtype=torch.bfloat16, device=DEV)
+    for _ in range(2):
+        moe.moe_grouped_fc2_combine_mxfp8(ac, asc, tpe, wd, r["permuted_probs"], st,
+                                          r["row_id_map"], out=out)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+        out.fill_(float("nan"))
+
+
+def test_fc2_combine_mxfp8_on_an_empty_batch_and_no_rows():
+    """T = 0 is a no-op; max_rows = 0 (every token dropped) writes zero rows."""
+    E, h, f = 4, 128, 128
+    rng = np.random.default_rng(5)
+    wd = _weights(rng, E, h, f, 0.05)
+    cnt = torch.zeros((E,), dtype=torch.int32, device=DEV)
+    import ctypes
+    lib = moe.load()
+    q = ctypes.c_void_p(16)
+    assert lib.moe_grouped_fc2_combine_mxfp8(E, h, f, 0, 0, None, None, None, None, None, None,
+                                             None, None, None, None) == 0
+    T = 70
+    rid = torch.full((T,), -1, dtype=torch.int32, device=DEV)
+    out = torch.full((T, h), 3.0, dtype=torch.bfloat16, device=DEV)
+    p = lambda t: ctypes.c_void_p(t.data_ptr())
+    st = lib.moe_grouped_fc2_combine_mxfp8(E, h, f, 0, T, None, None, p(cnt), p(wd[0]), p(wd[1]),
+                                           None, None, p(rid), p(out),
+                                           ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert st == 0
+    torch.cuda.synchronize()
+    assert (out == 0).all()
+    assert lib.moe_grouped_fc2_combine_mxfp8(E, 192, f, 8, T, q, q, q, q, q, q, q, q, q, None) == 2
+
+
 def _act_bound(act_exact, sens, scale_bytes):
     """Allowed |dq(act) - act_exact|: half an E4M3 step under the block scale
     (or the saturation error) plus the MFMA accumulation bound."""
@@ -353,8 +414,9 @@ def test_layer_mxfp8_full_size_sampled(name, n_tok):
         dq = mx.mx_dequantize(act_c[rows], act_s[rows])
         bad = np.abs(dq - exact) > _act_bound(exact, sens, act_s[rows])
         assert not bad.any(), (name, e, int(bad.sum()))
-        assert_close(gpu_rows(layer.expert_out, rows), y_rows(rows, e, wd), "bf16",
-                     f"expert_out[{name}, e={e}]")
+        if not layer.fused_combine:  # (the fused FC2 writes no expert_out)
+            assert_close(gpu_rows(layer.expert_out, rows), y_rows(rows, e, wd), "bf16",
+                         f"expert_out[{name}, e={e}]")
     # sampled tokens: combine of the oracle's expert outputs (from the GPU's act codes)
     toks = rng.choice(cfg.T, size=n_tok, replace=False)
     shared = None
@@ -373,3 +435,13 @@ def test_layer_mxfp8_full_size_sampled(name, n_tok):
         if shared is not None:
             acc += shared[i]
         assert_close(gpu_rows(out, [t]), oracle.round_bf16(acc)[None], "bf16", f"out[{name}, t={t}]")
+    if layer.fused_combine:
+        # the fused FC2 + combine gives the bits of the two calls
+        out = out.clone()
+        plain = MoELayerForward(inp, K=cfg.K, score=cfg.score, pre_softmax=cfg.pre_softmax,
+                                capacity_factor=cfg.capacity_factor,
+                                min_capacity=cfg.min_capacity, gather=True, overlap_shared=True,
+                                precision="mxfp8", fuse_combine=False)
+        o2 = plain.forward()
+        torch.cuda.synchronize()
+        assert torch.equal(out, o2)
