@@ -552,7 +552,7 @@ void launch_bf16(const AOperand& a, const void* B0, const void* B1, void* C, con
                        static_cast<uint16_t*>(C), counts, static_cast<int>(E), static_cast<int>(N),
                        static_cast<int>(K), max_rows, cmb.epi, cmb.row_id_map, static_cast<int>(z));
   };
-  if constexpr (!FC1 && BMAX != 256) {  // (launch_gemm runs the combine epilogue on <= 128 rows)
+  if constexpr (!FC1 && (BMAX != 256 || BN == 128)) {  // (the combine epilogue's launches)
     if (cmb.epi.out) {
       args(gmm_bf16_kernel<FC1, BMAX, BN, NW, B256, B128, B64, true>);
       return;
@@ -578,23 +578,25 @@ void launch_f32(const AOperand& a, const void* B0, const void* B1, void* C, cons
 // not.  All variants run 8 waves (two per SIMD, so one wave's MFMAs cover
 // the other's waits); the shapes were chosen by timing the variants on the
 // five layer shapes.
-// FC1 takes 256-row m-tiles from 128 rows per expert on: an expert with
-// 129-256 rows is then one tile (the 256-row body) instead of a full tile
-// and a short one that streams the same weight slab again (timed on the
-// Switch layer with capacity 160: 440 vs 445 us).
-int pick_bm(int64_t max_rows, int64_t E, bool fc1) {
+// 256-row m-tiles from 128 rows per expert on: an expert with 129-256 rows
+// is then one tile (the 256-row body) instead of a full tile and a short
+// one that streams the same weight slab again (timed on the Switch layer
+// with capacity 160: FC1 440 vs 445 us, FC2 with the combine 234 vs 246 us).
+int pick_bm(int64_t max_rows, int64_t E) {
   const int64_t avg = max_rows / E;
-  if (avg >= (fc1 ? 128 : 192)) return 256;
+  if (avg >= 128) return 256;
   if (avg >= 80) return 128;
   return 64;
 }
 
 // Tile bodies (8 waves each; shapes chosen by timing variants on the five
 // layer shapes with random operands).  All bodies of one launch share the
-// column tiling.  256-row launches (large experts, MFMA-bound): FC1 tiles
-// hold BN=128 columns of W_gate and of W_up, FC2 tiles 256 columns of
-// W_down, and ragged tails run 128- or 64-row bodies.  128- and 64-row
-// launches (small experts, weight-streaming bound) use one body each.
+// column tiling.  256-row launches: FC1 tiles hold BN=128 columns of
+// W_gate and of W_up; FC2 tiles 256 columns of W_down from 192 rows per
+// expert on (MFMA-bound), else 128 (weight-streaming bound; also the
+// bodies of the combine epilogue); ragged tails run 128- or 64-row
+// bodies.  128- and 64-row launches (small experts, weight-streaming
+// bound) use one body each.
 using Fc1B256 = Body<256, 128, 2, 4, true, 2, 64, kSchedRing, 2>;
 using Fc1B128 = Body<128, 128, 2, 4, true, 3, 64, kSchedRing, 2>;
 using Fc1B64 = Body<64, 128, 2, 4, true, 4, 64>;
@@ -602,6 +604,8 @@ using Fc2B256 = Body<256, 256, 4, 2, false, 2, 64, kSchedRing, 2>;
 using Fc2B128 = Body<128, 256, 2, 4, false, 3, 64, kSchedRing, 2>;
 using Fc2B64 = Body<64, 256, 2, 4, false, 4, 64>;
 using Fc2B128n = Body<128, 128, 2, 4, false, 4, 64, kSchedRing, 1>;  // 128-row launches
+using Fc2N256 = Body<256, 128, 2, 4, false, 3, 64, kSchedRing, 2>;    // 256 rows, 128 columns
+using Fc2N64 = Body<64, 128, 2, 4, false, 4, 64>;
 
 template <bool FC1>
 void launch_gemm(int32_t dtype, const AOperand& A, const void* B0, const void* B1, void* C,
@@ -611,8 +615,7 @@ void launch_gemm(int32_t dtype, const AOperand& A, const void* B0, const void* B
     launch_f32<FC1>(A, B0, B1, C, counts, E, N, K, max_rows, s);
     return;
   }
-  int bm = pick_bm(max_rows, E, FC1);
-  if (!FC1 && cmb.epi.out && bm == 256) bm = 128;  // the combine epilogue runs 128- and 64-row bodies
+  const int bm = pick_bm(max_rows, E);
   if constexpr (FC1) {
     if (bm == 256)
       launch_bf16<true, 256, 128, 8, Fc1B256, Fc1B128, Fc1B64>(A, B0, B1, C, counts, E, N, K, max_rows, s);
@@ -621,8 +624,10 @@ void launch_gemm(int32_t dtype, const AOperand& A, const void* B0, const void* B
     else
       launch_bf16<true, 64, 128, 8, Fc1B64, Fc1B64, Fc1B64>(A, B0, B1, C, counts, E, N, K, max_rows, s);
   } else {
-    if (bm == 256)
+    if (bm == 256 && max_rows / E >= 192 && !cmb.epi.out)
       launch_bf16<false, 256, 256, 8, Fc2B256, Fc2B128, Fc2B64>(A, B0, B1, C, counts, E, N, K, max_rows, s);
+    else if (bm == 256)
+      launch_bf16<false, 256, 128, 8, Fc2N256, Fc2B128n, Fc2N64>(A, B0, B1, C, counts, E, N, K, max_rows, s, cmb);
     else if (bm == 128)
       launch_bf16<false, 128, 128, 8, Fc2B128n, Fc2B128n, Fc2B128n>(A, B0, B1, C, counts, E, N, K, max_rows, s, cmb);
     else

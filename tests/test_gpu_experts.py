@@ -34,7 +34,9 @@ CASES = [
     # counts, h, f, dtype
     ([60, 0, 13, 100], 64, 128, torch.bfloat16),
     ([130, 1, 0, 64, 200], 128, 192, torch.bfloat16),
-    ([100, 90, 150, 0, 97], 128, 192, torch.bfloat16),  # 128-row tiles (80 <= avg < 192)
+    ([100, 90, 150, 0, 97], 128, 192, torch.bfloat16),  # 128-row tiles (80 <= avg < 128)
+    # 256-row tiles of 128 columns in FC2 (128 <= avg < 192): 256-, 128- and 64-row bodies
+    ([150, 129, 100, 60, 270, 90], 128, 192, torch.bfloat16),
     ([300, 250], 128, 256, torch.bfloat16),          # 256-row tiles (avg >= 192)
     ([700, 513, 1], 192, 384, torch.bfloat16),       # tallest tiles (avg >= 512)
     ([0, 0, 5], 64, 64, torch.bfloat16),
@@ -87,7 +89,7 @@ def test_grouped_mlp_all_experts_share_weights():
 
 
 def test_weight_streaming_tiles_over_several_rounds():
-    """128-row tiles (80 <= rows per expert < 192), more tiles than the chip
+    """128-row tiles (80 <= rows per expert < 128), more tiles than the chip
     runs at once, an empty expert; the gathering FC1 reads the same rows
     through sorted_token and must give bitwise the same act."""
     rng = np.random.default_rng(11)

@@ -160,9 +160,10 @@ def test_route_permute_is_bitwise_route_then_permute(T, h, E, K, score, cf, poli
 
 
 FC2_COMBINE_CASES = [
-    # T, h, f, E, capacity_factor, hot: 64-, 128- and (forced to 128-) 256-row regimes
+    # T, h, f, E, capacity_factor, hot: the 64-, 128- and 256-row launches
     (515, 128, 256, 16, 1.0, 2.0),     # drops, ~32 rows per expert
-    (2000, 256, 128, 16, 1.25, 1.0),   # ~125 rows per expert (128-row tiles)
+    (2000, 256, 128, 16, 1.25, 1.0),   # capacity 157 (256-row tiles of 128 columns)
+    (1500, 128, 128, 16, 0.0, 0.0),    # dropless, ~94 rows per expert (128-row tiles)
     (3000, 128, 192, 8, 0.0, 0.0),     # dropless, ~375 rows per expert
     (1, 64, 64, 4, 0.0, 0.0),
     (40, 64, 128, 4, 0.05, 3.0),       # most tokens dropped
