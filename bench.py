@@ -145,6 +145,29 @@ def stage_work(cfg, n, T, fs, gather=False, mx=False):
     return w
 
 
+def copy_bandwidth(dev, mib=512, reps=10):
+    """GB/s (bytes read + written) of torch's device-to-device copy of a
+    `mib` MiB buffer: the plain streaming rate the HBM-bound kernels are
+    compared with."""
+    import torch
+
+    n = mib * (1 << 20) // 4
+    a = torch.ones(n, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(2):
+        b.copy_(a)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    t1.record()
+    torch.cuda.synchronize()
+    sec = t0.elapsed_time(t1) * 1e-3 / reps
+    del a, b
+    return 2 * n * 4 / sec / 1e9
+
+
 def cpu_baseline(cfg, inp, sample_tokens, min_seconds=10.0):
     """The oracle, as it stands, on the first `sample_tokens` tokens of the
     batch run as a batch of their own (same weights and routing options)."""
@@ -313,6 +336,10 @@ def main():
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = read_traffic(dom, cfg.name, mx)
     roof["kernel"] = dom
+    if roof["bound"] == "hbm":
+        # context for `frac`: what a plain device copy reaches on this GPU now
+        roof["copy_GBs"] = copy_bandwidth(dev)
+        roof["frac_of_copy"] = roof["achieved"] / roof["copy_GBs"]
     roof["algorithmic_bytes"] = nbytes
     roof["algorithmic_flops"] = flops
     roof["avg_launch_ms"] = dom_avg
