@@ -291,7 +291,7 @@ __global__ void __launch_bounds__(256) router_logits_ring(const uint16_t* __rest
 constexpr int kMaxSplit = 8;  // partial-logit planes at most
 
 struct MfmaPlan {
-  int shape;  // 0: 256 x 32 (E <= 32), 1: 256 x 64 (E <= 64), 2: 128 x 128 tokens x experts
+  int shape;  // 0: 256 x 32 (E <= 32), 1: 128 x 64 (E <= 64), 2: 128 x 128 tokens x experts
   int bt, be;
   int64_t gx, gz;
   int ksplit, kchunk;
@@ -306,7 +306,7 @@ struct MfmaPlan {
 MfmaPlan mfma_plan(int64_t T, int64_t h, int64_t E) {
   MfmaPlan p;
   p.shape = E <= 32 ? 0 : E <= 64 ? 1 : 2;
-  p.bt = p.shape == 2 ? 128 : 256;
+  p.bt = p.shape == 0 ? 256 : 128;
   p.be = p.shape == 0 ? 32 : p.shape == 1 ? 64 : 128;
   p.gx = ceil_div(T, p.bt);
   p.gz = ceil_div(E, p.be);
@@ -1068,7 +1068,7 @@ moe_status route_impl(const moe_route_desc* d, const void* x, const float* w_rou
       hipLaunchKernelGGL((router_logits_ring<4, 1, 1, 2, 3, 32>), grid, dim3(256), 0, s, xb, w_router,
                          part_ws, T, hh, Ei, p.kchunk);
     else if (p.shape == 1)
-      hipLaunchKernelGGL((router_logits_ring<2, 2, 1, 4, 3, 32>), grid, dim3(256), 0, s, xb, w_router,
+      hipLaunchKernelGGL((router_logits_ring<2, 2, 1, 2, 3, 32>), grid, dim3(256), 0, s, xb, w_router,
                          part_ws, T, hh, Ei, p.kchunk);
     else
       hipLaunchKernelGGL((router_logits_ring<1, 4, 1, 4, 3, 32>), grid, dim3(256), 0, s, xb, w_router,
