@@ -1,0 +1,51 @@
+"""Host-side logic of bench.py (no GPU): the one-GPU refusal and the
+algorithmic byte / flop accounting the roofline divides by."""
+import os
+import subprocess
+import sys
+
+import bench
+import datagen
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_bench_refuses_more_than_one_gpu():
+    p = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert p.returncode == 2
+    assert "one GPU" in p.stderr
+
+
+def _counts(cfg):
+    # a plausible capacity-limited load: every expert between 1 and 160 rows
+    return [1 + (37 * e) % 160 for e in range(cfg.E)]
+
+
+def test_fused_stages_move_fewer_bytes_than_the_pair_they_replace():
+    cfg = datagen.CONFIGS["switch"]
+    n = _counts(cfg)
+    N = sum(n)
+    for mx in (False, True):
+        w = bench.stage_work(cfg, n, cfg.T, 0, gather=True, mx=mx)
+        # FC2 + combine: same flops as FC2, no expert_out round trip (2 N h bf16
+        # bytes); the fused epilogue reads each row's token index besides its prob
+        assert w["fc2_combine"][1] == w["fc2"][1] == 2.0 * N * cfg.h * cfg.f
+        saved = w["fc2"][0] + w["combine"][0] - w["fc2_combine"][0]
+        assert saved == 2 * N * cfg.h * 2 - 4 * N
+        # route + permute as one call: the sum of the two
+        assert w["route_permute"][0] == w["route"][0] + w["permute"][0]
+        assert w["route_permute"][1] == w["route"][1]
+
+
+def test_mxfp8_gemm_bytes_are_about_half_of_bf16():
+    cfg = datagen.CONFIGS["switch"]
+    n = _counts(cfg)
+    bf = bench.stage_work(cfg, n, cfg.T, 0, gather=True, mx=False)
+    mx = bench.stage_work(cfg, n, cfg.T, 0, gather=True, mx=True)
+    for s in ("fc1", "fc2", "fc2_combine"):
+        assert mx[s][1] == bf[s][1]
+        assert 0.45 < mx[s][0] / bf[s][0] < 0.6, s
+    # FC1 weights dominate: 2 E_active h f values (one byte + a scale byte per 32)
+    active = sum(1 for v in n if v)
+    assert mx["fc1"][0] >= 2 * active * cfg.h * cfg.f * (1 + 1 / 32)
