@@ -68,7 +68,7 @@ __global__ void __launch_bounds__(256) count_scan_kernel(const int32_t* __restri
                                                          int32_t* __restrict__ kept, int64_t T,
                                                          float* __restrict__ probs,
                                                          uint8_t* __restrict__ rmap) {
-  constexpr int kPre = 1024;  // map column bytes of a chunk held in LDS (64 blocks)
+  constexpr int kPre = 1024;  // map column bytes of a chunk held in LDS (up to 64 blocks)
   __shared__ int64_t scratch[4];
   __shared__ int s_past;  // first block of the chunk whose entries all rank >= cap
   __shared__ uint8_t s_m[kPre];
@@ -178,8 +178,10 @@ void launch_block_hist(const uint8_t* map, int64_t T, int64_t E, int32_t* hist, 
 
 void launch_count_scan(const int32_t* hist, int64_t nblk, int64_t E, int64_t cap, int32_t* blkoff,
                        int32_t* kept, hipStream_t s, int64_t T, float* probs, uint8_t* rmap) {
-  // chunks of about 64 blocks, at most 16 per expert (each reads the whole row)
-  const int64_t chunks = std::min<int64_t>(16, std::max<int64_t>(1, ceil_div(nblk, 64)));
+  // chunks of about 32 blocks, at most 32 per expert (each reads the whole
+  // row); on the Switch-shaped router 9.0 us against 9.8 with 64-block
+  // chunks and 13.1 with 128
+  const int64_t chunks = std::min<int64_t>(32, std::max<int64_t>(1, ceil_div(nblk, 32)));
   hipLaunchKernelGGL(count_scan_kernel, dim3(static_cast<unsigned>(E), static_cast<unsigned>(chunks)),
                      dim3(256), 0, s, hist,
                      static_cast<int>(nblk), static_cast<int>(E), cap, blkoff, kept, T, probs, rmap);
