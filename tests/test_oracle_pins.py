@@ -121,6 +121,32 @@ def test_topk_signed_zero_is_a_tie():
     assert oracle.topk_indices(v, 1).tolist() == [[0]]
 
 
+# ------------------------------------------------------ gating linear
+
+def test_router_logits_golden_with_and_without_bias():
+    """The gating linear against hand-derived logits: a dropped bias, a bias
+    added after rounding, or fp32 accumulation each change a value."""
+    g = json.load(open(os.path.join(GOLDEN, "router_logits_worked.json")))
+    x, w, b = (np.array(g[k], np.float64) for k in ("x", "w", "b"))
+    got = oracle.router_logits(x, w, b)
+    assert got.dtype == np.float32
+    assert got.tolist() == g["logits"], g["cite"]
+    assert oracle.router_logits(x, w).tolist() == g["logits_no_bias"], g["cite"]
+    # bf16-representable inputs given as bf16-rounded float32 give the same
+    assert oracle.router_logits(x.astype(np.float32), w.astype(np.float32),
+                                b.astype(np.float32)).tolist() == g["logits"]
+
+
+def test_router_logits_transposes_the_weight():
+    """logits[t, e] pairs token t with weight row e (a square case, where a
+    transposed operand would still have the right shape)."""
+    x = np.array([[1.0, 0.0], [0.0, 1.0]])
+    w = np.array([[1.0, 2.0], [3.0, 4.0]])
+    assert oracle.router_logits(x, w).tolist() == [[1.0, 3.0], [2.0, 4.0]]
+    assert oracle.router_logits(x, w, np.array([10.0, 20.0])).tolist() == [[11.0, 23.0],
+                                                                             [12.0, 24.0]]
+
+
 # ------------------------------------------------------ routing worked cases
 
 def test_routing_golden_cases():
