@@ -62,7 +62,7 @@ struct MxOut {
   uint8_t* scales;     // FC1: act scales, k-tiled [N/128, max_rows, 4]
   uint16_t* bf16;      // FC2: expert_out [max_rows, N]
   int64_t rows;        // max_rows
-  CombineEpi cmb{nullptr, nullptr, nullptr, 0};  // FC2 with the top-1 combine: out [T, N]
+  CombineEpi cmb{nullptr, nullptr, nullptr, 0, nullptr};  // FC2 with the top-1 combine: out [T, N]
   const int32_t* row_id_map = nullptr;           // [T] (dropped tokens' zero rows)
 };
 
@@ -302,9 +302,10 @@ __device__ __forceinline__ void mx_tile(const Tile& tile, char* smem, const MxA&
             O.scales[((nc / kMxK) * O.rows + grow) * 4 + ((nc / 32) & 3)] = static_cast<uint8_t>(e + 127);
         }
       } else if constexpr (CMB) {
-        if (!row_ok || nc >= N) continue;
+        int64_t t;
+        if (!row_ok || nc >= N || !O.cmb.owns(grow, &t)) continue;
         const float p = O.cmb.prob[grow];
-        uint16_t* crow = O.cmb.out + O.cmb.token(grow) * N;
+        uint16_t* crow = O.cmb.out + t * N;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           uint2 pk;
@@ -494,7 +495,7 @@ extern "C" moe_status moe_grouped_fc2_combine_mxfp8(
   const MxA a{act_codes, act_scales, nullptr, max_rows, true};
   const MxB b{wd_codes, wd_scales, nullptr, nullptr};
   MxOut o{nullptr, nullptr, nullptr, max_rows};
-  o.cmb = CombineEpi{sorted_token, permuted_probs, static_cast<uint16_t*>(out), T};
+  o.cmb = CombineEpi{sorted_token, permuted_probs, static_cast<uint16_t*>(out), T, row_id_map};
   o.row_id_map = row_id_map;
   launch_fc2_mx(a, b, o, tokens_per_expert, E, h, f, max_rows, as_stream(stream));
   return check_launch("moe_grouped_fc2_combine_mxfp8");

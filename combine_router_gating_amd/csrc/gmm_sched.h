@@ -111,6 +111,27 @@ __device__ __forceinline__ int64_t xcd_tile(int64_t bid, int64_t total) {
   return L < total ? L : -1;
 }
 
+// Logical tile L of one dense GEMM (a single expert, e.g. the shared
+// expert) in grouped order: m-tiles are taken in bands of G, and a band is
+// walked n-tile by n-tile, so a run of consecutive tiles (one XCD's
+// workgroups at a time) covers a G x (run / G) block of output tiles.  Its
+// A and weight slabs are then a few each, not every m-tile of A against
+// one weight slab (as the expert-major order gives with one expert).
+template <int BM, int G>
+__device__ Tile dense_tile_at(int64_t L, int NT, int64_t rows, int64_t row_base) {
+  const int64_t MT = (rows + BM - 1) / BM;
+  const int64_t band = L / (static_cast<int64_t>(G) * NT);
+  const int64_t r = L - band * G * NT;
+  const int64_t gm = min(static_cast<int64_t>(G), MT - band * G);  // m-tiles in this band
+  const int64_t mt = band * G + r % gm;
+  Tile tile;
+  tile.e = 0;
+  tile.row0 = row_base + mt * BM;
+  tile.nrows = static_cast<int>(min(static_cast<int64_t>(BM), rows - mt * BM));
+  tile.n0 = static_cast<int>(r / gm);
+  return tile;
+}
+
 // Decode this workgroup's tile.  s_toff/s_roff/s_n: LDS arrays of E+1 / E+1 / E.
 template <int BM, int NTHREADS = kGemmThreads>
 __device__ bool decode_tile(const int32_t* __restrict__ counts, int E, int64_t max_rows, int NT,
@@ -123,19 +144,44 @@ __device__ bool decode_tile(const int32_t* __restrict__ counts, int E, int64_t m
   return true;
 }
 
+// Dense variant of decode_tile (E = 1): grouped order of dense_tile_at.
+template <int BM, int G>
+__device__ bool decode_dense_tile(const int32_t* __restrict__ counts, int64_t max_rows, int NT,
+                                  int* s_n, Tile& tile) {
+  if (threadIdx.x == 0) {
+    const int v = counts[0];
+    s_n[0] = v < 0 ? 0 : (v > max_rows ? static_cast<int>(max_rows) : v);
+  }
+  __syncthreads();
+  const int64_t rows = s_n[0];
+  const int64_t L = xcd_tile(blockIdx.x, (rows + BM - 1) / BM * NT);
+  if (L < 0) return false;
+  tile = dense_tile_at<BM, G>(L, NT, rows, 0);
+  return true;
+}
+
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
 
 // FC2 with the K = 1 combine as its epilogue: row r of the tile goes to
 // out[tok[r]] scaled by prob[r], rounded as the separate FC2 and combine
 // round it (y to bf16 first, then p*y + 0 in fp32, then to bf16), so the
-// result is bitwise theirs.
+// result is bitwise theirs.  Only the row a token's combine slot names
+// (rid[t] == r) is stored: with padding to capacity a token also owns rows
+// of prob 0 in other experts, which the combine never reads and which
+// must not overwrite its output.
 struct CombineEpi {
   const int32_t* tok;
   const float* prob;
   uint16_t* out;
   int64_t T;
+  const int32_t* rid;  // row_id_map [T] (K = 1)
   __device__ __forceinline__ int64_t token(int64_t r) const {
     return min(max(static_cast<int64_t>(tok[r]), int64_t(0)), T - 1);
+  }
+  // true when row r is its token's combine slot; *t receives the token
+  __device__ __forceinline__ bool owns(int64_t r, int64_t* t) const {
+    *t = token(r);
+    return static_cast<int64_t>(rid[*t]) == r;
   }
 };
 

@@ -126,3 +126,47 @@ def test_small_layer_with_options_against_the_oracle():
                              shared=shared_weights_from(inp), logits=logits)
     np.testing.assert_array_equal(layer.routing_map.cpu().numpy(), ref["routing_map"])
     assert_close(f64(out), ref["out"], cfg.dtype, "out")
+
+
+PAD_CFGS = [
+    # capacity 1.25 of a skewed top-1 router: some experts get fewer routed
+    # tokens than the capacity and are padded with tokens routed elsewhere
+    datagen.MoEConfig("pad-top1", T=515, h=128, E=16, K=1, f=256, dtype="bf16",
+                      capacity_factor=1.25, gate_bias="zipf"),
+    # capacity >= T: every token reaches every expert, all but one row of
+    # each token carry prob 0
+    datagen.MoEConfig("pad-all", T=96, h=128, E=4, K=1, f=128, dtype="bf16",
+                      capacity_factor=8.0),
+]
+
+
+@pytest.mark.parametrize("precision", ["bf16", "mxfp8"])
+@pytest.mark.parametrize("policy", ["position", "probs"])
+@pytest.mark.parametrize("cfg", PAD_CFGS, ids=lambda c: c.name)
+def test_fused_combine_with_padding_to_capacity(cfg, policy, precision):
+    """FC2 with the top-1 combine on a padded map: a token's padded rows
+    (prob 0, in other experts) must not overwrite its output.  The fused
+    output equals FC2 followed by the combine bit for bit, and the bf16
+    layer matches the oracle."""
+    log(f"fused combine, padded map ({policy}, {precision}): {cfg}")
+    inp = datagen.make_inputs(cfg, seed=11, device=DEV)
+    kw = dict(K=cfg.K, capacity_factor=cfg.capacity_factor, drop_policy=policy,
+              pad_to_capacity=True, gather=True, precision=precision)
+    fused = MoELayerForward(inp, fuse_combine=True, **kw)
+    plain = MoELayerForward(inp, fuse_combine=False, **kw)
+    assert fused.fused_combine and not plain.fused_combine
+    a = fused.forward().clone()
+    b = plain.forward().clone()
+    torch.cuda.synchronize()
+    N = int(fused.expert_offsets[-1].item())
+    # the padding really gave some token rows beyond its combine slot
+    assert N > int((fused.row_id_map >= 0).sum().item())
+    assert torch.equal(a, b)
+    if precision == "bf16":
+        ref = oracle.moe_forward(f64(inp["x"]), None, None,
+                                 (f64(inp["w_gate"]), f64(inp["w_up"]), f64(inp["w_down"])),
+                                 K=cfg.K, dtype=cfg.dtype, capacity_factor=cfg.capacity_factor,
+                                 drop_policy=policy, pad_to_capacity=True,
+                                 logits=fused.logits.cpu().numpy())
+        np.testing.assert_array_equal(fused.routing_map.cpu().numpy(), ref["routing_map"])
+        assert_close(f64(a), ref["out"], cfg.dtype, "out")
