@@ -153,19 +153,22 @@ __device__ __forceinline__ void lds_piece(int o, int& row, int& c) {
 // Direct global -> LDS 16-byte load: lane i writes LDS bytes
 // [lds_base + 16 i, lds_base + 16 i + 16).  Issued as inline assembly so the
 // compiler does not serialise the pipeline with conservative waits; the
-// kernel waits for these loads itself (vmcnt) before a barrier.
+// kernel waits for these loads itself (vmcnt) before a barrier.  The LDS
+// destination goes in m0 as an input operand of the statement, so the
+// compiler writes m0 itself and knows the statement reads it; the s_nop
+// covers the wait state between that write and the load.
 __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                :
-               : "v"(gptr), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "v"(gptr), "{m0}"(__builtin_amdgcn_readfirstlane(lds_base))
                : "memory");
 }
 
 // Direct 4-byte global -> LDS load: lane i writes LDS bytes [base + 4 i, +4).
 __device__ __forceinline__ void dma4(const void* gptr, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off"
                :
-               : "v"(gptr), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "v"(gptr), "{m0}"(__builtin_amdgcn_readfirstlane(lds_base))
                : "memory");
 }
 
