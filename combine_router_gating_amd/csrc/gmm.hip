@@ -41,6 +41,8 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kThreads = 256;
 constexpr int BK = 64;
+// m-tiles per band of the dense (single-expert) tile order
+constexpr int kDenseBand = 8;
 
 
 // ----------------------------------------------------------------- bf16 MFMA
@@ -122,8 +124,10 @@ __device__ __forceinline__ void store_tile_combine(const f32x16 (&acc)[1][MI][NI
     const int ml = wm * WTM + mi * 32 + l32;
     if (ml >= nrows) continue;
     const int64_t r = row0 + ml;
+    int64_t t;
+    if (!epi.owns(r, &t)) continue;
     const float p = epi.prob[r];
-    uint16_t* crow = epi.out + epi.token(r) * static_cast<int64_t>(N);
+    uint16_t* crow = epi.out + t * static_cast<int64_t>(N);
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
@@ -389,7 +393,7 @@ __device__ __forceinline__ void gmm_tile(const Tile& tile, char* smem,
 // bound and one body serves every tile.  The choice is uniform per
 // workgroup.
 template <bool FC1, int BMAX, int BN, int NW, class Body256, class Body128, class Body64,
-          bool CMB = false>
+          bool CMB = false, bool DENSE = false>
 __global__ void __launch_bounds__(NW * 64) gmm_bf16_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ gather, int64_t a_rows,
     const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1,
@@ -416,7 +420,9 @@ __global__ void __launch_bounds__(NW * 64) gmm_bf16_kernel(
     int* s_n = s_roff + kMaxExperts;
     int64_t* s_scan = reinterpret_cast<int64_t*>(s_n + kMaxExperts + 1);
     const bool mine =
-        decode_tile<BMAX, NW * 64>(counts, E, max_rows, NT, s_toff, s_roff, s_n, s_scan, tile);
+        DENSE ? decode_dense_tile<BMAX, kDenseBand>(counts, max_rows, NT, s_n, tile)
+              : decode_tile<BMAX, NW * 64>(counts, E, max_rows, NT, s_toff, s_roff, s_n, s_scan,
+                                           tile);
     __syncthreads();  // decode scratch is reused by the stages below
     if (!mine) return;
   }
@@ -535,7 +541,7 @@ struct AOperand {
 // workgroups after the tile workgroups zero the dropped tokens' rows (they
 // are dispatched last, onto CUs the last round of tiles leaves idle).
 struct CombineArgs {
-  CombineEpi epi{nullptr, nullptr, nullptr, 0};
+  CombineEpi epi{nullptr, nullptr, nullptr, 0, nullptr};
   const int32_t* row_id_map = nullptr;
 };
 
@@ -557,6 +563,10 @@ void launch_bf16(const AOperand& a, const void* B0, const void* B1, void* C, con
       args(gmm_bf16_kernel<FC1, BMAX, BN, NW, B256, B128, B64, true>);
       return;
     }
+  }
+  if (E == 1) {  // one dense GEMM (the shared expert): grouped tile order
+    args(gmm_bf16_kernel<FC1, BMAX, BN, NW, B256, B128, B64, false, true>);
+    return;
   }
   args(gmm_bf16_kernel<FC1, BMAX, BN, NW, B256, B128, B64, false>);
 }
@@ -721,7 +731,7 @@ extern "C" moe_status moe_grouped_fc2_combine(int64_t E, int64_t h, int64_t f, i
   MOE_REQUIRE(max_rows == 0 || (act && permuted_probs && sorted_token), MOE_ERR_ARG,
               "moe_grouped_fc2_combine: NULL tensor argument");
   CombineArgs cmb;
-  cmb.epi = CombineEpi{sorted_token, permuted_probs, static_cast<uint16_t*>(out), T};
+  cmb.epi = CombineEpi{sorted_token, permuted_probs, static_cast<uint16_t*>(out), T, row_id_map};
   cmb.row_id_map = row_id_map;
   launch_gemm<false>(dtype, AOperand{act, nullptr, max_rows}, w_down, nullptr, nullptr,
                      tokens_per_expert, E, h, f, max_rows, as_stream(stream), cmb);
