@@ -2,9 +2,10 @@
 
 One step = one full layer forward (route -> permute -> FC1+SwiGLU -> FC2
 (-> shared expert) -> combine) over one synthetic batch already resident in
-HBM.  Prints ONE JSON line.  The default workload is the Switch-style layer
-(T=8192, h=2048, E=64, top-1, capacity factor 1.25, bf16 with an fp32
-router); --config picks another layer shape.
+HBM.  Prints ONE JSON line.  The default workload is the DeepSeek-V3-shaped
+layer, the largest of the five layer shapes (T=8192, h=7168, E=256, top-8
+sigmoid with a selection-only expert bias, ffn 2048, one shared expert of
+ffn 2048, bf16 with an fp32 router); --config picks another layer shape.
 
 Per-stage durations come from HIP events recorded at every stage boundary
 on the stream the kernels run on, in a pass of K steps of their own
@@ -59,7 +60,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--config", default="switch")
+    p.add_argument("--config", default="dsv3")
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--cpu-sample-tokens", type=int, default=None,
                    help="tokens the oracle runs for the cpu_baseline leg (default: per layer)")
@@ -181,6 +182,7 @@ def cpu_baseline(cfg, inp, sample_tokens, min_seconds=10.0):
         blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         blas_threads = 1
+    affinity = len(os.sched_getaffinity(0))
     S = min(sample_tokens, cfg.T)
     f64 = datagen.to_f64
     x = f64(inp["x"][:S])
@@ -208,10 +210,72 @@ def cpu_baseline(cfg, inp, sample_tokens, min_seconds=10.0):
         total += time.perf_counter() - t0
         runs += 1
     dt = total / runs
-    return {"value": S / dt, "unit": "tokens/s", "cores": int(blas_threads), "kind": "oracle",
+    # the oracle's only multi-threaded part is NumPy's BLAS (the float64
+    # matmuls); everything else runs on one thread
+    return {"value": S / dt, "unit": "tokens/s", "cores": int(min(blas_threads, affinity)),
+            "kind": "oracle",
             "sample": f"first {S} of {cfg.T} tokens run as one batch (same weights and routing "
                       f"options; capacity recomputed for that batch), float64 NumPy, "
-                      f"{runs} run(s), {total:.1f} s in total"}
+                      f"{runs} run(s), {total:.1f} s in total",
+            "affinity_cores": affinity, "blas_threads": int(blas_threads),
+            "cpu_model": cpu_model()}
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return "unknown"
+
+
+class ClockSampler:
+    """Polls the GPU's reported shader clock (MHz, amd-smi through torch)
+    from a background thread while active; None if the query is not
+    available."""
+
+    def __init__(self, period_s: float = 0.01):
+        import threading
+        self.period = period_s
+        self.samples = []
+        self.stop = threading.Event()
+        self.thread = threading.Thread(target=self._run, daemon=True)
+        self.ok = True
+
+    def _run(self):
+        import torch
+        while not self.stop.is_set():
+            try:
+                self.samples.append(int(torch.cuda.clock_rate(0)))
+            except Exception:  # pragma: no cover - query unavailable
+                self.ok = False
+                return
+            self.stop.wait(self.period)
+
+    def __enter__(self):
+        import torch
+        try:  # the first query initialises amd-smi: keep it out of the timed steps
+            torch.cuda.clock_rate(0)
+        except Exception:  # pragma: no cover - query unavailable
+            self.ok = False
+            return self
+        self.thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self.stop.set()
+        if self.thread.is_alive():
+            self.thread.join()
+
+    def summary(self):
+        if not self.ok or not self.samples:
+            return None
+        v = sorted(self.samples)
+        return {"unit": "MHz", "min": v[0], "median": v[len(v) // 2], "max": v[-1],
+                "samples": len(v), "source": "amd-smi GFX clock via torch.cuda.clock_rate, "
+                "polled every 10 ms during the timed steps"}
 
 
 def torch_float32():
@@ -220,6 +284,16 @@ def torch_float32():
 
 
 DEFAULT_CPU_SAMPLE = {"tiny": 256, "switch": 8192, "mixtral": 256, "qwen3": 512, "dsv3": 128}
+
+
+def load_stats(n):
+    """tokens_per_expert spread: min, max, mean, coefficient of variation."""
+    import numpy as np
+    a = np.asarray(n, np.float64)
+    mean = float(a.mean()) if a.size else 0.0
+    return {"min": int(a.min()) if a.size else 0, "max": int(a.max()) if a.size else 0,
+            "mean": mean, "cv": float(a.std() / mean) if mean else 0.0,
+            "empty_experts": int((a == 0).sum())}
 
 
 def pct(v, q):
@@ -303,11 +377,12 @@ def main():
         return m
 
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        layer.forward(dom_mark(i))
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    with ClockSampler() as clock:
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            layer.forward(dom_mark(i))
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     dom_ms = [a.elapsed_time(b) for a, b in dom_ev]
 
@@ -336,10 +411,11 @@ def main():
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = read_traffic(dom, cfg.name, mx)
     roof["kernel"] = dom
+    # context for HBM fractions: what a plain device copy reaches on this GPU now
+    copy_gbs = copy_bandwidth(dev)
     if roof["bound"] == "hbm":
-        # context for `frac`: what a plain device copy reaches on this GPU now
-        roof["copy_GBs"] = copy_bandwidth(dev)
-        roof["frac_of_copy"] = roof["achieved"] / roof["copy_GBs"]
+        roof["copy_GBs"] = copy_gbs
+        roof["frac_of_copy"] = roof["achieved"] / copy_gbs
     roof["algorithmic_bytes"] = nbytes
     roof["algorithmic_flops"] = flops
     roof["avg_launch_ms"] = dom_avg
@@ -353,6 +429,9 @@ def main():
                            "p90": round(pct(per_step[s], 90), 4),
                            "GB/s": round(nb / sec_s / 1e9, 1),
                            "TFLOP/s": round(fl / sec_s / 1e12, 1) if fl else 0.0}
+        if s in ("permute", "combine", "quantize"):  # HBM-bound stages
+            stage_report[s]["frac_of_hbm_peak"] = round(nb / sec_s / 1e9 / HBM_PEAK_GBS, 4)
+            stage_report[s]["frac_of_copy"] = round(nb / sec_s / 1e9 / copy_gbs, 4)
 
     cold = None
     if not args.no_cold:
@@ -387,7 +466,8 @@ def main():
                    "parallelism": "single GPU, EP=1",
                    "gather_fc1": layer.gather, "shared_overlap": layer.overlap_shared,
                    "route_permute_fused": layer.fused, "fc2_combine_fused": layer.fused_combine,
-                   "expert_precision": args.precision},
+                   "expert_precision": args.precision,
+                   "tokens_per_expert": load_stats(n)},
         "forward_ms": {"mean": sum(fwd) / len(fwd), "p10": pct(fwd, 10), "p50": pct(fwd, 50),
                        "p90": pct(fwd, 90)},
         "gemm_tflops": gemm_tflops,
@@ -396,6 +476,8 @@ def main():
         "gemm_frac_of_attainable": gemm_tflops / attainable_tf,
         "stages": stage_report,
         "roofline": roof,
+        "copy_GBs": copy_gbs,
+        "clock": clock.summary(),
     }
     if cold:
         rec["cold"] = cold

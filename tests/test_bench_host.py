@@ -49,3 +49,19 @@ def test_mxfp8_gemm_bytes_are_about_half_of_bf16():
     # FC1 weights dominate: 2 E_active h f values (one byte + a scale byte per 32)
     active = sum(1 for v in n if v)
     assert mx["fc1"][0] >= 2 * active * cfg.h * cfg.f * (1 + 1 / 32)
+
+
+def test_load_stats_of_tokens_per_expert():
+    s = bench.load_stats([0, 2, 4, 6])
+    assert (s["min"], s["max"], s["mean"], s["empty_experts"]) == (0, 6, 3.0, 1)
+    assert abs(s["cv"] - (5.0 ** 0.5) / 3.0) < 1e-12  # population std sqrt(5) over mean 3
+
+
+def test_default_workload_is_the_largest_layer():
+    import sys as _sys
+    old = _sys.argv
+    _sys.argv = ["bench.py"]
+    try:
+        assert bench.parse().config == "dsv3"
+    finally:
+        _sys.argv = old
