@@ -73,6 +73,9 @@ def parse():
                    help="route and permute as two library calls")
     p.add_argument("--no-fuse-combine", action="store_true",
                    help="top-1 layers: FC2 and the combine as two library calls")
+    p.add_argument("--no-fold-shared", action="store_true",
+                   help="shared expert in launches of its own (on a second stream unless "
+                        "--no-overlap) instead of the routed launches' last tiles")
     p.add_argument("--no-cold", action="store_true", help="skip the cache-flushed pass")
     p.add_argument("--precision", default="bf16", choices=("bf16", "mxfp8"),
                    help="expert GEMM operands (mxfp8: OCP MX blocks of 32, E4M3)")
@@ -108,11 +111,12 @@ def read_traffic(stage: str, workload: str, mx: bool = False):
         return None
 
 
-def stage_work(cfg, n, T, fs, gather=False, mx=False):
+def stage_work(cfg, n, T, fs, gather=False, mx=False, fold=False):
     """Algorithmic bytes and flops of each stage (kept rows only, no padding,
     each tensor moved once).  With `gather` the permute moves no rows; with
     `mx` the GEMM operands are MXFP8 (1 byte per value + 1 scale byte per 32)
-    and the expert outputs bf16."""
+    and the expert outputs bf16; with `fold` the fc1 and fc2 stages also run
+    the shared expert's FC1 and FC2 (one launch each)."""
     b = 4 if cfg.dtype == "f32" else 2
     h, f, E, K = cfg.h, cfg.f, cfg.E, cfg.K
     N = int(sum(n))
@@ -127,6 +131,10 @@ def stage_work(cfg, n, T, fs, gather=False, mx=False):
     }
     if fs:
         w["shared"] = (3 * h * fs * b + 2 * T * h * b + 2 * T * fs * b, 6.0 * T * h * fs)
+        if fold:
+            f1, f2 = w["fc1"], w["fc2"]
+            w["fc1"] = (f1[0] + 2 * h * fs * b + T * h * b + T * fs * b, f1[1] + 4.0 * T * h * fs)
+            w["fc2"] = (f2[0] + h * fs * b + T * fs * b + T * h * b, f2[1] + 2.0 * T * h * fs)
     # route and permute as one call: the map and probs are written once and
     # read back by the scatter
     w["route_permute"] = (w["route"][0] + w["permute"][0], w["route"][1])
@@ -330,7 +338,8 @@ def main():
                             gather=gather, overlap_shared=not args.no_overlap,
                             precision=args.precision,
                             fuse_route_permute=not args.no_fuse_route_permute,
-                            fuse_combine=not args.no_fuse_combine)
+                            fuse_combine=not args.no_fuse_combine,
+                            fold_shared=not args.no_fold_shared)
     for _ in range(args.warmup):
         layer.forward()
     torch.cuda.synchronize()
@@ -388,7 +397,8 @@ def main():
 
     n = layer.tokens_per_expert.cpu().tolist()
     N = int(sum(n))
-    work = stage_work(cfg, n, cfg.T, layer.fs if layer.shared else 0, gather, mx)
+    work = stage_work(cfg, n, cfg.T, layer.fs if layer.shared else 0, gather, mx,
+                      layer.fold_shared)
     gemm_stages = [s for s in ("fc1", "fc2", "fc2_combine", "shared") if s in stage_ms]
     gemm_flops = sum(work[s][1] for s in gemm_stages)
     gemm_bytes = sum(work[s][0] for s in gemm_stages)
@@ -466,6 +476,7 @@ def main():
                    "parallelism": "single GPU, EP=1",
                    "gather_fc1": layer.gather, "shared_overlap": layer.overlap_shared,
                    "route_permute_fused": layer.fused, "fc2_combine_fused": layer.fused_combine,
+                   "shared_folded": layer.fold_shared,
                    "expert_precision": args.precision,
                    "tokens_per_expert": load_stats(n)},
         "forward_ms": {"mean": sum(fwd) / len(fwd), "p10": pct(fwd, 10), "p50": pct(fwd, 50),

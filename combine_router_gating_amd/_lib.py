@@ -54,6 +54,11 @@ SIGNATURES = {
                                        c_vp, c_vp, c_vp]),
     "moe_grouped_fc1_swiglu_gather": (c_i32, [c_i64, c_i64, c_i64, c_i64, c_i32, c_i64, c_vp,
                                               c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
+    "moe_grouped_fc1_swiglu_gather_shared": (c_i32, [c_i64, c_i64, c_i64, c_i64, c_i32, c_i64,
+                                                     c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64,
+                                                     c_vp, c_vp, c_vp, c_vp]),
+    "moe_grouped_fc2_shared": (c_i32, [c_i64, c_i64, c_i64, c_i64, c_i32, c_vp, c_vp, c_vp, c_vp,
+                                       c_i64, c_i64, c_vp, c_vp, c_vp, c_vp]),
     "moe_mxfp8_quantize": (c_i32, [c_i64, c_i64, c_i64, c_i32, c_vp, c_vp, c_vp, c_vp]),
     "moe_grouped_fc1_swiglu_mxfp8": (c_i32, [c_i64, c_i64, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp,
                                              c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),

@@ -392,13 +392,28 @@ __device__ __forceinline__ void gmm_tile(const Tile& tile, char* smem,
 // spent on padding); with shorter m-tiles the layer is weight-streaming
 // bound and one body serves every tile.  The choice is uniform per
 // workgroup.
+// A dense GEMM run by the last `wgs` workgroups of a grouped launch (the
+// shared expert: all tokens through one weight, [MC] §11), so that its tiles
+// fill the tail of the routed experts' tiles in one launch.  Grouped tile
+// order as dense_tile_at; A rows are not gathered.
+struct DenseTail {
+  const uint16_t* A;
+  const uint16_t* B0;
+  const uint16_t* B1;
+  uint16_t* C;
+  int64_t rows;
+  int N, K;
+  int wgs;
+};
+
 template <bool FC1, int BMAX, int BN, int NW, class Body256, class Body128, class Body64,
-          bool CMB = false, bool DENSE = false>
+          bool CMB = false, bool DENSE = false, bool TAIL = false>
 __global__ void __launch_bounds__(NW * 64) gmm_bf16_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ gather, int64_t a_rows,
     const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1,
     uint16_t* __restrict__ C, const int32_t* __restrict__ counts, int E, int N, int K,
-    int64_t max_rows, CombineEpi epi, const int32_t* __restrict__ row_id_map, int zero_wgs) {
+    int64_t max_rows, CombineEpi epi, const int32_t* __restrict__ row_id_map, int zero_wgs,
+    DenseTail dn) {
   if constexpr (CMB) {
     const int z = static_cast<int>(blockIdx.x) - static_cast<int>(gridDim.x - zero_wgs);
     if (z >= 0) {  // the last workgroups zero the dropped tokens (in the tail of the tiles)
@@ -412,29 +427,53 @@ __global__ void __launch_bounds__(NW * 64) gmm_bf16_kernel(
   constexpr int DECODE_BYTES = (3 * kMaxExperts + 1) * 4 + 64;
   static_assert(LDS >= DECODE_BYTES, "decode scratch aliases the stages");
   __shared__ __attribute__((aligned(1024))) char smem[LDS];
-  const int NT = (N + BN - 1) / BN;
+  // this workgroup's tile and its operands (the routed experts', or the
+  // dense tail's), then one call of the body its row count selects
   Tile tile;
-  {
+  const uint16_t* a = A;
+  const int32_t* g = gather;
+  int64_t ar = a_rows;
+  const uint16_t* b0 = B0;
+  const uint16_t* b1 = B1;
+  uint16_t* c = C;
+  int n = N, k = K;
+  bool mine;
+  // the tail starts at a multiple of 8, so d % 8 is this workgroup's XCD
+  const int d = TAIL ? static_cast<int>(blockIdx.x) - static_cast<int>(gridDim.x - dn.wgs) : -1;
+  if (TAIL && d >= 0) {
+    const int ntd = (dn.N + BN - 1) / BN;
+    const int64_t L = xcd_tile(d, (dn.rows + BMAX - 1) / BMAX * ntd);
+    mine = L >= 0;
+    if (mine) tile = dense_tile_at<BMAX, kDenseBand>(L, ntd, dn.rows, 0);
+    a = dn.A;
+    g = nullptr;
+    ar = dn.rows;
+    b0 = dn.B0;
+    b1 = dn.B1;
+    c = dn.C;
+    n = dn.N;
+    k = dn.K;
+  } else {
+    const int NT = (N + BN - 1) / BN;
     int* s_toff = reinterpret_cast<int*>(smem);
     int* s_roff = s_toff + kMaxExperts + 1;
     int* s_n = s_roff + kMaxExperts;
     int64_t* s_scan = reinterpret_cast<int64_t*>(s_n + kMaxExperts + 1);
-    const bool mine =
-        DENSE ? decode_dense_tile<BMAX, kDenseBand>(counts, max_rows, NT, s_n, tile)
-              : decode_tile<BMAX, NW * 64>(counts, E, max_rows, NT, s_toff, s_roff, s_n, s_scan,
-                                           tile);
+    mine = DENSE ? decode_dense_tile<BMAX, kDenseBand>(counts, max_rows, NT, s_n, tile)
+                 : decode_tile<BMAX, NW * 64>(counts, E, max_rows, NT, s_toff, s_roff, s_n, s_scan,
+                                              tile);
     __syncthreads();  // decode scratch is reused by the stages below
-    if (!mine) return;
   }
+  if (!mine) return;
   tile.nrows = __builtin_amdgcn_readfirstlane(tile.nrows);
   if constexpr (BMAX == 256) {
-    if (tile.nrows > 128) Body256::template run<CMB>(tile, smem, A, gather, a_rows, B0, B1, C, N, K, epi);
-    else if (tile.nrows > 64) Body128::template run<CMB>(tile, smem, A, gather, a_rows, B0, B1, C, N, K, epi);
-    else Body64::template run<CMB>(tile, smem, A, gather, a_rows, B0, B1, C, N, K, epi);
+    if (tile.nrows > 128) Body256::template run<CMB>(tile, smem, a, g, ar, b0, b1, c, n, k, epi);
+    else if (tile.nrows > 64) Body128::template run<CMB>(tile, smem, a, g, ar, b0, b1, c, n, k, epi);
+    else Body64::template run<CMB>(tile, smem, a, g, ar, b0, b1, c, n, k, epi);
   } else if constexpr (BMAX == 128) {
-    Body128::template run<CMB>(tile, smem, A, gather, a_rows, B0, B1, C, N, K, epi);
+    Body128::template run<CMB>(tile, smem, a, g, ar, b0, b1, c, n, k, epi);
   } else {
-    Body64::template run<CMB>(tile, smem, A, gather, a_rows, B0, B1, C, N, K, epi);
+    Body64::template run<CMB>(tile, smem, a, g, ar, b0, b1, c, n, k, epi);
   }
 }
 
@@ -545,19 +584,37 @@ struct CombineArgs {
   const int32_t* row_id_map = nullptr;
 };
 
+// The shared expert's dense GEMM, run in the same launch (see DenseTail).
+struct SharedArgs {
+  const void* A = nullptr;  // [rows, K]
+  const void* B0 = nullptr;
+  const void* B1 = nullptr;
+  void* C = nullptr;  // [rows, N]
+  int64_t rows = 0, N = 0, K = 0;
+};
+
 template <bool FC1, int BMAX, int BN, int NW, class B256, class B128, class B64>
 void launch_bf16(const AOperand& a, const void* B0, const void* B1, void* C, const int32_t* counts,
                  int64_t E, int64_t N, int64_t K, int64_t max_rows, hipStream_t s,
-                 const CombineArgs& cmb = CombineArgs{}) {
+                 const CombineArgs& cmb = CombineArgs{}, const SharedArgs& sh = SharedArgs{}) {
   const int64_t g = grid_for(max_rows, E, BMAX, N, BN);
   const int64_t z = cmb.epi.out ? ceil_div(cmb.epi.T, NW * 16) : 0;
+  DenseTail dn{static_cast<const uint16_t*>(sh.A), static_cast<const uint16_t*>(sh.B0),
+               static_cast<const uint16_t*>(sh.B1), static_cast<uint16_t*>(sh.C), sh.rows,
+               static_cast<int>(sh.N), static_cast<int>(sh.K), 0};
+  if (sh.rows > 0) dn.wgs = static_cast<int>(grid_for(sh.rows, 1, BMAX, sh.N, BN));
   const auto args = [&](auto kernel) {
-    hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(g + z)), dim3(NW * 64), 0, s,
+    hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(g + z + dn.wgs)), dim3(NW * 64), 0, s,
                        static_cast<const uint16_t*>(a.base), a.gather, a.rows,
                        static_cast<const uint16_t*>(B0), static_cast<const uint16_t*>(B1),
                        static_cast<uint16_t*>(C), counts, static_cast<int>(E), static_cast<int>(N),
-                       static_cast<int>(K), max_rows, cmb.epi, cmb.row_id_map, static_cast<int>(z));
+                       static_cast<int>(K), max_rows, cmb.epi, cmb.row_id_map, static_cast<int>(z),
+                       dn);
   };
+  if (dn.wgs > 0) {  // routed tiles, then the shared expert's (never with the combine epilogue)
+    args(gmm_bf16_kernel<FC1, BMAX, BN, NW, B256, B128, B64, false, false, true>);
+    return;
+  }
   if constexpr (!FC1 && (BMAX != 256 || BN == 128)) {  // (the combine epilogue's launches)
     if (cmb.epi.out) {
       args(gmm_bf16_kernel<FC1, BMAX, BN, NW, B256, B128, B64, true>);
@@ -620,7 +677,8 @@ using Fc2N64 = Body<64, 128, 2, 4, false, 4, 64>;
 template <bool FC1>
 void launch_gemm(int32_t dtype, const AOperand& A, const void* B0, const void* B1, void* C,
                  const int32_t* counts, int64_t E, int64_t N, int64_t K, int64_t max_rows,
-                 hipStream_t s, const CombineArgs& cmb = CombineArgs{}) {
+                 hipStream_t s, const CombineArgs& cmb = CombineArgs{},
+                 const SharedArgs& sh = SharedArgs{}) {
   if (dtype == MOE_F32) {
     launch_f32<FC1>(A, B0, B1, C, counts, E, N, K, max_rows, s);
     return;
@@ -628,20 +686,20 @@ void launch_gemm(int32_t dtype, const AOperand& A, const void* B0, const void* B
   const int bm = pick_bm(max_rows, E);
   if constexpr (FC1) {
     if (bm == 256)
-      launch_bf16<true, 256, 128, 8, Fc1B256, Fc1B128, Fc1B64>(A, B0, B1, C, counts, E, N, K, max_rows, s);
+      launch_bf16<true, 256, 128, 8, Fc1B256, Fc1B128, Fc1B64>(A, B0, B1, C, counts, E, N, K, max_rows, s, cmb, sh);
     else if (bm == 128)
-      launch_bf16<true, 128, 128, 8, Fc1B128, Fc1B128, Fc1B128>(A, B0, B1, C, counts, E, N, K, max_rows, s);
+      launch_bf16<true, 128, 128, 8, Fc1B128, Fc1B128, Fc1B128>(A, B0, B1, C, counts, E, N, K, max_rows, s, cmb, sh);
     else
-      launch_bf16<true, 64, 128, 8, Fc1B64, Fc1B64, Fc1B64>(A, B0, B1, C, counts, E, N, K, max_rows, s);
+      launch_bf16<true, 64, 128, 8, Fc1B64, Fc1B64, Fc1B64>(A, B0, B1, C, counts, E, N, K, max_rows, s, cmb, sh);
   } else {
     if (bm == 256 && max_rows / E >= 192 && !cmb.epi.out)
-      launch_bf16<false, 256, 256, 8, Fc2B256, Fc2B128, Fc2B64>(A, B0, B1, C, counts, E, N, K, max_rows, s);
+      launch_bf16<false, 256, 256, 8, Fc2B256, Fc2B128, Fc2B64>(A, B0, B1, C, counts, E, N, K, max_rows, s, cmb, sh);
     else if (bm == 256)
-      launch_bf16<false, 256, 128, 8, Fc2N256, Fc2B128n, Fc2N64>(A, B0, B1, C, counts, E, N, K, max_rows, s, cmb);
+      launch_bf16<false, 256, 128, 8, Fc2N256, Fc2B128n, Fc2N64>(A, B0, B1, C, counts, E, N, K, max_rows, s, cmb, sh);
     else if (bm == 128)
-      launch_bf16<false, 128, 128, 8, Fc2B128n, Fc2B128n, Fc2B128n>(A, B0, B1, C, counts, E, N, K, max_rows, s, cmb);
+      launch_bf16<false, 128, 128, 8, Fc2B128n, Fc2B128n, Fc2B128n>(A, B0, B1, C, counts, E, N, K, max_rows, s, cmb, sh);
     else
-      launch_bf16<false, 64, 256, 8, Fc2B64, Fc2B64, Fc2B64>(A, B0, B1, C, counts, E, N, K, max_rows, s, cmb);
+      launch_bf16<false, 64, 256, 8, Fc2B64, Fc2B64, Fc2B64>(A, B0, B1, C, counts, E, N, K, max_rows, s, cmb, sh);
   }
 }
 
@@ -700,6 +758,37 @@ extern "C" moe_status moe_grouped_fc1_swiglu_gather(int64_t E, int64_t h, int64_
   return check_launch("moe_grouped_fc1_swiglu_gather");
 }
 
+extern "C" moe_status moe_grouped_fc1_swiglu_gather_shared(
+    int64_t E, int64_t h, int64_t f, int64_t max_rows, int32_t dtype, int64_t T, const void* x,
+    const int32_t* sorted_token, const int32_t* tokens_per_expert, const void* w_gate,
+    const void* w_up, void* act, int64_t fs, const void* shared_gate, const void* shared_up,
+    void* shared_act, void* stream) {
+  const char* who = "moe_grouped_fc1_swiglu_gather_shared";
+  moe_status st = validate(who, E, h, f, max_rows, dtype);
+  if (st != MOE_OK) return st;
+  st = validate(who, 1, h, fs, T, dtype);  // the shared expert: one expert of T rows
+  if (st != MOE_OK) return st;
+  MOE_REQUIRE(T >= 0 && T < (int64_t(1) << 31), MOE_ERR_ARG, "%s: T out of range", who);
+  if (T == 0) return MOE_OK;
+  MOE_REQUIRE(x && shared_gate && shared_up && shared_act, MOE_ERR_ARG, "%s: NULL tensor argument",
+              who);
+  MOE_REQUIRE(max_rows == 0 || (sorted_token && tokens_per_expert && w_gate && w_up && act),
+              MOE_ERR_ARG, "%s: NULL tensor argument", who);
+  MOE_REQUIRE(dtype == MOE_BF16, MOE_ERR_UNSUPPORTED, "%s: bf16 only", who);
+  const hipStream_t s = as_stream(stream);
+  SharedArgs sh;
+  sh.A = x;
+  sh.B0 = shared_gate;
+  sh.B1 = shared_up;
+  sh.C = shared_act;
+  sh.rows = T;
+  sh.N = fs;
+  sh.K = h;
+  launch_gemm<true>(dtype, AOperand{x, sorted_token, T}, w_gate, w_up, act, tokens_per_expert, E, f,
+                    h, max_rows, s, CombineArgs{}, sh);
+  return check_launch(who);
+}
+
 extern "C" moe_status moe_grouped_fc2(int64_t E, int64_t h, int64_t f, int64_t max_rows,
                                       int32_t dtype, const void* act,
                                       const int32_t* tokens_per_expert, const void* w_down,
@@ -712,6 +801,37 @@ extern "C" moe_status moe_grouped_fc2(int64_t E, int64_t h, int64_t f, int64_t m
   launch_gemm<false>(dtype, AOperand{act, nullptr, max_rows}, w_down, nullptr, expert_out,
                      tokens_per_expert, E, h, f, max_rows, as_stream(stream));
   return check_launch("moe_grouped_fc2");
+}
+
+extern "C" moe_status moe_grouped_fc2_shared(int64_t E, int64_t h, int64_t f, int64_t max_rows,
+                                             int32_t dtype, const void* act,
+                                             const int32_t* tokens_per_expert, const void* w_down,
+                                             void* expert_out, int64_t T, int64_t fs,
+                                             const void* shared_act, const void* shared_down,
+                                             void* shared_out, void* stream) {
+  const char* who = "moe_grouped_fc2_shared";
+  moe_status st = validate(who, E, h, f, max_rows, dtype);
+  if (st != MOE_OK) return st;
+  st = validate(who, 1, h, fs, T, dtype);
+  if (st != MOE_OK) return st;
+  MOE_REQUIRE(T >= 0 && T < (int64_t(1) << 31), MOE_ERR_ARG, "%s: T out of range", who);
+  if (T == 0) return MOE_OK;
+  MOE_REQUIRE(shared_act && shared_down && shared_out, MOE_ERR_ARG, "%s: NULL tensor argument",
+              who);
+  MOE_REQUIRE(max_rows == 0 || (act && tokens_per_expert && w_down && expert_out), MOE_ERR_ARG,
+              "%s: NULL tensor argument", who);
+  MOE_REQUIRE(dtype == MOE_BF16, MOE_ERR_UNSUPPORTED, "%s: bf16 only", who);
+  const hipStream_t s = as_stream(stream);
+  SharedArgs sh;
+  sh.A = shared_act;
+  sh.B0 = shared_down;
+  sh.C = shared_out;
+  sh.rows = T;
+  sh.N = h;
+  sh.K = fs;
+  launch_gemm<false>(dtype, AOperand{act, nullptr, max_rows}, w_down, nullptr, expert_out,
+                     tokens_per_expert, E, h, f, max_rows, s, CombineArgs{}, sh);
+  return check_launch(who);
 }
 
 extern "C" moe_status moe_grouped_fc2_combine(int64_t E, int64_t h, int64_t f, int64_t max_rows,

@@ -11,6 +11,10 @@ priority) from the start of the forward, joined before the combine;
 runs FC2 with the combine as its epilogue (moe_grouped_fc2_combine, or
 moe_grouped_fc2_combine_mxfp8 for MXFP8 experts; one "fc2_combine" stage):
 no expert_out round trip, bitwise the same output.
+`fold_shared` (on by default; bf16 layers with a shared expert and the
+gathering FC1) runs the shared expert's FC1 and FC2 as the last tiles of
+the routed experts' FC1 and FC2 launches (moe_grouped_fc1_swiglu_gather_shared,
+moe_grouped_fc2_shared): one stream, bitwise the same output.
 `fuse_route_permute` (on by default) runs route and permute as one library
 call (moe_route_permute, one "route_permute" stage), which reuses the
 router's per-block counts for the permute; the outputs are bitwise those of
@@ -43,7 +47,8 @@ class MoELayerForward:
                  pre_softmax: bool = True, capacity_factor: float = 0.0, min_capacity: int = 0,
                  drop_policy: str = "position", pad_to_capacity: bool = False,
                  gather: bool = False, overlap_shared: bool = False, precision: str = "bf16",
-                 fuse_route_permute: bool = True, fuse_combine: bool = True):
+                 fuse_route_permute: bool = True, fuse_combine: bool = True,
+                 fold_shared: bool = True):
         self.lib = _lib.load()
         self.inp = inp
         x = _need(inp["x"], "x")
@@ -103,7 +108,11 @@ class MoELayerForward:
                 fs = self.fs
                 self.shared_actq = (e((T, fs), dtype=u8, device=dev),
                                     e((fs // 128, T, 4), dtype=u8, device=dev))
-        self.overlap_shared = bool(overlap_shared and self.shared)
+        # bf16 layers with a shared expert and the gathering FC1 run the shared
+        # expert's GEMMs as the last tiles of the routed launches
+        self.fold_shared = bool(fold_shared and self.shared and self.gather and not self.mx
+                                and x.dtype == torch.bfloat16)
+        self.overlap_shared = bool(overlap_shared and self.shared and not self.fold_shared)
         self.fused_combine = bool(fuse_combine and K == 1 and not self.shared
                                   and x.dtype == torch.bfloat16)
         if self.overlap_shared:
@@ -163,6 +172,14 @@ class MoELayerForward:
                 _p(self.sorted_token), _p(self.tokens_per_expert), _p(wg[0]), _p(wg[1]),
                 _p(wu[0]), _p(wu[1]), _p(self.actq[0]), _p(self.actq[1]), self._stream()))
             return
+        if self.fold_shared:
+            check("moe_grouped_fc1_swiglu_gather_shared",
+                  self.lib.moe_grouped_fc1_swiglu_gather_shared(
+                      self.E, self.h, self.f, self.max_rows, self.dt, self.T, _p(i["x"]),
+                      _p(self.sorted_token), _p(self.tokens_per_expert), _p(i["w_gate"]),
+                      _p(i["w_up"]), _p(self.act), self.fs, _p(i["shared_gate"]),
+                      _p(i["shared_up"]), _p(self.shared_act), self._stream()))
+            return
         if self.gather:
             check("moe_grouped_fc1_swiglu_gather", self.lib.moe_grouped_fc1_swiglu_gather(
                 self.E, self.h, self.f, self.max_rows, self.dt, self.T, _p(i["x"]),
@@ -180,6 +197,14 @@ class MoELayerForward:
             check("moe_grouped_fc2_mxfp8", self.lib.moe_grouped_fc2_mxfp8(
                 self.E, self.h, self.f, self.max_rows, _p(self.actq[0]), _p(self.actq[1]),
                 _p(self.tokens_per_expert), _p(wd[0]), _p(wd[1]), _p(self.expert_out),
+                self._stream()))
+            return
+        if self.fold_shared:
+            i = self.inp
+            check("moe_grouped_fc2_shared", self.lib.moe_grouped_fc2_shared(
+                self.E, self.h, self.f, self.max_rows, self.dt, _p(self.act),
+                _p(self.tokens_per_expert), _p(i["w_down"]), _p(self.expert_out), self.T,
+                self.fs, _p(self.shared_act), _p(i["shared_down"]), _p(self.shared_out),
                 self._stream()))
             return
         check("moe_grouped_fc2", self.lib.moe_grouped_fc2(
@@ -235,7 +260,7 @@ class MoELayerForward:
         for n in self.STAGES:
             if n == "quantize" and not self.mx:
                 continue
-            if n == "shared" and (not self.shared or self.overlap_shared):
+            if n == "shared" and (not self.shared or self.overlap_shared or self.fold_shared):
                 continue
             if n in ("route", "permute") and self.fused:
                 continue

@@ -167,16 +167,15 @@ def moe_route_permute(x: Optional[torch.Tensor], w_router: Optional[torch.Tensor
            "max_rows": rows, "capacity": moe_route_capacity(desc)}
     logits = e((T_, E), dtype=torch.float32, device=dev) if want_logits else None
     scores = e((T_, E), dtype=torch.float32, device=dev) if want_scores else None
+    args = (ctypes.byref(desc), _ptr(x) if (logits_in is None or copy_rows) else None,
+            _ptr(w_router) if logits_in is None else None, _ptr(b_router), _ptr(expert_bias),
+            _ptr(logits_in), _ptr(logits), _ptr(scores), _ptr(out["probs"]),
+            _ptr(out["routing_map"]), _ptr(out["tokens_per_expert"]), rows,
+            _ptr(out["permuted_x"]), _ptr(out["permuted_probs"]), _ptr(out["sorted_token"]),
+            _ptr(out["row_id_map"]), _ptr(out["expert_offsets"]))
     ws_bytes = int(lib.moe_route_permute_workspace_size(ctypes.byref(desc)))
     ws = e((max(ws_bytes, 1),), dtype=torch.uint8, device=dev)
-    st = lib.moe_route_permute(
-        ctypes.byref(desc), _ptr(x) if (logits_in is None or copy_rows) else None,
-        _ptr(w_router) if logits_in is None else None, _ptr(b_router), _ptr(expert_bias),
-        _ptr(logits_in), _ptr(logits), _ptr(scores), _ptr(out["probs"]), _ptr(out["routing_map"]),
-        _ptr(out["tokens_per_expert"]), rows, _ptr(out["permuted_x"]), _ptr(out["permuted_probs"]),
-        _ptr(out["sorted_token"]), _ptr(out["row_id_map"]), _ptr(out["expert_offsets"]), _ptr(ws),
-        ws_bytes, _stream())
-    check("moe_route_permute", st)
+    check("moe_route_permute", lib.moe_route_permute(*args, _ptr(ws), ws_bytes, _stream()))
     if logits is not None:
         out["logits"] = logits
     if scores is not None:
@@ -301,6 +300,62 @@ def moe_grouped_fc1_swiglu_gather(x: torch.Tensor, sorted_token: torch.Tensor,
                                                    _ptr(w_gate), _ptr(w_up), _ptr(act), _stream())
     check("moe_grouped_fc1_swiglu_gather", st)
     return act
+
+
+def moe_grouped_fc1_swiglu_gather_shared(x: torch.Tensor, sorted_token: torch.Tensor,
+                                         tokens_per_expert: torch.Tensor, w_gate: torch.Tensor,
+                                         w_up: torch.Tensor, shared_gate: torch.Tensor,
+                                         shared_up: torch.Tensor, act: Optional[torch.Tensor] = None,
+                                         shared_act: Optional[torch.Tensor] = None):
+    """The gathering FC1 of the routed experts and the shared expert's FC1
+    over all tokens in one launch; returns (act, shared_act)."""
+    E = _mlp_args(x, tokens_per_expert, w_gate, w_up)
+    T, h = x.shape
+    rows = sorted_token.shape[0]
+    _need(sorted_token, "sorted_token", torch.int32, (rows,))
+    f = w_gate.shape[1]
+    _need(w_gate, "w_gate", x.dtype, (E, f, h))
+    fs = shared_gate.shape[0]
+    _need(shared_gate, "shared_gate", x.dtype, (fs, h))
+    _need(shared_up, "shared_up", x.dtype, (fs, h))
+    if act is None:
+        act = torch.empty((rows, f), dtype=x.dtype, device=x.device)
+    if shared_act is None:
+        shared_act = torch.empty((T, fs), dtype=x.dtype, device=x.device)
+    _need(act, "act", x.dtype, (rows, f))
+    _need(shared_act, "shared_act", x.dtype, (T, fs))
+    st = _lib.load().moe_grouped_fc1_swiglu_gather_shared(
+        E, h, f, rows, _dtype_code(x, "x"), T, _ptr(x), _ptr(sorted_token),
+        _ptr(tokens_per_expert), _ptr(w_gate), _ptr(w_up), _ptr(act), fs, _ptr(shared_gate),
+        _ptr(shared_up), _ptr(shared_act), _stream())
+    check("moe_grouped_fc1_swiglu_gather_shared", st)
+    return act, shared_act
+
+
+def moe_grouped_fc2_shared(act: torch.Tensor, tokens_per_expert: torch.Tensor,
+                           w_down: torch.Tensor, shared_act: torch.Tensor,
+                           shared_down: torch.Tensor, expert_out: Optional[torch.Tensor] = None,
+                           shared_out: Optional[torch.Tensor] = None):
+    """The routed experts' FC2 and the shared expert's FC2 in one launch;
+    returns (expert_out, shared_out)."""
+    E = _mlp_args(act, tokens_per_expert, w_down)
+    rows, f = act.shape
+    h = w_down.shape[1]
+    _need(w_down, "w_down", act.dtype, (E, h, f))
+    T, fs = shared_act.shape
+    _need(shared_act, "shared_act", act.dtype, (T, fs))
+    _need(shared_down, "shared_down", act.dtype, (h, fs))
+    if expert_out is None:
+        expert_out = torch.empty((rows, h), dtype=act.dtype, device=act.device)
+    if shared_out is None:
+        shared_out = torch.empty((T, h), dtype=act.dtype, device=act.device)
+    _need(expert_out, "expert_out", act.dtype, (rows, h))
+    _need(shared_out, "shared_out", act.dtype, (T, h))
+    st = _lib.load().moe_grouped_fc2_shared(
+        E, h, f, rows, _dtype_code(act, "act"), _ptr(act), _ptr(tokens_per_expert), _ptr(w_down),
+        _ptr(expert_out), T, fs, _ptr(shared_act), _ptr(shared_down), _ptr(shared_out), _stream())
+    check("moe_grouped_fc2_shared", st)
+    return expert_out, shared_out
 
 
 def moe_grouped_fc2(act: torch.Tensor, tokens_per_expert: torch.Tensor, w_down: torch.Tensor,

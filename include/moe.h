@@ -62,7 +62,8 @@ typedef enum { MOE_DROP_POSITION = 0, MOE_DROP_PROBS = 1 } moe_drop_policy;
 /* Version of this interface (2: drop policy, padding to capacity,
  * sqrtsoftplus scores, router side outputs, gathering FC1, MXFP8 GEMMs;
  * 3: moe_route_permute, moe_grouped_fc2_combine,
- * moe_grouped_fc2_combine_mxfp8). */
+ * moe_grouped_fc2_combine_mxfp8; 4: moe_grouped_fc1_swiglu_gather_shared,
+ * moe_grouped_fc2_shared). */
 int moe_abi_version(void);
 
 /* Message for the last non-OK status returned on the calling thread. */
@@ -322,6 +323,47 @@ moe_status moe_grouped_fc1_swiglu_gather(int64_t E, int64_t h, int64_t f, int64_
                                          const int32_t* sorted_token,
                                          const int32_t* tokens_per_expert, const void* w_gate,
                                          const void* w_up, void* act, void* stream);
+
+/*
+ * moe_grouped_fc1_swiglu_gather_shared — moe_grouped_fc1_swiglu_gather and
+ * the shared expert's FC1 in ONE launch.  [MC] §2 and §11: the shared
+ * expert runs on every token beside the routed experts and its output is
+ * added after the combine; here its tiles are the last workgroups of the
+ * routed launch, so they fill the routed tiles' tail instead of competing
+ * with the router on a second stream.
+ *   routed arguments  as moe_grouped_fc1_swiglu_gather (max_rows may be 0)
+ *   fs                shared expert ffn size (a multiple of 64)
+ *   shared_gate, shared_up [fs,h] bf16
+ *   shared_act        [T,fs]  bf16  out: silu(x Wsg^T) * (x Wsu^T) for every token
+ * Results are bitwise those of the separate calls (moe_grouped_fc1_swiglu
+ * with E = 1 and T rows for the shared part).  bf16 only
+ * (MOE_ERR_UNSUPPORTED for fp32).
+ */
+moe_status moe_grouped_fc1_swiglu_gather_shared(int64_t E, int64_t h, int64_t f,
+                                                int64_t max_rows, int32_t dtype, int64_t T,
+                                                const void* x, const int32_t* sorted_token,
+                                                const int32_t* tokens_per_expert,
+                                                const void* w_gate, const void* w_up, void* act,
+                                                int64_t fs, const void* shared_gate,
+                                                const void* shared_up, void* shared_act,
+                                                void* stream);
+
+/*
+ * moe_grouped_fc2_shared — moe_grouped_fc2 and the shared expert's FC2 in
+ * ONE launch (as moe_grouped_fc1_swiglu_gather_shared is to FC1).
+ *   routed arguments  as moe_grouped_fc2 (max_rows may be 0)
+ *   T, fs             tokens and shared ffn size
+ *   shared_act        [T,fs] bf16
+ *   shared_down       [h,fs] bf16
+ *   shared_out        [T,h]  bf16  out: shared_act Wsd^T (pass it to moe_combine)
+ * Bitwise the separate calls.  bf16 only.
+ */
+moe_status moe_grouped_fc2_shared(int64_t E, int64_t h, int64_t f, int64_t max_rows,
+                                  int32_t dtype, const void* act,
+                                  const int32_t* tokens_per_expert, const void* w_down,
+                                  void* expert_out, int64_t T, int64_t fs,
+                                  const void* shared_act, const void* shared_down,
+                                  void* shared_out, void* stream);
 
 /* The second half of moe_grouped_mlp: expert_out = act W_down^T. */
 moe_status moe_grouped_fc2(int64_t E, int64_t h, int64_t f, int64_t max_rows, int32_t dtype,

@@ -28,7 +28,7 @@ def test_library_exports_every_declared_function():
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(_lib.SIGNATURES) == names
-    assert lib.moe_abi_version() == 3
+    assert lib.moe_abi_version() == 4
 
 
 def test_route_desc_layout_matches_c():
@@ -253,3 +253,4 @@ def test_fused_entry_points_reject_bad_arguments_before_launching():
     st, msg = _status("moe_grouped_fc2_combine_mxfp8", 8, 192, 256, 64, 10, p, p, p, p, p, p, p,
                       p, p, None)
     assert st == _lib.MOE_ERR_UNSUPPORTED and "multiples of 128" in msg
+

@@ -65,3 +65,12 @@ def test_default_workload_is_the_largest_layer():
         assert bench.parse().config == "dsv3"
     finally:
         _sys.argv = old
+
+
+def test_folded_stages_carry_the_shared_expert():
+    cfg = datagen.CONFIGS["dsv3"]
+    n = [256] * cfg.E
+    a = bench.stage_work(cfg, n, cfg.T, cfg.shared_f, gather=True)
+    b = bench.stage_work(cfg, n, cfg.T, cfg.shared_f, gather=True, fold=True)
+    for i in (0, 1):  # bytes, flops: fc1 + fc2 folded = routed pair + shared stage
+        assert b["fc1"][i] + b["fc2"][i] == a["fc1"][i] + a["fc2"][i] + a["shared"][i]

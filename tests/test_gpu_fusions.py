@@ -78,11 +78,15 @@ def test_layer_options_give_identical_outputs(name):
     kw = dict(K=cfg.K, score=cfg.score, pre_softmax=cfg.pre_softmax,
               capacity_factor=cfg.capacity_factor, min_capacity=cfg.min_capacity)
     outs = []
-    for gather, overlap, fuse, fcmb in ((False, False, False, False), (True, False, True, True),
-                                        (True, True, True, False), (False, True, False, True),
-                                        (False, False, True, True)):
+    for gather, overlap, fuse, fcmb, fold in ((False, False, False, False, False),
+                                              (True, False, True, True, True),
+                                              (True, True, True, False, False),
+                                              (False, True, False, True, True),
+                                              (False, False, True, True, False),
+                                              (True, False, False, False, True)):
         layer = MoELayerForward(inp, gather=gather, overlap_shared=overlap,
-                                fuse_route_permute=fuse, fuse_combine=fcmb, **kw)
+                                fuse_route_permute=fuse, fuse_combine=fcmb, fold_shared=fold,
+                                **kw)
         for _ in range(2):
             out = layer.forward()
         torch.cuda.synchronize()
@@ -170,3 +174,40 @@ def test_fused_combine_with_padding_to_capacity(cfg, policy, precision):
                                  logits=fused.logits.cpu().numpy())
         np.testing.assert_array_equal(fused.routing_map.cpu().numpy(), ref["routing_map"])
         assert_close(f64(a), ref["out"], cfg.dtype, "out")
+
+
+@pytest.mark.parametrize("T,E,K,f,fs,h", [(1024, 256, 8, 2048, 2048, 512),  # DSv3-like experts
+                                          (300, 8, 2, 512, 192, 256),
+                                          (77, 16, 1, 128, 320, 128)])
+def test_shared_expert_folded_into_the_routed_launches(T, E, K, f, fs, h):
+    """FC1 and FC2 with the shared expert's tiles appended: routed and shared
+    outputs bitwise the separate calls (the shared ones as an E = 1 GEMM of
+    T rows); also with no routed rows at all."""
+    cfg = datagen.MoEConfig("fold", T=T, h=h, E=E, K=K, f=f, dtype="bf16", score="sigmoid",
+                            expert_bias=True, shared_f=fs)
+    log(f"folded shared expert: {cfg}")
+    inp = datagen.make_inputs(cfg, seed=13, device=DEV)
+    r = moe.moe_route_permute(inp["x"], inp["w_router"], K=K, score="sigmoid",
+                              expert_bias=inp["expert_bias"], copy_rows=False)
+    x, st, tpe = inp["x"], r["sorted_token"], r["tokens_per_expert"]
+    act, sact = moe.moe_grouped_fc1_swiglu_gather_shared(
+        x, st, tpe, inp["w_gate"], inp["w_up"], inp["shared_gate"], inp["shared_up"])
+    y, sout = moe.moe_grouped_fc2_shared(act, tpe, inp["w_down"], sact, inp["shared_down"])
+    ones = torch.full((1,), T, dtype=torch.int32, device=DEV)
+    act_ref = moe.moe_grouped_fc1_swiglu_gather(x, st, tpe, inp["w_gate"], inp["w_up"])
+    sact_ref = moe.moe_grouped_fc1_swiglu(x, ones, inp["shared_gate"][None], inp["shared_up"][None])
+    y_ref = moe.moe_grouped_fc2(act_ref, tpe, inp["w_down"])
+    sout_ref = moe.moe_grouped_fc2(sact_ref, ones, inp["shared_down"][None])
+    torch.cuda.synchronize()
+    N = int(r["expert_offsets"][-1].item())
+    assert torch.equal(act[:N], act_ref[:N]) and torch.equal(y[:N], y_ref[:N])
+    assert torch.equal(sact, sact_ref) and torch.equal(sout, sout_ref)
+    # no routed rows: the launch is the shared expert's tiles alone
+    zero = torch.zeros_like(tpe)
+    _, sact0 = moe.moe_grouped_fc1_swiglu_gather_shared(
+        x, st[:0], zero, inp["w_gate"], inp["w_up"], inp["shared_gate"], inp["shared_up"],
+        act=act[:0])
+    _, sout0 = moe.moe_grouped_fc2_shared(act[:0], zero, inp["w_down"], sact0, inp["shared_down"],
+                                          expert_out=y[:0])
+    torch.cuda.synchronize()
+    assert torch.equal(sact0, sact_ref) and torch.equal(sout0, sout_ref)
