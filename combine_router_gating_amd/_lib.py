@@ -14,6 +14,7 @@ MOE_OK, MOE_ERR_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range
 MOE_F32, MOE_BF16 = 0, 1
 MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID, MOE_SCORE_SQRTSOFTPLUS = 0, 1, 2
 MOE_DROP_POSITION, MOE_DROP_PROBS = 0, 1
+MOE_NOALLOC_SCRATCH_BYTES = 32 << 20  # include/moe.h
 
 
 class RouteDesc(ctypes.Structure):
@@ -46,6 +47,9 @@ SIGNATURES = {
     "moe_route_permute": (c_i32, [ctypes.POINTER(RouteDesc), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                   c_vp, c_vp, c_vp, c_vp, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp,
                                   c_vp, c_sz, c_vp]),
+    "moe_route_permute_noalloc": (c_i32, [ctypes.POINTER(RouteDesc), c_vp, c_vp, c_vp, c_vp, c_vp,
+                                          c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_vp, c_vp, c_vp,
+                                          c_vp, c_vp, c_vp]),
     "moe_permute": (c_i32, [c_i64, c_i64, c_i64, c_i64, c_i32, c_vp, c_vp, c_vp, c_i64, c_vp,
                             c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "moe_grouped_mlp": (c_i32, [c_i64, c_i64, c_i64, c_i64, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp,

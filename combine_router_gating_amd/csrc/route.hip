@@ -23,6 +23,7 @@
 //                          with a capacity, also clears the entries ranked >= capacity
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 
 #include "moe_internal.h"
 
@@ -1232,4 +1233,74 @@ extern "C" moe_status moe_update_expert_bias(int64_t E, int64_t* local_tokens_pe
   hipLaunchKernelGGL(update_bias_kernel, dim3(1), dim3(256), 0, as_stream(stream),
                      static_cast<int>(E), local_tokens_per_expert, expert_bias, update_rate, reset);
   return check_launch("moe_update_expert_bias");
+}
+
+// ------------------------------------------------ allocation-free variant
+// moe_route_permute_noalloc takes its workspace from `scratch`, a file-scope
+// device array (each GPU the library runs on holds its own copy until the
+// process ends).  In host code the array's name is not a device address:
+// its address on the current device comes from hipGetSymbolAddress, looked
+// up once per device and kept in g_scratch_ptr.  No kernel here needs the
+// workspace cleared (every word a kernel reads was written earlier in the
+// same call), and calls that overlap on one GPU share the array and race.
+namespace moe {
+namespace {
+constexpr size_t kNoAllocScratchBytes = MOE_NOALLOC_SCRATCH_BYTES;
+static_assert(kNoAllocScratchBytes % 256 == 0, "whole 256-byte units");
+}  // namespace
+}  // namespace moe
+
+static __device__ __align__(256) char scratch[moe::kNoAllocScratchBytes];
+
+namespace moe {
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+moe_status scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess)
+    return fail(MOE_ERR_HIP, "moe_route_permute_noalloc: hipGetDevice: %s", hipGetErrorString(e));
+  MOE_REQUIRE(dev >= 0 && dev < kMaxDevices, MOE_ERR_UNSUPPORTED,
+              "moe_route_permute_noalloc: device %d beyond the %d the library tracks", dev,
+              kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(MOE_ERR_HIP, "moe_route_permute_noalloc: hipGetSymbolAddress(scratch): %s",
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+}  // namespace
+}  // namespace moe
+
+extern "C" moe_status moe_route_permute_noalloc(
+    const moe_route_desc* d, const void* x, const float* w_router, const float* b_router,
+    const float* expert_bias, const float* logits_in, float* logits_out, float* scores_out,
+    float* probs, uint8_t* routing_map, int32_t* tokens_per_expert, int64_t max_rows,
+    void* permuted_x, float* permuted_probs, int32_t* sorted_token, int32_t* row_id_map,
+    int32_t* expert_offsets, void* stream) {
+  moe_status st = validate(d);
+  if (st != MOE_OK) return st;
+  const size_t need = moe_route_permute_workspace_size(d);
+  MOE_REQUIRE(need <= kNoAllocScratchBytes, MOE_ERR_UNSUPPORTED,
+              "moe_route_permute_noalloc: this layer needs %zu bytes of workspace, more than the "
+              "%zu bytes of static scratch (use moe_route_permute with a workspace)",
+              need, kNoAllocScratchBytes);
+  void* ws = nullptr;
+  if (need > 0) {
+    st = scratch_address(&ws);
+    if (st != MOE_OK) return st;
+  }
+  return moe_route_permute(d, x, w_router, b_router, expert_bias, logits_in, logits_out,
+                           scores_out, probs, routing_map, tokens_per_expert, max_rows, permuted_x,
+                           permuted_probs, sorted_token, row_id_map, expert_offsets, ws,
+                           need > 0 ? kNoAllocScratchBytes : 0, stream);
 }

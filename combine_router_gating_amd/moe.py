@@ -128,9 +128,11 @@ def moe_route_permute(x: Optional[torch.Tensor], w_router: Optional[torch.Tensor
                       drop_policy: str = "position", pad_to_capacity: bool = False,
                       logits_in: Optional[torch.Tensor] = None, want_logits: bool = False,
                       want_scores: bool = False, copy_rows: bool = True,
-                      h: Optional[int] = None) -> Dict[str, torch.Tensor]:
+                      h: Optional[int] = None, noalloc: bool = False) -> Dict[str, torch.Tensor]:
     """moe_route then moe_permute of its outputs in one library call (the
-    permute reuses the router's counting); the union of both results."""
+    permute reuses the router's counting); the union of both results.  With
+    noalloc=True the call is moe_route_permute_noalloc (workspace in the
+    library's static scratch; the outputs are still allocated here)."""
     lib = _lib.load()
     if logits_in is not None:
         _need(logits_in, "logits_in", torch.float32)
@@ -173,9 +175,13 @@ def moe_route_permute(x: Optional[torch.Tensor], w_router: Optional[torch.Tensor
             _ptr(out["routing_map"]), _ptr(out["tokens_per_expert"]), rows,
             _ptr(out["permuted_x"]), _ptr(out["permuted_probs"]), _ptr(out["sorted_token"]),
             _ptr(out["row_id_map"]), _ptr(out["expert_offsets"]))
-    ws_bytes = int(lib.moe_route_permute_workspace_size(ctypes.byref(desc)))
-    ws = e((max(ws_bytes, 1),), dtype=torch.uint8, device=dev)
-    check("moe_route_permute", lib.moe_route_permute(*args, _ptr(ws), ws_bytes, _stream()))
+    if noalloc:
+        # the library's static scratch: no workspace is allocated here
+        check("moe_route_permute_noalloc", lib.moe_route_permute_noalloc(*args, _stream()))
+    else:
+        ws_bytes = int(lib.moe_route_permute_workspace_size(ctypes.byref(desc)))
+        ws = e((max(ws_bytes, 1),), dtype=torch.uint8, device=dev)
+        check("moe_route_permute", lib.moe_route_permute(*args, _ptr(ws), ws_bytes, _stream()))
     if logits is not None:
         out["logits"] = logits
     if scores is not None:

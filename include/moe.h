@@ -17,7 +17,9 @@
  * Conventions shared by every entry point:
  *   - Every tensor pointer is a DEVICE pointer owned by the caller.  The
  *     library never allocates or frees device memory and keeps no state
- *     between calls beyond the thread-local error message.
+ *     between calls beyond the thread-local error message (and, for
+ *     moe_route_permute_noalloc only, a static scratch array on each GPU
+ *     and its device address).
  *   - Tensors are dense, row-major (last index fastest), with no padding.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Calls only
  *     enqueue work on it and return; they never synchronise and never read
@@ -63,7 +65,7 @@ typedef enum { MOE_DROP_POSITION = 0, MOE_DROP_PROBS = 1 } moe_drop_policy;
  * sqrtsoftplus scores, router side outputs, gathering FC1, MXFP8 GEMMs;
  * 3: moe_route_permute, moe_grouped_fc2_combine,
  * moe_grouped_fc2_combine_mxfp8; 4: moe_grouped_fc1_swiglu_gather_shared,
- * moe_grouped_fc2_shared). */
+ * moe_grouped_fc2_shared; 5: moe_route_permute_noalloc). */
 int moe_abi_version(void);
 
 /* Message for the last non-OK status returned on the calling thread. */
@@ -250,6 +252,33 @@ moe_status moe_route_permute(const moe_route_desc* d, const void* x, const float
                              int64_t max_rows, void* permuted_x, float* permuted_probs,
                              int32_t* sorted_token, int32_t* row_id_map, int32_t* expert_offsets,
                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * moe_route_permute_noalloc — moe_route_permute for callers that cannot
+ * allocate device memory (code under graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same outputs, bit for bit, with the
+ * workspace taken from a static scratch array that the library holds on
+ * each GPU it runs on (MOE_NOALLOC_SCRATCH_BYTES per GPU, kept until the
+ * process ends; its device address is looked up once per device).  No
+ * allocation of any kind happens in the call.
+ *   arguments  as moe_route_permute, without workspace and workspace_bytes
+ * Errors: those of moe_route_permute; MOE_ERR_UNSUPPORTED (before anything
+ * is launched) when moe_route_permute_workspace_size(d) exceeds
+ * MOE_NOALLOC_SCRATCH_BYTES; MOE_ERR_HIP if the scratch address cannot be
+ * found.  Every call on one GPU uses the same scratch: calls that overlap
+ * in time on one GPU (different streams, or threads) race and must be
+ * serialised by the caller.  Nothing in the scratch needs clearing between
+ * calls (each call writes every word it reads).
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+moe_status moe_route_permute_noalloc(const moe_route_desc* d, const void* x,
+                                     const float* w_router, const float* b_router,
+                                     const float* expert_bias, const float* logits_in,
+                                     float* logits_out, float* scores_out, float* probs,
+                                     uint8_t* routing_map, int32_t* tokens_per_expert,
+                                     int64_t max_rows, void* permuted_x, float* permuted_probs,
+                                     int32_t* sorted_token, int32_t* row_id_map,
+                                     int32_t* expert_offsets, void* stream);
 
 /* ------------------------------------------------------------------------
  * Experts: SwiGLU MLP of every local expert as one grouped GEMM per layer.

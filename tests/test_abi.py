@@ -28,7 +28,7 @@ def test_library_exports_every_declared_function():
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(_lib.SIGNATURES) == names
-    assert lib.moe_abi_version() == 4
+    assert lib.moe_abi_version() == 5
 
 
 def test_route_desc_layout_matches_c():
@@ -254,3 +254,20 @@ def test_fused_entry_points_reject_bad_arguments_before_launching():
                       p, p, None)
     assert st == _lib.MOE_ERR_UNSUPPORTED and "multiples of 128" in msg
 
+
+def test_noalloc_rejects_layers_beyond_the_static_scratch():
+    """moe_route_permute_noalloc refuses, before any HIP call, a layer whose
+    workspace exceeds the static scratch (T=65536, E=256 needs ~80 MiB)."""
+    lib = moe.load()
+    d = moe.route_desc(65536, 4096, 256, 8, torch.bfloat16, "sigmoid", True, 0.0, 0, "position",
+                       False)
+    need = int(lib.moe_route_permute_workspace_size(ctypes.byref(d)))
+    assert need > _lib.MOE_NOALLOC_SCRATCH_BYTES
+    st = lib.moe_route_permute_noalloc(ctypes.byref(d), *([None] * 10), 65536 * 8,
+                                       *([None] * 5), None)
+    assert st == _lib.MOE_ERR_UNSUPPORTED
+    assert b"static scratch" in lib.moe_last_error()
+    # the limit the header states is the one the library applies
+    text = open(HEADER).read()
+    assert "#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)" in text
+    assert _lib.MOE_NOALLOC_SCRATCH_BYTES == 32 << 20
