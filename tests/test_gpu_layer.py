@@ -158,16 +158,16 @@ def test_layer_graph_capture_replays_match_eager():
 
 @pytest.mark.parametrize("name,n_tok", [("switch", 16), ("mixtral", 6), ("qwen3", 4), ("dsv3", 3)])
 def test_layer_bench_configuration_full_size_sampled(name, n_tok):
-    """The layer object exactly as the benchmark runs it (gathering FC1,
-    shared expert on a second stream) against the oracle on sampled tokens
-    of the full-size layer."""
+    """The layer object with the benchmark's options (gathering FC1; the
+    shared expert, where there is one, folded into the routed launches)
+    against the oracle on sampled tokens of the full-size layer."""
     from combine_router_gating_amd.layer import MoELayerForward
     cfg = datagen.CONFIGS[name]
     log(f"layer bench configuration: {cfg}")
     inp = datagen.make_inputs(cfg, seed=1, device=DEV)
     layer = MoELayerForward(inp, K=cfg.K, score=cfg.score, pre_softmax=cfg.pre_softmax,
                             capacity_factor=cfg.capacity_factor, min_capacity=cfg.min_capacity,
-                            gather=True, overlap_shared=True)
+                            gather=True)
     out = layer.forward()
     torch.cuda.synchronize()
     logits = layer.logits.cpu().numpy()
