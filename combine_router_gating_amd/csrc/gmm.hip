@@ -21,14 +21,29 @@
 // so that each of the 8 XCDs (which dispatch ids round-robin and own one L2
 // each) runs a contiguous range of logical tiles.
 //
-// bf16 path: 256 threads (4 waves), tile BM x BN per weight matrix, k-steps
-// of 64 staged through LDS (double-buffered, global loads for step k+1 in
-// flight while step k is multiplied), v_mfma_f32_32x32x16_bf16 with fp32
-// accumulation.  LDS rows are 128 bytes (8 chunks of 16 bytes) with chunk c
-// of row r stored at c ^ (r & 7), so both the 16-byte writes and the
-// 16-byte fragment reads are bank-conflict free.  The weight tile feeds the
-// MFMA's first operand and the activation tile its second, so each lane
-// ends with 4 consecutive output columns of one row (8-byte bf16 stores).
+// bf16 path: 8 waves per workgroup (two per SIMD); a tile body (the Body<>
+// table near the launch code) is BM rows x BN weight rows per matrix, with
+// one 32x32 block grid per wave and v_mfma_f32_32x32x16_bf16 accumulating in
+// fp32.  The operands stream through a ring of 2-4 LDS stages of 64 k each,
+// filled by direct global->LDS 16-byte loads (dma16) whose waits are
+// counted explicitly: before the last 16-wide k step of stage kt every wave
+// holds its fragments, the workgroup waits for stage kt+1 and passes one
+// barrier, and stage kt's slot is refilled with stage kt+STAGES, the new
+// loads issued one every SPREAD MFMAs.  LDS rows are 16-byte chunks
+// XOR-swizzled (lds_chunk_byte in moe_internal.h) so that the direct loads
+// fill contiguous 1 KB pieces and 16 lanes reading one chunk of 16 rows
+// touch 16 different bank groups.  The weight fragment is the MFMA's first
+// operand, so each lane ends with 4 consecutive output columns of one row
+// (8-byte bf16 stores); FC1 holds gate and up accumulators for the same
+// columns and applies silu(gate) * up in the epilogue.
+//
+// Launch variants: a 256-row launch picks the 256-, 128- or 64-row body per
+// tile from its row count; single-expert launches take a grouped (banded)
+// tile order; the shared expert's dense GEMM can ride as the last
+// workgroups of a routed launch (DenseTail); layers of large, alike experts
+// run one persistent workgroup per CU; top-1 layers can take the combine
+// as FC2's epilogue.
+#include <algorithm>
 #include <type_traits>
 
 #include "gmm_sched.h"
@@ -43,6 +58,8 @@ constexpr int kThreads = 256;
 constexpr int BK = 64;
 // m-tiles per band of the dense (single-expert) tile order
 constexpr int kDenseBand = 8;
+// experts a persistent launch keeps its decoded tables for
+constexpr int kPersistMaxExperts = 256;
 
 
 // ----------------------------------------------------------------- bf16 MFMA
@@ -407,7 +424,7 @@ struct DenseTail {
 };
 
 template <bool FC1, int BMAX, int BN, int NW, class Body256, class Body128, class Body64,
-          bool CMB = false, bool DENSE = false, bool TAIL = false>
+          bool CMB = false, bool DENSE = false, bool TAIL = false, bool PERSIST = false>
 __global__ void __launch_bounds__(NW * 64) gmm_bf16_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ gather, int64_t a_rows,
     const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1,
@@ -453,6 +470,49 @@ __global__ void __launch_bounds__(NW * 64) gmm_bf16_kernel(
     c = dn.C;
     n = dn.N;
     k = dn.K;
+  } else if constexpr (PERSIST) {
+    // One workgroup per CU runs tiles b, b + grid, b + 2 grid, ... of the
+    // XCD-ordered sequence (grid a multiple of 8, so each keeps its XCD):
+    // at each step the workgroups of an XCD hold consecutive tiles, as a
+    // one-tile-per-workgroup grid would, but the counts are decoded once
+    // and no workgroup is launched per tile.  Used where experts are
+    // large and alike in size (the tiles take about equal time, so the
+    // fixed assignment stays balanced).
+    const int NT = (N + BN - 1) / BN;
+    __shared__ int p_toff[kPersistMaxExperts + 1], p_roff[kPersistMaxExperts],
+        p_n[kPersistMaxExperts];
+    {
+      int* s_toff = reinterpret_cast<int*>(smem);
+      int* s_roff = s_toff + kMaxExperts + 1;
+      int* s_n = s_roff + kMaxExperts;
+      int64_t* s_scan = reinterpret_cast<int64_t*>(s_n + kMaxExperts + 1);
+      decode_counts<BMAX, NW * 64>(counts, E, max_rows, s_toff, s_roff, s_n, s_scan);
+      for (int i = threadIdx.x; i <= E; i += blockDim.x) {
+        p_toff[i] = s_toff[i];
+        if (i < E) {
+          p_roff[i] = s_roff[i];
+          p_n[i] = s_n[i];
+        }
+      }
+      __syncthreads();  // tables copied out of the stage area
+    }
+    const int64_t total = static_cast<int64_t>(p_toff[E]) * NT;
+    for (int64_t j = blockIdx.x;; j += gridDim.x) {
+      const int64_t L = xcd_tile(j, total);
+      if (L < 0) return;  // uniform: every wave of the workgroup leaves here
+      Tile t = tile_at<BMAX>(L, NT, E, p_toff, p_roff, p_n);
+      t.nrows = __builtin_amdgcn_readfirstlane(t.nrows);
+      if constexpr (BMAX == 256) {
+        if (t.nrows > 128) Body256::template run<CMB>(t, smem, a, g, ar, b0, b1, c, n, k, epi);
+        else if (t.nrows > 64) Body128::template run<CMB>(t, smem, a, g, ar, b0, b1, c, n, k, epi);
+        else Body64::template run<CMB>(t, smem, a, g, ar, b0, b1, c, n, k, epi);
+      } else if constexpr (BMAX == 128) {
+        Body128::template run<CMB>(t, smem, a, g, ar, b0, b1, c, n, k, epi);
+      } else {
+        Body64::template run<CMB>(t, smem, a, g, ar, b0, b1, c, n, k, epi);
+      }
+      __syncthreads();  // every wave is past the tile before its stages are refilled
+    }
   } else {
     const int NT = (N + BN - 1) / BN;
     int* s_toff = reinterpret_cast<int*>(smem);
@@ -593,7 +653,19 @@ struct SharedArgs {
   int64_t rows = 0, N = 0, K = 0;
 };
 
-template <bool FC1, int BMAX, int BN, int NW, class B256, class B128, class B64>
+// Workgroups of a persistent launch: one per CU (a multiple of 8, so that
+// each workgroup stays on one XCD), never more than the tiles.
+int64_t persistent_grid(int64_t tiles_grid) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus < 8)
+    cus = 256;
+  return std::min<int64_t>(tiles_grid, cus / 8 * 8);
+}
+
+template <bool FC1, int BMAX, int BN, int NW, class B256, class B128, class B64,
+          bool PERSIST = false>
 void launch_bf16(const AOperand& a, const void* B0, const void* B1, void* C, const int32_t* counts,
                  int64_t E, int64_t N, int64_t K, int64_t max_rows, hipStream_t s,
                  const CombineArgs& cmb = CombineArgs{}, const SharedArgs& sh = SharedArgs{}) {
@@ -613,6 +685,16 @@ void launch_bf16(const AOperand& a, const void* B0, const void* B1, void* C, con
   };
   if (dn.wgs > 0) {  // routed tiles, then the shared expert's (never with the combine epilogue)
     args(gmm_bf16_kernel<FC1, BMAX, BN, NW, B256, B128, B64, false, false, true>);
+    return;
+  }
+  if constexpr (PERSIST) {  // callers exclude the combine epilogue and the shared tail
+    if (g == 0) return;
+    hipLaunchKernelGGL((gmm_bf16_kernel<FC1, BMAX, BN, NW, B256, B128, B64, false, false, false, true>),
+                       dim3(static_cast<unsigned>(persistent_grid(g))), dim3(NW * 64), 0, s,
+                       static_cast<const uint16_t*>(a.base), a.gather, a.rows,
+                       static_cast<const uint16_t*>(B0), static_cast<const uint16_t*>(B1),
+                       static_cast<uint16_t*>(C), counts, static_cast<int>(E), static_cast<int>(N),
+                       static_cast<int>(K), max_rows, cmb.epi, cmb.row_id_map, 0, dn);
     return;
   }
   if constexpr (!FC1 && (BMAX != 256 || BN == 128)) {  // (the combine epilogue's launches)
@@ -673,6 +755,21 @@ using Fc2B64 = Body<64, 256, 2, 4, false, 4, 64>;
 using Fc2B128n = Body<128, 128, 2, 4, false, 4, 64, kSchedRing, 1>;  // 128-row launches
 using Fc2N256 = Body<256, 128, 2, 4, false, 3, 64, kSchedRing, 2>;    // 256 rows, 128 columns
 using Fc2N64 = Body<64, 128, 2, 4, false, 4, 64>;
+// 64-row bodies of persistent launches: 3 stages, leaving LDS for the
+// decoded per-expert tables
+using Fc1B64p = Body<64, 128, 2, 4, true, 3, 64>;
+using Fc2B64p = Body<64, 256, 2, 4, false, 3, 64>;
+
+// Persistent launches (see gmm_bf16_kernel) for experts of >= 512 rows on
+// average, at most kPersistMaxExperts of them: measured on the Mixtral- and
+// Qwen3-shaped layers FC1 -3 to -4 %, FC2 -5 to -10 %.  With smaller,
+// unevenly sized experts (the DeepSeek-V3-shaped layer, 1..836 rows) the
+// fixed tile assignment lets workgroups drift apart and lose their shared
+// L2 lines (FC1 +17 %), so those keep one tile per workgroup, which the
+// dispatcher hands out in order.
+bool use_persistent(int64_t max_rows, int64_t E) {
+  return E > 1 && E <= kPersistMaxExperts && max_rows / E >= 512;
+}
 
 template <bool FC1>
 void launch_gemm(int32_t dtype, const AOperand& A, const void* B0, const void* B1, void* C,
@@ -684,6 +781,13 @@ void launch_gemm(int32_t dtype, const AOperand& A, const void* B0, const void* B
     return;
   }
   const int bm = pick_bm(max_rows, E);
+  if (!cmb.epi.out && sh.rows == 0 && use_persistent(max_rows, E)) {  // bm == 256 here
+    if constexpr (FC1)
+      launch_bf16<true, 256, 128, 8, Fc1B256, Fc1B128, Fc1B64p, true>(A, B0, B1, C, counts, E, N, K, max_rows, s);
+    else
+      launch_bf16<false, 256, 256, 8, Fc2B256, Fc2B128, Fc2B64p, true>(A, B0, B1, C, counts, E, N, K, max_rows, s);
+    return;
+  }
   if constexpr (FC1) {
     if (bm == 256)
       launch_bf16<true, 256, 128, 8, Fc1B256, Fc1B128, Fc1B64>(A, B0, B1, C, counts, E, N, K, max_rows, s, cmb, sh);
