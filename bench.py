@@ -73,6 +73,8 @@ def parse():
                    help="route and permute as two library calls")
     p.add_argument("--no-fuse-combine", action="store_true",
                    help="top-1 layers: FC2 and the combine as two library calls")
+    p.add_argument("--no-tile-queue", action="store_true",
+                   help="grouped GEMMs with one workgroup per tile instead of the per-XCD tile queue")
     p.add_argument("--no-fold-shared", action="store_true",
                    help="shared expert in launches of its own (on a second stream unless "
                         "--no-overlap) instead of the routed launches' last tiles")
@@ -339,7 +341,8 @@ def main():
                             precision=args.precision,
                             fuse_route_permute=not args.no_fuse_route_permute,
                             fuse_combine=not args.no_fuse_combine,
-                            fold_shared=not args.no_fold_shared)
+                            fold_shared=not args.no_fold_shared,
+                            tile_queue=not args.no_tile_queue)
     for _ in range(args.warmup):
         layer.forward()
     torch.cuda.synchronize()
@@ -476,7 +479,7 @@ def main():
                    "parallelism": "single GPU, EP=1",
                    "gather_fc1": layer.gather, "shared_overlap": layer.overlap_shared,
                    "route_permute_fused": layer.fused, "fc2_combine_fused": layer.fused_combine,
-                   "shared_folded": layer.fold_shared,
+                   "shared_folded": layer.fold_shared, "tile_queue": layer.queue is not None,
                    "expert_precision": args.precision,
                    "tokens_per_expert": load_stats(n)},
         "forward_ms": {"mean": sum(fwd) / len(fwd), "p10": pct(fwd, 10), "p50": pct(fwd, 50),

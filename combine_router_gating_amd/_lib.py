@@ -15,6 +15,7 @@ MOE_F32, MOE_BF16 = 0, 1
 MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID, MOE_SCORE_SQRTSOFTPLUS = 0, 1, 2
 MOE_DROP_POSITION, MOE_DROP_PROBS = 0, 1
 MOE_NOALLOC_SCRATCH_BYTES = 32 << 20  # include/moe.h
+MOE_GEMM_QUEUE_BYTES = 2048  # include/moe.h
 
 
 class RouteDesc(ctypes.Structure):
@@ -53,16 +54,16 @@ SIGNATURES = {
     "moe_permute": (c_i32, [c_i64, c_i64, c_i64, c_i64, c_i32, c_vp, c_vp, c_vp, c_i64, c_vp,
                             c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "moe_grouped_mlp": (c_i32, [c_i64, c_i64, c_i64, c_i64, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp,
-                                c_vp, c_vp, c_vp]),
+                                c_vp, c_vp, c_vp, c_vp]),
     "moe_grouped_fc1_swiglu": (c_i32, [c_i64, c_i64, c_i64, c_i64, c_i32, c_vp, c_vp, c_vp,
-                                       c_vp, c_vp, c_vp]),
+                                       c_vp, c_vp, c_vp, c_vp]),
     "moe_grouped_fc1_swiglu_gather": (c_i32, [c_i64, c_i64, c_i64, c_i64, c_i32, c_i64, c_vp,
-                                              c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
+                                              c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "moe_grouped_fc1_swiglu_gather_shared": (c_i32, [c_i64, c_i64, c_i64, c_i64, c_i32, c_i64,
                                                      c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64,
-                                                     c_vp, c_vp, c_vp, c_vp]),
+                                                     c_vp, c_vp, c_vp, c_vp, c_vp]),
     "moe_grouped_fc2_shared": (c_i32, [c_i64, c_i64, c_i64, c_i64, c_i32, c_vp, c_vp, c_vp, c_vp,
-                                       c_i64, c_i64, c_vp, c_vp, c_vp, c_vp]),
+                                       c_i64, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "moe_mxfp8_quantize": (c_i32, [c_i64, c_i64, c_i64, c_i32, c_vp, c_vp, c_vp, c_vp]),
     "moe_grouped_fc1_swiglu_mxfp8": (c_i32, [c_i64, c_i64, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp,
                                              c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
@@ -70,7 +71,7 @@ SIGNATURES = {
                                       c_vp, c_vp]),
     "moe_grouped_fc2_combine_mxfp8": (c_i32, [c_i64, c_i64, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp,
                                               c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
-    "moe_grouped_fc2": (c_i32, [c_i64, c_i64, c_i64, c_i64, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp]),
+    "moe_grouped_fc2": (c_i32, [c_i64, c_i64, c_i64, c_i64, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "moe_grouped_fc2_combine": (c_i32, [c_i64, c_i64, c_i64, c_i64, c_i32, c_i64, c_vp, c_vp, c_vp,
                                         c_vp, c_vp, c_vp, c_vp, c_vp]),
     "moe_combine": (c_i32, [c_i64, c_i64, c_i64, c_i32, c_vp, c_vp, c_vp, c_i64, c_vp, c_vp,

@@ -57,7 +57,16 @@ struct Chunk<false> {
 // A wave's loads for KG of its token's K rows (KU 16-byte chunks per lane of
 // each) are all issued before any is accumulated, so a token keeps KG*KU*1 KB
 // in flight instead of one row's chunks at a time; the accumulation order
-// (ascending k, one fma per element) is unchanged.
+// (ascending k, one fma per element) is unchanged.  Expert rows and shared
+// rows are read exactly once, so their loads are non-temporal (measured on
+// the DeepSeek-V3-shaped layer: 247 -> 219 us, 4.8 -> 5.35 TB/s; the
+// output stores keep the default policy, non-temporal stores were slower).
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_once(const uint4* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 template <bool BF16, int KG, int KU>
 __global__ void __launch_bounds__(256) combine_kernel(const uint4* __restrict__ y,
                                                       const float* __restrict__ pprobs,
@@ -85,7 +94,7 @@ __global__ void __launch_bounds__(256) combine_kernel(const uint4* __restrict__ 
 #pragma unroll
       for (int u = 0; u < KU; ++u) {
         const int c = c0 + u * 64 + lane;
-        if (c < chunks) sh[u] = shared[t * chunks + c];
+        if (c < chunks) sh[u] = load_once(shared + t * chunks + c);
       }
     }
     float acc[KU][C::N];
@@ -110,7 +119,7 @@ __global__ void __launch_bounds__(256) combine_kernel(const uint4* __restrict__ 
 #pragma unroll
         for (int u = 0; u < KU; ++u) {
           const int c = c0 + u * 64 + lane;
-          if (c < chunks) raw[g][u] = src[c];
+          if (c < chunks) raw[g][u] = load_once(src + c);
         }
       }
 #pragma unroll

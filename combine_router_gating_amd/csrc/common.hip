@@ -189,6 +189,6 @@ void launch_count_scan(const int32_t* hist, int64_t nblk, int64_t E, int64_t cap
 
 }  // namespace moe
 
-extern "C" int moe_abi_version(void) { return 5; }
+extern "C" int moe_abi_version(void) { return 6; }
 
 extern "C" const char* moe_last_error(void) { return moe::g_last_error.c_str(); }

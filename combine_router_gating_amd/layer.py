@@ -48,7 +48,7 @@ class MoELayerForward:
                  drop_policy: str = "position", pad_to_capacity: bool = False,
                  gather: bool = False, overlap_shared: bool = False, precision: str = "bf16",
                  fuse_route_permute: bool = True, fuse_combine: bool = True,
-                 fold_shared: bool = True):
+                 fold_shared: bool = True, tile_queue: bool = True):
         self.lib = _lib.load()
         self.inp = inp
         x = _need(inp["x"], "x")
@@ -113,6 +113,9 @@ class MoELayerForward:
         self.fold_shared = bool(fold_shared and self.shared and self.gather and not self.mx
                                 and x.dtype == torch.bfloat16)
         self.overlap_shared = bool(overlap_shared and self.shared and not self.fold_shared)
+        # the grouped GEMMs' tile queue (zeroed once; every call leaves it zeroed)
+        self.queue = (torch.zeros((_lib.MOE_GEMM_QUEUE_BYTES // 4,), dtype=torch.int32, device=dev)
+                      if tile_queue else None)
         self.fused_combine = bool(fuse_combine and K == 1 and not self.shared
                                   and x.dtype == torch.bfloat16)
         if self.overlap_shared:
@@ -178,18 +181,18 @@ class MoELayerForward:
                       self.E, self.h, self.f, self.max_rows, self.dt, self.T, _p(i["x"]),
                       _p(self.sorted_token), _p(self.tokens_per_expert), _p(i["w_gate"]),
                       _p(i["w_up"]), _p(self.act), self.fs, _p(i["shared_gate"]),
-                      _p(i["shared_up"]), _p(self.shared_act), self._stream()))
+                      _p(i["shared_up"]), _p(self.shared_act), _p(self.queue), self._stream()))
             return
         if self.gather:
             check("moe_grouped_fc1_swiglu_gather", self.lib.moe_grouped_fc1_swiglu_gather(
                 self.E, self.h, self.f, self.max_rows, self.dt, self.T, _p(i["x"]),
                 _p(self.sorted_token), _p(self.tokens_per_expert), _p(i["w_gate"]), _p(i["w_up"]),
-                _p(self.act), self._stream()))
+                _p(self.act), _p(self.queue), self._stream()))
             return
         check("moe_grouped_fc1_swiglu", self.lib.moe_grouped_fc1_swiglu(
             self.E, self.h, self.f, self.max_rows, self.dt, _p(self.permuted_x),
             _p(self.tokens_per_expert), _p(i["w_gate"]), _p(i["w_up"]), _p(self.act),
-            self._stream()))
+            _p(self.queue), self._stream()))
 
     def fc2(self):
         if self.mx:
@@ -205,12 +208,12 @@ class MoELayerForward:
                 self.E, self.h, self.f, self.max_rows, self.dt, _p(self.act),
                 _p(self.tokens_per_expert), _p(i["w_down"]), _p(self.expert_out), self.T,
                 self.fs, _p(self.shared_act), _p(i["shared_down"]), _p(self.shared_out),
-                self._stream()))
+                _p(self.queue), self._stream()))
             return
         check("moe_grouped_fc2", self.lib.moe_grouped_fc2(
             self.E, self.h, self.f, self.max_rows, self.dt, _p(self.act),
             _p(self.tokens_per_expert), _p(self.inp["w_down"]), _p(self.expert_out),
-            self._stream()))
+            _p(self.queue), self._stream()))
 
     def shared_expert(self):
         if not self.shared:
@@ -229,10 +232,10 @@ class MoELayerForward:
             return
         check("moe_grouped_fc1_swiglu", self.lib.moe_grouped_fc1_swiglu(
             1, self.h, self.fs, self.T, self.dt, _p(i["x"]), _p(self.shared_count),
-            _p(i["shared_gate"]), _p(i["shared_up"]), _p(self.shared_act), self._stream()))
+            _p(i["shared_gate"]), _p(i["shared_up"]), _p(self.shared_act), None, self._stream()))
         check("moe_grouped_fc2", self.lib.moe_grouped_fc2(
             1, self.h, self.fs, self.T, self.dt, _p(self.shared_act), _p(self.shared_count),
-            _p(i["shared_down"]), _p(self.shared_out), self._stream()))
+            _p(i["shared_down"]), _p(self.shared_out), None, self._stream()))
 
     def fc2_combine(self):
         if self.mx:

@@ -258,6 +258,12 @@ def moe_permute(x: torch.Tensor, routing_map: torch.Tensor, probs: torch.Tensor,
             "expert_offsets": offs}
 
 
+def gemm_queue(device) -> torch.Tensor:
+    """A zeroed tile-queue buffer for the grouped GEMM entry points
+    (MOE_GEMM_QUEUE_BYTES; the calls leave it zeroed)."""
+    return torch.zeros((_lib.MOE_GEMM_QUEUE_BYTES // 4,), dtype=torch.int32, device=device)
+
+
 def _mlp_args(permuted_x, tokens_per_expert, w_a, w_b=None):
     _need(permuted_x, "rows")
     _need(tokens_per_expert, "tokens_per_expert", torch.int32)
@@ -272,7 +278,8 @@ def _mlp_args(permuted_x, tokens_per_expert, w_a, w_b=None):
 
 def moe_grouped_fc1_swiglu(permuted_x: torch.Tensor, tokens_per_expert: torch.Tensor,
                            w_gate: torch.Tensor, w_up: torch.Tensor,
-                           act: Optional[torch.Tensor] = None) -> torch.Tensor:
+                           act: Optional[torch.Tensor] = None,
+                           queue: Optional[torch.Tensor] = None) -> torch.Tensor:
     """act = silu(x W_gate^T) * (x W_up^T), per expert row range."""
     E = _mlp_args(permuted_x, tokens_per_expert, w_gate, w_up)
     rows, h = permuted_x.shape
@@ -283,14 +290,16 @@ def moe_grouped_fc1_swiglu(permuted_x: torch.Tensor, tokens_per_expert: torch.Te
     _need(act, "act", permuted_x.dtype, (rows, f))
     st = _lib.load().moe_grouped_fc1_swiglu(E, h, f, rows, _dtype_code(permuted_x, "x"),
                                             _ptr(permuted_x), _ptr(tokens_per_expert),
-                                            _ptr(w_gate), _ptr(w_up), _ptr(act), _stream())
+                                            _ptr(w_gate), _ptr(w_up), _ptr(act), _ptr(queue),
+                                            _stream())
     check("moe_grouped_fc1_swiglu", st)
     return act
 
 
 def moe_grouped_fc1_swiglu_gather(x: torch.Tensor, sorted_token: torch.Tensor,
                                   tokens_per_expert: torch.Tensor, w_gate: torch.Tensor,
-                                  w_up: torch.Tensor, act: Optional[torch.Tensor] = None) -> torch.Tensor:
+                                  w_up: torch.Tensor, act: Optional[torch.Tensor] = None,
+                                  queue: Optional[torch.Tensor] = None) -> torch.Tensor:
     """act = silu(x[sorted_token] W_gate^T) * (x[sorted_token] W_up^T), per expert row range."""
     E = _mlp_args(x, tokens_per_expert, w_gate, w_up)
     T, h = x.shape
@@ -303,7 +312,8 @@ def moe_grouped_fc1_swiglu_gather(x: torch.Tensor, sorted_token: torch.Tensor,
     _need(act, "act", x.dtype, (rows, f))
     st = _lib.load().moe_grouped_fc1_swiglu_gather(E, h, f, rows, _dtype_code(x, "x"), T, _ptr(x),
                                                    _ptr(sorted_token), _ptr(tokens_per_expert),
-                                                   _ptr(w_gate), _ptr(w_up), _ptr(act), _stream())
+                                                   _ptr(w_gate), _ptr(w_up), _ptr(act), _ptr(queue),
+                                                   _stream())
     check("moe_grouped_fc1_swiglu_gather", st)
     return act
 
@@ -312,7 +322,8 @@ def moe_grouped_fc1_swiglu_gather_shared(x: torch.Tensor, sorted_token: torch.Te
                                          tokens_per_expert: torch.Tensor, w_gate: torch.Tensor,
                                          w_up: torch.Tensor, shared_gate: torch.Tensor,
                                          shared_up: torch.Tensor, act: Optional[torch.Tensor] = None,
-                                         shared_act: Optional[torch.Tensor] = None):
+                                         shared_act: Optional[torch.Tensor] = None,
+                                         queue: Optional[torch.Tensor] = None):
     """The gathering FC1 of the routed experts and the shared expert's FC1
     over all tokens in one launch; returns (act, shared_act)."""
     E = _mlp_args(x, tokens_per_expert, w_gate, w_up)
@@ -333,7 +344,7 @@ def moe_grouped_fc1_swiglu_gather_shared(x: torch.Tensor, sorted_token: torch.Te
     st = _lib.load().moe_grouped_fc1_swiglu_gather_shared(
         E, h, f, rows, _dtype_code(x, "x"), T, _ptr(x), _ptr(sorted_token),
         _ptr(tokens_per_expert), _ptr(w_gate), _ptr(w_up), _ptr(act), fs, _ptr(shared_gate),
-        _ptr(shared_up), _ptr(shared_act), _stream())
+        _ptr(shared_up), _ptr(shared_act), _ptr(queue), _stream())
     check("moe_grouped_fc1_swiglu_gather_shared", st)
     return act, shared_act
 
@@ -341,7 +352,8 @@ def moe_grouped_fc1_swiglu_gather_shared(x: torch.Tensor, sorted_token: torch.Te
 def moe_grouped_fc2_shared(act: torch.Tensor, tokens_per_expert: torch.Tensor,
                            w_down: torch.Tensor, shared_act: torch.Tensor,
                            shared_down: torch.Tensor, expert_out: Optional[torch.Tensor] = None,
-                           shared_out: Optional[torch.Tensor] = None):
+                           shared_out: Optional[torch.Tensor] = None,
+                           queue: Optional[torch.Tensor] = None):
     """The routed experts' FC2 and the shared expert's FC2 in one launch;
     returns (expert_out, shared_out)."""
     E = _mlp_args(act, tokens_per_expert, w_down)
@@ -359,13 +371,14 @@ def moe_grouped_fc2_shared(act: torch.Tensor, tokens_per_expert: torch.Tensor,
     _need(shared_out, "shared_out", act.dtype, (T, h))
     st = _lib.load().moe_grouped_fc2_shared(
         E, h, f, rows, _dtype_code(act, "act"), _ptr(act), _ptr(tokens_per_expert), _ptr(w_down),
-        _ptr(expert_out), T, fs, _ptr(shared_act), _ptr(shared_down), _ptr(shared_out), _stream())
+        _ptr(expert_out), T, fs, _ptr(shared_act), _ptr(shared_down), _ptr(shared_out), _ptr(queue), _stream())
     check("moe_grouped_fc2_shared", st)
     return expert_out, shared_out
 
 
 def moe_grouped_fc2(act: torch.Tensor, tokens_per_expert: torch.Tensor, w_down: torch.Tensor,
-                    expert_out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                    expert_out: Optional[torch.Tensor] = None,
+                    queue: Optional[torch.Tensor] = None) -> torch.Tensor:
     """expert_out = act W_down^T, per expert row range."""
     E = _mlp_args(act, tokens_per_expert, w_down)
     rows, f = act.shape
@@ -376,7 +389,7 @@ def moe_grouped_fc2(act: torch.Tensor, tokens_per_expert: torch.Tensor, w_down: 
     _need(expert_out, "expert_out", act.dtype, (rows, h))
     st = _lib.load().moe_grouped_fc2(E, h, f, rows, _dtype_code(act, "act"), _ptr(act),
                                      _ptr(tokens_per_expert), _ptr(w_down), _ptr(expert_out),
-                                     _stream())
+                                     _ptr(queue), _stream())
     check("moe_grouped_fc2", st)
     return expert_out
 
@@ -410,7 +423,8 @@ def moe_grouped_fc2_combine(act: torch.Tensor, tokens_per_expert: torch.Tensor,
 
 
 def moe_grouped_mlp(permuted_x: torch.Tensor, tokens_per_expert: torch.Tensor,
-                    w_gate: torch.Tensor, w_up: torch.Tensor, w_down: torch.Tensor):
+                    w_gate: torch.Tensor, w_up: torch.Tensor, w_down: torch.Tensor,
+                    queue: Optional[torch.Tensor] = None):
     """SwiGLU MLP of every expert over its row range; returns (act, expert_out)."""
     E = _mlp_args(permuted_x, tokens_per_expert, w_gate, w_up)
     rows, h = permuted_x.shape
@@ -421,7 +435,8 @@ def moe_grouped_mlp(permuted_x: torch.Tensor, tokens_per_expert: torch.Tensor,
     out = torch.empty((rows, h), dtype=permuted_x.dtype, device=permuted_x.device)
     st = _lib.load().moe_grouped_mlp(E, h, f, rows, _dtype_code(permuted_x, "x"), _ptr(permuted_x),
                                      _ptr(tokens_per_expert), _ptr(w_gate), _ptr(w_up),
-                                     _ptr(w_down), _ptr(act), _ptr(out), _stream())
+                                     _ptr(w_down), _ptr(act), _ptr(out), _ptr(queue),
+                                     _stream())
     check("moe_grouped_mlp", st)
     return act, out
 

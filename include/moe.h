@@ -65,7 +65,8 @@ typedef enum { MOE_DROP_POSITION = 0, MOE_DROP_PROBS = 1 } moe_drop_policy;
  * sqrtsoftplus scores, router side outputs, gathering FC1, MXFP8 GEMMs;
  * 3: moe_route_permute, moe_grouped_fc2_combine,
  * moe_grouped_fc2_combine_mxfp8; 4: moe_grouped_fc1_swiglu_gather_shared,
- * moe_grouped_fc2_shared; 5: moe_route_permute_noalloc). */
+ * moe_grouped_fc2_shared; 5: moe_route_permute_noalloc; 6: the queue
+ * argument of the bf16 GEMM entry points). */
 int moe_abi_version(void);
 
 /* Message for the last non-OK status returned on the calling thread. */
@@ -292,7 +293,21 @@ moe_status moe_route_permute_noalloc(const moe_route_desc* d, const void* x,
  * (bf16 rounded to nearest-even).  Sizes for MOE_BF16: h and f multiples
  * of 64.  Rows at index >= sum(n_e) of act/expert_out are left untouched;
  * counts are clamped so that no row index reaches max_rows.
+ *
+ * queue (every GEMM entry point below that takes one): NULL, or a device
+ * buffer of MOE_GEMM_QUEUE_BYTES that is all zero before the first call
+ * that uses it.  With a queue, a bf16 launch of 2 to 256 experts whose
+ * average row count (max_rows / E) is >= 192 runs one workgroup per CU,
+ * and each takes the next tile of its XCD's share from a counter in the
+ * queue (tile groups of 32 dealt to the XCDs in turn), instead of one
+ * workgroup per tile handed out by the hardware; other launches ignore the
+ * queue.  The last workgroup leaves the counters at zero, so
+ * one queue serves any number of calls in stream order.  Calls that can
+ * run at the same time (different streams) need different queues.  The
+ * results do not depend on it (each tile is computed by one workgroup, in
+ * the same way).  NULL: one workgroup per tile.
  * ------------------------------------------------------------------------ */
+#define MOE_GEMM_QUEUE_BYTES ((size_t)2048)
 
 /*
  * moe_grouped_fc2_combine — moe_grouped_fc2 with moe_combine as its
@@ -328,13 +343,13 @@ moe_status moe_grouped_fc2_combine(int64_t E, int64_t h, int64_t f, int64_t max_
 moe_status moe_grouped_mlp(int64_t E, int64_t h, int64_t f, int64_t max_rows, int32_t dtype,
                            const void* permuted_x, const int32_t* tokens_per_expert,
                            const void* w_gate, const void* w_up, const void* w_down, void* act,
-                           void* expert_out, void* stream);
+                           void* expert_out, void* queue, void* stream);
 
 /* The first half of moe_grouped_mlp: act = silu(x W_gate^T) * (x W_up^T). */
 moe_status moe_grouped_fc1_swiglu(int64_t E, int64_t h, int64_t f, int64_t max_rows,
                                   int32_t dtype, const void* permuted_x,
                                   const int32_t* tokens_per_expert, const void* w_gate,
-                                  const void* w_up, void* act, void* stream);
+                                  const void* w_up, void* act, void* queue, void* stream);
 
 /*
  * moe_grouped_fc1_swiglu_gather — the first half of moe_grouped_mlp reading
@@ -351,7 +366,7 @@ moe_status moe_grouped_fc1_swiglu_gather(int64_t E, int64_t h, int64_t f, int64_
                                          int32_t dtype, int64_t T, const void* x,
                                          const int32_t* sorted_token,
                                          const int32_t* tokens_per_expert, const void* w_gate,
-                                         const void* w_up, void* act, void* stream);
+                                         const void* w_up, void* act, void* queue, void* stream);
 
 /*
  * moe_grouped_fc1_swiglu_gather_shared — moe_grouped_fc1_swiglu_gather and
@@ -375,7 +390,7 @@ moe_status moe_grouped_fc1_swiglu_gather_shared(int64_t E, int64_t h, int64_t f,
                                                 const void* w_gate, const void* w_up, void* act,
                                                 int64_t fs, const void* shared_gate,
                                                 const void* shared_up, void* shared_act,
-                                                void* stream);
+                                                void* queue, void* stream);
 
 /*
  * moe_grouped_fc2_shared — moe_grouped_fc2 and the shared expert's FC2 in
@@ -392,12 +407,12 @@ moe_status moe_grouped_fc2_shared(int64_t E, int64_t h, int64_t f, int64_t max_r
                                   const int32_t* tokens_per_expert, const void* w_down,
                                   void* expert_out, int64_t T, int64_t fs,
                                   const void* shared_act, const void* shared_down,
-                                  void* shared_out, void* stream);
+                                  void* shared_out, void* queue, void* stream);
 
 /* The second half of moe_grouped_mlp: expert_out = act W_down^T. */
 moe_status moe_grouped_fc2(int64_t E, int64_t h, int64_t f, int64_t max_rows, int32_t dtype,
                            const void* act, const int32_t* tokens_per_expert,
-                           const void* w_down, void* expert_out, void* stream);
+                           const void* w_down, void* expert_out, void* queue, void* stream);
 
 /* ------------------------------------------------------------------------
  * MXFP8 expert GEMMs.  [MG] FP8/FP4 低精度训练 and 计算效率优化 name FP8 GEMMs for

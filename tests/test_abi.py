@@ -28,7 +28,7 @@ def test_library_exports_every_declared_function():
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(_lib.SIGNATURES) == names
-    assert lib.moe_abi_version() == 5
+    assert lib.moe_abi_version() == 6
 
 
 def test_route_desc_layout_matches_c():
@@ -111,13 +111,15 @@ def test_permute_combine_mlp_reject_bad_sizes():
     assert st == _lib.MOE_ERR_UNSUPPORTED
     st, _ = _status("moe_combine", 10, 16, 0, _lib.MOE_BF16, p, p, p, 20, None, p, None)
     assert st == _lib.MOE_ERR_ARG
-    st, msg = _status("moe_grouped_mlp", 8, 100, 256, 64, _lib.MOE_BF16, p, p, p, p, p, p, p, None)
+    st, msg = _status("moe_grouped_mlp", 8, 100, 256, 64, _lib.MOE_BF16, p, p, p, p, p, p, p, None,
+                      None)
     assert st == _lib.MOE_ERR_UNSUPPORTED and "multiples of 64" in msg
-    st, _ = _status("moe_grouped_fc2", 0, 128, 256, 64, _lib.MOE_BF16, p, p, p, p, None)
+    st, _ = _status("moe_grouped_fc2", 0, 128, 256, 64, _lib.MOE_BF16, p, p, p, p, None, None)
     assert st == _lib.MOE_ERR_ARG
-    st, _ = _status("moe_grouped_fc1_swiglu", 4, 64, 64, 8, 7, p, p, p, p, p, None)
+    st, _ = _status("moe_grouped_fc1_swiglu", 4, 64, 64, 8, 7, p, p, p, p, p, None, None)
     assert st == _lib.MOE_ERR_ARG  # dtype
-    st, _ = _status("moe_grouped_fc1_swiglu", 4, 64, 64, 8, _lib.MOE_BF16, p, None, p, p, p, None)
+    st, _ = _status("moe_grouped_fc1_swiglu", 4, 64, 64, 8, _lib.MOE_BF16, p, None, p, p, p, None,
+                    None)
     assert st == _lib.MOE_ERR_ARG  # NULL counts
 
 

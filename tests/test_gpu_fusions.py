@@ -211,3 +211,55 @@ def test_shared_expert_folded_into_the_routed_launches(T, E, K, f, fs, h):
                                           expert_out=y[:0])
     torch.cuda.synchronize()
     assert torch.equal(sact0, sact_ref) and torch.equal(sout0, sout_ref)
+
+
+@pytest.mark.parametrize("T,E,K,f,h,fs", [(2048, 64, 5, 512, 256, 0),      # 160 rows: no queue
+                                          (2048, 64, 8, 256, 512, 256),    # + shared tail
+                                          (4096, 8, 2, 256, 128, 0),       # large experts
+                                          (600, 64, 1, 256, 128, 0)])      # 64-row launch: no queue
+def test_tile_queue_matches_one_tile_per_workgroup(T, E, K, f, h, fs):
+    """The tile-queue launches (one workgroup per CU taking tiles from per-XCD
+    counters) give the same bits as one workgroup per tile, on repeated calls
+    with one queue, and leave the queue zeroed."""
+    cfg = datagen.MoEConfig("queue", T=T, h=h, E=E, K=K, f=f, dtype="bf16", score="sigmoid",
+                            expert_bias=True, shared_f=fs)
+    log(f"tile queue: {cfg}")
+    inp = datagen.make_inputs(cfg, seed=17, device=DEV)
+    r = moe.moe_route_permute(inp["x"], inp["w_router"], K=K, score="sigmoid",
+                              expert_bias=inp["expert_bias"], copy_rows=False)
+    x, st, tpe = inp["x"], r["sorted_token"], r["tokens_per_expert"]
+    q = moe.gemm_queue(DEV)
+    N = int(r["expert_offsets"][-1].item())
+    for _ in range(3):
+        if fs:
+            a0, s0 = moe.moe_grouped_fc1_swiglu_gather_shared(
+                x, st, tpe, inp["w_gate"], inp["w_up"], inp["shared_gate"], inp["shared_up"])
+            a1, s1 = moe.moe_grouped_fc1_swiglu_gather_shared(
+                x, st, tpe, inp["w_gate"], inp["w_up"], inp["shared_gate"], inp["shared_up"],
+                queue=q)
+            y0, o0 = moe.moe_grouped_fc2_shared(a0, tpe, inp["w_down"], s0, inp["shared_down"])
+            y1, o1 = moe.moe_grouped_fc2_shared(a1, tpe, inp["w_down"], s1, inp["shared_down"],
+                                                queue=q)
+        else:
+            a0 = moe.moe_grouped_fc1_swiglu_gather(x, st, tpe, inp["w_gate"], inp["w_up"])
+            a1 = moe.moe_grouped_fc1_swiglu_gather(x, st, tpe, inp["w_gate"], inp["w_up"], queue=q)
+            y0 = moe.moe_grouped_fc2(a0, tpe, inp["w_down"])
+            y1 = moe.moe_grouped_fc2(a1, tpe, inp["w_down"], queue=q)
+        torch.cuda.synchronize()
+        assert torch.equal(a0[:N], a1[:N]) and torch.equal(y0[:N], y1[:N])
+        if fs:
+            assert torch.equal(s0, s1) and torch.equal(o0, o1)
+        assert int(q.abs().sum().item()) == 0, "the queue is left zeroed"
+
+
+def test_layer_with_and_without_tile_queue():
+    cfg = datagen.CONFIGS["dsv3"].replace(T=2048)
+    inp = datagen.make_inputs(cfg, seed=0, device=DEV)
+    kw = dict(K=cfg.K, score=cfg.score, gather=True)
+    a = MoELayerForward(inp, tile_queue=True, **kw)
+    b = MoELayerForward(inp, tile_queue=False, **kw)
+    outs = []
+    for layer in (a, b, a):
+        outs.append(layer.forward().clone())
+        torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
