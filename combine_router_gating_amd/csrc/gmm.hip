@@ -455,8 +455,8 @@ __global__ void __launch_bounds__(NW * 64) gmm_bf16_kernel(
     // tail's) are cut into groups of kQGroup consecutive tiles, and XCD x
     // owns groups x, x + 8, x + 16, ...; each workgroup takes its XCD's next
     // tile from that XCD's counter when it finishes one.  Nothing waits on
-    // another workgroup; every workgroup leaves once its XCD's tiles run
-    // out, and the last one to leave sets the counters back to zero.
+    // another workgroup; every workgroup leaves once all tiles are taken,
+    // and the last one to leave sets the counters back to zero.
     const int NT = (N + BN - 1) / BN;
     __shared__ int p_toff[kPersistMaxExperts + 1], p_roff[kPersistMaxExperts],
         p_n[kPersistMaxExperts];
@@ -479,15 +479,21 @@ __global__ void __launch_bounds__(NW * 64) gmm_bf16_kernel(
     const int64_t routed = static_cast<int64_t>(p_toff[E]) * NT;
     const int ntd = TAIL ? (dn.N + BN - 1) / BN : 0;
     const int64_t total = routed + (TAIL ? (dn.rows + BMAX - 1) / BMAX * ntd : 0);
+    // Once its own XCD's tiles run out, a workgroup takes the remaining
+    // tiles of the other XCDs, one XCD after another (a counter only grows,
+    // so an XCD found empty stays empty): the XCDs end together.
     const int x = static_cast<int>(blockIdx.x % 8);
-    int* counter = queue + x * kQStride;
-    for (;;) {
-      if (threadIdx.x == 0) s_kq = atomicAdd(counter, 1);
+    for (int v = 0; v < 8;) {
+      const int xv = (x + v) % 8;
+      if (threadIdx.x == 0) s_kq = atomicAdd(queue + xv * kQStride, 1);
       __syncthreads();
       const int64_t kq = s_kq;
       __syncthreads();  // s_kq is rewritten by the next take
-      const int64_t L = ((kq / kQGroup) * 8 + x) * kQGroup + kq % kQGroup;
-      if (kq < 0 || L >= total) break;  // uniform over the workgroup
+      const int64_t L = ((kq / kQGroup) * 8 + xv) * kQGroup + kq % kQGroup;
+      if (kq < 0 || L >= total) {  // uniform over the workgroup
+        ++v;
+        continue;
+      }
       Tile t;
       const uint16_t* ta = A;
       const int32_t* tg = gather;
