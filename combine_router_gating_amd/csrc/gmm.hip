@@ -636,9 +636,14 @@ struct Body {
   }
 };
 
-// ----------------------------------------------------------------- fp32 SIMT
-// For fp32 layers: 64x64 tiles, 16x16 threads with 4x4 outputs each (per
-// weight matrix), k-slabs of 16 through LDS; any N and K.
+// ----------------------------------------------------------------- fp32 MFMA
+// For fp32 layers: 64x64 tiles (per weight matrix) on the fp32 matrix
+// cores, v_mfma_f32_32x32x2_f32: four waves, each owning a 32x32 block of
+// the tile, multiply k-slabs of 16 staged through LDS (k-major, so lane l of
+// a wave reads row l % 32 of its block at k = 2s + l / 32 without bank
+// conflicts); any N and K (the slab past K is zero-filled).  Every product
+// and sum is fp32, as in the layer's fp32 arithmetic; the order of the
+// k-sums differs from a sequential loop by rounding only.
 constexpr int FM = 64, FN = 64, FK = 16;
 
 template <bool FC1>
@@ -651,6 +656,7 @@ __global__ void __launch_bounds__(kThreads) gmm_f32_kernel(const float* __restri
                                                            const int32_t* __restrict__ counts,
                                                            int E, int N, int K, int64_t max_rows) {
   constexpr int NB = FC1 ? 2 : 1;
+  static_assert(kThreads == 256, "four waves, one 32x32 block each");
   __shared__ float as[FK][FM + 4];
   __shared__ float bs[NB][FK][FN + 4];
   __shared__ int s_toff[kMaxExperts + 1];
@@ -661,8 +667,14 @@ __global__ void __launch_bounds__(kThreads) gmm_f32_kernel(const float* __restri
   Tile tile;
   if (!decode_tile<FM>(counts, E, max_rows, NT, s_toff, s_roff, s_n, s_scan, tile)) return;
   const int n0 = tile.n0 * FN;
-  const int tid = threadIdx.x, tx = tid % 16, ty = tid / 16;
-  float acc[NB][4][4] = {};
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
+  const int l32 = lane & 31, hi = lane >> 5;
+  f32x16 acc[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int q = 0; q < 16; ++q) acc[b][q] = 0.f;
   for (int k0 = 0; k0 < K; k0 += FK) {
     for (int i = tid; i < FM * FK; i += kThreads) {
       const int rr = i / FK, kk = i % FK;
@@ -680,35 +692,28 @@ __global__ void __launch_bounds__(kThreads) gmm_f32_kernel(const float* __restri
     }
     __syncthreads();
 #pragma unroll
-    for (int kk = 0; kk < FK; ++kk) {
-      float av[4], bv[NB][4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) av[i] = as[kk][ty * 4 + i];
-#pragma unroll
-      for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) bv[b][j] = bs[b][kk][tx * 4 + j];
+    for (int s = 0; s < FK / 2; ++s) {
+      // weights as the first operand: lane l then holds output row
+      // (token) l % 32 and columns 8 g + 4 (l / 32) + q in acc[4 g + q]
+      const float av = as[2 * s + hi][wm * 32 + l32];
 #pragma unroll
       for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) acc[b][i][j] = fmaf(av[i], bv[b][j], acc[b][i][j]);
+        acc[b] = __builtin_amdgcn_mfma_f32_32x32x2f32(bs[b][2 * s + hi][wn * 32 + l32], av, acc[b],
+                                                      0, 0, 0);
     }
     __syncthreads();
   }
+  const int ml = wm * 32 + l32;
+  if (ml >= tile.nrows) return;
+  float* crow = C + (tile.row0 + ml) * static_cast<int64_t>(N);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int ml = ty * 4 + i;
-    if (ml >= tile.nrows) continue;
+  for (int g = 0; g < 4; ++g)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int n = n0 + tx * 4 + j;
+    for (int q = 0; q < 4; ++q) {
+      const int n = n0 + wn * 32 + g * 8 + hi * 4 + q;
       if (n >= N) continue;
-      const float v = FC1 ? silu_mul(acc[0][i][j], acc[NB - 1][i][j]) : acc[0][i][j];
-      C[(tile.row0 + ml) * static_cast<int64_t>(N) + n] = v;
+      crow[n] = FC1 ? silu_mul(acc[0][g * 4 + q], acc[NB - 1][g * 4 + q]) : acc[0][g * 4 + q];
     }
-  }
 }
 
 // ----------------------------------------------------------------- launch

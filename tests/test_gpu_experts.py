@@ -42,6 +42,7 @@ CASES = [
     ([0, 0, 5], 64, 64, torch.bfloat16),
     ([33, 7, 90], 40, 72, torch.float32),            # fp32 path, odd sizes
     ([256], 128, 256, torch.float32),
+    ([70, 0, 129, 64], 200, 136, torch.float32),    # fp32: ragged k-slabs and column tiles
 ]
 
 
