@@ -241,51 +241,35 @@ def cpu_model() -> str:
     return "unknown"
 
 
-class ClockSampler:
-    """Polls the GPU's reported shader clock (MHz, amd-smi through torch)
-    from a background thread while active; None if the query is not
-    available."""
-
-    def __init__(self, period_s: float = 0.01):
-        import threading
-        self.period = period_s
-        self.samples = []
-        self.stop = threading.Event()
-        self.thread = threading.Thread(target=self._run, daemon=True)
-        self.ok = True
-
-    def _run(self):
-        import torch
-        while not self.stop.is_set():
-            try:
-                self.samples.append(int(torch.cuda.clock_rate(0)))
-            except Exception:  # pragma: no cover - query unavailable
-                self.ok = False
-                return
-            self.stop.wait(self.period)
-
-    def __enter__(self):
-        import torch
-        try:  # the first query initialises amd-smi: keep it out of the timed steps
-            torch.cuda.clock_rate(0)
-        except Exception:  # pragma: no cover - query unavailable
-            self.ok = False
-            return self
-        self.thread.start()
-        return self
-
-    def __exit__(self, *exc):
-        self.stop.set()
-        if self.thread.is_alive():
-            self.thread.join()
-
-    def summary(self):
-        if not self.ok or not self.samples:
-            return None
-        v = sorted(self.samples)
-        return {"unit": "MHz", "min": v[0], "median": v[len(v) // 2], "max": v[-1],
-                "samples": len(v), "source": "amd-smi GFX clock via torch.cuda.clock_rate, "
-                "polled every 10 ms during the timed steps"}
+def clock_pass(layer, dev, step_ms: float, steps: int):
+    """Shader clock while the layer runs: one-wave probes (moe_clock_probe:
+    s_memtime cycles over s_memrealtime ticks) queued back to back on a
+    second stream during extra forwards whose times are not used.  A probe
+    wave holds registers on one CU, which keeps one GEMM workgroup off that
+    CU while it runs, so this pass is separate from the timed ones."""
+    import torch
+    import combine_router_gating_amd as moe_lib
+    total_us = max(1000.0, min(steps * step_ms * 1e3, 300e3))
+    window = int(max(200.0, min(5000.0, total_us / 8)))
+    n = max(1, int(total_us // window))
+    buf = torch.zeros((n, 2), dtype=torch.int64, device=dev)
+    side = torch.cuda.Stream(device=dev)
+    nsteps = int(total_us / (step_ms * 1e3)) + 2
+    torch.cuda.synchronize()
+    with torch.cuda.stream(side):
+        for k in range(n):
+            moe_lib.moe_clock_probe(buf[k], window)
+    for _ in range(nsteps):
+        layer.forward()
+    torch.cuda.synchronize()
+    mhz = sorted(100.0 * c / t for c, t in buf.cpu().tolist() if t > 0)
+    if not mhz:
+        return None
+    return {"unit": "MHz", "min": round(mhz[0]), "median": round(mhz[len(mhz) // 2]),
+            "max": round(mhz[-1]), "windows": len(mhz), "window_us": window,
+            "source": "s_memtime cycles / s_memrealtime ticks of one-wave probes "
+                      "(moe_clock_probe) on a second stream, back to back during "
+                      f"{nsteps} extra forwards"}
 
 
 def torch_float32():
@@ -389,12 +373,11 @@ def main():
         return m
 
     torch.cuda.synchronize()
-    with ClockSampler() as clock:
-        t0 = time.perf_counter()
-        for i in range(args.steps):
-            layer.forward(dom_mark(i))
-        torch.cuda.synchronize()
-        t1 = time.perf_counter()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        layer.forward(dom_mark(i))
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     dom_ms = [a.elapsed_time(b) for a, b in dom_ev]
 
@@ -446,6 +429,8 @@ def main():
             stage_report[s]["frac_of_hbm_peak"] = round(nb / sec_s / 1e9 / HBM_PEAK_GBS, 4)
             stage_report[s]["frac_of_copy"] = round(nb / sec_s / 1e9 / copy_gbs, 4)
 
+    clock = clock_pass(layer, dev, ms_per_step, args.steps)
+
     cold = None
     if not args.no_cold:
         flush = torch.empty((512 << 20) // 4, dtype=torch.float32, device=dev)
@@ -491,7 +476,7 @@ def main():
         "stages": stage_report,
         "roofline": roof,
         "copy_GBs": copy_gbs,
-        "clock": clock.summary(),
+        "clock": clock,
     }
     if cold:
         rec["cold"] = cold

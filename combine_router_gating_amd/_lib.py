@@ -33,6 +33,7 @@ class RouteDesc(ctypes.Structure):
 SIGNATURES = {
     "moe_abi_version": (c_i32, []),
     "moe_last_error": (ctypes.c_char_p, []),
+    "moe_clock_probe": (c_i32, [c_vp, c_i64, c_vp]),
     "moe_route_workspace_size": (c_sz, [ctypes.POINTER(RouteDesc)]),
     "moe_route_capacity": (c_i64, [ctypes.POINTER(RouteDesc)]),
     "moe_max_rows": (c_i64, [ctypes.POINTER(RouteDesc)]),

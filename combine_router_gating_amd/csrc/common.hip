@@ -189,6 +189,39 @@ void launch_count_scan(const int32_t* hist, int64_t nblk, int64_t E, int64_t cap
 
 }  // namespace moe
 
-extern "C" int moe_abi_version(void) { return 6; }
+namespace moe {
+
+// One wave; lane 0 sleeps in short steps until `ticks` of the constant
+// 100 MHz counter have passed, then stores the shader-clock cycles
+// (s_memtime) and real-time ticks (s_memrealtime) that elapsed meanwhile.
+__global__ void __launch_bounds__(64) clock_probe_kernel(unsigned long long* __restrict__ out,
+                                                         unsigned long long ticks) {
+  if (threadIdx.x != 0) return;
+  const unsigned long long r0 = __builtin_amdgcn_s_memrealtime();
+  const unsigned long long c0 = __builtin_readcyclecounter();
+  unsigned long long r = r0;
+  while (r - r0 < ticks) {
+    __builtin_amdgcn_s_sleep(8);
+    r = __builtin_amdgcn_s_memrealtime();
+  }
+  const unsigned long long c1 = __builtin_readcyclecounter();
+  out[0] = c1 - c0;
+  out[1] = r - r0;
+}
+
+}  // namespace moe
+
+extern "C" moe_status moe_clock_probe(uint64_t* out, int64_t spin_us, void* stream) {
+  if (!out) return moe::fail(MOE_ERR_ARG, "moe_clock_probe: out is null");
+  if (spin_us <= 0 || spin_us > 1000000)
+    return moe::fail(MOE_ERR_ARG, "moe_clock_probe: spin_us %lld outside (0, 1e6]",
+                     static_cast<long long>(spin_us));
+  hipLaunchKernelGGL(moe::clock_probe_kernel, dim3(1), dim3(64), 0, moe::as_stream(stream),
+                     reinterpret_cast<unsigned long long*>(out),
+                     static_cast<unsigned long long>(spin_us) * 100ull);
+  return moe::check_launch("moe_clock_probe");
+}
+
+extern "C" int moe_abi_version(void) { return 7; }
 
 extern "C" const char* moe_last_error(void) { return moe::g_last_error.c_str(); }

@@ -258,6 +258,15 @@ def moe_permute(x: torch.Tensor, routing_map: torch.Tensor, probs: torch.Tensor,
             "expert_offsets": offs}
 
 
+def moe_clock_probe(out: torch.Tensor, spin_us: int) -> torch.Tensor:
+    """Queue one clock probe on the current stream: after spin_us
+    microseconds, out (int64[2] on the GPU) holds the shader-clock cycles and
+    the 100 MHz ticks that elapsed (clock MHz = 100 * out[0] / out[1])."""
+    _need(out, "out", torch.int64, (2,))
+    check("moe_clock_probe", _lib.load().moe_clock_probe(_ptr(out), int(spin_us), _stream()))
+    return out
+
+
 def gemm_queue(device) -> torch.Tensor:
     """A zeroed tile-queue buffer for the grouped GEMM entry points
     (MOE_GEMM_QUEUE_BYTES; the calls leave it zeroed)."""

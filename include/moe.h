@@ -66,11 +66,22 @@ typedef enum { MOE_DROP_POSITION = 0, MOE_DROP_PROBS = 1 } moe_drop_policy;
  * 3: moe_route_permute, moe_grouped_fc2_combine,
  * moe_grouped_fc2_combine_mxfp8; 4: moe_grouped_fc1_swiglu_gather_shared,
  * moe_grouped_fc2_shared; 5: moe_route_permute_noalloc; 6: the queue
- * argument of the bf16 GEMM entry points). */
+ * argument of the bf16 GEMM entry points; 7: moe_clock_probe). */
 int moe_abi_version(void);
 
 /* Message for the last non-OK status returned on the calling thread. */
 const char* moe_last_error(void);
+
+/* Measurement utility, not a stage of the layer: the shader clock the GPU
+ * runs at while other work is in flight.  Launches one wave on `stream`
+ * that waits spin_us microseconds of the GPU's constant 100 MHz counter and
+ * then writes two values to `out` (device memory, 2 x uint64, caller-owned):
+ * out[0] = shader-clock cycles elapsed (s_memtime), out[1] = 100 MHz ticks
+ * elapsed (s_memrealtime); the clock in MHz is 100 * out[0] / out[1].  The
+ * wave sleeps between reads and holds no LDS, so it shares a CU with other
+ * kernels' workgroups.  Errors: MOE_ERR_ARG (out null, spin_us outside
+ * (0, 1e6]); MOE_ERR_HIP. */
+moe_status moe_clock_probe(uint64_t* out, int64_t spin_us, void* stream);
 
 /* ------------------------------------------------------------------------
  * Router: gating linear + score function + top-k + capacity drop.

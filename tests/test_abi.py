@@ -28,7 +28,7 @@ def test_library_exports_every_declared_function():
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(_lib.SIGNATURES) == names
-    assert lib.moe_abi_version() == 6
+    assert lib.moe_abi_version() == 7
 
 
 def test_route_desc_layout_matches_c():
@@ -273,3 +273,14 @@ def test_noalloc_rejects_layers_beyond_the_static_scratch():
     text = open(HEADER).read()
     assert "#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)" in text
     assert _lib.MOE_NOALLOC_SCRATCH_BYTES == 32 << 20
+
+
+def test_clock_probe_rejects_bad_arguments_before_launching():
+    """moe_clock_probe validates on the host: no launch for a null output or
+    a spin outside (0, 1 s]."""
+    lib = moe.load()
+    out = ctypes.c_void_p(16)  # never dereferenced: validation fails first
+    assert lib.moe_clock_probe(None, 100, None) == 1
+    assert lib.moe_clock_probe(out, 0, None) == 1
+    assert lib.moe_clock_probe(out, 1000001, None) == 1
+    assert b"spin_us" in lib.moe_last_error()
