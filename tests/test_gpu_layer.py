@@ -75,7 +75,7 @@ def test_layer_small_full_compare(cfg):
 
 
 def test_layer_shared_weights_reduce_to_dense_times_prob_sum():
-    """Spec invariant: all experts sharing weights, out = SwiGLU(x) * sum(p)."""
+    """Invariant: with all experts sharing weights, out = SwiGLU(x) * sum(p)."""
     cfg = datagen.MoEConfig("shared-w", T=400, h=128, E=8, K=2, f=256, dtype="f32")
     inp = datagen.make_inputs(cfg, seed=4, device=DEV)
     for k in ("w_gate", "w_up", "w_down"):
