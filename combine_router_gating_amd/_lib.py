@@ -67,9 +67,16 @@ SIGNATURES = {
                                        c_i64, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "moe_mxfp8_quantize": (c_i32, [c_i64, c_i64, c_i64, c_i32, c_vp, c_vp, c_vp, c_vp]),
     "moe_grouped_fc1_swiglu_mxfp8": (c_i32, [c_i64, c_i64, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp,
-                                             c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
+                                             c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
+    "moe_grouped_fc1_swiglu_mxfp8_shared": (c_i32, [c_i64, c_i64, c_i64, c_i64, c_i64, c_vp, c_vp,
+                                                    c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                                    c_i64, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                                    c_vp]),
     "moe_grouped_fc2_mxfp8": (c_i32, [c_i64, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp,
-                                      c_vp, c_vp]),
+                                      c_vp, c_vp, c_vp]),
+    "moe_grouped_fc2_mxfp8_shared": (c_i32, [c_i64, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp,
+                                             c_vp, c_vp, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                             c_vp, c_vp]),
     "moe_grouped_fc2_combine_mxfp8": (c_i32, [c_i64, c_i64, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp,
                                               c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "moe_grouped_fc2": (c_i32, [c_i64, c_i64, c_i64, c_i64, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),

@@ -222,6 +222,6 @@ extern "C" moe_status moe_clock_probe(uint64_t* out, int64_t spin_us, void* stre
   return moe::check_launch("moe_clock_probe");
 }
 
-extern "C" int moe_abi_version(void) { return 7; }
+extern "C" int moe_abi_version(void) { return 8; }
 
 extern "C" const char* moe_last_error(void) { return moe::g_last_error.c_str(); }

@@ -56,15 +56,6 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kThreads = 256;
 constexpr int BK = 64;
-// m-tiles per band of the dense (single-expert) tile order
-constexpr int kDenseBand = 8;
-// experts a persistent launch keeps its decoded tables for
-constexpr int kPersistMaxExperts = 256;
-// tile queue: groups of consecutive logical tiles per XCD turn, and the
-// spacing of the counters in the queue buffer (128-byte lines apart)
-constexpr int kQGroup = 32;
-constexpr int kQStride = 32;
-static_assert(9 * kQStride * 4 <= MOE_GEMM_QUEUE_BYTES, "queue counters fit the buffer");
 
 
 // ----------------------------------------------------------------- bf16 MFMA
@@ -451,37 +442,21 @@ __global__ void __launch_bounds__(NW * 64) gmm_bf16_kernel(
   static_assert(LDS >= DECODE_BYTES, "decode scratch aliases the stages");
   __shared__ __attribute__((aligned(1024))) char smem[LDS];
   if constexpr (QUEUE) {
-    // One workgroup per CU.  The logical tiles (routed, then the dense
-    // tail's) are cut into groups of kQGroup consecutive tiles, and XCD x
-    // owns groups x, x + 8, x + 16, ...; each workgroup takes its XCD's next
-    // tile from that XCD's counter when it finishes one.  Nothing waits on
-    // another workgroup; every workgroup leaves once all tiles are taken,
-    // and the last one to leave sets the counters back to zero.
+    // One workgroup per CU takes tiles from the queue (queue_tiles): the
+    // routed experts' logical tiles, then the dense tail's.
     const int NT = (N + BN - 1) / BN;
     __shared__ int p_toff[kPersistMaxExperts + 1], p_roff[kPersistMaxExperts],
         p_n[kPersistMaxExperts];
     __shared__ int s_kq;
-    {
-      int* s_toff = reinterpret_cast<int*>(smem);
-      int* s_roff = s_toff + kMaxExperts + 1;
-      int* s_n = s_roff + kMaxExperts;
-      int64_t* s_scan = reinterpret_cast<int64_t*>(s_n + kMaxExperts + 1);
-      decode_counts<BMAX, NW * 64>(counts, E, max_rows, s_toff, s_roff, s_n, s_scan);
-      for (int i = threadIdx.x; i <= E; i += blockDim.x) {
-        p_toff[i] = s_toff[i];
-        if (i < E) {
-          p_roff[i] = s_roff[i];
-          p_n[i] = s_n[i];
-        }
-      }
-      __syncthreads();  // tables copied out of the stage area
-    }
+    decode_to_tables<BMAX, NW * 64>(counts, E, max_rows, smem, p_toff, p_roff, p_n);
     const int64_t routed = static_cast<int64_t>(p_toff[E]) * NT;
     const int ntd = TAIL ? (dn.N + BN - 1) / BN : 0;
     const int64_t total = routed + (TAIL ? (dn.rows + BMAX - 1) / BMAX * ntd : 0);
     // Once its own XCD's tiles run out, a workgroup takes the remaining
     // tiles of the other XCDs, one XCD after another (a counter only grows,
-    // so an XCD found empty stays empty): the XCDs end together.
+    // so an XCD found empty stays empty): the XCDs end together.  (The same
+    // loop as queue_tiles, written out: through the lambda the FC2 kernels
+    // spilled two registers.)
     const int x = static_cast<int>(blockIdx.x % 8);
     for (int v = 0; v < 8;) {
       const int xv = (x + v) % 8;
@@ -521,12 +496,7 @@ __global__ void __launch_bounds__(NW * 64) gmm_bf16_kernel(
       else Body64::template run<CMB>(t, smem, ta, tg, tar, tb0, tb1, tc, tn, tk, epi);
       __syncthreads();  // every wave is past the tile before its stages are refilled
     }
-    if (threadIdx.x == 0) {
-      if (atomicAdd(queue + 8 * kQStride, 1) == static_cast<int>(gridDim.x) - 1) {
-        for (int i = 0; i < 8; ++i) atomicExch(queue + i * kQStride, 0);
-        atomicExch(queue + 8 * kQStride, 0);
-      }
-    }
+    queue_leave(queue);
     return;
   }
   // this workgroup's tile and its operands (the routed experts', or the
@@ -566,21 +536,7 @@ __global__ void __launch_bounds__(NW * 64) gmm_bf16_kernel(
     const int NT = (N + BN - 1) / BN;
     __shared__ int p_toff[kPersistMaxExperts + 1], p_roff[kPersistMaxExperts],
         p_n[kPersistMaxExperts];
-    {
-      int* s_toff = reinterpret_cast<int*>(smem);
-      int* s_roff = s_toff + kMaxExperts + 1;
-      int* s_n = s_roff + kMaxExperts;
-      int64_t* s_scan = reinterpret_cast<int64_t*>(s_n + kMaxExperts + 1);
-      decode_counts<BMAX, NW * 64>(counts, E, max_rows, s_toff, s_roff, s_n, s_scan);
-      for (int i = threadIdx.x; i <= E; i += blockDim.x) {
-        p_toff[i] = s_toff[i];
-        if (i < E) {
-          p_roff[i] = s_roff[i];
-          p_n[i] = s_n[i];
-        }
-      }
-      __syncthreads();  // tables copied out of the stage area
-    }
+    decode_to_tables<BMAX, NW * 64>(counts, E, max_rows, smem, p_toff, p_roff, p_n);
     const int64_t total = static_cast<int64_t>(p_toff[E]) * NT;
     for (int64_t j = blockIdx.x;; j += gridDim.x) {
       const int64_t L = xcd_tile(j, total);
@@ -742,17 +698,6 @@ struct SharedArgs {
   void* C = nullptr;  // [rows, N]
   int64_t rows = 0, N = 0, K = 0;
 };
-
-// Workgroups of a persistent launch: one per CU (a multiple of 8, so that
-// each workgroup stays on one XCD), never more than the tiles.
-int64_t persistent_grid(int64_t tiles_grid) {
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      cus < 8)
-    cus = 256;
-  return std::min<int64_t>(tiles_grid, cus / 8 * 8);
-}
 
 template <bool FC1, int BMAX, int BN, int NW, class B256, class B128, class B64,
           bool PERSIST = false, bool QUEUE = false>

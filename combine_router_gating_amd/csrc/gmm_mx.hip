@@ -343,13 +343,31 @@ struct MxBody {
   }
 };
 
+// The shared expert's dense GEMM (all tokens through one weight, [MC] §11)
+// riding as the last tiles of a grouped launch, so that its tiles fill the
+// tail of the routed experts' tiles: its operands, rows and sizes (tile
+// order as dense_tile_at; A rows are not gathered).  With one workgroup per
+// tile, the last `wgs` workgroups of the grid take these tiles.
+struct MxDense {
+  MxA A;
+  MxB B;
+  MxOut O;
+  int64_t rows;
+  int N, K;
+  int wgs;
+};
+
 // Decode this workgroup's tile (Body::BM-row m-tiles, Body::BN columns), run the body.
 // With the combine epilogue (CMB), the last zero_wgs workgroups write the
-// dropped tokens' zero rows.
-template <bool FC1, class Body, bool CMB = false>
+// dropped tokens' zero rows.  TAIL: the dense tail's tiles follow the routed
+// ones.  QUEUE: one workgroup per CU takes tiles from the queue
+// (queue_tiles) instead of one tile per workgroup.
+template <bool FC1, class Body, bool CMB = false, bool TAIL = false, bool QUEUE = false>
 __global__ void __launch_bounds__(512) gmm_mx_kernel(MxA A, MxB B, MxOut O,
                                                      const int32_t* __restrict__ counts, int E,
-                                                     int N, int K, int64_t max_rows, int zero_wgs) {
+                                                     int N, int K, int64_t max_rows, int zero_wgs,
+                                                     MxDense dn, int* __restrict__ queue) {
+  static_assert(!(CMB && (TAIL || QUEUE)), "the combine epilogue runs in one-tile launches");
   if constexpr (CMB) {
     const int z = static_cast<int>(blockIdx.x) - static_cast<int>(gridDim.x - zero_wgs);
     if (z >= 0) {
@@ -357,28 +375,67 @@ __global__ void __launch_bounds__(512) gmm_mx_kernel(MxA A, MxB B, MxOut O,
       return;
     }
   }
+  constexpr int BM = Body::BM, BN = Body::BN;
   constexpr int DECODE_BYTES = (3 * kMaxExperts + 1) * 4 + 64;
   static_assert(Body::lds >= DECODE_BYTES, "decode scratch aliases the stages");
   __shared__ __attribute__((aligned(1024))) char smem[Body::lds];
-  const int NT = (N + Body::BN - 1) / Body::BN;
+  const int NT = (N + BN - 1) / BN;
+  const int ntd = TAIL ? (dn.N + BN - 1) / BN : 0;
+  // one call of the body per kernel; the operands are the routed experts'
+  // or the dense tail's
+  auto run = [&](Tile t, bool dense) {
+    t.e = __builtin_amdgcn_readfirstlane(t.e);
+    t.n0 = __builtin_amdgcn_readfirstlane(t.n0);
+    t.nrows = __builtin_amdgcn_readfirstlane(t.nrows);
+    t.row0 = static_cast<int64_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(t.row0)));
+    MxA ta = A;
+    MxB tb = B;
+    MxOut to = O;
+    int tn = N, tk = K;
+    if (TAIL && dense) {
+      ta = dn.A;
+      tb = dn.B;
+      to = dn.O;
+      tn = dn.N;
+      tk = dn.K;
+    }
+    Body::template run<CMB>(t, smem, ta, tb, to, tn, tk);
+  };
+  if constexpr (QUEUE) {
+    __shared__ int p_toff[kPersistMaxExperts + 1], p_roff[kPersistMaxExperts],
+        p_n[kPersistMaxExperts];
+    __shared__ int s_kq;
+    decode_to_tables<BM, 512>(counts, E, max_rows, smem, p_toff, p_roff, p_n);
+    const int64_t routed = static_cast<int64_t>(p_toff[E]) * NT;
+    const int64_t total = routed + (TAIL ? (dn.rows + BM - 1) / BM * ntd : 0);
+    queue_tiles(queue, total, &s_kq, [&](int64_t L) {
+      const bool dense = TAIL && L >= routed;
+      run(dense ? dense_tile_at<BM, kDenseBand>(L - routed, ntd, dn.rows, 0)
+                : tile_at<BM>(L, NT, E, p_toff, p_roff, p_n),
+          dense);
+    });
+    return;
+  }
   Tile tile;
-  {
+  bool mine;
+  // the tail starts at a multiple of 8, so d % 8 is this workgroup's XCD
+  const int d = TAIL ? static_cast<int>(blockIdx.x) - static_cast<int>(gridDim.x - dn.wgs) : -1;
+  if (TAIL && d >= 0) {
+    const int64_t L = xcd_tile(d, (dn.rows + BM - 1) / BM * ntd);
+    mine = L >= 0;
+    if (mine) tile = dense_tile_at<BM, kDenseBand>(L, ntd, dn.rows, 0);
+  } else {
     int* s_toff = reinterpret_cast<int*>(smem);
     int* s_roff = s_toff + kMaxExperts + 1;
     int* s_n = s_roff + kMaxExperts;
     int64_t* s_scan = reinterpret_cast<int64_t*>(s_n + kMaxExperts + 1);
-    const bool mine =
-        decode_tile<Body::BM, 512>(counts, E, max_rows, NT, s_toff, s_roff, s_n, s_scan, tile);
+    mine = decode_tile<BM, 512>(counts, E, max_rows, NT, s_toff, s_roff, s_n, s_scan, tile);
     __syncthreads();
-    // the decode is the same in every lane: say so to the compiler, so that
-    // the tile loop runs as uniform (scalar) control flow
-    if (!__builtin_amdgcn_readfirstlane(static_cast<int>(mine))) return;
   }
-  tile.e = __builtin_amdgcn_readfirstlane(tile.e);
-  tile.n0 = __builtin_amdgcn_readfirstlane(tile.n0);
-  tile.nrows = __builtin_amdgcn_readfirstlane(tile.nrows);
-  tile.row0 = static_cast<int64_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(tile.row0)));
-  Body::template run<CMB>(tile, smem, A, B, O, N, K);
+  // the decode is the same in every lane: say so to the compiler, so that
+  // the tile loop runs as uniform (scalar) control flow
+  if (!__builtin_amdgcn_readfirstlane(static_cast<int>(mine))) return;
+  run(tile, TAIL && d >= 0);
 }
 
 // Bodies (8 waves, two per SIMD).  LDS per stage = rows * 128 + 2 KB of
@@ -391,22 +448,43 @@ using MxFc2B128w = MxBody<128, 256, 2, 4, false, 3, 1>;
 using MxFc2B128 = MxBody<128, 128, 2, 4, false, 4, 0>;
 using MxFc2B64w = MxBody<64, 256, 2, 4, false, 3, 0>;
 
+// Queue launches from 192 rows per expert on average (as the bf16 GEMM).
+bool use_queue_mx(int64_t max_rows, int64_t E) {
+  return E > 1 && E <= kPersistMaxExperts && max_rows / E >= 192;
+}
+
 template <bool FC1, class Body>
 void launch_mx(const MxA& a, const MxB& b, const MxOut& o, const int32_t* counts, int64_t E,
-               int64_t N, int64_t K, int64_t max_rows, hipStream_t s) {
+               int64_t N, int64_t K, int64_t max_rows, hipStream_t s,
+               const MxDense* dense = nullptr, int* queue = nullptr) {
   const int64_t g = grid_for(max_rows, E, Body::BM, N, Body::BN);
+  MxDense dn{MxA{}, MxB{}, MxOut{}, 0, 0, 0, 0};
+  if (dense && dense->rows > 0) {
+    dn = *dense;
+    dn.wgs = static_cast<int>(grid_for(dn.rows, 1, Body::BM, dn.N, Body::BN));
+  }
+  const int e = static_cast<int>(E), n = static_cast<int>(N), k = static_cast<int>(K);
   if constexpr (!FC1) {
-    if (o.cmb.out) {
+    if (o.cmb.out) {  // callers pass neither a tail nor a queue
       const int64_t z = ceil_div(o.cmb.T, 8 * 16);  // 8 waves of 16 tokens
       hipLaunchKernelGGL((gmm_mx_kernel<FC1, Body, true>), dim3(static_cast<unsigned>(g + z)),
-                         dim3(512), 0, s, a, b, o, counts, static_cast<int>(E), static_cast<int>(N),
-                         static_cast<int>(K), max_rows, static_cast<int>(z));
+                         dim3(512), 0, s, a, b, o, counts, e, n, k, max_rows,
+                         static_cast<int>(z), dn, static_cast<int*>(nullptr));
       return;
     }
   }
-  hipLaunchKernelGGL((gmm_mx_kernel<FC1, Body>), dim3(static_cast<unsigned>(g)), dim3(512), 0, s, a,
-                     b, o, counts, static_cast<int>(E), static_cast<int>(N), static_cast<int>(K),
-                     max_rows, 0);
+  if (queue && use_queue_mx(max_rows, E)) {
+    if (g + dn.wgs == 0) return;
+    const auto kern = dn.wgs > 0 ? gmm_mx_kernel<FC1, Body, false, true, true>
+                                 : gmm_mx_kernel<FC1, Body, false, false, true>;
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(persistent_grid(g + dn.wgs))), dim3(512), 0,
+                       s, a, b, o, counts, e, n, k, max_rows, 0, dn, queue);
+    return;
+  }
+  const auto kern = dn.wgs > 0 ? gmm_mx_kernel<FC1, Body, false, true>
+                               : gmm_mx_kernel<FC1, Body>;
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(g + dn.wgs)), dim3(512), 0, s, a, b, o,
+                     counts, e, n, k, max_rows, 0, dn, static_cast<int*>(nullptr));
 }
 
 moe_status validate_mx(const char* who, int64_t E, int64_t h, int64_t f, int64_t max_rows) {
@@ -423,14 +501,24 @@ moe_status validate_mx(const char* who, int64_t E, int64_t h, int64_t f, int64_t
 }
 
 void launch_fc2_mx(const MxA& a, const MxB& b, const MxOut& o, const int32_t* counts, int64_t E,
-                   int64_t h, int64_t f, int64_t max_rows, hipStream_t s) {
+                   int64_t h, int64_t f, int64_t max_rows, hipStream_t s,
+                   const MxDense* dense = nullptr, int* queue = nullptr) {
   const int64_t avg = max_rows / E;
   if (avg >= 192)
-    launch_mx<false, MxFc2B128w>(a, b, o, counts, E, h, f, max_rows, s);
+    launch_mx<false, MxFc2B128w>(a, b, o, counts, E, h, f, max_rows, s, dense, queue);
   else if (avg >= 80)
-    launch_mx<false, MxFc2B128>(a, b, o, counts, E, h, f, max_rows, s);
+    launch_mx<false, MxFc2B128>(a, b, o, counts, E, h, f, max_rows, s, dense, queue);
   else
-    launch_mx<false, MxFc2B64w>(a, b, o, counts, E, h, f, max_rows, s);
+    launch_mx<false, MxFc2B64w>(a, b, o, counts, E, h, f, max_rows, s, dense, queue);
+}
+
+void launch_fc1_mx(const MxA& a, const MxB& b, const MxOut& o, const int32_t* counts, int64_t E,
+                   int64_t h, int64_t f, int64_t max_rows, hipStream_t s,
+                   const MxDense* dense = nullptr, int* queue = nullptr) {
+  if (max_rows / E >= 80)
+    launch_mx<true, MxFc1B128>(a, b, o, counts, E, f, h, max_rows, s, dense, queue);
+  else
+    launch_mx<true, MxFc1B64>(a, b, o, counts, E, f, h, max_rows, s, dense, queue);
 }
 
 }  // namespace
@@ -442,7 +530,7 @@ extern "C" moe_status moe_grouped_fc1_swiglu_mxfp8(
     int64_t E, int64_t h, int64_t f, int64_t max_rows, int64_t T, const uint8_t* x_codes,
     const uint8_t* x_scales, const int32_t* sorted_token, const int32_t* tokens_per_expert,
     const uint8_t* wg_codes, const uint8_t* wg_scales, const uint8_t* wu_codes,
-    const uint8_t* wu_scales, uint8_t* act_codes, uint8_t* act_scales, void* stream) {
+    const uint8_t* wu_scales, uint8_t* act_codes, uint8_t* act_scales, void* queue, void* stream) {
   moe_status st = validate_mx("moe_grouped_fc1_swiglu_mxfp8", E, h, f, max_rows);
   if (st != MOE_OK) return st;
   MOE_REQUIRE(T >= 0 && T < (int64_t(1) << 31), MOE_ERR_ARG, "moe_grouped_fc1_swiglu_mxfp8: T out of range");
@@ -453,18 +541,47 @@ extern "C" moe_status moe_grouped_fc1_swiglu_mxfp8(
   const MxA a{x_codes, x_scales, sorted_token, sorted_token ? T : max_rows, false};
   const MxB b{wg_codes, wg_scales, wu_codes, wu_scales};
   const MxOut o{act_codes, act_scales, nullptr, max_rows};
-  const hipStream_t s = as_stream(stream);
-  if (max_rows / E >= 80)
-    launch_mx<true, MxFc1B128>(a, b, o, tokens_per_expert, E, f, h, max_rows, s);
-  else
-    launch_mx<true, MxFc1B64>(a, b, o, tokens_per_expert, E, f, h, max_rows, s);
+  launch_fc1_mx(a, b, o, tokens_per_expert, E, h, f, max_rows, as_stream(stream), nullptr,
+                static_cast<int*>(queue));
   return check_launch("moe_grouped_fc1_swiglu_mxfp8");
+}
+
+extern "C" moe_status moe_grouped_fc1_swiglu_mxfp8_shared(
+    int64_t E, int64_t h, int64_t f, int64_t max_rows, int64_t T, const uint8_t* x_codes,
+    const uint8_t* x_scales, const int32_t* sorted_token, const int32_t* tokens_per_expert,
+    const uint8_t* wg_codes, const uint8_t* wg_scales, const uint8_t* wu_codes,
+    const uint8_t* wu_scales, uint8_t* act_codes, uint8_t* act_scales, int64_t fs,
+    const uint8_t* sg_codes, const uint8_t* sg_scales, const uint8_t* su_codes,
+    const uint8_t* su_scales, uint8_t* shared_act_codes, uint8_t* shared_act_scales, void* queue,
+    void* stream) {
+  const char* who = "moe_grouped_fc1_swiglu_mxfp8_shared";
+  moe_status st = validate_mx(who, E, h, f, max_rows);
+  if (st != MOE_OK) return st;
+  MOE_REQUIRE(T >= 0 && T < (int64_t(1) << 31), MOE_ERR_ARG, "%s: T out of range", who);
+  st = validate_mx(who, 1, h, fs, T);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  MOE_REQUIRE(sorted_token, MOE_ERR_ARG, "%s: the routed rows are gathered (sorted_token)", who);
+  MOE_REQUIRE(x_codes && x_scales && tokens_per_expert && wg_codes && wg_scales && wu_codes &&
+                  wu_scales && sg_codes && sg_scales && su_codes && su_scales &&
+                  shared_act_codes && shared_act_scales && (max_rows == 0 || (act_codes && act_scales)),
+              MOE_ERR_ARG, "%s: NULL tensor argument", who);
+  const MxA a{x_codes, x_scales, sorted_token, T, false};
+  const MxB b{wg_codes, wg_scales, wu_codes, wu_scales};
+  const MxOut o{act_codes, act_scales, nullptr, max_rows};
+  const MxDense dn{MxA{x_codes, x_scales, nullptr, T, false},
+                   MxB{sg_codes, sg_scales, su_codes, su_scales},
+                   MxOut{shared_act_codes, shared_act_scales, nullptr, T},
+                   T, static_cast<int>(fs), static_cast<int>(h), 0};
+  launch_fc1_mx(a, b, o, tokens_per_expert, E, h, f, max_rows, as_stream(stream), &dn,
+                static_cast<int*>(queue));
+  return check_launch(who);
 }
 
 extern "C" moe_status moe_grouped_fc2_mxfp8(int64_t E, int64_t h, int64_t f, int64_t max_rows,
                                             const uint8_t* act_codes, const uint8_t* act_scales,
                                             const int32_t* tokens_per_expert, const uint8_t* wd_codes,
-                                            const uint8_t* wd_scales, void* expert_out,
+                                            const uint8_t* wd_scales, void* expert_out, void* queue,
                                             void* stream) {
   moe_status st = validate_mx("moe_grouped_fc2_mxfp8", E, h, f, max_rows);
   if (st != MOE_OK) return st;
@@ -474,8 +591,38 @@ extern "C" moe_status moe_grouped_fc2_mxfp8(int64_t E, int64_t h, int64_t f, int
   const MxA a{act_codes, act_scales, nullptr, max_rows, true};
   const MxB b{wd_codes, wd_scales, nullptr, nullptr};
   MxOut o{nullptr, nullptr, static_cast<uint16_t*>(expert_out), max_rows};
-  launch_fc2_mx(a, b, o, tokens_per_expert, E, h, f, max_rows, as_stream(stream));
+  launch_fc2_mx(a, b, o, tokens_per_expert, E, h, f, max_rows, as_stream(stream), nullptr,
+                static_cast<int*>(queue));
   return check_launch("moe_grouped_fc2_mxfp8");
+}
+
+extern "C" moe_status moe_grouped_fc2_mxfp8_shared(
+    int64_t E, int64_t h, int64_t f, int64_t max_rows, const uint8_t* act_codes,
+    const uint8_t* act_scales, const int32_t* tokens_per_expert, const uint8_t* wd_codes,
+    const uint8_t* wd_scales, void* expert_out, int64_t T, int64_t fs,
+    const uint8_t* shared_act_codes, const uint8_t* shared_act_scales, const uint8_t* sd_codes,
+    const uint8_t* sd_scales, void* shared_out, void* queue, void* stream) {
+  const char* who = "moe_grouped_fc2_mxfp8_shared";
+  moe_status st = validate_mx(who, E, h, f, max_rows);
+  if (st != MOE_OK) return st;
+  MOE_REQUIRE(T >= 0 && T < (int64_t(1) << 31), MOE_ERR_ARG, "%s: T out of range", who);
+  st = validate_mx(who, 1, h, fs, T);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  MOE_REQUIRE(tokens_per_expert && wd_codes && wd_scales && shared_act_codes && shared_act_scales &&
+                  sd_codes && sd_scales && shared_out &&
+                  (max_rows == 0 || (act_codes && act_scales && expert_out)),
+              MOE_ERR_ARG, "%s: NULL tensor argument", who);
+  const MxA a{act_codes, act_scales, nullptr, max_rows, true};
+  const MxB b{wd_codes, wd_scales, nullptr, nullptr};
+  MxOut o{nullptr, nullptr, static_cast<uint16_t*>(expert_out), max_rows};
+  const MxDense dn{MxA{shared_act_codes, shared_act_scales, nullptr, T, true},
+                   MxB{sd_codes, sd_scales, nullptr, nullptr},
+                   MxOut{nullptr, nullptr, static_cast<uint16_t*>(shared_out), T},
+                   T, static_cast<int>(h), static_cast<int>(fs), 0};
+  launch_fc2_mx(a, b, o, tokens_per_expert, E, h, f, max_rows, as_stream(stream), &dn,
+                static_cast<int*>(queue));
+  return check_launch(who);
 }
 
 extern "C" moe_status moe_grouped_fc2_combine_mxfp8(

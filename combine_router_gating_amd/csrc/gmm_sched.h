@@ -208,6 +208,89 @@ __device__ __forceinline__ void zero_dropped_rows(const int32_t* __restrict__ ro
   }
 }
 
+// m-tiles per band of the dense (single-expert) tile order
+constexpr int kDenseBand = 8;
+// experts whose decoded tables a persistent or queue launch keeps in LDS
+constexpr int kPersistMaxExperts = 256;
+// Tile queue (one workgroup per CU): the logical tiles are cut into groups
+// of kQGroup consecutive tiles and XCD x owns groups x, x + 8, x + 16, ...;
+// each XCD's counter sits kQStride ints (a 128-byte line) after the
+// previous one, and the leave counter after the eight.
+constexpr int kQGroup = 32;
+constexpr int kQStride = 32;
+static_assert(9 * kQStride * 4 <= MOE_GEMM_QUEUE_BYTES, "queue counters fit the buffer");
+
+// Decode the counts once for a workgroup that runs many tiles: the scan
+// uses `scratch` (LDS that the tile stages reuse afterwards), the tables it
+// keeps are copied to p_toff [E+1], p_roff [E], p_n [E] (E <= kPersistMaxExperts).
+template <int BM, int NTHREADS>
+__device__ __forceinline__ void decode_to_tables(const int32_t* __restrict__ counts, int E,
+                                                 int64_t max_rows, char* scratch, int* p_toff,
+                                                 int* p_roff, int* p_n) {
+  int* s_toff = reinterpret_cast<int*>(scratch);
+  int* s_roff = s_toff + kMaxExperts + 1;
+  int* s_n = s_roff + kMaxExperts;
+  int64_t* s_scan = reinterpret_cast<int64_t*>(s_n + kMaxExperts + 1);
+  decode_counts<BM, NTHREADS>(counts, E, max_rows, s_toff, s_roff, s_n, s_scan);
+  for (int i = threadIdx.x; i <= E; i += blockDim.x) {
+    p_toff[i] = s_toff[i];
+    if (i < E) {
+      p_roff[i] = s_roff[i];
+      p_n[i] = s_n[i];
+    }
+  }
+  __syncthreads();  // tables copied out of the scratch area
+}
+
+// A workgroup leaving the queue: the last of the launch to leave sets the
+// counters back to zero, so the queue is zero again when the launch ends.
+__device__ __forceinline__ void queue_leave(int* __restrict__ queue) {
+  if (threadIdx.x == 0) {
+    if (atomicAdd(queue + 8 * kQStride, 1) == static_cast<int>(gridDim.x) - 1) {
+      for (int i = 0; i < 8; ++i) atomicExch(queue + i * kQStride, 0);
+      atomicExch(queue + 8 * kQStride, 0);
+    }
+  }
+}
+
+// Runs run(L) for every logical tile L < total that this workgroup takes from
+// the queue: its XCD's next tile while there is one, then the other XCDs'
+// remaining tiles, one XCD after another (a counter only grows, so an XCD
+// found empty stays empty), so that the XCDs end together.  Nothing waits
+// on another workgroup; each leaves through queue_leave.  Uniform over the
+// workgroup; s_kq is one int of LDS.
+template <class Run>
+__device__ __forceinline__ void queue_tiles(int* __restrict__ queue, int64_t total, int* s_kq,
+                                            Run&& run) {
+  const int x = static_cast<int>(blockIdx.x % 8);
+  for (int v = 0; v < 8;) {
+    const int xv = (x + v) % 8;
+    if (threadIdx.x == 0) *s_kq = atomicAdd(queue + xv * kQStride, 1);
+    __syncthreads();
+    const int64_t kq = *s_kq;
+    __syncthreads();  // s_kq is rewritten by the next take
+    const int64_t L = ((kq / kQGroup) * 8 + xv) * kQGroup + kq % kQGroup;
+    if (kq < 0 || L >= total) {  // uniform over the workgroup
+      ++v;
+      continue;
+    }
+    run(L);
+    __syncthreads();  // every wave is past the tile before its stages are refilled
+  }
+  queue_leave(queue);
+}
+
+// Workgroups of a persistent or queue launch: one per CU (a multiple of 8,
+// so that each workgroup stays on one XCD), never more than the tiles.
+inline int64_t persistent_grid(int64_t tiles_grid) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus < 8)
+    cus = 256;
+  return tiles_grid < cus / 8 * 8 ? tiles_grid : cus / 8 * 8;
+}
+
 // Workgroups for the worst case: every expert's row count rounded up to BM
 // (surplus workgroups exit after decoding), a multiple of 8 (one per XCD).
 inline int64_t grid_for(int64_t max_rows, int64_t E, int BM, int64_t N, int BN) {

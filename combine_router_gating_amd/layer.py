@@ -11,10 +11,12 @@ priority) from the start of the forward, joined before the combine;
 runs FC2 with the combine as its epilogue (moe_grouped_fc2_combine, or
 moe_grouped_fc2_combine_mxfp8 for MXFP8 experts; one "fc2_combine" stage):
 no expert_out round trip, bitwise the same output.
-`fold_shared` (on by default; bf16 layers with a shared expert and the
+`fold_shared` (on by default; layers with a shared expert and the
 gathering FC1) runs the shared expert's FC1 and FC2 as the last tiles of
 the routed experts' FC1 and FC2 launches (moe_grouped_fc1_swiglu_gather_shared,
-moe_grouped_fc2_shared): one stream, bitwise the same output.
+moe_grouped_fc2_shared; the _mxfp8_shared pair for MXFP8 experts): one
+stream, bitwise the same output.  `tile_queue` (on by default) gives the
+grouped GEMMs a tile queue (used where experts average >= 192 rows).
 `fuse_route_permute` (on by default) runs route and permute as one library
 call (moe_route_permute, one "route_permute" stage), which reuses the
 router's per-block counts for the permute; the outputs are bitwise those of
@@ -108,9 +110,10 @@ class MoELayerForward:
                 fs = self.fs
                 self.shared_actq = (e((T, fs), dtype=u8, device=dev),
                                     e((fs // 128, T, 4), dtype=u8, device=dev))
-        # bf16 layers with a shared expert and the gathering FC1 run the shared
-        # expert's GEMMs as the last tiles of the routed launches
-        self.fold_shared = bool(fold_shared and self.shared and self.gather and not self.mx
+        # layers with a shared expert and the gathering FC1 (bf16 or MXFP8
+        # experts) run the shared expert's GEMMs as the last tiles of the
+        # routed launches
+        self.fold_shared = bool(fold_shared and self.shared and self.gather
                                 and x.dtype == torch.bfloat16)
         self.overlap_shared = bool(overlap_shared and self.shared and not self.fold_shared)
         # the grouped GEMMs' tile queue (zeroed once; every call leaves it zeroed)
@@ -170,10 +173,22 @@ class MoELayerForward:
         i = self.inp
         if self.mx:
             wg, wu = self.wq["w_gate"], self.wq["w_up"]
+            if self.fold_shared:
+                sg, su = self.wq["shared_gate"], self.wq["shared_up"]
+                check("moe_grouped_fc1_swiglu_mxfp8_shared",
+                      self.lib.moe_grouped_fc1_swiglu_mxfp8_shared(
+                          self.E, self.h, self.f, self.max_rows, self.T, _p(self.xq[0]),
+                          _p(self.xq[1]), _p(self.sorted_token), _p(self.tokens_per_expert),
+                          _p(wg[0]), _p(wg[1]), _p(wu[0]), _p(wu[1]), _p(self.actq[0]),
+                          _p(self.actq[1]), self.fs, _p(sg[0]), _p(sg[1]), _p(su[0]), _p(su[1]),
+                          _p(self.shared_actq[0]), _p(self.shared_actq[1]), _p(self.queue),
+                          self._stream()))
+                return
             check("moe_grouped_fc1_swiglu_mxfp8", self.lib.moe_grouped_fc1_swiglu_mxfp8(
                 self.E, self.h, self.f, self.max_rows, self.T, _p(self.xq[0]), _p(self.xq[1]),
                 _p(self.sorted_token), _p(self.tokens_per_expert), _p(wg[0]), _p(wg[1]),
-                _p(wu[0]), _p(wu[1]), _p(self.actq[0]), _p(self.actq[1]), self._stream()))
+                _p(wu[0]), _p(wu[1]), _p(self.actq[0]), _p(self.actq[1]), _p(self.queue),
+                self._stream()))
             return
         if self.fold_shared:
             check("moe_grouped_fc1_swiglu_gather_shared",
@@ -197,10 +212,18 @@ class MoELayerForward:
     def fc2(self):
         if self.mx:
             wd = self.wq["w_down"]
+            if self.fold_shared:
+                sd = self.wq["shared_down"]
+                check("moe_grouped_fc2_mxfp8_shared", self.lib.moe_grouped_fc2_mxfp8_shared(
+                    self.E, self.h, self.f, self.max_rows, _p(self.actq[0]), _p(self.actq[1]),
+                    _p(self.tokens_per_expert), _p(wd[0]), _p(wd[1]), _p(self.expert_out),
+                    self.T, self.fs, _p(self.shared_actq[0]), _p(self.shared_actq[1]),
+                    _p(sd[0]), _p(sd[1]), _p(self.shared_out), _p(self.queue), self._stream()))
+                return
             check("moe_grouped_fc2_mxfp8", self.lib.moe_grouped_fc2_mxfp8(
                 self.E, self.h, self.f, self.max_rows, _p(self.actq[0]), _p(self.actq[1]),
                 _p(self.tokens_per_expert), _p(wd[0]), _p(wd[1]), _p(self.expert_out),
-                self._stream()))
+                _p(self.queue), self._stream()))
             return
         if self.fold_shared:
             i = self.inp
@@ -224,10 +247,10 @@ class MoELayerForward:
             check("moe_grouped_fc1_swiglu_mxfp8", self.lib.moe_grouped_fc1_swiglu_mxfp8(
                 1, self.h, self.fs, self.T, self.T, _p(self.xq[0]), _p(self.xq[1]), None,
                 _p(self.shared_count), _p(wg[0]), _p(wg[1]), _p(wu[0]), _p(wu[1]),
-                _p(self.shared_actq[0]), _p(self.shared_actq[1]), self._stream()))
+                _p(self.shared_actq[0]), _p(self.shared_actq[1]), None, self._stream()))
             check("moe_grouped_fc2_mxfp8", self.lib.moe_grouped_fc2_mxfp8(
                 1, self.h, self.fs, self.T, _p(self.shared_actq[0]), _p(self.shared_actq[1]),
-                _p(self.shared_count), _p(wd[0]), _p(wd[1]), _p(self.shared_out),
+                _p(self.shared_count), _p(wd[0]), _p(wd[1]), _p(self.shared_out), None,
                 self._stream()))
             return
         check("moe_grouped_fc1_swiglu", self.lib.moe_grouped_fc1_swiglu(

@@ -477,7 +477,7 @@ def moe_mxfp8_quantize_weight(w: torch.Tensor):
 
 
 def moe_grouped_fc1_swiglu_mxfp8(x_codes, x_scales, sorted_token, tokens_per_expert, wg, wu,
-                                 max_rows: int, act=None):
+                                 max_rows: int, act=None, queue: Optional[torch.Tensor] = None):
     """MXFP8 FC1 + SwiGLU: wg/wu from moe_mxfp8_quantize_weight; returns
     (act_codes [max_rows,f], act_scales k-tiled [f/128, max_rows, 4])."""
     T, h = x_codes.shape
@@ -503,12 +503,53 @@ def moe_grouped_fc1_swiglu_mxfp8(x_codes, x_scales, sorted_token, tokens_per_exp
     st = _lib.load().moe_grouped_fc1_swiglu_mxfp8(
         E, h, f, max_rows, T, _ptr(x_codes), _ptr(x_scales), _ptr(sorted_token),
         _ptr(tokens_per_expert), _ptr(wg[0]), _ptr(wg[1]), _ptr(wu[0]), _ptr(wu[1]), _ptr(act[0]),
-        _ptr(act[1]), _stream())
+        _ptr(act[1]), _ptr(queue), _stream())
     check("moe_grouped_fc1_swiglu_mxfp8", st)
     return act
 
 
-def moe_grouped_fc2_mxfp8(act_codes, act_scales, tokens_per_expert, wd, expert_out=None):
+def moe_grouped_fc1_swiglu_mxfp8_shared(x_codes, x_scales, sorted_token, tokens_per_expert, wg,
+                                        wu, max_rows: int, sg, su, act=None, shared_act=None,
+                                        queue: Optional[torch.Tensor] = None):
+    """The gathering MXFP8 FC1 of the routed experts and the shared expert's
+    MXFP8 FC1 over all tokens in one launch; sg/su from
+    moe_mxfp8_quantize_weight (E = 1); returns (act, shared_act), each
+    (codes, k-tiled scales)."""
+    T, h = x_codes.shape
+    E, f, _ = wg[0].shape
+    fs = sg[0].shape[1]
+    _need(x_codes, "x_codes", torch.uint8)
+    _need(x_scales, "x_scales", torch.uint8, (T, h // 32))
+    _need(tokens_per_expert, "tokens_per_expert", torch.int32, (E,))
+    _need(sorted_token, "sorted_token", torch.int32)
+    if sorted_token.numel() < max_rows:
+        raise ValueError("sorted_token needs max_rows entries")
+    for name, (c, sc), rows, fdim in (("wg", wg, E, f), ("wu", wu, E, f), ("sg", sg, 1, fs),
+                                      ("su", su, 1, fs)):
+        _need(c, name, torch.uint8, (rows, fdim, h))
+        _need(sc, name + " scales", torch.uint8, (rows, h // 128, fdim, 4))
+    dev = x_codes.device
+    if act is None:
+        act = (torch.empty((max_rows, f), dtype=torch.uint8, device=dev),
+               torch.empty((f // 128, max_rows, 4), dtype=torch.uint8, device=dev))
+    if shared_act is None:
+        shared_act = (torch.empty((T, fs), dtype=torch.uint8, device=dev),
+                      torch.empty((fs // 128, T, 4), dtype=torch.uint8, device=dev))
+    _need(act[0], "act codes", torch.uint8, (max_rows, f))
+    _need(act[1], "act scales", torch.uint8, (f // 128, max_rows, 4))
+    _need(shared_act[0], "shared act codes", torch.uint8, (T, fs))
+    _need(shared_act[1], "shared act scales", torch.uint8, (fs // 128, T, 4))
+    st = _lib.load().moe_grouped_fc1_swiglu_mxfp8_shared(
+        E, h, f, max_rows, T, _ptr(x_codes), _ptr(x_scales), _ptr(sorted_token),
+        _ptr(tokens_per_expert), _ptr(wg[0]), _ptr(wg[1]), _ptr(wu[0]), _ptr(wu[1]), _ptr(act[0]),
+        _ptr(act[1]), fs, _ptr(sg[0]), _ptr(sg[1]), _ptr(su[0]), _ptr(su[1]), _ptr(shared_act[0]),
+        _ptr(shared_act[1]), _ptr(queue), _stream())
+    check("moe_grouped_fc1_swiglu_mxfp8_shared", st)
+    return act, shared_act
+
+
+def moe_grouped_fc2_mxfp8(act_codes, act_scales, tokens_per_expert, wd, expert_out=None,
+                          queue: Optional[torch.Tensor] = None):
     """MXFP8 FC2 on FC1's act: wd from moe_mxfp8_quantize_weight; returns bf16 [max_rows,h]."""
     rows, f = act_codes.shape
     E, h, _ = wd[0].shape
@@ -520,9 +561,43 @@ def moe_grouped_fc2_mxfp8(act_codes, act_scales, tokens_per_expert, wd, expert_o
         expert_out = torch.empty((rows, h), dtype=torch.bfloat16, device=act_codes.device)
     st = _lib.load().moe_grouped_fc2_mxfp8(E, h, f, rows, _ptr(act_codes), _ptr(act_scales),
                                            _ptr(tokens_per_expert), _ptr(wd[0]), _ptr(wd[1]),
-                                           _ptr(expert_out), _stream())
+                                           _ptr(expert_out), _ptr(queue), _stream())
     check("moe_grouped_fc2_mxfp8", st)
     return expert_out
+
+
+def moe_grouped_fc2_mxfp8_shared(act_codes, act_scales, tokens_per_expert, wd, shared_act, sd,
+                                 expert_out=None, shared_out=None,
+                                 queue: Optional[torch.Tensor] = None):
+    """The MXFP8 FC2 of the routed experts and the shared expert's MXFP8 FC2
+    in one launch; shared_act as moe_grouped_fc1_swiglu_mxfp8_shared returns
+    it, sd from moe_mxfp8_quantize_weight (E = 1); returns (expert_out,
+    shared_out), bf16."""
+    rows, f = act_codes.shape
+    E, h, _ = wd[0].shape
+    T, fs = shared_act[0].shape
+    _need(act_codes, "act_codes", torch.uint8)
+    _need(act_scales, "act_scales", torch.uint8, (f // 128, rows, 4))
+    _need(tokens_per_expert, "tokens_per_expert", torch.int32, (E,))
+    _need(wd[0], "wd", torch.uint8, (E, h, f))
+    _need(wd[1], "wd scales", torch.uint8, (E, f // 128, h, 4))
+    _need(shared_act[0], "shared act codes", torch.uint8, (T, fs))
+    _need(shared_act[1], "shared act scales", torch.uint8, (fs // 128, T, 4))
+    _need(sd[0], "sd", torch.uint8, (1, h, fs))
+    _need(sd[1], "sd scales", torch.uint8, (1, fs // 128, h, 4))
+    dev = act_codes.device
+    if expert_out is None:
+        expert_out = torch.empty((rows, h), dtype=torch.bfloat16, device=dev)
+    if shared_out is None:
+        shared_out = torch.empty((T, h), dtype=torch.bfloat16, device=dev)
+    _need(expert_out, "expert_out", torch.bfloat16, (rows, h))
+    _need(shared_out, "shared_out", torch.bfloat16, (T, h))
+    st = _lib.load().moe_grouped_fc2_mxfp8_shared(
+        E, h, f, rows, _ptr(act_codes), _ptr(act_scales), _ptr(tokens_per_expert), _ptr(wd[0]),
+        _ptr(wd[1]), _ptr(expert_out), T, fs, _ptr(shared_act[0]), _ptr(shared_act[1]),
+        _ptr(sd[0]), _ptr(sd[1]), _ptr(shared_out), _ptr(queue), _stream())
+    check("moe_grouped_fc2_mxfp8_shared", st)
+    return expert_out, shared_out
 
 
 def moe_grouped_fc2_combine_mxfp8(act_codes, act_scales, tokens_per_expert, wd, permuted_probs,

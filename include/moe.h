@@ -66,7 +66,9 @@ typedef enum { MOE_DROP_POSITION = 0, MOE_DROP_PROBS = 1 } moe_drop_policy;
  * 3: moe_route_permute, moe_grouped_fc2_combine,
  * moe_grouped_fc2_combine_mxfp8; 4: moe_grouped_fc1_swiglu_gather_shared,
  * moe_grouped_fc2_shared; 5: moe_route_permute_noalloc; 6: the queue
- * argument of the bf16 GEMM entry points; 7: moe_clock_probe). */
+ * argument of the bf16 GEMM entry points; 7: moe_clock_probe; 8: the
+ * queue argument of the MXFP8 GEMM entry points,
+ * moe_grouped_fc1_swiglu_mxfp8_shared, moe_grouped_fc2_mxfp8_shared). */
 int moe_abi_version(void);
 
 /* Message for the last non-OK status returned on the calling thread. */
@@ -458,6 +460,10 @@ moe_status moe_mxfp8_quantize(int64_t rows, int64_t cols, int64_t tile_rows, int
  *   wg_*, wu_*          codes [E,f,h], scales k-tiled with R = f
  *   act_codes           [max_rows,f]                          out
  *   act_scales          k-tiled [f/128, max_rows, 4] (R = max_rows)   out
+ *   queue               NULL, or a tile queue as for the bf16 GEMMs
+ *                       (MOE_GEMM_QUEUE_BYTES, zero on entry, zero again
+ *                       when the launch ends); used from 192 rows per
+ *                       expert on average, same results either way
  * h and f multiples of 128.  Rows >= sum(tokens_per_expert) untouched.
  */
 moe_status moe_grouped_fc1_swiglu_mxfp8(int64_t E, int64_t h, int64_t f, int64_t max_rows,
@@ -466,15 +472,52 @@ moe_status moe_grouped_fc1_swiglu_mxfp8(int64_t E, int64_t h, int64_t f, int64_t
                                         const int32_t* tokens_per_expert, const uint8_t* wg_codes,
                                         const uint8_t* wg_scales, const uint8_t* wu_codes,
                                         const uint8_t* wu_scales, uint8_t* act_codes,
-                                        uint8_t* act_scales, void* stream);
+                                        uint8_t* act_scales, void* queue, void* stream);
+
+/* moe_grouped_fc1_swiglu_mxfp8_shared — moe_grouped_fc1_swiglu_mxfp8 (with
+ * the gather) plus the shared expert's FC1 + SwiGLU in the same launch
+ * ([MC] §11: one expert that every token passes through), its tiles after
+ * the routed experts'.  The shared expert reads x_codes/x_scales as they
+ * are (all T rows, not gathered); sg_*, su_* are its weights (codes [fs,h],
+ * scales k-tiled with R = fs); shared_act_codes [T,fs] and
+ * shared_act_scales k-tiled [fs/128, T, 4] are written bitwise as
+ * moe_grouped_fc1_swiglu_mxfp8 with E = 1, counts {T}, max_rows = T and no
+ * gather writes them.  fs a multiple of 128.  Errors: those of
+ * moe_grouped_fc1_swiglu_mxfp8; MOE_ERR_ARG when sorted_token is NULL or a
+ * shared tensor is NULL (act may be NULL only when max_rows = 0).  T = 0
+ * is a no-op. */
+moe_status moe_grouped_fc1_swiglu_mxfp8_shared(
+    int64_t E, int64_t h, int64_t f, int64_t max_rows, int64_t T, const uint8_t* x_codes,
+    const uint8_t* x_scales, const int32_t* sorted_token, const int32_t* tokens_per_expert,
+    const uint8_t* wg_codes, const uint8_t* wg_scales, const uint8_t* wu_codes,
+    const uint8_t* wu_scales, uint8_t* act_codes, uint8_t* act_scales, int64_t fs,
+    const uint8_t* sg_codes, const uint8_t* sg_scales, const uint8_t* su_codes,
+    const uint8_t* su_scales, uint8_t* shared_act_codes, uint8_t* shared_act_scales, void* queue,
+    void* stream);
 
 /* moe_grouped_fc2_mxfp8 — expert_out [max_rows,h] (bf16) = act Wd^T on MXFP8
  * act (as moe_grouped_fc1_swiglu_mxfp8 writes it) and Wd (codes [E,h,f],
- * scales k-tiled with R = h). */
+ * scales k-tiled with R = h).  queue: as for moe_grouped_fc1_swiglu_mxfp8. */
 moe_status moe_grouped_fc2_mxfp8(int64_t E, int64_t h, int64_t f, int64_t max_rows,
                                  const uint8_t* act_codes, const uint8_t* act_scales,
                                  const int32_t* tokens_per_expert, const uint8_t* wd_codes,
-                                 const uint8_t* wd_scales, void* expert_out, void* stream);
+                                 const uint8_t* wd_scales, void* expert_out, void* queue,
+                                 void* stream);
+
+/* moe_grouped_fc2_mxfp8_shared — moe_grouped_fc2_mxfp8 plus the shared
+ * expert's FC2 in the same launch, its tiles after the routed experts':
+ * shared_out [T,h] (bf16) = shared_act sd^T, bitwise what
+ * moe_grouped_fc2_mxfp8 with E = 1, counts {T} and max_rows = T writes
+ * (shared_act as moe_grouped_fc1_swiglu_mxfp8_shared writes it; sd codes
+ * [h,fs], scales k-tiled with R = h).  Errors: those of
+ * moe_grouped_fc2_mxfp8; MOE_ERR_ARG for T out of range or a NULL shared
+ * tensor.  T = 0 is a no-op. */
+moe_status moe_grouped_fc2_mxfp8_shared(
+    int64_t E, int64_t h, int64_t f, int64_t max_rows, const uint8_t* act_codes,
+    const uint8_t* act_scales, const int32_t* tokens_per_expert, const uint8_t* wd_codes,
+    const uint8_t* wd_scales, void* expert_out, int64_t T, int64_t fs,
+    const uint8_t* shared_act_codes, const uint8_t* shared_act_scales, const uint8_t* sd_codes,
+    const uint8_t* sd_scales, void* shared_out, void* queue, void* stream);
 
 /* moe_grouped_fc2_combine_mxfp8 — moe_grouped_fc2_mxfp8 with the top-1
  * combine as its epilogue, as moe_grouped_fc2_combine is to

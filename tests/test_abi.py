@@ -28,7 +28,7 @@ def test_library_exports_every_declared_function():
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(_lib.SIGNATURES) == names
-    assert lib.moe_abi_version() == 7
+    assert lib.moe_abi_version() == 8
 
 
 def test_route_desc_layout_matches_c():
@@ -138,18 +138,47 @@ def test_mxfp8_entry_points_reject_bad_sizes():
     st, _ = _status("moe_mxfp8_quantize", 4, 128, 0, _lib.MOE_BF16, None, p, p, None)
     assert st == _lib.MOE_ERR_ARG  # NULL source
     st, msg = _status("moe_grouped_fc1_swiglu_mxfp8", 4, 192, 256, 8, 8, p, p, None, p, p, p, p, p,
-                      p, p, None)
+                      p, p, None, None)
     assert st == _lib.MOE_ERR_UNSUPPORTED and "multiples of 128" in msg
     st, _ = _status("moe_grouped_fc1_swiglu_mxfp8", 0, 128, 128, 8, 8, p, p, None, p, p, p, p, p,
-                    p, p, None)
+                    p, p, None, None)
     assert st == _lib.MOE_ERR_ARG  # E
     st, _ = _status("moe_grouped_fc1_swiglu_mxfp8", 4, 128, 128, 8, 8, p, p, None, None, p, p, p, p,
-                    p, p, None)
+                    p, p, None, None)
     assert st == _lib.MOE_ERR_ARG  # NULL counts
-    st, _ = _status("moe_grouped_fc2_mxfp8", 4, 128, 320, 8, p, p, p, p, p, p, None)
+    st, _ = _status("moe_grouped_fc2_mxfp8", 4, 128, 320, 8, p, p, p, p, p, p, None, None)
     assert st == _lib.MOE_ERR_UNSUPPORTED  # f % 128
-    st, _ = _status("moe_grouped_fc2_mxfp8", 4, 128, 128, 8, p, p, p, p, p, None, None)
+    st, _ = _status("moe_grouped_fc2_mxfp8", 4, 128, 128, 8, p, p, p, p, p, None, None, None)
     assert st == _lib.MOE_ERR_ARG  # NULL output
+
+
+def test_mxfp8_shared_entry_points_validate_before_launching():
+    p = ctypes.c_void_p(16)
+    # fc1: E, h, f, max_rows, T, x codes/scales, sorted_token, counts, wg, wu (codes, scales),
+    # act (codes, scales), fs, sg, su (codes, scales), shared act (codes, scales), queue, stream
+    def fc1(fs=128, sorted_token=p, shared_act=p, T=8):
+        return _status("moe_grouped_fc1_swiglu_mxfp8_shared", 4, 128, 128, 8, T, p, p, sorted_token,
+                       p, p, p, p, p, p, p, fs, p, p, p, p, shared_act, p, None, None)
+    st, msg = fc1(fs=192)
+    assert st == _lib.MOE_ERR_UNSUPPORTED and "multiples of 128" in msg  # the shared ffn
+    st, msg = fc1(sorted_token=None)
+    assert st == _lib.MOE_ERR_ARG and "sorted_token" in msg
+    st, _ = fc1(shared_act=None)
+    assert st == _lib.MOE_ERR_ARG
+    st, _ = fc1(T=-1)
+    assert st == _lib.MOE_ERR_ARG
+    assert fc1(T=0)[0] == 0  # no tokens: a no-op
+
+    # fc2: E, h, f, max_rows, act (codes, scales), counts, wd (codes, scales), expert_out, T, fs,
+    # shared act (codes, scales), sd (codes, scales), shared_out, queue, stream
+    def fc2(fs=128, shared_out=p, T=8):
+        return _status("moe_grouped_fc2_mxfp8_shared", 4, 128, 128, 8, p, p, p, p, p, p, T, fs, p,
+                       p, p, p, shared_out, None, None)
+    st, msg = fc2(fs=64)
+    assert st == _lib.MOE_ERR_UNSUPPORTED and "multiples of 128" in msg
+    st, _ = fc2(shared_out=None)
+    assert st == _lib.MOE_ERR_ARG
+    assert fc2(T=0)[0] == 0
 
 
 def test_wrapper_rejects_cpu_tensors():

@@ -160,21 +160,22 @@ def test_mxfp8_rejects_bad_sizes():
     assert lib.moe_mxfp8_quantize(4, 48, 0, 1, q, q, q, p) == 2       # cols % 32
     assert lib.moe_mxfp8_quantize(4, 96, 2, 1, q, q, q, p) == 2       # tiled: cols % 128
     assert lib.moe_mxfp8_quantize(6, 128, 4, 1, q, q, q, p) == 2      # tiled: rows % R
-    assert lib.moe_grouped_fc2_mxfp8(4, 192, 256, 8, q, q, q, q, q, q, p) == 2  # h % 128
+    assert lib.moe_grouped_fc2_mxfp8(4, 192, 256, 8, q, q, q, q, q, q, None, p) == 2  # h % 128
 
 
-@pytest.mark.parametrize("overlap", [False, True])
-def test_layer_mxfp8_against_the_oracle(overlap):
+@pytest.mark.parametrize("overlap,fold", [(False, True), (True, False), (False, False)])
+def test_layer_mxfp8_against_the_oracle(overlap, fold):
     import datagen
     import oracle
     from combine_router_gating_amd.layer import MoELayerForward
     from gpu_helpers import f64
     cfg = datagen.MoEConfig("mx-layer", T=300, h=256, E=16, K=2, f=384, dtype="bf16", score="sigmoid",
                             expert_bias=True, shared_f=256, capacity_factor=0.8)
-    log(f"mxfp8 layer overlap={overlap}: {cfg}")
+    log(f"mxfp8 layer overlap={overlap} fold={fold}: {cfg}")
     inp = datagen.make_inputs(cfg, seed=3, device=DEV)
     layer = MoELayerForward(inp, K=cfg.K, score=cfg.score, capacity_factor=cfg.capacity_factor,
-                            overlap_shared=overlap, precision="mxfp8")
+                            overlap_shared=overlap, precision="mxfp8", fold_shared=fold)
+    assert layer.fold_shared == fold and layer.overlap_shared == overlap
     out = layer.forward().clone()
     torch.cuda.synchronize()
     # routing is the bf16 layer's (same router kernels)
@@ -202,29 +203,33 @@ def test_layer_mxfp8_against_the_oracle(overlap):
     shared = oracle.round_bf16(sact @ swd.T)
     ref_out = oracle.combine(y, pm["permuted_probs"], pm["row_id_map"], "bf16", shared)
     assert_close(f64(out), ref_out, "bf16", "out")
-    # the same forward without the overlap gives the same bits
+    # the same forward with the shared expert in launches of its own on one
+    # stream gives the same bits
     plain = MoELayerForward(inp, K=cfg.K, score=cfg.score, capacity_factor=cfg.capacity_factor,
-                            precision="mxfp8")
+                            precision="mxfp8", fold_shared=False)
     o2 = plain.forward()
     torch.cuda.synchronize()
     assert torch.equal(out, o2)
 
 
-def test_layer_mxfp8_graph_capture_replays():
-    """The MXFP8 forward (x quantisation, router, permute, MXFP8 GEMMs,
-    shared expert on a second stream, combine) captures into a graph; replays
-    on new inputs equal the eager forward bit for bit."""
+@pytest.mark.parametrize("fold", [False, True])
+def test_layer_mxfp8_graph_capture_replays(fold):
+    """The MXFP8 forward (x quantisation, router, permute, MXFP8 GEMMs, the
+    shared expert on a second stream or folded into the routed launches,
+    combine) captures into a graph; replays on new inputs equal the eager
+    forward bit for bit."""
     import datagen
     from combine_router_gating_amd.layer import MoELayerForward
     cfg = datagen.MoEConfig("mx-graph", T=512, h=256, E=16, K=2, f=256, dtype="bf16", shared_f=128)
     inp = datagen.make_inputs(cfg, seed=5, device=DEV)
-    layer = MoELayerForward(inp, K=cfg.K, overlap_shared=True, precision="mxfp8")
+    layer = MoELayerForward(inp, K=cfg.K, overlap_shared=not fold, precision="mxfp8",
+                            fold_shared=fold)
     layer.forward()
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         out = layer.forward()
-    plain = MoELayerForward(inp, K=cfg.K, precision="mxfp8")
+    plain = MoELayerForward(inp, K=cfg.K, precision="mxfp8", fold_shared=False)
     for seed in (6, 7, 8):
         new = datagen.make_inputs(cfg, seed=seed, device=DEV, with_experts=False)
         inp["x"].copy_(new["x"])
@@ -258,8 +263,9 @@ def test_mxfp8_gemm_edge_cases():
     import ctypes
     lib = moe.load()
     q = ctypes.c_void_p(16)
-    assert lib.moe_grouped_fc1_swiglu_mxfp8(E, h, f, 0, 1, q, q, None, q, q, q, q, q, q, q, None) == 0
-    assert lib.moe_grouped_fc2_mxfp8(E, h, f, 0, q, q, q, q, q, q, None) == 0
+    assert lib.moe_grouped_fc1_swiglu_mxfp8(E, h, f, 0, 1, q, q, None, q, q, q, q, q, q, q, None,
+                                            None) == 0
+    assert lib.moe_grouped_fc2_mxfp8(E, h, f, 0, q, q, q, q, q, q, None, None) == 0
 
 
 def test_mxfp8_gemm_counts_past_max_rows_stay_in_bounds():
@@ -279,7 +285,8 @@ def test_mxfp8_gemm_counts_past_max_rows_stay_in_bounds():
     import ctypes
     p = lambda t: ctypes.c_void_p(t.data_ptr())
     st = moe.load().moe_grouped_fc2_mxfp8(E, h, f, R, p(act_c), p(act_s), p(cnt), p(wd[0]), p(wd[1]),
-                                         p(y), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+                                         p(y), None,
+                                         ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
     assert st == 0
     torch.cuda.synchronize()
     assert (act_c[R:] == 0x5a).all()
@@ -445,3 +452,52 @@ def test_layer_mxfp8_full_size_sampled(name, n_tok):
         o2 = plain.forward()
         torch.cuda.synchronize()
         assert torch.equal(out, o2)
+
+
+@pytest.mark.parametrize("fs", [0, 256])
+def test_mxfp8_tile_queue_and_folded_shared_expert_match_plain_launches(fs):
+    """The MXFP8 GEMMs with a tile queue (experts of >= 192 rows on average)
+    give the bits of one workgroup per tile, and with the shared expert's
+    tiles folded into the routed launches the shared act and output are the
+    bits of separate E = 1 launches; on repeated calls with one queue, which
+    is zero again afterwards."""
+    import datagen
+    cfg = datagen.MoEConfig("mx-queue", T=2048, h=256, E=16, K=2, f=384, dtype="bf16",
+                            score="sigmoid", expert_bias=True, shared_f=fs)
+    log(f"mxfp8 tile queue / fold: {cfg}")
+    inp = datagen.make_inputs(cfg, seed=21, device=DEV)
+    r = moe.moe_route_permute(inp["x"], inp["w_router"], K=cfg.K, score="sigmoid",
+                              expert_bias=inp["expert_bias"], copy_rows=False)
+    st, tpe = r["sorted_token"], r["tokens_per_expert"]
+    rows = st.shape[0]
+    N = int(r["expert_offsets"][-1].item())
+    assert rows // cfg.E >= 192  # the queue is used
+    xc, xs = moe.moe_mxfp8_quantize(inp["x"])
+    wg, wu, wd = (moe.moe_mxfp8_quantize_weight(inp[k]) for k in ("w_gate", "w_up", "w_down"))
+    q = moe.gemm_queue(DEV)
+    if fs:
+        sg, su, sd = (moe.moe_mxfp8_quantize_weight(inp[k][None])
+                      for k in ("shared_gate", "shared_up", "shared_down"))
+        allrows = torch.tensor([cfg.T], dtype=torch.int32, device=DEV)
+    for _ in range(3):
+        a0 = moe.moe_grouped_fc1_swiglu_mxfp8(xc, xs, st, tpe, wg, wu, rows)
+        a1 = moe.moe_grouped_fc1_swiglu_mxfp8(xc, xs, st, tpe, wg, wu, rows, queue=q)
+        y0 = moe.moe_grouped_fc2_mxfp8(a0[0], a0[1], tpe, wd)
+        y1 = moe.moe_grouped_fc2_mxfp8(a1[0], a1[1], tpe, wd, queue=q)
+        torch.cuda.synchronize()
+        assert torch.equal(a0[0][:N], a1[0][:N]) and torch.equal(a0[1][:, :N], a1[1][:, :N])
+        assert torch.equal(y0[:N], y1[:N])
+        if fs:
+            s0 = moe.moe_grouped_fc1_swiglu_mxfp8(xc, xs, None, allrows, sg, su, cfg.T)
+            o0 = moe.moe_grouped_fc2_mxfp8(s0[0], s0[1], allrows, sd)
+            for queue in (None, q):
+                a2, s2 = moe.moe_grouped_fc1_swiglu_mxfp8_shared(xc, xs, st, tpe, wg, wu, rows, sg,
+                                                                 su, queue=queue)
+                y2, o2 = moe.moe_grouped_fc2_mxfp8_shared(a2[0], a2[1], tpe, wd, s2, sd,
+                                                          queue=queue)
+                torch.cuda.synchronize()
+                assert torch.equal(a2[0][:N], a0[0][:N]) and torch.equal(a2[1][:, :N], a0[1][:, :N])
+                assert torch.equal(y2[:N], y0[:N])
+                assert torch.equal(s2[0], s0[0]) and torch.equal(s2[1], s0[1])
+                assert torch.equal(o2, o0)
+        assert int(torch.count_nonzero(q).item()) == 0
