@@ -79,6 +79,8 @@ def parse():
                    help="shared expert in launches of its own (on a second stream unless "
                         "--no-overlap) instead of the routed launches' last tiles")
     p.add_argument("--no-cold", action="store_true", help="skip the cache-flushed pass")
+    p.add_argument("--no-clock", action="store_true",
+                   help="skip the clock pass (extra forwards with clock probes on a second stream)")
     p.add_argument("--precision", default="bf16", choices=("bf16", "mxfp8"),
                    help="expert GEMM operands (mxfp8: OCP MX blocks of 32, E4M3)")
     return p.parse_args()
@@ -429,7 +431,7 @@ def main():
             stage_report[s]["frac_of_hbm_peak"] = round(nb / sec_s / 1e9 / HBM_PEAK_GBS, 4)
             stage_report[s]["frac_of_copy"] = round(nb / sec_s / 1e9 / copy_gbs, 4)
 
-    clock = clock_pass(layer, dev, ms_per_step, args.steps)
+    clock = None if args.no_clock else clock_pass(layer, dev, ms_per_step, args.steps)
 
     cold = None
     if not args.no_cold:
