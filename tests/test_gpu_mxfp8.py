@@ -501,3 +501,92 @@ def test_mxfp8_tile_queue_and_folded_shared_expert_match_plain_launches(fs):
                 assert torch.equal(s2[0], s0[0]) and torch.equal(s2[1], s0[1])
                 assert torch.equal(o2, o0)
         assert int(torch.count_nonzero(q).item()) == 0
+
+
+@pytest.mark.parametrize("name", ["dsv3", "mixtral"])
+def test_mxfp8_bench_layer_whole_experts(name):
+    """The MXFP8 layer at full size in the benchmark's launch configuration
+    (gathering FC1, tile queue, shared expert folded into the routed
+    launches): every row and column of act and expert_out for the busiest
+    expert, for one whose last 128-row m-tile is ragged and (DeepSeek-V3-
+    shaped) for the smallest; the folded shared expert on a whole 128-row
+    m-tile; and 256 tokens of the output as the combine of the checked
+    expert and shared outputs.  act within the accumulation bound of the
+    exact SwiGLU of the GPU's MXFP8 operands, expert_out and out within the
+    bf16 tolerance of the oracle run on the GPU's act codes."""
+    import datagen
+    import oracle
+    from combine_router_gating_amd.layer import MoELayerForward
+    from gpu_helpers import f64, routing_ref
+    cfg = datagen.CONFIGS[name]
+    log(f"mxfp8 full-size whole experts: {cfg}")
+    inp = datagen.make_inputs(cfg, seed=0, device=DEV)
+    layer = MoELayerForward(inp, K=cfg.K, score=cfg.score, pre_softmax=cfg.pre_softmax,
+                            capacity_factor=cfg.capacity_factor, min_capacity=cfg.min_capacity,
+                            gather=True, precision="mxfp8")
+    assert layer.fold_shared == ("shared_gate" in inp) and layer.queue is not None
+    out = layer.forward()
+    torch.cuda.synchronize()
+    eb = inp["expert_bias"].cpu().numpy() if "expert_bias" in inp else None
+    ref = routing_ref(cfg, layer.logits.cpu().numpy(), eb)
+    np.testing.assert_array_equal(_np(layer.routing_map), ref["routing_map"])
+    xc, xs = mx.mx_quantize(f64(inp["x"]))
+    np.testing.assert_array_equal(_np(layer.xq[0]), xc)
+    np.testing.assert_array_equal(_np(layer.xq[1]), xs)
+    xq = mx.mx_dequantize(xc, xs)
+    pm = oracle.permute(np.zeros((cfg.T, 1)), ref["routing_map"], ref["probs"], cfg.K)
+    n = pm["tokens_per_expert"]
+    offs = np.concatenate([[0], np.cumsum(n)])
+    st = pm["sorted_token"]
+    np.testing.assert_array_equal(_np(layer.sorted_token)[:offs[-1]], st)
+    act_s_all = layer.actq[1]
+
+    def check_rows(xr, wg, wu, wd, act_c, act_s, y_gpu, what):
+        g, u = xr @ wg.T, xr @ wu.T
+        sg = 1 / (1 + np.exp(-g))
+        exact = g * sg * u
+        sens = 1.1 * np.abs(u) * (np.abs(xr) @ np.abs(wg).T) + \
+            np.abs(g * sg) * (np.abs(xr) @ np.abs(wu).T)
+        dq = mx.mx_dequantize(act_c, act_s)
+        bad = np.abs(dq - exact) > _act_bound(exact, sens, act_s)
+        assert not bad.any(), (what, int(bad.sum()))
+        assert_close(y_gpu, oracle.round_bf16(dq @ wd.T), "bf16", what)
+
+    def expert_w(key, e):
+        c, s = layer.wq[key]
+        return mx.mx_dequantize(_np(c[e]), untile(s[e][None])[0])
+
+    busiest = int(np.argmax(n))
+    ragged = [int(e) for e in np.argsort(-n) if n[e] > 128 and n[e] % 128 and e != busiest]
+    experts = [busiest] + ragged[:1]
+    nz = np.nonzero(n)[0]
+    smallest = int(nz[np.argmin(n[nz])])
+    if n[smallest] < 64 and smallest not in experts:
+        experts.append(smallest)
+    act_rows_c = layer.actq[0]
+    for e in experts:
+        rows = np.arange(offs[e], offs[e + 1])
+        log(f"  expert {e}: {len(rows)} rows")
+        idx = torch.from_numpy(rows).to(DEV)
+        act_c = _np(act_rows_c[idx])
+        act_s = untile(act_s_all[:, idx])
+        check_rows(xq[st[rows]], expert_w("w_gate", e), expert_w("w_up", e),
+                   expert_w("w_down", e), act_c, act_s, f64(layer.expert_out[idx]),
+                   f"{name} expert {e}")
+    if layer.shared:
+        t0 = 1024
+        tok = np.arange(t0, t0 + 128)
+        sact_s = untile(layer.shared_actq[1][:, t0:t0 + 128])
+        check_rows(xq[tok], expert_w("shared_gate", 0), expert_w("shared_up", 0),
+                   expert_w("shared_down", 0), _np(layer.shared_actq[0][t0:t0 + 128]), sact_s,
+                   f64(layer.shared_out[t0:t0 + 128]), f"{name} shared expert")
+    # 256 tokens: combine of the GPU's expert rows (and shared rows), in the oracle's order
+    toks = np.sort(np.random.default_rng(7).choice(cfg.T, size=256, replace=False))
+    rid = pm["row_id_map"][toks]
+    rows_needed = np.unique(rid[rid >= 0])
+    y = np.zeros((int(offs[-1]), cfg.h))
+    y[rows_needed] = f64(layer.expert_out[torch.from_numpy(rows_needed).to(DEV)])
+    shared = f64(layer.shared_out)[toks] if layer.shared else None
+    sub_rid = np.where(rid >= 0, rid, -1)
+    exp = oracle.combine(y, pm["permuted_probs"], sub_rid, "bf16", shared)
+    assert_close(f64(out)[toks], exp, "bf16", f"out[{name}, 256 tokens]")
