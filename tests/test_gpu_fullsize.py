@@ -2,7 +2,7 @@
 as one call, gathering FC1, shared expert folded into the routed launches),
 on whole experts and on 256 tokens.
 
-For the DeepSeek-V3- and Mixtral-shaped layers: every row and every column
+For the DeepSeek-V3-, Mixtral- and Qwen3-shaped layers: every row and every column
 of act and expert_out for the busiest expert, for an expert whose last
 m-tile is ragged, and (DeepSeek-V3-shaped) for the smallest expert; and the
 layer output of 256 random tokens, element by element, at the bf16
@@ -46,7 +46,7 @@ def _token_outputs_by_expert(toks, x, rmap, probs, inp, shared, dtype):
     return oracle.round_to(acc, dtype)
 
 
-@pytest.mark.parametrize("name", ["dsv3", "mixtral"])
+@pytest.mark.parametrize("name", ["dsv3", "mixtral", "qwen3"])
 def test_bench_layer_whole_experts_and_256_tokens(name):
     cfg = datagen.CONFIGS[name]
     log(f"full-size whole experts: {cfg}")

@@ -503,7 +503,7 @@ def test_mxfp8_tile_queue_and_folded_shared_expert_match_plain_launches(fs):
         assert int(torch.count_nonzero(q).item()) == 0
 
 
-@pytest.mark.parametrize("name", ["dsv3", "mixtral"])
+@pytest.mark.parametrize("name", ["dsv3", "mixtral", "qwen3"])
 def test_mxfp8_bench_layer_whole_experts(name):
     """The MXFP8 layer at full size in the benchmark's launch configuration
     (gathering FC1, tile queue, shared expert folded into the routed
