@@ -309,8 +309,8 @@ moe_status moe_route_permute_noalloc(const moe_route_desc* d, const void* x,
  *
  * queue (every GEMM entry point below that takes one): NULL, or a device
  * buffer of MOE_GEMM_QUEUE_BYTES that is all zero before the first call
- * that uses it.  With a queue, a bf16 launch of 2 to 256 experts whose
- * average row count (max_rows / E) is >= 192 runs one workgroup per CU,
+ * that uses it.  With a queue, a bf16 or MXFP8 launch of 2 to 256 experts
+ * whose average row count (max_rows / E) is >= 192 runs one workgroup per CU,
  * and each takes the next tile of its XCD's share from a counter in the
  * queue (tile groups of 32 dealt to the XCDs in turn), instead of one
  * workgroup per tile handed out by the hardware; other launches ignore the
