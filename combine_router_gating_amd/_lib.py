@@ -16,6 +16,7 @@ MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID, MOE_SCORE_SQRTSOFTPLUS = 0, 1, 2
 MOE_DROP_POSITION, MOE_DROP_PROBS = 0, 1
 MOE_NOALLOC_SCRATCH_BYTES = 32 << 20  # include/moe.h
 MOE_GEMM_QUEUE_BYTES = 2048  # include/moe.h
+ABI_VERSION = 8  # moe_abi_version() of the library these signatures describe
 
 
 class RouteDesc(ctypes.Structure):
@@ -102,6 +103,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
             fn = getattr(lib, name)
             fn.restype = res
             fn.argtypes = args
+        if lib.moe_abi_version() != ABI_VERSION:
+            raise RuntimeError(f"{path} has interface version {lib.moe_abi_version()}, these "
+                               f"bindings expect {ABI_VERSION}: rebuild it")
         _lib = lib
     return _lib
 

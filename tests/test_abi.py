@@ -28,7 +28,7 @@ def test_library_exports_every_declared_function():
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(_lib.SIGNATURES) == names
-    assert lib.moe_abi_version() == 8
+    assert lib.moe_abi_version() == 8 == _lib.ABI_VERSION
 
 
 def test_route_desc_layout_matches_c():
