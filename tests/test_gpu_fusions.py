@@ -116,6 +116,43 @@ def test_layer_overlap_graph_capture_replays():
         assert torch.equal(out, ref), f"replay with seed {seed}"
 
 
+@pytest.mark.parametrize("precision", ["bf16", "mxfp8"])
+@pytest.mark.parametrize("fold", [False, True])
+def test_tile_queue_graph_capture_replays(precision, fold):
+    """Experts of ~512 rows, so the grouped GEMMs run their tile-queue
+    launches (with the shared expert's tiles in the same queue when folded):
+    the queue's counters are reset by the launches themselves, never by a
+    memset, so a captured forward replays correctly many times, with eager
+    calls that use the same queue in between; every replay equals a layer
+    without a queue bit for bit, and the counters end at zero."""
+    cfg = datagen.MoEConfig("g-graph-queue", T=2048, h=256, E=8, K=2, f=512, dtype="bf16",
+                            shared_f=256)
+    log(f"tile queue graph ({precision}, fold={fold}): {cfg}")
+    inp = datagen.make_inputs(cfg, seed=12, device=DEV)
+    kw = dict(K=cfg.K, gather=True, precision=precision)
+    layer = MoELayerForward(inp, fold_shared=fold, overlap_shared=False, tile_queue=True, **kw)
+    plain = MoELayerForward(inp, fold_shared=False, overlap_shared=False, tile_queue=False, **kw)
+    assert layer.queue is not None
+    layer.forward()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        out = layer.forward()
+    for seed in (13, 14, 15, 16):
+        new = datagen.make_inputs(cfg, seed=seed, device=DEV, with_experts=False)
+        inp["x"].copy_(new["x"])
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = out.clone()
+        eager = layer.forward().clone()  # the same queue, outside the graph
+        ref = plain.forward()
+        torch.cuda.synchronize()
+        assert torch.equal(got, ref), f"replay with seed {seed}"
+        assert torch.equal(eager, ref), f"eager call after replay, seed {seed}"
+        assert int(torch.count_nonzero(layer.queue).item()) == 0
+
+
 def test_small_layer_with_options_against_the_oracle():
     cfg = CFGS[2]
     inp = datagen.make_inputs(cfg, seed=9, device=DEV)
