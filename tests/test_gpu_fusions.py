@@ -289,6 +289,38 @@ def test_tile_queue_matches_one_tile_per_workgroup(T, E, K, f, h, fs):
         assert int(q.abs().sum().item()) == 0, "the queue is left zeroed"
 
 
+# every expert empty; every row in one expert; one row against the rest;
+# two halves; counts summing past max_rows (the second expert is clamped
+# to the rows left)
+DEGENERATE_COUNTS = [[0] * 8, [4096] + [0] * 7, [1] + [0] * 6 + [4095], [0, 0, 0, 2048, 0, 0, 0, 2048],
+                     [3000, 3000] + [0] * 6]
+
+
+@pytest.mark.parametrize("counts", DEGENERATE_COUNTS)
+def test_tile_queue_degenerate_counts(counts):
+    """Queue launches (max_rows / E = 512) over degenerate counts give the
+    bits of one workgroup per tile on every row the counts cover, on
+    repeated calls, and leave the counters zeroed."""
+    E, h, f, rows = 8, 256, 512, 4096
+    g = torch.Generator(device="cpu").manual_seed(3)
+    x = torch.randn(rows, h, generator=g).to(DEV, torch.bfloat16)
+    wg = (torch.randn(E, f, h, generator=g) * h ** -0.5).to(DEV, torch.bfloat16)
+    wu = (torch.randn(E, f, h, generator=g) * h ** -0.5).to(DEV, torch.bfloat16)
+    wd = (torch.randn(E, h, f, generator=g) * f ** -0.5).to(DEV, torch.bfloat16)
+    tpe = torch.tensor(counts, dtype=torch.int32, device=DEV)
+    N = min(sum(counts), rows)
+    log(f"tile queue, degenerate counts {counts}")
+    q = moe.gemm_queue(DEV)
+    for _ in range(2):
+        a0 = moe.moe_grouped_fc1_swiglu(x, tpe, wg, wu)
+        a1 = moe.moe_grouped_fc1_swiglu(x, tpe, wg, wu, queue=q)
+        y0 = moe.moe_grouped_fc2(a0, tpe, wd)
+        y1 = moe.moe_grouped_fc2(a0, tpe, wd, queue=q)
+        torch.cuda.synchronize()
+        assert torch.equal(a0[:N], a1[:N]) and torch.equal(y0[:N], y1[:N])
+        assert int(torch.count_nonzero(q).item()) == 0
+
+
 def test_layer_with_and_without_tile_queue():
     cfg = datagen.CONFIGS["dsv3"].replace(T=2048)
     inp = datagen.make_inputs(cfg, seed=0, device=DEV)

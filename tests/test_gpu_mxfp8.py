@@ -503,6 +503,33 @@ def test_mxfp8_tile_queue_and_folded_shared_expert_match_plain_launches(fs):
         assert int(torch.count_nonzero(q).item()) == 0
 
 
+@pytest.mark.parametrize("counts", [[0] * 8, [4096] + [0] * 7, [1] + [0] * 6 + [4095],
+                                    [3000, 3000] + [0] * 6])
+def test_mxfp8_tile_queue_degenerate_counts(counts):
+    """MXFP8 queue launches (max_rows / E = 512) over degenerate counts (all
+    empty, one expert, one row against the rest, counts past max_rows) give
+    the bits of one workgroup per tile and leave the counters zeroed."""
+    rng = np.random.default_rng(4)
+    E, h, f, rows = 8, 256, 512, 4096
+    x = torch.from_numpy(rng.standard_normal((rows, h))).to(torch.bfloat16).to(DEV)
+    xc, xs = moe.moe_mxfp8_quantize(x)
+    wg, wu = _weights(rng, E, f, h, h ** -0.5), _weights(rng, E, f, h, h ** -0.5)
+    wd = _weights(rng, E, h, f, f ** -0.5)
+    cnt = torch.tensor(counts, dtype=torch.int32, device=DEV)
+    N = min(sum(counts), rows)
+    log(f"mxfp8 tile queue, degenerate counts {counts}")
+    q = moe.gemm_queue(DEV)
+    for _ in range(2):
+        a0 = moe.moe_grouped_fc1_swiglu_mxfp8(xc, xs, None, cnt, wg, wu, rows)
+        a1 = moe.moe_grouped_fc1_swiglu_mxfp8(xc, xs, None, cnt, wg, wu, rows, queue=q)
+        y0 = moe.moe_grouped_fc2_mxfp8(a0[0], a0[1], cnt, wd)
+        y1 = moe.moe_grouped_fc2_mxfp8(a0[0], a0[1], cnt, wd, queue=q)
+        torch.cuda.synchronize()
+        assert torch.equal(a0[0][:N], a1[0][:N]) and torch.equal(a0[1][:, :N], a1[1][:, :N])
+        assert torch.equal(y0[:N], y1[:N])
+        assert int(torch.count_nonzero(q).item()) == 0
+
+
 @pytest.mark.parametrize("name", ["dsv3", "mixtral", "qwen3"])
 def test_mxfp8_bench_layer_whole_experts(name):
     """The MXFP8 layer at full size in the benchmark's launch configuration
