@@ -34,6 +34,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -86,14 +87,27 @@ def parse():
     return p.parse_args()
 
 
+def _code_only(text: str) -> str:
+    """C++ source without its comments and blank lines, so that a counter
+    summary stays current across comment edits but not across code edits.
+    (The sources hold no string literal with // or /* in it.)"""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+
+
 def source_hash(stage: str, mx: bool = False) -> str:
+    """Hash of the code a stage's kernel is built from: its source file and
+    the shared headers (comments and blank lines dropped), and the build
+    flags."""
     src = MX_SOURCES[stage] if mx and stage in MX_SOURCES else KERNEL_SOURCES[stage]
     path = os.path.join(ROOT, "combine_router_gating_amd", "csrc", src)
     csrc = os.path.join(ROOT, "combine_router_gating_amd", "csrc")
     headers = sorted(os.path.join(csrc, f) for f in os.listdir(csrc) if f.endswith(".h"))
     h = hashlib.sha256()
-    for f in [path] + headers + [os.path.join(ROOT, "combine_router_gating_amd", "build.py")]:
-        h.update(open(f, "rb").read())
+    for f in [path] + headers:
+        h.update(_code_only(open(f, encoding="utf-8").read()).encode())
+    h.update(open(os.path.join(ROOT, "combine_router_gating_amd", "build.py"), "rb").read())
     return h.hexdigest()[:16]
 
 

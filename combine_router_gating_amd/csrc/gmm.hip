@@ -40,9 +40,12 @@
 // Launch variants: a 256-row launch picks the 256-, 128- or 64-row body per
 // tile from its row count; single-expert launches take a grouped (banded)
 // tile order; the shared expert's dense GEMM can ride as the last
-// workgroups of a routed launch (DenseTail); layers of large, alike experts
-// run one persistent workgroup per CU; top-1 layers can take the combine
-// as FC2's epilogue.
+// workgroups of a routed launch (DenseTail); given a tile queue, layers of
+// experts with >= 192 rows on average run one workgroup per CU that takes
+// tiles from per-XCD counters (the shared expert's tiles after the routed
+// ones); without one, layers of large, alike experts run one persistent
+// workgroup per CU with a fixed tile sequence; top-1 layers can take the
+// combine as FC2's epilogue.
 #include <algorithm>
 #include <type_traits>
 
