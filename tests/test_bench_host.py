@@ -74,3 +74,33 @@ def test_folded_stages_carry_the_shared_expert():
     b = bench.stage_work(cfg, n, cfg.T, cfg.shared_f, gather=True, fold=True)
     for i in (0, 1):  # bytes, flops: fc1 + fc2 folded = routed pair + shared stage
         assert b["fc1"][i] + b["fc2"][i] == a["fc1"][i] + a["fc2"][i] + a["shared"][i]
+
+
+def test_source_hash_follows_code_not_comments():
+    a = "int x = 1;  // one\n/* a block\n   comment */\n\nint y = 2;\n"
+    b = "int x = 1;\nint y = 2;"
+    assert bench._code_only(a) == bench._code_only(b)
+    assert bench._code_only("int x = 1;") != bench._code_only("int x = 2;")
+
+
+def test_traffic_is_read_only_while_the_kernel_source_matches(tmp_path, monkeypatch):
+    """A counter summary's traffic is used while the hash of the kernel's
+    code (source file, csrc headers, build script) equals the one it
+    records: a comment edit keeps it, a code edit turns it off."""
+    import shutil
+    pkg = tmp_path / "combine_router_gating_amd"
+    shutil.copytree(os.path.join(ROOT, "combine_router_gating_amd", "csrc"), pkg / "csrc",
+                    ignore=shutil.ignore_patterns("*.so", "*.o"))
+    shutil.copy(os.path.join(ROOT, "combine_router_gating_amd", "build.py"), pkg / "build.py")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    (tmp_path / "profiles").mkdir()
+    (tmp_path / "profiles" / "pmc_fc1_probe.md").write_text(
+        "# probe\n\n- stage: fc1\n- traffic_bytes_per_launch: 12345\n"
+        f"- source_sha256: {bench.source_hash('fc1')}\n")
+    assert bench.read_traffic("fc1", "probe") == 12345.0
+    src = pkg / "csrc" / bench.KERNEL_SOURCES["fc1"]
+    src.write_text(src.read_text() + "\n// a comment added at the end\n")
+    assert bench.read_traffic("fc1", "probe") == 12345.0
+    src.write_text(src.read_text() + "\nstatic int probe_code_edit = 1;\n")
+    assert bench.read_traffic("fc1", "probe") is None
+    assert bench.read_traffic("fc1", "missing") is None
