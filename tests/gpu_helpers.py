@@ -75,3 +75,18 @@ def shared_weights_from(inp):
     if "shared_gate" not in inp:
         return None
     return f64(inp["shared_gate"]), f64(inp["shared_up"]), f64(inp["shared_down"])
+
+
+def untile(scales):
+    """k-tiled MXFP8 scales [G, cols/128, R, 4] (or [cols/128, R, 4]) ->
+    row-major [G, R, cols/32] (or [R, cols/32])."""
+    s = scales.cpu().numpy() if hasattr(scales, "cpu") else np.asarray(scales)
+    s = np.swapaxes(s, -3, -2)
+    return s.reshape(s.shape[:-2] + (-1,))
+
+
+def mx_dequantize_tiled(codes, scales):
+    """MXFP8 codes with k-tiled scales, dequantised by the oracle."""
+    from oracle import mx
+    c = codes.cpu().numpy() if hasattr(codes, "cpu") else np.asarray(codes)
+    return mx.mx_dequantize(c, untile(scales))

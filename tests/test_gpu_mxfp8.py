@@ -16,7 +16,7 @@ import pytest
 import torch
 
 import combine_router_gating_amd as moe
-from gpu_helpers import assert_close, log
+from gpu_helpers import assert_close, log, mx_dequantize_tiled as _dq, untile
 from oracle import mx
 
 pytestmark = pytest.mark.gpu
@@ -48,14 +48,6 @@ def test_quantize_bit_exact(dtype):
     np.testing.assert_array_equal(_np(codes), ref_c)
 
 
-def untile(scales):
-    """k-tiled scales [G, cols/128, R, 4] (or [cols/128, R, 4]) -> row-major
-    [G, R, cols/32] (or [R, cols/32])."""
-    s = _np(scales)
-    s = np.swapaxes(s, -3, -2)
-    return s.reshape(s.shape[:-2] + (-1,))
-
-
 @pytest.mark.parametrize("tile_rows", [1, 8, 96])
 def test_quantize_tiled_layout(tile_rows):
     rng = np.random.default_rng(tile_rows)
@@ -72,11 +64,6 @@ def test_quantize_tiled_layout(tile_rows):
 def _weights(rng, E, n, k, std):
     w = torch.from_numpy(rng.standard_normal((E, n, k)) * std).to(torch.bfloat16).to(DEV)
     return moe.moe_mxfp8_quantize_weight(w)
-
-
-def _dq(codes, scales):
-    """Dequantise codes with k-tiled scales."""
-    return mx.mx_dequantize(_np(codes), untile(scales))
 
 
 CASES = [  # E, h, f, counts

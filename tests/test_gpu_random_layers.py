@@ -9,8 +9,9 @@ logits at the fp32 tolerance, routing map bit-exact given the GPU's logits,
 output at the layer tolerance.  The second option set must give the same
 output bits (the options change where data is read and when kernels run,
 not the arithmetic).  MXFP8 cases (their oracle chain is in
-test_gpu_mxfp8.py) are checked for routing and for equal bits across the
-two option sets.
+test_gpu_mxfp8.py) are checked for routing, equal bits across the two
+option sets, bit-exact x quantisation, and the FC2 + combine chain the
+oracle computes from the GPU's act codes.
 """
 import numpy as np
 import pytest
@@ -19,7 +20,9 @@ import torch
 import datagen
 import oracle
 from combine_router_gating_amd.layer import MoELayerForward
-from gpu_helpers import assert_close, f64, log, logits_floor, shared_weights_from
+from gpu_helpers import (assert_close, f64, log, logits_floor, mx_dequantize_tiled,
+                         shared_weights_from, untile)
+from oracle import mx
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -72,6 +75,32 @@ def _draw(i):
     return cfg, policy, pad, precision, options(), options()
 
 
+def _check_mxfp8_chain(layer, inp, cfg, r, out):
+    """MXFP8 layer: x quantised bit-exactly; FC2, the shared expert's FC2 and
+    the combine recomputed by the oracle from the GPU's act codes (exact
+    inputs) and quantised weights match the output at the bf16 tolerance."""
+    xc, xs = mx.mx_quantize(f64(inp["x"]))
+    np.testing.assert_array_equal(layer.xq[0].cpu().numpy(), xc)
+    np.testing.assert_array_equal(layer.xq[1].cpu().numpy(), xs)
+    pm = oracle.permute(f64(inp["x"]), r["routing_map"], r["probs"], cfg.K)
+    np.testing.assert_array_equal(layer.tokens_per_expert.cpu().numpy(), pm["tokens_per_expert"])
+    N = int(pm["expert_offsets"][-1])
+    act = mx.mx_dequantize(layer.actq[0].cpu().numpy()[:N], untile(layer.actq[1])[:N])
+    wd = mx_dequantize_tiled(*layer.wq["w_down"])
+    off = pm["expert_offsets"]
+    y = np.zeros((N, cfg.h))
+    for e in range(cfg.E):
+        y[off[e]:off[e + 1]] = act[off[e]:off[e + 1]] @ wd[e].T
+    y = oracle.round_bf16(y)
+    shared = None
+    if cfg.shared_f:
+        sact = mx_dequantize_tiled(*layer.shared_actq)
+        swd = mx_dequantize_tiled(*layer.wq["shared_down"])[0]
+        shared = oracle.round_bf16(sact @ swd.T)
+    ref = oracle.combine(y, pm["permuted_probs"], pm["row_id_map"], "bf16", shared)
+    assert_close(f64(out), ref, "bf16", "out (MXFP8 chain)")
+
+
 @pytest.mark.parametrize("i", range(N_CASES))
 def test_random_layer_against_the_oracle(i):
     cfg, policy, pad, precision, opt_a, opt_b = _draw(i)
@@ -99,6 +128,7 @@ def test_random_layer_against_the_oracle(i):
                          expert_bias=eb, capacity_factor=cfg.capacity_factor,
                          min_capacity=cfg.min_capacity, drop_policy=policy, pad_to_capacity=pad)
         np.testing.assert_array_equal(a.routing_map.cpu().numpy(), r["routing_map"])
+        _check_mxfp8_chain(a, inp, cfg, r, out_a)
         return
     ref = oracle.moe_forward(f64(inp["x"]), None, None,
                              (f64(inp["w_gate"]), f64(inp["w_up"]), f64(inp["w_down"])),
