@@ -402,6 +402,250 @@ __device__ __forceinline__ void gmm_tile(const Tile& tile, char* smem,
 }
 
 
+// --------------------------------------------- split-ring body (queue launches)
+// The 256-row body of the tile-queue launches keeps the activation rows and
+// the weight rows in rings of their own: 2 activation slots and 3 weight
+// slots of 64 k (256 rows x 128 bytes each, 160 KB: all of LDS).  The weight
+// rows, which stream from HBM, are issued two stages ahead of their use; the
+// activation rows, which mostly hit L2, one stage ahead.  Waves 0-3 issue
+// every direct load (eight activation and eight weight pieces of 1 KB per
+// stage each) and waves 4-7 only multiply, so each SIMD holds one wave whose
+// MFMAs never wait behind a load issue.  Sources are 32-bit byte offsets from
+// a per-wave base in SGPRs (dma16s), sixteen of them in the registers that
+// eight 64-bit pointers take.
+constexpr int kSplitSlot = 256 * 128;
+constexpr int kSplitLds = 5 * kSplitSlot;
+
+template <int MI, int NB, int NI, int BN, int WTM, int WTN>
+__device__ __forceinline__ void load_frags_split(bf16x8 (&a)[MI], bf16x8 (&b)[NB][NI],
+                                                 const char* ast, const char* bst, int kk, int wm,
+                                                 int wn, int l32, int hi) {
+  const int c = kk * 2 + hi;
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi) {
+    const int row = wm * WTM + mi * 32 + l32;
+    a[mi] = *reinterpret_cast<const bf16x8*>(ast + lds_chunk_byte<64>(row, c));
+  }
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) {
+      const int row = nb * BN + wn * WTN + ni * 32 + l32;
+      b[nb][ni] = *reinterpret_cast<const bf16x8*>(bst + lds_chunk_byte<64>(row, c));
+    }
+}
+
+// One 256-row tile (BN columns of W_gate and of W_up for FC1, BN = 128; of
+// W_down for FC2, BN = 256).  Byte offsets of the activation rows must fit 31
+// bits (a_rows * K * 2 <= 2^31), and so must those of one expert's weight
+// rows (N * K * 2), and N must be a multiple of BN; the launcher checks all
+// three.
+//
+// Schedule, per stage kt (64 k, four 16-wide steps): the first step's
+// MFMAs carry the loaders' weight pieces of stage kt+2 (into the weight slot
+// stage kt-1 released); before the last step each wave holds its fragments,
+// the loaders wait until stage kt+1 has landed (the weight pieces of stage
+// kt+2 may stay in flight), the workgroup passes one barrier, and the last
+// step's MFMAs carry the activation pieces of stage kt+2 (into the slot
+// stage kt released).  Loads of one loader complete in issue order, so the
+// waits are counts of the pieces issued after the ones needed.
+template <int BN, int WM, int WN, bool FC1>
+__device__ __forceinline__ void gmm_tile_split(const Tile& tile, char* smem,
+                                               const uint16_t* __restrict__ A,
+                                               const int32_t* __restrict__ gather, int64_t a_rows,
+                                               const uint16_t* __restrict__ B0,
+                                               const uint16_t* __restrict__ B1,
+                                               uint16_t* __restrict__ C, int N, int K) {
+  constexpr int BM = 256, SBK = 64, KK = SBK / 16;
+  constexpr int NB = FC1 ? 2 : 1;
+  static_assert(NB * BN == 256, "256 weight rows per stage");
+  static_assert(WM * WN == 8, "8 waves");
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int MI = WTM / 32, NI = WTN / 32;
+  static_assert(NB * MI * NI == 8, "8 MFMAs per 16-wide step: two pieces at every other one");
+  const int n0 = tile.n0 * BN;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const uint32_t smem_base = static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)smem));
+  const int nk = K / SBK;
+
+  // Loader w (waves 0-3) fills pieces 8w .. 8w+7 of each block: rows 64w ..
+  // 64w+63 of the activation rows and of the weight rows (FC1: w < 2 reads
+  // W_gate, w >= 2 W_up).  Rows past the tile's rows (or past N) are clamped
+  // in range: they are computed but never stored.
+  const bool loader = wave < 4;
+  const int w = loader ? wave : 0;
+  const char* abase = uniform_ptr(A);
+  const char* bbase =
+      uniform_ptr((FC1 && w >= 2 ? B1 : B0) + static_cast<int64_t>(tile.e) * N * K);
+  // Weight piece j holds rows 8 (8w + j) + lane / 8, i.e. weight rows
+  // n0 + 64 (w % 2) + 8 j + lane / 8 (FC1) or n0 + 64 w + 8 j + lane / 8
+  // (FC2), all below N (N is a multiple of BN): a lane's pieces step by 8
+  // rows (folded into the base) and their 16-byte chunk depends on j's
+  // parity only (lds_piece's swizzle), so two offsets serve all eight.
+  uint32_t aoff[8], boff[2];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    int row, c;
+    lds_piece<SBK>((8 * w + j) * 1024 + lane * 16, row, c);
+    int64_t ar = tile.row0 + min(row, tile.nrows - 1);
+    if (gather) ar = min(max(static_cast<int64_t>(gather[ar]), int64_t(0)), a_rows - 1);
+    aoff[j] = static_cast<uint32_t>(ar * K * 2 + c * 16);
+    if (j < 2) {
+      const int n = n0 + row % BN;
+      boff[j] = static_cast<uint32_t>(static_cast<int64_t>(n) * K * 2 + c * 16);
+    }
+  }
+  auto slot_a = [&](int s) { return (s & 1) * kSplitSlot; };
+  auto slot_b = [&](int s) { return (2 + s % 3) * kSplitSlot; };
+  auto piece_a = [&](int s, int j) {
+    dma16s(aoff[j], abase + s * (SBK * 2), smem_base + slot_a(s) + (8 * w + j) * 1024);
+  };
+  auto piece_b = [&](int s, int j) {
+    dma16s(boff[j & 1], bbase + s * (SBK * 2) + static_cast<int64_t>(j & ~1) * 8 * K * 2,
+           smem_base + slot_b(s) + (8 * w + j) * 1024);
+  };
+
+  f32x16 acc[NB][MI][NI];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) acc[b][mi][ni][q] = 0.f;
+  bf16x8 ca[MI], cb[NB][NI], na[MI], nb[NB][NI];
+
+  // prologue: activation and weight pieces of stages 0 and 1, weights of
+  // stage 2 (those that exist), in that order; then stage 0 must be in
+  if (loader) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) piece_a(0, j);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) piece_b(0, j);
+    if (nk > 1) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) piece_a(1, j);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) piece_b(1, j);
+    }
+    if (nk > 2) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) piece_b(2, j);
+      wait_vmcnt<24>();
+    } else if (nk > 1) {
+      wait_vmcnt<16>();
+    } else {
+      wait_vmcnt<0>();
+    }
+  }
+  block_barrier();
+  load_frags_split<MI, NB, NI, BN, WTM, WTN>(ca, cb, smem, smem + slot_b(0), 0, wm, wn, l32, hi);
+
+  // one step's MFMAs; with IA (IB) the loader's eight activation (weight)
+  // pieces of stage s go out two at every other MFMA
+  auto mfmas = [&](auto ia_c, auto ib_c, int s) {
+    constexpr bool IA = decltype(ia_c)::value, IB = decltype(ib_c)::value;
+#pragma unroll
+    for (int q = 0; q < NB; ++q)
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) {
+          acc[q][mi][ni] =
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(cb[q][ni], ca[mi], acc[q][mi][ni], 0, 0, 0);
+          if constexpr (IA || IB) {
+            const int pos = (q * MI + mi) * NI + ni;
+            if (pos % 2 == 0) {
+              if constexpr (IA) {
+                piece_a(s, pos);
+                piece_a(s, pos + 1);
+              } else {
+                piece_b(s, pos);
+                piece_b(s, pos + 1);
+              }
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          }
+        }
+  };
+  auto advance = [&]() {
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) ca[mi] = na[mi];
+#pragma unroll
+    for (int q = 0; q < NB; ++q)
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) cb[q][ni] = nb[q][ni];
+  };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  // Stage kt.  LD: this wave is a loader; IB0: its first step issues the
+  // weight pieces of stage kt+2; IA3: its last step the activation pieces of
+  // stage kt+2; W8: the wait before the barrier leaves those weight pieces
+  // in flight; LAST: the final stage (no barrier).
+  auto iter = [&](auto ld_c, auto ib0_c, auto ia3_c, auto w8_c, auto last_c, int kt) {
+    constexpr bool LD = decltype(ld_c)::value;
+    constexpr bool IB0 = LD && decltype(ib0_c)::value, IA3 = LD && decltype(ia3_c)::value;
+    constexpr bool W8 = decltype(w8_c)::value, LAST = decltype(last_c)::value;
+    const char* ast = smem + slot_a(kt);
+    const char* bst = smem + slot_b(kt);
+#pragma unroll
+    for (int kk = 0; kk + 1 < KK; ++kk) {
+      __builtin_amdgcn_sched_barrier(0);
+      load_frags_split<MI, NB, NI, BN, WTM, WTN>(na, nb, ast, bst, kk + 1, wm, wn, l32, hi);
+      if (kk == 0) mfmas(F_{}, std::integral_constant<bool, IB0>{}, kt + 2);
+      else mfmas(F_{}, F_{}, 0);
+      advance();
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (!LAST) {
+      if constexpr (LD) {
+        if constexpr (W8) wait_vmcnt<8>();
+        else wait_vmcnt<0>();
+      }
+      wait_lgkm0();
+      block_barrier();
+      load_frags_split<MI, NB, NI, BN, WTM, WTN>(na, nb, smem + slot_a(kt + 1),
+                                                 smem + slot_b(kt + 1), 0, wm, wn, l32, hi);
+      mfmas(std::integral_constant<bool, IA3>{}, F_{}, kt + 2);
+      advance();
+    } else {
+      mfmas(F_{}, F_{}, 0);
+    }
+  };
+  auto run = [&](auto ld) {
+    if (nk == 1) {
+      iter(ld, F_{}, F_{}, F_{}, T_{}, 0);
+      return;
+    }
+    if (nk >= 3) iter(ld, F_{}, T_{}, T_{}, F_{}, 0);  // stage 2's weights came with the prologue
+    else iter(ld, F_{}, F_{}, F_{}, F_{}, 0);
+    int kt = 1;
+    for (; kt + 2 < nk; ++kt) iter(ld, T_{}, T_{}, T_{}, F_{}, kt);
+    if (kt == nk - 2) {
+      iter(ld, F_{}, F_{}, F_{}, F_{}, kt);
+      ++kt;
+    }
+    iter(ld, F_{}, F_{}, F_{}, T_{}, kt);
+  };
+  if (loader) run(T_{});
+  else run(F_{});
+  // the accumulators are complete here: keep the last MFMAs out of the
+  // epilogue's conditional blocks
+#pragma unroll
+  for (int q = 0; q < NB; ++q)
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) asm volatile("" : "+v"(acc[q][mi][ni]));
+  store_tile<MI, NB, NI, WTM, WTN, FC1>(acc, C, tile.row0, tile.nrows, n0, N, wm, wn, l32, hi);
+}
+
 // The grouped-GEMM kernel: decode this workgroup's tile with BMAX-row
 // m-tiles, then run a tile body.  With 256-row m-tiles an expert's last,
 // ragged tile runs the 128- or 64-row body when it fits (less MFMA work
@@ -579,6 +823,97 @@ __global__ void __launch_bounds__(NW * 64) gmm_bf16_kernel(
   } else {
     Body64::template run<CMB>(tile, smem, a, g, ar, b0, b1, c, n, k, epi);
   }
+}
+
+// Tile-queue launch with the split-ring 256-row body (gmm_tile_split): one
+// workgroup per CU takes tiles from the queue as queue_tiles does.  The
+// stages take all of LDS, so no decoded tables are kept: for each tile the
+// first wave decodes the counts again (WaveCounts, E <= kPersistMaxExperts)
+// and hands the tile to the others through the first bytes of LDS.  Ragged
+// tiles of <= 128 rows run the 128- and 64-row bodies of the plain queue
+// launch; the shared expert's tiles (DenseTail) follow the routed ones.
+template <bool FC1, int BN, int WM, int WN, class Body128, class Body64, bool TAIL>
+__global__ void __launch_bounds__(512) gmm_bf16_qsplit_kernel(
+    const uint16_t* __restrict__ A, const int32_t* __restrict__ gather, int64_t a_rows,
+    const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1, uint16_t* __restrict__ C,
+    const int32_t* __restrict__ counts, int E, int N, int K, int64_t max_rows, DenseTail dn,
+    int* __restrict__ queue) {
+  static_assert(Body128::lds <= kSplitLds && Body64::lds <= kSplitLds, "bodies fit the stages");
+  __shared__ __attribute__((aligned(1024))) char smem[kSplitLds];
+  int* hdr = reinterpret_cast<int*>(smem);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int NT = (N + BN - 1) / BN;
+  const int ntd = TAIL ? (dn.N + BN - 1) / BN : 0;
+  const int64_t dense = TAIL ? (dn.rows + 255) / 256 * ntd : 0;
+  const int x = static_cast<int>(blockIdx.x % 8);
+  int v = 0;  // XCDs drained so far (first wave)
+  for (;;) {
+    if (wave == 0) {
+      WaveCounts wc;
+      wc.load<256>(counts, E, max_rows);
+      const int64_t routed = static_cast<int64_t>(wc.mtiles) * NT;
+      const int64_t total = routed + dense;
+      int64_t L = -1;
+      while (v < 8) {  // its XCD's next tile, then the other XCDs' remaining ones
+        const int xv = (x + v) % 8;
+        int kq = 0;
+        if (lane == 0) kq = atomicAdd(queue + xv * kQStride, 1);
+        kq = __shfl(kq, 0, 64);
+        const int64_t Lc =
+            (static_cast<int64_t>(kq / kQGroup) * 8 + xv) * kQGroup + kq % kQGroup;
+        if (kq >= 0 && Lc < total) {
+          L = Lc;
+          break;
+        }
+        ++v;
+      }
+      Tile t{0, 0, 0, 0};
+      int src = -1;  // -1: none left; 0: routed; 1: dense tail
+      if (L >= 0) {
+        if (TAIL && L >= routed) {
+          t = dense_tile_at<256, kDenseBand>(L - routed, ntd, dn.rows, 0);
+          src = 1;
+        } else {
+          t = wc.tile<256>(L, NT, E);
+          src = 0;
+        }
+      }
+      if (lane == 0) {
+        hdr[0] = src;
+        hdr[1] = t.e;
+        hdr[2] = static_cast<int>(static_cast<uint32_t>(t.row0));
+        hdr[3] = static_cast<int>(static_cast<uint64_t>(t.row0) >> 32);
+        hdr[4] = t.nrows;
+        hdr[5] = t.n0;
+      }
+    }
+    __syncthreads();
+    const int src = __builtin_amdgcn_readfirstlane(hdr[0]);
+    Tile t;
+    t.e = __builtin_amdgcn_readfirstlane(hdr[1]);
+    t.row0 = static_cast<int64_t>(
+        (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(hdr[3]))) << 32) |
+        static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(hdr[2])));
+    t.nrows = __builtin_amdgcn_readfirstlane(hdr[4]);
+    t.n0 = __builtin_amdgcn_readfirstlane(hdr[5]);
+    __syncthreads();  // the header's bytes belong to the tile's first stage
+    if (src < 0) break;
+    const bool dn_tile = TAIL && src == 1;
+    const uint16_t* ta = dn_tile ? dn.A : A;
+    const int32_t* tg = dn_tile ? nullptr : gather;
+    const int64_t tar = dn_tile ? dn.rows : a_rows;
+    const uint16_t* tb0 = dn_tile ? dn.B0 : B0;
+    const uint16_t* tb1 = dn_tile ? dn.B1 : B1;
+    uint16_t* tc = dn_tile ? dn.C : C;
+    const int tn = dn_tile ? dn.N : N, tk = dn_tile ? dn.K : K;
+    const CombineEpi no_epi{nullptr, nullptr, nullptr, 0, nullptr};
+    if (t.nrows > 128) gmm_tile_split<BN, WM, WN, FC1>(t, smem, ta, tg, tar, tb0, tb1, tc, tn, tk);
+    else if (t.nrows > 64) Body128::template run<false>(t, smem, ta, tg, tar, tb0, tb1, tc, tn, tk, no_epi);
+    else Body64::template run<false>(t, smem, ta, tg, tar, tb0, tb1, tc, tn, tk, no_epi);
+    __syncthreads();  // every wave is past the tile before its stages are refilled
+  }
+  queue_leave(queue);
 }
 
 template <int BM, int BN, int WM, int WN, bool FC1, int STAGES, int SBK, int SCHED = kSchedCompute,
@@ -762,6 +1097,35 @@ void launch_bf16(const AOperand& a, const void* B0, const void* B1, void* C, con
   args(gmm_bf16_kernel<FC1, BMAX, BN, NW, B256, B128, B64, false>);
 }
 
+// The split-ring queue launch (gmm_bf16_qsplit_kernel) takes 32-bit source
+// offsets: every activation row and every expert's weight rows must lie
+// within 2^31 bytes of their base; and its n-tiles must be whole (N a
+// multiple of the tile width BN).
+bool split_fits(const AOperand& a, int64_t N, int64_t K, int BN, const SharedArgs& sh) {
+  const int64_t lim = int64_t(1) << 31;
+  if (a.rows * K * 2 > lim || N * K * 2 > lim || N % BN != 0) return false;
+  return sh.rows == 0 || (sh.rows * sh.K * 2 <= lim && sh.N * sh.K * 2 <= lim && sh.N % BN == 0);
+}
+
+template <bool FC1, int BN, int WM, int WN, class B128, class B64>
+void launch_qsplit(const AOperand& a, const void* B0, const void* B1, void* C,
+                   const int32_t* counts, int64_t E, int64_t N, int64_t K, int64_t max_rows,
+                   hipStream_t s, const SharedArgs& sh, int* queue) {
+  const int64_t g = grid_for(max_rows, E, 256, N, BN);
+  DenseTail dn{static_cast<const uint16_t*>(sh.A), static_cast<const uint16_t*>(sh.B0),
+               static_cast<const uint16_t*>(sh.B1), static_cast<uint16_t*>(sh.C), sh.rows,
+               static_cast<int>(sh.N), static_cast<int>(sh.K), 0};
+  if (sh.rows > 0) dn.wgs = static_cast<int>(grid_for(sh.rows, 1, 256, sh.N, BN));
+  if (g + dn.wgs == 0) return;
+  const auto k = dn.wgs > 0 ? gmm_bf16_qsplit_kernel<FC1, BN, WM, WN, B128, B64, true>
+                            : gmm_bf16_qsplit_kernel<FC1, BN, WM, WN, B128, B64, false>;
+  hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(persistent_grid(g + dn.wgs))), dim3(512), 0, s,
+                     static_cast<const uint16_t*>(a.base), a.gather, a.rows,
+                     static_cast<const uint16_t*>(B0), static_cast<const uint16_t*>(B1),
+                     static_cast<uint16_t*>(C), counts, static_cast<int>(E), static_cast<int>(N),
+                     static_cast<int>(K), max_rows, dn, queue);
+}
+
 template <bool FC1>
 void launch_f32(const AOperand& a, const void* B0, const void* B1, void* C, const int32_t* counts,
                 int64_t E, int64_t N, int64_t K, int64_t max_rows, hipStream_t s) {
@@ -846,6 +1210,13 @@ void launch_gemm(int32_t dtype, const AOperand& A, const void* B0, const void* B
   const int bm = pick_bm(max_rows, E);
   int* q = static_cast<int*>(queue);
   if (q && use_queue(max_rows, E) && !cmb.epi.out) {  // tile-queue launch (bm == 256 here)
+    if (split_fits(A, N, K, FC1 ? 128 : 256, sh)) {
+      if constexpr (FC1)
+        launch_qsplit<true, 128, 2, 4, Fc1B128, Fc1B64p>(A, B0, B1, C, counts, E, N, K, max_rows, s, sh, q);
+      else
+        launch_qsplit<false, 256, 4, 2, Fc2B128, Fc2B64p>(A, B0, B1, C, counts, E, N, K, max_rows, s, sh, q);
+      return;
+    }
     if constexpr (FC1)
       launch_bf16<true, 256, 128, 8, Fc1B256, Fc1B128, Fc1B64p, false, true>(A, B0, B1, C, counts, E, N, K, max_rows, s, cmb, sh, q);
     else

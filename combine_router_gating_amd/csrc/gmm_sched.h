@@ -75,8 +75,13 @@ __device__ int64_t decode_counts(const int32_t* __restrict__ counts, int E, int6
   return s_toff[E];
 }
 
-// Logical tile L (expert -> n-tile -> m-tile order, so the m-tiles sharing a
-// weight slab are adjacent) of the decoded counts; NT n-tiles per expert.
+// Logical tile L of the decoded counts; NT n-tiles per expert.  Order:
+// expert -> n-tile -> m-tile, the m-tiles walked forward on even n-tiles and
+// backward on odd ones, so that each tile shares an operand slab with the one
+// before it (the weight slab within an n-tile, the activation rows across an
+// n-tile change): a workgroup that takes the next tile from the queue starts
+// a few microseconds after its predecessor, while the shared lines are still
+// in L2.
 template <int BM>
 __device__ Tile tile_at(int64_t L, int NT, int E, const int* s_toff, const int* s_roff,
                         const int* s_n) {
@@ -90,7 +95,8 @@ __device__ Tile tile_at(int64_t L, int NT, int E, const int* s_toff, const int* 
   const int mt = s_toff[e + 1] - s_toff[e];
   const int64_t r = L - static_cast<int64_t>(s_toff[e]) * NT;
   const int nt = static_cast<int>(r / mt);
-  const int mtile = static_cast<int>(r % mt);
+  const int mi = static_cast<int>(r % mt);
+  const int mtile = (nt & 1) ? mt - 1 - mi : mi;
   Tile tile;
   tile.e = e;
   tile.row0 = s_roff[e] + static_cast<int64_t>(mtile) * BM;
@@ -98,6 +104,85 @@ __device__ Tile tile_at(int64_t L, int NT, int E, const int* s_toff, const int* 
   tile.n0 = nt;
   return tile;
 }
+
+// The same decode by one wave with no LDS tables (for launches whose stages
+// take all of LDS): lane l holds experts l, l + 64, l + 128 and l + 192
+// (E <= kPersistMaxExperts), their clamped row counts scanned into row and
+// m-tile offsets as decode_counts does.  WaveCounts::load runs on every lane
+// of the wave; the results are wave-uniform.
+struct WaveCounts {
+  int n[4], roff[4], toff[4];
+  int mtiles;  // all m-tiles (uniform)
+
+  template <int BM>
+  __device__ __forceinline__ void load(const int32_t* __restrict__ counts, int E, int64_t max_rows) {
+    const int lane = threadIdx.x & 63;
+    int cv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = j * 64 + lane;
+      const int v = e < E ? counts[e] : 0;
+      cv[j] = v < 0 ? 0 : (v > max_rows ? static_cast<int>(max_rows) : v);
+    }
+    int64_t run = 0;
+    int trun = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      int64_t incl = cv[j];
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int64_t o = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += o;
+      }
+      const int64_t pre = run + incl - cv[j];
+      run += __shfl(incl, 63, 64);
+      const int64_t start = pre < max_rows ? pre : max_rows;
+      const int64_t end = pre + cv[j] < max_rows ? pre + cv[j] : max_rows;
+      n[j] = static_cast<int>(end - start);
+      roff[j] = static_cast<int>(start);
+      const int tl = (n[j] + BM - 1) / BM;
+      int tincl = tl;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_up(tincl, off, 64);
+        if (lane >= off) tincl += o;
+      }
+      toff[j] = trun + tincl - tl;
+      trun += __shfl(tincl, 63, 64);
+    }
+    mtiles = __builtin_amdgcn_readfirstlane(trun);
+  }
+
+  // Logical tile L < mtiles * NT, in tile_at's order.
+  template <int BM>
+  __device__ __forceinline__ Tile tile(int64_t L, int NT, int E) const {
+    const int lane = threadIdx.x & 63;
+    // e = (experts e' < E with toff[e'] * NT <= L) - 1: toff never decreases,
+    // so this is the largest such e', which has tiles
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      cnt += __popcll(__ballot(j * 64 + lane < E && static_cast<int64_t>(toff[j]) * NT <= L));
+    const int e = cnt - 1;
+    const int j = e >> 6, l = e & 63;
+    const auto pick = [&](const int (&v)[4]) {
+      const int x = j == 0 ? v[0] : (j == 1 ? v[1] : (j == 2 ? v[2] : v[3]));
+      return __builtin_amdgcn_readlane(x, l);
+    };
+    const int te = pick(toff), re = pick(roff), ne = pick(n);
+    const int mt = (ne + BM - 1) / BM;
+    const int64_t r = L - static_cast<int64_t>(te) * NT;
+    const int nt = static_cast<int>(r / mt);
+    const int mi = static_cast<int>(r % mt);
+    const int mtile = (nt & 1) ? mt - 1 - mi : mi;
+    Tile t;
+    t.e = e;
+    t.row0 = re + static_cast<int64_t>(mtile) * BM;
+    t.nrows = min(BM, ne - mtile * BM);
+    t.n0 = nt;
+    return t;
+  }
+};
 
 // Logical tiles are spread so that each XCD (workgroup id mod 8) runs a
 // contiguous range of them (the weight slabs its CUs share stay in its L2):

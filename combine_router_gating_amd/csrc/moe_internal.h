@@ -164,6 +164,24 @@ __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
                : "memory");
 }
 
+// dma16 with the source as a 32-bit byte offset (per lane) from a 64-bit base
+// held in SGPRs (the saddr form), so that a lane's source takes one VGPR.
+__device__ __forceinline__ void dma16s(uint32_t voff, const void* sbase, uint32_t lds_base) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "{m0}"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "memory");
+}
+
+// A pointer the compiler can keep in SGPRs (its value taken from the first
+// active lane; callers pass wave-uniform pointers).
+__device__ __forceinline__ const char* uniform_ptr(const void* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<const char*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
 // Direct 4-byte global -> LDS load: lane i writes LDS bytes [base + 4 i, +4).
 __device__ __forceinline__ void dma4(const void* gptr, uint32_t lds_base) {
   asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off"

@@ -253,11 +253,21 @@ def test_shared_expert_folded_into_the_routed_launches(T, E, K, f, fs, h):
 @pytest.mark.parametrize("T,E,K,f,h,fs", [(2048, 64, 5, 512, 256, 0),      # 160 rows: no queue
                                           (2048, 64, 8, 256, 512, 256),    # + shared tail
                                           (4096, 8, 2, 256, 128, 0),       # large experts
-                                          (600, 64, 1, 256, 128, 0)])      # 64-row launch: no queue
+                                          (600, 64, 1, 256, 128, 0),       # 64-row launch: no queue
+                                          # k-loops of 1, 3 and 6 stages of 64 in the split-ring
+                                          # body (FC1 k = h, FC2 k = f); the other GEMM of each
+                                          # layer has N off the tile width and takes the plain
+                                          # queue body
+                                          (4096, 8, 2, 256, 64, 0),
+                                          (4096, 8, 2, 256, 192, 0),
+                                          (4096, 8, 2, 192, 256, 0),
+                                          (4096, 8, 2, 64, 256, 0),
+                                          (4096, 8, 2, 128, 384, 0)])
 def test_tile_queue_matches_one_tile_per_workgroup(T, E, K, f, h, fs):
     """The tile-queue launches (one workgroup per CU taking tiles from per-XCD
-    counters) give the same bits as one workgroup per tile, on repeated calls
-    with one queue, and leave the queue zeroed."""
+    counters; the 256-row tiles on the split-ring body when N is a multiple
+    of the tile width) give the same bits as one workgroup per tile, on
+    repeated calls with one queue, and leave the queue zeroed."""
     cfg = datagen.MoEConfig("queue", T=T, h=h, E=E, K=K, f=f, dtype="bf16", score="sigmoid",
                             expert_bias=True, shared_f=fs)
     log(f"tile queue: {cfg}")
