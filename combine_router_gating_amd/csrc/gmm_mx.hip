@@ -71,6 +71,75 @@ constexpr int mx_lds_bytes() {
   return STAGES * ((BM + (FC1 ? 2 : 1) * BN) * kMxK + NW * 64 * 4);
 }
 
+// Epilogue of an MXFP8 tile: lane holds C[m = l32][n = 8g + 4*hi + q] of
+// each 32x32 block.  FC1: act = silu(gate) * up quantised to MXFP8 along f;
+// FC2: bf16 expert_out, or with CMB the top-1 combine into out.
+template <int MI, int NB, int NI, int WTM, int WTN, bool FC1, bool CMB>
+__device__ __forceinline__ void mx_store(const f32x16 (&acc)[NB][MI][NI], const Tile& tile,
+                                         const MxOut& O, int N, int n0, int wm, int wn, int l32,
+                                         int hi) {
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi) {
+    const int ml = wm * WTM + mi * 32 + l32;
+    const bool row_ok = ml < tile.nrows;
+    const int64_t grow = tile.row0 + ml;
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) {
+      const int nc = n0 + wn * WTN + ni * 32;  // first column of this 32-column block
+      if constexpr (FC1) {
+        float v[16];
+        float amax = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float g = acc[0][mi][ni][i], u = acc[1][mi][ni][i];
+          v[i] = g / (1.0f + __expf(-g)) * u;
+          amax = fmaxf(amax, fabsf(v[i]));
+        }
+        amax = fmaxf(amax, __shfl_xor(amax, 32, 64));  // the row's other 16 columns
+        const int e = mx_scale_exp(amax);
+        const float inv = __uint_as_float(static_cast<uint32_t>(127 - e) << 23);
+        if (row_ok && nc < N) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            uint32_t word = 0;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) word |= e4m3_code(v[4 * g + q] * inv) << (8 * q);
+            *reinterpret_cast<uint32_t*>(O.codes + grow * N + nc + 8 * g + 4 * hi) = word;
+          }
+          if (hi == 0)
+            O.scales[((nc / kMxK) * O.rows + grow) * 4 + ((nc / 32) & 3)] = static_cast<uint8_t>(e + 127);
+        }
+      } else if constexpr (CMB) {
+        int64_t t;
+        if (!row_ok || nc >= N || !O.cmb.owns(grow, &t)) continue;
+        const float p = O.cmb.prob[grow];
+        uint16_t* crow = O.cmb.out + t * N;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          uint2 pk;
+          pk.x = static_cast<uint32_t>(combine_bf16(p, acc[0][mi][ni][4 * g])) |
+                 (static_cast<uint32_t>(combine_bf16(p, acc[0][mi][ni][4 * g + 1])) << 16);
+          pk.y = static_cast<uint32_t>(combine_bf16(p, acc[0][mi][ni][4 * g + 2])) |
+                 (static_cast<uint32_t>(combine_bf16(p, acc[0][mi][ni][4 * g + 3])) << 16);
+          *reinterpret_cast<uint2*>(crow + nc + 8 * g + 4 * hi) = pk;
+        }
+      } else {
+        if (!row_ok || nc >= N) continue;
+        uint16_t* crow = O.bf16 + grow * N;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          uint2 pk;
+          pk.x = static_cast<uint32_t>(f32_to_bf16_bits(acc[0][mi][ni][4 * g])) |
+                 (static_cast<uint32_t>(f32_to_bf16_bits(acc[0][mi][ni][4 * g + 1])) << 16);
+          pk.y = static_cast<uint32_t>(f32_to_bf16_bits(acc[0][mi][ni][4 * g + 2])) |
+                 (static_cast<uint32_t>(f32_to_bf16_bits(acc[0][mi][ni][4 * g + 3])) << 16);
+          *reinterpret_cast<uint2*>(crow + nc + 8 * g + 4 * hi) = pk;
+        }
+      }
+    }
+  }
+}
+
 // One output tile (BM rows of one expert x BN columns).
 template <int BM, int BN, int WM, int WN, bool FC1, int STAGES, int SPREAD, bool CMB>
 __device__ __forceinline__ void mx_tile(const Tile& tile, char* smem, const MxA& A, const MxB& B,
@@ -269,72 +338,269 @@ __device__ __forceinline__ void mx_tile(const Tile& tile, char* smem, const MxA&
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni) asm volatile("" : "+v"(acc[q][mi][ni]));
 
-  // epilogue: lane holds C[m = l32][n = 8g + 4*hi + q] of each 32x32 block
+  mx_store<MI, NB, NI, WTM, WTN, FC1, CMB>(acc, tile, O, N, n0, wm, wn, l32, hi);
+}
+
+// Split-ring body of the queue launches (as the bf16 GEMM's gmm_tile_split):
+// 128-row tiles with the activation rows in 2 LDS slots and the weight rows
+// (256: BN of W_gate and of W_up, or BN = 256 of W_down) in 3, each slot
+// holding its rows' 128 code bytes per stage and a padded block of scale
+// dwords (one per lane of each loader's 4-byte load); the weight stream is
+// issued two stages ahead, the activation rows one.  Waves 0-3 issue every
+// direct load (per stage and loader: 4 activation pieces and one activation
+// scale load, then 8 weight pieces and one weight scale load), waves 4-7 only
+// multiply.  Sources are 32-bit offsets from SGPR bases (a loader's weight
+// pieces step by 8 rows, so two offsets serve them).  Per stage kt: the
+// first 64-wide step's MFMAs carry the weight group of stage kt+2; before the
+// second step the loaders wait for stage kt+1 (that weight group may stay in
+// flight), the workgroup passes one barrier, and the second step's MFMAs
+// carry the activation group of stage kt+2.  Every scaled MFMA keeps its
+// fence (mx_mfma).  The launcher checks that the offsets fit (a_rows * K and
+// N * K below 2^31) and that N is a multiple of BN.
+constexpr int kMxASlot = 128 * kMxK + 256 * 4;  // codes + 4 loaders x 64 scale dwords
+constexpr int kMxBSlot = 256 * kMxK + 256 * 4;
+constexpr int kMxSplitLds = 2 * kMxASlot + 3 * kMxBSlot;
+
+template <int BN, int WM, int WN, bool FC1>
+__device__ __forceinline__ void mx_tile_split(const Tile& tile, char* smem, const MxA& A,
+                                              const MxB& B, const MxOut& O, int N, int K) {
+  constexpr int BM = 128;
+  constexpr int NB = FC1 ? 2 : 1;
+  static_assert(NB * BN == 256, "256 weight rows per stage");
+  static_assert(WM * WN == 8, "8 waves");
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int MI = WTM / 32, NI = WTN / 32;
+  constexpr int MPK = NB * MI * NI;  // MFMAs per 64-wide step
+  static_assert(MPK == 4, "four MFMAs per step: the groups below are spread over them");
+  constexpr int AG = 5, BG = 9;  // loads of a loader's activation / weight group
+  const int n0 = tile.n0 * BN;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const uint32_t smem_base = static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)smem));
+  const int nk = K / kMxK;
+  const int64_t KB = K / 32;
+
+  const bool loader = wave < 4;
+  const int w = loader ? wave : 0;
+  auto a_row = [&](int r) {
+    int64_t ar = tile.row0 + min(r, tile.nrows - 1);
+    if (A.gather) ar = min(max(static_cast<int64_t>(A.gather[ar]), int64_t(0)), A.rows - 1);
+    return ar;
+  };
+  // codes: activation pieces 4w .. 4w+3 (rows 32w .. 32w+31), weight pieces
+  // 8w .. 8w+7 (rows 64w .. 64w+63; FC1: w < 2 W_gate, w >= 2 W_up)
+  const bool up = FC1 && w >= 2;
+  const char* a_codes = uniform_ptr(A.codes);
+  const char* b_codes =
+      uniform_ptr((up ? B.codes1 : B.codes0) + static_cast<int64_t>(tile.e) * N * K);
+  uint32_t aoff[4], boff[2];
 #pragma unroll
-  for (int mi = 0; mi < MI; ++mi) {
-    const int ml = wm * WTM + mi * 32 + l32;
-    const bool row_ok = ml < tile.nrows;
-    const int64_t grow = tile.row0 + ml;
+  for (int j = 0; j < 4; ++j) {
+    int row, c;
+    lds_piece<64>((4 * w + j) * 1024 + lane * 16, row, c);
+    aoff[j] = static_cast<uint32_t>(a_row(row) * K + c * 16);
+  }
 #pragma unroll
-    for (int ni = 0; ni < NI; ++ni) {
-      const int nc = n0 + wn * WTN + ni * 32;  // first column of this 32-column block
-      if constexpr (FC1) {
-        float v[16];
-        float amax = 0.f;
+  for (int j = 0; j < 2; ++j) {
+    int row, c;
+    lds_piece<64>((8 * w + j) * 1024 + lane * 16, row, c);
+    boff[j] = static_cast<uint32_t>(static_cast<int64_t>(n0 + row % BN) * K + c * 16);
+  }
+  // scales: a loader's 4-byte load covers 64 rows (activation rows past 127
+  // are the clamped last row, never read)
+  const int64_t ar_s = a_row(min(64 * w + lane, BM - 1));
+  const uint32_t asoff = static_cast<uint32_t>(A.tiled ? ar_s * 4 : ar_s * KB);
+  const int64_t astep = A.tiled ? A.rows * 4 : 4;
+  const char* a_scales = uniform_ptr(A.scales);
+  const uint32_t bsoff = static_cast<uint32_t>((n0 + (64 * w + lane) % BN) * 4);
+  const char* b_scales = uniform_ptr((up ? B.scales1 : B.scales0) +
+                                     static_cast<int64_t>(tile.e) * nk * N * 4);
+  auto slot_a = [&](int s) { return (s & 1) * kMxASlot; };
+  auto slot_b = [&](int s) { return 2 * kMxASlot + (s % 3) * kMxBSlot; };
+  // piece q of a group: activation q < 4 codes, q == 4 scales; weight q < 8
+  // codes, q == 8 scales
+  auto piece_a = [&](int s, int q) {
+    const uint32_t dst = smem_base + slot_a(s);
+    if (q < 4) dma16s(aoff[q], a_codes + static_cast<int64_t>(s) * kMxK, dst + (4 * w + q) * 1024);
+    else dma4s(asoff, a_scales + s * astep, dst + BM * kMxK + w * 256);
+  };
+  auto piece_b = [&](int s, int q) {
+    const uint32_t dst = smem_base + slot_b(s);
+    if (q < 8)
+      dma16s(boff[q & 1], b_codes + static_cast<int64_t>(s) * kMxK + static_cast<int64_t>(q & ~1) * 8 * K,
+             dst + (8 * w + q) * 1024);
+    else
+      dma4s(bsoff, b_scales + static_cast<int64_t>(s) * N * 4, dst + 256 * kMxK + w * 256);
+  };
+
+  f32x16 acc[NB][MI][NI];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float g = acc[0][mi][ni][i], u = acc[1][mi][ni][i];
-          v[i] = g / (1.0f + __expf(-g)) * u;
-          amax = fmaxf(amax, fabsf(v[i]));
-        }
-        amax = fmaxf(amax, __shfl_xor(amax, 32, 64));  // the row's other 16 columns
-        const int e = mx_scale_exp(amax);
-        const float inv = __uint_as_float(static_cast<uint32_t>(127 - e) << 23);
-        if (row_ok && nc < N) {
+  for (int b = 0; b < NB; ++b)
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            uint32_t word = 0;
+    for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) word |= e4m3_code(v[4 * g + q] * inv) << (8 * q);
-            *reinterpret_cast<uint32_t*>(O.codes + grow * N + nc + 8 * g + 4 * hi) = word;
-          }
-          if (hi == 0)
-            O.scales[((nc / kMxK) * O.rows + grow) * 4 + ((nc / 32) & 3)] = static_cast<uint8_t>(e + 127);
-        }
-      } else if constexpr (CMB) {
-        int64_t t;
-        if (!row_ok || nc >= N || !O.cmb.owns(grow, &t)) continue;
-        const float p = O.cmb.prob[grow];
-        uint16_t* crow = O.cmb.out + t * N;
+      for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          uint2 pk;
-          pk.x = static_cast<uint32_t>(combine_bf16(p, acc[0][mi][ni][4 * g])) |
-                 (static_cast<uint32_t>(combine_bf16(p, acc[0][mi][ni][4 * g + 1])) << 16);
-          pk.y = static_cast<uint32_t>(combine_bf16(p, acc[0][mi][ni][4 * g + 2])) |
-                 (static_cast<uint32_t>(combine_bf16(p, acc[0][mi][ni][4 * g + 3])) << 16);
-          *reinterpret_cast<uint2*>(crow + nc + 8 * g + 4 * hi) = pk;
-        }
-      } else {
-        if (!row_ok || nc >= N) continue;
-        uint16_t* crow = O.bf16 + grow * N;
+        for (int q = 0; q < 16; ++q) acc[b][mi][ni][q] = 0.f;
+  i32x8 ca[MI], cb[NB][NI], na[MI], nb[NB][NI];
+  int cas[MI], cbs[NB][NI], nas[MI], nbs[NB][NI];
+  auto frag = [&](i32x8& f, int& sv, const char* st, int scale_at, int s, int row) {
+    const uint32_t* sc = reinterpret_cast<const uint32_t*>(st + scale_at);
+    const i32x4 lo = *reinterpret_cast<const i32x4*>(st + lds_chunk_byte<64>(row, 4 * s + hi));
+    const i32x4 upr = *reinterpret_cast<const i32x4*>(st + lds_chunk_byte<64>(row, 4 * s + 2 + hi));
+    f = __builtin_shufflevector(lo, upr, 0, 1, 2, 3, 4, 5, 6, 7);
+    sv = static_cast<int>(sc[row] >> (8 * (2 * s + hi)));
+  };
+  auto load_step = [&](i32x8 (&af)[MI], int (&as)[MI], i32x8 (&bf)[NB][NI], int (&bs)[NB][NI],
+                       int kt, int s) {
+    const char* ast = smem + slot_a(kt);
+    const char* bst = smem + slot_b(kt);
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          uint2 pk;
-          pk.x = static_cast<uint32_t>(f32_to_bf16_bits(acc[0][mi][ni][4 * g])) |
-                 (static_cast<uint32_t>(f32_to_bf16_bits(acc[0][mi][ni][4 * g + 1])) << 16);
-          pk.y = static_cast<uint32_t>(f32_to_bf16_bits(acc[0][mi][ni][4 * g + 2])) |
-                 (static_cast<uint32_t>(f32_to_bf16_bits(acc[0][mi][ni][4 * g + 3])) << 16);
-          *reinterpret_cast<uint2*>(crow + nc + 8 * g + 4 * hi) = pk;
-        }
-      }
+    for (int mi = 0; mi < MI; ++mi) frag(af[mi], as[mi], ast, BM * kMxK, s, wm * WTM + mi * 32 + l32);
+#pragma unroll
+    for (int q = 0; q < NB; ++q)
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+        frag(bf[q][ni], bs[q][ni], bst, 256 * kMxK, s, q * BN + wn * WTN + ni * 32 + l32);
+  };
+
+  // prologue: groups A0 B0 A1 B1 B2 (those that exist); then stage 0 must be in
+  if (loader) {
+#pragma unroll
+    for (int q = 0; q < AG; ++q) piece_a(0, q);
+#pragma unroll
+    for (int q = 0; q < BG; ++q) piece_b(0, q);
+    if (nk > 1) {
+#pragma unroll
+      for (int q = 0; q < AG; ++q) piece_a(1, q);
+#pragma unroll
+      for (int q = 0; q < BG; ++q) piece_b(1, q);
+    }
+    if (nk > 2) {
+#pragma unroll
+      for (int q = 0; q < BG; ++q) piece_b(2, q);
+      wait_vmcnt<AG + 2 * BG>();
+    } else if (nk > 1) {
+      wait_vmcnt<AG + BG>();
+    } else {
+      wait_vmcnt<0>();
     }
   }
+  block_barrier();
+  load_step(ca, cas, cb, cbs, 0, 0);
+
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  // one step's MFMAs of the current fragments, the next step's fragments read
+  // first (NEXT: stage nkt, step ns); with IA (IB) the loader's activation
+  // (weight) group of stage g goes out between the MFMAs (two or three loads
+  // after each)
+  auto step = [&](auto next_c, auto ia_c, auto ib_c, int nkt, int ns, int g) {
+    constexpr bool NEXT = decltype(next_c)::value;
+    constexpr bool IA = decltype(ia_c)::value, IB = decltype(ib_c)::value;
+    if constexpr (NEXT) load_step(na, nas, nb, nbs, nkt, ns);
+#pragma unroll
+    for (int q = 0; q < NB; ++q)
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) {
+          mx_mfma(acc[q][mi][ni], cb[q][ni], ca[mi], cbs[q][ni], cas[mi]);
+          if constexpr (IA || IB) {
+            constexpr int G = IA ? AG : BG;
+            const int pos = (q * MI + mi) * NI + ni;
+#pragma unroll
+            for (int p = 0; p < G; ++p)
+              if (p * MPK / G == pos) {
+                if constexpr (IA) piece_a(g, p);
+                else piece_b(g, p);
+              }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+    if constexpr (NEXT) {
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) {
+        ca[mi] = na[mi];
+        cas[mi] = nas[mi];
+      }
+#pragma unroll
+      for (int q = 0; q < NB; ++q)
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) {
+          cb[q][ni] = nb[q][ni];
+          cbs[q][ni] = nbs[q][ni];
+        }
+    }
+  };
+  // Stage kt (LD: loader; IB0, IA1: the first / second step carries the
+  // weight / activation group of stage kt+2; W: the wait leaves the weight
+  // group of stage kt+2 in flight; LAST: no barrier).
+  auto iter = [&](auto ld_c, auto ib0_c, auto ia1_c, auto w_c, auto last_c, int kt) {
+    constexpr bool LD = decltype(ld_c)::value;
+    constexpr bool IB0 = LD && decltype(ib0_c)::value, IA1 = LD && decltype(ia1_c)::value;
+    constexpr bool W = decltype(w_c)::value, LAST = decltype(last_c)::value;
+    step(T_{}, F_{}, std::integral_constant<bool, IB0>{}, kt, 1, kt + 2);
+    if constexpr (!LAST) {
+      if constexpr (LD) {
+        if constexpr (W) wait_vmcnt<BG>();
+        else wait_vmcnt<0>();
+      }
+      wait_lgkm0();
+      block_barrier();
+      step(T_{}, std::integral_constant<bool, IA1>{}, F_{}, kt + 1, 0, kt + 2);
+    } else {
+      step(F_{}, F_{}, F_{}, 0, 0, 0);
+    }
+  };
+  auto run = [&](auto ld) {
+    if (nk == 1) {
+      iter(ld, F_{}, F_{}, F_{}, T_{}, 0);
+      return;
+    }
+    if (nk >= 3) iter(ld, F_{}, T_{}, T_{}, F_{}, 0);  // stage 2's weights came with the prologue
+    else iter(ld, F_{}, F_{}, F_{}, F_{}, 0);
+    int kt = 1;
+    for (; kt + 2 < nk; ++kt) iter(ld, T_{}, T_{}, T_{}, F_{}, kt);
+    if (kt == nk - 2) {
+      iter(ld, F_{}, F_{}, F_{}, F_{}, kt);
+      ++kt;
+    }
+    iter(ld, F_{}, F_{}, F_{}, T_{}, kt);
+  };
+  if (loader) run(T_{});
+  else run(F_{});
+  // the accumulators are complete here: keep the last MFMAs (and their
+  // fences) out of the epilogue's conditional stores
+#pragma unroll
+  for (int q = 0; q < NB; ++q)
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) asm volatile("" : "+v"(acc[q][mi][ni]));
+  mx_store<MI, NB, NI, WTM, WTN, FC1, false>(acc, tile, O, N, n0, wm, wn, l32, hi);
 }
+
+template <int BN_, int WM, int WN, bool FC1>
+struct MxSplitBody {
+  static constexpr int BM = 128, BN = BN_;
+  static constexpr int lds = kMxSplitLds;
+  static constexpr bool combine = false;  // no top-1 combine epilogue
+  template <bool CMB>
+  __device__ __forceinline__ static void run(const Tile& t, char* smem, const MxA& A, const MxB& B,
+                                             const MxOut& O, int N, int K) {
+    static_assert(!CMB, "queue launches only");
+    mx_tile_split<BN, WM, WN, FC1>(t, smem, A, B, O, N, K);
+  }
+};
 
 template <int BM_, int BN_, int WM, int WN, bool FC1, int STAGES, int SPREAD>
 struct MxBody {
   static constexpr int BM = BM_, BN = BN_;
+  static constexpr bool combine = true;  // can run the top-1 combine epilogue
   static constexpr int lds = mx_lds_bytes<BM, BN, FC1, WM * WN, STAGES>();
   template <bool CMB>
   __device__ __forceinline__ static void run(const Tile& t, char* smem, const MxA& A, const MxB& B,
@@ -447,6 +713,22 @@ using MxFc1B64 = MxBody<64, 128, 2, 4, true, 3, 0>;
 using MxFc2B128w = MxBody<128, 256, 2, 4, false, 3, 1>;
 using MxFc2B128 = MxBody<128, 128, 2, 4, false, 4, 0>;
 using MxFc2B64w = MxBody<64, 256, 2, 4, false, 3, 0>;
+// split-ring bodies of the queue launches
+using MxFc1S = MxSplitBody<128, 2, 4, true>;
+using MxFc2S = MxSplitBody<256, 2, 4, false>;
+
+// The split-ring queue bodies take 32-bit source offsets (codes of every
+// activation row and of each expert's weight rows within 2^31 bytes of their
+// base) and whole n-tiles (N a multiple of BN), for the routed experts and
+// the dense tail alike.
+bool mx_split_fits(const MxA& a, int64_t N, int64_t K, int BN, const MxDense* dense) {
+  const int64_t lim = int64_t(1) << 31;
+  if (a.rows * K > lim || N * K > lim || N % BN != 0 || a.rows * (K / 32) > lim) return false;
+  if (dense && dense->rows > 0)
+    return dense->rows * dense->K <= lim && int64_t(dense->N) * dense->K <= lim &&
+           dense->N % BN == 0;
+  return true;
+}
 
 // Queue launches from 192 rows per expert on average (as the bf16 GEMM).
 bool use_queue_mx(int64_t max_rows, int64_t E) {
@@ -464,7 +746,7 @@ void launch_mx(const MxA& a, const MxB& b, const MxOut& o, const int32_t* counts
     dn.wgs = static_cast<int>(grid_for(dn.rows, 1, Body::BM, dn.N, Body::BN));
   }
   const int e = static_cast<int>(E), n = static_cast<int>(N), k = static_cast<int>(K);
-  if constexpr (!FC1) {
+  if constexpr (!FC1 && Body::combine) {
     if (o.cmb.out) {  // callers pass neither a tail nor a queue
       const int64_t z = ceil_div(o.cmb.T, 8 * 16);  // 8 waves of 16 tokens
       hipLaunchKernelGGL((gmm_mx_kernel<FC1, Body, true>), dim3(static_cast<unsigned>(g + z)),
@@ -504,7 +786,9 @@ void launch_fc2_mx(const MxA& a, const MxB& b, const MxOut& o, const int32_t* co
                    int64_t h, int64_t f, int64_t max_rows, hipStream_t s,
                    const MxDense* dense = nullptr, int* queue = nullptr) {
   const int64_t avg = max_rows / E;
-  if (avg >= 192)
+  if (queue && !o.cmb.out && use_queue_mx(max_rows, E) && mx_split_fits(a, h, f, 256, dense))
+    launch_mx<false, MxFc2S>(a, b, o, counts, E, h, f, max_rows, s, dense, queue);
+  else if (avg >= 192)
     launch_mx<false, MxFc2B128w>(a, b, o, counts, E, h, f, max_rows, s, dense, queue);
   else if (avg >= 80)
     launch_mx<false, MxFc2B128>(a, b, o, counts, E, h, f, max_rows, s, dense, queue);
@@ -515,7 +799,9 @@ void launch_fc2_mx(const MxA& a, const MxB& b, const MxOut& o, const int32_t* co
 void launch_fc1_mx(const MxA& a, const MxB& b, const MxOut& o, const int32_t* counts, int64_t E,
                    int64_t h, int64_t f, int64_t max_rows, hipStream_t s,
                    const MxDense* dense = nullptr, int* queue = nullptr) {
-  if (max_rows / E >= 80)
+  if (queue && use_queue_mx(max_rows, E) && mx_split_fits(a, f, h, 128, dense))
+    launch_mx<true, MxFc1S>(a, b, o, counts, E, f, h, max_rows, s, dense, queue);
+  else if (max_rows / E >= 80)
     launch_mx<true, MxFc1B128>(a, b, o, counts, E, f, h, max_rows, s, dense, queue);
   else
     launch_mx<true, MxFc1B64>(a, b, o, counts, E, f, h, max_rows, s, dense, queue);

@@ -173,6 +173,14 @@ __device__ __forceinline__ void dma16s(uint32_t voff, const void* sbase, uint32_
                : "memory");
 }
 
+// dma4 with the source as a 32-bit byte offset from a base held in SGPRs.
+__device__ __forceinline__ void dma4s(uint32_t voff, const void* sbase, uint32_t lds_base) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "{m0}"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "memory");
+}
+
 // A pointer the compiler can keep in SGPRs (its value taken from the first
 // active lane; callers pass wave-uniform pointers).
 __device__ __forceinline__ const char* uniform_ptr(const void* p) {

@@ -441,15 +441,21 @@ def test_layer_mxfp8_full_size_sampled(name, n_tok):
         assert torch.equal(out, o2)
 
 
-@pytest.mark.parametrize("fs", [0, 256])
-def test_mxfp8_tile_queue_and_folded_shared_expert_match_plain_launches(fs):
+# (h, f): FC1 runs k = h in stages of 128 over N = f, FC2 k = f over N = h; the
+# split-ring queue bodies need N a multiple of 128 (FC1) / 256 (FC2), else the
+# plain queue body runs: (256, 384) splits both with 2 and 3 stages, (128, 256)
+# splits FC1 with 1 stage and FC2 falls back, (512, 128) splits FC1 with 4
+# stages and FC2 with 1
+@pytest.mark.parametrize("h,f,fs", [(256, 384, 0), (256, 384, 256), (128, 256, 0), (128, 256, 128),
+                                    (512, 128, 0), (512, 128, 256)])
+def test_mxfp8_tile_queue_and_folded_shared_expert_match_plain_launches(h, f, fs):
     """The MXFP8 GEMMs with a tile queue (experts of >= 192 rows on average)
     give the bits of one workgroup per tile, and with the shared expert's
     tiles folded into the routed launches the shared act and output are the
     bits of separate E = 1 launches; on repeated calls with one queue, which
     is zero again afterwards."""
     import datagen
-    cfg = datagen.MoEConfig("mx-queue", T=2048, h=256, E=16, K=2, f=384, dtype="bf16",
+    cfg = datagen.MoEConfig("mx-queue", T=2048, h=h, E=16, K=2, f=f, dtype="bf16",
                             score="sigmoid", expert_bias=True, shared_f=fs)
     log(f"mxfp8 tile queue / fold: {cfg}")
     inp = datagen.make_inputs(cfg, seed=21, device=DEV)
