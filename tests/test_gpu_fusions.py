@@ -297,6 +297,15 @@ def test_tile_queue_matches_one_tile_per_workgroup(T, E, K, f, h, fs):
         if fs:
             assert torch.equal(s0, s1) and torch.equal(o0, o1)
         assert int(q.abs().sum().item()) == 0, "the queue is left zeroed"
+    if fs:
+        # no routed rows: the queue holds the shared expert's tiles alone
+        zero = torch.zeros_like(tpe)
+        _, s2 = moe.moe_grouped_fc1_swiglu_gather_shared(
+            x, st, zero, inp["w_gate"], inp["w_up"], inp["shared_gate"], inp["shared_up"], queue=q)
+        _, o2 = moe.moe_grouped_fc2_shared(a1, zero, inp["w_down"], s2, inp["shared_down"], queue=q)
+        torch.cuda.synchronize()
+        assert torch.equal(s2, s0) and torch.equal(o2, o0)
+        assert int(q.abs().sum().item()) == 0, "the queue is left zeroed"
 
 
 # every expert empty; every row in one expert; one row against the rest;
