@@ -1196,6 +1196,10 @@ using Fc2N64 = Body<64, 128, 2, 4, false, 4, 64>;
 // decoded per-expert tables
 using Fc1B64p = Body<64, 128, 2, 4, true, 3, 64>;
 using Fc2B64p = Body<64, 256, 2, 4, false, 3, 64>;
+// 64-row bodies of the split-ring queue launches, which keep no tables in
+// LDS: 4 stages (160 KB), three in flight for these weight-streaming tiles
+using Fc1B64q = Body<64, 128, 2, 4, true, 4, 64>;
+using Fc2B64q = Body<64, 256, 2, 4, false, 4, 64>;
 
 // Persistent launches (see gmm_bf16_kernel) for experts of >= 512 rows on
 // average, at most kPersistMaxExperts of them: measured on the Mixtral- and
@@ -1233,9 +1237,9 @@ void launch_gemm(int32_t dtype, const AOperand& A, const void* B0, const void* B
   if (q && use_queue(max_rows, E) && !cmb.epi.out) {  // tile-queue launch (bm == 256 here)
     if (split_fits(A, N, K, FC1 ? 128 : 256, sh)) {
       if constexpr (FC1)
-        launch_qsplit<true, 128, 2, 4, Fc1B128, Fc1B64p>(A, B0, B1, C, counts, E, N, K, max_rows, s, sh, q);
+        launch_qsplit<true, 128, 2, 4, Fc1B128, Fc1B64q>(A, B0, B1, C, counts, E, N, K, max_rows, s, sh, q);
       else
-        launch_qsplit<false, 256, 4, 2, Fc2B128, Fc2B64p>(A, B0, B1, C, counts, E, N, K, max_rows, s, sh, q);
+        launch_qsplit<false, 256, 4, 2, Fc2B128, Fc2B64q>(A, B0, B1, C, counts, E, N, K, max_rows, s, sh, q);
       return;
     }
     if constexpr (FC1)
