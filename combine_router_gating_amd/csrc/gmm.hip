@@ -43,9 +43,11 @@
 // workgroups of a routed launch (DenseTail); given a tile queue, layers of
 // experts with >= 192 rows on average run one workgroup per CU that takes
 // tiles from per-XCD counters (the shared expert's tiles after the routed
-// ones); without one, layers of large, alike experts run one persistent
-// workgroup per CU with a fixed tile sequence; top-1 layers can take the
-// combine as FC2's epilogue.
+// ones), their 256-row tiles on the split-ring body (gmm_tile_split:
+// activation and weight rows in separate LDS rings, waves 0-3 issuing every
+// load, waves 4-7 only multiplying); without one, layers of large, alike
+// experts run one persistent workgroup per CU with a fixed tile sequence;
+// top-1 layers can take the combine as FC2's epilogue.
 #include <algorithm>
 #include <type_traits>
 

@@ -16,7 +16,8 @@
 //   FC2: expert_out = act Wd^T, stored bf16.
 // The tile scheduler is the bf16 GEMM's (gmm_sched.h); a stage holds 128 k
 // (128 bytes per row, the same swizzled LDS layout) plus the rows' 4 scale
-// bytes, all filled by direct global->LDS loads.
+// bytes, all filled by direct global->LDS loads.  Tile-queue launches run the
+// split-ring body (mx_tile_split) as the bf16 GEMM's do.
 #include <type_traits>
 
 #include "gmm_sched.h"
