@@ -42,7 +42,7 @@
 // tile order; the shared expert's dense GEMM can ride as the last
 // workgroups of a routed launch (DenseTail); given a tile queue, layers of
 // experts with >= 192 rows on average run one workgroup per CU that takes
-// tiles from per-XCD counters (the shared expert's tiles after the routed
+// tiles from per-XCD counters (the shared expert's tiles before the routed
 // ones), their 256-row tiles on the split-ring body (gmm_tile_split:
 // activation and weight rows in separate LDS rings, waves 0-3 issuing every
 // load, waves 4-7 only multiplying); without one, layers of large, alike
@@ -692,7 +692,7 @@ __global__ void __launch_bounds__(NW * 64) gmm_bf16_kernel(
   __shared__ __attribute__((aligned(1024))) char smem[LDS];
   if constexpr (QUEUE) {
     // One workgroup per CU takes tiles from the queue (queue_tiles): the
-    // routed experts' logical tiles, then the dense tail's.
+    // dense tail's logical tiles, then the routed experts' (kDenseFirst).
     const int NT = (N + BN - 1) / BN;
     __shared__ int p_toff[kPersistMaxExperts + 1], p_roff[kPersistMaxExperts],
         p_n[kPersistMaxExperts];
@@ -726,8 +726,9 @@ __global__ void __launch_bounds__(NW * 64) gmm_bf16_kernel(
       const uint16_t* tb1 = B1;
       uint16_t* tc = C;
       int tn = N, tk = K;
-      if (TAIL && L >= routed) {
-        t = dense_tile_at<BMAX, kDenseBand>(L - routed, ntd, dn.rows, 0);
+      const int64_t nd = total - routed;  // the dense tail's tiles
+      if (TAIL && (kDenseFirst ? L < nd : L >= routed)) {
+        t = dense_tile_at<BMAX, kDenseBand>(kDenseFirst ? L : L - routed, ntd, dn.rows, 0);
         ta = dn.A;
         tg = nullptr;
         tar = dn.rows;
@@ -737,7 +738,7 @@ __global__ void __launch_bounds__(NW * 64) gmm_bf16_kernel(
         tn = dn.N;
         tk = dn.K;
       } else {
-        t = tile_at<BMAX>(L, NT, E, p_toff, p_roff, p_n);
+        t = tile_at<BMAX>(TAIL && kDenseFirst ? L - nd : L, NT, E, p_toff, p_roff, p_n);
       }
       t.nrows = __builtin_amdgcn_readfirstlane(t.nrows);
       if (t.nrows > 128) Body256::template run<CMB>(t, smem, ta, tg, tar, tb0, tb1, tc, tn, tk, epi);
@@ -833,7 +834,8 @@ __global__ void __launch_bounds__(NW * 64) gmm_bf16_kernel(
 // first wave decodes the counts again (WaveCounts, E <= kPersistMaxExperts)
 // and hands the tile to the others through the first bytes of LDS.  Ragged
 // tiles of <= 128 rows run the 128- and 64-row bodies of the plain queue
-// launch; the shared expert's tiles (DenseTail) follow the routed ones.
+// launch; the shared expert's tiles (DenseTail) come before the routed ones
+// (kDenseFirst).
 template <bool FC1, int BN, int WM, int WN, class Body128, class Body64, bool TAIL>
 __global__ void __launch_bounds__(512) gmm_bf16_qsplit_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ gather, int64_t a_rows,
@@ -894,11 +896,11 @@ __global__ void __launch_bounds__(512) gmm_bf16_qsplit_kernel(
       Tile t{0, 0, 0, 0};
       int src = -1;  // -1: none left; 0: routed; 1: dense tail
       if (L >= 0) {
-        if (TAIL && L >= routed) {
-          t = dense_tile_at<256, kDenseBand>(L - routed, ntd, dn.rows, 0);
+        if (TAIL && (kDenseFirst ? L < dense : L >= routed)) {
+          t = dense_tile_at<256, kDenseBand>(kDenseFirst ? L : L - routed, ntd, dn.rows, 0);
           src = 1;
         } else {
-          t = wc.tile<256>(L, NT, E);
+          t = wc.tile<256>(TAIL && kDenseFirst ? L - dense : L, NT, E);
           src = 0;
         }
       }

@@ -303,6 +303,13 @@ constexpr int kPersistMaxExperts = 256;
 // previous one, and the leave counter after the eight.
 constexpr int kQGroup = 32;
 constexpr int kQStride = 32;
+// bf16 queue launches that carry the shared expert's dense tiles take them
+// first: those tiles are all full and alike, and the launch then ends on
+// the routed experts' tiles, whose ragged ones are shorter (measured on the
+// DeepSeek-V3-shaped layer: FC1 -0.9 %, FC2 -1.6 %, the combine +5 %, as
+// the shared expert's output is no longer the last thing FC2 wrote; the
+// MXFP8 launches, where FC2 came out slower, keep the shared tiles last).
+constexpr bool kDenseFirst = true;
 static_assert(9 * kQStride * 4 <= MOE_GEMM_QUEUE_BYTES, "queue counters fit the buffer");
 
 // Decode the counts once for a workgroup that runs many tiles: the scan
