@@ -385,9 +385,10 @@ moe_status moe_grouped_fc1_swiglu_gather(int64_t E, int64_t h, int64_t f, int64_
  * moe_grouped_fc1_swiglu_gather_shared — moe_grouped_fc1_swiglu_gather and
  * the shared expert's FC1 in ONE launch.  [MC] §2 and §11: the shared
  * expert runs on every token beside the routed experts and its output is
- * added after the combine; here its tiles are the last workgroups of the
- * routed launch, so they fill the routed tiles' tail instead of competing
- * with the router on a second stream.
+ * added after the combine; here its tiles ride in the routed launch (the
+ * last workgroups of a one-tile-per-workgroup launch, the first tiles a
+ * tile-queue launch hands out) instead of competing with the router on a
+ * second stream.
  *   routed arguments  as moe_grouped_fc1_swiglu_gather (max_rows may be 0)
  *   fs                shared expert ffn size (a multiple of 64)
  *   shared_gate, shared_up [fs,h] bf16
