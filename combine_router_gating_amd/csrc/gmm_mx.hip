@@ -17,7 +17,8 @@
 // The tile scheduler is the bf16 GEMM's (gmm_sched.h); a stage holds 128 k
 // (128 bytes per row, the same swizzled LDS layout) plus the rows' 4 scale
 // bytes, all filled by direct global->LDS loads.  Tile-queue launches run the
-// split-ring body (mx_tile_split) as the bf16 GEMM's do.
+// split-ring body (mx_tile_split) as the bf16 GEMM's do, and their ragged
+// tiles of at most 64 rows a 64-row body.
 #include <type_traits>
 
 #include "gmm_sched.h"
@@ -585,18 +586,6 @@ __device__ __forceinline__ void mx_tile_split(const Tile& tile, char* smem, cons
   mx_store<MI, NB, NI, WTM, WTN, FC1, false>(acc, tile, O, N, n0, wm, wn, l32, hi);
 }
 
-template <int BN_, int WM, int WN, bool FC1>
-struct MxSplitBody {
-  static constexpr int BM = 128, BN = BN_;
-  static constexpr int lds = kMxSplitLds;
-  static constexpr bool combine = false;  // no top-1 combine epilogue
-  template <bool CMB>
-  __device__ __forceinline__ static void run(const Tile& t, char* smem, const MxA& A, const MxB& B,
-                                             const MxOut& O, int N, int K) {
-    static_assert(!CMB, "queue launches only");
-    mx_tile_split<BN, WM, WN, FC1>(t, smem, A, B, O, N, K);
-  }
-};
 
 template <int BM_, int BN_, int WM, int WN, bool FC1, int STAGES, int SPREAD>
 struct MxBody {
@@ -607,6 +596,24 @@ struct MxBody {
   __device__ __forceinline__ static void run(const Tile& t, char* smem, const MxA& A, const MxB& B,
                                              const MxOut& O, int N, int K) {
     mx_tile<BM, BN, WM, WN, FC1, STAGES, SPREAD, CMB>(t, smem, A, B, O, N, K);
+  }
+};
+
+// The queue launches' body: the split ring for tiles of more than 64 rows, a
+// 64-row body (Small, the same weight columns) for the shorter ragged tiles,
+// which then spend half the MFMA work on padding rows.
+template <int BN_, int WM, int WN, bool FC1, class Small>
+struct MxSplitBody {
+  static_assert(Small::BN == BN_ && Small::BM == 64, "a 64-row body of the same columns");
+  static constexpr int BM = 128, BN = BN_;
+  static constexpr int lds = kMxSplitLds > Small::lds ? kMxSplitLds : Small::lds;
+  static constexpr bool combine = false;  // no top-1 combine epilogue
+  template <bool CMB>
+  __device__ __forceinline__ static void run(const Tile& t, char* smem, const MxA& A, const MxB& B,
+                                             const MxOut& O, int N, int K) {
+    static_assert(!CMB, "queue launches only");
+    if (t.nrows > 64) mx_tile_split<BN, WM, WN, FC1>(t, smem, A, B, O, N, K);
+    else Small::template run<false>(t, smem, A, B, O, N, K);
   }
 };
 
@@ -715,8 +722,8 @@ using MxFc2B128w = MxBody<128, 256, 2, 4, false, 3, 1>;
 using MxFc2B128 = MxBody<128, 128, 2, 4, false, 4, 0>;
 using MxFc2B64w = MxBody<64, 256, 2, 4, false, 3, 0>;
 // split-ring bodies of the queue launches
-using MxFc1S = MxSplitBody<128, 2, 4, true>;
-using MxFc2S = MxSplitBody<256, 2, 4, false>;
+using MxFc1S = MxSplitBody<128, 2, 4, true, MxFc1B64>;
+using MxFc2S = MxSplitBody<256, 2, 4, false, MxFc2B64w>;
 
 // The split-ring queue bodies take 32-bit source offsets (codes of every
 // activation row and of each expert's weight rows within 2^31 bytes of their
